@@ -1,0 +1,191 @@
+"""Planted mistakes in the oracle (on the CPU) must each fail at least one
+pin.  This shows the pins are sharp enough to catch a dropped term, a wrong
+sign, a wrong axis or index, or a wrong rounding rule.  CPU only."""
+import numpy as np
+import pytest
+
+import oracle
+import oracle.attention as oatt
+import oracle.quant as oq
+import oracle.rvq as orvq
+import oracle.zoned as oz
+import test_oracle_attention as TA
+import test_oracle_quant as TQ
+import test_oracle_rvq as TR
+import test_oracle_zoned as TZ
+
+_orig_qg = oq.quantize_groups
+
+
+def _qg_variant(levels_fn=None, round_fn=np.rint, zero_fn=None, fp32_scale=False):
+    def qg(x16, bits):
+        x16 = np.asarray(x16, np.float16)
+        L = np.float32(levels_fn(bits) if levels_fn else 2 ** bits - 1)
+        x = x16.astype(np.float32)
+        mn, mx = x.min(-1), x.max(-1)
+        s32 = (mx - mn) / L
+        s = s32.astype(np.float16)
+        z = (zero_fn(mn, mx) if zero_fn else mn).astype(np.float16)
+        sf = (s32 if fp32_scale else s.astype(np.float32))[..., None]
+        zf = z.astype(np.float32)[..., None]
+        with np.errstate(divide="ignore", invalid="ignore"):
+            t = (x - zf) / sf
+        q = np.clip(round_fn(t), 0, L)
+        q = np.where(sf == 0, 0, q)
+        return q.astype(np.uint8), s, z
+    return qg
+
+
+def _half_away(t):
+    return np.sign(t) * np.floor(np.abs(t) + 0.5)
+
+
+QUANT_MUTANTS = {
+    "levels_2^b": _qg_variant(levels_fn=lambda b: 2 ** b),
+    "floor": _qg_variant(round_fn=np.floor),
+    "round_half_away": _qg_variant(round_fn=_half_away),
+    "zero_is_mean": _qg_variant(zero_fn=lambda mn, mx: (mn + mx) / 2),
+    "codes_vs_fp32_scale": _qg_variant(fp32_scale=True),
+}
+
+
+def _run_quant_pins():
+    for case in TQ._read_quant_cases():
+        TQ.test_hand_fixtures(case)
+    for bits in (2, 4, 8):
+        TQ.test_levels_are_exactly_two_to_the_b(bits)
+        TQ.test_error_at_most_half_scale(bits)
+        TQ.test_codes_hit_both_ends(bits)
+
+
+@pytest.mark.parametrize("name", sorted(QUANT_MUTANTS))
+def test_quantizer_mutants_are_caught(monkeypatch, name):
+    _run_quant_pins()                                    # clean oracle passes
+    monkeypatch.setattr(TQ, "quantize_groups", QUANT_MUTANTS[name])
+    with pytest.raises(AssertionError):
+        _run_quant_pins()
+
+
+def test_key_axis_mutant_is_caught(monkeypatch):
+    # keys grouped along channels instead of tokens
+    monkeypatch.setattr(TQ, "quantize_k", oq.quantize_v)
+    monkeypatch.setattr(oracle, "dequantize_k", oq.dequantize_v)
+    with pytest.raises(AssertionError):
+        TQ.test_axis_pins_keys_per_channel_values_per_token()
+
+
+def test_pack_order_mutant_is_caught(monkeypatch):
+    def pack_msb_first(codes, bits):
+        codes = np.asarray(codes)
+        per = 32 // bits
+        flat = codes.reshape(-1, per).astype(np.uint64)
+        w = np.zeros(flat.shape[0], np.uint64)
+        for j in range(per):
+            w |= flat[:, j] << np.uint64((per - 1 - j) * bits)
+        return w.astype(np.uint32).reshape(codes.shape[:-1] + (codes.shape[-1] * bits // 32,))
+    monkeypatch.setattr(TQ, "pack_codes", pack_msb_first)
+    with pytest.raises(AssertionError):
+        for case in TQ._read_pack_cases():
+            TQ.test_pack_hand_fixtures(case)
+
+
+def test_rope_mutants_are_caught(monkeypatch):
+    orig = oatt.rope_rotate
+
+    def sign_flipped(x, positions, theta):
+        return orig(x, -np.asarray(positions, np.float64), theta)
+
+    def half_split(x, positions, theta):
+        x = np.asarray(x, np.float64)
+        T, d = x.shape
+        w = oatt.rope_frequencies(d, theta)
+        phi = np.asarray(positions, np.float64)[:, None] * w[None]
+        a, b = x[:, :d // 2], x[:, d // 2:]
+        return np.concatenate([a * np.cos(phi) - b * np.sin(phi), a * np.sin(phi) + b * np.cos(phi)], 1)
+
+    for mutant in (sign_flipped, half_split):
+        monkeypatch.setattr(TA, "rope_rotate", mutant)
+        with pytest.raises(AssertionError):
+            TA.test_rope_properties()
+
+
+def test_attention_mutants_are_caught(monkeypatch):
+    def no_scale(q, k, v, sm_scale):
+        return oatt.attention_fp64.__wrapped__(q, k, v, 1.0) if hasattr(oatt.attention_fp64, "__wrapped__") else _attn(q, k, v, 1.0)
+
+    def _attn(q, k, v, s):
+        lg = s * (np.asarray(q, np.float64) @ np.asarray(k, np.float64).T)
+        p = np.exp(lg - lg.max(1, keepdims=True))
+        return (p / p.sum(1, keepdims=True)) @ np.asarray(v, np.float64)
+
+    def transposed_weights(q, k, v, s):
+        lg = s * (np.asarray(q, np.float64) @ np.asarray(k, np.float64).T)
+        p = np.exp(lg - lg.max(1, keepdims=True))
+        p = p / p.sum(1, keepdims=True)
+        return p[:, ::-1] @ np.asarray(v, np.float64)
+
+    for mutant in (no_scale, transposed_weights):
+        monkeypatch.setattr(TA, "attention_fp64", mutant)
+        with pytest.raises(AssertionError):
+            TA.test_matches_library_sdpa()
+
+
+def test_gqa_mapping_mutant_is_caught(monkeypatch):
+    orig = oatt.kivi_decode_attention
+
+    def modulo_mapping(q16, cache, sm_scale, rows=None):
+        c = dict(cache)
+        # query head h reads KV head h % Hkv instead of h // G
+        B, Hq, Hkv = c["B"], c["Hq"], c["Hkv"]
+        out = np.empty((B, Hq, c["d"]))
+        for h in range(Hq):
+            sub = dict(c, Hq=Hkv)
+            qq = np.asarray(q16)[:, [h] * Hkv]
+            out[:, h] = orig(qq, sub, sm_scale)[:, h % Hkv]
+        return out
+
+    monkeypatch.setattr(TA, "kivi_decode_attention", modulo_mapping)
+    with pytest.raises(AssertionError):
+        TA.test_gqa_head_mapping()
+
+
+def test_rvq_mutants_are_caught(monkeypatch):
+    orig_dist = orvq.rvq_stage_distances
+
+    def plus_residual(x16, cbs, prefix=None):
+        cbs = np.asarray(cbs, np.float16)
+        r = np.asarray(x16, np.float16).astype(np.float32)
+        idx = np.empty((r.shape[0], cbs.shape[0]), np.int64)
+        for s in range(cbs.shape[0]):
+            idx[:, s] = orig_dist(r, cbs[s]).argmin(1)
+            r = r + cbs[s][idx[:, s]].astype(np.float32)      # wrong sign
+        return idx.astype(np.int16), r
+
+    def last_tie(x16, cbs, prefix=None):
+        cbs = np.asarray(cbs, np.float16)
+        r = np.asarray(x16, np.float16).astype(np.float32)
+        idx = np.empty((r.shape[0], cbs.shape[0]), np.int64)
+        for s in range(cbs.shape[0]):
+            dd = orig_dist(r, cbs[s])
+            idx[:, s] = dd.shape[1] - 1 - dd[:, ::-1].argmin(1)  # highest index on ties
+            r = r - cbs[s][idx[:, s]].astype(np.float32)
+        return idx.astype(np.int16), r
+
+    monkeypatch.setattr(TR, "rvq_encode", plus_residual)
+    with pytest.raises(AssertionError):
+        TR.test_brute_force_nearest_tiny_codebooks()
+    monkeypatch.setattr(TR, "rvq_encode", last_tie)
+    with pytest.raises(AssertionError):
+        TR.test_ties_go_to_lowest_index_small_integers()
+
+
+def test_zoned_eviction_mutant_is_caught(monkeypatch):
+    orig_layout = oz._unit_layout
+
+    def keep_evicted(vb, kb, d, C):
+        vb = np.where(np.asarray(vb) == 0, 2, vb)         # width 0 kept at 2 bits
+        return orig_layout(vb, kb, d, C)
+
+    monkeypatch.setattr(oz, "_unit_layout", keep_evicted)
+    with pytest.raises(AssertionError):
+        TZ.test_width_zero_is_eviction()
