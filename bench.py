@@ -1,0 +1,177 @@
+"""Benchmark: decode attention over a 2-bit uniform (KIVI-layout) KV cache on
+one MI355X, Llama-3.1-8B-shaped GQA workload (batch 4, 32 query / 8 KV
+heads, head dim 128, 32768 quantized tokens + 128 fp16 recent tokens, RoPE
+theta 5e5).
+
+One step = one decode_attention_qkv call over the whole batch: every
+quantized token's packed codes and scales plus the fp16 recent zone are read
+from HBM, dequantized, rotated and attended (one fused launch; the
+cross-split merge runs inside it).  Inputs are resident in HBM before the
+timed region.  The compressed cache (~98 MiB) fits in the 256 MB Infinity
+Cache, so the timed steps rotate over several independent replicas whose
+total exceeds it.
+
+Prints one JSON line.  Usage:
+    python bench.py [--steps K] [--warmup W] [--bits 2|4] [--replicas R]
+                    [--no-cpu-baseline] [--rows]
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E, published
+
+
+def algorithmic_bytes(cfg, bits):
+    """Bytes one decode step must move: packed codes, fp16 scale/zero of K
+    and V, the fp16 recent zone, the query and the fp32 output."""
+    B, Hq, Hkv, d, T_q, R = cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["d"], cfg["T_q"], cfg["R"]
+    units = B * Hkv
+    codes = 2 * units * T_q * d * bits // 8
+    k_sz = units * (T_q // 32) * d * 2 * 2
+    v_sz = units * T_q * (d // 32) * 2 * 2
+    recent = 2 * units * R * d * 2
+    return codes + k_sz + v_sz + recent + B * Hq * d * 2 + B * Hq * d * 4
+
+
+def cpu_baseline(inp, cfg, bits, scale, budget_s=12.0):
+    """Time the oracle's decode (dequantization from packed buffers + fp64
+    attention) on whole (batch, KV head) units until the budget is spent;
+    scale to KV-tokens/s of the full step."""
+    import oracle
+    from threadpoolctl import threadpool_info
+    B, Hkv, G = cfg["B"], cfg["Hkv"], cfg["Hq"] // cfg["Hkv"]
+    units = [(b, h) for b in range(B) for h in range(Hkv)]
+    done, elapsed = 0, 0.0
+    for b, h in units:
+        sub = {k: v[b:b + 1, h:h + 1] for k, v in inp.items() if k != "q"}
+        kc, ks, kz = oracle.quantize_k(sub["k"], bits)          # not timed: cache build
+        vc, vs, vz = oracle.quantize_v(sub["v"], bits)
+        cache = dict(B=1, Hq=G, Hkv=1, d=cfg["d"], bits=bits, T_q=cfg["T_q"], R=cfg["R"],
+                     rope_theta=cfg["rope_theta"], k_codes=oracle.pack_codes(kc, bits),
+                     v_codes=oracle.pack_codes(vc, bits), k_scale=ks, k_zero=kz,
+                     v_scale=vs, v_zero=vz, k_recent=sub["k_recent"], v_recent=sub["v_recent"])
+        q = inp["q"][b:b + 1, h * G:(h + 1) * G]
+        t0 = time.perf_counter()
+        oracle.kivi_decode_attention(q, cache, scale)
+        elapsed += time.perf_counter() - t0
+        done += 1
+        if elapsed > budget_s:
+            break
+    step_s = elapsed / done * len(units)
+    blas = [i.get("num_threads", 1) for i in threadpool_info()]
+    return dict(value=B * (cfg["T_q"] + cfg["R"]) / step_s, unit="KV-tokens/s",
+                cores=int(max(blas) if blas else 1), kind="oracle",
+                sample=f"{done} of {len(units)} (batch, KV head) units, {elapsed:.1f} s; "
+                       f"numpy dequantization + fp64 attention, scaled to the full step")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--bits", type=int, default=2, choices=[2, 4])
+    ap.add_argument("--replicas", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rows", action="store_true", help="also time the other hot-path rows")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for {args.gpus}); the decode path shards "
+              f"by (batch, KV head) with no communication, see DESIGN.md", file=sys.stderr)
+        return 2
+
+    import torch
+    import dequant_decode_attention_amd as dqa
+    from workloads import CONFIGS, kivi_inputs
+
+    cfg = CONFIGS["c3"]
+    bits = args.bits
+    dev = torch.device("cuda:0")
+    inp = kivi_inputs(cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["d"], cfg["T_q"], cfg["R"], seed=3,
+                      outliers=cfg["outliers"])
+    scale = 1.0 / math.sqrt(cfg["d"])
+    k = torch.from_numpy(inp["k"]).to(dev)
+    v = torch.from_numpy(inp["v"]).to(dev)
+    kc, ks, kz = dqa.quantize_pack_k(k, bits)
+    vc, vs, vz = dqa.quantize_pack_v(v, bits)
+    kr = torch.from_numpy(inp["k_recent"]).to(dev)
+    vr = torch.from_numpy(inp["v_recent"]).to(dev)
+    q = torch.from_numpy(inp["q"]).to(dev)
+    del k, v
+    caches = []
+    for r in range(args.replicas):
+        t = [x.clone() for x in (kc, ks, kz, vc, vs, vz, kr, vr)]
+        caches.append(dqa.KiviCache(cfg["Hq"], bits, *t, rope_theta=cfg["rope_theta"]))
+    out = torch.empty((cfg["B"], cfg["Hq"], cfg["d"]), dtype=torch.float32, device=dev)
+    ws = [c.workspace(dev) for c in caches]
+    torch.cuda.synchronize()
+
+    for i in range(args.warmup):
+        dqa.decode_attention_qkv(q, caches[i % len(caches)], scale, out=out, workspace=ws[i % len(ws)])
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        dqa.decode_attention_qkv(q, caches[i % len(caches)], scale, out=out, workspace=ws[i % len(ws)])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+
+    nbytes = algorithmic_bytes(cfg, bits)
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    kv_tokens = cfg["B"] * (cfg["T_q"] + cfg["R"])
+    line = {
+        "metric": "decode attention KV-tokens/s over a 2-bit cache (+ achieved HBM GB/s, % of peak)"
+                  if bits == 2 else "decode attention KV-tokens/s over a 4-bit cache",
+        "value": kv_tokens / (ms * 1e-3),
+        "unit": "KV-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg["workload"], "batch": cfg["B"], "q_heads": cfg["Hq"],
+                   "kv_heads": cfg["Hkv"], "head_dim": cfg["d"], "quantized_tokens": cfg["T_q"],
+                   "recent_tokens": cfg["R"], "bits": bits, "group": 32,
+                   "rope_theta": cfg["rope_theta"], "replicas": args.replicas},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "algorithmic_bytes": nbytes, "kernel": "kivi_decode_kernel"},
+    }
+
+    # achievable streaming rate on a buffer of the same size, same run
+    src = torch.empty(nbytes // 16 * 16 * 4, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dqa.stream_copy(src, dst)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(10):
+        dqa.stream_copy(src, dst)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    line["stream_copy_gbps"] = 2 * src.numel() * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(inp, cfg, bits, scale)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,283 @@
+"""Python binding of libdqattn (decode attention over a low-bit KV cache on
+MI355X / gfx950).
+
+Argument marshalling only: every step runs in the HIP kernels of
+``libdqattn.so``.  PyTorch supplies device memory (outputs and workspaces
+are allocated with torch) and the current stream.  Importing this package
+raises if the library has not been built; there is no fallback path.
+
+Function names and semantics mirror ``include/dqattn.h``.
+"""
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdqattn.so")
+
+DQA_OK = 0
+_STATUS = {0: "DQA_OK", 1: "DQA_ERR_NULL", 2: "DQA_ERR_SHAPE", 3: "DQA_ERR_BITS",
+           4: "DQA_ERR_WORKSPACE", 5: "DQA_ERR_UNSUPPORTED", 6: "DQA_ERR_HIP",
+           7: "DQA_ERR_PLAN"}
+
+
+class DqaError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn}: {lib.dqa_status_string(status).decode()}")
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python dequant_decode_attention_amd/build.py`")
+
+lib = ctypes.CDLL(LIB_PATH)
+
+_vp, _i, _sz, _f, _i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_float, ctypes.c_int64
+
+
+class KiviCacheStruct(ctypes.Structure):
+    """Mirror of ``dqa_kivi_cache``."""
+    _fields_ = [("B", _i), ("Hq", _i), ("Hkv", _i), ("d", _i), ("bits", _i),
+                ("T_q", _i), ("R", _i), ("rope_theta", _f),
+                ("k_codes", _vp), ("k_scale", _vp), ("k_zero", _vp),
+                ("v_codes", _vp), ("v_scale", _vp), ("v_zero", _vp),
+                ("k_recent", _vp), ("v_recent", _vp)]
+
+
+_SIGS = {
+    "dqa_status_string": (ctypes.c_char_p, [_i]),
+    "dqa_abi_version": (_i, []),
+    "quantize_pack_k": (_i, [_vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp]),
+    "quantize_pack_v": (_i, [_vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp]),
+    "decode_attention_workspace_bytes": (_sz, [ctypes.POINTER(KiviCacheStruct)]),
+    "decode_attention_qkv": (_i, [_vp, ctypes.POINTER(KiviCacheStruct), _f, _vp, _sz, _vp, _vp]),
+    "zoned_plan_words": (_sz, [_i, _i, _i, _i]),
+    "zoned_plan": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _vp, _sz, ctypes.POINTER(_sz)]),
+    "zoned_pack": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "decode_attention_zoned_workspace_bytes": (_sz, [_vp, _i]),
+    "decode_attention_zoned": (_i, [_vp, _i, _vp, _vp, _vp, _f, _vp, _sz, _vp, _vp]),
+    "rvq_encode_workspace_bytes": (_sz, [_i, _i]),
+    "rvq_encode": (_i, [_vp, _i64, _i, _vp, _i, _i, _vp, _vp, _sz, _vp]),
+    "rvq_decode_attention_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
+    "rvq_decode_attention": (_i, [_vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _i, _i, _f,
+                                  _vp, _sz, _vp, _vp]),
+    "dqa_stream_copy": (_i, [_vp, _vp, _sz, _vp]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _fn = getattr(lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+
+def _check(fn, status):
+    if status != DQA_OK:
+        raise DqaError(fn, status)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dev16(t, name):
+    if t.dtype != torch.float16 or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA float16 tensor")
+    return t.contiguous()
+
+
+# ---------------------------------------------------------------- quantize
+
+def quantize_pack_k(k, bits):
+    """k: fp16 [B, Hkv, T, d] -> (codes int32 [B, Hkv, T, d*bits/32] holding
+    uint32 words, scale fp16 [B, Hkv, T/32, d], zero fp16 [B, Hkv, T/32, d])."""
+    k = _dev16(k, "k")
+    B, H, T, d = k.shape
+    codes = torch.empty((B, H, T, d * bits // 32), dtype=torch.int32, device=k.device)
+    scale = torch.empty((B, H, T // 32, d), dtype=torch.float16, device=k.device)
+    zero = torch.empty_like(scale)
+    _check("quantize_pack_k", lib.quantize_pack_k(_ptr(k), B, H, T, d, bits, _ptr(codes),
+                                                  _ptr(scale), _ptr(zero), _stream(k.device)))
+    return codes, scale, zero
+
+
+def quantize_pack_v(v, bits):
+    """v: fp16 [B, Hkv, T, d] -> (codes int32 [B, Hkv, T, d*bits/32], scale fp16
+    [B, Hkv, T, d/32], zero fp16 [B, Hkv, T, d/32])."""
+    v = _dev16(v, "v")
+    B, H, T, d = v.shape
+    codes = torch.empty((B, H, T, d * bits // 32), dtype=torch.int32, device=v.device)
+    scale = torch.empty((B, H, T, d // 32), dtype=torch.float16, device=v.device)
+    zero = torch.empty_like(scale)
+    _check("quantize_pack_v", lib.quantize_pack_v(_ptr(v), B, H, T, d, bits, _ptr(codes),
+                                                  _ptr(scale), _ptr(zero), _stream(v.device)))
+    return codes, scale, zero
+
+
+# ---------------------------------------------------------------- KIVI decode
+
+class KiviCache:
+    """Device tensors of a uniform-layout cache plus its descriptor.
+
+    k_codes/v_codes int32 [B, Hkv, T_q, d*bits/32]; k_scale/k_zero fp16
+    [B, Hkv, T_q/32, d]; v_scale/v_zero fp16 [B, Hkv, T_q, d/32];
+    k_recent/v_recent fp16 [B, Hkv, R, d] (keys before RoPE) or None.
+    """
+
+    def __init__(self, Hq, bits, k_codes, k_scale, k_zero, v_codes, v_scale, v_zero,
+                 k_recent=None, v_recent=None, rope_theta=0.0, T_q=None, B=None, Hkv=None, d=None):
+        ref = k_codes if k_codes is not None else k_recent
+        self.B = ref.shape[0] if B is None else B
+        self.Hkv = ref.shape[1] if Hkv is None else Hkv
+        self.d = (k_scale.shape[3] if k_scale is not None else k_recent.shape[3]) if d is None else d
+        self.T_q = (k_codes.shape[2] if k_codes is not None else 0) if T_q is None else T_q
+        self.R = k_recent.shape[2] if k_recent is not None else 0
+        self.Hq, self.bits, self.rope_theta = Hq, bits, float(rope_theta)
+        self.tensors = dict(k_codes=k_codes, k_scale=k_scale, k_zero=k_zero, v_codes=v_codes,
+                            v_scale=v_scale, v_zero=v_zero, k_recent=k_recent, v_recent=v_recent)
+        self.tensors = {k: (None if v is None else v.contiguous()) for k, v in self.tensors.items()}
+        self._ws = None
+
+    def struct(self):
+        t = self.tensors
+        return KiviCacheStruct(self.B, self.Hq, self.Hkv, self.d, self.bits, self.T_q, self.R,
+                               self.rope_theta, *[(None if t[n] is None else t[n].data_ptr()) for n in
+                                                  ("k_codes", "k_scale", "k_zero", "v_codes",
+                                                   "v_scale", "v_zero", "k_recent", "v_recent")])
+
+    def workspace_bytes(self):
+        return lib.decode_attention_workspace_bytes(ctypes.byref(self.struct()))
+
+    def workspace(self, device):
+        """A zero-initialized workspace, cached on the cache object (the
+        library leaves its counters zero after each call)."""
+        n = self.workspace_bytes()
+        if self._ws is None or self._ws.numel() < n or self._ws.device != device:
+            self._ws = torch.zeros(max(n, 1), dtype=torch.uint8, device=device)
+        return self._ws
+
+
+def decode_attention_workspace_bytes(cache):
+    return cache.workspace_bytes()
+
+
+def decode_attention_qkv(q, cache, sm_scale, out=None, workspace=None):
+    """q: fp16 [B, Hq, d] (rotated when the cache uses RoPE) -> fp32 [B, Hq, d]."""
+    q = _dev16(q, "q")
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    ws = cache.workspace(q.device) if workspace is None else workspace
+    st = cache.struct()
+    _check("decode_attention_qkv",
+           lib.decode_attention_qkv(_ptr(q), ctypes.byref(st), float(sm_scale), _ptr(ws),
+                                    ws.numel(), _ptr(out), _stream(q.device)))
+    return out
+
+
+# ---------------------------------------------------------------- zoned
+
+class ZonedPlan:
+    """Host plan words (numpy int32), their device copy and the blob size."""
+
+    def __init__(self, words, blob_bytes, device):
+        self.words = words
+        self.blob_bytes = blob_bytes
+        self.dev = torch.from_numpy(words).to(device)
+
+    def host_ptr(self):
+        return ctypes.c_void_p(self.words.ctypes.data)
+
+
+def zoned_plan(v_bits, k_bits, C_new, d, device):
+    """v_bits int8 [B, Hkv, T_old] in {0,2,4,8,16}; k_bits int8 [B, Hkv, d] in
+    {2,4,8,16} (host arrays) -> ZonedPlan."""
+    v_bits = np.ascontiguousarray(np.asarray(v_bits, dtype=np.int8))
+    k_bits = np.ascontiguousarray(np.asarray(k_bits, dtype=np.int8))
+    B, H, T = v_bits.shape
+    n = lib.zoned_plan_words(B, H, T, d)
+    if n == 0:
+        raise DqaError("zoned_plan_words", 2)
+    words = np.zeros(n, dtype=np.int32)
+    blob = ctypes.c_size_t(0)
+    _check("zoned_plan", lib.zoned_plan(ctypes.c_void_p(v_bits.ctypes.data),
+                                        ctypes.c_void_p(k_bits.ctypes.data), B, H, T, C_new, d,
+                                        ctypes.c_void_p(words.ctypes.data), n, ctypes.byref(blob)))
+    return ZonedPlan(words, blob.value, device)
+
+
+def zoned_pack(plan, k, v, k_new=None, v_new=None):
+    """Pack fp16 caches into a uint8 blob of plan.blob_bytes bytes."""
+    k, v = _dev16(k, "k"), _dev16(v, "v")
+    k_new = None if k_new is None else _dev16(k_new, "k_new")
+    v_new = None if v_new is None else _dev16(v_new, "v_new")
+    blob = torch.empty(plan.blob_bytes, dtype=torch.uint8, device=k.device)
+    _check("zoned_pack", lib.zoned_pack(plan.host_ptr(), _ptr(plan.dev), _ptr(k), _ptr(v),
+                                        _ptr(k_new), _ptr(v_new), _ptr(blob), _stream(k.device)))
+    return blob
+
+
+def decode_attention_zoned(q, plan, blob, sm_scale, out=None, workspace=None):
+    q = _dev16(q, "q")
+    Hq = q.shape[1]
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    if workspace is None:
+        n = lib.decode_attention_zoned_workspace_bytes(plan.host_ptr(), Hq)
+        workspace = torch.zeros(max(n, 1), dtype=torch.uint8, device=q.device)
+    _check("decode_attention_zoned",
+           lib.decode_attention_zoned(_ptr(q), Hq, plan.host_ptr(), _ptr(plan.dev), _ptr(blob),
+                                      float(sm_scale), _ptr(workspace), workspace.numel(),
+                                      _ptr(out), _stream(q.device)))
+    return out
+
+
+# ---------------------------------------------------------------- RVQ
+
+def rvq_encode(x, codebooks, workspace=None):
+    """x fp16 [n, d]; codebooks fp16 [N, Kc, d] -> idx int16 [n, N]."""
+    x, codebooks = _dev16(x, "x"), _dev16(codebooks, "codebooks")
+    n, d = x.shape
+    N, Kc, _ = codebooks.shape
+    idx = torch.empty((n, N), dtype=torch.int16, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(max(lib.rvq_encode_workspace_bytes(N, Kc), 1), dtype=torch.uint8,
+                                device=x.device)
+    _check("rvq_encode", lib.rvq_encode(_ptr(x), n, d, _ptr(codebooks), N, Kc, _ptr(idx),
+                                        _ptr(workspace), workspace.numel(), _stream(x.device)))
+    return idx
+
+
+def rvq_decode_attention(q, k_idx, v_idx, k_codebooks, v_codebooks, sm_scale, out=None,
+                         workspace=None):
+    """q fp16 [B, Hq, d]; k_idx/v_idx int16 [B, Hkv, T, N]; codebooks fp16
+    [N, Kc, d] -> fp32 [B, Hq, d]."""
+    q = _dev16(q, "q")
+    B, Hq, d = q.shape
+    _, Hkv, T, N = k_idx.shape
+    Kc = k_codebooks.shape[1]
+    k_idx, v_idx = k_idx.contiguous(), v_idx.contiguous()
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    if workspace is None:
+        n = lib.rvq_decode_attention_workspace_bytes(B, Hq, Hkv, T, d)
+        workspace = torch.zeros(max(n, 1), dtype=torch.uint8, device=q.device)
+    _check("rvq_decode_attention",
+           lib.rvq_decode_attention(_ptr(q), B, Hq, Hkv, T, d, _ptr(k_idx), _ptr(v_idx),
+                                    _ptr(_dev16(k_codebooks, "k_codebooks")),
+                                    _ptr(_dev16(v_codebooks, "v_codebooks")), N, Kc,
+                                    float(sm_scale), _ptr(workspace), workspace.numel(),
+                                    _ptr(out), _stream(q.device)))
+    return out
+
+
+def stream_copy(src, dst):
+    """Plain device copy of src.numel()*element_size bytes into dst."""
+    nbytes = src.numel() * src.element_size()
+    _check("dqa_stream_copy", lib.dqa_stream_copy(_ptr(src), _ptr(dst), nbytes,
+                                                  _stream(src.device)))

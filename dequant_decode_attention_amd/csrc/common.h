@@ -1,0 +1,78 @@
+// Shared device/host helpers of the dqattn library (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/dqattn.h"
+
+namespace dqa {
+
+constexpr int kGroup = 32;       // quantization group length ([P1 para 1])
+constexpr int kWave = 64;        // CDNA wavefront width
+constexpr int kMaxRecent = 128;  // residual-buffer bound ([P1 para 8])
+
+// Launch geometry target: enough workgroups to give every one of the 256
+// compute units several resident workgroups.  Fixed (not queried) so that
+// workspace sizes depend on the shape only.
+constexpr int kTargetWorkgroups = 1024;
+
+#define DQA_CHECK_LAUNCH()                               \
+  do {                                                   \
+    if (hipPeekAtLastError() != hipSuccess) return DQA_ERR_HIP; \
+  } while (0)
+
+__device__ __forceinline__ float h2f(uint16_t bits) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, bits));
+}
+
+__device__ __forceinline__ uint16_t f2h(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
+}
+
+// Butterfly exchange inside a quad / half-row with DPP (no LDS traffic).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                         0xF, 0xF, false));
+}
+constexpr int kDppQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;   // row_half_mirror (lane i <-> 7-i in 8)
+constexpr int kDppRowMirror = 0x140;    // row_mirror (lane i <-> 15-i in 16)
+
+// Sum over N adjacent lanes (N in {1, 2, 4, 8, 16}); every lane of the
+// aligned N-lane block receives the block sum.
+template <int N>
+__device__ __forceinline__ float sum_adjacent(float v) {
+  if constexpr (N >= 2) v += dpp<kDppQuadXor1>(v);
+  if constexpr (N >= 4) v += dpp<kDppQuadXor2>(v);
+  if constexpr (N >= 8) v += dpp<kDppHalfMirror>(v);
+  if constexpr (N >= 16) v += dpp<kDppRowMirror>(v);
+  return v;
+}
+
+// Wave-wide reduction over lanes with stride S (S a power of two): every
+// lane ends with the reduction over its residue class lane % S.
+template <int S>
+__device__ __forceinline__ float max_strided(float v) {
+#pragma unroll
+  for (int m = S; m < kWave; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
+  return v;
+}
+template <int S>
+__device__ __forceinline__ float sum_strided(float v) {
+#pragma unroll
+  for (int m = S; m < kWave; m <<= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+
+// Merge weight of a partial softmax state with running max m (log2 domain)
+// into a combined max M; empty partials carry m = -inf.
+__device__ __forceinline__ float merge_weight(float m, float M) {
+  return (m == -INFINITY) ? 0.0f : exp2f(m - M);
+}
+
+}  // namespace dqa

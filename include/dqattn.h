@@ -1,0 +1,254 @@
+/*
+ * dqattn -- decode attention over a low-bit KV cache, for AMD MI355X (gfx950).
+ *
+ * The KV cache is held as low-bit integer codes (or residual-VQ indices) in
+ * HBM; each decode step reads the codes back and dequantizes them inside
+ * the attention kernel.  Method pages cited below:
+ *   [P1] ihal.it/?p=61653 -- article on KV-cache quantization axes (KIVI,
+ *        KVQuant, InnerQ); no headings, cited by paragraph number and topic.
+ *   [P2] "VQKV: High-Fidelity and High-Ratio Cache Compression via
+ *        Vector-Quantization", gist.science/it/paper/2603.16435.
+ *   [P3] "Riepilogo Tecnico: RDKV - Allocazione dei Bit per
+ *        Distorsione-Rate ...", gist.science/it/paper/2605.08317; its two
+ *        sections numbered 2.2 are cited by title ("bit-allocation
+ *        pipeline", "TriZone packed decoding").
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers marked (device) are device memory owned by the caller; the
+ *     library never allocates, frees or synchronizes.  Pointers marked
+ *     (host) are host memory read synchronously during the call.
+ *   - fp16 tensors travel as raw IEEE binary16 bit patterns (uint16_t).
+ *   - `stream` is a hipStream_t passed as void*; NULL is the default stream.
+ *     All device work is enqueued on it, in stream order.
+ *   - Every argument is validated on the host before any HIP call; a
+ *     non-zero return means nothing was enqueued and outputs are untouched.
+ *     DQA_ERR_HIP means a launch failed (the HIP error is left pending).
+ *     Device faults surface at the caller's next synchronization.
+ *   - Tensors are dense, row-major, in the layouts stated per argument.
+ *   - Thread safety: entry points are stateless and may be called from
+ *     several host threads; calls that share a workspace must be ordered by
+ *     the caller (same stream or events).
+ */
+#ifndef DQATTN_H
+#define DQATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point that returns int. */
+enum {
+  DQA_OK = 0,
+  DQA_ERR_NULL = 1,        /* a required pointer is NULL */
+  DQA_ERR_SHAPE = 2,       /* a size is out of range or inconsistent */
+  DQA_ERR_BITS = 3,        /* unsupported bit width */
+  DQA_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required */
+  DQA_ERR_UNSUPPORTED = 5, /* valid by the method but not built (e.g. head ratio) */
+  DQA_ERR_HIP = 6,         /* a HIP launch failed */
+  DQA_ERR_PLAN = 7         /* a zoned plan is malformed or does not match */
+};
+
+/* Human-readable name of a status code; never NULL. */
+const char* dqa_status_string(int status);
+
+/* Version of this interface (increments on any signature or layout change). */
+int dqa_abi_version(void);
+
+/* ------------------------------------------------------------------------
+ * Quantize + bit-pack  ([P1 para 1, 3, 4, 5])
+ *
+ * Asymmetric uniform quantization in groups of 32: the group's range
+ * [min, max] is split into 2^bits levels.  scale s = fp16_rne((max - min) /
+ * (2^bits - 1)) computed in IEEE fp32; zero z = min (fp16, exact); code
+ * q = clamp(rint_half_even((x - z) / s), 0, 2^bits - 1) with IEEE fp32
+ * subtraction and division against the stored fp16 s and z; a group with
+ * s == 0 gets all-zero codes.  Dequantized value: q * s + z.
+ *
+ * Packing: the codes of the [B][Hkv][T][d] tensor, in row-major order, form
+ * one little-endian bit stream; element f occupies bits [f*bits, f*bits +
+ * bits), i.e. uint32 word (f*bits)/32 at bit (f*bits)%32.
+ * ------------------------------------------------------------------------ */
+
+/* Keys grouped per channel over 32 consecutive tokens ([P1 para 4]); keys are
+ * quantized before RoPE ([P1 para 7]).
+ *   k      (device) fp16 [B][Hkv][T][d]
+ *   T      multiple of 32, >= 0;  d in {64, 128};  bits in {2, 4, 8}
+ *   codes  (device) uint32 [B*Hkv*T*d*bits/32]
+ *   scale, zero (device) fp16 [B][Hkv][T/32][d]
+ * Errors: DQA_ERR_NULL, DQA_ERR_SHAPE, DQA_ERR_BITS, DQA_ERR_HIP. */
+int quantize_pack_k(const uint16_t* k, int B, int Hkv, int T, int d, int bits,
+                    uint32_t* codes, uint16_t* scale, uint16_t* zero,
+                    void* stream);
+
+/* Values grouped per token over 32 consecutive channels ([P1 para 5]).
+ *   v      (device) fp16 [B][Hkv][T][d]; T >= 0; d in {64, 128}
+ *   codes  (device) uint32 [B*Hkv*T*d*bits/32]
+ *   scale, zero (device) fp16 [B][Hkv][T][d/32]
+ * Errors as quantize_pack_k. */
+int quantize_pack_v(const uint16_t* v, int B, int Hkv, int T, int d, int bits,
+                    uint32_t* codes, uint16_t* scale, uint16_t* zero,
+                    void* stream);
+
+/* ------------------------------------------------------------------------
+ * Decode attention over the uniform (KIVI) layout  ([P1 para 2, 6, 7, 8])
+ * ------------------------------------------------------------------------ */
+
+/* A quantized cache plus its fp16 recent zone.  All pointers (device). */
+typedef struct dqa_kivi_cache {
+  int B, Hq, Hkv;         /* batch, query heads, KV heads (Hq % Hkv == 0)       */
+  int d;                  /* head dim, 64 or 128                                */
+  int bits;               /* 2, 4 or 8                                          */
+  int T_q;                /* quantized tokens, multiple of 32, >= 0             */
+  int R;                  /* fp16 recent tokens, 0..128 ([P1 para 8])           */
+  float rope_theta;       /* > 0: rotate keys after dequantization (interleaved */
+                          /* pairs, omega_i = theta^(-2i/d)); <= 0: no RoPE     */
+  const uint32_t* k_codes;  /* quantize_pack_k layout, [B][Hkv][T_q][d]         */
+  const uint16_t* k_scale;  /* fp16 [B][Hkv][T_q/32][d]                         */
+  const uint16_t* k_zero;
+  const uint32_t* v_codes;  /* quantize_pack_v layout                           */
+  const uint16_t* v_scale;  /* fp16 [B][Hkv][T_q][d/32]                         */
+  const uint16_t* v_zero;
+  const uint16_t* k_recent; /* fp16 [B][Hkv][R][d], keys before RoPE            */
+  const uint16_t* v_recent; /* fp16 [B][Hkv][R][d]                              */
+} dqa_kivi_cache;
+
+/* Bytes of workspace decode_attention_qkv needs for this cache shape
+ * (0 if the shape is invalid).  The workspace holds per-split partial
+ * softmax states and one completion counter per (batch, KV head); its
+ * counter region must be zero before first use (e.g. allocate it zeroed)
+ * and every completed call leaves it zero again. */
+size_t decode_attention_workspace_bytes(const dqa_kivi_cache* cache);
+
+/* One decode step: out[b][h] = softmax(sm_scale * q[b][h] . K_hat^T) V_hat,
+ * over the dequantized quantized tokens (positions 0..T_q-1) followed by the
+ * recent tokens (positions T_q..T_q+R-1).  Query head h reads KV head
+ * h / (Hq/Hkv).  With rope_theta > 0 each key is rotated at its position
+ * after dequantization ([P1 para 7]); q must already be rotated.
+ *   q    (device) fp16 [B][Hq][d]
+ *   cache (host) pointer to the descriptor above
+ *   ws   (device) workspace of ws_bytes >= decode_attention_workspace_bytes
+ *   out  (device) fp32 [B][Hq][d]; zeros when T_q + R == 0
+ * Supported head ratios Hq/Hkv: 1, 2, 4 (else DQA_ERR_UNSUPPORTED).
+ * Errors: DQA_ERR_NULL, DQA_ERR_SHAPE, DQA_ERR_BITS, DQA_ERR_WORKSPACE,
+ * DQA_ERR_UNSUPPORTED, DQA_ERR_HIP. */
+int decode_attention_qkv(const uint16_t* q, const dqa_kivi_cache* cache,
+                         float sm_scale, void* ws, size_t ws_bytes, float* out,
+                         void* stream);
+
+/* ------------------------------------------------------------------------
+ * Mixed-bitwidth zoned cache  ([P3 sec 2.2, bit-allocation pipeline] and
+ * [P3 sec 2.2, TriZone packed decoding])
+ *
+ * Value width per (batch, KV head, token) in {0, 2, 4, 8, 16}; key width
+ * per (batch, KV head, channel) in {2, 4, 8, 16}.  Width 0 evicts the token
+ * (key and value).  Zone A: kept tokens grouped into segments by value
+ * width (2, 4, 8, 16), each cut into 32-slot groups (last one padded with
+ * masked slots); per group the key rows (channels grouped into width
+ * classes 2, 4, 8, 16; one scale/zero per (group, quantized channel); 16-bit
+ * channels raw fp16) and, for widths 2/4/8, the value rows quantized per
+ * token in 32-channel groups.  Zone B: fp16 value rows of 16-bit tokens.
+ * Zone C: fp16 keys and values of the C newest tokens.  The byte layout is
+ * fixed and documented with the oracle that reproduces it.
+ * ------------------------------------------------------------------------ */
+
+/* int32 words a plan needs for these sizes (0 if invalid). */
+size_t zoned_plan_words(int B, int Hkv, int T_old, int d);
+
+/* Build the plan on the host from the width maps.
+ *   v_bits (host) int8 [B][Hkv][T_old], values in {0,2,4,8,16}
+ *   k_bits (host) int8 [B][Hkv][d], values in {2,4,8,16}
+ *   C_new  new fp16 tokens per unit, 0..256;  d in {64, 128}
+ *   plan   (host) int32 [plan_words], plan_words >= zoned_plan_words(...)
+ *   blob_bytes (host) receives the size of the packed blob
+ * The plan is self-describing; the caller copies the same words to device
+ * memory for zoned_pack / decode_attention_zoned.
+ * Errors: DQA_ERR_NULL, DQA_ERR_SHAPE, DQA_ERR_BITS (a width outside its
+ * set), DQA_ERR_WORKSPACE (plan_words too small). */
+int zoned_plan(const int8_t* v_bits, const int8_t* k_bits, int B, int Hkv,
+               int T_old, int C_new, int d, int32_t* plan, size_t plan_words,
+               size_t* blob_bytes);
+
+/* Pack the cache into the blob described by the plan.
+ *   plan_host (host) and plan_dev (device): the same words from zoned_plan
+ *   k, v      (device) fp16 [B][Hkv][T_old][d]
+ *   k_new, v_new (device) fp16 [B][Hkv][C_new][d] (may be NULL if C_new == 0)
+ *   blob      (device) blob_bytes bytes (every byte is written)
+ * Errors: DQA_ERR_NULL, DQA_ERR_PLAN, DQA_ERR_HIP. */
+int zoned_pack(const int32_t* plan_host, const int32_t* plan_dev,
+               const uint16_t* k, const uint16_t* v, const uint16_t* k_new,
+               const uint16_t* v_new, void* blob, void* stream);
+
+/* Workspace bytes for decode_attention_zoned (0 if invalid); same counter
+ * convention as decode_attention_workspace_bytes. */
+size_t decode_attention_zoned_workspace_bytes(const int32_t* plan_host, int Hq);
+
+/* Decode attention over zones A (kept tokens, masked slots skipped), B and
+ * C, with dequantization fused into the products.
+ *   q (device) fp16 [B][Hq][d], Hq a multiple of Hkv (ratio as above)
+ *   out (device) fp32 [B][Hq][d]
+ * Errors: DQA_ERR_NULL, DQA_ERR_PLAN, DQA_ERR_SHAPE, DQA_ERR_WORKSPACE,
+ * DQA_ERR_UNSUPPORTED, DQA_ERR_HIP. */
+int decode_attention_zoned(const uint16_t* q, int Hq, const int32_t* plan_host,
+                           const int32_t* plan_dev, const void* blob,
+                           float sm_scale, void* ws, size_t ws_bytes,
+                           float* out, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Residual vector quantization  ([P2 sec 2, key components])
+ *
+ * Stage s picks the codeword of codebook s nearest (squared Euclidean) to
+ * the running fp32 residual, lowest index on exact ties, then subtracts it.
+ * Distances are formed on the matrix cores as |c|^2 - 2 r.c with r split
+ * into two fp16 halves and fp32 accumulation, so two codewords whose exact
+ * distances differ by less than that arithmetic's error bound may come out
+ * in either order.
+ * ------------------------------------------------------------------------ */
+
+/* Workspace bytes for rvq_encode (codeword norms). */
+size_t rvq_encode_workspace_bytes(int N, int Kc);
+
+/* Encode n vectors.
+ *   x         (device) fp16 [n][d], d == 128
+ *   codebooks (device) fp16 [N][Kc][d], 1 <= N <= 8, 16 <= Kc <= 32768, Kc % 16 == 0
+ *   idx       (device) int16 [n][N]
+ *   ws        (device) >= rvq_encode_workspace_bytes(N, Kc)
+ * Errors: DQA_ERR_NULL, DQA_ERR_SHAPE, DQA_ERR_WORKSPACE, DQA_ERR_HIP. */
+int rvq_encode(const uint16_t* x, int64_t n, int d, const uint16_t* codebooks,
+               int N, int Kc, int16_t* idx, void* ws, size_t ws_bytes,
+               void* stream);
+
+/* Workspace bytes for rvq_decode_attention (same counter convention as
+ * decode_attention_workspace_bytes). */
+size_t rvq_decode_attention_workspace_bytes(int B, int Hq, int Hkv, int T, int d);
+
+/* Decode attention with keys and values rebuilt on the fly from their
+ * indices ([P2 sec 2, decoding phase]): k_hat = sum_s Ck_s[k_idx[s]],
+ * v_hat likewise, summed in fp32 in stage order.
+ *   q (device) fp16 [B][Hq][d]; k_idx, v_idx (device) int16 [B][Hkv][T][N]
+ *   k_codebooks, v_codebooks (device) fp16 [N][Kc][d]
+ *   out (device) fp32 [B][Hq][d]
+ * Errors: DQA_ERR_NULL, DQA_ERR_SHAPE, DQA_ERR_WORKSPACE,
+ * DQA_ERR_UNSUPPORTED, DQA_ERR_HIP. */
+int rvq_decode_attention(const uint16_t* q, int B, int Hq, int Hkv, int T,
+                         int d, const int16_t* k_idx, const int16_t* v_idx,
+                         const uint16_t* k_codebooks,
+                         const uint16_t* v_codebooks, int N, int Kc,
+                         float sm_scale, void* ws, size_t ws_bytes, float* out,
+                         void* stream);
+
+/* ------------------------------------------------------------------------
+ * Measurement helper (not part of the method): a plain streaming copy used
+ * to calibrate bandwidth counters and to measure the achievable HBM rate.
+ *   src, dst (device), bytes a multiple of 16, both 16-byte aligned.
+ * Errors: DQA_ERR_NULL, DQA_ERR_SHAPE, DQA_ERR_HIP.
+ * ------------------------------------------------------------------------ */
+int dqa_stream_copy(const void* src, void* dst, size_t bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DQATTN_H */

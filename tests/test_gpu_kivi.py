@@ -1,0 +1,151 @@
+"""GPU parity of the uniform-layout path against the oracle: quantize +
+pack bit-exact, decode attention within relative L2 1e-3 of the oracle's
+fp64 attention over its own dequantized cache."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import say, dev, host, rel_l2, worst_row_rel, oracle_cache, gpu_cache
+from workloads import kivi_inputs, CONFIGS
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-3
+
+
+@pytest.fixture(scope="module")
+def dqa():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    import dequant_decode_attention_amd as m
+    return m
+
+
+def _special_k(rng, B, H, T, d):
+    """Keys with constant groups, outlier channels, tiny ranges, ties."""
+    k = rng.standard_normal((B, H, T, d)).astype(np.float32)
+    k[..., 5] *= 50.0
+    k[:, :, :32, 7] = 3.25                       # constant key group
+    k[:, :, 32:64, 9] = 1000.0 + rng.integers(0, 4, size=(B, H, 32)) * 0.5   # few levels
+    k[..., 11] *= 1e-3                           # tiny range
+    k[:, :, :, 13] = np.round(k[:, :, :, 13] * 2) / 2   # values on half-integers
+    return k.astype(np.float16)
+
+
+SHAPES = [(1, 1, 256, 64, 2), (2, 3, 96, 128, 2), (2, 3, 96, 128, 4), (2, 3, 96, 128, 8),
+          (1, 2, 64, 64, 4), (3, 1, 32, 128, 8), (1, 1, 0, 128, 2)]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_quantize_pack_bit_exact(dqa, shape):
+    B, H, T, d, bits = shape
+    rng = np.random.default_rng(hash(shape) % 2 ** 32)
+    k = _special_k(rng, B, H, T, d)
+    v = k.transpose(0, 1, 2, 3).copy()
+    v[..., :32] = rng.standard_normal((B, H, T, 32)).astype(np.float16)
+    v[:, :, :3, 32:64] = -2.5                    # constant value groups
+    say("quantize_pack_k/v", shape)
+    gk = dqa.quantize_pack_k(dev(k), bits)
+    gv = dqa.quantize_pack_v(dev(v), bits)
+    torch.cuda.synchronize()
+    kc, ks, kz = oracle.quantize_k(k, bits)
+    vc, vs, vz = oracle.quantize_v(v, bits)
+    np.testing.assert_array_equal(host(gk[0]).view(np.uint32), oracle.pack_codes(kc, bits))
+    np.testing.assert_array_equal(host(gk[1]).view(np.uint16), ks.view(np.uint16))
+    np.testing.assert_array_equal(host(gk[2]).view(np.uint16), kz.view(np.uint16))
+    np.testing.assert_array_equal(host(gv[0]).view(np.uint32), oracle.pack_codes(vc, bits))
+    np.testing.assert_array_equal(host(gv[1]).view(np.uint16), vs.view(np.uint16))
+    np.testing.assert_array_equal(host(gv[2]).view(np.uint16), vz.view(np.uint16))
+
+
+@pytest.mark.parametrize("name", ["c2", "c3"])
+def test_quantize_full_config_sampled_units(dqa, name):
+    """Full-size quantization on the GPU; the oracle re-quantizes sampled
+    (batch, KV head) units and compares them bit for bit."""
+    cfg = CONFIGS[name]
+    inp = kivi_inputs(cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["d"], cfg["T_q"], 0,
+                      seed=int(name[1:]), outliers=cfg["outliers"])
+    for bits in cfg["bits"]:
+        say("quantize full", name, bits)
+        gk = dqa.quantize_pack_k(dev(inp["k"]), bits)
+        gv = dqa.quantize_pack_v(dev(inp["v"]), bits)
+        torch.cuda.synchronize()
+        rng = np.random.default_rng(0)
+        for _ in range(3):
+            b, h = int(rng.integers(cfg["B"])), int(rng.integers(cfg["Hkv"]))
+            kc, ks, kz = oracle.quantize_k(inp["k"][b:b + 1, h:h + 1], bits)
+            vc, vs, vz = oracle.quantize_v(inp["v"][b:b + 1, h:h + 1], bits)
+            np.testing.assert_array_equal(host(gk[0][b, h]).view(np.uint32), oracle.pack_codes(kc, bits)[0, 0])
+            np.testing.assert_array_equal(host(gk[1][b, h]).view(np.uint16), ks[0, 0].view(np.uint16))
+            np.testing.assert_array_equal(host(gk[2][b, h]).view(np.uint16), kz[0, 0].view(np.uint16))
+            np.testing.assert_array_equal(host(gv[0][b, h]).view(np.uint32), oracle.pack_codes(vc, bits)[0, 0])
+            np.testing.assert_array_equal(host(gv[1][b, h]).view(np.uint16), vs[0, 0].view(np.uint16))
+            np.testing.assert_array_equal(host(gv[2][b, h]).view(np.uint16), vz[0, 0].view(np.uint16))
+
+
+DECODE_CASES = [
+    # B, Hq, Hkv, d, T_q, R, bits, rope
+    (1, 1, 1, 64, 256, 0, 2, 0.0),          # c1 shape
+    (2, 8, 2, 128, 320, 37, 2, 500000.0),   # GQA 4, ragged recent zone, RoPE
+    (2, 8, 2, 128, 320, 37, 4, 500000.0),
+    (1, 4, 4, 128, 128, 128, 8, 10000.0),   # MHA, full recent zone
+    (2, 4, 2, 64, 96, 5, 2, 500000.0),      # d 64, G 2
+    (1, 4, 1, 64, 64, 0, 4, 0.0),           # d 64, G 4
+    (3, 2, 2, 128, 32, 1, 2, 0.0),          # single tile + one recent token
+    (1, 4, 1, 128, 0, 100, 2, 500000.0),    # only recent tokens
+    (1, 4, 1, 128, 4096, 0, 2, 500000.0),   # many tiles -> many splits
+    (2, 2, 1, 128, 0, 0, 2, 0.0),           # empty cache -> zeros
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_decode_attention_parity(dqa, case):
+    B, Hq, Hkv, d, T_q, R, bits, rope = case
+    inp = kivi_inputs(B, Hq, Hkv, d, T_q, R, seed=T_q + R + d,
+                      outliers=("lognormal", 0.04, 3.0, 1.0))
+    scale = 1.0 / math.sqrt(d)
+    ref = oracle.kivi_decode_attention(inp["q"], oracle_cache(inp, bits, Hq, rope), scale)
+    say("decode_attention_qkv", case)
+    cache = gpu_cache(dqa, inp, bits, Hq, rope)
+    out = dqa.decode_attention_qkv(dev(inp["q"]), cache, scale)
+    torch.cuda.synchronize()
+    got = host(out)
+    if T_q + R == 0:
+        assert np.all(got == 0)
+        return
+    err = rel_l2(got, ref)
+    print(f"rel_l2={err:.3e} worst_row={worst_row_rel(got, ref):.3e}", flush=True)
+    assert err <= TOL
+    # a second call reuses the workspace (its counters were reset) and is
+    # bit-identical: the split merge runs in a fixed order
+    out2 = dqa.decode_attention_qkv(dev(inp["q"]), cache, scale)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(out2), got)
+
+
+@pytest.mark.parametrize("name,bits", [("c3", 2), ("c3", 4), ("c2", 2), ("c1", 2)])
+def test_decode_full_config_sampled_rows(dqa, name, bits):
+    """Full-size decode in the launch configuration the bench times; the
+    oracle computes sampled output rows one by one."""
+    cfg = CONFIGS[name]
+    inp = kivi_inputs(cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["d"], cfg["T_q"], cfg["R"],
+                      seed=int(name[1:]), outliers=cfg["outliers"])
+    scale = 1.0 / math.sqrt(cfg["d"])
+    say("decode full", name, bits)
+    cache = gpu_cache(dqa, inp, bits, cfg["Hq"], cfg["rope_theta"])
+    out = host(dqa.decode_attention_qkv(dev(inp["q"]), cache, scale))
+    rng = np.random.default_rng(1)
+    rows = sorted({(int(rng.integers(cfg["B"])), int(rng.integers(cfg["Hq"]))) for _ in range(6)})
+    # the oracle quantizes only the units it needs
+    units = sorted({(b, h // (cfg["Hq"] // cfg["Hkv"])) for b, h in rows})
+    for b, u in units:
+        sub = {k: v[b:b + 1, u:u + 1] for k, v in inp.items() if k != "q"}
+        G = cfg["Hq"] // cfg["Hkv"]
+        sub["q"] = inp["q"][b:b + 1, u * G:(u + 1) * G]
+        ref = oracle.kivi_decode_attention(sub["q"], oracle_cache(sub, bits, G, cfg["rope_theta"]), scale)
+        got = out[b, u * G:(u + 1) * G][None]
+        err = rel_l2(got, ref)
+        print(f"{name} bits={bits} unit=({b},{u}) rel_l2={err:.3e}", flush=True)
+        assert err <= TOL
