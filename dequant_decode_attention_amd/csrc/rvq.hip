@@ -1,10 +1,524 @@
-// Residual VQ encoder and decode attention (in progress).
+// Residual vector quantization: nearest-codeword encoder on the matrix cores,
+// and decode attention that rebuilds keys/values from their indices.
+//
+// [P2 sec 2, key components]: a cache vector is matched to the nearest entry
+// of a codebook, the residual (vector minus that entry) goes to the next
+// codebook, N times; only the N indices are kept (prefill phase); at decode
+// time the vectors are rebuilt on demand inside attention.  [P2 sec 2,
+// computational optimization]: quantization is parallelized over blocks of
+// cache vectors.
+//
+// Encoder (the one dense contraction of the path): for a block of 256
+// vectors and one stage, the keys |c|^2 - 2 r.c of all Kc codewords are a
+// [256 x 128] x [128 x Kc] product.  It runs on v_mfma_f32_16x16x32_f16:
+// the residual r (fp32) is split as -2r = hi + lo with hi = fp16(-2r) and
+// lo = fp16(-2r - hi) (exact products with fp16 codewords, fp32
+// accumulation; stage 0 has lo = 0 exactly and skips it), the accumulator
+// starts at |c|^2.  Codebook tiles of 64 codewords are staged in LDS, double
+// buffered, shared by the 8 waves of the workgroup.  Each lane keeps a
+// running (key, index) minimum for its output rows (strict < over
+// increasing codeword index, then a lexicographic cross-lane reduction), so
+// exact ties go to the lowest index.  The residual stays in registers in the
+// MFMA A-operand layout and is updated in fp32 after each stage.
 #include "common.h"
 
-extern "C" size_t rvq_encode_workspace_bytes(int, int) { return 0; }
-extern "C" int rvq_encode(const uint16_t*, int64_t, int, const uint16_t*, int, int, int16_t*, void*,
-                          size_t, void*) { return DQA_ERR_UNSUPPORTED; }
-extern "C" size_t rvq_decode_attention_workspace_bytes(int, int, int, int, int) { return 0; }
-extern "C" int rvq_decode_attention(const uint16_t*, int, int, int, int, int, const int16_t*,
-                                    const int16_t*, const uint16_t*, const uint16_t*, int, int, float,
-                                    void*, size_t, float*, void*) { return DQA_ERR_UNSUPPORTED; }
+namespace dqa {
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+
+constexpr int kD = 128;
+constexpr int kEncRows = 256;        // vectors per workgroup
+constexpr int kEncWaves = 8;         // 32 rows (2 MFMA row blocks) per wave
+constexpr int kTileCW = 64;          // codewords per LDS tile
+constexpr int kRowPad = kD + 8;      // LDS row stride in halves (bank spread)
+
+__global__ __launch_bounds__(256) void rvq_norms_kernel(const uint16_t* __restrict__ cb, size_t n_cw,
+                                                        float* __restrict__ norms) {
+  const size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= n_cw) return;
+  const uint16_t* c = cb + i * kD;
+  float s = 0.0f;
+  for (int k = 0; k < kD; ++k) {
+    const float v = h2f(c[k]);
+    s = fmaf(v, v, s);
+  }
+  norms[i] = s;
+}
+
+__device__ __forceinline__ void split_neg2(const float* r, half8& hi, half8& lo) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float t = -2.0f * r[j];
+    const _Float16 h = static_cast<_Float16>(t);
+    hi[j] = h;
+    lo[j] = static_cast<_Float16>(t - static_cast<float>(h));
+  }
+}
+
+__global__ __launch_bounds__(512) void rvq_encode_kernel(const uint16_t* __restrict__ x, int64_t n,
+                                                         const uint16_t* __restrict__ cbs,
+                                                         const float* __restrict__ norms, int N,
+                                                         int Kc, int16_t* __restrict__ idx_out) {
+  __shared__ __attribute__((aligned(16))) _Float16 lds_cb[2][kTileCW][kRowPad];
+  __shared__ float lds_norm[2][kTileCW];
+  __shared__ int lds_idx[kEncWaves][32];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int64_t row_base = static_cast<int64_t>(blockIdx.x) * kEncRows + wave * 32;
+
+  // residual in A-operand layout: row = row_base + 16*mb + col, channels
+  // 32*ks + 8*grp + 0..7
+  float res[2][4][8];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    const int64_t row = row_base + 16 * mb + col;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      if (row < n) {
+        const uint4 u = *reinterpret_cast<const uint4*>(x + row * kD + 32 * ks + 8 * grp);
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          res[mb][ks][2 * j] = h2f(static_cast<uint16_t>(w[j] & 0xFFFFu));
+          res[mb][ks][2 * j + 1] = h2f(static_cast<uint16_t>(w[j] >> 16));
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) res[mb][ks][j] = 0.0f;
+      }
+    }
+  }
+
+  const int n_tiles = Kc / kTileCW;
+  for (int s = 0; s < N; ++s) {
+    const uint16_t* cb = cbs + static_cast<size_t>(s) * Kc * kD;
+    const float* nrm = norms + static_cast<size_t>(s) * Kc;
+    half8 ahi[2][4], alo[2][4];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) split_neg2(res[mb][ks], ahi[mb][ks], alo[mb][ks]);
+    float bestk[2][4];
+    int besti[2][4];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        bestk[mb][r] = INFINITY;
+        besti[mb][r] = 0;
+      }
+
+    // tile 0 -> LDS buffer 0
+    uint4 pre[2];
+    auto gload = [&](int t) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int c = tid * 2 + q;                 // 16-byte chunk of the tile
+        pre[q] = *reinterpret_cast<const uint4*>(cb + (static_cast<size_t>(t) * kTileCW + c / 16) * kD + (c % 16) * 8);
+      }
+    };
+    auto lstore = [&](int buf, int t) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int c = tid * 2 + q;
+        *reinterpret_cast<uint4*>(&lds_cb[buf][c / 16][(c % 16) * 8]) = pre[q];
+      }
+      if (tid < kTileCW) lds_norm[buf][tid] = nrm[t * kTileCW + tid];
+    };
+    gload(0);
+    lstore(0, 0);
+    __syncthreads();
+    for (int t = 0; t < n_tiles; ++t) {
+      const int buf = t & 1;
+      if (t + 1 < n_tiles) gload(t + 1);
+      float4v acc[2][4];
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const float nv = lds_norm[buf][16 * nb + col];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) acc[mb][nb] = float4v{nv, nv, nv, nv};
+      }
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          const half8 bf = *reinterpret_cast<const half8*>(&lds_cb[buf][16 * nb + col][32 * ks + 8 * grp]);
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[mb][ks], bf, acc[mb][nb], 0, 0, 0);
+          if (s > 0) {
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+              acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[mb][ks], bf, acc[mb][nb], 0, 0, 0);
+          }
+        }
+      }
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const int cw = t * kTileCW + 16 * nb + col;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float key = acc[mb][nb][r];
+            if (key < bestk[mb][r]) {
+              bestk[mb][r] = key;
+              besti[mb][r] = cw;
+            }
+          }
+      }
+      if (t + 1 < n_tiles) lstore(buf ^ 1, t + 1);
+      __syncthreads();
+    }
+
+    // lexicographic (key, index) minimum across the 16 lanes of a row group
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float k = bestk[mb][r];
+        int i = besti[mb][r];
+#pragma unroll
+        for (int m = 1; m < 16; m <<= 1) {
+          const float ko = __shfl_xor(k, m, 64);
+          const int io = __shfl_xor(i, m, 64);
+          if (ko < k || (ko == k && io < i)) {
+            k = ko;
+            i = io;
+          }
+        }
+        besti[mb][r] = i;
+      }
+    if (col == 0) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int local = 16 * mb + 4 * grp + r;
+          lds_idx[wave][local] = besti[mb][r];
+          const int64_t row = row_base + local;
+          if (row < n) idx_out[row * N + s] = static_cast<int16_t>(besti[mb][r]);
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // residual update in fp32: r <- r - C_s[idx]
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const int ci = lds_idx[wave][16 * mb + col];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const uint4 u = *reinterpret_cast<const uint4*>(cb + static_cast<size_t>(ci) * kD + 32 * ks + 8 * grp);
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          res[mb][ks][2 * j] -= h2f(static_cast<uint16_t>(w[j] & 0xFFFFu));
+          res[mb][ks][2 * j + 1] -= h2f(static_cast<uint16_t>(w[j] >> 16));
+        }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+// ------------------------------------------------------------------ decode
+
+constexpr int kDecWaves = 4;
+
+struct RvqDecArgs {
+  const uint16_t* q;
+  const int16_t* k_idx;
+  const int16_t* v_idx;
+  const uint16_t* k_cb;
+  const uint16_t* v_cb;
+  float* out;
+  float* partials;
+  unsigned* tickets;
+  int Hq, Hkv, T, N, Kc, n_tiles, tiles_per_split, splits;
+  float q_scale;
+};
+
+// Sum over stages of the lane's 16 channels of the indexed codewords (fp32,
+// stage order).
+__device__ __forceinline__ void rebuild16(const uint16_t* cb, const int16_t* idx, int N, int Kc,
+                                          int c0, float* out) {
+#pragma unroll
+  for (int c = 0; c < 16; ++c) out[c] = 0.0f;
+  for (int s = 0; s < N; ++s) {
+    // indices are in [0, Kc) when produced by rvq_encode; clamp so that a
+    // corrupt index cannot read outside the codebook
+    const uint32_t ci = min(static_cast<uint32_t>(static_cast<uint16_t>(idx[s])), static_cast<uint32_t>(Kc - 1));
+    const uint16_t* row = cb + (static_cast<size_t>(s) * Kc + ci) * kD + c0;
+    const uint4 a = reinterpret_cast<const uint4*>(row)[0];
+    const uint4 b = reinterpret_cast<const uint4*>(row)[1];
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      out[2 * i] += h2f(static_cast<uint16_t>(w[i] & 0xFFFFu));
+      out[2 * i + 1] += h2f(static_cast<uint16_t>(w[i] >> 16));
+    }
+  }
+}
+
+// Lane = (token j of 8, 16-channel chunk ck of 8); 32-token tiles; online
+// softmax per tile; the same ticketed split merge as the uniform decoder.
+template <int G>
+__global__ __launch_bounds__(256) void rvq_decode_kernel(RvqDecArgs a) {
+  constexpr int NCK = 8, TL = 8, IT = 4;
+  __shared__ float lds_m[kDecWaves][G], lds_l[kDecWaves][G], lds_o[kDecWaves][G][kD];
+  __shared__ int lds_last;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int j = lane / NCK, ck = lane % NCK, c0 = 16 * ck;
+  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const size_t unit = static_cast<size_t>(b) * a.Hkv + kvh;
+  float qr[G][16];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const uint16_t* qp = a.q + (static_cast<size_t>(b) * a.Hq + kvh * G + h) * kD + c0;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) qr[h][c] = h2f(qp[c]) * a.q_scale;
+  }
+  float m[G], l[G], acc[G][16];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m[h] = -INFINITY;
+    l[h] = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) acc[h][c] = 0.0f;
+  }
+  const int tb = split * a.tiles_per_split;
+  const int te = min(a.n_tiles, tb + a.tiles_per_split);
+  for (int ti = tb + wave; ti < te; ti += kDecWaves) {
+    float lg[IT][G];
+    bool valid[IT];
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int t = ti * kGroup + it * TL + j;
+      valid[it] = t < a.T;
+      float kh[16];
+      if (valid[it]) {
+        rebuild16(a.k_cb, a.k_idx + (unit * a.T + t) * a.N, a.N, a.Kc, c0, kh);
+      } else {
+#pragma unroll
+        for (int c = 0; c < 16; ++c) kh[c] = 0.0f;
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float s = 0.0f;
+#pragma unroll
+        for (int c = 0; c < 16; ++c) s = fmaf(qr[h][c], kh[c], s);
+        lg[it][h] = sum_adjacent<NCK>(s);
+      }
+    }
+    bool grow = false;
+    float mnew[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float t = -INFINITY;
+#pragma unroll
+      for (int it = 0; it < IT; ++it) t = valid[it] ? fmaxf(t, lg[it][h]) : t;
+      t = max_strided<NCK>(t);
+      mnew[h] = fmaxf(m[h], t);
+      grow |= mnew[h] > m[h];
+    }
+    if (grow) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float sc = merge_weight(m[h], mnew[h]);
+        l[h] *= sc;
+#pragma unroll
+        for (int c = 0; c < 16; ++c) acc[h][c] *= sc;
+        m[h] = mnew[h];
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      if (!valid[it]) continue;
+      const int t = ti * kGroup + it * TL + j;
+      float vh[16];
+      rebuild16(a.v_cb, a.v_idx + (unit * a.T + t) * a.N, a.N, a.Kc, c0, vh);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float p = exp2f(lg[it][h] - m[h]);
+        l[h] += p;
+#pragma unroll
+        for (int c = 0; c < 16; ++c) acc[h][c] = fmaf(p, vh[c], acc[h][c]);
+      }
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    l[h] = sum_strided<NCK>(l[h]);
+#pragma unroll
+    for (int c = 0; c < 16; ++c) acc[h][c] = sum_strided<NCK>(acc[h][c]);
+  }
+  if (j == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int c = 0; c < 16; ++c) lds_o[wave][h][c0 + c] = acc[h][c];
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      lds_m[wave][h] = m[h];
+      lds_l[wave][h] = l[h];
+    }
+  }
+  __syncthreads();
+  float* part = a.partials + (unit * a.splits + split) * G * (kD + 2);
+  for (int e = threadIdx.x; e < G * kD; e += blockDim.x) {
+    const int h = e / kD, c = e % kD;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, lds_m[w][h]);
+    float L = 0.0f, O = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) {
+      const float wt = merge_weight(lds_m[w][h], M);
+      L = fmaf(lds_l[w][h], wt, L);
+      O = fmaf(lds_o[w][h][c], wt, O);
+    }
+    if (a.splits == 1) {
+      a.out[(static_cast<size_t>(b) * a.Hq + kvh * G + h) * kD + c] = (L > 0.0f) ? O / L : 0.0f;
+    } else {
+      if (c == 0) {
+        part[h * (kD + 2)] = M;
+        part[h * (kD + 2) + 1] = L;
+      }
+      part[h * (kD + 2) + 2 + c] = O;
+    }
+  }
+  if (a.splits == 1) return;
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned prev = atomicAdd(a.tickets + unit, 1u);
+    lds_last = (prev == static_cast<unsigned>(a.splits - 1));
+  }
+  __syncthreads();
+  if (!lds_last) return;
+  __threadfence();
+  const float* parts = a.partials + unit * a.splits * G * (kD + 2);
+  for (int e = threadIdx.x; e < G * kD; e += blockDim.x) {
+    const int h = e / kD, c = e % kD;
+    float M = -INFINITY;
+    for (int s = 0; s < a.splits; ++s) M = fmaxf(M, parts[(s * G + h) * (kD + 2)]);
+    float L = 0.0f, O = 0.0f;
+    for (int s = 0; s < a.splits; ++s) {
+      const float* ps = parts + (s * G + h) * (kD + 2);
+      const float wt = merge_weight(ps[0], M);
+      L = fmaf(ps[1], wt, L);
+      O = fmaf(ps[2 + c], wt, O);
+    }
+    a.out[(static_cast<size_t>(b) * a.Hq + kvh * G + h) * kD + c] = (L > 0.0f) ? O / L : 0.0f;
+  }
+  if (threadIdx.x == 0) a.tickets[unit] = 0u;
+}
+
+struct RvqGeometry {
+  int G, n_tiles, tps, splits;
+  size_t units, ticket_bytes, ws_bytes;
+};
+
+int rvq_geometry(int B, int Hq, int Hkv, int T, int d, RvqGeometry* g) {
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || T < 0 || Hq % Hkv != 0) return DQA_ERR_SHAPE;
+  if (d != kD) return DQA_ERR_SHAPE;
+  if (B > 65535 || Hkv > 65535) return DQA_ERR_SHAPE;
+  g->G = Hq / Hkv;
+  if (g->G < 1 || g->G > 4) return DQA_ERR_UNSUPPORTED;
+  g->units = static_cast<size_t>(B) * Hkv;
+  g->n_tiles = (T + kGroup - 1) / kGroup;
+  long long s = (kTargetWorkgroups + static_cast<long long>(g->units) - 1) /
+                static_cast<long long>(g->units > 0 ? g->units : 1);
+  if (s > g->n_tiles) s = g->n_tiles;
+  if (s < 1) s = 1;
+  g->tps = g->n_tiles > 0 ? static_cast<int>((g->n_tiles + s - 1) / s) : 1;
+  g->splits = g->n_tiles > 0 ? (g->n_tiles + g->tps - 1) / g->tps : 1;
+  g->ticket_bytes = (g->units * 4 + 255) / 256 * 256;
+  g->ws_bytes = g->ticket_bytes + g->units * g->splits * g->G * (kD + 2) * sizeof(float);
+  return DQA_OK;
+}
+
+}  // namespace
+}  // namespace dqa
+
+using namespace dqa;
+
+extern "C" size_t rvq_encode_workspace_bytes(int N, int Kc) {
+  if (N < 1 || N > 8 || Kc < kTileCW || Kc > 32768 || Kc % kTileCW != 0) return 0;
+  return static_cast<size_t>(N) * Kc * sizeof(float);
+}
+
+extern "C" int rvq_encode(const uint16_t* x, int64_t n, int d, const uint16_t* codebooks, int N,
+                          int Kc, int16_t* idx, void* ws, size_t ws_bytes, void* stream) {
+  if (n < 0 || d != kD) return DQA_ERR_SHAPE;
+  if (N < 1 || N > 8 || Kc < kTileCW || Kc > 32768 || Kc % kTileCW != 0) return DQA_ERR_SHAPE;
+  if (n == 0) return DQA_OK;
+  if (!x || !codebooks || !idx) return DQA_ERR_NULL;
+  if (!ws || ws_bytes < rvq_encode_workspace_bytes(N, Kc)) return DQA_ERR_WORKSPACE;
+  const int64_t blocks = (n + kEncRows - 1) / kEncRows;
+  if (blocks > 0x7FFFFFFF) return DQA_ERR_SHAPE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* norms = static_cast<float*>(ws);
+  const size_t n_cw = static_cast<size_t>(N) * Kc;
+  hipLaunchKernelGGL(rvq_norms_kernel, dim3(static_cast<unsigned>((n_cw + 255) / 256)), dim3(256), 0, s,
+                     codebooks, n_cw, norms);
+  DQA_CHECK_LAUNCH();
+  hipLaunchKernelGGL(rvq_encode_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kEncWaves * 64), 0, s,
+                     x, n, codebooks, norms, N, Kc, idx);
+  DQA_CHECK_LAUNCH();
+  return DQA_OK;
+}
+
+extern "C" size_t rvq_decode_attention_workspace_bytes(int B, int Hq, int Hkv, int T, int d) {
+  RvqGeometry g;
+  if (rvq_geometry(B, Hq, Hkv, T, d, &g) != DQA_OK) return 0;
+  return g.ws_bytes;
+}
+
+extern "C" int rvq_decode_attention(const uint16_t* q, int B, int Hq, int Hkv, int T, int d,
+                                    const int16_t* k_idx, const int16_t* v_idx, const uint16_t* k_cb,
+                                    const uint16_t* v_cb, int N, int Kc, float sm_scale, void* ws,
+                                    size_t ws_bytes, float* out, void* stream) {
+  RvqGeometry g;
+  int st = rvq_geometry(B, Hq, Hkv, T, d, &g);
+  if (st != DQA_OK) return st;
+  if (N < 1 || N > 8 || Kc < 1 || Kc > 32768) return DQA_ERR_SHAPE;
+  if (g.units == 0) return DQA_OK;
+  if (!q || !out) return DQA_ERR_NULL;
+  if (T > 0 && (!k_idx || !v_idx || !k_cb || !v_cb)) return DQA_ERR_NULL;
+  if (!ws || ws_bytes < g.ws_bytes) return DQA_ERR_WORKSPACE;
+  RvqDecArgs a;
+  a.q = q;
+  a.k_idx = k_idx;
+  a.v_idx = v_idx;
+  a.k_cb = k_cb;
+  a.v_cb = v_cb;
+  a.out = out;
+  a.tickets = static_cast<unsigned*>(ws);
+  a.partials = reinterpret_cast<float*>(static_cast<char*>(ws) + g.ticket_bytes);
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.T = T;
+  a.N = N;
+  a.Kc = Kc;
+  a.n_tiles = g.n_tiles;
+  a.tiles_per_split = g.tps;
+  a.splits = g.splits;
+  a.q_scale = sm_scale * 1.4426950408889634f;
+  const dim3 grid(g.splits, Hkv, B);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (g.G) {
+    case 1: hipLaunchKernelGGL(rvq_decode_kernel<1>, grid, dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL(rvq_decode_kernel<2>, grid, dim3(256), 0, s, a); break;
+    case 3: hipLaunchKernelGGL(rvq_decode_kernel<3>, grid, dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL(rvq_decode_kernel<4>, grid, dim3(256), 0, s, a); break;
+    default: return DQA_ERR_UNSUPPORTED;
+  }
+  DQA_CHECK_LAUNCH();
+  return DQA_OK;
+}

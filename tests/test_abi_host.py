@@ -92,3 +92,89 @@ def test_stream_copy_validation():
     assert lib.dqa_stream_copy(FAKE, None, 64, None) == 1
     assert lib.dqa_stream_copy(FAKE, FAKE, 20, None) == 2
     assert lib.dqa_stream_copy(ctypes.c_void_p(0x1008), FAKE, 64, None) == 2
+
+
+def _plan(vb, kb, C, d):
+    vb = np.ascontiguousarray(vb, np.int8)
+    kb = np.ascontiguousarray(kb, np.int8)
+    B, H, T = vb.shape
+    n = lib.zoned_plan_words(B, H, T, d)
+    words = np.zeros(n, np.int32)
+    blob = ctypes.c_size_t(0)
+    st = lib.zoned_plan(ctypes.c_void_p(vb.ctypes.data), ctypes.c_void_p(kb.ctypes.data), B, H, T,
+                        C, d, ctypes.c_void_p(words.ctypes.data), n, ctypes.byref(blob))
+    return st, words, blob.value
+
+
+@pytest.mark.parametrize("seed,T,C,d", [(0, 500, 64, 128), (1, 77, 0, 64), (2, 1, 3, 128), (3, 0, 5, 64)])
+def test_zoned_plan_matches_oracle_layout(seed, T, C, d):
+    """The host planner (C++) and the oracle's layout agree on the blob size
+    (and hence on every segment/zone size) for random width maps."""
+    import oracle
+    rng = np.random.default_rng(seed)
+    B, H = 2, 3
+    vb = rng.choice([0, 2, 4, 8, 16], size=(B, H, T), p=[.5, .2, .15, .1, .05]).astype(np.int8)
+    kb = rng.choice([2, 4, 8, 16], size=(B, H, d), p=[.4, .3, .2, .1]).astype(np.int8)
+    st, words, blob = _plan(vb, kb, C, d)
+    assert st == 0
+    _, total = oracle.zoned_layout(vb, kb, d, C)
+    assert blob == total
+    ws = lib.decode_attention_zoned_workspace_bytes(ctypes.c_void_p(words.ctypes.data), 4 * H)
+    assert ws > 0
+
+
+def test_zoned_plan_validation():
+    vb = np.full((1, 1, 64), 2, np.int8)
+    kb = np.full((1, 1, 128), 4, np.int8)
+    assert _plan(vb, kb, 0, 128)[0] == 0
+    bad_v = vb.copy()
+    bad_v[0, 0, 5] = 3
+    assert _plan(bad_v, kb, 0, 128)[0] == 3
+    bad_k = kb.copy()
+    bad_k[0, 0, 1] = 0              # keys have no width 0
+    assert _plan(vb, bad_k, 0, 128)[0] == 3
+    assert _plan(vb, kb, 300, 128)[0] == 2                  # C too large
+    assert lib.zoned_plan_words(1, 1, 64, 96) == 0
+    n = lib.zoned_plan_words(1, 1, 64, 128)
+    words = np.zeros(n, np.int32)
+    blob = ctypes.c_size_t(0)
+    assert lib.zoned_plan(ctypes.c_void_p(vb.ctypes.data), ctypes.c_void_p(kb.ctypes.data), 1, 1,
+                          64, 0, 128, ctypes.c_void_p(words.ctypes.data), n - 1,
+                          ctypes.byref(blob)) == 4
+    # a corrupted plan is refused by the device entry points before any launch
+    st, words, blob = _plan(vb, kb, 0, 128)
+    words[0] ^= 1
+    assert lib.zoned_pack(ctypes.c_void_p(words.ctypes.data), FAKE, FAKE, FAKE, None, None, FAKE,
+                          None) == 7
+    assert lib.decode_attention_zoned(FAKE, 4, ctypes.c_void_p(words.ctypes.data), FAKE, FAKE,
+                                      0.1, FAKE, 1 << 20, FAKE, None) == 7
+    st, words, blob = _plan(vb, kb, 0, 128)
+    assert lib.decode_attention_zoned(FAKE, 3, ctypes.c_void_p(words.ctypes.data), FAKE, FAKE,
+                                      0.1, FAKE, 1 << 20, FAKE, None) == 5   # ratio 3 not built
+    assert lib.decode_attention_zoned(FAKE, 4, ctypes.c_void_p(words.ctypes.data), FAKE, FAKE,
+                                      0.1, FAKE, 16, FAKE, None) == 4
+
+
+def test_rvq_validation_and_workspace():
+    assert lib.rvq_encode_workspace_bytes(4, 1024) == 4 * 1024 * 4
+    assert lib.rvq_encode_workspace_bytes(9, 1024) == 0
+    assert lib.rvq_encode_workspace_bytes(4, 1000) == 0          # Kc % 64
+    ws = 1 << 20
+    assert lib.rvq_encode(FAKE, 10, 64, FAKE, 4, 1024, FAKE, FAKE, ws, None) == 2   # d
+    assert lib.rvq_encode(FAKE, 10, 128, FAKE, 0, 1024, FAKE, FAKE, ws, None) == 2  # N
+    assert lib.rvq_encode(FAKE, 10, 128, FAKE, 4, 32, FAKE, FAKE, ws, None) == 2    # Kc
+    assert lib.rvq_encode(None, 10, 128, FAKE, 4, 1024, FAKE, FAKE, ws, None) == 1
+    assert lib.rvq_encode(FAKE, 10, 128, FAKE, 4, 1024, FAKE, FAKE, 100, None) == 4
+    assert lib.rvq_encode(None, 0, 128, None, 4, 1024, None, None, 0, None) == 0    # empty
+    w = lib.rvq_decode_attention_workspace_bytes(2, 24, 8, 8192, 128)
+    assert w > 0
+    assert lib.rvq_decode_attention_workspace_bytes(2, 24, 8, 8192, 64) == 0
+    assert lib.rvq_decode_attention_workspace_bytes(2, 40, 8, 8192, 128) == 5 - 5   # ratio 5
+    args = lambda **k: [k.get(n, v) for n, v in [
+        ("q", FAKE), ("B", 2), ("Hq", 24), ("Hkv", 8), ("T", 100), ("d", 128), ("ki", FAKE),
+        ("vi", FAKE), ("kc", FAKE), ("vc", FAKE), ("N", 4), ("Kc", 1024), ("sc", 0.1),
+        ("ws", FAKE), ("wsb", w), ("out", FAKE), ("st", None)]]
+    assert lib.rvq_decode_attention(*args(Hq=40)) == 5
+    assert lib.rvq_decode_attention(*args(N=9)) == 2
+    assert lib.rvq_decode_attention(*args(ki=None)) == 1
+    assert lib.rvq_decode_attention(*args(wsb=16)) == 4

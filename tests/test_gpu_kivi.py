@@ -28,7 +28,8 @@ def _special_k(rng, B, H, T, d):
     k = rng.standard_normal((B, H, T, d)).astype(np.float32)
     k[..., 5] *= 50.0
     k[:, :, :32, 7] = 3.25                       # constant key group
-    k[:, :, 32:64, 9] = 1000.0 + rng.integers(0, 4, size=(B, H, 32)) * 0.5   # few levels
+    if T >= 64:                                  # a group with few distinct levels
+        k[:, :, 32:64, 9] = 1000.0 + rng.integers(0, 4, size=(B, H, 32)) * 0.5
     k[..., 11] *= 1e-3                           # tiny range
     k[:, :, :, 13] = np.round(k[:, :, :, 13] * 2) / 2   # values on half-integers
     return k.astype(np.float16)
