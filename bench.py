@@ -57,7 +57,7 @@ def cpu_baseline(inp, cfg, bits, scale, budget_s=12.0):
         vc, vs, vz = oracle.quantize_v(sub["v"], bits)
         cache = dict(B=1, Hq=G, Hkv=1, d=cfg["d"], bits=bits, T_q=cfg["T_q"], R=cfg["R"],
                      rope_theta=cfg["rope_theta"], k_codes=oracle.pack_codes(kc, bits),
-                     v_codes=oracle.pack_codes(vc, bits), k_scale=ks, k_zero=kz,
+                     v_codes=oracle.pack_v_codes(vc, bits), k_scale=ks, k_zero=kz,
                      v_scale=vs, v_zero=vz, k_recent=sub["k_recent"], v_recent=sub["v_recent"])
         q = inp["q"][b:b + 1, h * G:(h + 1) * G]
         t0 = time.perf_counter()

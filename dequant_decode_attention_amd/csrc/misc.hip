@@ -33,7 +33,7 @@ extern "C" const char* dqa_status_string(int status) {
   }
 }
 
-extern "C" int dqa_abi_version(void) { return 1; }
+extern "C" int dqa_abi_version(void) { return 2; }
 
 extern "C" int dqa_stream_copy(const void* src, void* dst, size_t bytes, void* stream) {
   if (bytes == 0) return DQA_OK;

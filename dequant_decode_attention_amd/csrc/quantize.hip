@@ -84,15 +84,24 @@ __global__ __launch_bounds__(D) void quantize_k_kernel(
   }
 }
 
-// Values: one thread per (token, 32-channel group); it reads the group's 64
-// contiguous bytes, reduces min/max in registers and writes `bits` words.
-__global__ __launch_bounds__(256) void quantize_v_kernel(
-    const uint16_t* __restrict__ v, size_t n_groups, int bits,
+// Values: one workgroup per (32-token block, KV head, batch); thread
+// (token t, 32-channel group g) reduces its group's min/max in registers and
+// stages its codes in LDS; the block is then written channel-major (for each
+// channel, the 32 tokens' codes in token order), the layout in which the
+// decode kernel's matrix-core operands read 8 consecutive tokens of one
+// channel.
+template <int D>
+__global__ __launch_bounds__(D) void quantize_v_kernel(
+    const uint16_t* __restrict__ v, int T, int Hkv, int bits,
     uint32_t* __restrict__ codes, uint16_t* __restrict__ scale,
     uint16_t* __restrict__ zero) {
-  const size_t gidx = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (gidx >= n_groups) return;
-  const uint4* src = reinterpret_cast<const uint4*>(v + gidx * kGroup);
+  __shared__ __attribute__((aligned(16))) uint8_t lds_codes[D][kGroup];   // [channel][token]
+  const int tid = threadIdx.x;
+  const int t = tid % kGroup, g = tid / kGroup;
+  const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const size_t unit = static_cast<size_t>(b) * Hkv + h;
+  const size_t tok = unit * T + static_cast<size_t>(blk) * kGroup + t;
+  const uint4* src = reinterpret_cast<const uint4*>(v + tok * D + g * kGroup);
   float x[kGroup];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -111,14 +120,19 @@ __global__ __launch_bounds__(256) void quantize_v_kernel(
     mx = fmaxf(mx, x[i]);
   }
   const GroupParams p = group_params(mn, mx, bits);
-  scale[gidx] = p.s16;
-  zero[gidx] = p.z16;
+  scale[tok * (D / kGroup) + g] = p.s16;
+  zero[tok * (D / kGroup) + g] = p.z16;
+#pragma unroll
+  for (int i = 0; i < kGroup; ++i) lds_codes[g * kGroup + i][t] = static_cast<uint8_t>(quant_code(x[i], p));
+  __syncthreads();
+  // channel-major block: stream index c*32 + t, `per_word` codes per word
   const int per_word = 32 / bits;
-  uint32_t* dst = codes + gidx * bits;
-  for (int w = 0; w < bits; ++w) {
+  uint32_t* dst = codes + (unit * (T / kGroup) + blk) * static_cast<size_t>(D * bits);
+  for (int w = tid; w < D * bits; w += D) {
+    const int f0 = w * per_word;
+    const int c = f0 / kGroup, t0 = f0 % kGroup;
     uint32_t word = 0;
-#pragma unroll 8
-    for (int j = 0; j < per_word; ++j) word |= quant_code(x[w * per_word + j], p) << (j * bits);
+    for (int j = 0; j < per_word; ++j) word |= static_cast<uint32_t>(lds_codes[c][t0 + j]) << (j * bits);
     dst[w] = word;
   }
 }
@@ -162,12 +176,15 @@ extern "C" int quantize_pack_v(const uint16_t* v, int B, int Hkv, int T, int d,
                                uint16_t* zero, void* stream) {
   int st = check_common(v, B, Hkv, T, d, bits, codes, scale, zero);
   if (st != DQA_OK) return st;
-  const size_t n_groups = static_cast<size_t>(B) * Hkv * T * (d / kGroup);
-  if (n_groups == 0) return DQA_OK;
-  const size_t blocks = (n_groups + 255) / 256;
-  if (blocks > 0x7FFFFFFFu) return DQA_ERR_SHAPE;
-  hipLaunchKernelGGL(quantize_v_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
-                     static_cast<hipStream_t>(stream), v, n_groups, bits, codes, scale, zero);
+  if (T % kGroup != 0) return DQA_ERR_SHAPE;
+  if (static_cast<long long>(B) * Hkv * T == 0) return DQA_OK;
+  if (B > 65535 || Hkv > 65535) return DQA_ERR_SHAPE;
+  dim3 grid(T / kGroup, Hkv, B);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (d == 128)
+    hipLaunchKernelGGL(quantize_v_kernel<128>, grid, dim3(128), 0, s, v, T, Hkv, bits, codes, scale, zero);
+  else
+    hipLaunchKernelGGL(quantize_v_kernel<64>, grid, dim3(64), 0, s, v, T, Hkv, bits, codes, scale, zero);
   DQA_CHECK_LAUNCH();
   return DQA_OK;
 }

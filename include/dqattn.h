@@ -55,7 +55,7 @@ enum {
 const char* dqa_status_string(int status);
 
 /* Version of this interface (increments on any signature or layout change). */
-int dqa_abi_version(void);
+int dqa_abi_version(void);  /* 2: values packed channel-major per 32 tokens */
 
 /* ------------------------------------------------------------------------
  * Quantize + bit-pack  ([P1 para 1, 3, 4, 5])
@@ -67,9 +67,11 @@ int dqa_abi_version(void);
  * subtraction and division against the stored fp16 s and z; a group with
  * s == 0 gets all-zero codes.  Dequantized value: q * s + z.
  *
- * Packing: the codes of the [B][Hkv][T][d] tensor, in row-major order, form
- * one little-endian bit stream; element f occupies bits [f*bits, f*bits +
- * bits), i.e. uint32 word (f*bits)/32 at bit (f*bits)%32.
+ * Packing: codes form little-endian bit streams; stream element f occupies
+ * bits [f*bits, f*bits + bits), i.e. uint32 word (f*bits)/32 at bit
+ * (f*bits)%32.  Keys: the [B][Hkv][T][d] tensor in row-major order (element
+ * (t, c) of a unit at t*d + c).  Values: blocks of 32 tokens, channel-major
+ * inside a block (element (t, c) of a unit at (t/32)*32*d + c*32 + t%32).
  * ------------------------------------------------------------------------ */
 
 /* Keys grouped per channel over 32 consecutive tokens ([P1 para 4]); keys are
@@ -84,7 +86,7 @@ int quantize_pack_k(const uint16_t* k, int B, int Hkv, int T, int d, int bits,
                     void* stream);
 
 /* Values grouped per token over 32 consecutive channels ([P1 para 5]).
- *   v      (device) fp16 [B][Hkv][T][d]; T >= 0; d in {64, 128}
+ *   v      (device) fp16 [B][Hkv][T][d]; T multiple of 32, >= 0; d in {64, 128}
  *   codes  (device) uint32 [B*Hkv*T*d*bits/32]
  *   scale, zero (device) fp16 [B][Hkv][T][d/32]
  * Errors as quantize_pack_k. */
@@ -108,7 +110,7 @@ typedef struct dqa_kivi_cache {
   const uint32_t* k_codes;  /* quantize_pack_k layout, [B][Hkv][T_q][d]         */
   const uint16_t* k_scale;  /* fp16 [B][Hkv][T_q/32][d]                         */
   const uint16_t* k_zero;
-  const uint32_t* v_codes;  /* quantize_pack_v layout                           */
+  const uint32_t* v_codes;  /* quantize_pack_v layout (32-token channel-major)  */
   const uint16_t* v_scale;  /* fp16 [B][Hkv][T_q][d/32]                         */
   const uint16_t* v_zero;
   const uint16_t* k_recent; /* fp16 [B][Hkv][R][d], keys before RoPE            */

@@ -43,6 +43,8 @@ from .quant import (
     dequantize_v,
     pack_codes,
     unpack_codes,
+    pack_v_codes,
+    unpack_v_codes,
 )
 from .attention import (
     rope_frequencies,
@@ -65,7 +67,7 @@ from .rvq import (
 
 __all__ = [
     "GROUP", "quantize_groups", "quantize_k", "quantize_v", "dequantize_k",
-    "dequantize_v", "pack_codes", "unpack_codes", "rope_frequencies",
+    "dequantize_v", "pack_codes", "unpack_codes", "pack_v_codes", "unpack_v_codes", "rope_frequencies",
     "rope_rotate", "attention_fp64", "kivi_decode_attention", "WIDTHS",
     "zoned_layout", "zoned_pack", "zoned_decode_attention", "rvq_encode",
     "rvq_reconstruct", "rvq_decode_attention", "rvq_stage_distances",

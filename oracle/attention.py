@@ -24,7 +24,7 @@ at T_q..T_q+R-1; the query arrives already rotated.
 
 import numpy as np
 
-from .quant import GROUP, unpack_codes, dequantize_k, dequantize_v
+from .quant import GROUP, unpack_codes, unpack_v_codes, dequantize_k, dequantize_v
 
 
 def rope_frequencies(d, theta):
@@ -79,7 +79,7 @@ def _dequant_unit(cache, b, h):
     parts_k, parts_v = [], []
     if T_q > 0:
         kc = unpack_codes(cache["k_codes"][b, h], bits, d)[None, None]
-        vc = unpack_codes(cache["v_codes"][b, h], bits, d)[None, None]
+        vc = unpack_v_codes(cache["v_codes"][b, h], bits, d)[None, None]
         parts_k.append(dequantize_k(kc, cache["k_scale"][b, h][None, None],
                                     cache["k_zero"][b, h][None, None])[0, 0])
         parts_v.append(dequantize_v(vc, cache["v_scale"][b, h][None, None],
@@ -98,8 +98,10 @@ def kivi_decode_attention(q16, cache, sm_scale, rows=None):
 
     q16   : float16 [B, Hq, d] (already rotated when RoPE is on)
     cache : dict with keys B, Hq, Hkv, d, bits, T_q, R, rope_theta (<= 0: no
-            RoPE), k_codes/v_codes (packed uint32 words [B, Hkv, T_q,
-            d*bits/32]), k_scale/k_zero (fp16 [B, Hkv, T_q/32, d]),
+            RoPE), k_codes (packed uint32 words [B, Hkv, T_q, d*bits/32],
+            token-major), v_codes (uint32 [B, Hkv, T_q/32, d*bits], 32-token
+            blocks stored channel-major), k_scale/k_zero (fp16 [B, Hkv,
+            T_q/32, d]),
             v_scale/v_zero (fp16 [B, Hkv, T_q, d/32]), k_recent/v_recent
             (fp16 [B, Hkv, R, d], keys before RoPE).
     rows  : optional iterable of (b, hq) pairs; only those output rows are

@@ -22,10 +22,12 @@ Readings fixed here (the pages give no formula):
   and division, rint = round half to even.  A group whose stored scale is 0
   (constant group) gets all-zero codes.
 * dequantized value  x_hat = q * s + z.
-* packing: the codes of a tensor, in row-major element order, form one
-  little-endian bit stream; element f occupies bits [f*b, f*b + b), i.e.
-  word f*b // 32, bit (f*b) % 32.  32 is a multiple of every supported width
-  so no code straddles a word.
+* packing: a sequence of codes forms one little-endian bit stream; element
+  f occupies bits [f*b, f*b + b), i.e. word f*b // 32, bit (f*b) % 32.  32 is
+  a multiple of every supported width so no code straddles a word.  Keys
+  are packed in row-major [token][channel] order.  Values are packed in
+  blocks of 32 tokens, channel-major inside a block: block k holds, for
+  channel 0, 1, ..., d-1 in turn, the codes of tokens 32k..32k+31.
 """
 
 import numpy as np
@@ -134,6 +136,27 @@ def pack_codes(codes, bits):
         words |= flat[:, j] << np.uint64(j * bits)
     out_shape = codes.shape[:-1] + (codes.shape[-1] * bits // 32,)
     return words.astype(np.uint32).reshape(out_shape)
+
+
+def pack_v_codes(codes, bits):
+    """Value codes [B, H, T, d] (T a multiple of 32) -> words [B, H, T/32,
+    d*bits]: each 32-token block is stored channel-major (for each channel,
+    its 32 tokens' codes in token order), as one bit stream."""
+    codes = np.asarray(codes)
+    B, H, T, d = codes.shape
+    assert T % GROUP == 0
+    blocks = codes.reshape(B, H, T // GROUP, GROUP, d).transpose(0, 1, 2, 4, 3)
+    return pack_codes(blocks.reshape(B, H, T // GROUP, d * GROUP), bits)
+
+
+def unpack_v_codes(words, bits, d):
+    """Inverse of :func:`pack_v_codes`: words [..., T/32, d*bits] -> codes
+    [..., T, d]."""
+    words = np.asarray(words, dtype=np.uint32)
+    lead = words.shape[:-2]
+    nb = words.shape[-2]
+    c = unpack_codes(words, bits, d * GROUP).reshape(lead + (nb, d, GROUP))
+    return np.swapaxes(c, -1, -2).reshape(lead + (nb * GROUP, d))
 
 
 def unpack_codes(words, bits, last_dim):

@@ -46,7 +46,7 @@ def oracle_cache(inp, bits, Hq, rope_theta):
     kc, ks, kz = oracle.quantize_k(inp["k"], bits)
     vc, vs, vz = oracle.quantize_v(inp["v"], bits)
     return dict(B=B, Hq=Hq, Hkv=Hkv, d=d, bits=bits, T_q=T_q, R=R, rope_theta=rope_theta,
-                k_codes=oracle.pack_codes(kc, bits), v_codes=oracle.pack_codes(vc, bits),
+                k_codes=oracle.pack_codes(kc, bits), v_codes=oracle.pack_v_codes(vc, bits),
                 k_scale=ks, k_zero=kz, v_scale=vs, v_zero=vz,
                 k_recent=inp["k_recent"], v_recent=inp["v_recent"])
 

@@ -56,7 +56,7 @@ def test_quantize_pack_bit_exact(dqa, shape):
     np.testing.assert_array_equal(host(gk[0]).view(np.uint32), oracle.pack_codes(kc, bits))
     np.testing.assert_array_equal(host(gk[1]).view(np.uint16), ks.view(np.uint16))
     np.testing.assert_array_equal(host(gk[2]).view(np.uint16), kz.view(np.uint16))
-    np.testing.assert_array_equal(host(gv[0]).view(np.uint32), oracle.pack_codes(vc, bits))
+    np.testing.assert_array_equal(host(gv[0]).view(np.uint32), oracle.pack_v_codes(vc, bits).reshape(host(gv[0]).shape))
     np.testing.assert_array_equal(host(gv[1]).view(np.uint16), vs.view(np.uint16))
     np.testing.assert_array_equal(host(gv[2]).view(np.uint16), vz.view(np.uint16))
 
@@ -81,7 +81,7 @@ def test_quantize_full_config_sampled_units(dqa, name):
             np.testing.assert_array_equal(host(gk[0][b, h]).view(np.uint32), oracle.pack_codes(kc, bits)[0, 0])
             np.testing.assert_array_equal(host(gk[1][b, h]).view(np.uint16), ks[0, 0].view(np.uint16))
             np.testing.assert_array_equal(host(gk[2][b, h]).view(np.uint16), kz[0, 0].view(np.uint16))
-            np.testing.assert_array_equal(host(gv[0][b, h]).view(np.uint32), oracle.pack_codes(vc, bits)[0, 0])
+            np.testing.assert_array_equal(host(gv[0][b, h]).view(np.uint32), oracle.pack_v_codes(vc, bits)[0, 0].reshape(host(gv[0][b, h]).shape))
             np.testing.assert_array_equal(host(gv[1][b, h]).view(np.uint16), vs[0, 0].view(np.uint16))
             np.testing.assert_array_equal(host(gv[2][b, h]).view(np.uint16), vz[0, 0].view(np.uint16))
 

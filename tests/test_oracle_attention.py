@@ -108,7 +108,7 @@ def _cache_from(inp, bits, rope, Hq=None):
     vc, vs, vz = oracle.quantize_v(inp["v"], bits)
     return dict(B=B, Hq=Hq or inp["q"].shape[1], Hkv=Hkv, d=d, bits=bits, T_q=T_q,
                 R=R, rope_theta=rope, k_codes=oracle.pack_codes(kc, bits),
-                v_codes=oracle.pack_codes(vc, bits), k_scale=ks, k_zero=kz,
+                v_codes=oracle.pack_v_codes(vc, bits), k_scale=ks, k_zero=kz,
                 v_scale=vs, v_zero=vz, k_recent=inp["k_recent"], v_recent=inp["v_recent"])
 
 

@@ -179,3 +179,36 @@ def test_pack_bit_positions_brute_force(bits):
     for f, c in enumerate(codes.reshape(-1).tolist()):
         assert (stream >> (f * bits)) & (2 ** bits - 1) == c
     np.testing.assert_array_equal(unpack_codes(words, bits, 64), codes)
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_value_pack_block_order_brute_force(bits):
+    """Value codes: 32-token blocks, channel-major inside a block, one bit
+    stream; element (t, c) of a unit sits at stream index
+    (t // 32) * 32 * d + c * 32 + t % 32."""
+    rng = np.random.default_rng(7)
+    d, T = 64, 96
+    codes = rng.integers(0, 2 ** bits, size=(2, 1, T, d), dtype=np.uint8)
+    words = oracle.pack_v_codes(codes, bits)
+    assert words.shape == (2, 1, T // 32, d * bits)
+    for b in range(2):
+        stream = 0
+        for i, w in enumerate(words[b, 0].reshape(-1).tolist()):
+            stream |= int(w) << (32 * i)
+        for t in range(T):
+            for c in range(d):
+                f = (t // 32) * 32 * d + c * 32 + t % 32
+                assert (stream >> (f * bits)) & (2 ** bits - 1) == codes[b, 0, t, c]
+    np.testing.assert_array_equal(oracle.unpack_v_codes(words, bits, d), codes)
+
+
+def test_value_pack_hand_word():
+    # 2-bit, one 32-token block, d = 32: channel 0's tokens 0..15 fill word
+    # 0; token 1 of channel 0 has code 3 -> bits 2..3 -> 0x0000000C; token 16
+    # of channel 1 (stream index 32 + 16 = 48 -> word 3, bits 0..1) has code 1
+    codes = np.zeros((1, 1, 32, 32), np.uint8)
+    codes[0, 0, 1, 0] = 3
+    codes[0, 0, 16, 1] = 1
+    words = oracle.pack_v_codes(codes, 2)[0, 0, 0]
+    assert words[0] == 0x0000000C and words[3] == 0x00000001
+    assert np.count_nonzero(words) == 2

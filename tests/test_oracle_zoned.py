@@ -74,7 +74,7 @@ def test_single_width_equals_uniform_layout():
     kc, ks, kz = oracle.quantize_k(inp["k"], 2)
     vc, vs, vz = oracle.quantize_v(inp["v"], 2)
     cache = dict(B=1, Hq=4, Hkv=2, d=64, bits=2, T_q=192, R=0, rope_theta=0.0,
-                 k_codes=oracle.pack_codes(kc, 2), v_codes=oracle.pack_codes(vc, 2),
+                 k_codes=oracle.pack_codes(kc, 2), v_codes=oracle.pack_v_codes(vc, 2),
                  k_scale=ks, k_zero=kz, v_scale=vs, v_zero=vz,
                  k_recent=np.zeros((1, 2, 0, 64), np.float16), v_recent=np.zeros((1, 2, 0, 64), np.float16))
     ref = oracle.kivi_decode_attention(inp["q"], cache, 0.125)
