@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libdqattn.so")
 DQA_OK = 0
 _STATUS = {0: "DQA_OK", 1: "DQA_ERR_NULL", 2: "DQA_ERR_SHAPE", 3: "DQA_ERR_BITS",
            4: "DQA_ERR_WORKSPACE", 5: "DQA_ERR_UNSUPPORTED", 6: "DQA_ERR_HIP",
-           7: "DQA_ERR_PLAN"}
+           7: "DQA_ERR_PLAN", 8: "DQA_ERR_ALIGN"}
 
 
 class DqaError(RuntimeError):
@@ -155,11 +155,11 @@ class KiviCache:
         return lib.decode_attention_workspace_bytes(ctypes.byref(self.struct()))
 
     def workspace(self, device):
-        """A zero-initialized workspace, cached on the cache object (the
-        library leaves its counters zero after each call)."""
+        """A workspace of the required size, cached on the cache object
+        (it needs no initialization)."""
         n = self.workspace_bytes()
         if self._ws is None or self._ws.numel() < n or self._ws.device != device:
-            self._ws = torch.zeros(max(n, 1), dtype=torch.uint8, device=device)
+            self._ws = torch.empty(max(n, 256), dtype=torch.uint8, device=device)
         return self._ws
 
 

@@ -29,11 +29,12 @@ extern "C" const char* dqa_status_string(int status) {
     case DQA_ERR_UNSUPPORTED: return "DQA_ERR_UNSUPPORTED: configuration not built";
     case DQA_ERR_HIP: return "DQA_ERR_HIP: a HIP launch failed";
     case DQA_ERR_PLAN: return "DQA_ERR_PLAN: zoned plan malformed or mismatched";
+    case DQA_ERR_ALIGN: return "DQA_ERR_ALIGN: a device pointer is not 16-byte aligned";
     default: return "DQA_ERR_UNKNOWN";
   }
 }
 
-extern "C" int dqa_abi_version(void) { return 2; }
+extern "C" int dqa_abi_version(void) { return 3; }
 
 extern "C" int dqa_stream_copy(const void* src, void* dst, size_t bytes, void* stream) {
   if (bytes == 0) return DQA_OK;

@@ -48,14 +48,15 @@ enum {
   DQA_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required */
   DQA_ERR_UNSUPPORTED = 5, /* valid by the method but not built (e.g. head ratio) */
   DQA_ERR_HIP = 6,         /* a HIP launch failed */
-  DQA_ERR_PLAN = 7         /* a zoned plan is malformed or does not match */
+  DQA_ERR_PLAN = 7,        /* a zoned plan is malformed or does not match */
+  DQA_ERR_ALIGN = 8        /* a device pointer is not 16-byte aligned */
 };
 
 /* Human-readable name of a status code; never NULL. */
 const char* dqa_status_string(int status);
 
 /* Version of this interface (increments on any signature or layout change). */
-int dqa_abi_version(void);  /* 2: values packed channel-major per 32 tokens */
+int dqa_abi_version(void);  /* 3: 16-byte pointer alignment checked (DQA_ERR_ALIGN) */
 
 /* ------------------------------------------------------------------------
  * Quantize + bit-pack  ([P1 para 1, 3, 4, 5])
@@ -118,10 +119,10 @@ typedef struct dqa_kivi_cache {
 } dqa_kivi_cache;
 
 /* Bytes of workspace decode_attention_qkv needs for this cache shape
- * (0 if the shape is invalid).  The workspace holds per-split partial
- * softmax states and one completion counter per (batch, KV head); its
- * counter region must be zero before first use (e.g. allocate it zeroed)
- * and every completed call leaves it zero again. */
+ * (0 if the shape is invalid; at least 256 otherwise).  The workspace holds
+ * the per-split partial softmax states; it needs no initialization and its
+ * contents after a call are unspecified.  Calls that share a workspace must
+ * not overlap (same stream, or ordered by events). */
 size_t decode_attention_workspace_bytes(const dqa_kivi_cache* cache);
 
 /* One decode step: out[b][h] = softmax(sm_scale * q[b][h] . K_hat^T) V_hat,
@@ -133,9 +134,14 @@ size_t decode_attention_workspace_bytes(const dqa_kivi_cache* cache);
  *   cache (host) pointer to the descriptor above
  *   ws   (device) workspace of ws_bytes >= decode_attention_workspace_bytes
  *   out  (device) fp32 [B][Hq][d]; zeros when T_q + R == 0
+ * Enqueues one kernel, or two when the tokens of a (batch, KV head) are
+ * split over several workgroups (the second merges the splits in a fixed
+ * order, so results are bit-reproducible run to run).
+ * Every device pointer (q, ws, out and the cache buffers in use) must be
+ * 16-byte aligned (hipMalloc returns 256-byte aligned memory).
  * Supported head ratios Hq/Hkv: 1, 2, 4 (else DQA_ERR_UNSUPPORTED).
  * Errors: DQA_ERR_NULL, DQA_ERR_SHAPE, DQA_ERR_BITS, DQA_ERR_WORKSPACE,
- * DQA_ERR_UNSUPPORTED, DQA_ERR_HIP. */
+ * DQA_ERR_ALIGN, DQA_ERR_UNSUPPORTED, DQA_ERR_HIP. */
 int decode_attention_qkv(const uint16_t* q, const dqa_kivi_cache* cache,
                          float sm_scale, void* ws, size_t ws_bytes, float* out,
                          void* stream);

@@ -41,8 +41,9 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_status_strings():
-    for s in range(8):
+    for s in range(9):
         assert lib.dqa_status_string(s).startswith(b"DQA_")
+    assert lib.dqa_status_string(8).startswith(b"DQA_ERR_ALIGN")
     assert lib.dqa_status_string(99) == b"DQA_ERR_UNKNOWN"
     assert lib.dqa_abi_version() >= 1
 
@@ -71,9 +72,11 @@ def _cache(**kw):
 
 def test_decode_workspace_query_and_validation():
     ws = lib.decode_attention_workspace_bytes(ctypes.byref(_cache()))
-    assert ws > 0
-    # counters (one per unit, 256-byte region) + partial states
-    assert ws >= 256 + 2 * 2 * 4 * 130 * 4
+    # 3 tiles per (batch, KV head): a single split, no partial states
+    assert ws == 256
+    # 128 + 1 tiles over 4 units: 33 splits of partial states [m, l, o[d]] per head
+    big = lib.decode_attention_workspace_bytes(ctypes.byref(_cache(T_q=4096)))
+    assert big == 4 * 33 * 4 * (128 + 2) * 4
     for bad, code in [(dict(d=96), 2), (dict(bits=3), 3), (dict(T_q=40), 2), (dict(R=129), 2),
                       (dict(Hq=6, Hkv=4), 2), (dict(Hq=24, Hkv=2), 5), (dict(Hq=16, Hkv=2), 5),
                       (dict(k_codes=None), 1), (dict(k_recent=None), 1)]:
@@ -84,6 +87,16 @@ def test_decode_workspace_query_and_validation():
     assert lib.decode_attention_qkv(None, ctypes.byref(c), 0.1, FAKE, 1 << 30, FAKE, None) == 1
     assert lib.decode_attention_qkv(FAKE, ctypes.byref(c), 0.1, None, 1 << 30, FAKE, None) == 4
     assert lib.decode_attention_qkv(FAKE, ctypes.byref(c), 0.1, FAKE, ws - 1, FAKE, None) == 4
+    # every device pointer must be 16-byte aligned (checked before any launch)
+    odd = ctypes.c_void_p(0x1008)
+    assert lib.decode_attention_qkv(odd, ctypes.byref(c), 0.1, FAKE, 1 << 30, FAKE, None) == 8
+    assert lib.decode_attention_qkv(FAKE, ctypes.byref(c), 0.1, FAKE, 1 << 30, odd, None) == 8
+    for name in ["k_codes", "v_scale", "v_recent"]:
+        c2 = _cache(**{name: 0x1004})
+        assert lib.decode_attention_qkv(FAKE, ctypes.byref(c2), 0.1, FAKE, 1 << 30, FAKE, None) == 8
+    # the recent-zone pointers are not used (nor checked) without recent tokens
+    c3 = _cache(R=0, k_recent=0x1002, v_recent=None)
+    assert lib.decode_attention_qkv(FAKE, ctypes.byref(c3), 0.1, None, 1 << 30, FAKE, None) == 4
     assert lib.decode_attention_workspace_bytes(ctypes.byref(_cache(d=80))) == 0
     assert lib.decode_attention_workspace_bytes(None) == 0
 
