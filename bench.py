@@ -3,13 +3,16 @@ one MI355X, Llama-3.1-8B-shaped GQA workload (batch 4, 32 query / 8 KV
 heads, head dim 128, 32768 quantized tokens + 128 fp16 recent tokens, RoPE
 theta 5e5).
 
-One step = one decode_attention_qkv call over the whole batch: every
+One step = one decode step over the whole batch, i.e. what
+decode_attention_qkv enqueues: the split kernel (kivi_decode_kernel: every
 quantized token's packed codes and scales plus the fp16 recent zone are read
-from HBM, dequantized, rotated and attended (one fused launch; the
-cross-split merge runs inside it).  Inputs are resident in HBM before the
-timed region.  The compressed cache (~98 MiB) fits in the 256 MB Infinity
-Cache, so the timed steps rotate over several independent replicas whose
-total exceeds it.
+from HBM, dequantized, rotated and attended) and the merge of the splits
+(kivi_merge_kernel).  The two phases are enqueued through their own entry
+points so that HIP events can bracket the split kernel inside the timed
+region; its average duration gives the roofline figure.  Inputs are resident
+in HBM before the timed region.  The compressed cache (~98 MiB) fits in the
+256 MB Infinity Cache, so the timed steps rotate over several independent
+replicas whose total exceeds it.
 
 Prints one JSON line.  Usage:
     python bench.py [--steps K] [--warmup W] [--bits 2|4] [--replicas R]
@@ -28,6 +31,30 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E, published
+KERNEL_SOURCE = os.path.join(ROOT, "dequant_decode_attention_amd", "csrc", "decode_kivi.hip")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "kivi_decode_kernel_llama8b_gqa_32k_traffic.md")
+
+
+def measured_traffic(bits):
+    """HBM bytes per launch of the split kernel from the committed
+    rocprofv3 counter summary (FETCH_SIZE + WRITE_SIZE, scaled by the
+    copy-kernel calibration), or None when the summary is missing, covers
+    another bit width, or was taken on a different kernel source."""
+    import hashlib
+    try:
+        text = open(TRAFFIC_SUMMARY).read()
+    except OSError:
+        return None
+    fields = {}
+    for line in text.splitlines():
+        if line.startswith("- ") and ":" in line:
+            k, v = line[2:].split(":", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    src = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+    if fields.get("kernel_source_sha256") != src:
+        return None
+    key = f"traffic_bytes_per_launch_{bits}bit"
+    return int(fields[key]) if key in fields else None
 
 
 def algorithmic_bytes(cfg, bits):
@@ -115,20 +142,44 @@ def main():
     ws = [c.workspace(dev) for c in caches]
     torch.cuda.synchronize()
 
-    for i in range(args.warmup):
-        dqa.decode_attention_qkv(q, caches[i % len(caches)], scale, out=out, workspace=ws[i % len(ws)])
-    torch.cuda.synchronize()
+    def step(i, ev=None):
+        c, w = caches[i % len(caches)], ws[i % len(ws)]
+        if ev is not None:
+            ev[0].record(stream)
+        dqa.decode_attention_qkv_partial(q, c, scale, out, w)
+        if ev is not None:
+            ev[1].record(stream)
+        dqa.decode_attention_qkv_merge(c, out, w)
+
     stream = torch.cuda.current_stream(dev)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # timed region: K steps (value, ms_per_step)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for i in range(args.steps):
-        dqa.decode_attention_qkv(q, caches[i % len(caches)], scale, out=out, workspace=ws[i % len(ws)])
+        step(i)
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
+    # the same K steps again with events bracketing every split-kernel launch
+    # on its stream: the kernel's average duration for the roofline (the
+    # events add a few microseconds to each step, so the step rate above is
+    # taken without them)
+    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    e0.record(stream)
+    for i in range(args.steps):
+        step(i, kev[i])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    kernel_ms = sum(a.elapsed_time(b) for a, b in kev) / args.steps
+    ms_events = e0.elapsed_time(e1) / args.steps
 
     nbytes = algorithmic_bytes(cfg, bits)
-    achieved = nbytes / (ms * 1e-3) / 1e9
+    achieved = nbytes / (kernel_ms * 1e-3) / 1e9
+    traffic = measured_traffic(bits)
     kv_tokens = cfg["B"] * (cfg["T_q"] + cfg["R"])
     line = {
         "metric": "decode attention KV-tokens/s over a 2-bit cache (+ achieved HBM GB/s, % of peak)"
@@ -149,8 +200,9 @@ def main():
                    "recent_tokens": cfg["R"], "bits": bits, "group": 32,
                    "rope_theta": cfg["rope_theta"], "replicas": args.replicas},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
-                     "algorithmic_bytes": nbytes, "kernel": "kivi_decode_kernel"},
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+                     "algorithmic_bytes": nbytes, "kernel": "kivi_decode_kernel",
+                     "kernel_ms": kernel_ms},
     }
 
     # achievable streaming rate on a buffer of the same size, same run
@@ -164,6 +216,7 @@ def main():
         dqa.stream_copy(src, dst)
     e1.record(stream)
     torch.cuda.synchronize()
+    line["ms_per_step_with_kernel_events"] = ms_events
     line["stream_copy_gbps"] = 2 * src.numel() * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
     del src, dst
 

@@ -55,6 +55,8 @@ _SIGS = {
     "quantize_pack_v": (_i, [_vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp]),
     "decode_attention_workspace_bytes": (_sz, [ctypes.POINTER(KiviCacheStruct)]),
     "decode_attention_qkv": (_i, [_vp, ctypes.POINTER(KiviCacheStruct), _f, _vp, _sz, _vp, _vp]),
+    "decode_attention_qkv_partial": (_i, [_vp, ctypes.POINTER(KiviCacheStruct), _f, _vp, _sz, _vp, _vp]),
+    "decode_attention_qkv_merge": (_i, [ctypes.POINTER(KiviCacheStruct), _vp, _sz, _vp, _vp]),
     "zoned_plan_words": (_sz, [_i, _i, _i, _i]),
     "zoned_plan": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _vp, _sz, ctypes.POINTER(_sz)]),
     "zoned_pack": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
@@ -177,6 +179,26 @@ def decode_attention_qkv(q, cache, sm_scale, out=None, workspace=None):
     _check("decode_attention_qkv",
            lib.decode_attention_qkv(_ptr(q), ctypes.byref(st), float(sm_scale), _ptr(ws),
                                     ws.numel(), _ptr(out), _stream(q.device)))
+    return out
+
+
+def decode_attention_qkv_partial(q, cache, sm_scale, out, workspace):
+    """First phase of decode_attention_qkv (the split kernel); see the header."""
+    q = _dev16(q, "q")
+    st = cache.struct()
+    _check("decode_attention_qkv_partial",
+           lib.decode_attention_qkv_partial(_ptr(q), ctypes.byref(st), float(sm_scale),
+                                            _ptr(workspace), workspace.numel(), _ptr(out),
+                                            _stream(q.device)))
+    return out
+
+
+def decode_attention_qkv_merge(cache, out, workspace):
+    """Second phase of decode_attention_qkv (merge of the splits)."""
+    st = cache.struct()
+    _check("decode_attention_qkv_merge",
+           lib.decode_attention_qkv_merge(ctypes.byref(st), _ptr(workspace), workspace.numel(),
+                                          _ptr(out), _stream(out.device)))
     return out
 
 

@@ -251,38 +251,39 @@ __device__ __forceinline__ void write_split_state(const KiviArgs& a, size_t unit
 }
 
 // Cross-split merge, launched after the decode kernel when a (batch, KV
-// head) has several splits: one workgroup per (batch, KV head) combines
-// the partial states in split order (deterministic) and writes the output.
+// head) has several splits.  One wave per (64 output channels of one query
+// head, KV head, batch): the lanes first compute the merge weight of every
+// split (max over splits, then exp2 weights and the weighted row sum), then
+// each lane sums its channel over the splits in split order, so the result
+// does not depend on scheduling.
 template <int D, int G>
-__global__ __launch_bounds__(256) void kivi_merge_kernel(const float* __restrict__ partials, int total_splits,
-                                                         int Hq, int Hkv, float* __restrict__ out) {
-  __shared__ float wts[kMaxSplitsMerge][G];
-  __shared__ float scal[G];
-  const int kvh = blockIdx.x, b = blockIdx.y;
+__global__ __launch_bounds__(64) void kivi_merge_kernel(const float* __restrict__ partials, int total_splits,
+                                                        int Hq, int Hkv, float* __restrict__ out) {
+  __shared__ float wts[kMaxSplitsMerge];
+  __shared__ float inv_l;
+  constexpr int CB = D / 64;                 // 64-channel blocks per head
+  const int h = blockIdx.x / CB, c = (blockIdx.x % CB) * 64 + threadIdx.x;
+  const int kvh = blockIdx.y, b = blockIdx.z;
   const size_t unit = static_cast<size_t>(b) * Hkv + kvh;
-  const float* parts = partials + unit * total_splits * G * (D + 2);
-  for (int h = threadIdx.x; h < G; h += blockDim.x) {
-    float M = -INFINITY;
-#pragma unroll 8
-    for (int sl = 0; sl < total_splits; ++sl) M = fmaxf(M, parts[(sl * G + h) * (D + 2)]);
+  const float* parts = partials + unit * total_splits * G * (D + 2) + h * (D + 2);
+  constexpr size_t kSplitStride = static_cast<size_t>(G) * (D + 2);
+  float M = -INFINITY;
+  for (int sl = threadIdx.x; sl < total_splits; sl += 64) M = fmaxf(M, parts[sl * kSplitStride]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+  for (int sl = threadIdx.x; sl < total_splits; sl += 64) wts[sl] = merge_weight(parts[sl * kSplitStride], M);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __syncthreads();
+  if (threadIdx.x == 0) {
     float L = 0.0f;
-#pragma unroll 8
-    for (int sl = 0; sl < total_splits; ++sl) {
-      const float* ps = parts + (sl * G + h) * (D + 2);
-      const float wt = merge_weight(ps[0], M);
-      wts[sl][h] = wt;
-      L = fmaf(ps[1], wt, L);
-    }
-    scal[h] = (L > 0.0f) ? 1.0f / L : 0.0f;
+    for (int sl = 0; sl < total_splits; ++sl) L = fmaf(parts[sl * kSplitStride + 1], wts[sl], L);
+    inv_l = (L > 0.0f) ? 1.0f / L : 0.0f;
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < G * D; e += blockDim.x) {
-    const int h = e / D, c = e % D;
-    float O = 0.0f;
+  float O = 0.0f;
 #pragma unroll 8
-    for (int sl = 0; sl < total_splits; ++sl) O = fmaf(parts[(sl * G + h) * (D + 2) + 2 + c], wts[sl][h], O);
-    out[(static_cast<size_t>(b) * Hq + kvh * G + h) * D + c] = O * scal[h];
-  }
+  for (int sl = 0; sl < total_splits; ++sl) O = fmaf(parts[sl * kSplitStride + 2 + c], wts[sl], O);
+  out[(static_cast<size_t>(b) * Hq + kvh * G + h) * D + c] = O * inv_l;
 }
 
 // Reductions over the 4 lanes L, L^16, L^32, L^48 (the four 16-lane rows),
@@ -731,10 +732,11 @@ void launch_decode(const KiviArgs& a, int G, int bits, bool rope, dim3 grid, hip
 }
 
 template <int D>
-void launch_merge(const float* partials, int total, int Hq, int Hkv, int G, float* out, dim3 grid, hipStream_t s) {
-  if (G == 1) hipLaunchKernelGGL((kivi_merge_kernel<D, 1>), grid, dim3(256), 0, s, partials, total, Hq, Hkv, out);
-  else if (G == 2) hipLaunchKernelGGL((kivi_merge_kernel<D, 2>), grid, dim3(256), 0, s, partials, total, Hq, Hkv, out);
-  else hipLaunchKernelGGL((kivi_merge_kernel<D, 4>), grid, dim3(256), 0, s, partials, total, Hq, Hkv, out);
+void launch_merge(const float* partials, int total, int Hq, int Hkv, int G, int B, float* out, hipStream_t s) {
+  const dim3 grid(G * (D / 64), Hkv, B);
+  if (G == 1) hipLaunchKernelGGL((kivi_merge_kernel<D, 1>), grid, dim3(64), 0, s, partials, total, Hq, Hkv, out);
+  else if (G == 2) hipLaunchKernelGGL((kivi_merge_kernel<D, 2>), grid, dim3(64), 0, s, partials, total, Hq, Hkv, out);
+  else hipLaunchKernelGGL((kivi_merge_kernel<D, 4>), grid, dim3(64), 0, s, partials, total, Hq, Hkv, out);
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -750,25 +752,37 @@ extern "C" size_t decode_attention_workspace_bytes(const dqa_kivi_cache* cache) 
   return p.ws_bytes;
 }
 
-extern "C" int decode_attention_qkv(const uint16_t* q, const dqa_kivi_cache* c,
-                                    float sm_scale, void* ws, size_t ws_bytes,
-                                    float* out, void* stream) {
-  Plan p;
-  int st = make_plan(c, &p);
+namespace {
+
+// Validation shared by the decode entry points; fills the plan.
+int check_decode(const uint16_t* q, const dqa_kivi_cache* c, const void* ws, size_t ws_bytes,
+                 const float* out, Plan* p) {
+  int st = make_plan(c, p);
   if (st != DQA_OK) return st;
-  if (p.units == 0) return DQA_OK;
+  if (p->units == 0) return DQA_OK;
   if (!q || !out) return DQA_ERR_NULL;
   if (c->T_q > 0 && (!c->k_codes || !c->k_scale || !c->k_zero || !c->v_codes ||
                      !c->v_scale || !c->v_zero))
     return DQA_ERR_NULL;
   if (c->R > 0 && (!c->k_recent || !c->v_recent)) return DQA_ERR_NULL;
   if (!ws) return DQA_ERR_WORKSPACE;
-  if (ws_bytes < p.ws_bytes) return DQA_ERR_WORKSPACE;
+  if (ws_bytes < p->ws_bytes) return DQA_ERR_WORKSPACE;
   if (!aligned16(q) || !aligned16(ws) || !aligned16(out)) return DQA_ERR_ALIGN;
   if (c->T_q > 0 && (!aligned16(c->k_codes) || !aligned16(c->k_scale) || !aligned16(c->k_zero) ||
                      !aligned16(c->v_codes) || !aligned16(c->v_scale) || !aligned16(c->v_zero)))
     return DQA_ERR_ALIGN;
   if (c->R > 0 && (!aligned16(c->k_recent) || !aligned16(c->v_recent))) return DQA_ERR_ALIGN;
+  return DQA_OK;
+}
+
+}  // namespace
+
+extern "C" int decode_attention_qkv_partial(const uint16_t* q, const dqa_kivi_cache* c,
+                                            float sm_scale, void* ws, size_t ws_bytes,
+                                            float* out, void* stream) {
+  Plan p;
+  const int st = check_decode(q, c, ws, ws_bytes, out, &p);
+  if (st != DQA_OK || p.units == 0) return st;
   KiviArgs a;
   a.q = q;
   a.k_codes = c->k_codes;
@@ -797,11 +811,31 @@ extern "C" int decode_attention_qkv(const uint16_t* q, const dqa_kivi_cache* c,
   if (c->d == 128) launch_decode<128>(a, p.G, c->bits, rope, grid, s);
   else launch_decode<64>(a, p.G, c->bits, rope, grid, s);
   DQA_CHECK_LAUNCH();
-  if (p.total > 1) {
-    const dim3 mgrid(c->Hkv, c->B);
-    if (c->d == 128) launch_merge<128>(a.partials, p.total, c->Hq, c->Hkv, p.G, out, mgrid, s);
-    else launch_merge<64>(a.partials, p.total, c->Hq, c->Hkv, p.G, out, mgrid, s);
-    DQA_CHECK_LAUNCH();
-  }
   return DQA_OK;
+}
+
+extern "C" int decode_attention_qkv_merge(const dqa_kivi_cache* c, const void* ws, size_t ws_bytes,
+                                          float* out, void* stream) {
+  Plan p;
+  int st = make_plan(c, &p);
+  if (st != DQA_OK || p.units == 0) return st;
+  if (!out) return DQA_ERR_NULL;
+  if (!ws) return DQA_ERR_WORKSPACE;
+  if (ws_bytes < p.ws_bytes) return DQA_ERR_WORKSPACE;
+  if (!aligned16(ws) || !aligned16(out)) return DQA_ERR_ALIGN;
+  if (p.total == 1) return DQA_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const float* parts = static_cast<const float*>(ws);
+  if (c->d == 128) launch_merge<128>(parts, p.total, c->Hq, c->Hkv, p.G, c->B, out, s);
+  else launch_merge<64>(parts, p.total, c->Hq, c->Hkv, p.G, c->B, out, s);
+  DQA_CHECK_LAUNCH();
+  return DQA_OK;
+}
+
+extern "C" int decode_attention_qkv(const uint16_t* q, const dqa_kivi_cache* c,
+                                    float sm_scale, void* ws, size_t ws_bytes,
+                                    float* out, void* stream) {
+  const int st = decode_attention_qkv_partial(q, c, sm_scale, ws, ws_bytes, out, stream);
+  if (st != DQA_OK) return st;
+  return decode_attention_qkv_merge(c, ws, ws_bytes, out, stream);
 }

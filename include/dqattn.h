@@ -146,6 +146,22 @@ int decode_attention_qkv(const uint16_t* q, const dqa_kivi_cache* cache,
                          float sm_scale, void* ws, size_t ws_bytes, float* out,
                          void* stream);
 
+/* The two phases of decode_attention_qkv, for callers that schedule or time
+ * them separately; decode_attention_qkv is exactly _partial then _merge on
+ * the same stream, with the same cache, workspace and out.
+ * decode_attention_qkv_partial enqueues the split kernel: every split of a
+ * (batch, KV head) writes its partial softmax state into ws, or -- when the
+ * cache shape gives a single split -- the final output into out.
+ * decode_attention_qkv_merge enqueues the merge of the partial states in
+ * split order into out (nothing when there is a single split); it reads ws
+ * as left by the preceding _partial call.  Arguments, alignment and errors
+ * as decode_attention_qkv (the merge checks cache, ws, ws_bytes and out). */
+int decode_attention_qkv_partial(const uint16_t* q, const dqa_kivi_cache* cache,
+                                 float sm_scale, void* ws, size_t ws_bytes,
+                                 float* out, void* stream);
+int decode_attention_qkv_merge(const dqa_kivi_cache* cache, const void* ws,
+                               size_t ws_bytes, float* out, void* stream);
+
 /* ------------------------------------------------------------------------
  * Mixed-bitwidth zoned cache  ([P3 sec 2.2, bit-allocation pipeline] and
  * [P3 sec 2.2, TriZone packed decoding])

@@ -97,6 +97,13 @@ def test_decode_workspace_query_and_validation():
     # the recent-zone pointers are not used (nor checked) without recent tokens
     c3 = _cache(R=0, k_recent=0x1002, v_recent=None)
     assert lib.decode_attention_qkv(FAKE, ctypes.byref(c3), 0.1, None, 1 << 30, FAKE, None) == 4
+    # the merge phase validates its own arguments
+    assert lib.decode_attention_qkv_merge(ctypes.byref(c), FAKE, 1 << 30, None, None) == 1
+    assert lib.decode_attention_qkv_merge(ctypes.byref(c), None, 1 << 30, FAKE, None) == 4
+    assert lib.decode_attention_qkv_merge(ctypes.byref(c), FAKE, ws - 1, FAKE, None) == 4
+    assert lib.decode_attention_qkv_merge(ctypes.byref(c), FAKE, 1 << 30, odd, None) == 8
+    assert lib.decode_attention_qkv_merge(ctypes.byref(_cache(bits=3)), FAKE, 1 << 30, FAKE, None) == 3
+    assert lib.decode_attention_qkv_partial(None, ctypes.byref(c), 0.1, FAKE, 1 << 30, FAKE, None) == 1
     assert lib.decode_attention_workspace_bytes(ctypes.byref(_cache(d=80))) == 0
     assert lib.decode_attention_workspace_bytes(None) == 0
 

@@ -126,6 +126,24 @@ def test_decode_attention_parity(dqa, case):
     assert np.array_equal(host(out2), got)
 
 
+@pytest.mark.parametrize("T_q,R", [(4096, 77), (64, 5)])
+def test_decode_two_phase_equals_one_call(dqa, T_q, R):
+    """decode_attention_qkv is exactly _partial then _merge (bit-identical),
+    with many splits and with a single split."""
+    B, Hq, Hkv, d, bits = 2, 8, 2, 128, 4
+    inp = kivi_inputs(B, Hq, Hkv, d, T_q, R, seed=7, outliers=("lognormal", 0.04, 3.0, 1.0))
+    say("decode two-phase", T_q, R)
+    cache = gpu_cache(dqa, inp, bits, Hq, 500000.0)
+    q = dev(inp["q"])
+    ref = host(dqa.decode_attention_qkv(q, cache, 0.088))
+    ws = cache.workspace(q.device)
+    out = torch.full((B, Hq, d), float("nan"), dtype=torch.float32, device=q.device)
+    dqa.decode_attention_qkv_partial(q, cache, 0.088, out, ws)
+    dqa.decode_attention_qkv_merge(cache, out, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(out), ref)
+
+
 @pytest.mark.parametrize("name,bits", [("c3", 2), ("c3", 4), ("c2", 2), ("c1", 2)])
 def test_decode_full_config_sampled_rows(dqa, name, bits):
     """Full-size decode in the launch configuration the bench times; the
