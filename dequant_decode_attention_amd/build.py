@@ -29,6 +29,9 @@ DEVICE_FLAGS = [
     "-fPIC",
     "-ffp-contract=fast",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core accumulators stay in ordinary VGPRs (no accumulator-register
+    # copies around each MFMA whose result the VALU also updates)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wno-unused-command-line-argument",
     "-I" + os.path.join(ROOT, "include"),
 ]

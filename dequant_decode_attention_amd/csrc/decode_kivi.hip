@@ -126,6 +126,27 @@ __device__ __forceinline__ uint64_t key_chunk(const uint32_t* w, int ks) {
   else return static_cast<uint64_t>(w[2 * ks]) | (static_cast<uint64_t>(w[2 * ks + 1]) << 32);
 }
 
+// A value the compiler must treat as unknown (keeps a VGPR constant out of
+// the scalar constant bus, and keeps byte extractions from being folded
+// back into bit-field extracts).
+__device__ __forceinline__ uint32_t opaque(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+// The 16 2-bit codes of one 32-bit key word (two K-steps of 8 channels) as
+// fp32: four masked shifts put four codes in the bytes of a register, and
+// each byte is converted on its own (code index 4b + j in byte b of
+// shift j; K-step 2wi + b/2, channel 4 (b & 1) + j).
+__device__ __forceinline__ void key_codes16_2bit(uint32_t w, float (*f)[8]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t d = opaque((w >> (2 * j)) & 0x03030303u);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) f[b >> 1][4 * (b & 1) + j] = static_cast<float>((d >> (8 * b)) & 0xFFu);
+  }
+}
+
 // The lane's 8-code chunk of one value channel (8 consecutive tokens); BITS
 // bytes at `p`.
 template <int BITS>
@@ -165,23 +186,23 @@ __device__ __forceinline__ void key_codes8(uint64_t chunk, float* f) {
 // probabilities).  1024 + code is built in the fp16 bit pattern and 1024
 // subtracted with a packed half add.
 template <int BITS>
-__device__ __forceinline__ half8 value_codes8(uint64_t chunk) {
+__device__ __forceinline__ half8 value_codes8(uint64_t chunk, uint32_t mask, uint32_t magic) {
   uint32_t r[4];
   if constexpr (BITS == 2) {
     const uint32_t v = static_cast<uint32_t>(chunk);
     const uint32_t u = v | (v << 8);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) r[i] = ((u >> (2 * i)) & 0x00030003u) | 0x64006400u;
+    for (int i = 0; i < 4; ++i) r[i] = ((u >> (2 * i)) & mask) | magic;
   } else if constexpr (BITS == 4) {
     const uint32_t w = static_cast<uint32_t>(chunk);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) r[i] = ((w >> (4 * i)) & 0x000F000Fu) | 0x64006400u;
+    for (int i = 0; i < 4; ++i) r[i] = ((w >> (4 * i)) & mask) | magic;
   } else {
     const uint32_t lo = static_cast<uint32_t>(chunk), hi = static_cast<uint32_t>(chunk >> 32);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       r[i] = __builtin_amdgcn_perm(hi, lo, static_cast<uint32_t>(i | (0x0C << 8) | ((4 + i) << 16) | (0x0C << 24))) |
-             0x64006400u;
+             magic;
   }
   half8 out;
   const half2v k1024 = {static_cast<_Float16>(1024.0f), static_cast<_Float16>(1024.0f)};
@@ -202,17 +223,32 @@ __device__ __forceinline__ constexpr int vtok(int e) { return (e >> 1) + 4 * (e 
 // is token 8g + 4s + r.
 __device__ __forceinline__ constexpr int row_token(int s, int m) { return 8 * (m >> 2) + 4 * s + (m & 3); }
 
+// x - (fp32) of the low / high fp16 half of h, exact (the fp16 value is
+// widened exactly and one fp32 rounding applies, none here since hi is x
+// rounded toward zero).  One mixed-precision FMA each; the compiler forms
+// a widening conversion and a subtraction instead.
+__device__ __forceinline__ float minus_half_lo(uint32_t h, float x) {
+  float r;
+  asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "v"(x));
+  return r;
+}
+__device__ __forceinline__ float minus_half_hi(uint32_t h, float x) {
+  float r;
+  asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "v"(x));
+  return r;
+}
+
 // Split 8 fp32 values into fp16 hi + lo (hi rounded toward zero; lo the
 // exact fp32 remainder rounded toward zero).
 __device__ __forceinline__ void split8(const float* x, half8& hi, half8& lo) {
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
-    const half2v h = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(x[2 * p], x[2 * p + 1]));
+    const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(x[2 * p], x[2 * p + 1]));
+    const half2v hv = __builtin_bit_cast(half2v, h);
     const half2v l = __builtin_bit_cast(
-        half2v, __builtin_amdgcn_cvt_pkrtz(x[2 * p] - static_cast<float>(h[0]),
-                                           x[2 * p + 1] - static_cast<float>(h[1])));
-    hi[2 * p] = h[0];
-    hi[2 * p + 1] = h[1];
+        half2v, __builtin_amdgcn_cvt_pkrtz(minus_half_lo(h, x[2 * p]), minus_half_hi(h, x[2 * p + 1])));
+    hi[2 * p] = hv[0];
+    hi[2 * p + 1] = hv[1];
     lo[2 * p] = l[0];
     lo[2 * p + 1] = l[1];
   }
@@ -343,13 +379,29 @@ __global__ __launch_bounds__(256) void kivi_decode_kernel(KiviArgs a) {
   const int col = lane & 15, grp = lane >> 4;
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const size_t unit = static_cast<size_t>(b) * a.Hkv + kvh;
-  // the wave's contiguous tile range: the (batch, KV head)'s quantized tiles
-  // followed by its recent tiles, spread evenly over all its waves
+  // The wave's work: the (batch, KV head)'s n_q quantized and n_r recent
+  // tiles form a sequence of n_q + n_r slots cut evenly over all its waves
+  // (contiguous runs [u0, u1)).  Recent tile r sits at slot
+  // floor((2r + 1)(n_q + n_r) / (2 n_r)), so the recent tiles land in
+  // different waves far apart; the other slots hold the quantized tiles in
+  // order.  A wave attends its recent tiles first, then its contiguous run
+  // [qb, qe) of quantized tiles.
   const int n_tiles = a.n_qtiles + a.n_rtiles;
   const long long nw = static_cast<long long>(a.total_splits) * kWavesPerWG;
   const long long gw = static_cast<long long>(split) * kWavesPerWG + wave;
-  const int wb = static_cast<int>(gw * n_tiles / nw);
-  const int we = static_cast<int>((gw + 1) * n_tiles / nw);
+  const int u0 = static_cast<int>(gw * n_tiles / nw);
+  const int u1 = static_cast<int>((gw + 1) * n_tiles / nw);
+  int r_before = 0, r_mine = 0, r_first = 0;
+  for (int r = 0; r < a.n_rtiles; ++r) {
+    const int slot = static_cast<int>((2LL * r + 1) * n_tiles / (2LL * a.n_rtiles));
+    if (slot < u0) ++r_before;
+    else if (slot < u1) {
+      if (r_mine == 0) r_first = r;
+      ++r_mine;
+    }
+  }
+  const int qb = u0 - r_before;
+  const int qe = u1 - r_before - r_mine;
 
   // in-tile rotation table E[j][i] = e^{i j omega_i}, j = 0..31: thread
   // (pair i, block q) evaluates e^{i 8q omega_i} and e^{i omega_i} accurately
@@ -373,10 +425,8 @@ __global__ __launch_bounds__(256) void kivi_decode_kernel(KiviArgs a) {
         bs = ns;
       }
     }
-    if (wb < we) {
-      rope_unit(static_cast<double>(wb) * kGroup, a.omega[pi], an_c, an_s);
-      rope_unit(static_cast<double>(kGroup), a.omega[pi], w32c, w32s);
-    }
+    if (qb < qe) rope_unit(static_cast<double>(qb) * kGroup, a.omega[pi], an_c, an_s);
+    rope_unit(static_cast<double>(kGroup), a.omega[pi], w32c, w32s);
     __syncthreads();
   }
 
@@ -396,15 +446,15 @@ __global__ __launch_bounds__(256) void kivi_decode_kernel(KiviArgs a) {
   _Float16* const wq = lds_w[wave];
   // B operand of the logit product for the current tile: the query rotated
   // back by the tile position, split hi/lo, [hi|lo][head][channel]
-  auto write_query = [&]() {
+  auto write_query = [&](float cth, float sth) {
 #pragma unroll
     for (int k = 0; k < HPL; ++k) {
       const int h = lane / NPAIR + k * LPP;
       if (h < G) {
         float r0 = qv[k][0], r1 = qv[k][1];
         if constexpr (ROPE) {
-          r0 = qv[k][0] * an_c + qv[k][1] * an_s;
-          r1 = qv[k][1] * an_c - qv[k][0] * an_s;
+          r0 = qv[k][0] * cth + qv[k][1] * sth;
+          r1 = qv[k][1] * cth - qv[k][0] * sth;
         }
         const half2v hi = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(r0, r1));
         const half2v lo = __builtin_bit_cast(
@@ -415,7 +465,7 @@ __global__ __launch_bounds__(256) void kivi_decode_kernel(KiviArgs a) {
     }
   };
   if constexpr (!ROPE) {
-    write_query();
+    write_query(1.0f, 0.0f);
     wave_sync();
   }
 
@@ -497,6 +547,9 @@ __global__ __launch_bounds__(256) void kivi_decode_kernel(KiviArgs a) {
   const uint8_t* const kbase = reinterpret_cast<const uint8_t*>(a.k_codes) + unit * a.T_q * KROW;
   const uint8_t* const vbase = reinterpret_cast<const uint8_t*>(a.v_codes) + unit * a.n_qtiles * VBLK;
   constexpr int VW = BITS == 8 ? 2 : 1;   // 32-bit words per value chunk
+  // fp16 1024 + code: code bits under the 0x6400 exponent pattern
+  const uint32_t vmask = opaque(BITS == 2 ? 0x00030003u : 0x000F000Fu);
+  const uint32_t vmagic = opaque(0x64006400u);
   // a tile's raw inputs, loaded one tile ahead into registers that are not
   // touched until the tile is processed
   struct TileIn {
@@ -549,7 +602,7 @@ __global__ __launch_bounds__(256) void kivi_decode_kernel(KiviArgs a) {
     }
     if (prefetch) load_tile(ti + 1, nxt);
     if constexpr (ROPE) {
-      write_query();
+      write_query(an_c, an_s);
       const float nc = an_c * w32c - an_s * w32s;
       const float ns = an_c * w32s + an_s * w32c;
       an_c = nc;
@@ -558,9 +611,16 @@ __global__ __launch_bounds__(256) void kivi_decode_kernel(KiviArgs a) {
     wave_sync();
 
     float lg[8], p[8];
+    float kc2[2][2][8];   // 2-bit: codes of the current pair of K-steps, per half
     tile_logits(ti * kGroup,
                 [&](int s, int ks, float* x) {
-                  key_codes8<BITS>(key_chunk<BITS>(cur.k[s].w, ks), x);
+                  if constexpr (BITS == 2) {
+                    if ((ks & 1) == 0) key_codes16_2bit(cur.k[s].w[ks >> 1], kc2[s]);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) x[e] = kc2[s][ks & 1][e];
+                  } else {
+                    key_codes8<BITS>(key_chunk<BITS>(cur.k[s].w, ks), x);
+                  }
                   const int c0 = CPL * grp + 8 * ks;
                   const half8 sh = *reinterpret_cast<const half8*>(&lds_ksz[wave][0][c0]);
                   const half8 zh = *reinterpret_cast<const half8*>(&lds_ksz[wave][1][c0]);
@@ -583,7 +643,7 @@ __global__ __launch_bounds__(256) void kivi_decode_kernel(KiviArgs a) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       const uint64_t ch = VW == 2 ? (static_cast<uint64_t>(cur.v[mb][VW - 1]) << 32) | cur.v[mb][0] : cur.v[mb][0];
-      acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(value_codes8<BITS>(ch), bv, acc[mb], 0, 0, 0);
+      acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(value_codes8<BITS>(ch, vmask, vmagic), bv, acc[mb], 0, 0, 0);
     }
     wave_sync();
   };
@@ -591,23 +651,37 @@ __global__ __launch_bounds__(256) void kivi_decode_kernel(KiviArgs a) {
   // ------------------------------------------------------ fp16 recent tile
   const uint16_t* const krb = a.k_recent + unit * a.R * D;
   const uint16_t* const vrb = a.v_recent + unit * a.R * D;
-  auto recent_tile = [&](int ti) {
-    const int r0 = (ti - a.n_qtiles) * kGroup;
-    write_query();    // the value staging below reuses the query area
-    if constexpr (ROPE) {
-      const float nc = an_c * w32c - an_s * w32s;
-      const float ns = an_c * w32s + an_s * w32c;
-      an_c = nc;
-      an_s = ns;
+  auto recent_tile = [&](int rt) {
+    const int r0 = rt * kGroup;
+    // every load of the tile is issued before any is used: keys (the lane's
+    // 8 channels of K-step ks for its two tokens) and value slabs (token
+    // lane/2, 8 channels of 16-channel block mb)
+    uint4 kin[2][KS], vin[MB];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const int r = r0 + row_token(s2, col);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        kin[s2][ks] = uint4{0u, 0u, 0u, 0u};
+        if (r < a.R) kin[s2][ks] = *reinterpret_cast<const uint4*>(krb + static_cast<size_t>(r) * D + CPL * grp + 8 * ks);
+      }
     }
+    {
+      const int r = r0 + (lane >> 1);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        vin[mb] = uint4{0u, 0u, 0u, 0u};
+        if (r < a.R) vin[mb] = *reinterpret_cast<const uint4*>(vrb + static_cast<size_t>(r) * D + 16 * mb + 8 * (lane & 1));
+      }
+    }
+    float rc = 1.0f, rs = 0.0f;
+    if constexpr (ROPE) rope_unit(static_cast<double>(a.n_qtiles + rt) * kGroup, a.omega[pi], rc, rs);
+    write_query(rc, rs);    // the value staging below reuses the query area
     wave_sync();
     float lg[8], p[8];
-    tile_logits(ti * kGroup,
-                [&](int s, int ks, float* x) {
-                  const int r = r0 + row_token(s, col);
-                  uint4 u = uint4{0u, 0u, 0u, 0u};
-                  if (r < a.R) u = *reinterpret_cast<const uint4*>(krb + static_cast<size_t>(r) * D + CPL * grp + 8 * ks);
-                  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    tile_logits((a.n_qtiles + rt) * kGroup,
+                [&](int s2, int ks, float* x) {
+                  const uint32_t w[4] = {kin[s2][ks].x, kin[s2][ks].y, kin[s2][ks].z, kin[s2][ks].w};
 #pragma unroll
                   for (int i = 0; i < 4; ++i) {
                     x[2 * i] = h2f(static_cast<uint16_t>(w[i] & 0xFFFFu));
@@ -624,13 +698,10 @@ __global__ __launch_bounds__(256) void kivi_decode_kernel(KiviArgs a) {
     for (int e = 0; e < 8; ++e) bv[e] = static_cast<_Float16>(col < NCOL ? p[e] : 0.0f);
     wave_sync();
     // values pass through LDS 16 channels at a time to form the
-    // channel-major operand: lane -> (token lane/2, 8 channels)
-#pragma unroll 1
+    // channel-major operand
+#pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-      const int t = lane >> 1, r = r0 + t;
-      uint4 u = uint4{0u, 0u, 0u, 0u};
-      if (r < a.R) u = *reinterpret_cast<const uint4*>(vrb + static_cast<size_t>(r) * D + 16 * mb + 8 * (lane & 1));
-      *reinterpret_cast<uint4*>(&wq[t * VST + 8 * (lane & 1)]) = u;
+      *reinterpret_cast<uint4*>(&wq[(lane >> 1) * VST + 8 * (lane & 1)]) = vin[mb];
       wave_sync();
       half8 av;
 #pragma unroll
@@ -640,18 +711,20 @@ __global__ __launch_bounds__(256) void kivi_decode_kernel(KiviArgs a) {
     }
   };
 
-  // tiles in order; two register buffers alternate so that the loads of
-  // tile i+1 stay in flight during tile i
-  const int qend = min(we, a.n_qtiles);
+  // the wave's recent tiles, then its quantized run; two register buffers
+  // alternate so that the loads of tile i+1 stay in flight during tile i
   TileIn buf0, buf1;
-  if (wb < qend) load_tile(wb, buf0);
-  for (int ti = wb; ti < we; ti += 2) {
-    if (ti < a.n_qtiles) quantized_tile(ti, buf0, buf1, ti + 1 < qend);
-    else recent_tile(ti);
-    if (ti + 1 < we) {
-      if (ti + 1 < a.n_qtiles) quantized_tile(ti + 1, buf1, buf0, ti + 2 < qend);
-      else recent_tile(ti + 1);
+  if (qb < qe) load_tile(qb, buf0);
+  for (int k = 0; k < r_mine; ++k) recent_tile(r_first + k);
+  if constexpr (!ROPE) {
+    if (r_mine > 0) {
+      write_query(1.0f, 0.0f);   // restore the query area used for staging
+      wave_sync();
     }
+  }
+  for (int ti = qb; ti < qe; ti += 2) {
+    quantized_tile(ti, buf0, buf1, ti + 1 < qe);
+    if (ti + 1 < qe) quantized_tile(ti + 1, buf1, buf0, ti + 2 < qe);
   }
 
   // ---- wave state -> LDS: row sums and zero-point sums over the 4 row
