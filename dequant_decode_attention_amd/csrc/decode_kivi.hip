@@ -46,6 +46,9 @@ constexpr int kWavesPerWG = 4;
 // splits per (batch, KV head) at most (the merge keeps one weight per
 // (split, head) in LDS)
 constexpr int kMaxSplitsMerge = 255;
+// workgroups of the decode kernel that are resident at once on 256 compute
+// units at 2 workgroups (8 waves) per unit
+constexpr int kDecodeWorkgroups = 512;
 
 struct KiviArgs {
   const uint16_t* q;
@@ -181,39 +184,41 @@ __device__ __forceinline__ void key_codes8(uint64_t chunk, float* f) {
   }
 }
 
-// Value chunk (8 tokens of one channel) -> exact fp16 codes.  Element 2i
-// holds token i, element 2i+1 token i+4 (the same order is used for the
-// probabilities).  1024 + code is built in the fp16 bit pattern and 1024
-// subtracted with a packed half add.
+// Value chunk (8 tokens of one channel) -> fp16 operand holding code *
+// 2^-24 exactly: a code placed in the low bits of an fp16 bit pattern with a
+// zero exponent field is the subnormal code * 2^-24, which the matrix cores
+// multiply exactly (the accumulator is rescaled by 2^24 once, at the end).
+// Element 2i holds token i, element 2i+1 token i+4 (the same order is used
+// for the probabilities).
 template <int BITS>
-__device__ __forceinline__ half8 value_codes8(uint64_t chunk, uint32_t mask, uint32_t magic) {
+__device__ __forceinline__ half8 value_codes8(uint64_t chunk, uint32_t mask) {
   uint32_t r[4];
   if constexpr (BITS == 2) {
     const uint32_t v = static_cast<uint32_t>(chunk);
     const uint32_t u = v | (v << 8);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) r[i] = ((u >> (2 * i)) & mask) | magic;
+    for (int i = 0; i < 4; ++i) r[i] = (u >> (2 * i)) & mask;
   } else if constexpr (BITS == 4) {
     const uint32_t w = static_cast<uint32_t>(chunk);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) r[i] = ((w >> (4 * i)) & mask) | magic;
+    for (int i = 0; i < 4; ++i) r[i] = (w >> (4 * i)) & mask;
   } else {
     const uint32_t lo = static_cast<uint32_t>(chunk), hi = static_cast<uint32_t>(chunk >> 32);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      r[i] = __builtin_amdgcn_perm(hi, lo, static_cast<uint32_t>(i | (0x0C << 8) | ((4 + i) << 16) | (0x0C << 24))) |
-             magic;
+      r[i] = __builtin_amdgcn_perm(hi, lo, static_cast<uint32_t>(i | (0x0C << 8) | ((4 + i) << 16) | (0x0C << 24)));
   }
   half8 out;
-  const half2v k1024 = {static_cast<_Float16>(1024.0f), static_cast<_Float16>(1024.0f)};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const half2v h = __builtin_bit_cast(half2v, r[i]) - k1024;
+    const half2v h = __builtin_bit_cast(half2v, r[i]);
     out[2 * i] = h[0];
     out[2 * i + 1] = h[1];
   }
   return out;
 }
+// the value accumulator of quantized tiles is kept scaled by 2^-24
+constexpr float kCodeScale = 16777216.0f;   // 2^24
 
 // token offset (inside the lane's 8-token run) of operand element e
 __device__ __forceinline__ constexpr int vtok(int e) { return (e >> 1) + 4 * (e & 1); }
@@ -295,6 +300,7 @@ __device__ __forceinline__ void write_split_state(const KiviArgs& a, size_t unit
 template <int D, int G>
 __global__ __launch_bounds__(64) void kivi_merge_kernel(const float* __restrict__ partials, int total_splits,
                                                         int Hq, int Hkv, float* __restrict__ out) {
+  constexpr int kEarly = 16;                 // splits whose outputs are loaded with the states
   __shared__ float wts[kMaxSplitsMerge];
   __shared__ float inv_l;
   constexpr int CB = D / 64;                 // 64-channel blocks per head
@@ -303,22 +309,31 @@ __global__ __launch_bounds__(64) void kivi_merge_kernel(const float* __restrict_
   const size_t unit = static_cast<size_t>(b) * Hkv + kvh;
   const float* parts = partials + unit * total_splits * G * (D + 2) + h * (D + 2);
   constexpr size_t kSplitStride = static_cast<size_t>(G) * (D + 2);
+  // every load that does not depend on another is issued first
+  float early[kEarly];
+#pragma unroll
+  for (int i = 0; i < kEarly; ++i) early[i] = (i < total_splits) ? parts[i * kSplitStride + 2 + c] : 0.0f;
   float M = -INFINITY;
   for (int sl = threadIdx.x; sl < total_splits; sl += 64) M = fmaxf(M, parts[sl * kSplitStride]);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
-  for (int sl = threadIdx.x; sl < total_splits; sl += 64) wts[sl] = merge_weight(parts[sl * kSplitStride], M);
+  float L = 0.0f;
+  for (int sl = threadIdx.x; sl < total_splits; sl += 64) {
+    const float wt = merge_weight(parts[sl * kSplitStride], M);
+    wts[sl] = wt;
+    L = fmaf(parts[sl * kSplitStride + 1], wt, L);
+  }
+  // lane partial sums combined in a fixed butterfly order
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o, 64);
+  if (threadIdx.x == 0) inv_l = (L > 0.0f) ? 1.0f / L : 0.0f;
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __syncthreads();
-  if (threadIdx.x == 0) {
-    float L = 0.0f;
-    for (int sl = 0; sl < total_splits; ++sl) L = fmaf(parts[sl * kSplitStride + 1], wts[sl], L);
-    inv_l = (L > 0.0f) ? 1.0f / L : 0.0f;
-  }
-  __syncthreads();
   float O = 0.0f;
-#pragma unroll 8
-  for (int sl = 0; sl < total_splits; ++sl) O = fmaf(parts[sl * kSplitStride + 2 + c], wts[sl], O);
+#pragma unroll
+  for (int i = 0; i < kEarly; ++i)
+    if (i < total_splits) O = fmaf(early[i], wts[i], O);
+  for (int sl = kEarly; sl < total_splits; ++sl) O = fmaf(parts[sl * kSplitStride + 2 + c], wts[sl], O);
   out[(static_cast<size_t>(b) * Hq + kvh * G + h) * D + c] = O * inv_l;
 }
 
@@ -547,9 +562,8 @@ __global__ __launch_bounds__(256) void kivi_decode_kernel(KiviArgs a) {
   const uint8_t* const kbase = reinterpret_cast<const uint8_t*>(a.k_codes) + unit * a.T_q * KROW;
   const uint8_t* const vbase = reinterpret_cast<const uint8_t*>(a.v_codes) + unit * a.n_qtiles * VBLK;
   constexpr int VW = BITS == 8 ? 2 : 1;   // 32-bit words per value chunk
-  // fp16 1024 + code: code bits under the 0x6400 exponent pattern
+  // two codes per register: one in each fp16 half (subnormal code * 2^-24)
   const uint32_t vmask = opaque(BITS == 2 ? 0x00030003u : 0x000F000Fu);
-  const uint32_t vmagic = opaque(0x64006400u);
   // a tile's raw inputs, loaded one tile ahead into registers that are not
   // touched until the tile is processed
   struct TileIn {
@@ -643,7 +657,7 @@ __global__ __launch_bounds__(256) void kivi_decode_kernel(KiviArgs a) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       const uint64_t ch = VW == 2 ? (static_cast<uint64_t>(cur.v[mb][VW - 1]) << 32) | cur.v[mb][0] : cur.v[mb][0];
-      acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(value_codes8<BITS>(ch, vmask, vmagic), bv, acc[mb], 0, 0, 0);
+      acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(value_codes8<BITS>(ch, vmask), bv, acc[mb], 0, 0, 0);
     }
     wave_sync();
   };
@@ -716,6 +730,12 @@ __global__ __launch_bounds__(256) void kivi_decode_kernel(KiviArgs a) {
   TileIn buf0, buf1;
   if (qb < qe) load_tile(qb, buf0);
   for (int k = 0; k < r_mine; ++k) recent_tile(r_first + k);
+  // fp16 value products are exact-scale; switch the accumulator to the
+  // 2^-24 domain of the code products (exact: a power of two)
+  if (r_mine > 0) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[mb] *= 1.0f / kCodeScale;
+  }
   if constexpr (!ROPE) {
     if (r_mine > 0) {
       write_query(1.0f, 0.0f);   // restore the query area used for staging
@@ -736,7 +756,7 @@ __global__ __launch_bounds__(256) void kivi_decode_kernel(KiviArgs a) {
     for (int mb = 0; mb < MB; ++mb)
       if (mb / 2 == vg)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) lds_o[wave][qh][16 * mb + 4 * grp + r] = acc[mb][r] + zacc;
+        for (int r = 0; r < 4; ++r) lds_o[wave][qh][16 * mb + 4 * grp + r] = fmaf(acc[mb][r], kCodeScale, zacc);
   }
   if (lane < G) {
     lds_m[wave][lane] = m;
@@ -766,11 +786,11 @@ int make_plan(const dqa_kivi_cache* c, Plan* p) {
   p->units = static_cast<size_t>(c->B) * c->Hkv;
   p->n_qtiles = c->T_q / kGroup;
   p->n_rtiles = (c->R + kGroup - 1) / kGroup;
-  // enough workgroups to fill the chip, at least one tile per wave when the
-  // cache is long enough; the recent tiles follow the quantized ones in the
-  // same tile range, and an empty cache still gets one split (zero output)
+  // One resident round of workgroups (2 per compute unit: the kernel runs
+  // at 2 waves per SIMD), at least one tile per wave when the cache is long
+  // enough; an empty cache still gets one split (zero output).
   const long long n_tiles = p->n_qtiles + p->n_rtiles;
-  long long want = (kTargetWorkgroups + static_cast<long long>(p->units) - 1) /
+  long long want = (kDecodeWorkgroups + static_cast<long long>(p->units) - 1) /
                    static_cast<long long>(p->units > 0 ? p->units : 1);
   long long cap = (n_tiles + kWavesPerWG - 1) / kWavesPerWG;
   if (want > cap) want = cap;
