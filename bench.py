@@ -14,9 +14,15 @@ in HBM before the timed region.  The compressed cache (~98 MiB) fits in the
 256 MB Infinity Cache, so the timed steps rotate over several independent
 replicas whose total exceeds it.
 
+The line also carries "rows": the other steps of the path timed on their
+own workloads with HIP events, each against its own roofline (quantize +
+pack of the 32k cache; zoned pack and decode on the mixed-width 16k cache;
+residual-VQ encode, MFMA-bound, and decode on the 8k Llama-3.2-3B-shaped
+cache), and "cpu_baseline": the oracle timed on a sample of the same step.
+
 Prints one JSON line.  Usage:
     python bench.py [--steps K] [--warmup W] [--bits 2|4] [--replicas R]
-                    [--no-cpu-baseline] [--rows]
+                    [--no-cpu-baseline] [--no-rows]
 """
 import argparse
 import json
@@ -101,6 +107,123 @@ def cpu_baseline(inp, cfg, bits, scale, budget_s=12.0):
                        f"numpy dequantization + fp64 attention, scaled to the full step")
 
 
+MFMA_FP16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 matrix peak, published
+
+
+def _event_ms(torch, fn, iters, warmup=3):
+    """Average duration of fn() over iters calls, HIP events on the current
+    stream (fn enqueues work only)."""
+    for _ in range(warmup):
+        fn(0)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(iters):
+        fn(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / iters
+
+
+def _hbm_row(kernel, workload, ms, nbytes, note=""):
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    r = {"kernel": kernel, "workload": workload, "us": ms * 1e3, "bound": "hbm",
+         "algorithmic_bytes": nbytes, "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+         "frac": gbps / HBM_PEAK_GBPS}
+    if note:
+        r["note"] = note
+    return r
+
+
+def time_quantize(dqa, torch, k, v, bits, cfg):
+    """Rows a1-a3: quantize + pack of the whole c3 cache (fp16 in, codes and
+    fp16 scale/zero out)."""
+    B, Hkv, T, d = k.shape
+    n = B * Hkv * T * d
+    nbytes = n * 2 + n * bits // 8 + 2 * 2 * (n // 32)
+    out = {}
+    for name, x, fn in (("quantize_k", k, dqa.quantize_pack_k), ("quantize_v", v, dqa.quantize_pack_v)):
+        ms = _event_ms(torch, lambda i: fn(x, bits), 10)
+        out[name] = _hbm_row(f"{name}_kernel", cfg["workload"], ms, nbytes)
+    return out
+
+
+def time_zoned(dqa, torch, dev):
+    """Rows a8-a9 on the mixed-width zoned workload (c4): packer (fp16 K/V of
+    kept tokens read, blob written) and decode (blob read; blob replicas
+    rotated past the Infinity Cache)."""
+    from workloads import CONFIGS, zoned_inputs
+    import numpy as np
+    cfg = CONFIGS["c4"]
+    inp = zoned_inputs(cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["d"], cfg["T_old"], cfg["C"], seed=4,
+                       v_width_probs=cfg["v_width_probs"], k_width_probs=cfg["k_width_probs"],
+                       outliers=cfg["outliers"])
+    plan = dqa.zoned_plan(inp["v_bits"], inp["k_bits"], cfg["C"], cfg["d"], dev)
+    k, v = torch.from_numpy(inp["k"]).to(dev), torch.from_numpy(inp["v"]).to(dev)
+    kn, vn = torch.from_numpy(inp["k_new"]).to(dev), torch.from_numpy(inp["v_new"]).to(dev)
+    q = torch.from_numpy(inp["q"]).to(dev)
+    kept = int((inp["v_bits"] > 0).sum())
+    d = cfg["d"]
+    pack_bytes = 2 * kept * d * 2 + 2 * kn.numel() * 2 + plan.blob_bytes
+    ms = _event_ms(torch, lambda i: dqa.zoned_pack(plan, k, v, kn, vn), 10)
+    out = {"zoned_pack": _hbm_row("zoned_pack_kernel", cfg["workload"], ms, pack_bytes,
+                                  "fp16 K/V of kept tokens and new tokens read, blob written")}
+    blob = dqa.zoned_pack(plan, k, v, kn, vn)
+    del k, v
+    reps = max(2, int(np.ceil(320e6 / max(plan.blob_bytes, 1))))
+    blobs = [blob.clone() for _ in range(reps)]
+    scale = 1.0 / math.sqrt(d)
+    res = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    n = dqa.lib.decode_attention_zoned_workspace_bytes(plan.host_ptr(), cfg["Hq"])
+    ws = torch.zeros(max(n, 1), dtype=torch.uint8, device=dev)
+    ms = _event_ms(torch, lambda i: dqa.decode_attention_zoned(q, plan, blobs[i % reps], scale,
+                                                                out=res, workspace=ws), 50)
+    nbytes = plan.blob_bytes + q.numel() * 2 + res.numel() * 4
+    out["zoned_decode"] = _hbm_row("zoned_decode_kernel", cfg["workload"], ms, nbytes,
+                                   f"blob {plan.blob_bytes} B, {reps} replicas rotated")
+    return out
+
+
+def time_rvq(dqa, torch, dev):
+    """Rows a10-a11 on the residual-VQ workload (c5): encoding of every key
+    and value vector (MFMA-bound: 2 N Kc d flop per vector) and decode
+    attention from the indices (a few MB per step: latency-bound)."""
+    from workloads import CONFIGS, rvq_inputs
+    cfg = CONFIGS["c5"]
+    inp = rvq_inputs(cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["d"], cfg["T"], cfg["N"], cfg["Kc"], seed=5)
+    d, N, Kc = cfg["d"], cfg["N"], cfg["Kc"]
+    k = torch.from_numpy(inp["k"]).to(dev).reshape(-1, d)
+    v = torch.from_numpy(inp["v"]).to(dev).reshape(-1, d)
+    kcb, vcb = torch.from_numpy(inp["k_cb"]).to(dev), torch.from_numpy(inp["v_cb"]).to(dev)
+    ws = torch.empty(max(dqa.lib.rvq_encode_workspace_bytes(N, Kc), 1), dtype=torch.uint8, device=dev)
+
+    def encode(i):
+        dqa.rvq_encode(k, kcb, workspace=ws)
+        dqa.rvq_encode(v, vcb, workspace=ws)
+    ms = _event_ms(torch, encode, 10)
+    flop = 2 * 2 * k.shape[0] * N * Kc * d
+    tf = flop / (ms * 1e-3) / 1e12
+    out = {"rvq_encode": {"kernel": "rvq_encode_kernel", "workload": cfg["workload"], "us": ms * 1e3,
+                          "bound": "mfma", "algorithmic_flop": flop, "achieved": tf,
+                          "peak": MFMA_FP16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                          "frac": tf / MFMA_FP16_PEAK_TFLOPS,
+                          "note": "keys and values, N stages x Kc codewords each; distances only"}}
+    kidx = dqa.rvq_encode(k, kcb, workspace=ws).reshape(cfg["B"], cfg["Hkv"], cfg["T"], N)
+    vidx = dqa.rvq_encode(v, vcb, workspace=ws).reshape(cfg["B"], cfg["Hkv"], cfg["T"], N)
+    q = torch.from_numpy(inp["q"]).to(dev)
+    res = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    n = dqa.lib.rvq_decode_attention_workspace_bytes(cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["T"], d)
+    wsd = torch.zeros(max(n, 1), dtype=torch.uint8, device=dev)
+    scale = 1.0 / math.sqrt(d)
+    ms = _event_ms(torch, lambda i: dqa.rvq_decode_attention(q, kidx, vidx, kcb, vcb, scale, out=res,
+                                                              workspace=wsd), 50)
+    nbytes = 2 * kidx.numel() * 2 + 2 * kcb.numel() * 2 + q.numel() * 2 + res.numel() * 4
+    out["rvq_decode"] = _hbm_row("rvq_decode_kernel", cfg["workload"], ms, nbytes,
+                                 "indices + codebooks (4 MB per step): latency-bound, not HBM")
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -109,7 +232,8 @@ def main():
     ap.add_argument("--bits", type=int, default=2, choices=[2, 4])
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--rows", action="store_true", help="also time the other hot-path rows")
+    ap.add_argument("--no-rows", action="store_true",
+                    help="skip timing the other hot-path rows (quantize, zoned, RVQ)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus}); the decode path shards "
@@ -130,6 +254,9 @@ def main():
     v = torch.from_numpy(inp["v"]).to(dev)
     kc, ks, kz = dqa.quantize_pack_k(k, bits)
     vc, vs, vz = dqa.quantize_pack_v(v, bits)
+    rows = {}
+    if not args.no_rows:
+        rows.update(time_quantize(dqa, torch, k, v, bits, cfg))
     kr = torch.from_numpy(inp["k_recent"]).to(dev)
     vr = torch.from_numpy(inp["v_recent"]).to(dev)
     q = torch.from_numpy(inp["q"]).to(dev)
@@ -220,6 +347,10 @@ def main():
     line["stream_copy_gbps"] = 2 * src.numel() * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
     del src, dst
 
+    if not args.no_rows:
+        rows.update(time_zoned(dqa, torch, dev))
+        rows.update(time_rvq(dqa, torch, dev))
+        line["rows"] = rows
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp, cfg, bits, scale)
     print(json.dumps(line), flush=True)
