@@ -30,22 +30,17 @@
 //     exactly the tokens that column n of the value operand needs, so no
 //     data moves between the two products.
 // The online softmax runs once per tile per column.  Each split writes its
-// partial softmax state; a second, small kernel merges the splits of every
-// (batch, KV head) in split order.  (A last-workgroup merge inside the
-// decode kernel would need a device-scope fence and a counter atomic per
-// workgroup; on this chip, whose L2 is private to each XCD, those cost more
-// than a third of the decode kernel's time.)
+// partial softmax state; split_merge_kernel (merge.h) merges the splits of
+// every (batch, KV head) in split order.
 #include <cmath>
 
 #include "common.h"
+#include "merge.h"
 
 namespace dqa {
 namespace {
 
 constexpr int kWavesPerWG = 4;
-// splits per (batch, KV head) at most (the merge keeps one weight per
-// (split, head) in LDS)
-constexpr int kMaxSplitsMerge = 255;
 // workgroups of the decode kernel that are resident at once on 256 compute
 // units at 2 workgroups (8 waves) per unit
 constexpr int kDecodeWorkgroups = 512;
@@ -257,84 +252,6 @@ __device__ __forceinline__ void split8(const float* x, half8& hi, half8& lo) {
     lo[2 * p] = l[0];
     lo[2 * p + 1] = l[1];
   }
-}
-
-// Merge the 4 wave states of a workgroup (in LDS) and write the split's
-// partial softmax state [m, l, o[D]] per head -- or, when the (batch, KV
-// head) has a single split, the normalized output.  Called by every thread.
-template <int D, int G>
-__device__ __forceinline__ void write_split_state(const KiviArgs& a, size_t unit, int b, int kvh, int slot,
-                                                  const float (*lm)[G], const float (*ll)[G],
-                                                  const float (*lo)[G][D]) {
-  float* part = a.partials + (unit * a.total_splits + slot) * G * (D + 2);
-  for (int e = threadIdx.x; e < G * D; e += blockDim.x) {
-    const int h = e / D, c = e % D;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kWavesPerWG; ++w) M = fmaxf(M, lm[w][h]);
-    float L = 0.0f, O = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kWavesPerWG; ++w) {
-      const float wt = merge_weight(lm[w][h], M);
-      L = fmaf(ll[w][h], wt, L);
-      O = fmaf(lo[w][h][c], wt, O);
-    }
-    if (a.total_splits == 1) {
-      a.out[(static_cast<size_t>(b) * a.Hq + kvh * G + h) * D + c] = (L > 0.0f) ? O / L : 0.0f;
-    } else {
-      if (c == 0) {
-        part[h * (D + 2) + 0] = M;
-        part[h * (D + 2) + 1] = L;
-      }
-      part[h * (D + 2) + 2 + c] = O;
-    }
-  }
-}
-
-// Cross-split merge, launched after the decode kernel when a (batch, KV
-// head) has several splits.  One wave per (64 output channels of one query
-// head, KV head, batch): the lanes first compute the merge weight of every
-// split (max over splits, then exp2 weights and the weighted row sum), then
-// each lane sums its channel over the splits in split order, so the result
-// does not depend on scheduling.
-template <int D, int G>
-__global__ __launch_bounds__(64) void kivi_merge_kernel(const float* __restrict__ partials, int total_splits,
-                                                        int Hq, int Hkv, float* __restrict__ out) {
-  constexpr int kEarly = 16;                 // splits whose outputs are loaded with the states
-  __shared__ float wts[kMaxSplitsMerge];
-  __shared__ float inv_l;
-  constexpr int CB = D / 64;                 // 64-channel blocks per head
-  const int h = blockIdx.x / CB, c = (blockIdx.x % CB) * 64 + threadIdx.x;
-  const int kvh = blockIdx.y, b = blockIdx.z;
-  const size_t unit = static_cast<size_t>(b) * Hkv + kvh;
-  const float* parts = partials + unit * total_splits * G * (D + 2) + h * (D + 2);
-  constexpr size_t kSplitStride = static_cast<size_t>(G) * (D + 2);
-  // every load that does not depend on another is issued first
-  float early[kEarly];
-#pragma unroll
-  for (int i = 0; i < kEarly; ++i) early[i] = (i < total_splits) ? parts[i * kSplitStride + 2 + c] : 0.0f;
-  float M = -INFINITY;
-  for (int sl = threadIdx.x; sl < total_splits; sl += 64) M = fmaxf(M, parts[sl * kSplitStride]);
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
-  float L = 0.0f;
-  for (int sl = threadIdx.x; sl < total_splits; sl += 64) {
-    const float wt = merge_weight(parts[sl * kSplitStride], M);
-    wts[sl] = wt;
-    L = fmaf(parts[sl * kSplitStride + 1], wt, L);
-  }
-  // lane partial sums combined in a fixed butterfly order
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o, 64);
-  if (threadIdx.x == 0) inv_l = (L > 0.0f) ? 1.0f / L : 0.0f;
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __syncthreads();
-  float O = 0.0f;
-#pragma unroll
-  for (int i = 0; i < kEarly; ++i)
-    if (i < total_splits) O = fmaf(early[i], wts[i], O);
-  for (int sl = kEarly; sl < total_splits; ++sl) O = fmaf(parts[sl * kSplitStride + 2 + c], wts[sl], O);
-  out[(static_cast<size_t>(b) * Hq + kvh * G + h) * D + c] = O * inv_l;
 }
 
 // Reductions over the 4 lanes L, L^16, L^32, L^48 (the four 16-lane rows),
@@ -763,7 +680,8 @@ __global__ __launch_bounds__(256) void kivi_decode_kernel(KiviArgs a) {
     lds_l[wave][lane] = lsum;
   }
   __syncthreads();
-  write_split_state<D, G>(a, unit, b, kvh, split, lds_m, lds_l, lds_o);
+  write_split_state<D, G, kWavesPerWG>(a.partials, a.out, a.Hq, unit, b, kvh, split, a.total_splits, lds_m,
+                                       lds_l, lds_o);
 }
 
 // ---------------------------------------------------------------- host side
@@ -797,8 +715,7 @@ int make_plan(const dqa_kivi_cache* c, Plan* p) {
   if (want > kMaxSplitsMerge - 1) want = kMaxSplitsMerge - 1;
   if (want < 1) want = 1;
   p->total = static_cast<int>(want);
-  // at least 256 bytes, so that 0 always means an invalid shape
-  p->ws_bytes = p->total == 1 ? 256 : p->units * static_cast<size_t>(p->total) * p->G * (c->d + 2) * sizeof(float);
+  p->ws_bytes = partial_state_bytes(p->units, p->total, p->G, c->d);
   return DQA_OK;
 }
 
@@ -822,14 +739,6 @@ void launch_decode(const KiviArgs& a, int G, int bits, bool rope, dim3 grid, hip
   if (bits == 2) launch_bits<D, 2>(a, G, rope, grid, s);
   else if (bits == 4) launch_bits<D, 4>(a, G, rope, grid, s);
   else launch_bits<D, 8>(a, G, rope, grid, s);
-}
-
-template <int D>
-void launch_merge(const float* partials, int total, int Hq, int Hkv, int G, int B, float* out, hipStream_t s) {
-  const dim3 grid(G * (D / 64), Hkv, B);
-  if (G == 1) hipLaunchKernelGGL((kivi_merge_kernel<D, 1>), grid, dim3(64), 0, s, partials, total, Hq, Hkv, out);
-  else if (G == 2) hipLaunchKernelGGL((kivi_merge_kernel<D, 2>), grid, dim3(64), 0, s, partials, total, Hq, Hkv, out);
-  else hipLaunchKernelGGL((kivi_merge_kernel<D, 4>), grid, dim3(64), 0, s, partials, total, Hq, Hkv, out);
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -919,10 +828,8 @@ extern "C" int decode_attention_qkv_merge(const dqa_kivi_cache* c, const void* w
   if (p.total == 1) return DQA_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const float* parts = static_cast<const float*>(ws);
-  if (c->d == 128) launch_merge<128>(parts, p.total, c->Hq, c->Hkv, p.G, c->B, out, s);
-  else launch_merge<64>(parts, p.total, c->Hq, c->Hkv, p.G, c->B, out, s);
-  DQA_CHECK_LAUNCH();
-  return DQA_OK;
+  if (c->d == 128) return launch_split_merge<128>(parts, p.total, c->B, c->Hq, c->Hkv, out, s);
+  return launch_split_merge<64>(parts, p.total, c->B, c->Hq, c->Hkv, out, s);
 }
 
 extern "C" int decode_attention_qkv(const uint16_t* q, const dqa_kivi_cache* c,

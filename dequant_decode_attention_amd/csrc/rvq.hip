@@ -21,6 +21,7 @@
 // exact ties go to the lowest index.  The residual stays in registers in the
 // MFMA A-operand layout and is updated in fp32 after each stage.
 #include "common.h"
+#include "merge.h"
 
 namespace dqa {
 namespace {
@@ -236,7 +237,6 @@ struct RvqDecArgs {
   const uint16_t* v_cb;
   float* out;
   float* partials;
-  unsigned* tickets;
   int Hq, Hkv, T, N, Kc, n_tiles, tiles_per_split, splits;
   float q_scale;
 };
@@ -264,12 +264,12 @@ __device__ __forceinline__ void rebuild16(const uint16_t* cb, const int16_t* idx
 }
 
 // Lane = (token j of 8, 16-channel chunk ck of 8); 32-token tiles; online
-// softmax per tile; the same ticketed split merge as the uniform decoder.
+// softmax per tile; each split writes its partial state, merged by
+// split_merge_kernel (merge.h) in split order.
 template <int G>
 __global__ __launch_bounds__(256) void rvq_decode_kernel(RvqDecArgs a) {
   constexpr int NCK = 8, TL = 8, IT = 4;
   __shared__ float lds_m[kDecWaves][G], lds_l[kDecWaves][G], lds_o[kDecWaves][G][kD];
-  __shared__ int lds_last;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int j = lane / NCK, ck = lane % NCK, c0 = 16 * ck;
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
@@ -369,59 +369,13 @@ __global__ __launch_bounds__(256) void rvq_decode_kernel(RvqDecArgs a) {
     }
   }
   __syncthreads();
-  float* part = a.partials + (unit * a.splits + split) * G * (kD + 2);
-  for (int e = threadIdx.x; e < G * kD; e += blockDim.x) {
-    const int h = e / kD, c = e % kD;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, lds_m[w][h]);
-    float L = 0.0f, O = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kDecWaves; ++w) {
-      const float wt = merge_weight(lds_m[w][h], M);
-      L = fmaf(lds_l[w][h], wt, L);
-      O = fmaf(lds_o[w][h][c], wt, O);
-    }
-    if (a.splits == 1) {
-      a.out[(static_cast<size_t>(b) * a.Hq + kvh * G + h) * kD + c] = (L > 0.0f) ? O / L : 0.0f;
-    } else {
-      if (c == 0) {
-        part[h * (kD + 2)] = M;
-        part[h * (kD + 2) + 1] = L;
-      }
-      part[h * (kD + 2) + 2 + c] = O;
-    }
-  }
-  if (a.splits == 1) return;
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const unsigned prev = atomicAdd(a.tickets + unit, 1u);
-    lds_last = (prev == static_cast<unsigned>(a.splits - 1));
-  }
-  __syncthreads();
-  if (!lds_last) return;
-  __threadfence();
-  const float* parts = a.partials + unit * a.splits * G * (kD + 2);
-  for (int e = threadIdx.x; e < G * kD; e += blockDim.x) {
-    const int h = e / kD, c = e % kD;
-    float M = -INFINITY;
-    for (int s = 0; s < a.splits; ++s) M = fmaxf(M, parts[(s * G + h) * (kD + 2)]);
-    float L = 0.0f, O = 0.0f;
-    for (int s = 0; s < a.splits; ++s) {
-      const float* ps = parts + (s * G + h) * (kD + 2);
-      const float wt = merge_weight(ps[0], M);
-      L = fmaf(ps[1], wt, L);
-      O = fmaf(ps[2 + c], wt, O);
-    }
-    a.out[(static_cast<size_t>(b) * a.Hq + kvh * G + h) * kD + c] = (L > 0.0f) ? O / L : 0.0f;
-  }
-  if (threadIdx.x == 0) a.tickets[unit] = 0u;
+  write_split_state<kD, G, kDecWaves>(a.partials, a.out, a.Hq, unit, b, kvh, split, a.splits, lds_m, lds_l,
+                                      lds_o);
 }
 
 struct RvqGeometry {
   int G, n_tiles, tps, splits;
-  size_t units, ticket_bytes, ws_bytes;
+  size_t units, ws_bytes;
 };
 
 int rvq_geometry(int B, int Hq, int Hkv, int T, int d, RvqGeometry* g) {
@@ -435,11 +389,11 @@ int rvq_geometry(int B, int Hq, int Hkv, int T, int d, RvqGeometry* g) {
   long long s = (kTargetWorkgroups + static_cast<long long>(g->units) - 1) /
                 static_cast<long long>(g->units > 0 ? g->units : 1);
   if (s > g->n_tiles) s = g->n_tiles;
+  if (s > kMaxSplitsMerge - 1) s = kMaxSplitsMerge - 1;
   if (s < 1) s = 1;
   g->tps = g->n_tiles > 0 ? static_cast<int>((g->n_tiles + s - 1) / s) : 1;
   g->splits = g->n_tiles > 0 ? (g->n_tiles + g->tps - 1) / g->tps : 1;
-  g->ticket_bytes = (g->units * 4 + 255) / 256 * 256;
-  g->ws_bytes = g->ticket_bytes + g->units * g->splits * g->G * (kD + 2) * sizeof(float);
+  g->ws_bytes = partial_state_bytes(g->units, g->splits, g->G, kD);
   return DQA_OK;
 }
 
@@ -499,8 +453,7 @@ extern "C" int rvq_decode_attention(const uint16_t* q, int B, int Hq, int Hkv, i
   a.k_cb = k_cb;
   a.v_cb = v_cb;
   a.out = out;
-  a.tickets = static_cast<unsigned*>(ws);
-  a.partials = reinterpret_cast<float*>(static_cast<char*>(ws) + g.ticket_bytes);
+  a.partials = static_cast<float*>(ws);
   a.Hq = Hq;
   a.Hkv = Hkv;
   a.T = T;
@@ -520,5 +473,5 @@ extern "C" int rvq_decode_attention(const uint16_t* q, int B, int Hq, int Hkv, i
     default: return DQA_ERR_UNSUPPORTED;
   }
   DQA_CHECK_LAUNCH();
-  return DQA_OK;
+  return launch_split_merge<kD>(a.partials, g.splits, B, Hq, Hkv, out, s);
 }

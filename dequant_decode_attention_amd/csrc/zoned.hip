@@ -23,6 +23,7 @@
 //   zone B = [P_16][d] fp16 value rows of segment 16; zone C = keys [C][d],
 //   then values [C][d], fp16.
 #include "common.h"
+#include "merge.h"
 
 namespace dqa {
 namespace {
@@ -246,7 +247,6 @@ struct ZDecodeArgs {
   const uint16_t* q;
   float* out;
   float* partials;
-  unsigned* tickets;
   int Hq, Hkv, C, items_per_split, splits;
   float q_scale;
 };
@@ -259,7 +259,6 @@ __global__ __launch_bounds__(256) void zoned_decode_kernel(ZDecodeArgs a) {
   __shared__ float lds_qp[G][D], lds_qn[G][D];      // query: permuted / natural order
   __shared__ float lds_p[kZWaves][kGroup][G];
   __shared__ float lds_m[kZWaves][G], lds_l[kZWaves][G], lds_o[kZWaves][G][D];
-  __shared__ int lds_last;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int split = blockIdx.x, unit = blockIdx.y;
   const int b = unit / a.Hkv, kvh = unit % a.Hkv;
@@ -459,59 +458,13 @@ __global__ __launch_bounds__(256) void zoned_decode_kernel(ZDecodeArgs a) {
     }
   }
   __syncthreads();
-  float* part = a.partials + (static_cast<size_t>(unit) * a.splits + split) * G * (D + 2);
-  for (int e = threadIdx.x; e < G * D; e += blockDim.x) {
-    const int h = e / D, c = e % D;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kZWaves; ++w) M = fmaxf(M, lds_m[w][h]);
-    float L = 0.0f, O = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kZWaves; ++w) {
-      const float wt = merge_weight(lds_m[w][h], M);
-      L = fmaf(lds_l[w][h], wt, L);
-      O = fmaf(lds_o[w][h][c], wt, O);
-    }
-    if (a.splits == 1) {
-      a.out[(static_cast<size_t>(b) * a.Hq + kvh * G + h) * D + c] = (L > 0.0f) ? O / L : 0.0f;
-    } else {
-      if (c == 0) {
-        part[h * (D + 2)] = M;
-        part[h * (D + 2) + 1] = L;
-      }
-      part[h * (D + 2) + 2 + c] = O;
-    }
-  }
-  if (a.splits == 1) return;
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const unsigned prev = atomicAdd(a.tickets + unit, 1u);
-    lds_last = (prev == static_cast<unsigned>(a.splits - 1));
-  }
-  __syncthreads();
-  if (!lds_last) return;
-  __threadfence();
-  const float* parts = a.partials + static_cast<size_t>(unit) * a.splits * G * (D + 2);
-  for (int e = threadIdx.x; e < G * D; e += blockDim.x) {
-    const int h = e / D, c = e % D;
-    float M = -INFINITY;
-    for (int s = 0; s < a.splits; ++s) M = fmaxf(M, parts[(s * G + h) * (D + 2)]);
-    float L = 0.0f, O = 0.0f;
-    for (int s = 0; s < a.splits; ++s) {
-      const float* ps = parts + (s * G + h) * (D + 2);
-      const float wt = merge_weight(ps[0], M);
-      L = fmaf(ps[1], wt, L);
-      O = fmaf(ps[2 + c], wt, O);
-    }
-    a.out[(static_cast<size_t>(b) * a.Hq + kvh * G + h) * D + c] = (L > 0.0f) ? O / L : 0.0f;
-  }
-  if (threadIdx.x == 0) a.tickets[unit] = 0u;
+  write_split_state<D, G, kZWaves>(a.partials, a.out, a.Hq, static_cast<size_t>(unit), b, kvh, split, a.splits,
+                                   lds_m, lds_l, lds_o);
 }
 
 struct ZGeometry {
   int G, units, items_max, ips, splits;
-  size_t ticket_bytes, ws_bytes;
+  size_t ws_bytes;
 };
 
 int zoned_geometry(const int32_t* p, int Hq, ZGeometry* g) {
@@ -525,12 +478,11 @@ int zoned_geometry(const int32_t* p, int Hq, ZGeometry* g) {
   g->items_max = p[H_MAX_GROUPS] + (p[H_C] + kGroup - 1) / kGroup;
   long long s = (kTargetWorkgroups + g->units - 1) / (g->units > 0 ? g->units : 1);
   if (s > g->items_max) s = g->items_max;
+  if (s > kMaxSplitsMerge - 1) s = kMaxSplitsMerge - 1;
   if (s < 1) s = 1;
   g->ips = g->items_max > 0 ? static_cast<int>((g->items_max + s - 1) / s) : 1;
   g->splits = g->items_max > 0 ? (g->items_max + g->ips - 1) / g->ips : 1;
-  g->ticket_bytes = pad(static_cast<size_t>(g->units) * 4, 256);
-  g->ws_bytes = g->ticket_bytes +
-                static_cast<size_t>(g->units) * g->splits * g->G * (p[H_D] + 2) * sizeof(float);
+  g->ws_bytes = partial_state_bytes(static_cast<size_t>(g->units), g->splits, g->G, p[H_D]);
   return DQA_OK;
 }
 
@@ -704,8 +656,7 @@ extern "C" int decode_attention_zoned(const uint16_t* q, int Hq, const int32_t* 
   a.blob = static_cast<const uint8_t*>(blob);
   a.q = q;
   a.out = out;
-  a.tickets = static_cast<unsigned*>(ws);
-  a.partials = reinterpret_cast<float*>(static_cast<char*>(ws) + g.ticket_bytes);
+  a.partials = static_cast<float*>(ws);
   a.Hq = Hq;
   a.Hkv = plan_host[H_HKV];
   a.C = plan_host[H_C];
@@ -714,6 +665,11 @@ extern "C" int decode_attention_zoned(const uint16_t* q, int Hq, const int32_t* 
   a.q_scale = sm_scale * 1.4426950408889634f;
   const dim3 grid(g.splits, g.units);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (plan_host[H_D] == 128) return zlaunch<128>(a, g.G, grid, s);
-  return zlaunch<64>(a, g.G, grid, s);
+  const int B = plan_host[H_B];
+  if (plan_host[H_D] == 128) {
+    st = zlaunch<128>(a, g.G, grid, s);
+    return st != DQA_OK ? st : launch_split_merge<128>(a.partials, g.splits, B, Hq, a.Hkv, out, s);
+  }
+  st = zlaunch<64>(a, g.G, grid, s);
+  return st != DQA_OK ? st : launch_split_merge<64>(a.partials, g.splits, B, Hq, a.Hkv, out, s);
 }

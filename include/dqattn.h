@@ -205,14 +205,15 @@ int zoned_pack(const int32_t* plan_host, const int32_t* plan_dev,
                const uint16_t* k, const uint16_t* v, const uint16_t* k_new,
                const uint16_t* v_new, void* blob, void* stream);
 
-/* Workspace bytes for decode_attention_zoned (0 if invalid); same counter
- * convention as decode_attention_workspace_bytes. */
+/* Workspace bytes for decode_attention_zoned (0 if invalid; at least 256
+ * otherwise): partial softmax states, no initialization needed. */
 size_t decode_attention_zoned_workspace_bytes(const int32_t* plan_host, int Hq);
 
 /* Decode attention over zones A (kept tokens, masked slots skipped), B and
  * C, with dequantization fused into the products.
  *   q (device) fp16 [B][Hq][d], Hq a multiple of Hkv (ratio as above)
  *   out (device) fp32 [B][Hq][d]
+ * Enqueues the split kernel and, with several splits, their merge.
  * Errors: DQA_ERR_NULL, DQA_ERR_PLAN, DQA_ERR_SHAPE, DQA_ERR_WORKSPACE,
  * DQA_ERR_UNSUPPORTED, DQA_ERR_HIP. */
 int decode_attention_zoned(const uint16_t* q, int Hq, const int32_t* plan_host,
@@ -236,7 +237,7 @@ size_t rvq_encode_workspace_bytes(int N, int Kc);
 
 /* Encode n vectors.
  *   x         (device) fp16 [n][d], d == 128
- *   codebooks (device) fp16 [N][Kc][d], 1 <= N <= 8, 16 <= Kc <= 32768, Kc % 16 == 0
+ *   codebooks (device) fp16 [N][Kc][d], 1 <= N <= 8, 64 <= Kc <= 32768, Kc % 64 == 0
  *   idx       (device) int16 [n][N]
  *   ws        (device) >= rvq_encode_workspace_bytes(N, Kc)
  * Errors: DQA_ERR_NULL, DQA_ERR_SHAPE, DQA_ERR_WORKSPACE, DQA_ERR_HIP. */
@@ -244,8 +245,8 @@ int rvq_encode(const uint16_t* x, int64_t n, int d, const uint16_t* codebooks,
                int N, int Kc, int16_t* idx, void* ws, size_t ws_bytes,
                void* stream);
 
-/* Workspace bytes for rvq_decode_attention (same counter convention as
- * decode_attention_workspace_bytes). */
+/* Workspace bytes for rvq_decode_attention (0 if invalid; at least 256
+ * otherwise): partial softmax states, no initialization needed. */
 size_t rvq_decode_attention_workspace_bytes(int B, int Hq, int Hkv, int T, int d);
 
 /* Decode attention with keys and values rebuilt on the fly from their
@@ -254,6 +255,7 @@ size_t rvq_decode_attention_workspace_bytes(int B, int Hq, int Hkv, int T, int d
  *   q (device) fp16 [B][Hq][d]; k_idx, v_idx (device) int16 [B][Hkv][T][N]
  *   k_codebooks, v_codebooks (device) fp16 [N][Kc][d]
  *   out (device) fp32 [B][Hq][d]
+ * Enqueues the split kernel and, with several splits, their merge.
  * Errors: DQA_ERR_NULL, DQA_ERR_SHAPE, DQA_ERR_WORKSPACE,
  * DQA_ERR_UNSUPPORTED, DQA_ERR_HIP. */
 int rvq_decode_attention(const uint16_t* q, int B, int Hq, int Hkv, int T,
