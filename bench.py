@@ -37,7 +37,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E, published
-KERNEL_SOURCE = os.path.join(ROOT, "dequant_decode_attention_amd", "csrc", "decode_kivi.hip")
+KERNEL_SOURCES = [os.path.join(ROOT, "dequant_decode_attention_amd", "csrc", f)
+                  for f in ("decode_kivi.hip", "merge.h", "common.h")]
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "kivi_decode_kernel_llama8b_gqa_32k_traffic.md")
 
 
@@ -56,7 +57,7 @@ def measured_traffic(bits):
         if line.startswith("- ") and ":" in line:
             k, v = line[2:].split(":", 1)
             fields[k.strip()] = v.strip().strip("`")
-    src = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+    src = hashlib.sha256(b"".join(open(f, "rb").read() for f in KERNEL_SOURCES)).hexdigest()
     if fields.get("kernel_source_sha256") != src:
         return None
     key = f"traffic_bytes_per_launch_{bits}bit"

@@ -98,6 +98,9 @@ DECODE_CASES = [
     (1, 4, 1, 128, 0, 100, 2, 500000.0),    # only recent tokens
     (1, 4, 1, 128, 4096, 0, 2, 500000.0),   # many tiles -> many splits
     (2, 2, 1, 128, 0, 0, 2, 0.0),           # empty cache -> zeros
+    (1, 4, 1, 128, 32768, 128, 2, 500000.0),  # one unit: split cap, recent tiles in 4 waves
+    (2, 4, 1, 64, 192, 70, 8, 10000.0),     # d 64, 8 bits, RoPE, 3 ragged recent tiles
+    (1, 4, 2, 128, 640, 31, 4, 0.0),        # G 2, 4 bits, no RoPE, ragged recent zone
 ]
 
 
