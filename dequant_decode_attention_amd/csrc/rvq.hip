@@ -18,10 +18,12 @@
 // buffered, shared by the 8 waves of the workgroup.  Each lane keeps a
 // running (key, index) minimum for its output rows (strict < over
 // increasing codeword index, then a lexicographic cross-lane reduction), so
-// exact ties go to the lowest index.  The residual stays in registers in the
-// MFMA A-operand layout and is updated in fp32 after each stage.
+// exact ties go to the lowest index.  The fp32 residual is rebuilt in the
+// MFMA A-operand layout at the start of each stage.
 #include "common.h"
 #include "merge.h"
+
+#include <type_traits>
 
 namespace dqa {
 namespace {
@@ -34,6 +36,7 @@ constexpr int kEncRows = 256;        // vectors per workgroup
 constexpr int kEncWaves = 8;         // 32 rows (2 MFMA row blocks) per wave
 constexpr int kTileCW = 64;          // codewords per LDS tile
 constexpr int kRowPad = kD + 8;      // LDS row stride in halves (bank spread)
+constexpr int kMaxStages = 8;        // codebooks per vector at most
 
 __global__ __launch_bounds__(256) void rvq_norms_kernel(const uint16_t* __restrict__ cb, size_t n_cw,
                                                         float* __restrict__ norms) {
@@ -63,44 +66,54 @@ __global__ __launch_bounds__(512) void rvq_encode_kernel(const uint16_t* __restr
                                                          const float* __restrict__ norms, int N,
                                                          int Kc, int16_t* __restrict__ idx_out) {
   __shared__ __attribute__((aligned(16))) _Float16 lds_cb[2][kTileCW][kRowPad];
-  __shared__ float lds_norm[2][kTileCW];
-  __shared__ int lds_idx[kEncWaves][32];
+  __shared__ int16_t lds_idx[kEncWaves][kMaxStages][32];   // chosen indices, per stage
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
   const int64_t row_base = static_cast<int64_t>(blockIdx.x) * kEncRows + wave * 32;
 
-  // residual in A-operand layout: row = row_base + 16*mb + col, channels
-  // 32*ks + 8*grp + 0..7
-  float res[2][4][8];
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
-    const int64_t row = row_base + 16 * mb + col;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      if (row < n) {
-        const uint4 u = *reinterpret_cast<const uint4*>(x + row * kD + 32 * ks + 8 * grp);
-        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          res[mb][ks][2 * j] = h2f(static_cast<uint16_t>(w[j] & 0xFFFFu));
-          res[mb][ks][2 * j + 1] = h2f(static_cast<uint16_t>(w[j] >> 16));
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) res[mb][ks][j] = 0.0f;
-      }
-    }
-  }
-
+  // The residual of stage s is rebuilt at the start of the stage from x and
+  // the codewords chosen at stages 0..s-1, subtracted in stage order -- the
+  // same fp32 operations, in the same order, as one running update -- so it
+  // holds no registers while the codeword tiles stream through.  Layout is
+  // the MFMA A operand's: row = row_base + 16*mb + col, channels
+  // 32*ks + 8*grp + 0..7.
   const int n_tiles = Kc / kTileCW;
   for (int s = 0; s < N; ++s) {
     const uint16_t* cb = cbs + static_cast<size_t>(s) * Kc * kD;
     const float* nrm = norms + static_cast<size_t>(s) * Kc;
     half8 ahi[2][4], alo[2][4];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < 2; ++mb) {
+      const int64_t row = row_base + 16 * mb + col;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) split_neg2(res[mb][ks], ahi[mb][ks], alo[mb][ks]);
+      for (int ks = 0; ks < 4; ++ks) {
+        float r[8];
+        if (row < n) {
+          const uint4 u = *reinterpret_cast<const uint4*>(x + row * kD + 32 * ks + 8 * grp);
+          const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            r[2 * j] = h2f(static_cast<uint16_t>(w[j] & 0xFFFFu));
+            r[2 * j + 1] = h2f(static_cast<uint16_t>(w[j] >> 16));
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) r[j] = 0.0f;
+        }
+        for (int sp = 0; sp < s; ++sp) {
+          const int ci = lds_idx[wave][sp][16 * mb + col];
+          const uint4 u = *reinterpret_cast<const uint4*>(cbs + (static_cast<size_t>(sp) * Kc + ci) * kD +
+                                                          32 * ks + 8 * grp);
+          const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            r[2 * j] -= h2f(static_cast<uint16_t>(w[j] & 0xFFFFu));
+            r[2 * j + 1] -= h2f(static_cast<uint16_t>(w[j] >> 16));
+          }
+        }
+        split_neg2(r, ahi[mb][ks], alo[mb][ks]);
+      }
+    }
     float bestk[2][4];
     int besti[2][4];
 #pragma unroll
@@ -111,68 +124,127 @@ __global__ __launch_bounds__(512) void rvq_encode_kernel(const uint16_t* __restr
         besti[mb][r] = 0;
       }
 
-    // tile 0 -> LDS buffer 0
-    uint4 pre[2];
-    auto gload = [&](int t) {
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int c = tid * 2 + q;                 // 16-byte chunk of the tile
-        pre[q] = *reinterpret_cast<const uint4*>(cb + (static_cast<size_t>(t) * kTileCW + c / 16) * kD + (c % 16) * 8);
-      }
+    // codeword tiles: thread tid moves 16-byte chunks 2*tid and 2*tid+1 of
+    // a 64-codeword tile (global -> registers -> LDS buffer); the tile after
+    // next is in flight while the current tile is consumed.  The norms |c|^2
+    // of the lane's 4 codeword columns come straight from global memory,
+    // one tile ahead.
+    const int ch0 = 2 * tid, ch1 = 2 * tid + 1;
+    auto gchunk = [&](int t, int c) {
+      return *reinterpret_cast<const uint4*>(cb + (static_cast<size_t>(t) * kTileCW + c / 16) * kD + (c % 16) * 8);
     };
-    auto lstore = [&](int buf, int t) {
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int c = tid * 2 + q;
-        *reinterpret_cast<uint4*>(&lds_cb[buf][c / 16][(c % 16) * 8]) = pre[q];
-      }
-      if (tid < kTileCW) lds_norm[buf][tid] = nrm[t * kTileCW + tid];
+    auto lstore = [&](int buf, uint4 u0, uint4 u1) {
+      *reinterpret_cast<uint4*>(&lds_cb[buf][ch0 / 16][(ch0 % 16) * 8]) = u0;
+      *reinterpret_cast<uint4*>(&lds_cb[buf][ch1 / 16][(ch1 % 16) * 8]) = u1;
     };
-    gload(0);
-    lstore(0, 0);
+    auto gnorms = [&](int t, float (&nv)[4]) {
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) nv[nb] = nrm[t * kTileCW + 16 * nb + col];
+    };
+    lstore(0, gchunk(0, ch0), gchunk(0, ch1));
     __syncthreads();
-    for (int t = 0; t < n_tiles; ++t) {
-      const int buf = t & 1;
-      if (t + 1 < n_tiles) gload(t + 1);
-      float4v acc[2][4];
+    // A codeword tile is consumed in two halves of 32 codewords (4 output
+    // blocks: 2 row blocks x 2 codeword blocks).  Keys are |c|^2 - 2 r.c,
+    // the accumulator starting at |c|^2.  The running minimum of one half
+    // (plain VALU) is interleaved with the matrix-core products of the next
+    // half, and each half's codeword fragments are read from LDS one half
+    // ahead; one barrier per tile guards the double-buffered LDS tile.
+    // Stage 0 (exact fp16 residual) has no low part.
+    auto read_half = [&](half8 (&bf)[2][4], int buf, int h) {
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const float nv = lds_norm[buf][16 * nb + col];
+      for (int nh = 0; nh < 2; ++nh)
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) acc[mb][nb] = float4v{nv, nv, nv, nv};
-      }
+        for (int ks = 0; ks < 4; ++ks)
+          bf[nh][ks] = *reinterpret_cast<const half8*>(&lds_cb[buf][16 * (2 * h + nh) + col][32 * ks + 8 * grp]);
+    };
+    auto init_acc = [&](float4v (&acc)[2][2], const float (&nv)[4], int h) {
+#pragma unroll
+      for (int nh = 0; nh < 2; ++nh)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          const float v = nv[2 * h + nh];
+          acc[mb][nh] = float4v{v, v, v, v};
+        }
+    };
+    auto products = [&](float4v (&acc)[2][2], const half8 (&bf)[2][4], auto lo_tag) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          const half8 bf = *reinterpret_cast<const half8*>(&lds_cb[buf][16 * nb + col][32 * ks + 8 * grp]);
+        for (int nh = 0; nh < 2; ++nh)
 #pragma unroll
           for (int mb = 0; mb < 2; ++mb)
-            acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[mb][ks], bf, acc[mb][nb], 0, 0, 0);
-          if (s > 0) {
+            acc[mb][nh] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[mb][ks], bf[nh][ks], acc[mb][nh], 0, 0, 0);
+        if constexpr (decltype(lo_tag)::value) {
+#pragma unroll
+          for (int nh = 0; nh < 2; ++nh)
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
-              acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[mb][ks], bf, acc[mb][nb], 0, 0, 0);
-          }
+              acc[mb][nh] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[mb][ks], bf[nh][ks], acc[mb][nh], 0, 0, 0);
         }
       }
+    };
+    // codewords visited in increasing index order per (row, lane): strict <
+    // keeps the lowest index of equal keys
+    auto running_min = [&](const float4v (&acc)[2][2], int cw0) {
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const int cw = t * kTileCW + 16 * nb + col;
+      for (int nh = 0; nh < 2; ++nh) {
+        const int cw = cw0 + 16 * nh + col;
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float key = acc[mb][nb][r];
-            if (key < bestk[mb][r]) {
-              bestk[mb][r] = key;
-              besti[mb][r] = cw;
-            }
+            const float key = acc[mb][nh][r];
+            const bool better = key < bestk[mb][r];
+            besti[mb][r] = better ? cw : besti[mb][r];
+            bestk[mb][r] = better ? key : bestk[mb][r];
           }
       }
-      if (t + 1 < n_tiles) lstore(buf ^ 1, t + 1);
-      __syncthreads();
-    }
+    };
+    // interleave: one product, then `per` VALU instructions, `n` times
+    auto interleave = [](auto n_tag, auto per_tag) {
+#pragma unroll
+      for (int i = 0; i < decltype(n_tag)::value; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, decltype(per_tag)::value, 0);
+      }
+    };
+    auto tiles = [&](auto lo_tag) {
+      constexpr bool LO = decltype(lo_tag)::value;
+      constexpr int kProducts = LO ? 32 : 16;     // per half tile
+      half8 bf0[2][4], bf1[2][4];
+      float4v acc0[2][2], acc1[2][2];
+      float nv[4];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nh = 0; nh < 2; ++nh) acc1[mb][nh] = float4v{INFINITY, INFINITY, INFINITY, INFINITY};
+      gnorms(0, nv);
+      uint4 u0 = gchunk(min(1, n_tiles - 1), ch0), u1 = gchunk(min(1, n_tiles - 1), ch1);
+      read_half(bf0, 0, 0);
+      for (int t = 0; t < n_tiles; ++t) {
+        const int buf = t & 1;
+        const int tn = min(t + 1, n_tiles - 1), t2 = min(t + 2, n_tiles - 1);
+        read_half(bf1, buf, 1);
+        init_acc(acc0, nv, 0);
+        products(acc0, bf0, lo_tag);
+        // before tile 0, acc1 holds +inf: no update
+        running_min(acc1, (t - 1) * kTileCW + 32);
+        lstore(buf ^ 1, u0, u1);                   // tile t+1 (the final tile rewrites a dead buffer)
+        u0 = gchunk(t2, ch0);
+        u1 = gchunk(t2, ch1);
+        init_acc(acc1, nv, 1);
+        gnorms(tn, nv);
+        products(acc1, bf1, lo_tag);
+        running_min(acc0, t * kTileCW);
+        interleave(std::integral_constant<int, kProducts>{}, std::integral_constant<int, LO ? 2 : 3>{});
+        interleave(std::integral_constant<int, kProducts>{}, std::integral_constant<int, LO ? 2 : 3>{});
+        __syncthreads();
+        if (t + 1 < n_tiles) read_half(bf0, buf ^ 1, 0);
+      }
+      running_min(acc1, (n_tiles - 1) * kTileCW + 32);
+    };
+    if (s == 0) tiles(std::false_type{});
+    else tiles(std::true_type{});
 
     // lexicographic (key, index) minimum across the 16 lanes of a row group
 #pragma unroll
@@ -198,30 +270,15 @@ __global__ __launch_bounds__(512) void rvq_encode_kernel(const uint16_t* __restr
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int local = 16 * mb + 4 * grp + r;
-          lds_idx[wave][local] = besti[mb][r];
+          lds_idx[wave][s][local] = static_cast<int16_t>(besti[mb][r]);
           const int64_t row = row_base + local;
           if (row < n) idx_out[row * N + s] = static_cast<int16_t>(besti[mb][r]);
         }
     }
+    // the next stage reads this stage's indices from LDS (same wave)
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // residual update in fp32: r <- r - C_s[idx]
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      const int ci = lds_idx[wave][16 * mb + col];
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const uint4 u = *reinterpret_cast<const uint4*>(cb + static_cast<size_t>(ci) * kD + 32 * ks + 8 * grp);
-        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          res[mb][ks][2 * j] -= h2f(static_cast<uint16_t>(w[j] & 0xFFFFu));
-          res[mb][ks][2 * j + 1] -= h2f(static_cast<uint16_t>(w[j] >> 16));
-        }
-      }
-    }
-    __builtin_amdgcn_wave_barrier();
   }
 }
 
@@ -403,14 +460,14 @@ int rvq_geometry(int B, int Hq, int Hkv, int T, int d, RvqGeometry* g) {
 using namespace dqa;
 
 extern "C" size_t rvq_encode_workspace_bytes(int N, int Kc) {
-  if (N < 1 || N > 8 || Kc < kTileCW || Kc > 32768 || Kc % kTileCW != 0) return 0;
+  if (N < 1 || N > kMaxStages || Kc < kTileCW || Kc > 32768 || Kc % kTileCW != 0) return 0;
   return static_cast<size_t>(N) * Kc * sizeof(float);
 }
 
 extern "C" int rvq_encode(const uint16_t* x, int64_t n, int d, const uint16_t* codebooks, int N,
                           int Kc, int16_t* idx, void* ws, size_t ws_bytes, void* stream) {
   if (n < 0 || d != kD) return DQA_ERR_SHAPE;
-  if (N < 1 || N > 8 || Kc < kTileCW || Kc > 32768 || Kc % kTileCW != 0) return DQA_ERR_SHAPE;
+  if (N < 1 || N > kMaxStages || Kc < kTileCW || Kc > 32768 || Kc % kTileCW != 0) return DQA_ERR_SHAPE;
   if (n == 0) return DQA_OK;
   if (!x || !codebooks || !idx) return DQA_ERR_NULL;
   if (!ws || ws_bytes < rvq_encode_workspace_bytes(N, Kc)) return DQA_ERR_WORKSPACE;
@@ -441,7 +498,7 @@ extern "C" int rvq_decode_attention(const uint16_t* q, int B, int Hq, int Hkv, i
   RvqGeometry g;
   int st = rvq_geometry(B, Hq, Hkv, T, d, &g);
   if (st != DQA_OK) return st;
-  if (N < 1 || N > 8 || Kc < 1 || Kc > 32768) return DQA_ERR_SHAPE;
+  if (N < 1 || N > kMaxStages || Kc < 1 || Kc > 32768) return DQA_ERR_SHAPE;
   if (g.units == 0) return DQA_OK;
   if (!q || !out) return DQA_ERR_NULL;
   if (T > 0 && (!k_idx || !v_idx || !k_cb || !v_cb)) return DQA_ERR_NULL;
