@@ -82,37 +82,49 @@ __global__ __launch_bounds__(512) void rvq_encode_kernel(const uint16_t* __restr
     const uint16_t* cb = cbs + static_cast<size_t>(s) * Kc * kD;
     const float* nrm = norms + static_cast<size_t>(s) * Kc;
     half8 ahi[2][4], alo[2][4];
+    {
+      // all of a stage's loads of x (or of one earlier stage's codewords)
+      // are issued together: one memory round trip per earlier stage
+      float r[2][4][8];
+      auto add_chunks = [&](const uint16_t* row0, const uint16_t* row1, bool subtract) {
+        uint4 u[2][4];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      const int64_t row = row_base + 16 * mb + col;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        float r[8];
-        if (row < n) {
-          const uint4 u = *reinterpret_cast<const uint4*>(x + row * kD + 32 * ks + 8 * grp);
-          const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            r[2 * j] = h2f(static_cast<uint16_t>(w[j] & 0xFFFFu));
-            r[2 * j + 1] = h2f(static_cast<uint16_t>(w[j] >> 16));
-          }
-        } else {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) r[j] = 0.0f;
+        for (int ks = 0; ks < 4; ++ks) {
+          u[0][ks] = *reinterpret_cast<const uint4*>(row0 + 32 * ks + 8 * grp);
+          u[1][ks] = *reinterpret_cast<const uint4*>(row1 + 32 * ks + 8 * grp);
         }
-        for (int sp = 0; sp < s; ++sp) {
-          const int ci = lds_idx[wave][sp][16 * mb + col];
-          const uint4 u = *reinterpret_cast<const uint4*>(cbs + (static_cast<size_t>(sp) * Kc + ci) * kD +
-                                                          32 * ks + 8 * grp);
-          const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            r[2 * j] -= h2f(static_cast<uint16_t>(w[j] & 0xFFFFu));
-            r[2 * j + 1] -= h2f(static_cast<uint16_t>(w[j] >> 16));
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) {
+            const uint32_t w[4] = {u[mb][ks].x, u[mb][ks].y, u[mb][ks].z, u[mb][ks].w};
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              const float c = h2f(static_cast<uint16_t>(j & 1 ? w[j >> 1] >> 16 : w[j >> 1] & 0xFFFFu));
+              r[mb][ks][j] = subtract ? r[mb][ks][j] - c : c;
+            }
           }
-        }
-        split_neg2(r, ahi[mb][ks], alo[mb][ks]);
+      };
+      // rows past the end of x read row 0 and are zeroed (their indices are
+      // never stored)
+      const bool valid[2] = {row_base + col < n, row_base + 16 + col < n};
+      add_chunks(x + (valid[0] ? row_base + col : 0) * kD, x + (valid[1] ? row_base + 16 + col : 0) * kD, false);
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+        if (!valid[mb])
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) r[mb][ks][j] = 0.0f;
+      for (int sp = 0; sp < s; ++sp) {
+        const uint16_t* cbp = cbs + static_cast<size_t>(sp) * Kc * kD;
+        add_chunks(cbp + static_cast<size_t>(lds_idx[wave][sp][col]) * kD,
+                   cbp + static_cast<size_t>(lds_idx[wave][sp][16 + col]) * kD, true);
       }
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) split_neg2(r[mb][ks], ahi[mb][ks], alo[mb][ks]);
     }
     float bestk[2][4];
     int besti[2][4];
@@ -146,9 +158,10 @@ __global__ __launch_bounds__(512) void rvq_encode_kernel(const uint16_t* __restr
     // A codeword tile is consumed in two halves of 32 codewords (4 output
     // blocks: 2 row blocks x 2 codeword blocks).  Keys are |c|^2 - 2 r.c,
     // the accumulator starting at |c|^2.  The running minimum of one half
-    // (plain VALU) is interleaved with the matrix-core products of the next
-    // half, and each half's codeword fragments are read from LDS one half
-    // ahead; one barrier per tile guards the double-buffered LDS tile.
+    // (plain VALU) sits beside the matrix-core products of the next half in
+    // one straight-line block, so the two overlap; each half's codeword
+    // fragments are read from LDS one half ahead; one barrier per tile
+    // guards the double-buffered LDS tile.
     // Stage 0 (exact fp16 residual) has no low part.
     auto read_half = [&](half8 (&bf)[2][4], int buf, int h) {
 #pragma unroll
@@ -200,17 +213,7 @@ __global__ __launch_bounds__(512) void rvq_encode_kernel(const uint16_t* __restr
           }
       }
     };
-    // interleave: one product, then `per` VALU instructions, `n` times
-    auto interleave = [](auto n_tag, auto per_tag) {
-#pragma unroll
-      for (int i = 0; i < decltype(n_tag)::value; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, decltype(per_tag)::value, 0);
-      }
-    };
     auto tiles = [&](auto lo_tag) {
-      constexpr bool LO = decltype(lo_tag)::value;
-      constexpr int kProducts = LO ? 32 : 16;     // per half tile
       half8 bf0[2][4], bf1[2][4];
       float4v acc0[2][2], acc1[2][2];
       float nv[4];
@@ -236,8 +239,6 @@ __global__ __launch_bounds__(512) void rvq_encode_kernel(const uint16_t* __restr
         gnorms(tn, nv);
         products(acc1, bf1, lo_tag);
         running_min(acc0, t * kTileCW);
-        interleave(std::integral_constant<int, kProducts>{}, std::integral_constant<int, LO ? 2 : 3>{});
-        interleave(std::integral_constant<int, kProducts>{}, std::integral_constant<int, LO ? 2 : 3>{});
         __syncthreads();
         if (t + 1 < n_tiles) read_half(bf0, buf ^ 1, 0);
       }
@@ -268,17 +269,18 @@ __global__ __launch_bounds__(512) void rvq_encode_kernel(const uint16_t* __restr
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int local = 16 * mb + 4 * grp + r;
-          lds_idx[wave][s][local] = static_cast<int16_t>(besti[mb][r]);
-          const int64_t row = row_base + local;
-          if (row < n) idx_out[row * N + s] = static_cast<int16_t>(besti[mb][r]);
-        }
+        for (int r = 0; r < 4; ++r) lds_idx[wave][s][16 * mb + 4 * grp + r] = static_cast<int16_t>(besti[mb][r]);
     }
-    // the next stage reads this stage's indices from LDS (same wave)
+    // the next stage (and the final store) read this stage's indices from
+    // LDS (same wave)
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+  // lane l < 32 stores the N indices of row row_base + l
+  if (lane < 32 && row_base + lane < n) {
+    int16_t* dst = idx_out + (row_base + lane) * N;
+    for (int s = 0; s < N; ++s) dst[s] = lds_idx[wave][s][lane];
   }
 }
 
