@@ -54,6 +54,47 @@ __device__ __forceinline__ float sum_adjacent(float v) {
   return v;
 }
 
+// Max over N adjacent lanes (as sum_adjacent).
+template <int N>
+__device__ __forceinline__ float max_adjacent(float v) {
+  if constexpr (N >= 2) v = fmaxf(v, dpp<kDppQuadXor1>(v));
+  if constexpr (N >= 4) v = fmaxf(v, dpp<kDppQuadXor2>(v));
+  if constexpr (N >= 8) v = fmaxf(v, dpp<kDppHalfMirror>(v));
+  if constexpr (N >= 16) v = fmaxf(v, dpp<kDppRowMirror>(v));
+  return v;
+}
+
+// Combine lane L with lane L ^ 32 (rows32) or L ^ 16 through the VALU
+// row-swap permutes; every lane gets the result.  The two values returned by
+// the permute are copied into scalars before they are reinterpreted (a bit
+// cast of an element of the returned vector reads element 0).
+template <bool MAX>
+__device__ __forceinline__ float swap_rows(float v, bool rows32) {
+  const unsigned x = __builtin_bit_cast(unsigned, v);
+  unsigned r0, r1;
+  if (rows32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    r0 = r[0];
+    r1 = r[1];
+  } else {
+    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    r0 = r[0];
+    r1 = r[1];
+  }
+  const float f0 = __builtin_bit_cast(float, r0), f1 = __builtin_bit_cast(float, r1);
+  return MAX ? fmaxf(f0, f1) : f0 + f1;
+}
+
+// Sum / max over all 64 lanes, and sum over each 32-lane half; every lane
+// gets the result.  Call with the whole wave active.
+__device__ __forceinline__ float wave_sum(float v) {
+  return swap_rows<false>(swap_rows<false>(sum_adjacent<16>(v), true), false);
+}
+__device__ __forceinline__ float wave_max(float v) {
+  return swap_rows<true>(swap_rows<true>(max_adjacent<16>(v), true), false);
+}
+__device__ __forceinline__ float half_sum(float v) { return swap_rows<false>(sum_adjacent<16>(v), false); }
+
 // Wave-wide reduction over lanes with stride S (S a power of two): every
 // lane ends with the reduction over its residue class lane % S.
 template <int S>

@@ -239,7 +239,13 @@ __global__ __launch_bounds__(128) void zoned_pack_kernel(PackArgs a) {
 // ------------------------------------------------------------------ reader
 
 constexpr int kZWaves = 4;
-constexpr int kStageBytes = 16384;   // >= the largest group (d = 128): 13312 B
+// Workgroups per launch: one resident round (two workgroups of four waves
+// per compute unit on 256 CUs), so every wave pays its start-up once.
+constexpr int kZoneWorkgroups = 512;
+// Staging bytes per wave: a zone-A group's key block (at most 8,480 B for
+// d = 128: 32 key rows of at most 66 words, then scales and zeros), or a
+// zone-C chunk's fp16 keys (8 KiB).  The host checks every unit against it.
+constexpr int kStageBytes = 8704;
 
 struct ZDecodeArgs {
   const int32_t* plan;
@@ -251,14 +257,82 @@ struct ZDecodeArgs {
   float q_scale;
 };
 
-// Decode over one unit's groups (zone A segments, then zone C chunks of 32).
+// Logit contributions of one key class: the lane's words [wlo, whi) of its
+// key row, `rot` rotating the visiting order (conflict-free LDS rows for
+// the fp16 rows of zone C).  Entry e of `tab` holds q_h * s (or q_h) of the
+// channel that sits at code position e of the class.
+template <int W, int G>
+__device__ __forceinline__ void key_class(const uint32_t* words, int wlo, int whi, int rot,
+                                          const float4* tab, float (&part)[G]) {
+  constexpr int CPW = 32 / W;           // codes per word
+  const int n = whi - wlo;
+  int r = n > 0 ? rot % n : 0;
+  for (int it = 0; it < n; ++it) {
+    const int wi = wlo + r;
+    r = (r + 1 == n) ? 0 : r + 1;
+    const uint32_t x = words[wi];
+    const float4* e = tab + wi * CPW;
+    float code[CPW];
+    if constexpr (W == 2) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t bts = (x >> (2 * k)) & 0x03030303u;   // codes 4m + k in byte m
+#pragma unroll
+        for (int m = 0; m < 4; ++m) code[4 * m + k] = static_cast<float>((bts >> (8 * m)) & 0xFFu);
+      }
+    } else if constexpr (W == 4) {
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const uint32_t bts = (x >> (4 * k)) & 0x0F0F0F0Fu;   // codes 2m + k in byte m
+#pragma unroll
+        for (int m = 0; m < 4; ++m) code[2 * m + k] = static_cast<float>((bts >> (8 * m)) & 0xFFu);
+      }
+    } else if constexpr (W == 8) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) code[m] = static_cast<float>((x >> (8 * m)) & 0xFFu);
+    } else {
+      code[0] = h2f(static_cast<uint16_t>(x & 0xFFFFu));
+      code[1] = h2f(static_cast<uint16_t>(x >> 16));
+    }
+#pragma unroll
+    for (int p = 0; p < CPW; ++p) {
+      const float4 t = e[p];
+      const float tv[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+      for (int h = 0; h < G; ++h) part[h] = fmaf(tv[h], code[p], part[h]);
+      // table reads in batches of four (bounded register use)
+      if ((p & 3) == 3) asm volatile("" ::: "memory");
+    }
+  }
+}
+
+// Decode over one unit's items (zone-A groups in segment order, then zone-C
+// chunks of 32 tokens); each wave takes whole items.
+//
+// Per item: the group's bytes are staged in the wave's LDS slice with
+// 16-byte loads.  Keys: logit_h(t) = sum_c q_h,c (s_c code_t,c + z_c)
+//   = sum_c (q_h,c s_c) code_t,c + sum_c q_h,c z_c;
+// the wave builds the table q_h,c s_c for the group once, and the bias
+// sum_c q_h,c z_c once.  Lane (slot t = lane % 32, half) walks half of the
+// words of every key class of t's row (both halves of the wave at the same
+// class, so the code width is uniform), converting codes to floats and
+// accumulating the G heads.  Values: lane = CV consecutive channels;
+// out_h,c += sum_t (p_h,t s_t,g) code_t,c, and the zero-point term
+// sum_t p_h,t z_t,g is kept per lane (one product per slot, head and value
+// group) and summed over lanes once at the end.  fp16 value rows (zone B,
+// zone C) are loaded into registers while the keys are staged.
 template <int D, int G>
-__global__ __launch_bounds__(256) void zoned_decode_kernel(ZDecodeArgs a) {
+__global__ __launch_bounds__(256, 2) void zoned_decode_kernel(ZDecodeArgs a) {
   constexpr int CV = D / 64;                        // value channels per lane
+  constexpr int NG = D / kGroup;                    // value groups per token
+  constexpr int NGH = NG / 2;                       // value groups per lane half
+  constexpr int kEntries = D + 26;                  // table entries: classes padded to whole words
+  static_assert(kZWaves * G * D * 4 <= kZWaves * kStageBytes, "wave states fit in the staging area");
   __shared__ __attribute__((aligned(16))) uint8_t lds_stage[kZWaves][kStageBytes];
-  __shared__ float lds_qp[G][D], lds_qn[G][D];      // query: permuted / natural order
-  __shared__ float lds_p[kZWaves][kGroup][G];
-  __shared__ float lds_m[kZWaves][G], lds_l[kZWaves][G], lds_o[kZWaves][G][D];
+  __shared__ __attribute__((aligned(16))) float4 lds_tab[kZWaves][kEntries];
+  __shared__ __attribute__((aligned(16))) float4 lds_ps[kZWaves][kGroup][NG];
+  __shared__ float lds_qp[G][D], lds_qn[G][D];      // query: permuted / natural channel order
+  __shared__ float lds_m[kZWaves][G], lds_l[kZWaves][G];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int split = blockIdx.x, unit = blockIdx.y;
   const int b = unit / a.Hkv, kvh = unit % a.Hkv;
@@ -276,23 +350,40 @@ __global__ __launch_bounds__(256) void zoned_decode_kernel(ZDecodeArgs a) {
   }
   __syncthreads();
 
-  const int m2 = U[U_M], m4 = U[U_M + 1], m8 = U[U_M + 2];
+  // key classes of the unit: channels, words, first channel, first table entry
+  int cm[4], ckw[4], cch[4], cent[4];
+  {
+    int ch = 0, en = 0;
+#pragma unroll
+    for (int ci = 0; ci < 4; ++ci) {
+      cm[ci] = U[U_M + ci];
+      ckw[ci] = U[U_KWORDS + ci];
+      cch[ci] = ch;
+      cent[ci] = en;
+      ch += cm[ci];
+      en += ckw[ci] * (32 / kSegW[ci]);
+    }
+  }
+  const int n_ent = cent[3] + ckw[3] * 2;
   const int n_kq = U[U_NKQ];
-  const int kw2 = U[U_KWORDS], kw4 = U[U_KWORDS + 1], kw8 = U[U_KWORDS + 2];
   const int W_K = U[U_WK];
+  const int kcodes_b = U[U_KCODES_B], ksz_b = U[U_KSZ_B];
   const int total = U[U_TOTAL_GROUPS];
   const int items = total + (a.C + kGroup - 1) / kGroup;
-  const int s_slot = lane & 31, hf = lane >> 5;
+  const int j = lane & 31, hf = lane >> 5;
+  const int c0 = lane * CV;
   uint8_t* st = lds_stage[wave];
+  float4* tab = lds_tab[wave];
 
-  float m[G], l[G], acc[G][CV], zacc[G];
+  float m[G], l[G], acc[G][CV], zp[G][NGH];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     m[h] = -INFINITY;
     l[h] = 0.0f;
-    zacc[h] = 0.0f;
 #pragma unroll
     for (int c = 0; c < CV; ++c) acc[h][c] = 0.0f;
+#pragma unroll
+    for (int gi = 0; gi < NGH; ++gi) zp[h][gi] = 0.0f;
   }
 
   const int ib = split * a.items_per_split;
@@ -300,9 +391,8 @@ __global__ __launch_bounds__(256) void zoned_decode_kernel(ZDecodeArgs a) {
   for (int item = ib + wave; item < ie; item += kZWaves) {
     const bool zone_c = item >= total;
     int seg = 3, g = 0, n_valid;
-    const uint8_t* gb = nullptr;
-    const uint16_t* zck = nullptr;
-    const uint16_t* zcv = nullptr;
+    const uint16_t* vrows = nullptr;          // fp16 value rows (zone B / zone C), else null
+    const uint8_t* gb = nullptr;              // zone-A group
     if (!zone_c) {
       seg = 0;
       g = item;
@@ -312,66 +402,138 @@ __global__ __launch_bounds__(256) void zoned_decode_kernel(ZDecodeArgs a) {
       }
       n_valid = min(kGroup, U[U_N + seg] - g * kGroup);
       gb = ub + U[U_SEG_OFF + seg] + static_cast<size_t>(g) * U[U_GRP_B + seg];
-      // stage the group's contiguous bytes
-      const int nb = U[U_GRP_B + seg];
+      const int nb = kcodes_b + 2 * ksz_b;         // the key block
       const uint4* src = reinterpret_cast<const uint4*>(gb);
       uint4* dst = reinterpret_cast<uint4*>(st);
       for (int i = lane; i < nb / 16; i += 64) dst[i] = src[i];
+      if (seg == 3)
+        vrows = reinterpret_cast<const uint16_t*>(ub + U[U_ZB]) + static_cast<size_t>(g) * kGroup * D;
     } else {
       const int cg = item - total;
       n_valid = min(kGroup, a.C - cg * kGroup);
-      zck = reinterpret_cast<const uint16_t*>(ub + U[U_ZC]) + static_cast<size_t>(cg) * kGroup * D;
-      zcv = zck + static_cast<size_t>(a.C) * D;
+      const uint16_t* zck = reinterpret_cast<const uint16_t*>(ub + U[U_ZC]) + static_cast<size_t>(cg) * kGroup * D;
+      const uint4* src = reinterpret_cast<const uint4*>(zck);
+      uint4* dst = reinterpret_cast<uint4*>(st);
+      for (int i = lane; i < n_valid * D * 2 / 16; i += 64) dst[i] = src[i];
+      vrows = zck + static_cast<size_t>(a.C) * D;
     }
     const int w = kSegW[seg];
+    // The lane's value bits of every slot straight into registers (slots
+    // past n_valid read 0): fp16 rows (zone B, zone C), or the code word
+    // holding its CV channels; with codes, the slot's scales and zeros of
+    // the lane's value groups.
+    uint32_t vr[kGroup];
+    uint32_t vsz[2] = {0u, 0u};
+    const int vwpt = D * w / 32;
+    const int widx = (c0 * w) >> 5, sh = (c0 * w) & 31;
+    const int vsz_b = (kGroup * NG * 2 + 15) / 16 * 16;
+    // slots past n_valid reload the last valid slot (in bounds) and are zeroed
+    const bool fp16v = zone_c || seg == 3;         // wave-uniform
+    if (fp16v) {
+#pragma unroll
+      for (int t = 0; t < kGroup; ++t) {
+        const int te = min(t, n_valid - 1);
+        uint32_t x;
+        if constexpr (CV == 2)
+          x = *reinterpret_cast<const uint32_t*>(vrows + static_cast<size_t>(te) * D + c0);
+        else
+          x = vrows[static_cast<size_t>(te) * D + c0];
+        vr[t] = t < n_valid ? x : 0u;
+      }
+    } else {
+      const uint8_t* vb = gb + kcodes_b + 2 * ksz_b;
+      const uint32_t* vcodes = reinterpret_cast<const uint32_t*>(vb);
+#pragma unroll
+      for (int t = 0; t < kGroup; ++t) {
+        const uint32_t x = vcodes[min(t, n_valid - 1) * vwpt + widx];
+        vr[t] = t < n_valid ? x : 0u;
+      }
+      const uint16_t* vs = reinterpret_cast<const uint16_t*>(vb + kGroup * vwpt * 4);
+      const uint16_t* vz = reinterpret_cast<const uint16_t*>(vb + kGroup * vwpt * 4 + vsz_b);
+      if constexpr (NGH == 2) {
+        vsz[0] = *reinterpret_cast<const uint32_t*>(vs + j * NG + 2 * hf);
+        vsz[1] = *reinterpret_cast<const uint32_t*>(vz + j * NG + 2 * hf);
+      } else {
+        vsz[0] = vs[j * NG + hf];
+        vsz[1] = vz[j * NG + hf];
+      }
+    }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-    // ---- logits: lane = (slot, half of the channels)
-    const bool valid = s_slot < n_valid;
+    // ---- table of q*s (and the bias sum q*z) for this item
+    float bias[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) bias[h] = 0.0f;
+    if (!zone_c) {
+      const uint16_t* ks = reinterpret_cast<const uint16_t*>(st + kcodes_b);
+      const uint16_t* kz = reinterpret_cast<const uint16_t*>(st + kcodes_b + ksz_b);
+      for (int e = lane; e < n_ent; e += 64) {
+        const int ci = (e >= cent[1]) + (e >= cent[2]) + (e >= cent[3]);
+        const int local = e - (ci == 0 ? cent[0] : ci == 1 ? cent[1] : ci == 2 ? cent[2] : cent[3]);
+        const int mm = ci == 0 ? cm[0] : ci == 1 ? cm[1] : ci == 2 ? cm[2] : cm[3];
+        const int pc = local + (ci == 0 ? cch[0] : ci == 1 ? cch[1] : ci == 2 ? cch[2] : cch[3]);
+        float tv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (local < mm) {
+          const bool quant = pc < n_kq;
+          const float sc = quant ? h2f(ks[pc]) : 1.0f;
+          const float zr = quant ? h2f(kz[pc]) : 0.0f;
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            const float qv = lds_qp[h][pc];
+            tv[h] = qv * sc;
+            bias[h] = fmaf(qv, zr, bias[h]);
+          }
+        }
+        tab[e] = make_float4(tv[0], tv[1], tv[2], tv[3]);
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h) bias[h] = wave_sum(bias[h]);
+    } else {
+      for (int e = lane; e < D; e += 64) {
+        float tv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int h = 0; h < G; ++h) tv[h] = lds_qn[h][e];
+        tab[e] = make_float4(tv[0], tv[1], tv[2], tv[3]);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // ---- logits: lane = (slot j, half of every class's words)
+    const bool valid = j < n_valid;
     float part[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) part[h] = 0.0f;
     if (valid) {
       if (!zone_c) {
-        const uint32_t* row = reinterpret_cast<const uint32_t*>(st) + s_slot * W_K;
-        const uint16_t* ks = reinterpret_cast<const uint16_t*>(st + U[U_KCODES_B]);
-        const uint16_t* kz = reinterpret_cast<const uint16_t*>(st + U[U_KCODES_B] + U[U_KSZ_B]);
-        for (int pc = hf * (D / 2); pc < (hf + 1) * (D / 2); ++pc) {
-          float kv;
-          if (pc < n_kq) {
-            int bits, idx, woff;
-            if (pc < m2) { bits = 2; idx = pc; woff = 0; }
-            else if (pc < m2 + m4) { bits = 4; idx = pc - m2; woff = kw2; }
-            else { bits = 8; idx = pc - m2 - m4; woff = kw2 + kw4; }
-            const int bit = idx * bits;
-            const uint32_t code = (row[woff + bit / 32] >> (bit % 32)) & ((1u << bits) - 1u);
-            kv = fmaf(static_cast<float>(code), h2f(ks[pc]), h2f(kz[pc]));
-          } else {
-            const int idx = pc - n_kq;
-            const uint32_t word = row[kw2 + kw4 + kw8 + idx / 2];
-            kv = h2f(static_cast<uint16_t>((idx & 1) ? (word >> 16) : (word & 0xFFFFu)));
-          }
+        const uint32_t* row = reinterpret_cast<const uint32_t*>(st) + j * W_K;
+        int wb = 0;
 #pragma unroll
-          for (int h = 0; h < G; ++h) part[h] = fmaf(lds_qp[h][pc], kv, part[h]);
+        for (int ci = 0; ci < 4; ++ci) {
+          const int kw = ckw[ci], h0 = (kw + 1) >> 1;
+          const int wlo = hf ? h0 : 0, whi = hf ? kw : h0;
+          const float4* tb = tab + cent[ci];
+          if (ci == 0) key_class<2, G>(row + wb, wlo, whi, 0, tb, part);
+          else if (ci == 1) key_class<4, G>(row + wb, wlo, whi, 0, tb, part);
+          else if (ci == 2) key_class<8, G>(row + wb, wlo, whi, 0, tb, part);
+          else key_class<16, G>(row + wb, wlo, whi, 0, tb, part);
+          wb += kw;
         }
       } else {
-        const uint16_t* kr = zck + static_cast<size_t>(s_slot) * D;
-        for (int c = hf * (D / 2); c < (hf + 1) * (D / 2); ++c) {
-          const float kv = h2f(kr[c]);
-#pragma unroll
-          for (int h = 0; h < G; ++h) part[h] = fmaf(lds_qn[h][c], kv, part[h]);
-        }
+        const uint32_t* row = reinterpret_cast<const uint32_t*>(st) + j * (D / 2);
+        const int wlo = hf ? D / 4 : 0, whi = hf ? D / 2 : D / 4;
+        key_class<16, G>(row, wlo, whi, j, tab, part);
       }
     }
-    float lg[G];
+    float lg[G], mnew[G];
     bool grow = false;
-    float mnew[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      lg[h] = part[h] + __shfl_xor(part[h], 32, 64);
-      const float t = max_strided<1>(valid ? lg[h] : -INFINITY);
+      lg[h] = swap_rows<false>(part[h], true) + bias[h];   // the two halves of slot j
+      const float t = wave_max(valid ? lg[h] : -INFINITY);
       mnew[h] = fmaxf(m[h], t);
       grow |= mnew[h] > m[h];
     }
@@ -380,76 +542,100 @@ __global__ __launch_bounds__(256) void zoned_decode_kernel(ZDecodeArgs a) {
       for (int h = 0; h < G; ++h) {
         const float sc = merge_weight(m[h], mnew[h]);
         l[h] *= sc;
-        zacc[h] *= sc;
 #pragma unroll
         for (int c = 0; c < CV; ++c) acc[h][c] *= sc;
+#pragma unroll
+        for (int gi = 0; gi < NGH; ++gi) zp[h][gi] *= sc;
         m[h] = mnew[h];
       }
     }
-    if (hf == 0) {
+    float p[G];
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float p = valid ? exp2f(lg[h] - m[h]) : 0.0f;
-        lds_p[wave][s_slot][h] = p;
-        l[h] += p;
+    for (int h = 0; h < G; ++h) {
+      p[h] = valid ? exp2f(lg[h] - m[h]) : 0.0f;
+      if (hf == 0) l[h] += p[h];
+    }
+
+    // ---- values
+    if (!fp16v) {
+      // p * scale per (slot, value group) into LDS; zero-point products kept
+      // per lane
+#pragma unroll
+      for (int gi = 0; gi < NGH; ++gi) {
+        const int gg = hf * NGH + gi;
+        const float sc = h2f(static_cast<uint16_t>(vsz[0] >> (16 * gi)));
+        const float zr = h2f(static_cast<uint16_t>(vsz[1] >> (16 * gi)));
+        float tv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          tv[h] = p[h] * sc;
+          zp[h][gi] = fmaf(p[h], zr, zp[h][gi]);
+        }
+        lds_ps[wave][j][gg] = make_float4(tv[0], tv[1], tv[2], tv[3]);
       }
+    } else if (hf == 0) {
+      float tv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int h = 0; h < G; ++h) tv[h] = p[h];
+      lds_ps[wave][j][0] = make_float4(tv[0], tv[1], tv[2], tv[3]);
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-    // ---- values: lane = CV consecutive channels
-    const int c0 = lane * CV;
-    if (!zone_c && w < 16) {
-      const int vwpt = D * w / 32;
-      const uint8_t* vb = st + U[U_KCODES_B] + 2 * U[U_KSZ_B];
-      const uint32_t* vcodes = reinterpret_cast<const uint32_t*>(vb);
-      const int vsz_b = (kGroup * (D / kGroup) * 2 + 15) / 16 * 16;
-      const uint16_t* vs = reinterpret_cast<const uint16_t*>(vb + kGroup * vwpt * 4);
-      const uint16_t* vz = reinterpret_cast<const uint16_t*>(vb + kGroup * vwpt * 4 + vsz_b);
-      const int vg = c0 / kGroup;
-      for (int s = 0; s < n_valid; ++s) {
-        const float sc = h2f(vs[s * (D / kGroup) + vg]);
-        const float zr = h2f(vz[s * (D / kGroup) + vg]);
+    const uint32_t mask = (1u << w) - 1u;
+    auto accumulate = [&](const float4 p4, const float (&vv)[CV]) {
+      const float pv[4] = {p4.x, p4.y, p4.z, p4.w};
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float p = lds_p[wave][s][h];
-          const float ps = p * sc;
-          zacc[h] = fmaf(p, zr, zacc[h]);
+      for (int h = 0; h < G; ++h)
 #pragma unroll
-          for (int c = 0; c < CV; ++c) {
-            const int bit = (c0 + c) * w;
-            const uint32_t code = (vcodes[s * vwpt + bit / 32] >> (bit % 32)) & ((1u << w) - 1u);
-            acc[h][c] = fmaf(ps, static_cast<float>(code), acc[h][c]);
-          }
+        for (int c = 0; c < CV; ++c) acc[h][c] = fmaf(pv[h], vv[c], acc[h][c]);
+    };
+    if (fp16v) {
+#pragma unroll
+      for (int t = 0; t < kGroup; ++t) {
+        float vv[CV];
+        if constexpr (CV == 2) {
+          vv[0] = h2f(static_cast<uint16_t>(vr[t] & 0xFFFFu));
+          vv[1] = h2f(static_cast<uint16_t>(vr[t] >> 16));
+        } else {
+          vv[0] = h2f(static_cast<uint16_t>(vr[t]));
         }
+        accumulate(lds_ps[wave][t][0], vv);
       }
     } else {
-      const uint16_t* vrows = zone_c ? zcv
-                                     : reinterpret_cast<const uint16_t*>(ub + U[U_ZB]) +
-                                           static_cast<size_t>(g) * kGroup * D;
-      for (int s = 0; s < n_valid; ++s) {
+      const int vg = c0 / kGroup;
+#pragma unroll
+      for (int t = 0; t < kGroup; ++t) {
         float vv[CV];
 #pragma unroll
-        for (int c = 0; c < CV; ++c) vv[c] = h2f(vrows[static_cast<size_t>(s) * D + c0 + c]);
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float p = lds_p[wave][s][h];
-#pragma unroll
-          for (int c = 0; c < CV; ++c) acc[h][c] = fmaf(p, vv[c], acc[h][c]);
-        }
+        for (int c = 0; c < CV; ++c) vv[c] = static_cast<float>((vr[t] >> (sh + c * w)) & mask);
+        accumulate(lds_ps[wave][t][vg], vv);
       }
     }
+    // the next item overwrites the staging area and the tables
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 
-  // ---- wave state -> LDS (l summed over the 32 slot lanes of half 0)
+  // ---- wave state -> LDS: l over all lanes; the zero-point products over
+  // the 32 lanes of each half, where lane c0 / 32 = its value group
+  float zsum[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    l[h] = sum_strided<1>(l[h]);
+    l[h] = wave_sum(l[h]);
+    float zs[NGH];
 #pragma unroll
-    for (int c = 0; c < CV; ++c) lds_o[wave][h][lane * CV + c] = acc[h][c] + zacc[h];
+    for (int gi = 0; gi < NGH; ++gi) zs[gi] = half_sum(zp[h][gi]);
+    zsum[h] = zs[0];
+    if constexpr (NGH == 2) zsum[h] = ((c0 / kGroup) & 1) ? zs[1] : zs[0];
   }
+  __syncthreads();                                  // staging area becomes the wave states
+  float (*lds_o)[G][D] = reinterpret_cast<float (*)[G][D]>(&lds_stage[0][0]);
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int c = 0; c < CV; ++c) lds_o[wave][h][c0 + c] = acc[h][c] + zsum[h];
   if (lane == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -475,8 +661,13 @@ int zoned_geometry(const int32_t* p, int Hq, ZGeometry* g) {
   g->G = Hq / Hkv;
   if (g->G != 1 && g->G != 2 && g->G != 4) return DQA_ERR_UNSUPPORTED;
   g->units = p[H_UNITS];
+  // every key block fits one staging slice
+  for (int u = 0; u < g->units; ++u) {
+    const int32_t* U = p + p[H_UNIT_OFF] + static_cast<size_t>(u) * kUnitWords;
+    if (U[U_KCODES_B] + 2 * U[U_KSZ_B] > kStageBytes) return DQA_ERR_PLAN;
+  }
   g->items_max = p[H_MAX_GROUPS] + (p[H_C] + kGroup - 1) / kGroup;
-  long long s = (kTargetWorkgroups + g->units - 1) / (g->units > 0 ? g->units : 1);
+  long long s = (kZoneWorkgroups + g->units - 1) / (g->units > 0 ? g->units : 1);
   if (s > g->items_max) s = g->items_max;
   if (s > kMaxSplitsMerge - 1) s = kMaxSplitsMerge - 1;
   if (s < 1) s = 1;
