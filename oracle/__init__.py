@@ -72,3 +72,8 @@ __all__ = [
     "zoned_layout", "zoned_pack", "zoned_decode_attention", "rvq_encode",
     "rvq_reconstruct", "rvq_decode_attention", "rvq_stage_distances",
 ]
+from .stream import (
+    empty_stream,
+    flush_count,
+    kivi_append,
+)

@@ -13,6 +13,8 @@ import test_oracle_attention as TA
 import test_oracle_quant as TQ
 import test_oracle_rvq as TR
 import test_oracle_zoned as TZ
+import test_oracle_stream as TS
+import oracle.stream as ost
 
 _orig_qg = oq.quantize_groups
 
@@ -189,3 +191,38 @@ def test_zoned_eviction_mutant_is_caught(monkeypatch):
     monkeypatch.setattr(oz, "_unit_layout", keep_evicted)
     with pytest.raises(AssertionError):
         TZ.test_width_zero_is_eviction()
+
+
+def test_stream_mutants_are_caught(monkeypatch):
+    orig_append = ost.kivi_append
+
+    def newest_first(state, k_new, v_new, bits, R_max):
+        # quantizes the newest 32 tokens of the window instead of the oldest
+        k_all = np.concatenate([state["k_recent"], np.asarray(k_new, np.float16)], axis=2)
+        v_all = np.concatenate([state["v_recent"], np.asarray(v_new, np.float16)], axis=2)
+        f = ost.flush_count(k_all.shape[2], R_max)
+        n, R = f * 32, k_all.shape[2] - f * 32
+        out = dict(state)
+        if f:
+            kc, ks, kz = oq.quantize_k(k_all[:, :, R:], bits)
+            vc, vs, vz = oq.quantize_v(v_all[:, :, R:], bits)
+            for name, x in [("k_codes", kc), ("k_scale", ks), ("k_zero", kz), ("v_codes", vc),
+                            ("v_scale", vs), ("v_zero", vz)]:
+                out[name] = np.concatenate([state[name], x], axis=2)
+        out["k_recent"], out["v_recent"] = k_all[:, :, :R].copy(), v_all[:, :, :R].copy()
+        return out
+
+    def flush_at_bound(rows, R_max):
+        f = 0
+        while rows >= R_max and rows >= 32:         # flushes when the window is merely full
+            rows -= 32
+            f += 1
+        return f
+
+    monkeypatch.setattr(TS, "kivi_append", newest_first)
+    with pytest.raises(AssertionError):
+        TS.test_streaming_equals_batch_quantization(2, 128, 1)
+    monkeypatch.setattr(TS, "kivi_append", orig_append)
+    monkeypatch.setattr(ost, "flush_count", flush_at_bound)
+    with pytest.raises(AssertionError):
+        TS.test_hand_counted_flushes_one_token_at_a_time()
