@@ -45,7 +45,7 @@ class KiviCacheStruct(ctypes.Structure):
                 ("T_q", _i), ("R", _i), ("rope_theta", _f),
                 ("k_codes", _vp), ("k_scale", _vp), ("k_zero", _vp),
                 ("v_codes", _vp), ("v_scale", _vp), ("v_zero", _vp),
-                ("k_recent", _vp), ("v_recent", _vp)]
+                ("k_recent", _vp), ("v_recent", _vp), ("T_cap", _i), ("R_cap", _i)]
 
 
 _SIGS = {
@@ -57,6 +57,8 @@ _SIGS = {
     "decode_attention_qkv": (_i, [_vp, ctypes.POINTER(KiviCacheStruct), _f, _vp, _sz, _vp, _vp]),
     "decode_attention_qkv_partial": (_i, [_vp, ctypes.POINTER(KiviCacheStruct), _f, _vp, _sz, _vp, _vp]),
     "decode_attention_qkv_merge": (_i, [ctypes.POINTER(KiviCacheStruct), _vp, _sz, _vp, _vp]),
+    "kivi_append_workspace_bytes": (_sz, [ctypes.POINTER(KiviCacheStruct), _i]),
+    "kivi_append": (_i, [ctypes.POINTER(KiviCacheStruct), _vp, _vp, _i, _i, _vp, _sz, _vp]),
     "zoned_plan_words": (_sz, [_i, _i, _i, _i]),
     "zoned_plan": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _vp, _sz, ctypes.POINTER(_sz)]),
     "zoned_pack": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
@@ -127,19 +129,24 @@ def quantize_pack_v(v, bits):
 class KiviCache:
     """Device tensors of a uniform-layout cache plus its descriptor.
 
-    k_codes/v_codes int32 [B, Hkv, T_q, d*bits/32]; k_scale/k_zero fp16
-    [B, Hkv, T_q/32, d]; v_scale/v_zero fp16 [B, Hkv, T_q, d/32];
-    k_recent/v_recent fp16 [B, Hkv, R, d] (keys before RoPE) or None.
+    k_codes/v_codes int32 [B, Hkv, T_cap, d*bits/32]; k_scale/k_zero fp16
+    [B, Hkv, T_cap/32, d]; v_scale/v_zero fp16 [B, Hkv, T_cap, d/32];
+    k_recent/v_recent fp16 [B, Hkv, R_cap, d] (keys before RoPE) or None.
+    The capacities are the tensors' token dimensions; T_q (default T_cap)
+    and R (default R_cap) are the tokens in use.
     """
 
     def __init__(self, Hq, bits, k_codes, k_scale, k_zero, v_codes, v_scale, v_zero,
-                 k_recent=None, v_recent=None, rope_theta=0.0, T_q=None, B=None, Hkv=None, d=None):
+                 k_recent=None, v_recent=None, rope_theta=0.0, T_q=None, B=None, Hkv=None, d=None,
+                 R=None):
         ref = k_codes if k_codes is not None else k_recent
         self.B = ref.shape[0] if B is None else B
         self.Hkv = ref.shape[1] if Hkv is None else Hkv
         self.d = (k_scale.shape[3] if k_scale is not None else k_recent.shape[3]) if d is None else d
-        self.T_q = (k_codes.shape[2] if k_codes is not None else 0) if T_q is None else T_q
-        self.R = k_recent.shape[2] if k_recent is not None else 0
+        self.T_cap = k_codes.shape[2] if k_codes is not None else 0
+        self.R_cap = k_recent.shape[2] if k_recent is not None else 0
+        self.T_q = self.T_cap if T_q is None else T_q
+        self.R = self.R_cap if R is None else R
         self.Hq, self.bits, self.rope_theta = Hq, bits, float(rope_theta)
         self.tensors = dict(k_codes=k_codes, k_scale=k_scale, k_zero=k_zero, v_codes=v_codes,
                             v_scale=v_scale, v_zero=v_zero, k_recent=k_recent, v_recent=v_recent)
@@ -151,7 +158,8 @@ class KiviCache:
         return KiviCacheStruct(self.B, self.Hq, self.Hkv, self.d, self.bits, self.T_q, self.R,
                                self.rope_theta, *[(None if t[n] is None else t[n].data_ptr()) for n in
                                                   ("k_codes", "k_scale", "k_zero", "v_codes",
-                                                   "v_scale", "v_zero", "k_recent", "v_recent")])
+                                                   "v_scale", "v_zero", "k_recent", "v_recent")],
+                               self.T_cap, self.R_cap)
 
     def workspace_bytes(self):
         return lib.decode_attention_workspace_bytes(ctypes.byref(self.struct()))
@@ -200,6 +208,29 @@ def decode_attention_qkv_merge(cache, out, workspace):
            lib.decode_attention_qkv_merge(ctypes.byref(st), _ptr(workspace), workspace.numel(),
                                           _ptr(out), _stream(out.device)))
     return out
+
+
+def kivi_append(cache, k_new, v_new, R_max=128, workspace=None):
+    """Append fp16 tokens k_new, v_new [B, Hkv, n_new, d] (keys before RoPE)
+    to the cache's recent zone, quantizing its oldest 32 tokens into the
+    quantized buffers while it holds more than R_max (see the header).
+    Updates cache.T_q and cache.R; returns the number of 32-token groups
+    quantized."""
+    n_new = 0
+    if k_new is not None:
+        k_new, v_new = _dev16(k_new, "k_new"), _dev16(v_new, "v_new")
+        n_new = k_new.shape[2]
+    dev = (k_new if k_new is not None else cache.tensors["k_recent"]).device
+    st = cache.struct()
+    n = lib.kivi_append_workspace_bytes(ctypes.byref(st), n_new)
+    if n == 0:
+        raise DqaError("kivi_append", 2)
+    ws = torch.empty(n, dtype=torch.uint8, device=dev) if workspace is None else workspace
+    T0 = cache.T_q
+    _check("kivi_append", lib.kivi_append(ctypes.byref(st), _ptr(k_new), _ptr(v_new), n_new, int(R_max),
+                                          _ptr(ws), ws.numel(), _stream(dev)))
+    cache.T_q, cache.R = st.T_q, st.R
+    return (cache.T_q - T0) // 32
 
 
 # ---------------------------------------------------------------- zoned

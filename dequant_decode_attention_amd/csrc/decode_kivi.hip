@@ -58,6 +58,8 @@ struct KiviArgs {
   float* out;
   float* partials;
   int Hq, Hkv, T_q, R;
+  int qtile_stride;     // 32-token tiles of quantized-buffer capacity per (batch, KV head)
+  int R_cap;            // recent-buffer rows per (batch, KV head)
   int n_qtiles;         // T_q / 32
   int n_rtiles;         // ceil(R / 32)
   int total_splits;     // splits (partial-state slots) per (batch, KV head)
@@ -476,8 +478,9 @@ __global__ __launch_bounds__(256) void kivi_decode_kernel(KiviArgs a) {
   };
 
   // ---------------------------------------------------------- quantized tile
-  const uint8_t* const kbase = reinterpret_cast<const uint8_t*>(a.k_codes) + unit * a.T_q * KROW;
-  const uint8_t* const vbase = reinterpret_cast<const uint8_t*>(a.v_codes) + unit * a.n_qtiles * VBLK;
+  const size_t qstride = static_cast<size_t>(a.qtile_stride);      // tiles per (batch, KV head)
+  const uint8_t* const kbase = reinterpret_cast<const uint8_t*>(a.k_codes) + unit * qstride * kGroup * KROW;
+  const uint8_t* const vbase = reinterpret_cast<const uint8_t*>(a.v_codes) + unit * qstride * VBLK;
   constexpr int VW = BITS == 8 ? 2 : 1;   // 32-bit words per value chunk
   // two codes per register: one in each fp16 half (subnormal code * 2^-24)
   const uint32_t vmask = opaque(BITS == 2 ? 0x00030003u : 0x000F000Fu);
@@ -508,8 +511,8 @@ __global__ __launch_bounds__(256) void kivi_decode_kernel(KiviArgs a) {
     }
     // scale blocks: lanes 0..31 read scales, 32..63 zeros
     const int half = lane >> 5, r = lane & 31;
-    const uint16_t* ksrc = (half ? a.k_zero : a.k_scale) + (unit * a.n_qtiles + ti) * D + r * (D / 32);
-    const uint16_t* vsrc = (half ? a.v_zero : a.v_scale) + (unit * a.T_q + static_cast<size_t>(ti) * kGroup + r) * NVG;
+    const uint16_t* ksrc = (half ? a.k_zero : a.k_scale) + (unit * qstride + ti) * D + r * (D / 32);
+    const uint16_t* vsrc = (half ? a.v_zero : a.v_scale) + ((unit * qstride + ti) * kGroup + r) * NVG;
     const Words<4 * SZW> kw = load_words<4 * SZW>(ksrc);
     const Words<4 * SZW> vw = load_words<4 * SZW>(vsrc);
 #pragma unroll
@@ -580,8 +583,8 @@ __global__ __launch_bounds__(256) void kivi_decode_kernel(KiviArgs a) {
   };
 
   // ------------------------------------------------------ fp16 recent tile
-  const uint16_t* const krb = a.k_recent + unit * a.R * D;
-  const uint16_t* const vrb = a.v_recent + unit * a.R * D;
+  const uint16_t* const krb = a.k_recent + unit * a.R_cap * D;
+  const uint16_t* const vrb = a.v_recent + unit * a.R_cap * D;
   auto recent_tile = [&](int rt) {
     const int r0 = rt * kGroup;
     // every load of the tile is issued before any is used: keys (the lane's
@@ -698,6 +701,8 @@ int make_plan(const dqa_kivi_cache* c, Plan* p) {
   if (c->bits != 2 && c->bits != 4 && c->bits != 8) return DQA_ERR_BITS;
   if (c->Hq % c->Hkv != 0) return DQA_ERR_SHAPE;
   if (c->T_q % kGroup != 0 || c->R > kMaxRecent) return DQA_ERR_SHAPE;
+  if (c->T_cap < 0 || c->T_cap % kGroup != 0 || (c->T_cap > 0 && c->T_cap < c->T_q)) return DQA_ERR_SHAPE;
+  if (c->R_cap < 0 || (c->R_cap > 0 && c->R_cap < c->R)) return DQA_ERR_SHAPE;
   if (c->B > 65535 || c->Hkv > 65535) return DQA_ERR_SHAPE;
   p->G = c->Hq / c->Hkv;
   if (p->G != 1 && p->G != 2 && p->G != 4) return DQA_ERR_UNSUPPORTED;
@@ -801,6 +806,8 @@ extern "C" int decode_attention_qkv_partial(const uint16_t* q, const dqa_kivi_ca
   a.Hkv = c->Hkv;
   a.T_q = c->T_q;
   a.R = c->R;
+  a.qtile_stride = (c->T_cap > 0 ? c->T_cap : c->T_q) / kGroup;
+  a.R_cap = c->R_cap > 0 ? c->R_cap : c->R;
   a.n_qtiles = p.n_qtiles;
   a.n_rtiles = p.n_rtiles;
   a.total_splits = p.total;

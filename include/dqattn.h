@@ -56,7 +56,9 @@ enum {
 const char* dqa_status_string(int status);
 
 /* Version of this interface (increments on any signature or layout change). */
-int dqa_abi_version(void);  /* 3: 16-byte pointer alignment checked (DQA_ERR_ALIGN) */
+int dqa_abi_version(void);  /* 4: dqa_kivi_cache carries buffer capacities
+                              (T_cap, R_cap) and kivi_append exists;
+                              3: 16-byte pointer alignment checked */
 
 /* ------------------------------------------------------------------------
  * Quantize + bit-pack  ([P1 para 1, 3, 4, 5])
@@ -106,16 +108,23 @@ typedef struct dqa_kivi_cache {
   int bits;               /* 2, 4 or 8                                          */
   int T_q;                /* quantized tokens, multiple of 32, >= 0             */
   int R;                  /* fp16 recent tokens, 0..128 ([P1 para 8])           */
+                          /* (the buffers below are laid out with the          */
+                          /* capacities T_cap and R_cap at the end)            */
   float rope_theta;       /* > 0: rotate keys after dequantization (interleaved */
                           /* pairs, omega_i = theta^(-2i/d)); <= 0: no RoPE     */
-  const uint32_t* k_codes;  /* quantize_pack_k layout, [B][Hkv][T_q][d]         */
-  const uint16_t* k_scale;  /* fp16 [B][Hkv][T_q/32][d]                         */
+  const uint32_t* k_codes;  /* quantize_pack_k layout, [B][Hkv][T_cap][d]       */
+  const uint16_t* k_scale;  /* fp16 [B][Hkv][T_cap/32][d]                       */
   const uint16_t* k_zero;
   const uint32_t* v_codes;  /* quantize_pack_v layout (32-token channel-major)  */
-  const uint16_t* v_scale;  /* fp16 [B][Hkv][T_q][d/32]                         */
+  const uint16_t* v_scale;  /* fp16 [B][Hkv][T_cap][d/32]                       */
   const uint16_t* v_zero;
-  const uint16_t* k_recent; /* fp16 [B][Hkv][R][d], keys before RoPE            */
-  const uint16_t* v_recent; /* fp16 [B][Hkv][R][d]                              */
+  const uint16_t* k_recent; /* fp16 [B][Hkv][R_cap][d], keys before RoPE        */
+  const uint16_t* v_recent; /* fp16 [B][Hkv][R_cap][d]                          */
+  int T_cap;              /* tokens the quantized buffers hold per (batch, KV   */
+                          /* head): the arrays above are [B][Hkv][T_cap]...     */
+                          /* with T_cap >= T_q, a multiple of 32; 0 means T_q   */
+  int R_cap;              /* rows of the recent buffers per (batch, KV head),   */
+                          /* >= R; 0 means R                                    */
 } dqa_kivi_cache;
 
 /* Bytes of workspace decode_attention_qkv needs for this cache shape
@@ -161,6 +170,31 @@ int decode_attention_qkv_partial(const uint16_t* q, const dqa_kivi_cache* cache,
                                  float* out, void* stream);
 int decode_attention_qkv_merge(const dqa_kivi_cache* cache, const void* ws,
                                size_t ws_bytes, float* out, void* stream);
+
+/* Streaming append to the cache ([P1 para 8]: per-channel key statistics
+ * need tokens not generated yet, so the newest tokens stay in fp16, up to
+ * 128 of them, and are quantized a group at a time once enough of them are
+ * there).  The n_new tokens are appended after the R recent tokens; then,
+ * while the recent zone holds more than R_max tokens and at least 32, its
+ * oldest 32 tokens are quantized exactly as quantize_pack_k /
+ * quantize_pack_v would quantize them (one key group per channel, one value
+ * group per token and 32 channels) into quantized positions T_q..T_q+31,
+ * and T_q grows by 32.  The remaining recent tokens move to the front of
+ * the recent buffers.  On success cache->T_q and cache->R are updated; the
+ * buffers the cache points to must be writable device memory.
+ *   cache  (host) descriptor with T_cap >= T_q + 32 * flushes and
+ *          R_cap >= the new R (else DQA_ERR_SHAPE and nothing is written)
+ *   k_new, v_new (device) fp16 [B][Hkv][n_new][d] (keys before RoPE);
+ *          may be null when n_new == 0
+ *   R_max  0..128
+ *   ws     (device) workspace of ws_bytes >= kivi_append_workspace_bytes
+ * Enqueues up to four kernels on `stream`; the recent buffers may be
+ * rewritten in place (the kernels read a staged copy from ws).
+ * Errors: DQA_ERR_NULL, DQA_ERR_SHAPE, DQA_ERR_BITS, DQA_ERR_WORKSPACE,
+ * DQA_ERR_ALIGN, DQA_ERR_HIP. */
+size_t kivi_append_workspace_bytes(const dqa_kivi_cache* cache, int n_new);
+int kivi_append(dqa_kivi_cache* cache, const uint16_t* k_new, const uint16_t* v_new,
+                int n_new, int R_max, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * Mixed-bitwidth zoned cache  ([P3 sec 2.2, bit-allocation pipeline] and

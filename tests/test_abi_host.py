@@ -65,7 +65,7 @@ def test_quantize_validation(fn):
 def _cache(**kw):
     base = dict(B=2, Hq=8, Hkv=2, d=128, bits=2, T_q=64, R=16, rope_theta=0.0,
                 k_codes=0x1000, k_scale=0x1000, k_zero=0x1000, v_codes=0x1000,
-                v_scale=0x1000, v_zero=0x1000, k_recent=0x1000, v_recent=0x1000)
+                v_scale=0x1000, v_zero=0x1000, k_recent=0x1000, v_recent=0x1000, T_cap=0, R_cap=0)
     base.update(kw)
     return KiviCacheStruct(*[base[n] for n, _ in KiviCacheStruct._fields_])
 
@@ -97,6 +97,13 @@ def test_decode_workspace_query_and_validation():
     # the recent-zone pointers are not used (nor checked) without recent tokens
     c3 = _cache(R=0, k_recent=0x1002, v_recent=None)
     assert lib.decode_attention_qkv(FAKE, ctypes.byref(c3), 0.1, None, 1 << 30, FAKE, None) == 4
+    # buffer capacities: 0 means dense; else at least the tokens in use, and
+    # the quantized capacity a multiple of 32
+    for bad in [dict(T_cap=32), dict(T_cap=96 + 8), dict(T_cap=-32), dict(R_cap=8), dict(R_cap=-1)]:
+        c4 = _cache(**bad)
+        assert lib.decode_attention_qkv(FAKE, ctypes.byref(c4), 0.1, FAKE, 1 << 30, FAKE, None) == 2, bad
+        assert lib.decode_attention_workspace_bytes(ctypes.byref(c4)) == 0, bad
+    assert lib.decode_attention_workspace_bytes(ctypes.byref(_cache(T_cap=4096, R_cap=128))) == ws
     # the merge phase validates its own arguments
     assert lib.decode_attention_qkv_merge(ctypes.byref(c), FAKE, 1 << 30, None, None) == 1
     assert lib.decode_attention_qkv_merge(ctypes.byref(c), None, 1 << 30, FAKE, None) == 4
@@ -198,3 +205,42 @@ def test_rvq_validation_and_workspace():
     assert lib.rvq_decode_attention(*args(N=9)) == 2
     assert lib.rvq_decode_attention(*args(ki=None)) == 1
     assert lib.rvq_decode_attention(*args(wsb=16)) == 4
+
+
+def test_kivi_append_validation():
+    """Argument checks of the streaming append (all fail before any launch)."""
+    assert lib.dqa_abi_version() == 4
+    c = _cache(T_cap=128, R_cap=128)
+    # staging holds the recent and the new rows of K and V
+    assert lib.kivi_append_workspace_bytes(ctypes.byref(c), 20) == 2 * 2 * 2 * (16 + 20) * 128 * 2
+    assert lib.kivi_append_workspace_bytes(ctypes.byref(_cache(d=96)), 1) == 0
+    assert lib.kivi_append_workspace_bytes(ctypes.byref(c), -1) == 0
+    ws = 1 << 30
+
+    def call(cache, n_new=20, R_max=16, k=FAKE, v=FAKE, w=FAKE, wb=ws):
+        before = (cache.T_q, cache.R)
+        st = lib.kivi_append(ctypes.byref(cache), k, v, n_new, R_max, w, wb, None)
+        assert (cache.T_q, cache.R) == before or st == 0
+        return st
+
+    assert call(_cache(T_cap=128, R_cap=128), R_max=129) == 2
+    assert call(_cache(T_cap=128, R_cap=128), R_max=-1) == 2
+    assert call(_cache(bits=3, T_cap=128, R_cap=128)) == 3
+    # 16 + 20 rows over R_max = 16: one group of 32 goes to quantized position 64
+    assert call(_cache(T_cap=64, R_cap=128)) == 2              # no room for the group
+    assert call(_cache(T_cap=0, R_cap=128)) == 2               # dense buffers have no room
+    assert call(_cache(T_cap=128, R_cap=2), R_max=0) == 2       # 4 rows stay, recent buffer holds 2
+    assert call(_cache(T_cap=128, R_cap=128), k=None) == 1
+    assert call(_cache(T_cap=128, R_cap=128, k_recent=None)) == 1
+    assert call(_cache(T_cap=128, R_cap=128, v_codes=None)) == 1
+    assert call(_cache(T_cap=128, R_cap=128), w=None) == 4
+    assert call(_cache(T_cap=128, R_cap=128), wb=100) == 4
+    assert call(_cache(T_cap=128, R_cap=128), k=ctypes.c_void_p(0x1008)) == 8
+    assert call(_cache(T_cap=128, R_cap=128, k_zero=0x1002)) == 8
+    # nothing to do: counts unchanged, no launch
+    c0 = _cache(R=0, T_cap=128, R_cap=128)
+    assert lib.kivi_append(ctypes.byref(c0), None, None, 0, 16, None, 0, None) == 0
+    assert (c0.T_q, c0.R) == (64, 0)
+    c1 = _cache(B=0, T_cap=128, R_cap=128)
+    assert lib.kivi_append(ctypes.byref(c1), FAKE, FAKE, 40, 16, None, 0, None) == 0
+    assert (c1.T_q, c1.R) == (64 + 32, 16 + 40 - 32)
