@@ -25,6 +25,7 @@ Prints one JSON line.  Usage:
                     [--no-cpu-baseline] [--no-rows]
 """
 import argparse
+import ctypes
 import json
 import math
 import os
@@ -148,6 +149,42 @@ def time_quantize(dqa, torch, k, v, bits, cfg):
         ms = _event_ms(torch, lambda i: fn(x, bits), 10)
         out[name] = _hbm_row(f"{name}_kernel", cfg["workload"], ms, nbytes)
     return out
+
+
+def time_append(dqa, torch, dev, cfg, bits):
+    """Streaming append on the c3 shape: one new token per (batch, KV head)
+    into a full 128-token fp16 window over a cache holding 32736 quantized
+    tokens, so every call quantizes one group of 32 per (batch, KV head)
+    (the counts are reset between calls)."""
+    B, Hkv, d, Hq = cfg["B"], cfg["Hkv"], cfg["d"], cfg["Hq"]
+    T_cap, T_q0, R_cap = cfg["T_q"], cfg["T_q"] - 32, 128
+    w = d * bits // 32
+    z = lambda *sh, dt=torch.float16: torch.zeros(sh, dtype=dt, device=dev)
+    cache = dqa.KiviCache(Hq, bits, z(B, Hkv, T_cap, w, dt=torch.int32), z(B, Hkv, T_cap // 32, d),
+                          z(B, Hkv, T_cap // 32, d), z(B, Hkv, T_cap, w, dt=torch.int32), z(B, Hkv, T_cap, d // 32),
+                          z(B, Hkv, T_cap, d // 32), torch.randn(B, Hkv, R_cap, d, device=dev).half(),
+                          torch.randn(B, Hkv, R_cap, d, device=dev).half(), rope_theta=cfg["rope_theta"],
+                          T_q=T_q0, R=R_cap)
+    kn = torch.randn(B, Hkv, 1, d, device=dev).half()
+    vn = torch.randn(B, Hkv, 1, d, device=dev).half()
+    cache.T_q, cache.R = T_q0, R_cap
+    st = cache.struct()
+    ws = torch.empty(dqa.lib.kivi_append_workspace_bytes(ctypes.byref(st), 1), dtype=torch.uint8, device=dev)
+
+    def call(i):
+        cache.T_q, cache.R = T_q0, R_cap
+        dqa.kivi_append(cache, kn, vn, 128, workspace=ws)
+
+    ms = _event_ms(torch, call, 50)
+    units = B * Hkv
+    nbytes = units * (2 * d * 2                       # the new token, K and V
+                      + 2 * (R_cap + 1) * d * 2       # the window read
+                      + 2 * (R_cap + 1 - 32) * d * 2  # the kept rows written back
+                      + 2 * 32 * w * 4                # the group's key and value codes
+                      + 2 * d * 2 + 2 * 32 * (d // 32) * 2)   # key and value scales and zeros
+    return {"kivi_append": _hbm_row("quantize_k_kernel + quantize_v_kernel + row copies", cfg["workload"], ms,
+                                    nbytes, "one token into a full window: one 32-token group quantized per "
+                                    "(batch, KV head); five small launches, latency-bound")}
 
 
 def time_zoned(dqa, torch, dev):
@@ -349,6 +386,7 @@ def main():
     del src, dst
 
     if not args.no_rows:
+        rows.update(time_append(dqa, torch, dev, cfg, bits))
         rows.update(time_zoned(dqa, torch, dev))
         rows.update(time_rvq(dqa, torch, dev))
         line["rows"] = rows
