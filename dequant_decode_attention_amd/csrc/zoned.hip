@@ -714,7 +714,7 @@ extern "C" int zoned_plan(const int8_t* v_bits, const int8_t* k_bits, int B, int
   }
   for (size_t i = 0; i < static_cast<size_t>(units) * d; ++i) {
     const int w = k_bits[i];
-    if (w != 2 && w != 4 && w != 8 && w != 16) return DQA_ERR_BITS;
+    if (w != 0 && w != 2 && w != 4 && w != 8 && w != 16) return DQA_ERR_BITS;
   }
   for (size_t i = 0; i < need; ++i) plan[i] = 0;
   plan[H_MAGIC] = kPlanMagic;
@@ -747,6 +747,10 @@ extern "C" int zoned_plan(const int8_t* v_bits, const int8_t* k_bits, int B, int
       U[U_M + ci] = m;
       U[U_KWORDS + ci] = (m * kSegW[ci] + 31) / 32;
     }
+    // evicted key channels (width 0) close the permutation; they are stored
+    // nowhere and read by no product
+    for (int c = 0; c < d; ++c)
+      if (kb[c] == 0) perm[np++] = c;
     int nt = 0;
     for (int si = 0; si < 4; ++si) {
       U[U_TOK_PREFIX + si] = nt;

@@ -201,8 +201,11 @@ int kivi_append(dqa_kivi_cache* cache, const uint16_t* k_new, const uint16_t* v_
  * [P3 sec 2.2, TriZone packed decoding])
  *
  * Value width per (batch, KV head, token) in {0, 2, 4, 8, 16}; key width
- * per (batch, KV head, channel) in {2, 4, 8, 16}.  Width 0 evicts the token
- * (key and value).  Zone A: kept tokens grouped into segments by value
+ * per (batch, KV head, channel) in {0, 2, 4, 8, 16}.  Value width 0 evicts
+ * the token (key and value); key width 0 evicts the channel from the kept
+ * old tokens' keys ([P3 sec 2.1]: a key channel's weight is the logit change
+ * of zeroing it), which then read 0 there; the new tokens of zone C keep
+ * every channel.  Zone A: kept tokens grouped into segments by value
  * width (2, 4, 8, 16), each cut into 32-slot groups (last one padded with
  * masked slots); per group the key rows (channels grouped into width
  * classes 2, 4, 8, 16; one scale/zero per (group, quantized channel); 16-bit
@@ -217,7 +220,7 @@ size_t zoned_plan_words(int B, int Hkv, int T_old, int d);
 
 /* Build the plan on the host from the width maps.
  *   v_bits (host) int8 [B][Hkv][T_old], values in {0,2,4,8,16}
- *   k_bits (host) int8 [B][Hkv][d], values in {2,4,8,16}
+ *   k_bits (host) int8 [B][Hkv][d], values in {0,2,4,8,16}
  *   C_new  new fp16 tokens per unit, 0..256;  d in {64, 128}
  *   plan   (host) int32 [plan_words], plan_words >= zoned_plan_words(...)
  *   blob_bytes (host) receives the size of the packed blob

@@ -7,7 +7,9 @@ TriZone packed decoding]):
 
 * bit widths come from the set {0, 2, 4, 8, 16}; width 0 means the unit is
   evicted.  Values get a width per token; keys get a width per channel, for
-  the tokens that were kept, independently of the token's value width.
+  the tokens that were kept, independently of the token's value width
+  ([P3 sec 2.1]: a key channel's weight is the logit deviation caused by
+  zeroing that channel, so an evicted key channel is a zeroed one).
 * zone A holds the packed old cache -- key rows and the kept value rows at 2,
   4 or 8 bits -- grouped by width so that each group dequantizes uniformly;
   zone B holds the fp16 value rows of 16-bit tokens; zone C holds fp16 keys
@@ -19,6 +21,9 @@ Readings (the pages give neither formulas nor byte layouts); all of them are
 listed in DESIGN.md:
 
 * a token whose value width is 0 is dropped together with its key.
+* a key channel whose width is 0 is not stored: the kept old tokens' keys
+  read 0 in that channel.  The new tokens of zone C keep every channel
+  (the widths are assigned to the cache present after prefill).
 * kept tokens are partitioned by value width into four segments, in the
   order 2, 4, 8, 16, keeping token order inside a segment; each segment is
   cut into groups of 32 slots, the last group padded with masked slots.
@@ -101,7 +106,8 @@ def zoned_layout(v_bits, k_bits, d, C):
     """Layout of every unit.
 
     v_bits : int array [B, Hkv, T_old] with values in {0, 2, 4, 8, 16}
-    k_bits : int array [B, Hkv, d] with values in {2, 4, 8, 16}
+    k_bits : int array [B, Hkv, d] with values in {0, 2, 4, 8, 16} (0: the
+             channel is evicted and not stored)
     Returns (list of per-unit layout dicts with an added 'base' byte offset,
     total blob size in bytes).
     """
@@ -159,7 +165,7 @@ def _dequant_unit(k16u, v16u, vb, kb, lay):
     ks, vs = [], []
     for w in SEGMENT_WIDTHS:
         for codes, scale, zero, raw, t in kq[w]:
-            kh = np.empty((len(t), d))
+            kh = np.zeros((len(t), d))                      # evicted key channels read 0
             kh[:, qchan] = codes * scale.astype(np.float64) + zero.astype(np.float64)
             kh[:, raw_chan] = raw.astype(np.float64)
             ks.append(kh)

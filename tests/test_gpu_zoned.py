@@ -42,6 +42,8 @@ CASES = [
     (1, 4, 2, 128, 128, 5, {2: 1.0}, {2: 1.0}),             # single width class
     (1, 4, 1, 64, 64, 4, {0: 1.0}, PK),                     # everything evicted: zone C only
     (2, 4, 2, 128, 1000, 64, {0: .3, 8: .7}, {8: .5, 16: .5}),
+    (1, 4, 2, 128, 300, 16, PV, {0: .25, 2: .25, 4: .2, 8: .15, 16: .15}),   # evicted key channels
+    (1, 4, 1, 64, 100, 4, PV, {0: 1.0}),                                    # every key channel evicted
 ]
 
 

@@ -164,3 +164,25 @@ def test_directional_values_per_token_under_peaked_attention():
     c, s, z = oracle.quantize_k(v, 2)
     e_ch = np.linalg.norm(p @ oracle.dequantize_k(c, s, z)[0, 0] - exact)
     assert e_tok < e_ch
+
+
+def test_key_width_zero_is_a_zeroed_channel():
+    """A key channel of width 0 ([P3 sec 2.1]: weight = logit change when the
+    channel is zeroed) equals that channel stored raw with every old token's
+    key component set to 0, bit for bit; the new tokens keep the channel."""
+    inp = _small(3, pk={0: 0.3, 2: 0.3, 4: 0.2, 16: 0.2})
+    ev = inp["k_bits"] == 0
+    assert ev.sum() > 5 and (~ev).sum() > 5
+    o = _zoned(inp)
+    k2, kb2 = inp["k"].copy(), inp["k_bits"].copy()
+    for b, h in np.ndindex(ev.shape[:2]):
+        k2[b, h][:, ev[b, h]] = 0
+        kb2[b, h][ev[b, h]] = 16
+    np.testing.assert_array_equal(o, _zoned(dict(inp, k=k2, k_bits=kb2)))
+    # evicting differs from keeping the channel at full precision
+    kb3 = np.where(ev, 16, inp["k_bits"]).astype(inp["k_bits"].dtype)
+    assert not np.allclose(o, _zoned(dict(inp, k_bits=kb3)))
+    # every key channel evicted: old tokens all score 0 against every query
+    o0 = _zoned(dict(inp, k_bits=np.zeros_like(inp["k_bits"])))
+    k4 = np.zeros_like(inp["k"])
+    np.testing.assert_array_equal(o0, _zoned(dict(inp, k=k4, k_bits=np.full_like(inp["k_bits"], 16))))
