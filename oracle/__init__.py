@@ -77,3 +77,13 @@ from .stream import (
     flush_count,
     kivi_append,
 )
+from .rdkv import (
+    token_weights,
+    token_weight_rows,
+    channel_weights,
+    widths_at,
+    multiplier,
+    allocate,
+    budget_bits,
+    rdkv_widths,
+)

@@ -15,6 +15,7 @@ import test_oracle_rvq as TR
 import test_oracle_zoned as TZ
 import test_oracle_stream as TS
 import oracle.stream as ost
+import oracle.rdkv as orr
 
 _orig_qg = oq.quantize_groups
 
@@ -226,3 +227,94 @@ def test_stream_mutants_are_caught(monkeypatch):
     monkeypatch.setattr(ost, "flush_count", flush_at_bound)
     with pytest.raises(AssertionError):
         TS.test_hand_counted_flushes_one_token_at_a_time()
+
+
+def _run_rdkv_pins():
+    import test_oracle_rdkv as TK
+    for name in dir(TK):
+        if name.startswith("test_"):
+            getattr(TK, name)()
+
+
+def _token_weights_variant(axis=0, upper=False, modulo=False):
+    def tw(q16, k16, sm_scale):
+        q = np.asarray(q16, np.float16).astype(np.float64)
+        k = np.asarray(k16, np.float16).astype(np.float64)
+        B, Hq, T, d = q.shape
+        Hkv = k.shape[1]
+        G = Hq // Hkv
+        w = np.zeros((B, Hkv, T))
+        mask = np.tril(np.ones((T, T), bool))
+        if upper:
+            mask = mask.T
+        for b in range(B):
+            for h in range(Hq):
+                kv = h % Hkv if modulo else h // G
+                s = sm_scale * (q[b, h] @ k[b, kv].T)
+                s = np.where(mask, s, -np.inf)
+                p = np.exp(s - s.max(axis=1, keepdims=True))
+                p /= p.sum(axis=1, keepdims=True)
+                w[b, kv] += p.sum(axis=axis)
+        return w
+    return tw
+
+
+def _channel_weights_variant(per_head=False, no_keep=False, no_sqrt_d=False):
+    def cw(q16, k16, keep):
+        q = np.asarray(q16, np.float16).astype(np.float64)
+        k = np.asarray(k16, np.float16).astype(np.float64)
+        B, Hq, T, d = q.shape
+        Hkv = k.shape[1]
+        G = Hq // Hkv
+        w = np.zeros((B, Hkv, d))
+        for b in range(B):
+            for h in range(Hkv):
+                heads = slice(h * G, h * G + 1) if per_head else slice(h * G, (h + 1) * G)
+                qn = np.sqrt((q[b, heads] ** 2).sum(axis=(0, 1)))
+                kept = np.ones(T, bool) if no_keep else np.asarray(keep[b, h]) != 0
+                kn = np.sqrt((k[b, h][kept] ** 2).sum(axis=0))
+                w[b, h] = qn * kn / (1.0 if no_sqrt_d else np.sqrt(d))
+        return w
+    return cw
+
+
+def _widths_at_ties_up(w, lam):
+    w = np.asarray(w, np.float64)
+    b = np.zeros(w.shape, np.int64)
+    for f, inc in orr.BREAKPOINTS:
+        b += inc * (lam <= w * f)
+    return b.astype(np.int8)
+
+
+def _multiplier_variant(pick):
+    def mult(w, budget):
+        w = np.asarray(w, np.float64).ravel()
+        if np.any(~np.isfinite(w)) or np.any(w < 0) or budget < 0:
+            raise ValueError("bad input")
+        cands = np.unique(np.concatenate([[0.0]] + [w * f for f, _ in orr.BREAKPOINTS]))
+        tot = np.array([orr.widths_at(w, c).astype(int).sum() for c in cands])
+        return cands[pick(np.flatnonzero(tot <= budget))]
+    return mult
+
+
+RDKV_MUTANTS = {
+    "row_sums": ("token_weights", _token_weights_variant(axis=1)),
+    "anti_causal": ("token_weights", _token_weights_variant(upper=True)),
+    "modulo_heads": ("token_weights", _token_weights_variant(modulo=True)),
+    "one_head_query_norm": ("channel_weights", _channel_weights_variant(per_head=True)),
+    "evicted_keys_counted": ("channel_weights", _channel_weights_variant(no_keep=True)),
+    "no_sqrt_d": ("channel_weights", _channel_weights_variant(no_sqrt_d=True)),
+    "ties_to_larger": ("widths_at", _widths_at_ties_up),
+    "largest_fitting_multiplier": ("multiplier", _multiplier_variant(lambda ok: ok[-1])),
+    "multiplier_one_step_low": ("multiplier", _multiplier_variant(lambda ok: max(ok[0] - 1, 0))),
+}
+
+
+@pytest.mark.parametrize("name", sorted(RDKV_MUTANTS))
+def test_rdkv_mutants_are_caught(monkeypatch, name):
+    _run_rdkv_pins()
+    attr, fn = RDKV_MUTANTS[name]
+    monkeypatch.setattr(orr, attr, fn)
+    monkeypatch.setattr(oracle, attr, fn)
+    with pytest.raises(AssertionError):
+        _run_rdkv_pins()
