@@ -223,6 +223,54 @@ def time_zoned(dqa, torch, dev):
     return out
 
 
+def time_rdkv(dqa, torch, dev):
+    """RDKV allocation on the mixed-width cache's shape (c4: 2 sequences, 32
+    query heads over 8 KV heads, 16384 prefill positions, d = 128): token
+    weights (two causal logit passes on the matrix cores, one exponential per
+    causal pair and pass), channel weights (one read of q and k), and the
+    two Lagrangian allocations; the budgets are the mean widths of c4's maps."""
+    from workloads import CONFIGS, rdkv_inputs
+    cfg = CONFIGS["c4"]
+    B, Hq, Hkv, d, T = cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["d"], cfg["T_old"]
+    inp = rdkv_inputs(B, Hq, Hkv, d, T, seed=4, outliers=cfg["outliers"])
+    q, k = torch.from_numpy(inp["q"]).to(dev), torch.from_numpy(inp["k"]).to(dev)
+    del inp
+    scale = 1.0 / math.sqrt(d)
+    vm, km = cfg["rdkv_mean_widths"]
+    vbud, kbud = int(math.floor(vm * Hkv * T)), int(math.floor(km * Hkv * d))
+    wl = cfg["workload"] + "-prefill"
+    ws = torch.empty(dqa.lib.rdkv_widths_workspace_bytes(B, Hq, Hkv, T, d), dtype=torch.uint8, device=dev)
+    ms_all = _event_ms(torch, lambda i: dqa.rdkv_widths(q, k, scale, vbud, kbud, workspace=ws), 5, warmup=1)
+    wst = torch.empty(max(dqa.lib.rdkv_token_weights_workspace_bytes(B, Hq, T), 1), dtype=torch.uint8,
+                      device=dev)
+    ms = _event_ms(torch, lambda i: dqa.rdkv_token_weights(q, k, scale, workspace=wst), 5, warmup=1)
+    pairs = T * (T + 1) // 2
+    flop = 2 * 2 * d * pairs * B * Hq
+    tf = flop / (ms * 1e-3) / 1e12
+    out = {"rdkv_token_weights": {
+        "kernel": "rdkv_lse_kernel + rdkv_colsum_kernel", "workload": wl, "us": ms * 1e3, "bound": "mfma",
+        "algorithmic_flop": flop, "achieved": tf, "peak": MFMA_FP16_PEAK_TFLOPS, "unit": "TFLOP/s",
+        "frac": tf / MFMA_FP16_PEAK_TFLOPS,
+        "exp_per_s": 2 * pairs * B * Hq / (ms * 1e-3),
+        "note": "two passes over the causal logits (2 d flop per pair and pass); the exponentials "
+                "on the vector ALU, not the matrix cores, set the pace"}}
+    wt = dqa.rdkv_token_weights(q, k, scale, workspace=wst)
+    vb = dqa.rdkv_allocate(wt.reshape(B, -1), vbud).reshape(B, Hkv, T)
+    ms = _event_ms(torch, lambda i: dqa.rdkv_channel_weights(q, k, vb), 10)
+    nbytes = q.numel() * 2 + k.numel() * 2 + vb.numel()
+    out["rdkv_channel_weights"] = _hbm_row("rdkv_chan_partial_kernel", wl, ms, nbytes)
+    wsa = torch.empty(dqa.lib.rdkv_allocate_workspace_bytes(B, Hkv * T), dtype=torch.uint8, device=dev)
+    wflat = wt.reshape(B, -1)
+    ms = _event_ms(torch, lambda i: dqa.rdkv_allocate(wflat, vbud, workspace=wsa), 20)
+    out["rdkv_allocate"] = _hbm_row("rdkv_hist_kernel + rdkv_select_kernel", wl, ms,
+                                    wflat.numel() * (4 * 7 + 1),
+                                    "value widths of 2 x 131072 tokens; 13 small launches: latency-bound")
+    out["rdkv_widths"] = {"workload": wl, "us": ms_all * 1e3,
+                          "note": "all three phases in one call (token weights, value widths, channel "
+                                  "weights over kept tokens, key widths)"}
+    return out
+
+
 def time_rvq(dqa, torch, dev):
     """Rows a10-a11 on the residual-VQ workload (c5): encoding of every key
     and value vector (MFMA-bound: 2 N Kc d flop per vector) and decode
@@ -389,6 +437,7 @@ def main():
         rows.update(time_append(dqa, torch, dev, cfg, bits))
         rows.update(time_zoned(dqa, torch, dev))
         rows.update(time_rvq(dqa, torch, dev))
+        rows.update(time_rdkv(dqa, torch, dev))
         line["rows"] = rows
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp, cfg, bits, scale)

@@ -69,6 +69,15 @@ _SIGS = {
     "rvq_decode_attention_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "rvq_decode_attention": (_i, [_vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _i, _i, _f,
                                   _vp, _sz, _vp, _vp]),
+    "rdkv_token_weights_workspace_bytes": (_sz, [_i, _i, _i]),
+    "rdkv_token_weights": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _f, _vp, _vp, _sz, _vp]),
+    "rdkv_channel_weights_workspace_bytes": (_sz, [_i, _i, _i, _i]),
+    "rdkv_channel_weights": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _sz, _vp]),
+    "rdkv_allocate_workspace_bytes": (_sz, [_i, _i]),
+    "rdkv_allocate": (_i, [_vp, _i, _i, ctypes.c_longlong, _vp, _vp, _sz, _vp]),
+    "rdkv_widths_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
+    "rdkv_widths": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _f, ctypes.c_longlong, ctypes.c_longlong,
+                         _vp, _vp, _vp, _sz, _vp]),
     "dqa_stream_copy": (_i, [_vp, _vp, _sz, _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
@@ -327,6 +336,76 @@ def rvq_decode_attention(q, k_idx, v_idx, k_codebooks, v_codebooks, sm_scale, ou
                                     float(sm_scale), _ptr(workspace), workspace.numel(),
                                     _ptr(out), _stream(q.device)))
     return out
+
+
+# ---------------------------------------------------------------- RDKV
+
+def _ws(nbytes, device):
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def rdkv_token_weights(q, k, sm_scale, workspace=None):
+    """q fp16 [B, Hq, T, d], k fp16 [B, Hkv, T, d] -> fp32 [B, Hkv, T]."""
+    q, k = _dev16(q, "q"), _dev16(k, "k")
+    B, Hq, T, d = q.shape
+    Hkv = k.shape[1]
+    w = torch.empty((B, Hkv, T), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = _ws(lib.rdkv_token_weights_workspace_bytes(B, Hq, T), q.device)
+    _check("rdkv_token_weights",
+           lib.rdkv_token_weights(_ptr(q), _ptr(k), B, Hq, Hkv, T, d, float(sm_scale), _ptr(w),
+                                  _ptr(workspace), workspace.numel(), _stream(q.device)))
+    return w
+
+
+def rdkv_channel_weights(q, k, keep, workspace=None):
+    """q, k as rdkv_token_weights; keep int8 [B, Hkv, T] -> fp32 [B, Hkv, d]."""
+    q, k = _dev16(q, "q"), _dev16(k, "k")
+    B, Hq, T, d = q.shape
+    Hkv = k.shape[1]
+    if keep.dtype != torch.int8 or not keep.is_cuda:
+        raise TypeError("keep must be a CUDA int8 tensor")
+    keep = keep.contiguous()
+    w = torch.empty((B, Hkv, d), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = _ws(lib.rdkv_channel_weights_workspace_bytes(B, Hkv, T, d), q.device)
+    _check("rdkv_channel_weights",
+           lib.rdkv_channel_weights(_ptr(q), _ptr(k), _ptr(keep), B, Hq, Hkv, T, d, _ptr(w),
+                                    _ptr(workspace), workspace.numel(), _stream(q.device)))
+    return w
+
+
+def rdkv_allocate(w, budget, workspace=None):
+    """w fp32 [..., n] -> int8 widths of the same shape; one allocation per
+    row (last axis), each row's total <= budget bits."""
+    if w.dtype != torch.float32 or not w.is_cuda:
+        raise TypeError("w must be a CUDA float32 tensor")
+    w = w.contiguous()
+    n = w.shape[-1] if w.dim() else 1
+    rows = w.numel() // n if n else 0
+    out = torch.empty(w.shape, dtype=torch.int8, device=w.device)
+    if workspace is None:
+        workspace = _ws(lib.rdkv_allocate_workspace_bytes(rows, n), w.device)
+    _check("rdkv_allocate", lib.rdkv_allocate(_ptr(w), rows, n, int(budget), _ptr(out), _ptr(workspace),
+                                              workspace.numel(), _stream(w.device)))
+    return out
+
+
+def rdkv_widths(q, k, sm_scale, v_budget, k_budget, workspace=None):
+    """All three phases: (v_bits int8 [B, Hkv, T], k_bits int8 [B, Hkv, d]),
+    per-sequence budgets in bits."""
+    q, k = _dev16(q, "q"), _dev16(k, "k")
+    B, Hq, T, d = q.shape
+    Hkv = k.shape[1]
+    v_bits = torch.empty((B, Hkv, T), dtype=torch.int8, device=q.device)
+    k_bits = torch.empty((B, Hkv, d), dtype=torch.int8, device=q.device)
+    if workspace is None:
+        workspace = _ws(lib.rdkv_widths_workspace_bytes(B, Hq, Hkv, T, d), q.device)
+    _check("rdkv_widths",
+           lib.rdkv_widths(_ptr(q), _ptr(k), B, Hq, Hkv, T, d, float(sm_scale), int(v_budget),
+                           int(k_budget), _ptr(v_bits), _ptr(k_bits), _ptr(workspace),
+                           workspace.numel(), _stream(q.device)))
+    return v_bits, k_bits
 
 
 def stream_copy(src, dst):

@@ -56,7 +56,8 @@ enum {
 const char* dqa_status_string(int status);
 
 /* Version of this interface (increments on any signature or layout change). */
-int dqa_abi_version(void);  /* 4: dqa_kivi_cache carries buffer capacities
+int dqa_abi_version(void);  /* 5: RDKV allocation entry points (rdkv_*);
+                              4: dqa_kivi_cache carries buffer capacities
                               (T_cap, R_cap) and kivi_append exists;
                               3: 16-byte pointer alignment checked */
 
@@ -301,6 +302,74 @@ int rvq_decode_attention(const uint16_t* q, int B, int Hq, int Hkv, int T,
                          const uint16_t* v_codebooks, int N, int Kc,
                          float sm_scale, void* ws, size_t ws_bytes, float* out,
                          void* stream);
+
+/* ------------------------------------------------------------------------
+ * RDKV bit allocation ([P3 sec 2.1, theoretical formulation]; [P3 sec 2.2,
+ * bit-allocation pipeline]): distortion weights of the cache units, and the
+ * widths in {0, 2, 4, 8, 16} that minimize sum_u w_u 2^(-b_u) under a total
+ * budget sum_u b_u <= B by Lagrangian relaxation.  The maps feed zoned_plan.
+ * Widths at multiplier lam: 2[lam < 3w/8] + 2[lam < 3w/32]
+ * + 4[lam < 15w/1024] + 8[lam < 255w/524288] (the minimizer of
+ * w 2^(-b) + lam b, ties to the smaller width); lam is the smallest value at
+ * which a row's widths fit its budget, found exactly (float64 breakpoints of
+ * float32 weights).  Weights that are NaN, negative or -0 count as 0;
+ * weights must otherwise be finite.  Supported head dims d: 64 and 128
+ * (else DQA_ERR_UNSUPPORTED); sm_scale must be positive and finite.
+ * ------------------------------------------------------------------------ */
+
+/* Workspace bytes for rdkv_token_weights: the per-row log-sum-exp. */
+size_t rdkv_token_weights_workspace_bytes(int B, int Hq, int T);
+
+/* Token weights w_t = sum over query positions tau >= t of the causal
+ * prefill attention a_{tau,t} (logits scaled by sm_scale), summed over the
+ * G = Hq/Hkv query heads that read each KV head.
+ *   q (device) fp16 [B][Hq][T][d] (every prefill query position),
+ *   k (device) fp16 [B][Hkv][T][d] (keys as attention reads them),
+ *   both 16-byte aligned; w (device) fp32 [B][Hkv][T].
+ * Deterministic (no atomics).  Errors: DQA_ERR_NULL, DQA_ERR_SHAPE,
+ * DQA_ERR_UNSUPPORTED, DQA_ERR_ALIGN, DQA_ERR_WORKSPACE, DQA_ERR_HIP. */
+int rdkv_token_weights(const uint16_t* q, const uint16_t* k, int B, int Hq,
+                       int Hkv, int T, int d, float sm_scale, float* w,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes for rdkv_channel_weights (0 if invalid or T == 0). */
+size_t rdkv_channel_weights_workspace_bytes(int B, int Hkv, int T, int d);
+
+/* Channel weights w_c = ||Q_{:,c}|| ||K_{kept,c}|| / sqrt(d): the query
+ * column over every position of the KV head's G query heads, the key
+ * column over the tokens whose keep entry is nonzero.
+ *   q, k as in rdkv_token_weights; keep (device) int8 [B][Hkv][T] (e.g.
+ *   the value widths: 0 = evicted); w (device) fp32 [B][Hkv][d].
+ * Errors: DQA_ERR_NULL, DQA_ERR_SHAPE, DQA_ERR_UNSUPPORTED, DQA_ERR_ALIGN,
+ * DQA_ERR_WORKSPACE, DQA_ERR_HIP. */
+int rdkv_channel_weights(const uint16_t* q, const uint16_t* k,
+                         const int8_t* keep, int B, int Hq, int Hkv, int T,
+                         int d, float* w, void* ws, size_t ws_bytes,
+                         void* stream);
+
+/* Workspace bytes for rdkv_allocate. */
+size_t rdkv_allocate_workspace_bytes(int rows, int n);
+
+/* One Lagrangian allocation per row: w (device) fp32 [rows][n] ->
+ * widths (device) int8 [rows][n], each row's total <= budget (bits).
+ * rows <= 65535, budget >= 0.  Errors: DQA_ERR_NULL, DQA_ERR_SHAPE,
+ * DQA_ERR_WORKSPACE, DQA_ERR_HIP. */
+int rdkv_allocate(const float* w, int rows, int n, long long budget,
+                  int8_t* widths, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes for rdkv_widths (0 if the shape is invalid). */
+size_t rdkv_widths_workspace_bytes(int B, int Hq, int Hkv, int T, int d);
+
+/* The three phases in one call, one allocation per sequence over all of its
+ * KV heads: token weights; value widths v_bits (device) int8 [B][Hkv][T]
+ * with sum over a sequence <= v_budget; channel weights over the tokens
+ * with nonzero value width; key widths k_bits (device) int8 [B][Hkv][d]
+ * with sum over a sequence <= k_budget.  Inputs as in rdkv_token_weights.
+ * Errors: those of the three steps. */
+int rdkv_widths(const uint16_t* q, const uint16_t* k, int B, int Hq, int Hkv,
+                int T, int d, float sm_scale, long long v_budget,
+                long long k_budget, int8_t* v_bits, int8_t* k_bits, void* ws,
+                size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * Measurement helper (not part of the method): a plain streaming copy used

@@ -26,7 +26,8 @@ def test_header_declares_the_entry_points():
     names = _declared()
     for n in ["quantize_pack_k", "quantize_pack_v", "decode_attention_qkv", "rvq_encode",
               "rvq_decode_attention", "zoned_plan", "zoned_pack", "decode_attention_zoned",
-              "dqa_status_string"]:
+              "dqa_status_string", "kivi_append", "rdkv_token_weights", "rdkv_channel_weights",
+              "rdkv_allocate", "rdkv_widths"]:
         assert n in names
 
 
@@ -158,8 +159,11 @@ def test_zoned_plan_validation():
     bad_v[0, 0, 5] = 3
     assert _plan(bad_v, kb, 0, 128)[0] == 3
     bad_k = kb.copy()
-    bad_k[0, 0, 1] = 0              # keys have no width 0
+    bad_k[0, 0, 1] = 3              # not a width of the set
     assert _plan(vb, bad_k, 0, 128)[0] == 3
+    evict_k = kb.copy()
+    evict_k[0, 0, 1] = 0            # width 0 evicts a key channel
+    assert _plan(vb, evict_k, 0, 128)[0] == 0
     assert _plan(vb, kb, 300, 128)[0] == 2                  # C too large
     assert lib.zoned_plan_words(1, 1, 64, 96) == 0
     n = lib.zoned_plan_words(1, 1, 64, 128)
@@ -209,7 +213,7 @@ def test_rvq_validation_and_workspace():
 
 def test_kivi_append_validation():
     """Argument checks of the streaming append (all fail before any launch)."""
-    assert lib.dqa_abi_version() == 4
+    assert lib.dqa_abi_version() == 5
     c = _cache(T_cap=128, R_cap=128)
     # staging holds the recent and the new rows of K and V
     assert lib.kivi_append_workspace_bytes(ctypes.byref(c), 20) == 2 * 2 * 2 * (16 + 20) * 128 * 2
@@ -244,3 +248,61 @@ def test_kivi_append_validation():
     c1 = _cache(B=0, T_cap=128, R_cap=128)
     assert lib.kivi_append(ctypes.byref(c1), FAKE, FAKE, 40, 16, None, 0, None) == 0
     assert (c1.T_q, c1.R) == (64 + 32, 16 + 40 - 32)
+
+
+def test_rdkv_validation():
+    """Argument checks of the RDKV allocation entry points (all fail before
+    any launch)."""
+    assert lib.rdkv_token_weights_workspace_bytes(2, 32, 1000) == 256 * ((2 * 32 * 1000 * 4 + 255) // 256)
+    tw = lambda **k: lib.rdkv_token_weights(*[k.get(n, v) for n, v in [
+        ("q", FAKE), ("k", FAKE), ("B", 2), ("Hq", 8), ("Hkv", 2), ("T", 100), ("d", 128),
+        ("sc", 0.1), ("w", FAKE), ("ws", FAKE), ("wsb", 1 << 20), ("st", None)]])
+    assert tw(d=96) == 5
+    assert tw(Hq=6, Hkv=4) == 2
+    assert tw(sc=0.0) == 2
+    assert tw(sc=-1.0) == 2
+    assert tw(sc=float("nan")) == 2
+    assert tw(q=None) == 1
+    assert tw(w=None) == 1
+    assert tw(k=ctypes.c_void_p(0x1008)) == 8
+    assert tw(wsb=100) == 4
+    assert tw(ws=None) == 4
+    assert tw(T=0, q=None, k=None, w=None) == 0            # empty: no work
+    assert tw(B=0, q=None, k=None, w=None) == 0
+    assert tw(B=40000, Hkv=2) == 2                          # B * Hkv above a grid dimension
+    cw = lambda **k: lib.rdkv_channel_weights(*[k.get(n, v) for n, v in [
+        ("q", FAKE), ("k", FAKE), ("keep", FAKE), ("B", 2), ("Hq", 8), ("Hkv", 2), ("T", 100),
+        ("d", 64), ("w", FAKE), ("ws", FAKE), ("wsb", 1 << 20), ("st", None)]])
+    assert lib.rdkv_channel_weights_workspace_bytes(2, 2, 100, 64) == 256 * ((1 * 2 * 2 * 2 * 64 * 4 + 255) // 256)
+    assert lib.rdkv_channel_weights_workspace_bytes(2, 2, 100, 96) == 0
+    assert cw(keep=None) == 1
+    assert cw(d=32) == 5
+    assert cw(wsb=16) == 4
+    assert cw(k=ctypes.c_void_p(0x1004)) == 8
+    al = lambda **k: lib.rdkv_allocate(*[k.get(n, v) for n, v in [
+        ("w", FAKE), ("rows", 2), ("n", 5000), ("bud", 100), ("out", FAKE), ("ws", FAKE),
+        ("wsb", 1 << 20), ("st", None)]])
+    # per row state (32 bytes) then 2048-bin histograms per 4096-weight chunk
+    assert lib.rdkv_allocate_workspace_bytes(2, 5000) == 256 + 2 * 2 * 2048 * 4
+    assert al(bud=-1) == 2
+    assert al(rows=70000) == 2
+    assert al(n=-1) == 2
+    assert al(w=None) == 1
+    assert al(out=None) == 1
+    assert al(wsb=256) == 4
+    assert al(rows=0, w=None, out=None, ws=None) == 0
+    assert al(n=0, w=None, out=None, ws=None) == 0
+    wd = lambda **k: lib.rdkv_widths(*[k.get(n, v) for n, v in [
+        ("q", FAKE), ("k", FAKE), ("B", 2), ("Hq", 8), ("Hkv", 2), ("T", 100), ("d", 128),
+        ("sc", 0.1), ("vb", 300), ("kb", 300), ("v", FAKE), ("kbits", FAKE), ("ws", FAKE),
+        ("wsb", 1 << 30), ("st", None)]])
+    need = lib.rdkv_widths_workspace_bytes(2, 8, 2, 100, 128)
+    assert need > lib.rdkv_token_weights_workspace_bytes(2, 8, 100)
+    assert lib.rdkv_widths_workspace_bytes(2, 8, 2, 100, 80) == 0
+    assert wd(vb=-1) == 2
+    assert wd(kb=-1) == 2
+    assert wd(v=None) == 1
+    assert wd(kbits=None) == 1
+    assert wd(wsb=need - 1) == 4
+    assert wd(d=80) == 5
+    assert wd(B=0, q=None, k=None, v=None, kbits=None, ws=None) == 0

@@ -35,7 +35,10 @@ CONFIGS = {
                Hkv=8, d=128, T_old=16384, C=64,
                v_width_probs={0: 0.5, 2: 0.2, 4: 0.15, 8: 0.1, 16: 0.05},
                k_width_probs={2: 0.4, 4: 0.3, 8: 0.2, 16: 0.1},
-               outliers=("lognormal", 0.04, 3.0, 1.0)),
+               outliers=("lognormal", 0.04, 3.0, 1.0),
+               # mean widths of the maps above (value bits per token, key bits
+               # per channel): the budgets of the allocator on this cache
+               rdkv_mean_widths=(2.6, 5.2)),
     # residual-VQ cache, Llama-3.2-3B shape: 4 codebooks x 1024 entries
     "c5": dict(workload="rvq-llama3.2-3b-8k", kind="rvq", B=2, Hq=24, Hkv=8,
                d=128, T=8192, N=4, Kc=1024),
@@ -100,6 +103,18 @@ def zoned_inputs(B, Hq, Hkv, d, T_old, C, seed, v_width_probs, k_width_probs,
     return dict(q=q, k=k[:, :, :T_old].copy(), v=v[:, :, :T_old].copy(),
                 k_new=k[:, :, T_old:].copy(), v_new=v[:, :, T_old:].copy(),
                 v_bits=v_bits, k_bits=k_bits)
+
+
+def rdkv_inputs(B, Hq, Hkv, d, T, seed, outliers=None):
+    """Prefill queries [B, Hq, T, d] (every position) and keys [B, Hkv, T, d]
+    (fp16), keys with the outlier channels of ``outliers``."""
+    rng = np.random.default_rng(seed)
+    q = _normal16(rng, (B, Hq, T, d))
+    k32 = rng.standard_normal(size=(B, Hkv, T, d), dtype=np.float32)
+    _outlier_keys(rng, k32, outliers)
+    k = k32.astype(np.float16)
+    del k32
+    return dict(q=q, k=k)
 
 
 def rvq_inputs(B, Hq, Hkv, d, T, N, Kc, seed):
