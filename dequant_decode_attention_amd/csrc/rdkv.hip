@@ -36,6 +36,8 @@
 // a per-chunk histogram (11, ..., 11, 8 bits) and a per-row selection.
 #include "common.h"
 
+#include <type_traits>
+
 namespace dqa {
 namespace {
 
@@ -49,7 +51,7 @@ constexpr int kSumKeys = 128;   // keys per workgroup in pass 2 (4 waves x 32)
 constexpr int kSumRows = 64;    // query rows per LDS tile in pass 2
 constexpr int kChanRows = 256;  // positions per workgroup of the channel sums
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kNegBig = -1.0e30f;  // finite start of a running max
+constexpr float kLazy = 8.0f;        // log2 headroom before the reference max moves
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -71,7 +73,8 @@ __global__ __launch_bounds__(256) void rdkv_lse_kernel(const uint16_t* __restric
   const int qt = nqt - 1 - static_cast<int>(blockIdx.x / heads);  // longest rows first
   const int kv = hu % Hkv, rest = hu / Hkv, g = rest % G, b = rest / G;
   const int h = kv * G + g;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int col = lane & 15, grp = lane >> 4;
   const int q0 = qt * kLseRows + wave * 32;
 
@@ -87,12 +90,12 @@ __global__ __launch_bounds__(256) void rdkv_lse_kernel(const uint16_t* __restric
       a[rb][s] = *reinterpret_cast<const half8*>(qh + static_cast<size_t>(row) * D + 32 * s + 8 * grp);
   }
 
-  float m[2][4], l[2][4];
+  float mc[2][4], l[2][4], tm[2][4];
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      m[rb][r] = kNegBig;
+      mc[rb][r] = 0.0f;
       l[rb][r] = 0.0f;
     }
 
@@ -134,26 +137,60 @@ __global__ __launch_bounds__(256) void rdkv_lse_kernel(const uint16_t* __restric
         acc[1][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[1][s], bf, acc[1][nb], 0, 0, 0);
       }
     }
-    const bool diag = kbase + kLseKeys - 1 > q0;
+    // Per lane and row: l = sum of exp2(c x - mc) against a reference mc
+    // (log2 units).  The reference moves only when a logit passes it by more
+    // than 2^8 (a uniform branch, rare after the first tiles); moving it by
+    // any delta (mc += delta, l *= 2^-delta) leaves the sum exact.  Key tile
+    // 0 always takes that branch: a lane with nothing accumulated yet takes
+    // its own maximum as the reference.  Every wave that reaches a later
+    // tile holds rows >= 64, all of which saw a valid key in tile 0, so no
+    // lane starts its sum after tile 0.
+    auto update = [&](auto masked) {
+      float t[2][4][4];
+      bool need = false;
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+      for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = q0 + 16 * rb + 4 * grp + r;
-        float x[4];
+        for (int r = 0; r < 4; ++r) {
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          x[nb] = acc[rb][nb][r];
-          if (diag && kbase + 16 * nb + col > row) x[nb] = -INFINITY;
+          for (int nb = 0; nb < 4; ++nb) {
+            t[rb][r][nb] = fmaf(acc[rb][nb][r], c, -mc[rb][r]);
+            if constexpr (decltype(masked)::value)
+              if (kbase + 16 * nb + col > q0 + 16 * rb + 4 * grp + r) t[rb][r][nb] = -INFINITY;
+          }
+          tm[rb][r] = fmaxf(fmaxf(t[rb][r][0], t[rb][r][1]), fmaxf(t[rb][r][2], t[rb][r][3]));
+          need |= tm[rb][r] > kLazy;
         }
-        const float tmax = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-        const float mnew = fmaxf(m[rb][r], tmax * c);
-        float sum = l[rb][r] * fast_exp2(m[rb][r] - mnew);
+      if (kt == 0 || __builtin_amdgcn_ballot_w64(need)) {
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) sum += fast_exp2(fmaf(x[nb], c, -mnew));
-        l[rb][r] = sum;
-        m[rb][r] = mnew;
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const bool fresh = l[rb][r] == 0.0f;
+            float delta = fresh ? tm[rb][r] : fmaxf(tm[rb][r], 0.0f);
+            delta = delta > -INFINITY ? delta : 0.0f;  // no valid key in this lane yet
+            mc[rb][r] += delta;
+            float sum = fresh ? 0.0f : l[rb][r] * fast_exp2(-delta);
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) sum += fast_exp2(t[rb][r][nb] - delta);
+            l[rb][r] = sum;
+          }
+      } else {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float sum = l[rb][r];
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) sum += fast_exp2(t[rb][r][nb]);
+            l[rb][r] = sum;
+          }
       }
+    };
+    if (kbase + kLseKeys - 1 > q0)
+      update(std::true_type{});
+    else
+      update(std::false_type{});
   }
 
   float* lrow = lse + (static_cast<size_t>(b) * Hq + h) * static_cast<size_t>(T);
@@ -161,8 +198,9 @@ __global__ __launch_bounds__(256) void rdkv_lse_kernel(const uint16_t* __restric
   for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float M = max_adjacent<16>(m[rb][r]);
-      const float L = sum_adjacent<16>(l[rb][r] * fast_exp2(m[rb][r] - M));
+      const bool has = l[rb][r] > 0.0f;  // lanes that saw no valid key carry nothing
+      const float M = max_adjacent<16>(has ? mc[rb][r] : -INFINITY);
+      const float L = sum_adjacent<16>(has ? l[rb][r] * fast_exp2(mc[rb][r] - M) : 0.0f);
       const int row = q0 + 16 * rb + 4 * grp + r;
       if (col == 0 && row < T) lrow[row] = M + __builtin_amdgcn_logf(L);
     }
@@ -186,7 +224,8 @@ __global__ __launch_bounds__(256) void rdkv_colsum_kernel(const uint16_t* __rest
   const int u = blockIdx.x % units;
   const int kt = static_cast<int>(blockIdx.x / units);  // most rows first
   const int b = u / Hkv, kv = u % Hkv;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int col = lane & 15, grp = lane >> 4;
   const int k0 = kt * kSumKeys + wave * 32;
 
@@ -245,22 +284,29 @@ __global__ __launch_bounds__(256) void rdkv_colsum_kernel(const uint16_t* __rest
         acc[rb][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bk[1][s], acc[rb][1], 0, 0, 0);
       }
     }
-    const bool edge = (r0 < k0 + 31) || (r0 + kSumRows > T);
+    auto accumulate = [&](auto masked) {
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      const float4 ls = *reinterpret_cast<const float4*>(&lds_lse[16 * rb + 4 * grp]);
-      const float lsr[4] = {ls.x, ls.y, ls.z, ls.w};
+      for (int rb = 0; rb < 4; ++rb) {
+        const float4 ls = *reinterpret_cast<const float4*>(&lds_lse[16 * rb + 4 * grp]);
+        const float lsr[4] = {ls.x, ls.y, ls.z, ls.w};
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = r0 + 16 * rb + 4 * grp + r;
+        for (int r = 0; r < 4; ++r) {
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          float p = fast_exp2(fmaf(acc[rb][nb][r], c, -lsr[r]));
-          if (edge && (k0 + 16 * nb + col > row || row >= T)) p = 0.0f;
-          cs[nb] += p;
+          for (int nb = 0; nb < 2; ++nb) {
+            float p = fast_exp2(fmaf(acc[rb][nb][r], c, -lsr[r]));
+            if constexpr (decltype(masked)::value) {
+              const int row = r0 + 16 * rb + 4 * grp + r;
+              if (k0 + 16 * nb + col > row || row >= T) p = 0.0f;
+            }
+            cs[nb] += p;
+          }
         }
       }
-    }
+    };
+    if (r0 < k0 + 31 || r0 + kSumRows > T)  // a key after a row, or rows past the end
+      accumulate(std::true_type{});
+    else
+      accumulate(std::false_type{});
   }
 
   float* wu = w + static_cast<size_t>(u) * T;
