@@ -185,9 +185,9 @@ def test_rvq_mutants_are_caught(monkeypatch):
 def test_zoned_eviction_mutant_is_caught(monkeypatch):
     orig_layout = oz._unit_layout
 
-    def keep_evicted(vb, kb, d, C):
+    def keep_evicted(vb, kb, d, C, sink=0, k_out=0):
         vb = np.where(np.asarray(vb) == 0, 2, vb)         # width 0 kept at 2 bits
-        return orig_layout(vb, kb, d, C)
+        return orig_layout(vb, kb, d, C, sink, k_out)
 
     monkeypatch.setattr(oz, "_unit_layout", keep_evicted)
     with pytest.raises(AssertionError):
@@ -318,3 +318,63 @@ def test_rdkv_mutants_are_caught(monkeypatch, name):
     monkeypatch.setattr(oracle, attr, fn)
     with pytest.raises(AssertionError):
         _run_rdkv_pins()
+
+
+def _iso_variant(tie_low=False, stale_mean=False):
+    def iso(x16, k_out):
+        x = np.asarray(x16, np.float16).astype(np.float32)
+        rem = list(range(len(x)))
+        out = []
+        for _ in range(k_out):
+            if len(rem) <= 2:
+                break
+            xs = x[rem]
+            if xs.min() == xs.max():
+                break
+            src = x if stale_mean else xs
+            total = np.float32(0.0)
+            for v in src:
+                total = np.float32(total + v)
+            mean = np.float32(total / np.float32(len(src)))
+            hi = rem[int(np.argmax(xs))]
+            lo = rem[int(np.argmin(xs))]
+            d_hi, d_lo = abs(np.float32(x[hi] - mean)), abs(np.float32(x[lo] - mean))
+            pick = (hi if d_hi > d_lo else lo) if tie_low else (hi if d_hi >= d_lo else lo)
+            out.append(pick)
+            rem.remove(pick)
+        return sorted(out)
+    return iso
+
+
+def test_zoned_sink_and_outlier_mutants_are_caught(monkeypatch):
+    for name, fn in (("ties_to_smallest", _iso_variant(tie_low=True)),
+                     ("stale_mean", _iso_variant(stale_mean=True))):
+        monkeypatch.setattr(oz, "isolate_outliers", fn)
+        with pytest.raises(AssertionError):
+            TZ.test_outlier_rule_hand_worked()
+    monkeypatch.undo()
+    orig_deq = oz._dequant_unit
+
+    def no_replacement(k16u, v16u, vb, kb, lay):
+        orig = oz._quantize_unit_keys
+
+        def strip(k, l):
+            return {w: [g[:5] + ([],) for g in gs] for w, gs in orig(k, l).items()}
+        oz._quantize_unit_keys = strip
+        try:
+            return orig_deq(k16u, v16u, vb, kb, lay)
+        finally:
+            oz._quantize_unit_keys = orig
+
+    monkeypatch.setattr(oz, "_dequant_unit", no_replacement)
+    with pytest.raises(AssertionError):
+        TZ.test_outlier_attention_and_layout()
+    monkeypatch.undo()
+    orig_layout = oz._unit_layout
+
+    def sink_ignored(vb, kb, d, C, sink=0, k_out=0):
+        return orig_layout(vb, kb, d, C, 0, k_out)          # sink tokens stay in the segments
+
+    monkeypatch.setattr(oz, "_unit_layout", sink_ignored)
+    with pytest.raises(AssertionError):
+        TZ.test_sink_tokens_are_new_tokens_at_the_front()

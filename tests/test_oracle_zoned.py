@@ -186,3 +186,149 @@ def test_key_width_zero_is_a_zeroed_channel():
     o0 = _zoned(dict(inp, k_bits=np.zeros_like(inp["k_bits"])))
     k4 = np.zeros_like(inp["k"])
     np.testing.assert_array_equal(o0, _zoned(dict(inp, k=k4, k_bits=np.full_like(inp["k_bits"], 16))))
+
+
+# ------------------------------------------------------------ sink window
+
+def test_sink_tokens_are_new_tokens_at_the_front():
+    # A sink of S tokens is the same cache as: those tokens evicted from the
+    # old cache and placed (fp16, all channels) before the new tokens.  Both
+    # the byte image and the attention must agree exactly.
+    inp = _small(21, T=150, C=5)
+    S = 9
+    kw = dict(sink=S)
+    o = _zoned(inp, **kw)
+    alt = dict(inp)
+    vb = inp["v_bits"].copy()
+    vb[:, :, :S] = 0
+    alt["v_bits"] = vb
+    alt["k_new"] = np.concatenate([inp["k"][:, :, :S], inp["k_new"]], axis=2)
+    alt["v_new"] = np.concatenate([inp["v"][:, :, :S], inp["v_new"]], axis=2)
+    np.testing.assert_allclose(o, _zoned(alt), rtol=1e-12, atol=1e-14)
+    b1 = zoned_pack(inp["k"], inp["v"], inp["v_bits"], inp["k_bits"], inp["k_new"], inp["v_new"], sink=S)
+    b2 = zoned_pack(alt["k"], alt["v"], alt["v_bits"], alt["k_bits"], alt["k_new"], alt["v_new"])
+    assert np.array_equal(b1, b2)
+    # the sink overrides eviction: a sink changes the result when its tokens
+    # were evicted
+    assert (inp["v_bits"][:, :, :S] == 0).any()
+    assert not np.allclose(o, _zoned(inp))
+
+
+def test_whole_cache_as_sink_is_unquantized_attention():
+    inp = _small(22, T=40, C=3)
+    o = _zoned(inp, sink=40)
+    B, Hq, d = inp["q"].shape
+    for b in range(B):
+        for h in range(Hq):
+            kv = h // 2
+            k = np.concatenate([inp["k"][b, kv], inp["k_new"][b, kv]]).astype(np.float64)
+            v = np.concatenate([inp["v"][b, kv], inp["v_new"][b, kv]]).astype(np.float64)
+            ref = attention_fp64(inp["q"][b, h][None].astype(np.float64), k, v, 0.125)
+            np.testing.assert_allclose(o[b, h], ref[0], rtol=1e-11, atol=1e-13)
+
+
+# ---------------------------------------------------------- outlier list
+
+def test_outlier_rule_hand_worked():
+    iso = oracle.zoned.isolate_outliers
+    # mean of (0, 1, 2, 100) = 25.75: the largest (100) is farther -> slot 3;
+    # then mean(0, 1, 2) = 1: both ends 1 away -> the largest (slot 2); then
+    # two values remain -> stop
+    assert iso(np.array([0, 1, 2, 100], np.float16), 1) == [3]
+    assert iso(np.array([0, 1, 2, 100], np.float16), 2) == [2, 3]
+    assert iso(np.array([0, 1, 2, 100], np.float16), 4) == [2, 3]
+    # a low spike: mean(-50, 3, 4, 5) = -9.5: -50 is 40.5 away, 5 is 14.5
+    assert iso(np.array([3, -50, 4, 5], np.float16), 1) == [1]
+    # equal values at the maximum: mean(9, 2, 9, 3, 3, 3) = 29/6, the 9s are
+    # 25/6 away, the 2 is 17/6 -> the first 9 (slot 0) goes
+    assert iso(np.array([9, 2, 9, 3, 3, 3], np.float16), 1) == [0]
+    # mean(7, 1, 7, 0) = 3.75: the 0 (3.75 away) beats the 7s (3.25)
+    assert iso(np.array([7, 1, 7, 0], np.float16), 1) == [3]
+    # constant groups and groups of two lose nothing
+    assert iso(np.full(5, 3, np.float16), 3) == []
+    assert iso(np.array([1, 9], np.float16), 1) == []
+
+
+def test_outlier_taken_out_of_the_range():
+    # a group with one spike: the other entries quantize exactly as the group
+    # without the spike, and the spike comes back exactly
+    rng = np.random.default_rng(23)
+    x = rng.standard_normal(32).astype(np.float16)
+    x[11] = np.float16(60.0)
+    codes, sc, z, out = oracle.zoned._quantize_channel(x, 2, 1)
+    assert out == [11]
+    keep = np.arange(32) != 11
+    c_ref, s_ref, z_ref = oracle.quantize_groups(x[keep][None], 2)
+    assert np.array_equal(codes[keep], c_ref[0]) and codes[11] == 0
+    assert sc == s_ref[0] and z == z_ref[0]
+    # the step shrinks: every kept entry within half the new step
+    xh = codes[keep] * np.float64(sc) + np.float64(z)
+    assert np.abs(xh - x[keep].astype(np.float64)).max() <= np.float64(sc) / 2 * (1 + 1e-3) + 1e-6
+    _, sc0, _, _ = oracle.zoned._quantize_channel(x, 2, 0)
+    assert sc < sc0 / 5
+
+
+def test_outlier_attention_and_layout():
+    inp = _small(24, T=130, C=4, d=64)
+    k = inp["k"].copy()
+    # spikes at known places of kept tokens
+    kept = np.flatnonzero(inp["v_bits"][0, 0] != 0)
+    qch = np.flatnonzero((inp["k_bits"][0, 0] > 0) & (inp["k_bits"][0, 0] < 16))
+    for i, t in enumerate(kept[:6]):
+        k[0, 0, t, qch[i]] = np.float16(80.0 if i % 2 else -80.0)
+    inp["k"] = k
+    o1 = _zoned(inp, k_out=1)
+    # against the definition: dequantize each group by hand
+    d = 64
+    lay = oracle.zoned._unit_layout(inp["v_bits"][0, 0], inp["k_bits"][0, 0], d, 4, 0, 1)
+    kq = oracle.zoned._quantize_unit_keys(inp["k"][0, 0], lay)
+    spikes = {(int(t), int(qch[i])) for i, t in enumerate(kept[:6])}
+    found = set()
+    qchan = np.concatenate([lay["classes"][w] for w in (2, 4, 8)])
+    for w in (2, 4, 8, 16):
+        for codes, scale, zero, raw, t, outl in kq[w]:
+            for slot, pc, val in outl:
+                found.add((int(t[slot]), int(qchan[pc])))
+                assert val == inp["k"][0, 0, t[slot], qchan[pc]]
+    assert spikes <= found
+    # no group's step grows (a subset's range is never wider), and the step
+    # of every spiked group shrinks by more than half
+    lay0 = oracle.zoned._unit_layout(inp["v_bits"][0, 0], inp["k_bits"][0, 0], d, 4, 0, 0)
+    kq0 = oracle.zoned._quantize_unit_keys(inp["k"][0, 0], lay0)
+    pos = {int(c): i for i, c in enumerate(qchan)}
+    for w in (2, 4, 8, 16):
+        for g, (c1, s1, z1, r1, t1, outl) in enumerate(kq[w]):
+            s0 = kq0[w][g][1]
+            assert np.all(s1.astype(np.float64) <= s0.astype(np.float64))
+            for tok, ch in spikes:
+                if tok in set(t1.tolist()):
+                    assert float(s1[pos[ch]]) < 0.5 * float(s0[pos[ch]])
+    assert np.all(np.isfinite(o1))
+    # the dequantized keys hold the spikes exactly
+    kh, _ = oracle.zoned._dequant_unit(inp["k"][0, 0], inp["v"][0, 0], inp["v_bits"][0, 0],
+                                       inp["k_bits"][0, 0], lay)
+    toks = np.concatenate([lay["seg"][w]["tokens"] for w in (2, 4, 8, 16)])
+    row = {int(t): i for i, t in enumerate(toks)}
+    for tok, ch in spikes:
+        assert kh[row[tok], ch] == float(inp["k"][0, 0, tok, ch])
+    # byte image: the side list sits after the key zeros of every group
+    blob = zoned_pack(inp["k"], inp["v"], inp["v_bits"], inp["k_bits"], inp["k_new"], inp["v_new"], k_out=1)
+    units, total = zoned_layout(inp["v_bits"], inp["k_bits"], d, 4, 0, 1)
+    assert blob.size == total
+    sg = units[0]["seg"][2]
+    go = units[0]["base"] + sg["offset"]
+    o = go + units[0]["k_codes_bytes"] + 2 * units[0]["k_sz_bytes"]
+    offs = blob[o:o + 66].view(np.uint16)
+    n = int(offs[32])
+    assert n == len(kq[2][0][5])
+    assert np.all(np.diff(offs.astype(int)) >= 0)
+
+
+def test_outlier_list_empty_is_the_plain_layout():
+    # groups of at most two valid slots lose nothing: attention equals the
+    # plain layout's exactly
+    inp = _small(25, T=40, C=2)
+    vb = np.zeros_like(inp["v_bits"])
+    vb[:, :, [3, 17]] = 4                               # two kept tokens per unit
+    inp["v_bits"] = vb
+    np.testing.assert_array_equal(_zoned(inp, k_out=2), _zoned(inp))
