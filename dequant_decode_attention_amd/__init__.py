@@ -60,7 +60,7 @@ _SIGS = {
     "kivi_append_workspace_bytes": (_sz, [ctypes.POINTER(KiviCacheStruct), _i]),
     "kivi_append": (_i, [ctypes.POINTER(KiviCacheStruct), _vp, _vp, _i, _i, _vp, _sz, _vp]),
     "zoned_plan_words": (_sz, [_i, _i, _i, _i]),
-    "zoned_plan": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _vp, _sz, ctypes.POINTER(_sz)]),
+    "zoned_plan": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp, _sz, ctypes.POINTER(_sz)]),
     "zoned_pack": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "decode_attention_zoned_workspace_bytes": (_sz, [_vp, _i]),
     "decode_attention_zoned": (_i, [_vp, _i, _vp, _vp, _vp, _f, _vp, _sz, _vp, _vp]),
@@ -256,9 +256,10 @@ class ZonedPlan:
         return ctypes.c_void_p(self.words.ctypes.data)
 
 
-def zoned_plan(v_bits, k_bits, C_new, d, device):
-    """v_bits int8 [B, Hkv, T_old] in {0,2,4,8,16}; k_bits int8 [B, Hkv, d] in
-    {2,4,8,16} (host arrays) -> ZonedPlan."""
+def zoned_plan(v_bits, k_bits, C_new, d, device, sink=0, k_out=0):
+    """v_bits int8 [B, Hkv, T_old] and k_bits int8 [B, Hkv, d] in
+    {0,2,4,8,16} (host arrays); sink: old tokens kept whole; k_out: outlier
+    side-list entries per key group -> ZonedPlan."""
     v_bits = np.ascontiguousarray(np.asarray(v_bits, dtype=np.int8))
     k_bits = np.ascontiguousarray(np.asarray(k_bits, dtype=np.int8))
     B, H, T = v_bits.shape
@@ -269,7 +270,8 @@ def zoned_plan(v_bits, k_bits, C_new, d, device):
     blob = ctypes.c_size_t(0)
     _check("zoned_plan", lib.zoned_plan(ctypes.c_void_p(v_bits.ctypes.data),
                                         ctypes.c_void_p(k_bits.ctypes.data), B, H, T, C_new, d,
-                                        ctypes.c_void_p(words.ctypes.data), n, ctypes.byref(blob)))
+                                        int(sink), int(k_out), ctypes.c_void_p(words.ctypes.data), n,
+                                        ctypes.byref(blob)))
     return ZonedPlan(words, blob.value, device)
 
 

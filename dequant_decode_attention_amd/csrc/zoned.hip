@@ -20,8 +20,23 @@
 //   ceil(m_w*w/32) words; 16: raw fp16, two per word); channels inside a
 //   class keep their order.  Key groups = (32-slot group, quantized channel)
 //   over the valid slots; value groups = (token, 32 channels).
-//   zone B = [P_16][d] fp16 value rows of segment 16; zone C = keys [C][d],
-//   then values [C][d], fp16.
+//   zone B = [P_16][d] fp16 value rows of segment 16; zone C = keys
+//   [S + C][d], then values [S + C][d], fp16: the S sink tokens, then the
+//   C new tokens.
+// Sink window ([P1 para 11]: high-precision windows for the attention sinks
+// as well as the recent tokens): the first S old tokens stay whole, whatever
+// their widths, at the front of zone C.
+// Outlier side list ([P1 para 9]: a small share of key outliers isolated
+// from the quantized groups): in every key quantization group up to k_out
+// entries are taken out one at a time -- the smallest or largest remaining
+// value, whichever lies farther from the float32 mean of the remaining
+// values (summed in slot order; the largest on a tie; the lowest slot among
+// equal values) -- while more than two values remain and they are not all
+// equal.  The group is quantized over the rest; a removed entry keeps code 0
+// and its fp16 value goes to the group's side list, placed after the key
+// zeros: slot offsets [33] uint16, class positions [n_kq*k_out] uint16,
+// values [n_kq*k_out] fp16 (16-byte aligned blocks, sorted by slot then
+// position).  The reader adds q.(value - zero) to the logit of that slot.
 #include "common.h"
 #include "merge.h"
 
@@ -33,9 +48,14 @@ constexpr int32_t kPlanMagic = 0x5A4F4E45;  // "ZONE"
 constexpr int kHeaderWords = 16;
 constexpr int kUnitWords = 40;
 
+constexpr int kPlanVersion = 2;
+constexpr int kMaxOutliers = 4;             // side-list entries per key group, at most
+constexpr int kMaxZoneC = 256;              // sink + new tokens in zone C, at most
+constexpr int kOffsBytes = 80;              // 33 uint16 slot offsets, padded to 16 bytes
+
 // Header word indices.
 enum { H_MAGIC, H_VERSION, H_B, H_HKV, H_TOLD, H_C, H_D, H_UNITS, H_BLOB_LO, H_BLOB_HI,
-       H_MAX_GROUPS, H_UNIT_OFF, H_PERM_OFF, H_TOK_OFF };
+       H_MAX_GROUPS, H_UNIT_OFF, H_PERM_OFF, H_TOK_OFF, H_SINK, H_KOUT };
 // Unit record word indices.
 enum { U_N = 0,        // [4] kept tokens per segment
        U_M = 4,        // [4] channels per key class
@@ -45,7 +65,8 @@ enum { U_N = 0,        // [4] kept tokens per segment
        U_SEG_OFF = 20, // [4] byte offset of each segment (relative to unit base)
        U_GRP_B = 24,   // [4] bytes per group of each segment
        U_ZB = 28, U_ZC = 29, U_BASE_LO = 30, U_BASE_HI = 31, U_SIZE = 32,
-       U_TOTAL_GROUPS = 33, U_TOK_PREFIX = 34 /* [4] token-map start per segment */ };
+       U_TOTAL_GROUPS = 33, U_TOK_PREFIX = 34 /* [4] token-map start per segment */,
+       U_OUT_B = 38 /* bytes of a group's outlier side list (0 without) */ };
 
 __host__ __device__ inline size_t pad(size_t n, size_t a) { return (n + a - 1) / a * a; }
 
@@ -56,9 +77,10 @@ size_t plan_words(int B, int Hkv, int T_old, int d) {
 
 int check_plan(const int32_t* p) {
   if (!p) return DQA_ERR_NULL;
-  if (p[H_MAGIC] != kPlanMagic || p[H_VERSION] != 1) return DQA_ERR_PLAN;
+  if (p[H_MAGIC] != kPlanMagic || p[H_VERSION] != kPlanVersion) return DQA_ERR_PLAN;
   if (p[H_D] != 64 && p[H_D] != 128) return DQA_ERR_PLAN;
-  if (p[H_B] < 0 || p[H_HKV] < 0 || p[H_C] < 0 || p[H_C] > 256) return DQA_ERR_PLAN;
+  if (p[H_B] < 0 || p[H_HKV] < 0 || p[H_C] < 0 || p[H_SINK] < 0 || p[H_SINK] > p[H_TOLD]) return DQA_ERR_PLAN;
+  if (p[H_C] + p[H_SINK] > kMaxZoneC || p[H_KOUT] < 0 || p[H_KOUT] > kMaxOutliers) return DQA_ERR_PLAN;
   if (static_cast<int64_t>(p[H_B]) * p[H_HKV] != p[H_UNITS]) return DQA_ERR_PLAN;
   return DQA_OK;
 }
@@ -72,7 +94,7 @@ struct PackArgs {
   const uint16_t* k_new;
   const uint16_t* v_new;
   uint8_t* blob;
-  int T_old, C, d;
+  int T_old, C, d, sink, k_out;
 };
 
 __device__ __forceinline__ uint32_t code_of(float x, float zf, float sf, float levels) {
@@ -94,6 +116,8 @@ __global__ __launch_bounds__(128) void zoned_pack_kernel(PackArgs a) {
   __shared__ uint16_t lds_k[kGroup][128];   // the group's key rows (fp16, original order)
   __shared__ uint8_t lds_c[kGroup][128];    // codes by permuted channel
   __shared__ int lds_tok[kGroup];
+  __shared__ uint8_t lds_os[128][kMaxOutliers];   // removed slots per class position (0xFF: none)
+  __shared__ int lds_cnt[kGroup];
   const int d = a.d;
   const int unit = blockIdx.y;
   const int grp = blockIdx.x;
@@ -108,13 +132,18 @@ __global__ __launch_bounds__(128) void zoned_pack_kernel(PackArgs a) {
   const size_t src_unit = static_cast<size_t>(unit) * a.T_old * d;
   const int total = U[U_TOTAL_GROUPS];
   if (grp > total) return;
-  if (grp == total) {                      // zone C: fp16 copies
+  if (grp == total) {                      // zone C: fp16 copies, sink tokens first
     uint16_t* zc = reinterpret_cast<uint16_t*>(ub + U[U_ZC]);
-    const size_t n = static_cast<size_t>(a.C) * d;
+    const size_t ns = static_cast<size_t>(a.sink) * d;
+    const size_t n = ns + static_cast<size_t>(a.C) * d;
     const size_t src = static_cast<size_t>(unit) * a.C * d;
-    for (size_t i = tid; i < n; i += blockDim.x) {
-      zc[i] = a.k_new[src + i];
-      zc[n + i] = a.v_new[src + i];
+    for (size_t i = tid; i < ns; i += blockDim.x) {
+      zc[i] = a.k[src_unit + i];
+      zc[n + i] = a.v[src_unit + i];
+    }
+    for (size_t i = tid; i < n - ns; i += blockDim.x) {
+      zc[ns + i] = a.k_new[src + i];
+      zc[n + ns + i] = a.v_new[src + i];
     }
     return;
   }
@@ -144,8 +173,29 @@ __global__ __launch_bounds__(128) void zoned_pack_kernel(PackArgs a) {
     const int ch = perm[pc];
     if (pc < n_kq) {
       const int bits = pc < m2 ? 2 : (pc < m2 + m4 ? 4 : 8);
+      // outliers: slots taken out of this channel's group (bit s of `out`)
+      uint32_t out = 0u;
+      for (int i = 0; i < kMaxOutliers; ++i) lds_os[pc][i] = 0xFF;
+      for (int i = 0; i < a.k_out; ++i) {
+        int count = 0, hi = -1, lo = -1;
+        float total = 0.0f, vhi = -INFINITY, vlo = INFINITY;
+        for (int s = 0; s < n_valid; ++s) {
+          if (out >> s & 1u) continue;
+          const float x = h2f(lds_k[s][ch]);
+          total += x;                          // slot order, float32
+          ++count;
+          if (x > vhi) { vhi = x; hi = s; }    // first slot of the largest
+          if (x < vlo) { vlo = x; lo = s; }    // first slot of the smallest
+        }
+        if (count <= 2 || vhi == vlo) break;
+        const float mean = total / static_cast<float>(count);
+        const int pick = fabsf(vhi - mean) >= fabsf(vlo - mean) ? hi : lo;
+        out |= 1u << pick;
+        lds_os[pc][i] = static_cast<uint8_t>(pick);
+      }
       float mn = INFINITY, mx = -INFINITY;
       for (int s = 0; s < n_valid; ++s) {
+        if (out >> s & 1u) continue;
         const float x = h2f(lds_k[s][ch]);
         mn = fminf(mn, x);
         mx = fmaxf(mx, x);
@@ -158,10 +208,39 @@ __global__ __launch_bounds__(128) void zoned_pack_kernel(PackArgs a) {
       ks[pc] = s16;
       kz[pc] = f2h(mn);
       for (int s = 0; s < kGroup; ++s)
-        lds_c[s][pc] = s < n_valid ? static_cast<uint8_t>(code_of(h2f(lds_k[s][ch]), mn, sf, levels)) : 0;
+        lds_c[s][pc] = s < n_valid && !(out >> s & 1u)
+                           ? static_cast<uint8_t>(code_of(h2f(lds_k[s][ch]), mn, sf, levels)) : 0;
     }
   }
   __syncthreads();
+  // side list: thread s gathers the entries of slot s in class-position order
+  if (a.k_out > 0) {
+    const int cap = n_kq * a.k_out;
+    uint8_t* ob = gb + U[U_KCODES_B] + 2 * U[U_KSZ_B];
+    uint16_t* offs = reinterpret_cast<uint16_t*>(ob);
+    uint16_t* opc = reinterpret_cast<uint16_t*>(ob + kOffsBytes);
+    uint16_t* oval = reinterpret_cast<uint16_t*>(ob + kOffsBytes + pad(static_cast<size_t>(cap) * 2, 16));
+    if (tid < kGroup) {
+      int n = 0;
+      for (int pc = 0; pc < n_kq; ++pc)
+        for (int i = 0; i < a.k_out; ++i) n += lds_os[pc][i] == tid;
+      lds_cnt[tid] = n;
+    }
+    __syncthreads();
+    if (tid < kGroup) {
+      int o = 0;
+      for (int s = 0; s < tid; ++s) o += lds_cnt[s];
+      offs[tid] = static_cast<uint16_t>(o);
+      if (tid == kGroup - 1) offs[kGroup] = static_cast<uint16_t>(o + lds_cnt[tid]);
+      for (int pc = 0; pc < n_kq; ++pc)
+        for (int i = 0; i < a.k_out; ++i)
+          if (lds_os[pc][i] == tid) {
+            opc[o] = static_cast<uint16_t>(pc);
+            oval[o] = lds_k[tid][perm[pc]];
+            ++o;
+          }
+    }
+  }
   // key rows: word (slot, wi) of each class block
   const int kw2 = U[U_KWORDS + 0], kw4 = U[U_KWORDS + 1], kw8 = U[U_KWORDS + 2];
   const int W_K = U[U_WK];
@@ -191,7 +270,7 @@ __global__ __launch_bounds__(128) void zoned_pack_kernel(PackArgs a) {
   // ---- values
   if (w < 16) {
     const int vwpt = d * w / 32;                 // value words per slot
-    uint8_t* vbase = gb + U[U_KCODES_B] + 2 * U[U_KSZ_B];
+    uint8_t* vbase = gb + U[U_KCODES_B] + 2 * U[U_KSZ_B] + U[U_OUT_B];
     uint32_t* vcodes = reinterpret_cast<uint32_t*>(vbase);
     const size_t vsz_b = pad(static_cast<size_t>(kGroup) * (d / kGroup) * 2, 16);
     uint16_t* vs = reinterpret_cast<uint16_t*>(vbase + kGroup * vwpt * 4);
@@ -253,7 +332,8 @@ struct ZDecodeArgs {
   const uint16_t* q;
   float* out;
   float* partials;
-  int Hq, Hkv, C, items_per_split, splits;
+  int Hq, Hkv, C, items_per_split, splits;   // C: zone-C rows (sink + new tokens)
+  int k_out;                                  // side-list entries per key group (0: none)
   float q_scale;
 };
 
@@ -367,7 +447,7 @@ __global__ __launch_bounds__(256, 2) void zoned_decode_kernel(ZDecodeArgs a) {
   const int n_ent = cent[3] + ckw[3] * 2;
   const int n_kq = U[U_NKQ];
   const int W_K = U[U_WK];
-  const int kcodes_b = U[U_KCODES_B], ksz_b = U[U_KSZ_B];
+  const int kcodes_b = U[U_KCODES_B], ksz_b = U[U_KSZ_B], out_b = U[U_OUT_B];
   const int total = U[U_TOTAL_GROUPS];
   const int items = total + (a.C + kGroup - 1) / kGroup;
   const int j = lane & 31, hf = lane >> 5;
@@ -402,7 +482,7 @@ __global__ __launch_bounds__(256, 2) void zoned_decode_kernel(ZDecodeArgs a) {
       }
       n_valid = min(kGroup, U[U_N + seg] - g * kGroup);
       gb = ub + U[U_SEG_OFF + seg] + static_cast<size_t>(g) * U[U_GRP_B + seg];
-      const int nb = kcodes_b + 2 * ksz_b;         // the key block
+      const int nb = kcodes_b + 2 * ksz_b + out_b;  // the key block (with its side list)
       const uint4* src = reinterpret_cast<const uint4*>(gb);
       uint4* dst = reinterpret_cast<uint4*>(st);
       for (int i = lane; i < nb / 16; i += 64) dst[i] = src[i];
@@ -441,7 +521,7 @@ __global__ __launch_bounds__(256, 2) void zoned_decode_kernel(ZDecodeArgs a) {
         vr[t] = t < n_valid ? x : 0u;
       }
     } else {
-      const uint8_t* vb = gb + kcodes_b + 2 * ksz_b;
+      const uint8_t* vb = gb + kcodes_b + 2 * ksz_b + out_b;
       const uint32_t* vcodes = reinterpret_cast<const uint32_t*>(vb);
 #pragma unroll
       for (int t = 0; t < kGroup; ++t) {
@@ -521,6 +601,22 @@ __global__ __launch_bounds__(256, 2) void zoned_decode_kernel(ZDecodeArgs a) {
           else if (ci == 2) key_class<8, G>(row + wb, wlo, whi, 0, tb, part);
           else key_class<16, G>(row + wb, wlo, whi, 0, tb, part);
           wb += kw;
+        }
+        if (a.k_out > 0) {
+          // side-list entries of slot j (the two halves take alternate
+          // entries): the key there is the stored value, not the code-0
+          // dequantization z
+          const uint16_t* offs = reinterpret_cast<const uint16_t*>(st + kcodes_b + 2 * ksz_b);
+          const uint16_t* opc = offs + kOffsBytes / 2;
+          const uint16_t* oval = opc + (n_kq * a.k_out * 2 + 15) / 16 * 8;
+          const uint16_t* kz = reinterpret_cast<const uint16_t*>(st + kcodes_b + ksz_b);
+          const int e_end = min(static_cast<int>(offs[j + 1]), n_kq * a.k_out);
+          for (int e = offs[j] + hf; e < e_end; e += 2) {
+            const int pc = min(static_cast<int>(opc[e]), n_kq - 1);
+            const float dv = h2f(oval[e]) - h2f(kz[pc]);
+#pragma unroll
+            for (int h = 0; h < G; ++h) part[h] = fmaf(dv, lds_qp[h][pc], part[h]);
+          }
         }
       } else {
         const uint32_t* row = reinterpret_cast<const uint32_t*>(st) + j * (D / 2);
@@ -664,9 +760,9 @@ int zoned_geometry(const int32_t* p, int Hq, ZGeometry* g) {
   // every key block fits one staging slice
   for (int u = 0; u < g->units; ++u) {
     const int32_t* U = p + p[H_UNIT_OFF] + static_cast<size_t>(u) * kUnitWords;
-    if (U[U_KCODES_B] + 2 * U[U_KSZ_B] > kStageBytes) return DQA_ERR_PLAN;
+    if (U[U_KCODES_B] + 2 * U[U_KSZ_B] + U[U_OUT_B] > kStageBytes) return DQA_ERR_PLAN;
   }
-  g->items_max = p[H_MAX_GROUPS] + (p[H_C] + kGroup - 1) / kGroup;
+  g->items_max = p[H_MAX_GROUPS] + (p[H_C] + p[H_SINK] + kGroup - 1) / kGroup;
   long long s = (kZoneWorkgroups + g->units - 1) / (g->units > 0 ? g->units : 1);
   if (s > g->items_max) s = g->items_max;
   if (s > kMaxSplitsMerge - 1) s = kMaxSplitsMerge - 1;
@@ -699,9 +795,11 @@ extern "C" size_t zoned_plan_words(int B, int Hkv, int T_old, int d) {
 }
 
 extern "C" int zoned_plan(const int8_t* v_bits, const int8_t* k_bits, int B, int Hkv, int T_old,
-                          int C_new, int d, int32_t* plan, size_t n_words, size_t* blob_bytes) {
+                          int C_new, int d, int sink, int k_out, int32_t* plan, size_t n_words,
+                          size_t* blob_bytes) {
   const size_t need = plan_words(B, Hkv, T_old, d);
-  if (need == 0 || C_new < 0 || C_new > 256) return DQA_ERR_SHAPE;
+  if (need == 0 || C_new < 0 || sink < 0 || sink > T_old || C_new + sink > kMaxZoneC) return DQA_ERR_SHAPE;
+  if (k_out < 0 || k_out > kMaxOutliers) return DQA_ERR_SHAPE;
   if (static_cast<int64_t>(B) * Hkv > (1 << 20) || T_old > (1 << 24)) return DQA_ERR_SHAPE;
   if (!plan || !blob_bytes) return DQA_ERR_NULL;
   if (static_cast<int64_t>(B) * Hkv * T_old > 0 && !v_bits) return DQA_ERR_NULL;
@@ -718,7 +816,7 @@ extern "C" int zoned_plan(const int8_t* v_bits, const int8_t* k_bits, int B, int
   }
   for (size_t i = 0; i < need; ++i) plan[i] = 0;
   plan[H_MAGIC] = kPlanMagic;
-  plan[H_VERSION] = 1;
+  plan[H_VERSION] = kPlanVersion;
   plan[H_B] = B;
   plan[H_HKV] = Hkv;
   plan[H_TOLD] = T_old;
@@ -728,6 +826,8 @@ extern "C" int zoned_plan(const int8_t* v_bits, const int8_t* k_bits, int B, int
   plan[H_UNIT_OFF] = kHeaderWords;
   plan[H_PERM_OFF] = kHeaderWords + units * kUnitWords;
   plan[H_TOK_OFF] = kHeaderWords + units * (kUnitWords + d);
+  plan[H_SINK] = sink;
+  plan[H_KOUT] = k_out;
   size_t base = 0;
   int max_groups = 0;
   for (int u = 0; u < units; ++u) {
@@ -755,7 +855,7 @@ extern "C" int zoned_plan(const int8_t* v_bits, const int8_t* k_bits, int B, int
     for (int si = 0; si < 4; ++si) {
       U[U_TOK_PREFIX + si] = nt;
       int n = 0;
-      for (int t = 0; t < T_old; ++t)
+      for (int t = sink; t < T_old; ++t)          // sink tokens live in zone C
         if (vb[t] == kSegW[si]) {
           tok[nt++] = t;
           ++n;
@@ -769,10 +869,12 @@ extern "C" int zoned_plan(const int8_t* v_bits, const int8_t* k_bits, int B, int
     U[U_NKQ] = n_kq;
     U[U_KCODES_B] = kGroup * W_K * 4;
     U[U_KSZ_B] = static_cast<int32_t>(pad(static_cast<size_t>(n_kq) * 2, 16));
+    U[U_OUT_B] = k_out > 0 ? kOffsBytes + 2 * static_cast<int32_t>(pad(static_cast<size_t>(n_kq) * k_out * 2, 16))
+                           : 0;
     size_t off = 0;
     int total = 0;
     for (int si = 0; si < 4; ++si) {
-      size_t gbytes = static_cast<size_t>(U[U_KCODES_B]) + 2 * static_cast<size_t>(U[U_KSZ_B]);
+      size_t gbytes = static_cast<size_t>(U[U_KCODES_B]) + 2 * static_cast<size_t>(U[U_KSZ_B]) + U[U_OUT_B];
       if (kSegW[si] < 16)
         gbytes += static_cast<size_t>(kGroup) * (d * kSegW[si] / 32) * 4 +
                   2 * pad(static_cast<size_t>(kGroup) * (d / kGroup) * 2, 16);
@@ -784,7 +886,7 @@ extern "C" int zoned_plan(const int8_t* v_bits, const int8_t* k_bits, int B, int
     U[U_ZB] = static_cast<int32_t>(off);
     off += static_cast<size_t>(U[U_GROUPS + 3]) * kGroup * d * 2;
     U[U_ZC] = static_cast<int32_t>(off);
-    off += 2 * static_cast<size_t>(C_new) * d * 2;
+    off += 2 * static_cast<size_t>(sink + C_new) * d * 2;
     const size_t size = pad(off, 256);
     if (size > 0x7FFFFFFFu) return DQA_ERR_SHAPE;
     U[U_SIZE] = static_cast<int32_t>(size);
@@ -812,7 +914,7 @@ extern "C" int zoned_pack(const int32_t* plan_host, const int32_t* plan_dev, con
                             (static_cast<size_t>(static_cast<uint32_t>(plan_host[H_BLOB_HI])) << 32);
   if (units == 0 || blob_bytes == 0) return DQA_OK;
   if (!blob) return DQA_ERR_NULL;
-  if (plan_host[H_TOLD] > 0 && (!k || !v)) return DQA_ERR_NULL;
+  if ((plan_host[H_TOLD] > 0 || plan_host[H_SINK] > 0) && (!k || !v)) return DQA_ERR_NULL;
   if (plan_host[H_C] > 0 && (!k_new || !v_new)) return DQA_ERR_NULL;
   if (units > 65535) return DQA_ERR_SHAPE;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -823,7 +925,7 @@ extern "C" int zoned_pack(const int32_t* plan_host, const int32_t* plan_dev, con
                      static_cast<uint32_t*>(blob), n_words);
   DQA_CHECK_LAUNCH();
   PackArgs a{plan_dev, k, v, k_new, v_new, static_cast<uint8_t*>(blob), plan_host[H_TOLD],
-             plan_host[H_C], plan_host[H_D]};
+             plan_host[H_C], plan_host[H_D], plan_host[H_SINK], plan_host[H_KOUT]};
   const dim3 grid(plan_host[H_MAX_GROUPS] + 1, units);
   hipLaunchKernelGGL(zoned_pack_kernel, grid, dim3(128), 0, s, a);
   DQA_CHECK_LAUNCH();
@@ -854,7 +956,8 @@ extern "C" int decode_attention_zoned(const uint16_t* q, int Hq, const int32_t* 
   a.partials = static_cast<float*>(ws);
   a.Hq = Hq;
   a.Hkv = plan_host[H_HKV];
-  a.C = plan_host[H_C];
+  a.C = plan_host[H_C] + plan_host[H_SINK];
+  a.k_out = plan_host[H_KOUT];
   a.items_per_split = g.ips;
   a.splits = g.splits;
   a.q_scale = sm_scale * 1.4426950408889634f;

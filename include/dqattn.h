@@ -56,7 +56,9 @@ enum {
 const char* dqa_status_string(int status);
 
 /* Version of this interface (increments on any signature or layout change). */
-int dqa_abi_version(void);  /* 5: RDKV allocation entry points (rdkv_*);
+int dqa_abi_version(void);  /* 6: zoned_plan takes a sink length and the
+                              outlier entries per key group;
+                              5: RDKV allocation entry points (rdkv_*);
                               4: dqa_kivi_cache carries buffer capacities
                               (T_cap, R_cap) and kivi_append exists;
                               3: 16-byte pointer alignment checked */
@@ -212,8 +214,17 @@ int kivi_append(dqa_kivi_cache* cache, const uint16_t* k_new, const uint16_t* v_
  * classes 2, 4, 8, 16; one scale/zero per (group, quantized channel); 16-bit
  * channels raw fp16) and, for widths 2/4/8, the value rows quantized per
  * token in 32-channel groups.  Zone B: fp16 value rows of 16-bit tokens.
- * Zone C: fp16 keys and values of the C newest tokens.  The byte layout is
- * fixed and documented with the oracle that reproduces it.
+ * Zone C: fp16 keys and values of the S sink tokens, then of the C newest
+ * tokens.  Sink window ([P1 para 11]: high-precision windows for attention
+ * sinks as well as recent tokens): the first S old tokens stay whole
+ * (fp16, every channel) whatever their widths.  Outlier side list ([P1
+ * para 9]: a small share of key outliers isolated): in every key
+ * quantization group up to k_out entries -- each time the smallest or
+ * largest remaining value, whichever is farther from the float32 mean of the
+ * remaining values (the largest on a tie) -- leave the group's range while
+ * more than two distinct values remain; they are stored as fp16 and read
+ * back exactly.  The byte layout is fixed and documented with the oracle
+ * that reproduces it.
  * ------------------------------------------------------------------------ */
 
 /* int32 words a plan needs for these sizes (0 if invalid). */
@@ -222,7 +233,10 @@ size_t zoned_plan_words(int B, int Hkv, int T_old, int d);
 /* Build the plan on the host from the width maps.
  *   v_bits (host) int8 [B][Hkv][T_old], values in {0,2,4,8,16}
  *   k_bits (host) int8 [B][Hkv][d], values in {0,2,4,8,16}
- *   C_new  new fp16 tokens per unit, 0..256;  d in {64, 128}
+ *   C_new  new fp16 tokens per unit;  d in {64, 128}
+ *   sink   old tokens kept whole at the front of zone C, 0..T_old, with
+ *          sink + C_new <= 256
+ *   k_out  side-list entries per key quantization group, 0..4 (0: none)
  *   plan   (host) int32 [plan_words], plan_words >= zoned_plan_words(...)
  *   blob_bytes (host) receives the size of the packed blob
  * The plan is self-describing; the caller copies the same words to device
@@ -230,12 +244,13 @@ size_t zoned_plan_words(int B, int Hkv, int T_old, int d);
  * Errors: DQA_ERR_NULL, DQA_ERR_SHAPE, DQA_ERR_BITS (a width outside its
  * set), DQA_ERR_WORKSPACE (plan_words too small). */
 int zoned_plan(const int8_t* v_bits, const int8_t* k_bits, int B, int Hkv,
-               int T_old, int C_new, int d, int32_t* plan, size_t plan_words,
-               size_t* blob_bytes);
+               int T_old, int C_new, int d, int sink, int k_out, int32_t* plan,
+               size_t plan_words, size_t* blob_bytes);
 
 /* Pack the cache into the blob described by the plan.
  *   plan_host (host) and plan_dev (device): the same words from zoned_plan
- *   k, v      (device) fp16 [B][Hkv][T_old][d]
+ *   k, v      (device) fp16 [B][Hkv][T_old][d] (the sink tokens are their
+ *             first rows)
  *   k_new, v_new (device) fp16 [B][Hkv][C_new][d] (may be NULL if C_new == 0)
  *   blob      (device) blob_bytes bytes (every byte is written)
  * Errors: DQA_ERR_NULL, DQA_ERR_PLAN, DQA_ERR_HIP. */

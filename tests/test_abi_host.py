@@ -122,7 +122,7 @@ def test_stream_copy_validation():
     assert lib.dqa_stream_copy(ctypes.c_void_p(0x1008), FAKE, 64, None) == 2
 
 
-def _plan(vb, kb, C, d):
+def _plan(vb, kb, C, d, sink=0, k_out=0):
     vb = np.ascontiguousarray(vb, np.int8)
     kb = np.ascontiguousarray(kb, np.int8)
     B, H, T = vb.shape
@@ -130,12 +130,15 @@ def _plan(vb, kb, C, d):
     words = np.zeros(n, np.int32)
     blob = ctypes.c_size_t(0)
     st = lib.zoned_plan(ctypes.c_void_p(vb.ctypes.data), ctypes.c_void_p(kb.ctypes.data), B, H, T,
-                        C, d, ctypes.c_void_p(words.ctypes.data), n, ctypes.byref(blob))
+                        C, d, sink, k_out, ctypes.c_void_p(words.ctypes.data), n, ctypes.byref(blob))
     return st, words, blob.value
 
 
-@pytest.mark.parametrize("seed,T,C,d", [(0, 500, 64, 128), (1, 77, 0, 64), (2, 1, 3, 128), (3, 0, 5, 64)])
-def test_zoned_plan_matches_oracle_layout(seed, T, C, d):
+@pytest.mark.parametrize("seed,T,C,d,sink,k_out", [(0, 500, 64, 128, 0, 0), (1, 77, 0, 64, 0, 0),
+                                                   (2, 1, 3, 128, 0, 0), (3, 0, 5, 64, 0, 0),
+                                                   (4, 300, 16, 128, 4, 1), (5, 90, 0, 64, 90, 2),
+                                                   (6, 200, 8, 128, 0, 4)])
+def test_zoned_plan_matches_oracle_layout(seed, T, C, d, sink, k_out):
     """The host planner (C++) and the oracle's layout agree on the blob size
     (and hence on every segment/zone size) for random width maps."""
     import oracle
@@ -143,9 +146,9 @@ def test_zoned_plan_matches_oracle_layout(seed, T, C, d):
     B, H = 2, 3
     vb = rng.choice([0, 2, 4, 8, 16], size=(B, H, T), p=[.5, .2, .15, .1, .05]).astype(np.int8)
     kb = rng.choice([2, 4, 8, 16], size=(B, H, d), p=[.4, .3, .2, .1]).astype(np.int8)
-    st, words, blob = _plan(vb, kb, C, d)
+    st, words, blob = _plan(vb, kb, C, d, sink, k_out)
     assert st == 0
-    _, total = oracle.zoned_layout(vb, kb, d, C)
+    _, total = oracle.zoned_layout(vb, kb, d, C, sink, k_out)
     assert blob == total
     ws = lib.decode_attention_zoned_workspace_bytes(ctypes.c_void_p(words.ctypes.data), 4 * H)
     assert ws > 0
@@ -165,12 +168,18 @@ def test_zoned_plan_validation():
     evict_k[0, 0, 1] = 0            # width 0 evicts a key channel
     assert _plan(vb, evict_k, 0, 128)[0] == 0
     assert _plan(vb, kb, 300, 128)[0] == 2                  # C too large
+    assert _plan(vb, kb, 200, 128, sink=60)[0] == 2         # sink + C too large
+    assert _plan(vb, kb, 0, 128, sink=65)[0] == 2           # sink longer than the cache
+    assert _plan(vb, kb, 0, 128, sink=-1)[0] == 2
+    assert _plan(vb, kb, 0, 128, k_out=5)[0] == 2           # side list too long
+    assert _plan(vb, kb, 0, 128, k_out=-1)[0] == 2
+    assert _plan(vb, kb, 0, 128, sink=64, k_out=4)[0] == 0
     assert lib.zoned_plan_words(1, 1, 64, 96) == 0
     n = lib.zoned_plan_words(1, 1, 64, 128)
     words = np.zeros(n, np.int32)
     blob = ctypes.c_size_t(0)
     assert lib.zoned_plan(ctypes.c_void_p(vb.ctypes.data), ctypes.c_void_p(kb.ctypes.data), 1, 1,
-                          64, 0, 128, ctypes.c_void_p(words.ctypes.data), n - 1,
+                          64, 0, 128, 0, 0, ctypes.c_void_p(words.ctypes.data), n - 1,
                           ctypes.byref(blob)) == 4
     # a corrupted plan is refused by the device entry points before any launch
     st, words, blob = _plan(vb, kb, 0, 128)
@@ -213,7 +222,7 @@ def test_rvq_validation_and_workspace():
 
 def test_kivi_append_validation():
     """Argument checks of the streaming append (all fail before any launch)."""
-    assert lib.dqa_abi_version() == 5
+    assert lib.dqa_abi_version() == 6
     c = _cache(T_cap=128, R_cap=128)
     # staging holds the recent and the new rows of K and V
     assert lib.kivi_append_workspace_bytes(ctypes.byref(c), 20) == 2 * 2 * 2 * (16 + 20) * 128 * 2

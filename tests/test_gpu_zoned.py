@@ -100,3 +100,46 @@ def test_zoned_full_config_sampled(dqa):
         err = rel_l2(out[b, h * G:(h + 1) * G][None], ref)
         print(f"c4 unit ({b},{h}) rel_l2={err:.3e}", flush=True)
         assert err <= TOL
+
+
+SINK_OUT_CASES = [
+    # B, Hq, Hkv, d, T_old, C, sink, k_out, v-probs, k-probs
+    (1, 4, 1, 128, 300, 8, 4, 0, PV, PK),                        # sink only
+    (1, 4, 2, 64, 200, 0, 0, 1, PV, PK),                         # outliers only
+    (2, 8, 2, 128, 513, 16, 16, 2, PV, PK),
+    (1, 4, 1, 128, 100, 4, 0, 4, {2: .5, 4: .5}, {2: .5, 8: .5}),
+    (1, 4, 2, 64, 70, 3, 70, 1, PV, PK),                         # the whole old cache as sink
+    (1, 4, 1, 128, 300, 16, 8, 3, PV, {0: .2, 2: .3, 4: .2, 8: .2, 16: .1}),   # with evicted channels
+]
+
+
+@pytest.mark.parametrize("case", SINK_OUT_CASES,
+                         ids=lambda c: f"{c[0]}x{c[1]}x{c[2]}x{c[3]}-T{c[4]}-C{c[5]}-S{c[6]}-o{c[7]}")
+def test_zoned_sink_and_outliers(dqa, case):
+    B, Hq, Hkv, d, T, C, S, ko, pv, pk = case
+    inp = zoned_inputs(B, Hq, Hkv, d, T, C, seed=3 * T + S + ko, v_width_probs=pv, k_width_probs=pk,
+                       outliers=("lognormal", 0.04, 3.0, 1.0))
+    # key spikes inside the groups, so that the side lists hold real outliers
+    rng = np.random.default_rng(T)
+    k = inp["k"].copy()
+    idx = rng.integers(0, [B, Hkv, T, d], size=(max(1, T // 10), 4))
+    k[idx[:, 0], idx[:, 1], idx[:, 2], idx[:, 3]] = np.float16(90.0)
+    inp["k"] = k
+    say("zoned sink/outliers", case[:8])
+    plan = dqa.zoned_plan(inp["v_bits"], inp["k_bits"], C, d, "cuda:0", sink=S, k_out=ko)
+    blob = dqa.zoned_pack(plan, dev(inp["k"]), dev(inp["v"]),
+                          dev(inp["k_new"]) if C else None, dev(inp["v_new"]) if C else None)
+    ref_blob = oracle.zoned_pack(inp["k"], inp["v"], inp["v_bits"], inp["k_bits"], inp["k_new"],
+                                 inp["v_new"], sink=S, k_out=ko)
+    got_blob = host(blob)
+    assert got_blob.size == ref_blob.size
+    if not np.array_equal(got_blob, ref_blob):
+        bad = np.flatnonzero(got_blob != ref_blob)
+        pytest.fail(f"blob differs at {bad.size} bytes, first {bad[:8]}")
+    scale = 1.0 / math.sqrt(d)
+    out = host(dqa.decode_attention_zoned(dev(inp["q"]), plan, blob, scale))
+    ref = oracle.zoned_decode_attention(inp["q"], inp["k"], inp["v"], inp["v_bits"], inp["k_bits"],
+                                        inp["k_new"], inp["v_new"], scale, sink=S, k_out=ko)
+    err = rel_l2(out, ref)
+    print(f"rel_l2={err:.3e} worst_row={worst_row_rel(out, ref):.3e}", flush=True)
+    assert err <= TOL
