@@ -190,36 +190,43 @@ def time_append(dqa, torch, dev, cfg, bits):
 def time_zoned(dqa, torch, dev):
     """Rows a8-a9 on the mixed-width zoned workload (c4): packer (fp16 K/V of
     kept tokens read, blob written) and decode (blob read; blob replicas
-    rotated past the Infinity Cache)."""
+    rotated past the Infinity Cache); then the same pair with c4's sink
+    window and key outlier side lists."""
     from workloads import CONFIGS, zoned_inputs
     import numpy as np
     cfg = CONFIGS["c4"]
     inp = zoned_inputs(cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["d"], cfg["T_old"], cfg["C"], seed=4,
                        v_width_probs=cfg["v_width_probs"], k_width_probs=cfg["k_width_probs"],
                        outliers=cfg["outliers"])
-    plan = dqa.zoned_plan(inp["v_bits"], inp["k_bits"], cfg["C"], cfg["d"], dev)
     k, v = torch.from_numpy(inp["k"]).to(dev), torch.from_numpy(inp["v"]).to(dev)
     kn, vn = torch.from_numpy(inp["k_new"]).to(dev), torch.from_numpy(inp["v_new"]).to(dev)
     q = torch.from_numpy(inp["q"]).to(dev)
-    kept = int((inp["v_bits"] > 0).sum())
     d = cfg["d"]
-    pack_bytes = 2 * kept * d * 2 + 2 * kn.numel() * 2 + plan.blob_bytes
-    ms = _event_ms(torch, lambda i: dqa.zoned_pack(plan, k, v, kn, vn), 10)
-    out = {"zoned_pack": _hbm_row("zoned_pack_kernel", cfg["workload"], ms, pack_bytes,
-                                  "fp16 K/V of kept tokens and new tokens read, blob written")}
-    blob = dqa.zoned_pack(plan, k, v, kn, vn)
-    del k, v
-    reps = max(2, int(np.ceil(320e6 / max(plan.blob_bytes, 1))))
-    blobs = [blob.clone() for _ in range(reps)]
     scale = 1.0 / math.sqrt(d)
-    res = torch.empty(q.shape, dtype=torch.float32, device=dev)
-    n = dqa.lib.decode_attention_zoned_workspace_bytes(plan.host_ptr(), cfg["Hq"])
-    ws = torch.zeros(max(n, 1), dtype=torch.uint8, device=dev)
-    ms = _event_ms(torch, lambda i: dqa.decode_attention_zoned(q, plan, blobs[i % reps], scale,
-                                                                out=res, workspace=ws), 50)
-    nbytes = plan.blob_bytes + q.numel() * 2 + res.numel() * 4
-    out["zoned_decode"] = _hbm_row("zoned_decode_kernel", cfg["workload"], ms, nbytes,
-                                   f"blob {plan.blob_bytes} B, {reps} replicas rotated")
+    out = {}
+    variants = (("", 0, 0), ("_sink_outliers", cfg["zoned_variant"]["sink"], cfg["zoned_variant"]["k_out"]))
+    for suffix, sink, k_out in variants:
+        plan = dqa.zoned_plan(inp["v_bits"], inp["k_bits"], cfg["C"], d, dev, sink=sink, k_out=k_out)
+        kept = int((inp["v_bits"][:, :, sink:] > 0).sum())
+        pack_bytes = 2 * kept * d * 2 + 2 * (kn.numel() + q.shape[0] * cfg["Hkv"] * sink * d) * 2 \
+            + plan.blob_bytes
+        note = "fp16 K/V of kept tokens and new tokens read, blob written"
+        if sink or k_out:
+            note += f"; {sink} sink tokens, {k_out} side-list entries per key group"
+        ms = _event_ms(torch, lambda i: dqa.zoned_pack(plan, k, v, kn, vn), 10)
+        out["zoned_pack" + suffix] = _hbm_row("zoned_pack_kernel", cfg["workload"], ms, pack_bytes, note)
+        blob = dqa.zoned_pack(plan, k, v, kn, vn)
+        reps = max(2, int(np.ceil(320e6 / max(plan.blob_bytes, 1))))
+        blobs = [blob.clone() for _ in range(reps)]
+        res = torch.empty(q.shape, dtype=torch.float32, device=dev)
+        n = dqa.lib.decode_attention_zoned_workspace_bytes(plan.host_ptr(), cfg["Hq"])
+        ws = torch.zeros(max(n, 1), dtype=torch.uint8, device=dev)
+        ms = _event_ms(torch, lambda i: dqa.decode_attention_zoned(q, plan, blobs[i % reps], scale,
+                                                                    out=res, workspace=ws), 50)
+        nbytes = plan.blob_bytes + q.numel() * 2 + res.numel() * 4
+        out["zoned_decode" + suffix] = _hbm_row("zoned_decode_kernel", cfg["workload"], ms, nbytes,
+                                                f"blob {plan.blob_bytes} B, {reps} replicas rotated")
+        del blobs, blob
     return out
 
 

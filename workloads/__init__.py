@@ -38,7 +38,10 @@ CONFIGS = {
                outliers=("lognormal", 0.04, 3.0, 1.0),
                # mean widths of the maps above (value bits per token, key bits
                # per channel): the budgets of the allocator on this cache
-               rdkv_mean_widths=(2.6, 5.2)),
+               rdkv_mean_widths=(2.6, 5.2),
+               # sink window and key outlier side lists measured beside the
+               # plain layout: 4 sink tokens, one entry per key group
+               zoned_variant=dict(sink=4, k_out=1)),
     # residual-VQ cache, Llama-3.2-3B shape: 4 codebooks x 1024 entries
     "c5": dict(workload="rvq-llama3.2-3b-8k", kind="rvq", B=2, Hq=24, Hkv=8,
                d=128, T=8192, N=4, Kc=1024),
