@@ -14,8 +14,11 @@
 // exact, fp32 accumulation):
 //   1. per query row, the log-sum-exp of its causal logits (base 2);
 //   2. per key tile, sum over rows and over the G heads of a KV head of
-//      exp2(logit - lse).  A workgroup owns its keys, so the sums are
-//      written without atomics and repeat bit for bit.
+//      exp2(logit - lse).  A workgroup owns its 128 keys (4 waves x 32,
+//      sharing each query tile), so the sums are written without atomics
+//      and repeat bit for bit.  Wider workgroups (8 or 16 waves) stream the
+//      query rows fewer times but measured slower: the caches already serve
+//      most re-reads, and the wider barrier costs more.
 // Both passes see identical logits (same operands, same order).  Pass 1
 // walks key tiles from 0 upward and pass 2 query tiles from the last one
 // downward, so the workgroups of one KV head that run together read the
@@ -47,7 +50,8 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));  // promotable (HIP'
 
 constexpr int kLseRows = 128;   // query rows per workgroup in pass 1 (4 waves x 32)
 constexpr int kLseKeys = 64;    // keys per LDS tile in pass 1
-constexpr int kSumKeys = 128;   // keys per workgroup in pass 2 (4 waves x 32)
+constexpr int kSumWaves = 4;    // waves per workgroup in pass 2, sharing one query tile
+constexpr int kSumKeys = 32 * kSumWaves;  // keys per workgroup in pass 2
 constexpr int kSumRows = 64;    // query rows per LDS tile in pass 2
 constexpr int kChanRows = 256;  // positions per workgroup of the channel sums
 constexpr float kLog2e = 1.4426950408889634f;
@@ -209,13 +213,14 @@ __global__ __launch_bounds__(256) void rdkv_lse_kernel(const uint16_t* __restric
 // ----------------------------------------------------- pass 2: column sums
 
 template <int D>
-__global__ __launch_bounds__(256) void rdkv_colsum_kernel(const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(64 * kSumWaves) void rdkv_colsum_kernel(const uint16_t* __restrict__ q,
                                                           const uint16_t* __restrict__ k, int B,
                                                           int Hq, int Hkv, int T, float c,
                                                           const float* __restrict__ lse,
                                                           float* __restrict__ w) {
   constexpr int KS = D / 32, PAD = D + 8, CH = D / 8;
-  constexpr int LOADS = kSumRows * CH / 256;
+  constexpr int NT = 64 * kSumWaves;
+  constexpr int LOADS = (kSumRows * CH + NT - 1) / NT;
   __shared__ __align__(16) _Float16 lds_q[kSumRows * PAD];
   __shared__ __align__(16) float lds_lse[kSumRows];
 
@@ -250,7 +255,7 @@ __global__ __launch_bounds__(256) void rdkv_colsum_kernel(const uint16_t* __rest
     const size_t hb = (static_cast<size_t>(b) * Hq + h) * static_cast<size_t>(T);
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {
-      const int cidx = tid + 256 * j, r = cidx / CH, ch = cidx % CH;
+      const int cidx = min(tid + NT * j, kSumRows * CH - 1), r = cidx / CH, ch = cidx % CH;
       const int row = min(qt * kSumRows + r, T - 1);
       pre[j] = *reinterpret_cast<const u32x4*>(q + (hb + row) * D + ch * 8);
     }
@@ -264,8 +269,8 @@ __global__ __launch_bounds__(256) void rdkv_colsum_kernel(const uint16_t* __rest
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {
-      const int cidx = tid + 256 * j, r = cidx / CH, ch = cidx % CH;
-      *reinterpret_cast<u32x4*>(&lds_q[r * PAD + ch * 8]) = pre[j];
+      const int cidx = tid + NT * j, r = cidx / CH, ch = cidx % CH;
+      if (cidx < kSumRows * CH) *reinterpret_cast<u32x4*>(&lds_q[r * PAD + ch * 8]) = pre[j];
     }
     if (tid < kSumRows) lds_lse[tid] = pre_lse;
     __syncthreads();
@@ -555,7 +560,7 @@ void launch_token(const uint16_t* q, const uint16_t* k, int B, int Hq, int Hkv, 
   const unsigned g1 = static_cast<unsigned>(static_cast<size_t>(B) * Hq * ((T + kLseRows - 1) / kLseRows));
   hipLaunchKernelGGL(rdkv_lse_kernel<D>, dim3(g1), dim3(256), 0, s, q, k, B, Hq, Hkv, T, c, lse);
   const unsigned g2 = static_cast<unsigned>(static_cast<size_t>(B) * Hkv * ((T + kSumKeys - 1) / kSumKeys));
-  hipLaunchKernelGGL(rdkv_colsum_kernel<D>, dim3(g2), dim3(256), 0, s, q, k, B, Hq, Hkv, T, c, lse, w);
+  hipLaunchKernelGGL(rdkv_colsum_kernel<D>, dim3(g2), dim3(64 * kSumWaves), 0, s, q, k, B, Hq, Hkv, T, c, lse, w);
 }
 
 template <int D>
