@@ -287,6 +287,14 @@ __global__ __launch_bounds__(512) void rvq_encode_kernel(const uint16_t* __restr
 // ------------------------------------------------------------------ decode
 
 constexpr int kDecWaves = 4;
+// Key logits through a table: q . k_hat = sum_s q . Ck_s[k_idx[s]], so a
+// table T[h][s][c] = q_h . Ck_s[c] (scaled into the log2 domain) turns each
+// key logit into N lookups instead of N gathered codewords.  Used when the
+// table of one (batch, KV head) fits this many floats of LDS.
+constexpr int kLutFloats = 16384;   // 64 KB
+
+// floats between the tables of consecutive units (16-byte aligned rows)
+__host__ __device__ inline int lut_stride(int G, int N, int Kc) { return (G * N * Kc + 63) / 64 * 64; }
 
 struct RvqDecArgs {
   const uint16_t* q;
@@ -296,9 +304,44 @@ struct RvqDecArgs {
   const uint16_t* v_cb;
   float* out;
   float* partials;
+  const float* lut;     // [units][G][N][Kc] key-logit table (table path only)
   int Hq, Hkv, T, N, Kc, n_tiles, tiles_per_split, splits;
   float q_scale;
 };
+
+// The key-logit table of every (batch, KV head), on the matrix cores: per
+// wave 16 codewords (A operand rows, exact fp16) against the fp16 query of
+// the G heads (B operand columns, exact; columns >= G are zero), fp32
+// accumulation over the 128 channels, then the log2-domain softmax scale.
+template <int G>
+__global__ __launch_bounds__(256) void rvq_lut_kernel(RvqDecArgs a, float* __restrict__ lut) {
+  const int unit = blockIdx.y;
+  const int b = unit / a.Hkv, kvh = unit % a.Hkv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int n_cw = a.N * a.Kc;
+  const int base = (blockIdx.x * 4 + wave) * 16;
+  if (base >= n_cw) return;
+  const int cw = min(base + col, n_cw - 1);
+  const uint16_t* qh = a.q + (static_cast<size_t>(b) * a.Hq + kvh * G + min(col, G - 1)) * kD;
+  float4v acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int ks = 0; ks < kD / 32; ++ks) {
+    const half8 av = *reinterpret_cast<const half8*>(a.k_cb + static_cast<size_t>(cw) * kD + 32 * ks + 8 * grp);
+    half8 bv = *reinterpret_cast<const half8*>(qh + 32 * ks + 8 * grp);
+    if (col >= G) bv = half8{0, 0, 0, 0, 0, 0, 0, 0};
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, acc, 0, 0, 0);
+  }
+  // D[row = codeword base + 4 grp + r][column = head col]
+  if (col < G) {
+    float* dst = lut + static_cast<size_t>(unit) * lut_stride(G, a.N, a.Kc) + static_cast<size_t>(col) * n_cw;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int e = base + 4 * grp + r;
+      if (e < n_cw) dst[e] = acc[r] * a.q_scale;
+    }
+  }
+}
 
 // Sum over stages of the lane's 16 channels of the indexed codewords (fp32,
 // stage order).
@@ -325,14 +368,36 @@ __device__ __forceinline__ void rebuild16(const uint16_t* cb, const int16_t* idx
 // Lane = (token j of 8, 16-channel chunk ck of 8); 32-token tiles; online
 // softmax per tile; each split writes its partial state, merged by
 // split_merge_kernel (merge.h) in split order.
-template <int G>
+template <int G, bool LUT>
 __global__ __launch_bounds__(256) void rvq_decode_kernel(RvqDecArgs a) {
   constexpr int NCK = 8, TL = 8, IT = 4;
   __shared__ float lds_m[kDecWaves][G], lds_l[kDecWaves][G], lds_o[kDecWaves][G][kD];
+  __shared__ __attribute__((aligned(16))) float lds_lut[LUT ? kLutFloats : 4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int j = lane / NCK, ck = lane % NCK, c0 = 16 * ck;
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const size_t unit = static_cast<size_t>(b) * a.Hkv + kvh;
+  if constexpr (LUT) {
+    // the unit's key-logit table into LDS (at most kLutFloats, checked on
+    // the host), eight 16-byte loads per thread in flight before any store
+    const int n4 = lut_stride(G, a.N, a.Kc) / 4;
+    const float4* src = reinterpret_cast<const float4*>(a.lut + unit * static_cast<size_t>(4 * n4));
+    float4* dst = reinterpret_cast<float4*>(lds_lut);
+    for (int base = 0; base < n4; base += 8 * 256) {
+      float4 r[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int i = base + 256 * k + static_cast<int>(threadIdx.x);
+        r[k] = i < n4 ? src[i] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int i = base + 256 * k + static_cast<int>(threadIdx.x);
+        if (i < n4) dst[i] = r[k];
+      }
+    }
+    __syncthreads();
+  }
   float qr[G][16];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -357,19 +422,34 @@ __global__ __launch_bounds__(256) void rvq_decode_kernel(RvqDecArgs a) {
     for (int it = 0; it < IT; ++it) {
       const int t = ti * kGroup + it * TL + j;
       valid[it] = t < a.T;
-      float kh[16];
-      if (valid[it]) {
-        rebuild16(a.k_cb, a.k_idx + (unit * a.T + t) * a.N, a.N, a.Kc, c0, kh);
+      if constexpr (LUT) {
+        // lane ck looks up stage ck (N <= 8 = NCK); the 8 lanes of token j sum
+        float part[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) part[h] = 0.0f;
+        if (valid[it] && ck < a.N) {
+          const int ci = min(static_cast<int>(static_cast<uint16_t>(a.k_idx[(unit * a.T + t) * a.N + ck])),
+                             a.Kc - 1);
+#pragma unroll
+          for (int h = 0; h < G; ++h) part[h] = lds_lut[(h * a.N + ck) * a.Kc + ci];
+        }
+#pragma unroll
+        for (int h = 0; h < G; ++h) lg[it][h] = sum_adjacent<NCK>(part[h]);
       } else {
+        float kh[16];
+        if (valid[it]) {
+          rebuild16(a.k_cb, a.k_idx + (unit * a.T + t) * a.N, a.N, a.Kc, c0, kh);
+        } else {
 #pragma unroll
-        for (int c = 0; c < 16; ++c) kh[c] = 0.0f;
-      }
+          for (int c = 0; c < 16; ++c) kh[c] = 0.0f;
+        }
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float s = 0.0f;
+        for (int h = 0; h < G; ++h) {
+          float s = 0.0f;
 #pragma unroll
-        for (int c = 0; c < 16; ++c) s = fmaf(qr[h][c], kh[c], s);
-        lg[it][h] = sum_adjacent<NCK>(s);
+          for (int c = 0; c < 16; ++c) s = fmaf(qr[h][c], kh[c], s);
+          lg[it][h] = sum_adjacent<NCK>(s);
+        }
       }
     }
     bool grow = false;
@@ -434,7 +514,7 @@ __global__ __launch_bounds__(256) void rvq_decode_kernel(RvqDecArgs a) {
 
 struct RvqGeometry {
   int G, n_tiles, tps, splits;
-  size_t units, ws_bytes;
+  size_t units, ws_bytes, lut_off;
 };
 
 int rvq_geometry(int B, int Hq, int Hkv, int T, int d, RvqGeometry* g) {
@@ -452,7 +532,9 @@ int rvq_geometry(int B, int Hq, int Hkv, int T, int d, RvqGeometry* g) {
   if (s < 1) s = 1;
   g->tps = g->n_tiles > 0 ? static_cast<int>((g->n_tiles + s - 1) / s) : 1;
   g->splits = g->n_tiles > 0 ? (g->n_tiles + g->tps - 1) / g->tps : 1;
-  g->ws_bytes = partial_state_bytes(g->units, g->splits, g->G, kD);
+  // partial states, then room for the key-logit table of every unit
+  g->lut_off = (partial_state_bytes(g->units, g->splits, g->G, kD) + 255) / 256 * 256;
+  g->ws_bytes = g->lut_off + g->units * kLutFloats * sizeof(float);
   return DQA_OK;
 }
 
@@ -504,6 +586,8 @@ extern "C" int rvq_decode_attention(const uint16_t* q, int B, int Hq, int Hkv, i
   if (g.units == 0) return DQA_OK;
   if (!q || !out) return DQA_ERR_NULL;
   if (T > 0 && (!k_idx || !v_idx || !k_cb || !v_cb)) return DQA_ERR_NULL;
+  auto a16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+  if (!a16(q) || (T > 0 && (!a16(k_cb) || !a16(v_cb)))) return DQA_ERR_ALIGN;
   if (!ws || ws_bytes < g.ws_bytes) return DQA_ERR_WORKSPACE;
   RvqDecArgs a;
   a.q = q;
@@ -513,6 +597,8 @@ extern "C" int rvq_decode_attention(const uint16_t* q, int B, int Hq, int Hkv, i
   a.v_cb = v_cb;
   a.out = out;
   a.partials = static_cast<float*>(ws);
+  float* lut = reinterpret_cast<float*>(static_cast<char*>(ws) + g.lut_off);
+  a.lut = lut;
   a.Hq = Hq;
   a.Hkv = Hkv;
   a.T = T;
@@ -524,11 +610,28 @@ extern "C" int rvq_decode_attention(const uint16_t* q, int B, int Hq, int Hkv, i
   a.q_scale = sm_scale * 1.4426950408889634f;
   const dim3 grid(g.splits, Hkv, B);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  switch (g.G) {
-    case 1: hipLaunchKernelGGL(rvq_decode_kernel<1>, grid, dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL(rvq_decode_kernel<2>, grid, dim3(256), 0, s, a); break;
-    case 3: hipLaunchKernelGGL(rvq_decode_kernel<3>, grid, dim3(256), 0, s, a); break;
-    case 4: hipLaunchKernelGGL(rvq_decode_kernel<4>, grid, dim3(256), 0, s, a); break;
+  // the table path needs the unit's table in LDS and one stage per lookup lane
+  const bool use_lut = T > 0 && static_cast<long long>(g.G) * N * Kc <= kLutFloats && N <= 8;
+  if (use_lut) {
+    const dim3 lgrid((N * Kc + 63) / 64, static_cast<unsigned>(g.units));
+    switch (g.G) {
+      case 1: hipLaunchKernelGGL(rvq_lut_kernel<1>, lgrid, dim3(256), 0, s, a, lut); break;
+      case 2: hipLaunchKernelGGL(rvq_lut_kernel<2>, lgrid, dim3(256), 0, s, a, lut); break;
+      case 3: hipLaunchKernelGGL(rvq_lut_kernel<3>, lgrid, dim3(256), 0, s, a, lut); break;
+      case 4: hipLaunchKernelGGL(rvq_lut_kernel<4>, lgrid, dim3(256), 0, s, a, lut); break;
+      default: return DQA_ERR_UNSUPPORTED;
+    }
+    DQA_CHECK_LAUNCH();
+  }
+  switch (g.G * 2 + (use_lut ? 1 : 0)) {
+    case 2: hipLaunchKernelGGL((rvq_decode_kernel<1, false>), grid, dim3(256), 0, s, a); break;
+    case 3: hipLaunchKernelGGL((rvq_decode_kernel<1, true>), grid, dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((rvq_decode_kernel<2, false>), grid, dim3(256), 0, s, a); break;
+    case 5: hipLaunchKernelGGL((rvq_decode_kernel<2, true>), grid, dim3(256), 0, s, a); break;
+    case 6: hipLaunchKernelGGL((rvq_decode_kernel<3, false>), grid, dim3(256), 0, s, a); break;
+    case 7: hipLaunchKernelGGL((rvq_decode_kernel<3, true>), grid, dim3(256), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((rvq_decode_kernel<4, false>), grid, dim3(256), 0, s, a); break;
+    case 9: hipLaunchKernelGGL((rvq_decode_kernel<4, true>), grid, dim3(256), 0, s, a); break;
     default: return DQA_ERR_UNSUPPORTED;
   }
   DQA_CHECK_LAUNCH();

@@ -298,8 +298,9 @@ int rvq_encode(const uint16_t* x, int64_t n, int d, const uint16_t* codebooks,
                int N, int Kc, int16_t* idx, void* ws, size_t ws_bytes,
                void* stream);
 
-/* Workspace bytes for rvq_decode_attention (0 if invalid; at least 256
- * otherwise): partial softmax states, no initialization needed. */
+/* Workspace bytes for rvq_decode_attention (0 if invalid): partial softmax
+ * states, then room for the key-logit table, 64 KB per (batch, KV head); no
+ * initialization needed. */
 size_t rvq_decode_attention_workspace_bytes(int B, int Hq, int Hkv, int T, int d);
 
 /* Decode attention with keys and values rebuilt on the fly from their
@@ -308,8 +309,15 @@ size_t rvq_decode_attention_workspace_bytes(int B, int Hq, int Hkv, int T, int d
  *   q (device) fp16 [B][Hq][d]; k_idx, v_idx (device) int16 [B][Hkv][T][N]
  *   k_codebooks, v_codebooks (device) fp16 [N][Kc][d]
  *   out (device) fp32 [B][Hq][d]
- * Enqueues the split kernel and, with several splits, their merge.
- * Errors: DQA_ERR_NULL, DQA_ERR_SHAPE, DQA_ERR_WORKSPACE,
+ *   q and the codebooks 16-byte aligned (else DQA_ERR_ALIGN)
+ * When G * N * Kc <= 16384 (G = Hq / Hkv) the key logits go through a
+ * per-(batch, KV head) table of q_h . Ck_s[c] kept in the workspace and
+ * staged in LDS, so each key costs N lookups instead of N gathered
+ * codewords (one extra small kernel enqueued first); otherwise keys are
+ * rebuilt like values.
+ * Enqueues the table kernel (when used), the split kernel and, with several
+ * splits, their merge.
+ * Errors: DQA_ERR_NULL, DQA_ERR_SHAPE, DQA_ERR_ALIGN, DQA_ERR_WORKSPACE,
  * DQA_ERR_UNSUPPORTED, DQA_ERR_HIP. */
 int rvq_decode_attention(const uint16_t* q, int B, int Hq, int Hkv, int T,
                          int d, const int16_t* k_idx, const int16_t* v_idx,

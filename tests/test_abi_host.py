@@ -207,7 +207,7 @@ def test_rvq_validation_and_workspace():
     assert lib.rvq_encode(FAKE, 10, 128, FAKE, 4, 1024, FAKE, FAKE, 100, None) == 4
     assert lib.rvq_encode(None, 0, 128, None, 4, 1024, None, None, 0, None) == 0    # empty
     w = lib.rvq_decode_attention_workspace_bytes(2, 24, 8, 8192, 128)
-    assert w > 0
+    assert w > 16 * 65536                     # room for a 64 KB key-logit table per unit
     assert lib.rvq_decode_attention_workspace_bytes(2, 24, 8, 8192, 64) == 0
     assert lib.rvq_decode_attention_workspace_bytes(2, 40, 8, 8192, 128) == 5 - 5   # ratio 5
     args = lambda **k: [k.get(n, v) for n, v in [
@@ -218,6 +218,8 @@ def test_rvq_validation_and_workspace():
     assert lib.rvq_decode_attention(*args(N=9)) == 2
     assert lib.rvq_decode_attention(*args(ki=None)) == 1
     assert lib.rvq_decode_attention(*args(wsb=16)) == 4
+    assert lib.rvq_decode_attention(*args(q=ctypes.c_void_p(0x1002))) == 8
+    assert lib.rvq_decode_attention(*args(vc=ctypes.c_void_p(0x1008))) == 8
 
 
 def test_kivi_append_validation():

@@ -114,8 +114,13 @@ def test_full_config_encode_and_decode(dqa):
         assert err <= TOL
 
 
+# key logits through the per-unit table when G * N * Kc <= 16384 floats, by
+# gathered codewords otherwise: the last two cases take the gather path, the
+# one before sits at the table's limit
 @pytest.mark.parametrize("B,Hq,Hkv,T,N,Kc", [(1, 3, 1, 100, 4, 64), (2, 8, 2, 33, 2, 128),
-                                             (1, 4, 4, 1, 1, 64), (2, 2, 1, 700, 8, 64)])
+                                             (1, 4, 4, 1, 1, 64), (2, 2, 1, 700, 8, 64),
+                                             (1, 4, 1, 90, 4, 1024), (1, 4, 1, 150, 8, 1024),
+                                             (1, 2, 1, 77, 4, 4096)])
 def test_decode_attention_small(dqa, B, Hq, Hkv, T, N, Kc):
     inp = rvq_inputs(B, Hq, Hkv, 128, T, N, Kc, seed=T)
     rng = np.random.default_rng(T)
