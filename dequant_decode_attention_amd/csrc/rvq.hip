@@ -292,6 +292,7 @@ constexpr int kDecWaves = 4;
 // key logit into N lookups instead of N gathered codewords.  Used when the
 // table of one (batch, KV head) fits this many floats of LDS.
 constexpr int kLutFloats = 16384;   // 64 KB
+constexpr int kLutWorkgroups = 512; // table-path workgroups resident at once (2 per compute unit)
 
 // floats between the tables of consecutive units (16-byte aligned rows)
 __host__ __device__ inline int lut_stride(int G, int N, int Kc) { return (G * N * Kc + 63) / 64 * 64; }
@@ -344,23 +345,34 @@ __global__ __launch_bounds__(256) void rvq_lut_kernel(RvqDecArgs a, float* __res
 }
 
 // Sum over stages of the lane's 16 channels of the indexed codewords (fp32,
-// stage order).
+// stage order).  The rows of up to four stages are requested before any is
+// summed, so a token costs one memory round trip per four stages.
 __device__ __forceinline__ void rebuild16(const uint16_t* cb, const int16_t* idx, int N, int Kc,
                                           int c0, float* out) {
 #pragma unroll
   for (int c = 0; c < 16; ++c) out[c] = 0.0f;
-  for (int s = 0; s < N; ++s) {
-    // indices are in [0, Kc) when produced by rvq_encode; clamp so that a
-    // corrupt index cannot read outside the codebook
-    const uint32_t ci = min(static_cast<uint32_t>(static_cast<uint16_t>(idx[s])), static_cast<uint32_t>(Kc - 1));
-    const uint16_t* row = cb + (static_cast<size_t>(s) * Kc + ci) * kD + c0;
-    const uint4 a = reinterpret_cast<const uint4*>(row)[0];
-    const uint4 b = reinterpret_cast<const uint4*>(row)[1];
-    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  for (int s0 = 0; s0 < N; s0 += 4) {
+    uint4 ra[4], rb[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      out[2 * i] += h2f(static_cast<uint16_t>(w[i] & 0xFFFFu));
-      out[2 * i + 1] += h2f(static_cast<uint16_t>(w[i] >> 16));
+    for (int k = 0; k < 4; ++k) {
+      // indices are in [0, Kc) when produced by rvq_encode; clamp so that a
+      // corrupt index cannot read outside the codebook (stages past N read
+      // row 0 of the last stage and are not summed)
+      const int s = min(s0 + k, N - 1);
+      const uint32_t ci = min(static_cast<uint32_t>(static_cast<uint16_t>(idx[s])), static_cast<uint32_t>(Kc - 1));
+      const uint4* row = reinterpret_cast<const uint4*>(cb + (static_cast<size_t>(s) * Kc + ci) * kD + c0);
+      ra[k] = row[0];
+      rb[k] = row[1];
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (s0 + k >= N) break;
+      const uint32_t w[8] = {ra[k].x, ra[k].y, ra[k].z, ra[k].w, rb[k].x, rb[k].y, rb[k].z, rb[k].w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        out[2 * i] += h2f(static_cast<uint16_t>(w[i] & 0xFFFFu));
+        out[2 * i + 1] += h2f(static_cast<uint16_t>(w[i] >> 16));
+      }
     }
   }
 }
@@ -607,11 +619,20 @@ extern "C" int rvq_decode_attention(const uint16_t* q, int B, int Hq, int Hkv, i
   a.n_tiles = g.n_tiles;
   a.tiles_per_split = g.tps;
   a.splits = g.splits;
+  const bool use_lut = T > 0 && static_cast<long long>(g.G) * N * Kc <= kLutFloats && N <= 8;
+  if (use_lut) {
+    // two table-holding workgroups fit a compute unit: one resident round
+    // of them, so that each stages its table once for more tiles
+    long long sp = kLutWorkgroups / static_cast<long long>(g.units);
+    if (sp > g.splits) sp = g.splits;
+    if (sp < 1) sp = 1;
+    a.tiles_per_split = static_cast<int>((g.n_tiles + sp - 1) / sp);
+    a.splits = (g.n_tiles + a.tiles_per_split - 1) / a.tiles_per_split;
+  }
   a.q_scale = sm_scale * 1.4426950408889634f;
-  const dim3 grid(g.splits, Hkv, B);
+  const dim3 grid(a.splits, Hkv, B);
   hipStream_t s = static_cast<hipStream_t>(stream);
   // the table path needs the unit's table in LDS and one stage per lookup lane
-  const bool use_lut = T > 0 && static_cast<long long>(g.G) * N * Kc <= kLutFloats && N <= 8;
   if (use_lut) {
     const dim3 lgrid((N * Kc + 63) / 64, static_cast<unsigned>(g.units));
     switch (g.G) {
@@ -635,5 +656,5 @@ extern "C" int rvq_decode_attention(const uint16_t* q, int B, int Hq, int Hkv, i
     default: return DQA_ERR_UNSUPPORTED;
   }
   DQA_CHECK_LAUNCH();
-  return launch_split_merge<kD>(a.partials, g.splits, B, Hq, Hkv, out, s);
+  return launch_split_merge<kD>(a.partials, a.splits, B, Hq, Hkv, out, s);
 }
