@@ -53,6 +53,10 @@ TOKEN_CASES = [
     (2, 8, 2, 300, 128),
     (1, 8, 2, 1000, 128),
     (1, 4, 4, 640, 64),
+    (1, 3, 3, 64, 128),      # one key tile exactly, head ratio 1
+    (2, 6, 3, 128, 128),     # one query tile exactly, 6 units
+    (1, 4, 1, 129, 64),      # one row past a tile
+    (3, 12, 3, 257, 128),    # 9 units, ragged
 ]
 
 

@@ -110,6 +110,8 @@ SINK_OUT_CASES = [
     (1, 4, 1, 128, 100, 4, 0, 4, {2: .5, 4: .5}, {2: .5, 8: .5}),
     (1, 4, 2, 64, 70, 3, 70, 1, PV, PK),                         # the whole old cache as sink
     (1, 4, 1, 128, 300, 16, 8, 3, PV, {0: .2, 2: .3, 4: .2, 8: .2, 16: .1}),   # with evicted channels
+    (2, 2, 2, 64, 257, 5, 33, 4, PV, PK),                        # head ratio 1, d 64, longest side list
+    (1, 4, 2, 128, 90, 0, 2, 2, {8: 1.0}, {2: .5, 4: .5}),       # head ratio 2, one width
 ]
 
 
