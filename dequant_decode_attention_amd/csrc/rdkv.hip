@@ -380,10 +380,20 @@ __global__ __launch_bounds__(128) void rdkv_chan_finish_kernel(const float* __re
   const int u = blockIdx.x, ch = threadIdx.x;
   if (ch >= D) return;
   double sq = 0.0, sk = 0.0;
-  for (int c = 0; c < chunks; ++c) {
-    const float* p = part + (static_cast<size_t>(c) * units + u) * 2 * D;
-    sq += p[ch];
-    sk += p[D + ch];
+  for (int c0 = 0; c0 < chunks; c0 += 8) {   // eight chunks in flight, summed in chunk order
+    float a[8], b[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float* p = part + (static_cast<size_t>(min(c0 + k, chunks - 1)) * units + u) * 2 * D;
+      a[k] = p[ch];
+      b[k] = p[D + ch];
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (c0 + k < chunks) {
+        sq += a[k];
+        sk += b[k];
+      }
   }
   w[static_cast<size_t>(u) * D + ch] = static_cast<float>(sqrt(sq) * sqrt(sk) / sqrt(static_cast<double>(D)));
 }
@@ -450,51 +460,62 @@ __global__ __launch_bounds__(256) void rdkv_hist_kernel(const float* __restrict_
   for (int i = tid; i < kBins; i += 256) out[i] = h[i];
 }
 
-__global__ __launch_bounds__(256) void rdkv_select_kernel(const unsigned* __restrict__ hist, int chunks,
-                                                          AllocState* __restrict__ st, int shift, int bits,
-                                                          int first_pass) {
-  __shared__ unsigned long long tot[256], above[256], total;
+constexpr int kSelectThreads = 1024;
+
+__global__ __launch_bounds__(kSelectThreads) void rdkv_select_kernel(const unsigned* __restrict__ hist,
+                                                                     int chunks, AllocState* __restrict__ st,
+                                                                     int shift, int bits, int first_pass) {
+  __shared__ unsigned long long suf[kSelectThreads];
   const int row = blockIdx.x, tid = threadIdx.x;
   if (st[row].done) return;
   const unsigned long long prefix = st[row].prefix;
   const unsigned long long rem = static_cast<unsigned long long>(st[row].remaining);
-  const int per = (1 << bits) / 256;  // bins per thread: 8 or 1
-  unsigned long long bin[8];
+  // thread t holds bins [per t, per t + per): 2 of 2048, or 1 of 256 for
+  // t < 256; each bin summed over the chunks in chunk order
+  const int nbins = 1 << bits;
+  const int per = nbins >= kSelectThreads ? nbins / kSelectThreads : 1;
+  const bool has = tid * per < nbins;
+  unsigned long long bin[2] = {0, 0};
   unsigned long long t = 0;
-  for (int j = 0; j < 8; ++j) {
-    bin[j] = 0;
-    if (j < per) {
+  if (has) {
+    for (int j = 0; j < per; ++j) {
       const unsigned* hp = hist + static_cast<size_t>(row) * chunks * kBins + tid * per + j;
-      for (int c = 0; c < chunks; ++c) bin[j] += hp[static_cast<size_t>(c) * kBins];
+      for (int c0 = 0; c0 < chunks; c0 += 8) {   // eight loads in flight, summed in chunk order
+        unsigned v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = c0 + k < chunks ? hp[static_cast<size_t>(c0 + k) * kBins] : 0u;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) bin[j] += v[k];
+      }
       t += bin[j];
     }
   }
-  tot[tid] = t;
+  // inclusive suffix sums over the threads (Hillis-Steele in LDS)
+  suf[tid] = t;
   __syncthreads();
-  if (tid == 0) {
-    unsigned long long a = 0;
-    for (int i = 255; i >= 0; --i) {
-      above[i] = a;
-      a += tot[i];
-    }
-    total = a;
+  for (int off = 1; off < kSelectThreads; off <<= 1) {
+    const unsigned long long v = tid + off < kSelectThreads ? suf[tid + off] : 0ull;
+    __syncthreads();
+    suf[tid] += v;
+    __syncthreads();
   }
-  __syncthreads();
+  const unsigned long long total = suf[0];
+  const unsigned long long above = suf[tid] - t;   // mass of the bins above this thread's
   if (first_pass && total <= rem) {
     if (tid == 0) st[row].done = 1;
     return;
   }
   // the thread whose bins hold the breakpoint where the mass counted from
   // the top first exceeds the remaining budget
-  if (above[tid] <= rem && rem < above[tid] + tot[tid]) {
-    unsigned long long a = above[tid];
+  if (has && above <= rem && rem < above + t) {
+    unsigned long long acc = above;
     for (int j = per - 1; j >= 0; --j) {
-      if (a + bin[j] > rem) {
+      if (acc + bin[j] > rem) {
         st[row].prefix = prefix | (static_cast<unsigned long long>(tid * per + j) << shift);
-        st[row].remaining = static_cast<long long>(rem - a);
+        st[row].remaining = static_cast<long long>(rem - acc);
         break;
       }
-      a += bin[j];
+      acc += bin[j];
     }
   }
 }
@@ -532,8 +553,8 @@ int alloc_run(const float* w, int rows, int n, long long budget, int8_t* widths,
     hipLaunchKernelGGL(rdkv_hist_kernel, dim3(chunks, rows), dim3(256), 0, s, w, n, chunks, st, kShift[p],
                        kBits[p], hist);
     DQA_CHECK_LAUNCH();
-    hipLaunchKernelGGL(rdkv_select_kernel, dim3(rows), dim3(256), 0, s, hist, chunks, st, kShift[p], kBits[p],
-                       p == 0 ? 1 : 0);
+    hipLaunchKernelGGL(rdkv_select_kernel, dim3(rows), dim3(kSelectThreads), 0, s, hist, chunks, st, kShift[p],
+                       kBits[p], p == 0 ? 1 : 0);
     DQA_CHECK_LAUNCH();
   }
   hipLaunchKernelGGL(rdkv_widths_kernel, dim3((n + 255) / 256, rows), dim3(256), 0, s, w, n, st, widths);
