@@ -51,8 +51,10 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));  // promotable (HIP'
 constexpr int kLseRows = 128;   // query rows per workgroup in pass 1 (4 waves x 32)
 constexpr int kLseKeys = 64;    // keys per LDS tile in pass 1
 constexpr int kSumWaves = 4;    // waves per workgroup in pass 2, sharing one query tile
-constexpr int kSumKeys = 32 * kSumWaves;  // keys per workgroup in pass 2
-constexpr int kSumRows = 64;    // query rows per LDS tile in pass 2
+constexpr int kSumNB = 2;       // 16-key blocks per wave in pass 2 (keys in registers)
+constexpr int kSumRB = 4;       // 16-row blocks per query tile in pass 2
+constexpr int kSumKeys = 16 * kSumNB * kSumWaves;  // keys per workgroup in pass 2
+constexpr int kSumRows = 16 * kSumRB;               // query rows per LDS tile in pass 2
 constexpr int kChanRows = 256;  // positions per workgroup of the channel sums
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazy = 8.0f;        // log2 headroom before the reference max moves
@@ -232,12 +234,12 @@ __global__ __launch_bounds__(64 * kSumWaves) void rdkv_colsum_kernel(const uint1
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int col = lane & 15, grp = lane >> 4;
-  const int k0 = kt * kSumKeys + wave * 32;
+  const int k0 = kt * kSumKeys + wave * 16 * kSumNB;
 
   const uint16_t* kh = k + static_cast<size_t>(u) * T * D;
-  half8 bk[2][KS];
+  half8 bk[kSumNB][KS];
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
+  for (int nb = 0; nb < kSumNB; ++nb) {
     const int key = min(k0 + 16 * nb + col, T - 1);
 #pragma unroll
     for (int s = 0; s < KS; ++s)
@@ -262,7 +264,9 @@ __global__ __launch_bounds__(64 * kSumWaves) void rdkv_colsum_kernel(const uint1
     if (tid < kSumRows) pre_lse = lse[hb + min(qt * kSumRows + tid, T - 1)];
   };
 
-  float cs[2] = {0.0f, 0.0f};
+  float cs[kSumNB];
+#pragma unroll
+  for (int nb = 0; nb < kSumNB; ++nb) cs[nb] = 0.0f;
   gload(0);
   for (int i = 0; i < iters; ++i) {
     const int r0 = (nqt - 1 - i / G) * kSumRows;
@@ -277,27 +281,28 @@ __global__ __launch_bounds__(64 * kSumWaves) void rdkv_colsum_kernel(const uint1
     gload(min(i + 1, iters - 1));  // unconditional: keeps the prefetch in registers
     if (r0 + kSumRows - 1 < k0) continue;  // every row of the tile precedes the wave's keys
 
-    float4v acc[4][2];
+    float4v acc[kSumRB][kSumNB];
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      acc[rb][0] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
-      acc[rb][1] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int rb = 0; rb < kSumRB; ++rb) {
+#pragma unroll
+      for (int nb = 0; nb < kSumNB; ++nb) acc[rb][nb] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
         const half8 af = *reinterpret_cast<const half8*>(&lds_q[(16 * rb + col) * PAD + 32 * s + 8 * grp]);
-        acc[rb][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bk[0][s], acc[rb][0], 0, 0, 0);
-        acc[rb][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bk[1][s], acc[rb][1], 0, 0, 0);
+#pragma unroll
+        for (int nb = 0; nb < kSumNB; ++nb)
+          acc[rb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bk[nb][s], acc[rb][nb], 0, 0, 0);
       }
     }
     auto accumulate = [&](auto masked) {
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
+      for (int rb = 0; rb < kSumRB; ++rb) {
         const float4 ls = *reinterpret_cast<const float4*>(&lds_lse[16 * rb + 4 * grp]);
         const float lsr[4] = {ls.x, ls.y, ls.z, ls.w};
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
 #pragma unroll
-          for (int nb = 0; nb < 2; ++nb) {
+          for (int nb = 0; nb < kSumNB; ++nb) {
             float p = fast_exp2(fmaf(acc[rb][nb][r], c, -lsr[r]));
             if constexpr (decltype(masked)::value) {
               const int row = r0 + 16 * rb + 4 * grp + r;
@@ -308,7 +313,7 @@ __global__ __launch_bounds__(64 * kSumWaves) void rdkv_colsum_kernel(const uint1
         }
       }
     };
-    if (r0 < k0 + 31 || r0 + kSumRows > T)  // a key after a row, or rows past the end
+    if (r0 < k0 + 16 * kSumNB - 1 || r0 + kSumRows > T)  // a key after a row, or rows past the end
       accumulate(std::true_type{});
     else
       accumulate(std::false_type{});
@@ -316,7 +321,7 @@ __global__ __launch_bounds__(64 * kSumWaves) void rdkv_colsum_kernel(const uint1
 
   float* wu = w + static_cast<size_t>(u) * T;
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
+  for (int nb = 0; nb < kSumNB; ++nb) {
     const float v = swap_rows<false>(swap_rows<false>(cs[nb], true), false);
     const int key = k0 + 16 * nb + col;
     if (grp == 0 && key < T) wu[key] = v;
