@@ -9,6 +9,8 @@ codebooks.
 
 The five workloads stand in for the model caches the pages measure on
 (Llama-2-13B, Llama-3.1-8B, Llama-3.2-3B shapes; no weights, no datasets).
+The bit allocator reads the prefill of the mixed-width cache: queries of
+every position and keys (``rdkv_inputs``, same draw order without values).
 Outlier channels imitate the stable high-magnitude key channels described
 in [P1 para 3] ([P1] = ihal.it/?p=61653, KV-cache quantization axes).
 """
