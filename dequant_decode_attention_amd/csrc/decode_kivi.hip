@@ -41,9 +41,13 @@ namespace dqa {
 namespace {
 
 constexpr int kWavesPerWG = 4;
-// workgroups of the decode kernel that are resident at once on 256 compute
-// units at 2 workgroups (8 waves) per unit
-constexpr int kDecodeWorkgroups = 512;
+// Waves per SIMD the decode kernel is compiled for, and the workgroups that
+// are then resident at once on 256 compute units (one workgroup = 4 waves,
+// so waves per SIMD = workgroups per unit).  The 2-bit kernel fits 3 waves
+// per SIMD (168 registers); the 4- and 8-bit kernels measured faster at 2.
+template <int BITS>
+constexpr int kDecodeWavesPerSimd = BITS == 2 ? 3 : 2;
+inline int decode_workgroups(int bits) { return 256 * (bits == 2 ? kDecodeWavesPerSimd<2> : kDecodeWavesPerSimd<4>); }
 
 struct KiviArgs {
   const uint16_t* q;
@@ -118,67 +122,81 @@ __device__ __forceinline__ Words<NB> load_words(const void* p) {
   return r;
 }
 
-// Codes of K-step ks (8 consecutive channels) from the lane's key words.
-template <int BITS>
-__device__ __forceinline__ uint64_t key_chunk(const uint32_t* w, int ks) {
-  if constexpr (BITS == 2) return (w[ks >> 1] >> ((ks & 1) * 16)) & 0xFFFFu;
-  else if constexpr (BITS == 4) return w[ks];
-  else return static_cast<uint64_t>(w[2 * ks]) | (static_cast<uint64_t>(w[2 * ks + 1]) << 32);
-}
-
 // A value the compiler must treat as unknown (keeps a VGPR constant out of
-// the scalar constant bus, and keeps byte extractions from being folded
-// back into bit-field extracts).
+// the scalar constant bus, and keeps shifted words from being folded back
+// into bit-field extracts).
 __device__ __forceinline__ uint32_t opaque(uint32_t v) {
   asm volatile("" : "+v"(v));
   return v;
 }
 
-// The 16 2-bit codes of one 32-bit key word (two K-steps of 8 channels) as
-// fp32: four masked shifts put four codes in the bytes of a register, and
-// each byte is converted on its own (code index 4b + j in byte b of
-// shift j; K-step 2wi + b/2, channel 4 (b & 1) + j).
-__device__ __forceinline__ void key_codes16_2bit(uint32_t w, float (*f)[8]) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t d = opaque((w >> (2 * j)) & 0x03030303u);
-#pragma unroll
-    for (int b = 0; b < 4; ++b) f[b >> 1][4 * (b & 1) + j] = static_cast<float>((d >> (8 * b)) & 0xFFu);
-  }
-}
-
-// The lane's 8-code chunk of one value channel (8 consecutive tokens); BITS
-// bytes at `p`.
+// Key codes as fp16 subnormals.  A code c placed in the low bits of an fp16
+// bit pattern whose exponent field is zero is the value c * 2^-24; a code
+// left at bit offset 2p (2-bit) or 4p (4-bit) inside its 16-bit half is
+// c * 2^(bits * p) * 2^-24, still subnormal while it stays below bit 10.  One
+// mask of the packed word therefore yields two such values (one per half),
+// and the mixed-precision FMA widens them exactly and multiplies by the fp32
+// scale pre-multiplied by 2^(24 - bits * p): code * scale + zero with one
+// rounding, the same result as an fp32 FMA on the integer code.
+//
+// Position p of K-step element e (channel c0 + e) inside its half.
 template <int BITS>
-__device__ __forceinline__ uint64_t load_chunk(const uint8_t* p) {
-  if constexpr (BITS == 2) return *reinterpret_cast<const uint16_t*>(p);
-  else if constexpr (BITS == 4) return *reinterpret_cast<const uint32_t*>(p);
-  else return *reinterpret_cast<const uint64_t*>(p);
+__device__ __forceinline__ constexpr int key_code_pos(int e) {
+  return BITS == 2 ? (e <= 4 ? e : e - 5) : (BITS == 4 ? (e & 1) : 0);
 }
-
-// Key chunk -> 8 fp32 codes, channel order.
+// The lane's masked key-code registers (key_code_reg / key_code_half give
+// the register and half of K-step element e).  2-bit: one word = 16
+// channels (two K-steps); register e holds channel e in the low half (even
+// K-step) and channel e + 8 in the high half (odd K-step).  4-bit: one word
+// = one K-step; register e & 3 holds channel e in half e >> 2.  8-bit: two
+// words = one K-step; word i gives registers 2i (channels 4i, 4i + 2) and
+// 2i + 1 (channels 4i + 1, 4i + 3).
 template <int BITS>
-__device__ __forceinline__ void key_codes8(uint64_t chunk, float* f) {
+__device__ __forceinline__ void key_code_regs(const uint32_t* w, int ks, uint32_t* m) {
   if constexpr (BITS == 2) {
-    const uint32_t v = static_cast<uint32_t>(chunk);
+    const uint32_t x = w[ks >> 1], x1 = opaque(x >> 10);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t m = (v >> (2 * j)) & 0x0303u;
-      f[j] = static_cast<float>(m & 0xFFu);
-      f[j + 4] = static_cast<float>(m >> 8);
-    }
+    for (int e = 0; e < 5; ++e) m[e] = x & (0x00030003u << (2 * e));
+#pragma unroll
+    for (int e = 5; e < 8; ++e) m[e] = x1 & (0x00030003u << (2 * (e - 5)));
   } else if constexpr (BITS == 4) {
-    const uint32_t w = static_cast<uint32_t>(chunk);
-    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      f[2 * k] = static_cast<float>((lo >> (8 * k)) & 0xFFu);
-      f[2 * k + 1] = static_cast<float>((hi >> (8 * k)) & 0xFFu);
-    }
+    const uint32_t x = w[ks], x1 = opaque(x >> 8);
+    m[0] = x & 0x000F000Fu;    // channels 0, 4
+    m[1] = x & 0x00F000F0u;    // channels 1, 5
+    m[2] = x1 & 0x000F000Fu;   // channels 2, 6
+    m[3] = x1 & 0x00F000F0u;   // channels 3, 7
   } else {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) f[k] = static_cast<float>((chunk >> (8 * k)) & 0xFFu);
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t x = w[2 * ks + i];
+      m[2 * i] = x & 0x00FF00FFu;                 // channels 4i, 4i + 2
+      m[2 * i + 1] = opaque(x >> 8) & 0x00FF00FFu; // channels 4i + 1, 4i + 3
+    }
   }
+}
+// register and half of K-step element e (ks: the K-step, for 2-bit)
+template <int BITS>
+__device__ __forceinline__ constexpr int key_code_reg(int e) {
+  return BITS == 2 ? e : (BITS == 4 ? (e & 3) : (2 * (e >> 2) + (e & 1)));
+}
+template <int BITS>
+__device__ __forceinline__ constexpr int key_code_half(int e, int ks) {
+  return BITS == 2 ? (ks & 1) : (BITS == 4 ? (e >> 2) : ((e >> 1) & 1));
+}
+
+// code (fp16 half A of m) * s + zero (fp16 half Z of z), one rounding
+template <int A, int Z>
+__device__ __forceinline__ float mix_dequant(uint32_t m, float s, uint32_t z) {
+  float r;
+  if constexpr (A == 0 && Z == 0)
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel_hi:[1,0,1]" : "=v"(r) : "v"(m), "v"(s), "v"(z));
+  else if constexpr (A == 1 && Z == 0)
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[1,0,0] op_sel_hi:[1,0,1]" : "=v"(r) : "v"(m), "v"(s), "v"(z));
+  else if constexpr (A == 0 && Z == 1)
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[0,0,1] op_sel_hi:[1,0,1]" : "=v"(r) : "v"(m), "v"(s), "v"(z));
+  else
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[1,0,1] op_sel_hi:[1,0,1]" : "=v"(r) : "v"(m), "v"(s), "v"(z));
+  return r;
 }
 
 // Value chunk (8 tokens of one channel) -> fp16 operand holding code *
@@ -280,10 +298,15 @@ __device__ __forceinline__ float combine2(float v, bool rows32) {
 __device__ __forceinline__ float max_rows(float v) { return combine2<true>(combine2<true>(v, true), false); }
 __device__ __forceinline__ float sum_rows(float v) { return combine2<false>(combine2<false>(v, true), false); }
 
+// First float of row j (token j of a tile) of the in-tile rotation table,
+// whose rows are ERF floats apart.
+template <int ERF>
+__device__ __forceinline__ constexpr int erow(int j) { return j * ERF + 16 * ((j >> 3) & 3); }
+
 // ------------------------------------------------------------- the kernel
 
 template <int D, int BITS, int G, bool ROPE>
-__global__ __launch_bounds__(256) void kivi_decode_kernel(KiviArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kDecodeWavesPerSimd<BITS>))) void kivi_decode_kernel(KiviArgs a) {
   constexpr int KS = D / 32;            // K-steps of the logit product
   constexpr int CPL = D / 4;            // key channels per lane (per token)
   constexpr int MB = D / 16;            // channel blocks of the value product
@@ -293,18 +316,26 @@ __global__ __launch_bounds__(256) void kivi_decode_kernel(KiviArgs a) {
   constexpr int LROW = CPL * BITS / 8;  // key bytes per lane per token
   constexpr int KROW = D * BITS / 8;    // key bytes per token
   constexpr int VBLK = 4 * D * BITS;    // value bytes per 32-token block
-  constexpr int ERS = NPAIR + 2;        // row stride of the in-tile rotation table (pairs)
+  // Row j of the in-tile rotation table starts at float j * ERF + 16 * ((j >> 3) & 3):
+  // ERF = 4 (mod 32) and the extra offset put the rows that one read
+  // instruction touches (tokens j, j + 8, j + 16, j + 24 of a lane group) in
+  // different LDS banks.
+  constexpr int ERF = ((2 * NPAIR + 44 + 31) / 32) * 32 + 4;
   constexpr int VST = 24;               // row stride of the fp16 value staging area (halves)
-  constexpr int QH = 2 * G * D;         // halves of the per-wave query operand (hi, lo)
+  constexpr int QS = D + 8;             // row stride of the query operand (halves): heads in different banks
+  constexpr int QH = 2 * G * QS;        // halves of the per-wave query operand (hi, lo)
   constexpr int WQ = QH > kGroup * VST ? QH : kGroup * VST;
   constexpr int LPP = kWave / NPAIR;    // lanes per RoPE pair in the query rotation
   constexpr int HPL = (G + LPP - 1) / LPP;  // heads per lane in the query rotation
   constexpr int SZW = D / 64;           // 32-bit words per lane of a tile's scale block
   static_assert(NCOL <= 16, "value-operand columns");
 
-  __shared__ __attribute__((aligned(16))) float lds_E[ROPE ? kGroup * ERS * 2 : 4];
+  __shared__ __attribute__((aligned(16))) float lds_E[ROPE ? kGroup * ERF : 4];
   __shared__ __attribute__((aligned(16))) _Float16 lds_w[kWavesPerWG][WQ];
-  __shared__ __attribute__((aligned(16))) _Float16 lds_ksz[kWavesPerWG][2][D];
+  // a tile's key scales (fp32, each times 2^(24 - BITS * p) for its code's
+  // bit position p: key_code_pos) and zeros (fp16)
+  __shared__ __attribute__((aligned(16))) float lds_ks[kWavesPerWG][D];
+  __shared__ __attribute__((aligned(16))) _Float16 lds_kz[kWavesPerWG][D];
   __shared__ __attribute__((aligned(16))) _Float16 lds_vsz[kWavesPerWG][2][NVG][kGroup];
   __shared__ float lds_m[kWavesPerWG][G], lds_l[kWavesPerWG][G];
   __shared__ float lds_o[kWavesPerWG][G][D];
@@ -351,8 +382,8 @@ __global__ __launch_bounds__(256) void kivi_decode_kernel(KiviArgs a) {
       rope_unit(1.0, a.omega[i], sc, ss);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        lds_E[((8 * q + j) * ERS + i) * 2] = bc;
-        lds_E[((8 * q + j) * ERS + i) * 2 + 1] = bs;
+        lds_E[erow<ERF>(8 * q + j) + 2 * i] = bc;
+        lds_E[erow<ERF>(8 * q + j) + 2 * i + 1] = bs;
         const float nc = bc * sc - bs * ss;
         const float ns = bc * ss + bs * sc;
         bc = nc;
@@ -390,11 +421,11 @@ __global__ __launch_bounds__(256) void kivi_decode_kernel(KiviArgs a) {
           r0 = qv[k][0] * cth + qv[k][1] * sth;
           r1 = qv[k][1] * cth - qv[k][0] * sth;
         }
-        const half2v hi = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(r0, r1));
+        const uint32_t hb = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(r0, r1));
         const half2v lo = __builtin_bit_cast(
-            half2v, __builtin_amdgcn_cvt_pkrtz(r0 - static_cast<float>(hi[0]), r1 - static_cast<float>(hi[1])));
-        *reinterpret_cast<half2v*>(&wq[h * D + 2 * pi]) = hi;
-        *reinterpret_cast<half2v*>(&wq[(G + h) * D + 2 * pi]) = lo;
+            half2v, __builtin_amdgcn_cvt_pkrtz(minus_half_lo(hb, r0), minus_half_hi(hb, r1)));
+        *reinterpret_cast<uint32_t*>(&wq[h * QS + 2 * pi]) = hb;
+        *reinterpret_cast<half2v*>(&wq[(G + h) * QS + 2 * pi]) = lo;
       }
     }
   };
@@ -417,16 +448,16 @@ __global__ __launch_bounds__(256) void kivi_decode_kernel(KiviArgs a) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int c0 = CPL * grp + 8 * ks;
-      const half8 bqh = *reinterpret_cast<const half8*>(&wq[qh * D + c0]);
-      const half8 bql = *reinterpret_cast<const half8*>(&wq[(G + qh) * D + c0]);
+      const half8 bqh = *reinterpret_cast<const half8*>(&wq[qh * QS + c0]);
+      const half8 bql = *reinterpret_cast<const half8*>(&wq[(G + qh) * QS + c0]);
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         float x[8];
         kf(s, ks, x);
         if constexpr (ROPE) {
           const int j = row_token(s, col);
-          const float4 e01 = *reinterpret_cast<const float4*>(&lds_E[(j * ERS + c0 / 2) * 2]);
-          const float4 e23 = *reinterpret_cast<const float4*>(&lds_E[(j * ERS + c0 / 2 + 2) * 2]);
+          const float4 e01 = *reinterpret_cast<const float4*>(&lds_E[erow<ERF>(j) + c0]);
+          const float4 e23 = *reinterpret_cast<const float4*>(&lds_E[erow<ERF>(j) + c0 + 4]);
           const float ec[4] = {e01.x, e01.z, e23.x, e23.z};
           const float es[4] = {e01.y, e01.w, e23.y, e23.w};
 #pragma unroll
@@ -478,6 +509,14 @@ __global__ __launch_bounds__(256) void kivi_decode_kernel(KiviArgs a) {
   };
 
   // ---------------------------------------------------------- quantized tile
+  // key-scale staging: lane r < 32 converts the scales of channels
+  // CPS * r .. CPS * r + CPS - 1, each times 2^(24 - BITS * p) for the bit
+  // position p of its code inside the masked register
+  constexpr int CPS = D / 32;
+  float sfac[CPS];
+#pragma unroll
+  for (int i = 0; i < CPS; ++i)
+    sfac[i] = __builtin_ldexpf(1.0f, 24 - BITS * key_code_pos<BITS>(((lane & 31) * CPS + i) & 7));
   const size_t qstride = static_cast<size_t>(a.qtile_stride);      // tiles per (batch, KV head)
   const uint8_t* const kbase = reinterpret_cast<const uint8_t*>(a.k_codes) + unit * qstride * kGroup * KROW;
   const uint8_t* const vbase = reinterpret_cast<const uint8_t*>(a.v_codes) + unit * qstride * VBLK;
@@ -524,10 +563,23 @@ __global__ __launch_bounds__(256) void kivi_decode_kernel(KiviArgs a) {
   auto quantized_tile = [&](int ti, const TileIn& cur, TileIn& nxt, bool prefetch) {
     {
       const int half = lane >> 5, r = lane & 31;
-      if constexpr (SZW == 2) {
-        *reinterpret_cast<uint2*>(&lds_ksz[wave][half][r * (D / 32)]) = uint2{cur.ksz[0], cur.ksz[1]};
+      if (half == 0) {
+        float sv[CPS];
+#pragma unroll
+        for (int i = 0; i < CPS; ++i)
+          sv[i] = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(cur.ksz[i >> 1] >> ((i & 1) * 16)))) *
+                  sfac[i];
+        if constexpr (CPS == 4) {
+          *reinterpret_cast<float4*>(&lds_ks[wave][r * CPS]) = float4{sv[0], sv[1], sv[2], sv[3]};
+        } else {
+          *reinterpret_cast<float2*>(&lds_ks[wave][r * CPS]) = float2{sv[0], sv[1]};
+        }
       } else {
-        *reinterpret_cast<uint32_t*>(&lds_ksz[wave][half][r * (D / 32)]) = cur.ksz[0];
+        if constexpr (SZW == 2) {
+          *reinterpret_cast<uint2*>(&lds_kz[wave][r * CPS]) = uint2{cur.ksz[0], cur.ksz[1]};
+        } else {
+          *reinterpret_cast<uint32_t*>(&lds_kz[wave][r * CPS]) = cur.ksz[0];
+        }
       }
 #pragma unroll
       for (int g = 0; g < NVG; ++g)
@@ -545,21 +597,24 @@ __global__ __launch_bounds__(256) void kivi_decode_kernel(KiviArgs a) {
     wave_sync();
 
     float lg[8], p[8];
-    float kc2[2][2][8];   // 2-bit: codes of the current pair of K-steps, per half
+    uint32_t km[2][8];   // masked key-code registers of the current word(s), per half
     tile_logits(ti * kGroup,
                 [&](int s, int ks, float* x) {
-                  if constexpr (BITS == 2) {
-                    if ((ks & 1) == 0) key_codes16_2bit(cur.k[s].w[ks >> 1], kc2[s]);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) x[e] = kc2[s][ks & 1][e];
-                  } else {
-                    key_codes8<BITS>(key_chunk<BITS>(cur.k[s].w, ks), x);
-                  }
+                  if (BITS != 2 || (ks & 1) == 0) key_code_regs<BITS>(cur.k[s].w, ks, km[s]);
                   const int c0 = CPL * grp + 8 * ks;
-                  const half8 sh = *reinterpret_cast<const half8*>(&lds_ksz[wave][0][c0]);
-                  const half8 zh = *reinterpret_cast<const half8*>(&lds_ksz[wave][1][c0]);
+                  const float4 s0 = *reinterpret_cast<const float4*>(&lds_ks[wave][c0]);
+                  const float4 s1 = *reinterpret_cast<const float4*>(&lds_ks[wave][c0 + 4]);
+                  const uint4 zq = *reinterpret_cast<const uint4*>(&lds_kz[wave][c0]);
+                  const float sc[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+                  const uint32_t zw[4] = {zq.x, zq.y, zq.z, zq.w};
 #pragma unroll
-                  for (int e = 0; e < 8; ++e) x[e] = fmaf(x[e], static_cast<float>(sh[e]), static_cast<float>(zh[e]));
+                  for (int e = 0; e < 8; ++e) {
+                    const uint32_t mr = km[s][key_code_reg<BITS>(e)];
+                    if (key_code_half<BITS>(e, ks) == 0)
+                      x[e] = (e & 1) ? mix_dequant<0, 1>(mr, sc[e], zw[e >> 1]) : mix_dequant<0, 0>(mr, sc[e], zw[e >> 1]);
+                    else
+                      x[e] = (e & 1) ? mix_dequant<1, 1>(mr, sc[e], zw[e >> 1]) : mix_dequant<1, 0>(mr, sc[e], zw[e >> 1]);
+                  }
                 },
                 lg);
     softmax_step(lg, p);
@@ -709,11 +764,11 @@ int make_plan(const dqa_kivi_cache* c, Plan* p) {
   p->units = static_cast<size_t>(c->B) * c->Hkv;
   p->n_qtiles = c->T_q / kGroup;
   p->n_rtiles = (c->R + kGroup - 1) / kGroup;
-  // One resident round of workgroups (2 per compute unit: the kernel runs
-  // at 2 waves per SIMD), at least one tile per wave when the cache is long
-  // enough; an empty cache still gets one split (zero output).
+  // One resident round of workgroups (as many per compute unit as the
+  // kernel has waves per SIMD), at least one tile per wave when the cache is
+  // long enough; an empty cache still gets one split (zero output).
   const long long n_tiles = p->n_qtiles + p->n_rtiles;
-  long long want = (kDecodeWorkgroups + static_cast<long long>(p->units) - 1) /
+  long long want = (decode_workgroups(c->bits) + static_cast<long long>(p->units) - 1) /
                    static_cast<long long>(p->units > 0 ? p->units : 1);
   long long cap = (n_tiles + kWavesPerWG - 1) / kWavesPerWG;
   if (want > cap) want = cap;
