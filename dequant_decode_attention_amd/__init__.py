@@ -107,27 +107,41 @@ def _dev16(t, name):
 
 # ---------------------------------------------------------------- quantize
 
-def quantize_pack_k(k, bits):
+def _quant_out(out, shapes, device):
+    """Output tensors of a quantizer: `out` (codes, scale, zero) checked
+    against the expected shapes, or fresh ones."""
+    dts = (torch.int32, torch.float16, torch.float16)
+    if out is None:
+        return tuple(torch.empty(sh, dtype=dt, device=device) for sh, dt in zip(shapes, dts))
+    if len(out) != 3:
+        raise ValueError("out must be (codes, scale, zero)")
+    for t, sh, dt in zip(out, shapes, dts):
+        if tuple(t.shape) != tuple(sh) or t.dtype != dt or t.device != device or not t.is_contiguous():
+            raise ValueError(f"out tensor {tuple(t.shape)} {t.dtype}: expected contiguous {tuple(sh)} {dt}")
+    return tuple(out)
+
+
+def quantize_pack_k(k, bits, out=None):
     """k: fp16 [B, Hkv, T, d] -> (codes int32 [B, Hkv, T, d*bits/32] holding
-    uint32 words, scale fp16 [B, Hkv, T/32, d], zero fp16 [B, Hkv, T/32, d])."""
+    uint32 words, scale fp16 [B, Hkv, T/32, d], zero fp16 [B, Hkv, T/32, d]),
+    written into `out` when given."""
     k = _dev16(k, "k")
     B, H, T, d = k.shape
-    codes = torch.empty((B, H, T, d * bits // 32), dtype=torch.int32, device=k.device)
-    scale = torch.empty((B, H, T // 32, d), dtype=torch.float16, device=k.device)
-    zero = torch.empty_like(scale)
+    codes, scale, zero = _quant_out(out, ((B, H, T, d * bits // 32), (B, H, T // 32, d), (B, H, T // 32, d)),
+                                    k.device)
     _check("quantize_pack_k", lib.quantize_pack_k(_ptr(k), B, H, T, d, bits, _ptr(codes),
                                                   _ptr(scale), _ptr(zero), _stream(k.device)))
     return codes, scale, zero
 
 
-def quantize_pack_v(v, bits):
+def quantize_pack_v(v, bits, out=None):
     """v: fp16 [B, Hkv, T, d] -> (codes int32 [B, Hkv, T, d*bits/32], scale fp16
-    [B, Hkv, T, d/32], zero fp16 [B, Hkv, T, d/32])."""
+    [B, Hkv, T, d/32], zero fp16 [B, Hkv, T, d/32]), written into `out` when
+    given."""
     v = _dev16(v, "v")
     B, H, T, d = v.shape
-    codes = torch.empty((B, H, T, d * bits // 32), dtype=torch.int32, device=v.device)
-    scale = torch.empty((B, H, T, d // 32), dtype=torch.float16, device=v.device)
-    zero = torch.empty_like(scale)
+    codes, scale, zero = _quant_out(out, ((B, H, T, d * bits // 32), (B, H, T, d // 32), (B, H, T, d // 32)),
+                                    v.device)
     _check("quantize_pack_v", lib.quantize_pack_v(_ptr(v), B, H, T, d, bits, _ptr(codes),
                                                   _ptr(scale), _ptr(zero), _stream(v.device)))
     return codes, scale, zero

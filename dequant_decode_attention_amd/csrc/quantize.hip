@@ -18,7 +18,7 @@ namespace dqa {
 namespace {
 
 struct GroupParams {
-  float sf, zf, levels;
+  float sf, zf, levels, rcp;
   uint16_t s16, z16;
 };
 
@@ -30,118 +30,358 @@ __device__ __forceinline__ GroupParams group_params(float mn, float mx, int bits
   p.z16 = f2h(mn);                  // exact: mn is an fp16 value
   p.sf = h2f(p.s16);
   p.zf = mn;
+  // approximate reciprocal for the fast quotient (0 for a zero scale, whose
+  // codes are all 0)
+  p.rcp = p.sf == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(p.sf);
   return p;
 }
 
-__device__ __forceinline__ uint32_t quant_code(float x, const GroupParams& p) {
-  if (p.sf == 0.0f) return 0u;
-  const float t = (x - p.zf) / p.sf;
-  const float q = fminf(fmaxf(rintf(t), 0.0f), p.levels);
-  return static_cast<uint32_t>(q);
+// code = clamp(rint((x - z) / s), 0, 2^b - 1) with the IEEE quotient.  The
+// quotient is first approximated as t * rcp(s): rcp is within 1 ulp of 1/s,
+// so t * rcp(s) and the IEEE quotient t / s differ by less than 2^-21 of
+// their size, and both lie in [0, 2^b) * (1 + 2^-10) -- less than 2^-13 for
+// every width up to 8 bits.  Unless the approximation lies within 2^-12 of
+// a half-integer, both round to the same integer (and neither is a tie);
+// otherwise the IEEE division decides.  The result is the IEEE-division
+// code in every case.
+__device__ __forceinline__ float quant_code_f(float x, const GroupParams& p) {
+  const float t = x - p.zf;
+  const float y = t * p.rcp;
+  float q = rintf(y);
+  // |y - rint(y)| >= 0.5 - 2^-12: y within 2^-12 of a half-integer
+  if (__builtin_expect(__builtin_fabsf(y - q) >= 0.499755859375f, 0)) q = rintf(t / p.sf);
+  return __builtin_amdgcn_fmed3f(q, 0.0f, p.levels);
 }
 
-// Keys: one workgroup per (32-token tile, KV head, batch); thread c owns
-// channel c.  Codes are staged in LDS as bytes and re-read to build the
-// token-major packed words.
+// Packed fp16 minimum / maximum of two pairs (exact; the inputs are finite
+// fp16 values, so the plain instructions are used without the canonicalizing
+// moves the compiler would add for signalling NaNs), and a DPP lane exchange
+// of a 32-bit register.
+__device__ __forceinline__ uint32_t pk_min_h2(uint32_t a, uint32_t b) {
+  uint32_t r;
+  asm("v_pk_min_f16 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ uint32_t pk_max_h2(uint32_t a, uint32_t b) {
+  uint32_t r;
+  asm("v_pk_max_f16 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppRowRor8 = 0x128;   // row_ror:8 (lane i <- lane (i + 8) mod 16 within its row)
+// Packed min (MAX = false) or max of lane L and lane L ^ 32 (rows32) or
+// L ^ 16, through the row-swap permutes; every lane gets the result.  The
+// permute's two results are copied into scalars before use.
+template <bool MAX>
+__device__ __forceinline__ uint32_t pk_swap_rows(uint32_t x, bool rows32) {
+  uint32_t r0, r1;
+  if (rows32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    r0 = r[0];
+    r1 = r[1];
+  } else {
+    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    r0 = r[0];
+    r1 = r[1];
+  }
+  return MAX ? pk_max_h2(r0, r1) : pk_min_h2(r0, r1);
+}
+
+// The same code from the group's zero, reciprocal and (only on the exact
+// path) scale, read from `sf`.
+template <int BITS>
+__device__ __forceinline__ float quant_code_f(float x, float zf, float rcp, const float* sf) {
+  const float t = x - zf;
+  const float y = t * rcp;
+  float q = rintf(y);
+  if (__builtin_expect(__builtin_fabsf(y - q) >= 0.499755859375f, 0)) q = rintf(t / *sf);
+  return __builtin_amdgcn_fmed3f(q, 0.0f, static_cast<float>((1 << BITS) - 1));
+}
+
+// Tile of 32 tokens x D channels, thread (token quad tq, channel octet co):
+// tokens 4 tq .. 4 tq + 3, channels 8 co .. 8 co + 7, read as four 16-byte
+// loads.  x[r][e] = token 4 tq + r, channel 8 co + e.
+template <int D>
+__device__ __forceinline__ void load_quad_octet(const uint16_t* rows, int tq, int co, float (*x)[8]) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint4 u = *reinterpret_cast<const uint4*>(rows + static_cast<size_t>(4 * tq + r) * D + 8 * co);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[r][2 * j] = h2f(static_cast<uint16_t>(w[j] & 0xFFFFu));
+      x[r][2 * j + 1] = h2f(static_cast<uint16_t>(w[j] >> 16));
+    }
+  }
+}
+
+// Keys: one workgroup per (32-token tile, KV head, batch), D threads; thread
+// tid = (D/8) tq + co holds tokens 4 tq .. 4 tq + 3 of channels 8 co ..
+// 8 co + 7, so a wave's 16-byte loads cover whole rows.  A channel's group
+// spans the 8 threads of equal co: their partial min/max (packed fp16, exact)
+// combine across the wave's 16-lane rows with the row-swap permutes and, at
+// head dim 128, across the two waves through LDS (at 64, one wave holds all
+// 8 token quads and a DPP rotation combines the two halves of each row).
+// Each thread assembles its (token, octet) pieces of the token-major code
+// rows in LDS, and the tile is then copied out contiguously; thread
+// (tq, co) also writes the scale and zero of channel 8 co + tq.
 // Source rows: src_T per (batch, KV head); destination: dst_tiles 32-token
 // tiles of capacity per (batch, KV head), this launch's tiles starting at
 // tile0 (quantize_pack_k: src_T = T, dst_tiles = T/32, tile0 = 0).
-template <int D>
+template <int D, int BITS>
 __global__ __launch_bounds__(D) void quantize_k_kernel(
-    const uint16_t* __restrict__ k, int src_T, int Hkv, int bits,
+    const uint16_t* __restrict__ k, int src_T, int Hkv,
     uint32_t* __restrict__ codes, uint16_t* __restrict__ scale,
     uint16_t* __restrict__ zero, int dst_tiles, int tile0) {
-  __shared__ uint8_t lds_codes[kGroup][D];
-  const int c = threadIdx.x;
+  constexpr int NCO = D / 8;             // channel octets per token
+  // per channel: zero, reciprocal of the scale, scale (fp32)
+  __shared__ __attribute__((aligned(16))) float lds_par[3][NCO][8];
+  const int tid = threadIdx.x, tq = tid / NCO, co = tid % NCO;
   const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const size_t unit = static_cast<size_t>(b) * Hkv + h;
   const size_t dtile = unit * dst_tiles + tile0 + tile;        // destination tile
   const uint16_t* src = k + (unit * src_T + static_cast<size_t>(tile) * kGroup) * D;
 
-  float x[kGroup];
+  // min/max per channel pair in packed fp16 (exact: the inputs are fp16),
+  // over the thread's 4 tokens and then over the channel's 8 adjacent lanes
+  uint32_t w[4][4];
 #pragma unroll
-  for (int t = 0; t < kGroup; ++t) x[t] = h2f(src[t * D + c]);
-  float mn = x[0], mx = x[0];
-#pragma unroll
-  for (int t = 1; t < kGroup; ++t) {
-    mn = fminf(mn, x[t]);
-    mx = fmaxf(mx, x[t]);
+  for (int r = 0; r < 4; ++r) {
+    const uint4 u = *reinterpret_cast<const uint4*>(src + static_cast<size_t>(4 * tq + r) * D + 8 * co);
+    w[r][0] = u.x;
+    w[r][1] = u.y;
+    w[r][2] = u.z;
+    w[r][3] = u.w;
   }
-  const GroupParams p = group_params(mn, mx, bits);
-  const size_t sz_off = dtile * D + c;
-  scale[sz_off] = p.s16;
-  zero[sz_off] = p.z16;
+  uint32_t mnp[4], mxp[4];
 #pragma unroll
-  for (int t = 0; t < kGroup; ++t) lds_codes[t][c] = static_cast<uint8_t>(quant_code(x[t], p));
-  __syncthreads();
-
-  // Packed words of the tile: 32 tokens x (D*bits/32) words, contiguous.
-  const int words_per_token = D * bits / 32;
-  const int per_word = 32 / bits;
-  uint32_t* dst = codes + dtile * kGroup * words_per_token;
-  for (int w = c; w < kGroup * words_per_token; w += D) {
-    const int t = w / words_per_token;
-    const int c0 = (w % words_per_token) * per_word;
-    uint32_t word = 0;
-    for (int j = 0; j < per_word; ++j) word |= static_cast<uint32_t>(lds_codes[t][c0 + j]) << (j * bits);
-    dst[w] = word;
+  for (int j = 0; j < 4; ++j) {
+    mnp[j] = pk_min_h2(pk_min_h2(w[0][j], w[1][j]), pk_min_h2(w[2][j], w[3][j]));
+    mxp[j] = pk_max_h2(pk_max_h2(w[0][j], w[1][j]), pk_max_h2(w[2][j], w[3][j]));
+    if constexpr (D == 64) {   // token quads tq and tq ^ 1 share a 16-lane row
+      mnp[j] = pk_min_h2(mnp[j], dpp_u32<kDppRowRor8>(mnp[j]));
+      mxp[j] = pk_max_h2(mxp[j], dpp_u32<kDppRowRor8>(mxp[j]));
+    }
+    mnp[j] = pk_swap_rows<false>(pk_swap_rows<false>(mnp[j], true), false);
+    mxp[j] = pk_swap_rows<true>(pk_swap_rows<true>(mxp[j], true), false);
   }
-}
-
-// Values: one workgroup per (32-token block, KV head, batch); thread
-// (token t, 32-channel group g) reduces its group's min/max in registers and
-// stages its codes in LDS; the block is then written channel-major (for each
-// channel, the 32 tokens' codes in token order), the layout in which the
-// decode kernel's matrix-core operands read 8 consecutive tokens of one
-// channel.
-// Source rows and destination tiles as quantize_k_kernel.
-template <int D>
-__global__ __launch_bounds__(D) void quantize_v_kernel(
-    const uint16_t* __restrict__ v, int src_T, int Hkv, int bits,
-    uint32_t* __restrict__ codes, uint16_t* __restrict__ scale,
-    uint16_t* __restrict__ zero, int dst_tiles, int tile0) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds_codes[D][kGroup];   // [channel][token]
-  const int tid = threadIdx.x;
-  const int t = tid % kGroup, g = tid / kGroup;
-  const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const size_t unit = static_cast<size_t>(b) * Hkv + h;
-  const size_t tok = unit * src_T + static_cast<size_t>(blk) * kGroup + t;          // source row
-  const size_t dtok = (unit * dst_tiles + tile0 + blk) * kGroup + t;                  // destination token
-  const uint4* src = reinterpret_cast<const uint4*>(v + tok * D + g * kGroup);
-  float x[kGroup];
+  if constexpr (D == 128) {   // the other wave's four token quads
+    __shared__ __attribute__((aligned(16))) uint32_t lds_red[2][NCO][8];
+    const int wave = tid / kWave;
+    if ((tid % kWave) < NCO) {
+      *reinterpret_cast<uint4*>(&lds_red[wave][co][0]) = uint4{mnp[0], mnp[1], mnp[2], mnp[3]};
+      *reinterpret_cast<uint4*>(&lds_red[wave][co][4]) = uint4{mxp[0], mxp[1], mxp[2], mxp[3]};
+    }
+    __syncthreads();
+    const uint4 omn = *reinterpret_cast<const uint4*>(&lds_red[1 - wave][co][0]);
+    const uint4 omx = *reinterpret_cast<const uint4*>(&lds_red[1 - wave][co][4]);
+    mnp[0] = pk_min_h2(mnp[0], omn.x);
+    mnp[1] = pk_min_h2(mnp[1], omn.y);
+    mnp[2] = pk_min_h2(mnp[2], omn.z);
+    mnp[3] = pk_min_h2(mnp[3], omn.w);
+    mxp[0] = pk_max_h2(mxp[0], omx.x);
+    mxp[1] = pk_max_h2(mxp[1], omx.y);
+    mxp[2] = pk_max_h2(mxp[2], omx.z);
+    mxp[3] = pk_max_h2(mxp[3], omx.w);
+  }
+  float x[4][8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint4 u = src[i];
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+  for (int r = 0; r < 4; ++r)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      x[i * 8 + 2 * j] = h2f(static_cast<uint16_t>(w[j] & 0xFFFFu));
-      x[i * 8 + 2 * j + 1] = h2f(static_cast<uint16_t>(w[j] >> 16));
+      x[r][2 * j] = h2f(static_cast<uint16_t>(w[r][j] & 0xFFFFu));
+      x[r][2 * j + 1] = h2f(static_cast<uint16_t>(w[r][j] >> 16));
+    }
+  // per token: the octet's codes, accumulated as exact integers in fp32
+  // (code e times 2^(BITS e); two halves of 4 codes each above 2 bits) or,
+  // at 8 bits, converted into the bytes of two words
+  float acc[4][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}, {0.0f, 0.0f}, {0.0f, 0.0f}};
+  uint32_t w8[4][2] = {{0u, 0u}, {0u, 0u}, {0u, 0u}, {0u, 0u}};
+  // thread (tq, co) derives the parameters of channel 8 co + tq, stores its
+  // scale and zero, and shares (zero, reciprocal, scale) through LDS
+  {
+    uint32_t mnw = mnp[0], mxw = mxp[0];
+#pragma unroll
+    for (int j = 1; j < 4; ++j) {
+      mnw = (tq >> 1) == j ? mnp[j] : mnw;
+      mxw = (tq >> 1) == j ? mxp[j] : mxw;
+    }
+    const int sh = (tq & 1) * 16;
+    const GroupParams p = group_params(h2f(static_cast<uint16_t>(mnw >> sh)), h2f(static_cast<uint16_t>(mxw >> sh)), BITS);
+    scale[dtile * D + 8 * co + tq] = p.s16;
+    zero[dtile * D + 8 * co + tq] = p.z16;
+    lds_par[0][co][tq] = p.zf;
+    lds_par[1][co][tq] = p.rcp;
+    lds_par[2][co][tq] = p.sf;
+  }
+  __syncthreads();
+  float pz[8], pr[8];
+  *reinterpret_cast<float4*>(&pz[0]) = *reinterpret_cast<const float4*>(&lds_par[0][co][0]);
+  *reinterpret_cast<float4*>(&pz[4]) = *reinterpret_cast<const float4*>(&lds_par[0][co][4]);
+  *reinterpret_cast<float4*>(&pr[0]) = *reinterpret_cast<const float4*>(&lds_par[1][co][0]);
+  *reinterpret_cast<float4*>(&pr[4]) = *reinterpret_cast<const float4*>(&lds_par[1][co][4]);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float c = quant_code_f<BITS>(x[r][e], pz[e], pr[e], &lds_par[2][co][e]);
+      if constexpr (BITS == 2) acc[r][0] = fmaf(c, static_cast<float>(1u << (2 * e)), acc[r][0]);
+      else if constexpr (BITS == 4) acc[r][e >> 2] = fmaf(c, static_cast<float>(1u << (4 * (e & 3))), acc[r][e >> 2]);
+      else w8[r][e >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(c, e & 3, w8[r][e >> 2]);
     }
   }
-  float mn = x[0], mx = x[0];
+  // The tile's codes (32 token rows of D * BITS / 8 bytes, this octet's at
+  // byte co * BITS of a row) are assembled in LDS, then copied out with
+  // 4 * BITS contiguous bytes per thread.
+  constexpr int RB = D * BITS / 8;
+  __shared__ __attribute__((aligned(16))) uint32_t lds_tile[kGroup * RB / 4];
+  uint8_t* lds = reinterpret_cast<uint8_t*>(lds_tile) + co * BITS;
 #pragma unroll
-  for (int i = 1; i < kGroup; ++i) {
-    mn = fminf(mn, x[i]);
-    mx = fmaxf(mx, x[i]);
+  for (int r = 0; r < 4; ++r) {
+    uint8_t* row = lds + (4 * tq + r) * RB;
+    if constexpr (BITS == 8) {
+      *reinterpret_cast<uint2*>(row) = uint2{w8[r][0], w8[r][1]};
+    } else if constexpr (BITS == 4) {
+      *reinterpret_cast<uint32_t*>(row) =
+          static_cast<uint32_t>(acc[r][0]) | (static_cast<uint32_t>(acc[r][1]) << 16);
+    } else {
+      *reinterpret_cast<uint16_t*>(row) = static_cast<uint16_t>(static_cast<uint32_t>(acc[r][0]));
+    }
   }
-  const GroupParams p = group_params(mn, mx, bits);
-  scale[dtok * (D / kGroup) + g] = p.s16;
-  zero[dtok * (D / kGroup) + g] = p.z16;
-#pragma unroll
-  for (int i = 0; i < kGroup; ++i) lds_codes[g * kGroup + i][t] = static_cast<uint8_t>(quant_code(x[i], p));
   __syncthreads();
-  // channel-major block: stream index c*32 + t, `per_word` codes per word
-  const int per_word = 32 / bits;
-  uint32_t* dst = codes + (unit * dst_tiles + tile0 + blk) * static_cast<size_t>(D * bits);
-  for (int w = tid; w < D * bits; w += D) {
-    const int f0 = w * per_word;
-    const int c = f0 / kGroup, t0 = f0 % kGroup;
-    uint32_t word = 0;
-    for (int j = 0; j < per_word; ++j) word |= static_cast<uint32_t>(lds_codes[c][t0 + j]) << (j * bits);
-    dst[w] = word;
+  uint32_t* dst = codes + dtile * (kGroup * RB / 4) + tid * BITS;   // 4 * BITS bytes per thread
+  const uint32_t* from = lds_tile + tid * BITS;
+  if constexpr (BITS == 2) {
+    *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(from);
+  } else {
+#pragma unroll
+    for (int i = 0; i < BITS / 4; ++i) reinterpret_cast<uint4*>(dst)[i] = reinterpret_cast<const uint4*>(from)[i];
   }
 }
+
+// Values: one workgroup per (32-token block, KV head, batch), D threads;
+// thread tid = (D/8) tq + co holds tokens 4 tq .. 4 tq + 3 of channels
+// 8 co .. 8 co + 7, so the 4 threads of a (token, 32-channel) group are
+// adjacent lanes and combine their partial min/max with DPP.  The block is
+// written channel-major (for each channel, the 32 tokens' codes in token
+// order, the layout in which the decode kernel's matrix-core operands read
+// 8 consecutive tokens of one channel): each thread puts the 4 tokens'
+// codes of each of its channels (4 * BITS bits) into LDS, then thread c
+// copies channel c's 4 * BITS bytes out.
+// Source rows and destination tiles as quantize_k_kernel.
+template <int D, int BITS>
+__global__ __launch_bounds__(D) void quantize_v_kernel(
+    const uint16_t* __restrict__ v, int src_T, int Hkv,
+    uint32_t* __restrict__ codes, uint16_t* __restrict__ scale,
+    uint16_t* __restrict__ zero, int dst_tiles, int tile0) {
+  constexpr int NCO = D / 8;             // channel octets per token
+  constexpr int CB = 4 * BITS;           // bytes of one channel in a block
+  // LDS byte offset of channel c: 4 bytes of padding per 8 channels put the
+  // channels that one store instruction touches in different banks
+  __shared__ __attribute__((aligned(16))) uint32_t lds_codes[(D * CB + (D / 8) * 4) / 4];
+  const int tid = threadIdx.x, tq = tid / NCO, co = tid % NCO;
+  const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const size_t unit = static_cast<size_t>(b) * Hkv + h;
+  const uint16_t* src = v + (unit * src_T + static_cast<size_t>(blk) * kGroup) * D;
+  const size_t dtok0 = (unit * dst_tiles + tile0 + blk) * kGroup;   // destination token of row 0
+
+  float x[4][8];
+  load_quad_octet<D>(src, tq, co, x);
+  // per channel: the 4 tokens' codes (token r at bit BITS r), accumulated
+  // as exact integers in fp32 or, at 8 bits, converted into bytes
+  float accv[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+  uint32_t w8[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+  // min/max of each of the 4 tokens over the group's 4 adjacent lanes; lane
+  // co % 4 == r then derives token r's parameters, stores its scale and
+  // zero, and the quad shares (zero, reciprocal, scale) by DPP broadcasts
+  float mnr = 0.0f, mxr = 0.0f;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    float mn = x[r][0], mx = x[r][0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) {
+      mn = fminf(mn, x[r][e]);
+      mx = fmaxf(mx, x[r][e]);
+    }
+    mn = -max_adjacent<4>(-mn);
+    mx = max_adjacent<4>(mx);
+    mnr = (co & 3) == r ? mn : mnr;
+    mxr = (co & 3) == r ? mx : mxr;
+  }
+  const GroupParams pm = group_params(mnr, mxr, BITS);
+  scale[(dtok0 + 4 * tq + (co & 3)) * (D / kGroup) + co / 4] = pm.s16;
+  zero[(dtok0 + 4 * tq + (co & 3)) * (D / kGroup) + co / 4] = pm.z16;
+  float pz[4], pr[4], ps[4];
+  pz[0] = dpp<0x00>(pm.zf);
+  pz[1] = dpp<0x55>(pm.zf);
+  pz[2] = dpp<0xAA>(pm.zf);
+  pz[3] = dpp<0xFF>(pm.zf);
+  pr[0] = dpp<0x00>(pm.rcp);
+  pr[1] = dpp<0x55>(pm.rcp);
+  pr[2] = dpp<0xAA>(pm.rcp);
+  pr[3] = dpp<0xFF>(pm.rcp);
+  ps[0] = dpp<0x00>(pm.sf);
+  ps[1] = dpp<0x55>(pm.sf);
+  ps[2] = dpp<0xAA>(pm.sf);
+  ps[3] = dpp<0xFF>(pm.sf);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float c = quant_code_f<BITS>(x[r][e], pz[r], pr[r], &ps[r]);
+      if constexpr (BITS == 8) w8[e] = __builtin_amdgcn_cvt_pk_u8_f32(c, r, w8[e]);
+      else accv[e] = fmaf(c, static_cast<float>(1u << (BITS * r)), accv[e]);
+    }
+  }
+  uint8_t* lds = reinterpret_cast<uint8_t*>(lds_codes);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int c = 8 * co + e;
+    uint8_t* at = lds + c * CB + (c >> 3) * 4 + tq * (BITS / 2);
+    if constexpr (BITS == 2) *at = static_cast<uint8_t>(static_cast<uint32_t>(accv[e]));
+    else if constexpr (BITS == 4) *reinterpret_cast<uint16_t*>(at) = static_cast<uint16_t>(static_cast<uint32_t>(accv[e]));
+    else *reinterpret_cast<uint32_t*>(at) = w8[e];
+  }
+  __syncthreads();
+  // thread c: channel c's CB bytes (4-byte aligned in LDS) to the block
+  const int c = tid;
+  const uint32_t* from = lds_codes + (c * CB + (c >> 3) * 4) / 4;
+  uint32_t* to = codes + (unit * dst_tiles + tile0 + blk) * static_cast<size_t>(D * BITS) + c * (CB / 4);
+  if constexpr (BITS == 2) {
+    *reinterpret_cast<uint2*>(to) = uint2{from[0], from[1]};
+  } else {
+#pragma unroll
+    for (int i = 0; i < CB / 16; ++i)
+      reinterpret_cast<uint4*>(to)[i] = uint4{from[4 * i], from[4 * i + 1], from[4 * i + 2], from[4 * i + 3]};
+  }
+}
+
+// Launch the K or V quantizer for head dim d and width bits over grid
+// (tiles, Hkv, B).
+template <bool KEYS>
+void launch_quantize(int d, int bits, dim3 grid, hipStream_t s, const uint16_t* x, int src_T, int Hkv,
+                     uint32_t* codes, uint16_t* scale, uint16_t* zero, int dst_tiles, int tile0) {
+#define DQA_QLAUNCH(D, BITS)                                                                             \
+  hipLaunchKernelGGL((KEYS ? quantize_k_kernel<D, BITS> : quantize_v_kernel<D, BITS>), grid, dim3(D), 0, s, \
+                     x, src_T, Hkv, codes, scale, zero, dst_tiles, tile0)
+  if (d == 128) {
+    if (bits == 2) DQA_QLAUNCH(128, 2);
+    else if (bits == 4) DQA_QLAUNCH(128, 4);
+    else DQA_QLAUNCH(128, 8);
+  } else {
+    if (bits == 2) DQA_QLAUNCH(64, 2);
+    else if (bits == 4) DQA_QLAUNCH(64, 4);
+    else DQA_QLAUNCH(64, 8);
+  }
+#undef DQA_QLAUNCH
+}
+
+
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int check_common(const void* in, int B, int Hkv, int T, int d, int bits,
                  const void* codes, const void* scale, const void* zero) {
@@ -167,14 +407,10 @@ extern "C" int quantize_pack_k(const uint16_t* k, int B, int Hkv, int T, int d,
   if (T % kGroup != 0) return DQA_ERR_SHAPE;
   if (static_cast<long long>(B) * Hkv * T == 0) return DQA_OK;
   if (B > 65535 || Hkv > 65535) return DQA_ERR_SHAPE;
+  if (!aligned16(k) || !aligned16(codes)) return DQA_ERR_ALIGN;
   dim3 grid(T / kGroup, Hkv, B);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (d == 128)
-    hipLaunchKernelGGL(quantize_k_kernel<128>, grid, dim3(128), 0, s, k, T, Hkv, bits, codes, scale, zero,
-                       T / kGroup, 0);
-  else
-    hipLaunchKernelGGL(quantize_k_kernel<64>, grid, dim3(64), 0, s, k, T, Hkv, bits, codes, scale, zero,
-                       T / kGroup, 0);
+  launch_quantize<true>(d, bits, grid, s, k, T, Hkv, codes, scale, zero, T / kGroup, 0);
   DQA_CHECK_LAUNCH();
   return DQA_OK;
 }
@@ -187,14 +423,10 @@ extern "C" int quantize_pack_v(const uint16_t* v, int B, int Hkv, int T, int d,
   if (T % kGroup != 0) return DQA_ERR_SHAPE;
   if (static_cast<long long>(B) * Hkv * T == 0) return DQA_OK;
   if (B > 65535 || Hkv > 65535) return DQA_ERR_SHAPE;
+  if (!aligned16(v) || !aligned16(codes)) return DQA_ERR_ALIGN;
   dim3 grid(T / kGroup, Hkv, B);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (d == 128)
-    hipLaunchKernelGGL(quantize_v_kernel<128>, grid, dim3(128), 0, s, v, T, Hkv, bits, codes, scale, zero,
-                       T / kGroup, 0);
-  else
-    hipLaunchKernelGGL(quantize_v_kernel<64>, grid, dim3(64), 0, s, v, T, Hkv, bits, codes, scale, zero,
-                       T / kGroup, 0);
+  launch_quantize<false>(d, bits, grid, s, v, T, Hkv, codes, scale, zero, T / kGroup, 0);
   DQA_CHECK_LAUNCH();
   return DQA_OK;
 }
@@ -248,8 +480,6 @@ __global__ __launch_bounds__(256) void unstage_rows_kernel(const uint16_t* __res
         reinterpret_cast<const uint4*>(src + (u * rows + skip + r) * d)[ch];
   }
 }
-
-bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Flushes (groups of 32 quantized) when `rows` tokens sit in the recent zone
 // bounded by R_max: while more than R_max and at least 32 remain.
@@ -347,17 +577,8 @@ extern "C" int kivi_append(dqa_kivi_cache* c, const uint16_t* k_new, const uint1
     uint16_t* vz = const_cast<uint16_t*>(c->v_zero);
     const dim3 grid(f, c->Hkv, c->B);
     const int dst_tiles = T_cap / kGroup, tile0 = c->T_q / kGroup;
-    if (d == 128) {
-      hipLaunchKernelGGL(quantize_k_kernel<128>, grid, dim3(128), 0, s, wk, rows, c->Hkv, c->bits, kc, ks, kz,
-                         dst_tiles, tile0);
-      hipLaunchKernelGGL(quantize_v_kernel<128>, grid, dim3(128), 0, s, wv, rows, c->Hkv, c->bits, vc, vs, vz,
-                         dst_tiles, tile0);
-    } else {
-      hipLaunchKernelGGL(quantize_k_kernel<64>, grid, dim3(64), 0, s, wk, rows, c->Hkv, c->bits, kc, ks, kz,
-                         dst_tiles, tile0);
-      hipLaunchKernelGGL(quantize_v_kernel<64>, grid, dim3(64), 0, s, wv, rows, c->Hkv, c->bits, vc, vs, vz,
-                         dst_tiles, tile0);
-    }
+    launch_quantize<true>(d, c->bits, grid, s, wk, rows, c->Hkv, kc, ks, kz, dst_tiles, tile0);
+    launch_quantize<false>(d, c->bits, grid, s, wv, rows, c->Hkv, vc, vs, vz, dst_tiles, tile0);
     DQA_CHECK_LAUNCH();
   }
   if (R_new > 0) {

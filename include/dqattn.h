@@ -86,7 +86,9 @@ int dqa_abi_version(void);  /* 6: zoned_plan takes a sink length and the
  *   T      multiple of 32, >= 0;  d in {64, 128};  bits in {2, 4, 8}
  *   codes  (device) uint32 [B*Hkv*T*d*bits/32]
  *   scale, zero (device) fp16 [B][Hkv][T/32][d]
- * Errors: DQA_ERR_NULL, DQA_ERR_SHAPE, DQA_ERR_BITS, DQA_ERR_HIP. */
+ * k and codes must be 16-byte aligned (DQA_ERR_ALIGN otherwise).
+ * Errors: DQA_ERR_NULL, DQA_ERR_SHAPE, DQA_ERR_BITS, DQA_ERR_ALIGN,
+ * DQA_ERR_HIP. */
 int quantize_pack_k(const uint16_t* k, int B, int Hkv, int T, int d, int bits,
                     uint32_t* codes, uint16_t* scale, uint16_t* zero,
                     void* stream);
@@ -95,7 +97,7 @@ int quantize_pack_k(const uint16_t* k, int B, int Hkv, int T, int d, int bits,
  *   v      (device) fp16 [B][Hkv][T][d]; T multiple of 32, >= 0; d in {64, 128}
  *   codes  (device) uint32 [B*Hkv*T*d*bits/32]
  *   scale, zero (device) fp16 [B][Hkv][T][d/32]
- * Errors as quantize_pack_k. */
+ * v and codes must be 16-byte aligned.  Errors as quantize_pack_k. */
 int quantize_pack_v(const uint16_t* v, int B, int Hkv, int T, int d, int bits,
                     uint32_t* codes, uint16_t* scale, uint16_t* zero,
                     void* stream);

@@ -59,6 +59,9 @@ def test_quantize_validation(fn):
     assert f(FAKE, 1, 1, 32, 128, 2, FAKE, None, FAKE, None) == 1
     assert f(FAKE, -1, 1, 32, 128, 2, FAKE, FAKE, FAKE, None) == 2
     assert f(None, 0, 4, 32, 128, 2, None, None, None, None) == 0         # empty: no work
+    odd2, odd4 = ctypes.c_void_p(0x1002), ctypes.c_void_p(0x1004)
+    assert f(odd2, 1, 1, 32, 128, 2, FAKE, FAKE, FAKE, None) == 8         # 16-byte alignment
+    assert f(FAKE, 1, 1, 32, 128, 2, odd4, FAKE, FAKE, None) == 8
     if fn == "quantize_pack_k":
         assert f(FAKE, 1, 1, 33, 128, 2, FAKE, FAKE, FAKE, None) == 2     # T % 32
 

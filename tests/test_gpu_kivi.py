@@ -61,6 +61,49 @@ def test_quantize_pack_bit_exact(dqa, shape):
     np.testing.assert_array_equal(host(gv[2]).view(np.uint16), vz.view(np.uint16))
 
 
+def _tie_group(rng, bits):
+    """32 fp16 values whose quotients (x - min) / scale sit exactly on
+    half-integers (ties, rounded half to even) or one fp16 step away from
+    them, with min 0 and max 2^bits - 1 so that the scale is exactly 1."""
+    L = (1 << bits) - 1
+    k = rng.integers(0, L, size=30)
+    step = np.float16(np.spacing(np.float16(L)))          # fp16 step at the top of the range
+    off = rng.choice(np.array([0.0, -1.0, 1.0]), size=30) * np.maximum(step, 2.0 ** -10)
+    vals = np.concatenate([[0.0, float(L)], k + 0.5 + off]).astype(np.float16)
+    return vals[rng.permutation(32)]
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("d", [64, 128])
+def test_quantize_rounding_ties(dqa, bits, d):
+    """Quotients on and next to the rounding boundaries: the codes must be
+    those of the IEEE division rounded half to even (the kernels take a
+    reciprocal product and fall back to the division near a boundary)."""
+    rng = np.random.default_rng(1000 * bits + d)
+    T = 64
+    k = np.empty((2, 1, T, d), np.float16)
+    for b in range(2):
+        for t0 in range(0, T, 32):
+            for c in range(d):
+                k[b, 0, t0:t0 + 32, c] = _tie_group(rng, bits)
+    v = np.empty((2, 1, T, d), np.float16)
+    for b in range(2):
+        for t in range(T):
+            for g in range(d // 32):
+                v[b, 0, t, 32 * g:32 * g + 32] = _tie_group(rng, bits)
+    say("quantize ties", bits, d)
+    gk = dqa.quantize_pack_k(dev(k), bits)
+    gv = dqa.quantize_pack_v(dev(v), bits)
+    torch.cuda.synchronize()
+    kc, ks, kz = oracle.quantize_k(k, bits)
+    vc, vs, vz = oracle.quantize_v(v, bits)
+    assert np.all(ks.astype(np.float32) == 1.0) and np.all(vs.astype(np.float32) == 1.0)
+    np.testing.assert_array_equal(host(gk[0]).view(np.uint32), oracle.pack_codes(kc, bits))
+    np.testing.assert_array_equal(host(gv[0]).view(np.uint32), oracle.pack_v_codes(vc, bits).reshape(host(gv[0]).shape))
+    np.testing.assert_array_equal(host(gk[1]).view(np.uint16), ks.view(np.uint16))
+    np.testing.assert_array_equal(host(gv[2]).view(np.uint16), vz.view(np.uint16))
+
+
 @pytest.mark.parametrize("name", ["c2", "c3"])
 def test_quantize_full_config_sampled_units(dqa, name):
     """Full-size quantization on the GPU; the oracle re-quantizes sampled
