@@ -36,23 +36,6 @@ __device__ __forceinline__ GroupParams group_params(float mn, float mx, int bits
   return p;
 }
 
-// code = clamp(rint((x - z) / s), 0, 2^b - 1) with the IEEE quotient.  The
-// quotient is first approximated as t * rcp(s): rcp is within 1 ulp of 1/s,
-// so t * rcp(s) and the IEEE quotient t / s differ by less than 2^-21 of
-// their size, and both lie in [0, 2^b) * (1 + 2^-10) -- less than 2^-13 for
-// every width up to 8 bits.  Unless the approximation lies within 2^-12 of
-// a half-integer, both round to the same integer (and neither is a tie);
-// otherwise the IEEE division decides.  The result is the IEEE-division
-// code in every case.
-__device__ __forceinline__ float quant_code_f(float x, const GroupParams& p) {
-  const float t = x - p.zf;
-  const float y = t * p.rcp;
-  float q = rintf(y);
-  // |y - rint(y)| >= 0.5 - 2^-12: y within 2^-12 of a half-integer
-  if (__builtin_expect(__builtin_fabsf(y - q) >= 0.499755859375f, 0)) q = rintf(t / p.sf);
-  return __builtin_amdgcn_fmed3f(q, 0.0f, p.levels);
-}
-
 // Packed fp16 minimum / maximum of two pairs (exact; the inputs are finite
 // fp16 values, so the plain instructions are used without the canonicalizing
 // moves the compiler would add for signalling NaNs), and a DPP lane exchange
@@ -90,31 +73,68 @@ __device__ __forceinline__ uint32_t pk_swap_rows(uint32_t x, bool rows32) {
   return MAX ? pk_max_h2(r0, r1) : pk_min_h2(r0, r1);
 }
 
-// The same code from the group's zero, reciprocal and (only on the exact
-// path) scale, read from `sf`.
-template <int BITS>
-__device__ __forceinline__ float quant_code_f(float x, float zf, float rcp, const float* sf) {
-  const float t = x - zf;
+// x - z for the fp16 value in half H of word w: one mixed-precision FMA
+// (x * 1 - z, a single rounding), which equals the fp32 subtraction of the
+// widened value.
+template <int H>
+__device__ __forceinline__ float minus_zero(uint32_t w, float zf) {
+  float r;
+  if constexpr (H == 0)
+    asm("v_fma_mix_f32 %0, %1, 1.0, -%2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(w), "v"(zf));
+  else
+    asm("v_fma_mix_f32 %0, %1, 1.0, -%2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(w), "v"(zf));
+  return r;
+}
+
+// code = clamp(rint((x - z) / s), 0, 2^b - 1) with the IEEE quotient, for
+// the fp16 value x in half H of word w, from its group's zero, reciprocal
+// and (only on the exact path) scale, read from `sf`.  The quotient is first
+// approximated as t * rcp(s): rcp is within 1 ulp of 1/s, so t * rcp(s) and
+// the IEEE quotient t / s differ by at most 2^-22 of t / s, and t / s < 2^9
+// (t <= max - min, and s is (max - min) / (2^b - 1) rounded to fp16, at
+// worst halved by subnormal rounding) -- less than 2^-13.  Unless the
+// approximation lies within 2^-12 of a half-integer, both round to the same
+// integer (and neither is a tie); otherwise the IEEE division decides.  The
+// result is the IEEE-division code in every case.
+template <int BITS, int H>
+__device__ __forceinline__ float quant_code_w(uint32_t w, float zf, float rcp, const float* sf) {
+  const float t = minus_zero<H>(w, zf);
   const float y = t * rcp;
   float q = rintf(y);
+  // |y - rint(y)| >= 0.5 - 2^-12: y within 2^-12 of a half-integer
   if (__builtin_expect(__builtin_fabsf(y - q) >= 0.499755859375f, 0)) q = rintf(t / *sf);
   return __builtin_amdgcn_fmed3f(q, 0.0f, static_cast<float>((1 << BITS) - 1));
+}
+template <int BITS>
+__device__ __forceinline__ float quant_code_e(uint32_t w, int e, float zf, float rcp, const float* sf) {
+  return (e & 1) ? quant_code_w<BITS, 1>(w, zf, rcp, sf) : quant_code_w<BITS, 0>(w, zf, rcp, sf);
+}
+
+// Both halves of the result hold min (or max) of the two halves of w.
+__device__ __forceinline__ uint32_t pk_min_halves(uint32_t w) {
+  uint32_t r;
+  asm("v_pk_min_f16 %0, %1, %1 op_sel:[1,0] op_sel_hi:[0,1]" : "=v"(r) : "v"(w));
+  return r;
+}
+__device__ __forceinline__ uint32_t pk_max_halves(uint32_t w) {
+  uint32_t r;
+  asm("v_pk_max_f16 %0, %1, %1 op_sel:[1,0] op_sel_hi:[0,1]" : "=v"(r) : "v"(w));
+  return r;
 }
 
 // Tile of 32 tokens x D channels, thread (token quad tq, channel octet co):
 // tokens 4 tq .. 4 tq + 3, channels 8 co .. 8 co + 7, read as four 16-byte
-// loads.  x[r][e] = token 4 tq + r, channel 8 co + e.
+// loads.  w[r][j] = token 4 tq + r, channels 8 co + 2 j (low half) and
+// 8 co + 2 j + 1 (high half).
 template <int D>
-__device__ __forceinline__ void load_quad_octet(const uint16_t* rows, int tq, int co, float (*x)[8]) {
+__device__ __forceinline__ void load_quad_octet(const uint16_t* rows, int tq, int co, uint32_t (*w)[4]) {
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const uint4 u = *reinterpret_cast<const uint4*>(rows + static_cast<size_t>(4 * tq + r) * D + 8 * co);
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      x[r][2 * j] = h2f(static_cast<uint16_t>(w[j] & 0xFFFFu));
-      x[r][2 * j + 1] = h2f(static_cast<uint16_t>(w[j] >> 16));
-    }
+    w[r][0] = u.x;
+    w[r][1] = u.y;
+    w[r][2] = u.z;
+    w[r][3] = u.w;
   }
 }
 
@@ -148,14 +168,7 @@ __global__ __launch_bounds__(D) void quantize_k_kernel(
   // min/max per channel pair in packed fp16 (exact: the inputs are fp16),
   // over the thread's 4 tokens and then over the channel's 8 adjacent lanes
   uint32_t w[4][4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const uint4 u = *reinterpret_cast<const uint4*>(src + static_cast<size_t>(4 * tq + r) * D + 8 * co);
-    w[r][0] = u.x;
-    w[r][1] = u.y;
-    w[r][2] = u.z;
-    w[r][3] = u.w;
-  }
+  load_quad_octet<D>(src, tq, co, w);
   uint32_t mnp[4], mxp[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -187,14 +200,6 @@ __global__ __launch_bounds__(D) void quantize_k_kernel(
     mxp[2] = pk_max_h2(mxp[2], omx.z);
     mxp[3] = pk_max_h2(mxp[3], omx.w);
   }
-  float x[4][8];
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      x[r][2 * j] = h2f(static_cast<uint16_t>(w[r][j] & 0xFFFFu));
-      x[r][2 * j + 1] = h2f(static_cast<uint16_t>(w[r][j] >> 16));
-    }
   // per token: the octet's codes, accumulated as exact integers in fp32
   // (code e times 2^(BITS e); two halves of 4 codes each above 2 bits) or,
   // at 8 bits, converted into the bytes of two words
@@ -227,7 +232,7 @@ __global__ __launch_bounds__(D) void quantize_k_kernel(
   for (int e = 0; e < 8; ++e) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float c = quant_code_f<BITS>(x[r][e], pz[e], pr[e], &lds_par[2][co][e]);
+      const float c = quant_code_e<BITS>(w[r][e >> 1], e, pz[e], pr[e], &lds_par[2][co][e]);
       if constexpr (BITS == 2) acc[r][0] = fmaf(c, static_cast<float>(1u << (2 * e)), acc[r][0]);
       else if constexpr (BITS == 4) acc[r][e >> 2] = fmaf(c, static_cast<float>(1u << (4 * (e & 3))), acc[r][e >> 2]);
       else w8[r][e >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(c, e & 3, w8[r][e >> 2]);
@@ -288,8 +293,8 @@ __global__ __launch_bounds__(D) void quantize_v_kernel(
   const uint16_t* src = v + (unit * src_T + static_cast<size_t>(blk) * kGroup) * D;
   const size_t dtok0 = (unit * dst_tiles + tile0 + blk) * kGroup;   // destination token of row 0
 
-  float x[4][8];
-  load_quad_octet<D>(src, tq, co, x);
+  uint32_t w[4][4];
+  load_quad_octet<D>(src, tq, co, w);
   // per channel: the 4 tokens' codes (token r at bit BITS r), accumulated
   // as exact integers in fp32 or, at 8 bits, converted into bytes
   float accv[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
@@ -300,16 +305,14 @@ __global__ __launch_bounds__(D) void quantize_v_kernel(
   float mnr = 0.0f, mxr = 0.0f;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    float mn = x[r][0], mx = x[r][0];
-#pragma unroll
-    for (int e = 1; e < 8; ++e) {
-      mn = fminf(mn, x[r][e]);
-      mx = fmaxf(mx, x[r][e]);
-    }
-    mn = -max_adjacent<4>(-mn);
-    mx = max_adjacent<4>(mx);
-    mnr = (co & 3) == r ? mn : mnr;
-    mxr = (co & 3) == r ? mx : mxr;
+    uint32_t mnw = pk_min_halves(pk_min_h2(pk_min_h2(w[r][0], w[r][1]), pk_min_h2(w[r][2], w[r][3])));
+    uint32_t mxw = pk_max_halves(pk_max_h2(pk_max_h2(w[r][0], w[r][1]), pk_max_h2(w[r][2], w[r][3])));
+    mnw = pk_min_h2(mnw, dpp_u32<kDppQuadXor1>(mnw));
+    mxw = pk_max_h2(mxw, dpp_u32<kDppQuadXor1>(mxw));
+    mnw = pk_min_h2(mnw, dpp_u32<kDppQuadXor2>(mnw));
+    mxw = pk_max_h2(mxw, dpp_u32<kDppQuadXor2>(mxw));
+    mnr = (co & 3) == r ? h2f(static_cast<uint16_t>(mnw)) : mnr;
+    mxr = (co & 3) == r ? h2f(static_cast<uint16_t>(mxw)) : mxr;
   }
   const GroupParams pm = group_params(mnr, mxr, BITS);
   scale[(dtok0 + 4 * tq + (co & 3)) * (D / kGroup) + co / 4] = pm.s16;
@@ -331,7 +334,7 @@ __global__ __launch_bounds__(D) void quantize_v_kernel(
   for (int r = 0; r < 4; ++r) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float c = quant_code_f<BITS>(x[r][e], pz[r], pr[r], &ps[r]);
+      const float c = quant_code_e<BITS>(w[r][e >> 1], e, pz[r], pr[r], &ps[r]);
       if constexpr (BITS == 8) w8[e] = __builtin_amdgcn_cvt_pk_u8_f32(c, r, w8[e]);
       else accv[e] = fmaf(c, static_cast<float>(1u << (BITS * r)), accv[e]);
     }
