@@ -38,16 +38,21 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E, published
+# Vector-ALU issue peak: 256 CUs x 4 SIMDs, one wave64 VALU instruction per
+# SIMD every 4 cycles (16 lanes per cycle) at the 2.4 GHz peak clock.
+VALU_PEAK_GINST = 256 * 4 * 2.4 / 4
 KERNEL_SOURCES = [os.path.join(ROOT, "dequant_decode_attention_amd", "csrc", f)
                   for f in ("decode_kivi.hip", "merge.h", "common.h")]
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "kivi_decode_kernel_llama8b_gqa_32k_traffic.md")
 
 
-def measured_traffic(bits):
+def measured_traffic(bits, key_fmt="traffic_bytes_per_launch_{bits}bit"):
     """HBM bytes per launch of the split kernel from the committed
     rocprofv3 counter summary (FETCH_SIZE + WRITE_SIZE, scaled by the
     copy-kernel calibration), or None when the summary is missing, covers
-    another bit width, or was taken on a different kernel source."""
+    another bit width, or was taken on a different kernel source.  With
+    key_fmt "valu_instructions_per_launch_{bits}bit": the kernel's VALU wave
+    instructions per launch (SQ_INSTS_VALU) under the same conditions."""
     import hashlib
     try:
         text = open(TRAFFIC_SUMMARY).read()
@@ -61,7 +66,7 @@ def measured_traffic(bits):
     src = hashlib.sha256(b"".join(open(f, "rb").read() for f in KERNEL_SOURCES)).hexdigest()
     if fields.get("kernel_source_sha256") != src:
         return None
-    key = f"traffic_bytes_per_launch_{bits}bit"
+    key = key_fmt.format(bits=bits)
     return int(fields[key]) if key in fields else None
 
 
@@ -425,6 +430,13 @@ def main():
                      "algorithmic_bytes": nbytes, "kernel": "kivi_decode_kernel",
                      "kernel_ms": kernel_ms},
     }
+    # the vector-ALU issue rate the same kernel sustains (its instruction
+    # count per launch from the committed counter summary)
+    valu = measured_traffic(bits, "valu_instructions_per_launch_{bits}bit")
+    if valu is not None:
+        rate = valu / (kernel_ms * 1e-3) / 1e9
+        line["roofline"]["valu"] = {"instructions": valu, "achieved": rate, "peak": VALU_PEAK_GINST,
+                                    "unit": "G wave-instructions/s", "frac": rate / VALU_PEAK_GINST}
 
     # achievable streaming rate on a buffer of the same size, same run
     src = torch.empty(nbytes // 16 * 16 * 4, dtype=torch.uint8, device=dev)
