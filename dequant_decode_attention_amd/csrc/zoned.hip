@@ -97,11 +97,21 @@ struct PackArgs {
   int T_old, C, d, sink, k_out;
 };
 
-__device__ __forceinline__ uint32_t code_of(float x, float zf, float sf, float levels) {
-  if (sf == 0.0f) return 0u;
-  const float t = (x - zf) / sf;
-  return static_cast<uint32_t>(fminf(fmaxf(rintf(t), 0.0f), levels));
+// code = clamp(rint((x - z) / s), 0, levels) with the IEEE quotient (0 for a
+// zero scale).  rcp = 1/s within 1 ulp (0 when s == 0): t * rcp and t / s
+// differ by at most 2^-22 of t / s < 2^9, i.e. less than 2^-13, so unless
+// t * rcp lies within 2^-12 of a half-integer both round alike; there the
+// IEEE division decides.
+__device__ __forceinline__ uint32_t code_of(float x, float zf, float sf, float rcp, float levels) {
+  const float t = x - zf;
+  const float y = t * rcp;
+  float q = rintf(y);
+  if (__builtin_expect(__builtin_fabsf(y - q) >= 0.499755859375f, 0) && sf != 0.0f) q = rintf(t / sf);
+  return static_cast<uint32_t>(__builtin_amdgcn_fmed3f(q, 0.0f, levels));
 }
+__device__ __forceinline__ float rcp_or_zero(float sf) { return sf == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(sf); }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Zero-fill (the blob's padding bytes are defined as zero).
 __global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t* p, size_t n_words) {
@@ -113,7 +123,7 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t* p, size_t n_wo
 // One workgroup (d threads) per (unit, group); the extra group index
 // `total_groups` copies zone C.
 __global__ __launch_bounds__(128) void zoned_pack_kernel(PackArgs a) {
-  __shared__ uint16_t lds_k[kGroup][128];   // the group's key rows (fp16, original order)
+  __shared__ __attribute__((aligned(16))) uint16_t lds_k[kGroup][128];   // the group's key rows (fp16, original order)
   __shared__ uint8_t lds_c[kGroup][128];    // codes by permuted channel
   __shared__ int lds_tok[kGroup];
   __shared__ uint8_t lds_os[128][kMaxOutliers];   // removed slots per class position (0xFF: none)
@@ -159,9 +169,12 @@ __global__ __launch_bounds__(128) void zoned_pack_kernel(PackArgs a) {
   uint8_t* gb = ub + U[U_SEG_OFF + seg] + static_cast<size_t>(g) * U[U_GRP_B + seg];
   if (tid < kGroup) lds_tok[tid] = tid < n_valid ? tokmap[U[U_TOK_PREFIX + seg] + g * kGroup + tid] : -1;
   __syncthreads();
-  for (int e = tid; e < kGroup * d; e += blockDim.x) {
-    const int s = e / d, c = e % d;
-    lds_k[s][c] = lds_tok[s] >= 0 ? a.k[src_unit + static_cast<size_t>(lds_tok[s]) * d + c] : 0;
+  // 16-byte pieces of the key rows (d / 8 per row)
+  for (int e = tid; e < kGroup * (d / 8); e += blockDim.x) {
+    const int s = e / (d / 8), c8 = e % (d / 8);
+    uint4 u = uint4{0u, 0u, 0u, 0u};
+    if (lds_tok[s] >= 0) u = *reinterpret_cast<const uint4*>(a.k + src_unit + static_cast<size_t>(lds_tok[s]) * d + 8 * c8);
+    *reinterpret_cast<uint4*>(&lds_k[s][8 * c8]) = u;
   }
   __syncthreads();
 
@@ -202,14 +215,14 @@ __global__ __launch_bounds__(128) void zoned_pack_kernel(PackArgs a) {
       }
       const float levels = static_cast<float>((1 << bits) - 1);
       const uint16_t s16 = f2h((mx - mn) / levels);
-      const float sf = h2f(s16);
+      const float sf = h2f(s16), rcp = rcp_or_zero(sf);
       uint16_t* ks = reinterpret_cast<uint16_t*>(gb + U[U_KCODES_B]);
       uint16_t* kz = reinterpret_cast<uint16_t*>(gb + U[U_KCODES_B] + U[U_KSZ_B]);
       ks[pc] = s16;
       kz[pc] = f2h(mn);
       for (int s = 0; s < kGroup; ++s)
         lds_c[s][pc] = s < n_valid && !(out >> s & 1u)
-                           ? static_cast<uint8_t>(code_of(h2f(lds_k[s][ch]), mn, sf, levels)) : 0;
+                           ? static_cast<uint8_t>(code_of(h2f(lds_k[s][ch]), mn, sf, rcp, levels)) : 0;
     }
   }
   __syncthreads();
@@ -284,23 +297,33 @@ __global__ __launch_bounds__(128) void zoned_pack_kernel(PackArgs a) {
         vz[e] = 0;
         continue;
       }
-      const uint16_t* src = a.v + src_unit + static_cast<size_t>(lds_tok[s]) * d + vg * kGroup;
+      const uint4* src = reinterpret_cast<const uint4*>(a.v + src_unit + static_cast<size_t>(lds_tok[s]) * d + vg * kGroup);
       float x[kGroup];
       float mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const uint4 u = src[q4];
+        const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          x[8 * q4 + 2 * j] = h2f(static_cast<uint16_t>(wd[j] & 0xFFFFu));
+          x[8 * q4 + 2 * j + 1] = h2f(static_cast<uint16_t>(wd[j] >> 16));
+        }
+      }
+#pragma unroll
       for (int i = 0; i < kGroup; ++i) {
-        x[i] = h2f(src[i]);
         mn = fminf(mn, x[i]);
         mx = fmaxf(mx, x[i]);
       }
       const float levels = static_cast<float>((1 << w) - 1);
       const uint16_t s16 = f2h((mx - mn) / levels);
-      const float sf = h2f(s16);
+      const float sf = h2f(s16), rcp = rcp_or_zero(sf);
       vs[e] = s16;
       vz[e] = f2h(mn);
       const int per = 32 / w;
       for (int i = 0; i < w; ++i) {
         uint32_t word = 0;
-        for (int j = 0; j < per; ++j) word |= code_of(x[i * per + j], mn, sf, levels) << (j * w);
+        for (int j = 0; j < per; ++j) word |= code_of(x[i * per + j], mn, sf, rcp, levels) << (j * w);
         dst[i] = word;
       }
     }
@@ -917,6 +940,8 @@ extern "C" int zoned_pack(const int32_t* plan_host, const int32_t* plan_dev, con
   if ((plan_host[H_TOLD] > 0 || plan_host[H_SINK] > 0) && (!k || !v)) return DQA_ERR_NULL;
   if (plan_host[H_C] > 0 && (!k_new || !v_new)) return DQA_ERR_NULL;
   if (units > 65535) return DQA_ERR_SHAPE;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(blob))
+    return DQA_ERR_ALIGN;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const size_t n_words = blob_bytes / 4;
   size_t fb = (n_words + 255) / 256;

@@ -255,7 +255,8 @@ int zoned_plan(const int8_t* v_bits, const int8_t* k_bits, int B, int Hkv,
  *             first rows)
  *   k_new, v_new (device) fp16 [B][Hkv][C_new][d] (may be NULL if C_new == 0)
  *   blob      (device) blob_bytes bytes (every byte is written)
- * Errors: DQA_ERR_NULL, DQA_ERR_PLAN, DQA_ERR_HIP. */
+ * k, v, k_new, v_new and blob must be 16-byte aligned (DQA_ERR_ALIGN).
+ * Errors: DQA_ERR_NULL, DQA_ERR_PLAN, DQA_ERR_ALIGN, DQA_ERR_HIP. */
 int zoned_pack(const int32_t* plan_host, const int32_t* plan_dev,
                const uint16_t* k, const uint16_t* v, const uint16_t* k_new,
                const uint16_t* v_new, void* blob, void* stream);
