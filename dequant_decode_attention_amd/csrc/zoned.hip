@@ -409,6 +409,29 @@ __device__ __forceinline__ void key_class(const uint32_t* words, int wlo, int wh
   }
 }
 
+// Copy n16 16-byte pieces (at most kStageBytes) into the wave's LDS slice:
+// every load is issued before the first store, so the wave waits for one
+// memory round trip per item rather than one per piece.
+// Pieces past n16 reload the last piece (in bounds, n16 >= 1) and are not
+// stored.
+__device__ __forceinline__ void stage_block(const uint4* src, uint4* dst, int n16, int lane) {
+  constexpr int kIters = (kStageBytes / 16 + kWave - 1) / kWave;
+  uint32_t t[kIters][4];
+#pragma unroll
+  for (int k = 0; k < kIters; ++k) {
+    const uint4 u = src[min(lane + kWave * k, n16 - 1)];
+    t[k][0] = u.x;
+    t[k][1] = u.y;
+    t[k][2] = u.z;
+    t[k][3] = u.w;
+  }
+#pragma unroll
+  for (int k = 0; k < kIters; ++k) {
+    const int i = lane + kWave * k;
+    if (i < n16) dst[i] = uint4{t[k][0], t[k][1], t[k][2], t[k][3]};
+  }
+}
+
 // Decode over one unit's items (zone-A groups in segment order, then zone-C
 // chunks of 32 tokens); each wave takes whole items.
 //
@@ -506,18 +529,14 @@ __global__ __launch_bounds__(256, 2) void zoned_decode_kernel(ZDecodeArgs a) {
       n_valid = min(kGroup, U[U_N + seg] - g * kGroup);
       gb = ub + U[U_SEG_OFF + seg] + static_cast<size_t>(g) * U[U_GRP_B + seg];
       const int nb = kcodes_b + 2 * ksz_b + out_b;  // the key block (with its side list)
-      const uint4* src = reinterpret_cast<const uint4*>(gb);
-      uint4* dst = reinterpret_cast<uint4*>(st);
-      for (int i = lane; i < nb / 16; i += 64) dst[i] = src[i];
+      stage_block(reinterpret_cast<const uint4*>(gb), reinterpret_cast<uint4*>(st), nb / 16, lane);
       if (seg == 3)
         vrows = reinterpret_cast<const uint16_t*>(ub + U[U_ZB]) + static_cast<size_t>(g) * kGroup * D;
     } else {
       const int cg = item - total;
       n_valid = min(kGroup, a.C - cg * kGroup);
       const uint16_t* zck = reinterpret_cast<const uint16_t*>(ub + U[U_ZC]) + static_cast<size_t>(cg) * kGroup * D;
-      const uint4* src = reinterpret_cast<const uint4*>(zck);
-      uint4* dst = reinterpret_cast<uint4*>(st);
-      for (int i = lane; i < n_valid * D * 2 / 16; i += 64) dst[i] = src[i];
+      stage_block(reinterpret_cast<const uint4*>(zck), reinterpret_cast<uint4*>(st), n_valid * D * 2 / 16, lane);
       vrows = zck + static_cast<size_t>(a.C) * D;
     }
     const int w = kSegW[seg];
