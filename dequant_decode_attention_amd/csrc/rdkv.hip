@@ -346,25 +346,36 @@ __global__ __launch_bounds__(256) void rdkv_chan_partial_kernel(const uint16_t* 
   float sq[8], sk[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) sq[e] = sk[e] = 0.0f;
-  auto accum = [&](float (&acc)[8], const uint16_t* src) {
-    const uint4 v = *reinterpret_cast<const uint4*>(src);
-    const unsigned wds[4] = {v.x, v.y, v.z, v.w};
+  // four rows' loads are issued before their products (accumulated in row
+  // order, as one row at a time would)
+  constexpr int kIn = 4;
+  auto accum4 = [&](float (&acc)[8], const uint16_t* base, const int8_t* kp) {
+    for (int t = t0 + rp; t < t1; t += kIn * RP) {
+      uint4 v[kIn];
+      bool use[kIn];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float lo = h2f(static_cast<uint16_t>(wds[e] & 0xFFFFu));
-      const float hi = h2f(static_cast<uint16_t>(wds[e] >> 16));
-      acc[2 * e] = fmaf(lo, lo, acc[2 * e]);
-      acc[2 * e + 1] = fmaf(hi, hi, acc[2 * e + 1]);
+      for (int i = 0; i < kIn; ++i) {
+        const int ti = min(t + i * RP, t1 - 1);           // in bounds; rows past t1 unused
+        v[i] = *reinterpret_cast<const uint4*>(base + static_cast<size_t>(ti) * D + c8 * 8);
+        use[i] = t + i * RP < t1 && (kp == nullptr || kp[ti] != 0);
+      }
+#pragma unroll
+      for (int i = 0; i < kIn; ++i) {
+        if (!use[i]) continue;
+        const unsigned wds[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float lo = h2f(static_cast<uint16_t>(wds[e] & 0xFFFFu));
+          const float hi = h2f(static_cast<uint16_t>(wds[e] >> 16));
+          acc[2 * e] = fmaf(lo, lo, acc[2 * e]);
+          acc[2 * e + 1] = fmaf(hi, hi, acc[2 * e + 1]);
+        }
+      }
     }
   };
-  for (int g = 0; g < G; ++g) {
-    const uint16_t* qh = q + (static_cast<size_t>(b) * Hq + kv * G + g) * static_cast<size_t>(T) * D;
-    for (int t = t0 + rp; t < t1; t += RP) accum(sq, qh + static_cast<size_t>(t) * D + c8 * 8);
-  }
-  const uint16_t* kh = k + static_cast<size_t>(u) * T * D;
-  const int8_t* kp = keep + static_cast<size_t>(u) * T;
-  for (int t = t0 + rp; t < t1; t += RP)
-    if (kp[t] != 0) accum(sk, kh + static_cast<size_t>(t) * D + c8 * 8);
+  for (int g = 0; g < G; ++g)
+    accum4(sq, q + (static_cast<size_t>(b) * Hq + kv * G + g) * static_cast<size_t>(T) * D, nullptr);
+  accum4(sk, k + static_cast<size_t>(u) * T * D, keep + static_cast<size_t>(u) * T);
 
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
