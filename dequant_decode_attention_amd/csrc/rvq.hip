@@ -427,9 +427,24 @@ __global__ __launch_bounds__(256) void rvq_decode_kernel(RvqDecArgs a) {
   }
   const int tb = split * a.tiles_per_split;
   const int te = min(a.n_tiles, tb + a.tiles_per_split);
+  // value rows of up to 4 stages are prefetched one sub-tile ahead when
+  // N <= 4 (wave-uniform); larger N rebuilds each sub-tile on its own
+  const bool vpre = a.N <= 4;
   for (int ti = tb + wave; ti < te; ti += kDecWaves) {
     float lg[IT][G];
     bool valid[IT];
+    // the tile's indices, every load issued before any is used: lane ck's
+    // key index (stage ck) and the value indices of token j (stages 0..3),
+    // per sub-tile; positions past T read the last token (in bounds)
+    int kci[IT], vci[IT][4];
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int t = min(ti * kGroup + it * TL + j, a.T - 1);
+      const int16_t* vix = a.v_idx + (unit * a.T + t) * a.N;
+      if constexpr (LUT) kci[it] = static_cast<uint16_t>(a.k_idx[(unit * a.T + t) * a.N + min(ck, a.N - 1)]);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) vci[it][k] = static_cast<uint16_t>(vix[min(k, a.N - 1)]);
+    }
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
       const int t = ti * kGroup + it * TL + j;
@@ -440,8 +455,7 @@ __global__ __launch_bounds__(256) void rvq_decode_kernel(RvqDecArgs a) {
 #pragma unroll
         for (int h = 0; h < G; ++h) part[h] = 0.0f;
         if (valid[it] && ck < a.N) {
-          const int ci = min(static_cast<int>(static_cast<uint16_t>(a.k_idx[(unit * a.T + t) * a.N + ck])),
-                             a.Kc - 1);
+          const int ci = min(kci[it], a.Kc - 1);
 #pragma unroll
           for (int h = 0; h < G; ++h) part[h] = lds_lut[(h * a.N + ck) * a.Kc + ci];
         }
@@ -485,12 +499,44 @@ __global__ __launch_bounds__(256) void rvq_decode_kernel(RvqDecArgs a) {
         m[h] = mnew[h];
       }
     }
+    // values: the 4 stages' codeword rows (the lane's 16 channels, two
+    // 16-byte loads each) of sub-tile it + 1 are in flight while sub-tile
+    // it is summed
+    uint4 rows[2][4][2];
+    auto issue_rows = [&](int it, uint4 (&r)[4][2]) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int st = min(k, a.N - 1);
+        const uint32_t ci = min(static_cast<uint32_t>(vci[it][k]), static_cast<uint32_t>(a.Kc - 1));
+        const uint4* row = reinterpret_cast<const uint4*>(a.v_cb + (static_cast<size_t>(st) * a.Kc + ci) * kD + c0);
+        r[k][0] = row[0];
+        r[k][1] = row[1];
+      }
+    };
+    if (vpre) issue_rows(0, rows[0]);
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
+      if (vpre && it + 1 < IT) issue_rows(it + 1, rows[(it + 1) & 1]);
       if (!valid[it]) continue;
-      const int t = ti * kGroup + it * TL + j;
       float vh[16];
-      rebuild16(a.v_cb, a.v_idx + (unit * a.T + t) * a.N, a.N, a.Kc, c0, vh);
+      if (vpre) {
+#pragma unroll
+        for (int c = 0; c < 16; ++c) vh[c] = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          if (k >= a.N) break;
+          const uint4 ra = rows[it & 1][k][0], rb = rows[it & 1][k][1];
+          const uint32_t w[8] = {ra.x, ra.y, ra.z, ra.w, rb.x, rb.y, rb.z, rb.w};
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            vh[2 * i] += h2f(static_cast<uint16_t>(w[i] & 0xFFFFu));
+            vh[2 * i + 1] += h2f(static_cast<uint16_t>(w[i] >> 16));
+          }
+        }
+      } else {
+        const int t = ti * kGroup + it * TL + j;
+        rebuild16(a.v_cb, a.v_idx + (unit * a.T + t) * a.N, a.N, a.Kc, c0, vh);
+      }
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         const float p = exp2f(lg[it][h] - m[h]);
