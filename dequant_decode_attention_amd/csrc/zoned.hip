@@ -413,7 +413,9 @@ __device__ __forceinline__ void key_class(const uint32_t* words, int wlo, int wh
 // every load is issued before the first store, so the wave waits for one
 // memory round trip per item rather than one per piece.
 // Pieces past n16 reload the last piece (in bounds, n16 >= 1) and are not
-// stored.
+// stored.  The empty asm statements take every loaded value before the first
+// store, so the compiler cannot move each load next to its (conditional)
+// store.
 __device__ __forceinline__ void stage_block(const uint4* src, uint4* dst, int n16, int lane) {
   constexpr int kIters = (kStageBytes / 16 + kWave - 1) / kWave;
   uint32_t t[kIters][4];
@@ -425,6 +427,8 @@ __device__ __forceinline__ void stage_block(const uint4* src, uint4* dst, int n1
     t[k][2] = u.z;
     t[k][3] = u.w;
   }
+#pragma unroll
+  for (int k = 0; k < kIters; ++k) asm volatile("" : "+v"(t[k][0]), "+v"(t[k][1]), "+v"(t[k][2]), "+v"(t[k][3]));
 #pragma unroll
   for (int k = 0; k < kIters; ++k) {
     const int i = lane + kWave * k;
