@@ -152,15 +152,14 @@ __device__ __forceinline__ void load_quad_octet(const uint16_t* rows, int tq, in
 // tiles of capacity per (batch, KV head), this launch's tiles starting at
 // tile0 (quantize_pack_k: src_T = T, dst_tiles = T/32, tile0 = 0).
 template <int D, int BITS>
-__global__ __launch_bounds__(D) void quantize_k_kernel(
+__device__ __forceinline__ void quantize_k_tile(
     const uint16_t* __restrict__ k, int src_T, int Hkv,
     uint32_t* __restrict__ codes, uint16_t* __restrict__ scale,
-    uint16_t* __restrict__ zero, int dst_tiles, int tile0) {
+    uint16_t* __restrict__ zero, int dst_tiles, int tile0, int tile, int h, int b) {
   constexpr int NCO = D / 8;             // channel octets per token
   // per channel: zero, reciprocal of the scale, scale (fp32)
   __shared__ __attribute__((aligned(16))) float lds_par[3][NCO][8];
   const int tid = threadIdx.x, tq = tid / NCO, co = tid % NCO;
-  const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const size_t unit = static_cast<size_t>(b) * Hkv + h;
   const size_t dtile = unit * dst_tiles + tile0 + tile;        // destination tile
   const uint16_t* src = k + (unit * src_T + static_cast<size_t>(tile) * kGroup) * D;
@@ -278,17 +277,16 @@ __global__ __launch_bounds__(D) void quantize_k_kernel(
 // copies channel c's 4 * BITS bytes out.
 // Source rows and destination tiles as quantize_k_kernel.
 template <int D, int BITS>
-__global__ __launch_bounds__(D) void quantize_v_kernel(
+__device__ __forceinline__ void quantize_v_tile(
     const uint16_t* __restrict__ v, int src_T, int Hkv,
     uint32_t* __restrict__ codes, uint16_t* __restrict__ scale,
-    uint16_t* __restrict__ zero, int dst_tiles, int tile0) {
+    uint16_t* __restrict__ zero, int dst_tiles, int tile0, int blk, int h, int b) {
   constexpr int NCO = D / 8;             // channel octets per token
   constexpr int CB = 4 * BITS;           // bytes of one channel in a block
   // LDS byte offset of channel c: 4 bytes of padding per 8 channels put the
   // channels that one store instruction touches in different banks
   __shared__ __attribute__((aligned(16))) uint32_t lds_codes[(D * CB + (D / 8) * 4) / 4];
   const int tid = threadIdx.x, tq = tid / NCO, co = tid % NCO;
-  const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const size_t unit = static_cast<size_t>(b) * Hkv + h;
   const uint16_t* src = v + (unit * src_T + static_cast<size_t>(blk) * kGroup) * D;
   const size_t dtok0 = (unit * dst_tiles + tile0 + blk) * kGroup;   // destination token of row 0
@@ -360,6 +358,57 @@ __global__ __launch_bounds__(D) void quantize_v_kernel(
     for (int i = 0; i < CB / 16; ++i)
       reinterpret_cast<uint4*>(to)[i] = uint4{from[4 * i], from[4 * i + 1], from[4 * i + 2], from[4 * i + 3]};
   }
+}
+
+template <int D, int BITS>
+__global__ __launch_bounds__(D) void quantize_k_kernel(
+    const uint16_t* __restrict__ k, int src_T, int Hkv,
+    uint32_t* __restrict__ codes, uint16_t* __restrict__ scale,
+    uint16_t* __restrict__ zero, int dst_tiles, int tile0) {
+  quantize_k_tile<D, BITS>(k, src_T, Hkv, codes, scale, zero, dst_tiles, tile0, blockIdx.x, blockIdx.y, blockIdx.z);
+}
+template <int D, int BITS>
+__global__ __launch_bounds__(D) void quantize_v_kernel(
+    const uint16_t* __restrict__ v, int src_T, int Hkv,
+    uint32_t* __restrict__ codes, uint16_t* __restrict__ scale,
+    uint16_t* __restrict__ zero, int dst_tiles, int tile0) {
+  quantize_v_tile<D, BITS>(v, src_T, Hkv, codes, scale, zero, dst_tiles, tile0, blockIdx.x, blockIdx.y, blockIdx.z);
+}
+
+// Keys and values of the same tiles in one launch (grid z = 2 B: keys for
+// z < B, values for z >= B), for the streaming append.
+struct QuantizeOut {
+  uint32_t* codes;
+  uint16_t* scale;
+  uint16_t* zero;
+};
+template <int D, int BITS>
+__global__ __launch_bounds__(D) void quantize_kv_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                                                        int src_T, int Hkv, QuantizeOut ko, QuantizeOut vo,
+                                                        int dst_tiles, int tile0, int B) {
+  const int z = blockIdx.z;
+  if (z < B)
+    quantize_k_tile<D, BITS>(k, src_T, Hkv, ko.codes, ko.scale, ko.zero, dst_tiles, tile0, blockIdx.x, blockIdx.y, z);
+  else
+    quantize_v_tile<D, BITS>(v, src_T, Hkv, vo.codes, vo.scale, vo.zero, dst_tiles, tile0, blockIdx.x, blockIdx.y,
+                             z - B);
+}
+
+void launch_quantize_kv(int d, int bits, dim3 grid, hipStream_t s, const uint16_t* k, const uint16_t* v, int src_T,
+                        int Hkv, QuantizeOut ko, QuantizeOut vo, int dst_tiles, int tile0, int B) {
+#define DQA_QKV(D, BITS)                                                                                   \
+  hipLaunchKernelGGL((quantize_kv_kernel<D, BITS>), grid, dim3(D), 0, s, k, v, src_T, Hkv, ko, vo, dst_tiles, \
+                     tile0, B)
+  if (d == 128) {
+    if (bits == 2) DQA_QKV(128, 2);
+    else if (bits == 4) DQA_QKV(128, 4);
+    else DQA_QKV(128, 8);
+  } else {
+    if (bits == 2) DQA_QKV(64, 2);
+    else if (bits == 4) DQA_QKV(64, 4);
+    else DQA_QKV(64, 8);
+  }
+#undef DQA_QKV
 }
 
 // Launch the K or V quantizer for head dim d and width bits over grid
@@ -451,36 +500,48 @@ namespace {
 // Rows [0, R) of src_a (R_cap rows per unit) followed by rows [0, n) of
 // src_b (n rows per unit) into dst (R + n rows per unit), 16 bytes per
 // thread; d / 8 chunks per row.
-__global__ __launch_bounds__(256) void stage_rows_kernel(const uint16_t* __restrict__ src_a, int R, int R_cap,
-                                                         const uint16_t* __restrict__ src_b, int n,
-                                                         uint16_t* __restrict__ dst, size_t units, int d) {
+// Keys and values in one launch: index space [0, 2 total), the second half
+// for the values.
+struct RowPair {
+  const uint16_t* a;   // recent rows (R_cap per unit)
+  const uint16_t* b;   // new rows (n per unit)
+  uint16_t* dst;       // staged rows (R + n per unit)
+};
+__global__ __launch_bounds__(256) void stage_rows_kernel(RowPair kp, RowPair vp, int R, int R_cap, int n,
+                                                         size_t units, int d) {
   const int cpr = d / 8;
   const size_t rows = static_cast<size_t>(R) + n;
   const size_t total = units * rows * cpr;
-  for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total;
-       i += static_cast<size_t>(gridDim.x) * blockDim.x) {
+  for (size_t i2 = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i2 < 2 * total;
+       i2 += static_cast<size_t>(gridDim.x) * blockDim.x) {
+    const RowPair& p = i2 < total ? kp : vp;
+    const size_t i = i2 < total ? i2 : i2 - total;
     const size_t u = i / (rows * cpr);
     const size_t rem = i % (rows * cpr);
     const int r = static_cast<int>(rem / cpr), ch = static_cast<int>(rem % cpr);
-    const uint16_t* s = r < R ? src_a + (u * R_cap + r) * d : src_b + (u * n + (r - R)) * d;
-    reinterpret_cast<uint4*>(dst + (u * rows + r) * d)[ch] = reinterpret_cast<const uint4*>(s)[ch];
+    const uint16_t* s = r < R ? p.a + (u * R_cap + r) * d : p.b + (u * n + (r - R)) * d;
+    reinterpret_cast<uint4*>(p.dst + (u * rows + r) * d)[ch] = reinterpret_cast<const uint4*>(s)[ch];
   }
 }
 
 // Rows [skip, skip + keep) of src (rows per unit) to rows [0, keep) of dst
-// (R_cap rows per unit).
-__global__ __launch_bounds__(256) void unstage_rows_kernel(const uint16_t* __restrict__ src, int rows, int skip,
-                                                           int keep, uint16_t* __restrict__ dst, int R_cap,
-                                                           size_t units, int d) {
+// (R_cap rows per unit), keys and values in one launch.
+__global__ __launch_bounds__(256) void unstage_rows_kernel(const uint16_t* __restrict__ ksrc,
+                                                           const uint16_t* __restrict__ vsrc, int rows, int skip,
+                                                           int keep, uint16_t* __restrict__ kdst,
+                                                           uint16_t* __restrict__ vdst, int R_cap, size_t units,
+                                                           int d) {
   const int cpr = d / 8;
   const size_t total = units * static_cast<size_t>(keep) * cpr;
-  for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total;
-       i += static_cast<size_t>(gridDim.x) * blockDim.x) {
+  for (size_t i2 = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i2 < 2 * total;
+       i2 += static_cast<size_t>(gridDim.x) * blockDim.x) {
+    const bool keys = i2 < total;
+    const size_t i = keys ? i2 : i2 - total;
     const size_t u = i / (static_cast<size_t>(keep) * cpr);
     const size_t rem = i % (static_cast<size_t>(keep) * cpr);
     const int r = static_cast<int>(rem / cpr), ch = static_cast<int>(rem % cpr);
-    reinterpret_cast<uint4*>(dst + (u * R_cap + r) * d)[ch] =
-        reinterpret_cast<const uint4*>(src + (u * rows + skip + r) * d)[ch];
+    reinterpret_cast<uint4*>((keys ? kdst : vdst) + (u * R_cap + r) * d)[ch] =
+        reinterpret_cast<const uint4*>((keys ? ksrc : vsrc) + (u * rows + skip + r) * d)[ch];
   }
 }
 
@@ -504,7 +565,7 @@ int append_shape(const dqa_kivi_cache* c, int n_new) {
   if (c->T_cap < 0 || c->T_cap % kGroup != 0 || (c->T_cap > 0 && c->T_cap < c->T_q)) return DQA_ERR_SHAPE;
   if (c->R_cap < 0 || (c->R_cap > 0 && c->R_cap < c->R)) return DQA_ERR_SHAPE;
   if (static_cast<long long>(c->R) + n_new > (1 << 24)) return DQA_ERR_SHAPE;
-  if (c->B > 65535 || c->Hkv > 65535) return DQA_ERR_SHAPE;
+  if (c->B > 32767 || c->Hkv > 65535) return DQA_ERR_SHAPE;   // keys and values share one grid z
   return DQA_OK;
 }
 
@@ -566,10 +627,8 @@ extern "C" int kivi_append(dqa_kivi_cache* c, const uint16_t* k_new, const uint1
   uint16_t* wk = static_cast<uint16_t*>(ws);
   uint16_t* wv = wk + units * static_cast<size_t>(rows) * d;
   const size_t chunks = units * static_cast<size_t>(rows) * (d / 8);
-  hipLaunchKernelGGL(stage_rows_kernel, dim3(copy_blocks(chunks)), dim3(256), 0, s, c->k_recent, c->R, R_cap, k_new,
-                     n_new, wk, units, d);
-  hipLaunchKernelGGL(stage_rows_kernel, dim3(copy_blocks(chunks)), dim3(256), 0, s, c->v_recent, c->R, R_cap, v_new,
-                     n_new, wv, units, d);
+  hipLaunchKernelGGL(stage_rows_kernel, dim3(copy_blocks(2 * chunks)), dim3(256), 0, s,
+                     RowPair{c->k_recent, k_new, wk}, RowPair{c->v_recent, v_new, wv}, c->R, R_cap, n_new, units, d);
   DQA_CHECK_LAUNCH();
   if (f > 0) {
     uint32_t* kc = const_cast<uint32_t*>(c->k_codes);
@@ -578,18 +637,17 @@ extern "C" int kivi_append(dqa_kivi_cache* c, const uint16_t* k_new, const uint1
     uint32_t* vc = const_cast<uint32_t*>(c->v_codes);
     uint16_t* vs = const_cast<uint16_t*>(c->v_scale);
     uint16_t* vz = const_cast<uint16_t*>(c->v_zero);
-    const dim3 grid(f, c->Hkv, c->B);
+    const dim3 grid(f, c->Hkv, 2 * c->B);
     const int dst_tiles = T_cap / kGroup, tile0 = c->T_q / kGroup;
-    launch_quantize<true>(d, c->bits, grid, s, wk, rows, c->Hkv, kc, ks, kz, dst_tiles, tile0);
-    launch_quantize<false>(d, c->bits, grid, s, wv, rows, c->Hkv, vc, vs, vz, dst_tiles, tile0);
+    launch_quantize_kv(d, c->bits, grid, s, wk, wv, rows, c->Hkv, QuantizeOut{kc, ks, kz}, QuantizeOut{vc, vs, vz},
+                       dst_tiles, tile0, c->B);
     DQA_CHECK_LAUNCH();
   }
   if (R_new > 0) {
     const size_t kchunks = units * static_cast<size_t>(R_new) * (d / 8);
-    hipLaunchKernelGGL(unstage_rows_kernel, dim3(copy_blocks(kchunks)), dim3(256), 0, s, wk, rows, f * kGroup, R_new,
-                       const_cast<uint16_t*>(c->k_recent), R_cap, units, d);
-    hipLaunchKernelGGL(unstage_rows_kernel, dim3(copy_blocks(kchunks)), dim3(256), 0, s, wv, rows, f * kGroup, R_new,
-                       const_cast<uint16_t*>(c->v_recent), R_cap, units, d);
+    hipLaunchKernelGGL(unstage_rows_kernel, dim3(copy_blocks(2 * kchunks)), dim3(256), 0, s, wk, wv, rows,
+                       f * kGroup, R_new, const_cast<uint16_t*>(c->k_recent), const_cast<uint16_t*>(c->v_recent),
+                       R_cap, units, d);
     DQA_CHECK_LAUNCH();
   }
   c->T_q = T_new;

@@ -193,7 +193,8 @@ int decode_attention_qkv_merge(const dqa_kivi_cache* cache, const void* ws,
  *          may be null when n_new == 0
  *   R_max  0..128
  *   ws     (device) workspace of ws_bytes >= kivi_append_workspace_bytes
- * Enqueues up to four kernels on `stream`; the recent buffers may be
+ * B <= 32767.  Enqueues up to three kernels on `stream` (stage, quantize,
+ * move back; keys and values together in each); the recent buffers may be
  * rewritten in place (the kernels read a staged copy from ws).
  * Errors: DQA_ERR_NULL, DQA_ERR_SHAPE, DQA_ERR_BITS, DQA_ERR_WORKSPACE,
  * DQA_ERR_ALIGN, DQA_ERR_HIP. */
