@@ -113,6 +113,32 @@ __device__ __forceinline__ float rcp_or_zero(float sf) { return sf == 0.0f ? 0.0
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// n16 16-byte pieces from src to dst by a 128-thread workgroup, four loads
+// in flight per thread (dst and src 16-byte aligned).
+__device__ __forceinline__ void copy16(uint16_t* dst, const uint16_t* src, size_t n16, int tid) {
+  const uint4* s4 = reinterpret_cast<const uint4*>(src);
+  uint4* d4 = reinterpret_cast<uint4*>(dst);
+  for (size_t i0 = tid; i0 < n16; i0 += 4 * 128) {
+    uint32_t u[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const size_t e = i0 + 128 * i;
+      const uint4 x = s4[e < n16 ? e : n16 - 1];
+      u[i][0] = x.x;
+      u[i][1] = x.y;
+      u[i][2] = x.z;
+      u[i][3] = x.w;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(u[i][0]), "+v"(u[i][1]), "+v"(u[i][2]), "+v"(u[i][3]));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const size_t e = i0 + 128 * i;
+      if (e < n16) d4[e] = uint4{u[i][0], u[i][1], u[i][2], u[i][3]};
+    }
+  }
+}
+
 // Zero-fill (the blob's padding bytes are defined as zero).
 __global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t* p, size_t n_words) {
   size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -147,14 +173,12 @@ __global__ __launch_bounds__(128) void zoned_pack_kernel(PackArgs a) {
     const size_t ns = static_cast<size_t>(a.sink) * d;
     const size_t n = ns + static_cast<size_t>(a.C) * d;
     const size_t src = static_cast<size_t>(unit) * a.C * d;
-    for (size_t i = tid; i < ns; i += blockDim.x) {
-      zc[i] = a.k[src_unit + i];
-      zc[n + i] = a.v[src_unit + i];
-    }
-    for (size_t i = tid; i < n - ns; i += blockDim.x) {
-      zc[ns + i] = a.k_new[src + i];
-      zc[n + ns + i] = a.v_new[src + i];
-    }
+    // 16-byte pieces (rows are multiples of 16 bytes, every block 16-byte
+    // aligned), four loads in flight per thread
+    copy16(zc, a.k + src_unit, ns / 8, tid);
+    copy16(zc + n, a.v + src_unit, ns / 8, tid);
+    copy16(zc + ns, a.k_new + src, (n - ns) / 8, tid);
+    copy16(zc + n + ns, a.v_new + src, (n - ns) / 8, tid);
     return;
   }
   // locate the segment of this group
@@ -328,11 +352,27 @@ __global__ __launch_bounds__(128) void zoned_pack_kernel(PackArgs a) {
       }
     }
   } else {
-    // zone B rows of this group's slots
+    // zone B rows of this group's slots, 16-byte pieces, four in flight
     uint16_t* zb = reinterpret_cast<uint16_t*>(ub + U[U_ZB]) + static_cast<size_t>(g) * kGroup * d;
-    for (int e = tid; e < kGroup * d; e += blockDim.x) {
-      const int s = e / d, c = e % d;
-      zb[e] = lds_tok[s] >= 0 ? a.v[src_unit + static_cast<size_t>(lds_tok[s]) * d + c] : 0;
+    const int pr = d / 8;                        // pieces per row
+    for (int e0 = tid; e0 < kGroup * pr; e0 += 4 * 128) {
+      uint32_t u[4][4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = min(e0 + 128 * i, kGroup * pr - 1), s = e / pr, c8 = e % pr;
+        const int tok = lds_tok[s] >= 0 ? lds_tok[s] : 0;    // masked slots read row 0 and store zeros
+        const uint4 x = *reinterpret_cast<const uint4*>(a.v + src_unit + static_cast<size_t>(tok) * d + 8 * c8);
+        const bool keep = lds_tok[s] >= 0;
+        u[i][0] = keep ? x.x : 0u;
+        u[i][1] = keep ? x.y : 0u;
+        u[i][2] = keep ? x.z : 0u;
+        u[i][3] = keep ? x.w : 0u;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = e0 + 128 * i;
+        if (e < kGroup * pr) reinterpret_cast<uint4*>(zb)[e] = uint4{u[i][0], u[i][1], u[i][2], u[i][3]};
+      }
     }
   }
 }
