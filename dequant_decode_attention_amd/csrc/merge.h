@@ -59,11 +59,11 @@ __device__ __forceinline__ void write_split_state(float* partials, float* out, i
 // lanes compute the merge weight of every split (max over splits, then
 // exp2 weights and the weighted row sum, combined in a fixed butterfly
 // order), then each lane sums its channel over the splits in split order.
-// The first 16 splits' outputs are loaded together with the states.
+// The first 32 splits' outputs are loaded together with the states.
 template <int D, int G>
 __global__ __launch_bounds__(64) void split_merge_kernel(const float* __restrict__ partials, int total_splits,
                                                          int Hq, int Hkv, float* __restrict__ out) {
-  constexpr int kEarly = 16;
+  constexpr int kEarly = 32;
   __shared__ float wts[kMaxSplitsMerge];
   __shared__ float inv_l;
   constexpr int CB = D / 64;                 // 64-channel blocks per head
