@@ -563,6 +563,8 @@ __global__ __launch_bounds__(256, 2) void zoned_decode_kernel(ZDecodeArgs a) {
     int seg = 3, g = 0, n_valid;
     const uint16_t* vrows = nullptr;          // fp16 value rows (zone B / zone C), else null
     const uint8_t* gb = nullptr;              // zone-A group
+    const uint4* stage_src;                   // the item's key block / zone-C keys, staged below
+    int stage_n16;
     if (!zone_c) {
       seg = 0;
       g = item;
@@ -573,14 +575,16 @@ __global__ __launch_bounds__(256, 2) void zoned_decode_kernel(ZDecodeArgs a) {
       n_valid = min(kGroup, U[U_N + seg] - g * kGroup);
       gb = ub + U[U_SEG_OFF + seg] + static_cast<size_t>(g) * U[U_GRP_B + seg];
       const int nb = kcodes_b + 2 * ksz_b + out_b;  // the key block (with its side list)
-      stage_block(reinterpret_cast<const uint4*>(gb), reinterpret_cast<uint4*>(st), nb / 16, lane);
+      stage_src = reinterpret_cast<const uint4*>(gb);
+      stage_n16 = nb / 16;
       if (seg == 3)
         vrows = reinterpret_cast<const uint16_t*>(ub + U[U_ZB]) + static_cast<size_t>(g) * kGroup * D;
     } else {
       const int cg = item - total;
       n_valid = min(kGroup, a.C - cg * kGroup);
       const uint16_t* zck = reinterpret_cast<const uint16_t*>(ub + U[U_ZC]) + static_cast<size_t>(cg) * kGroup * D;
-      stage_block(reinterpret_cast<const uint4*>(zck), reinterpret_cast<uint4*>(st), n_valid * D * 2 / 16, lane);
+      stage_src = reinterpret_cast<const uint4*>(zck);
+      stage_n16 = n_valid * D * 2 / 16;
       vrows = zck + static_cast<size_t>(a.C) * D;
     }
     const int w = kSegW[seg];
@@ -624,6 +628,9 @@ __global__ __launch_bounds__(256, 2) void zoned_decode_kernel(ZDecodeArgs a) {
         vsz[1] = vz[j * NG + hf];
       }
     }
+    // the key block's loads follow the value loads, so both are in flight
+    // together (one memory round trip per item)
+    stage_block(stage_src, reinterpret_cast<uint4*>(st), stage_n16, lane);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
