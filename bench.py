@@ -144,7 +144,7 @@ def _hbm_row(kernel, workload, ms, nbytes, note=""):
 
 
 def time_quantize(dqa, torch, k, v, bits, cfg):
-    """Rows a1-a3: quantize + pack of the whole c3 cache (fp16 in, codes and
+    """Rows a1-a3: quantize + pack of the whole llama3.1-8b-gqa-32k cache (fp16 in, codes and
     fp16 scale/zero out)."""
     B, Hkv, T, d = k.shape
     n = B * Hkv * T * d
@@ -158,7 +158,7 @@ def time_quantize(dqa, torch, k, v, bits, cfg):
 
 
 def time_append(dqa, torch, dev, cfg, bits):
-    """Streaming append on the c3 shape: one new token per (batch, KV head)
+    """Streaming append on the llama3.1-8b-gqa-32k shape: one new token per (batch, KV head)
     into a full 128-token fp16 window over a cache holding 32736 quantized
     tokens, so every call quantizes one group of 32 per (batch, KV head)
     (the counts are reset between calls)."""
@@ -194,13 +194,13 @@ def time_append(dqa, torch, dev, cfg, bits):
 
 
 def time_zoned(dqa, torch, dev):
-    """Rows a8-a9 on the mixed-width zoned workload (c4): packer (fp16 K/V of
+    """Rows a8-a9 on the mixed-width-zoned-16k workload: packer (fp16 K/V of
     kept tokens read, blob written) and decode (blob read; blob replicas
-    rotated past the Infinity Cache); then the same pair with c4's sink
+    rotated past the Infinity Cache); then the same pair with that workload's sink
     window and key outlier side lists."""
     from workloads import CONFIGS, zoned_inputs
     import numpy as np
-    cfg = CONFIGS["c4"]
+    cfg = CONFIGS["mixed-width-zoned-16k"]
     inp = zoned_inputs(cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["d"], cfg["T_old"], cfg["C"], seed=4,
                        v_width_probs=cfg["v_width_probs"], k_width_probs=cfg["k_width_probs"],
                        outliers=cfg["outliers"])
@@ -237,13 +237,13 @@ def time_zoned(dqa, torch, dev):
 
 
 def time_rdkv(dqa, torch, dev):
-    """RDKV allocation on the mixed-width cache's shape (c4: 2 sequences, 32
+    """RDKV allocation on the mixed-width cache's shape (2 sequences, 32
     query heads over 8 KV heads, 16384 prefill positions, d = 128): token
     weights (two causal logit passes on the matrix cores, one exponential per
     causal pair and pass), channel weights (one read of q and k), and the
-    two Lagrangian allocations; the budgets are the mean widths of c4's maps."""
+    two Lagrangian allocations; the budgets are the mean widths of that cache's random maps."""
     from workloads import CONFIGS, rdkv_inputs
-    cfg = CONFIGS["c4"]
+    cfg = CONFIGS["mixed-width-zoned-16k"]
     B, Hq, Hkv, d, T = cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["d"], cfg["T_old"]
     inp = rdkv_inputs(B, Hq, Hkv, d, T, seed=4, outliers=cfg["outliers"])
     q, k = torch.from_numpy(inp["q"]).to(dev), torch.from_numpy(inp["k"]).to(dev)
@@ -285,11 +285,11 @@ def time_rdkv(dqa, torch, dev):
 
 
 def time_rvq(dqa, torch, dev):
-    """Rows a10-a11 on the residual-VQ workload (c5): encoding of every key
+    """Rows a10-a11 on the residual-VQ workload (rvq-llama3.2-3b-8k): encoding of every key
     and value vector (MFMA-bound: 2 N Kc d flop per vector) and decode
     attention from the indices (a few MB per step: latency-bound)."""
     from workloads import CONFIGS, rvq_inputs
-    cfg = CONFIGS["c5"]
+    cfg = CONFIGS["rvq-llama3.2-3b-8k"]
     inp = rvq_inputs(cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["d"], cfg["T"], cfg["N"], cfg["Kc"], seed=5)
     d, N, Kc = cfg["d"], cfg["N"], cfg["Kc"]
     k = torch.from_numpy(inp["k"]).to(dev).reshape(-1, d)
@@ -336,14 +336,14 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus}); the decode path shards "
-              f"by (batch, KV head) with no communication, see DESIGN.md", file=sys.stderr)
+              f"by (batch, KV head) with no communication", file=sys.stderr)
         return 2
 
     import torch
     import dequant_decode_attention_amd as dqa
     from workloads import CONFIGS, kivi_inputs
 
-    cfg = CONFIGS["c3"]
+    cfg = CONFIGS["llama3.1-8b-gqa-32k"]
     bits = args.bits
     dev = torch.device("cuda:0")
     inp = kivi_inputs(cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["d"], cfg["T_q"], cfg["R"], seed=3,

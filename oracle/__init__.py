@@ -20,8 +20,8 @@ by page and section.  Page keys used throughout this repository:
   title (the page numbers two sections "2.2": "bit-allocation pipeline" and
   "TriZone packed decoding").
 
-Arithmetic conventions (readings of what the pages leave open are listed in
-the design doc of the repository):
+Arithmetic conventions (each module's docstring states the readings it
+takes where the pages leave a step open):
 
 * fp16 inputs are widened to fp32 exactly; the quantizer runs in IEEE fp32
   with numpy float32 arrays (one rounding per operation, no fused

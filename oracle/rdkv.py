@@ -14,7 +14,7 @@ What the page defines ([P3 sec 2.1, theoretical formulation] and [P3 sec
   weights are computed once after prefill from the full cache; phase 2
   assigns token widths, phase 3 channel widths over the tokens phase 2 kept.
 
-Readings fixed here (listed in the design doc):
+Readings fixed here:
 
 * a_{tau,t} is the causal prefill attention (t <= tau) with logits scaled by
   sm_scale; with grouped heads a KV token's weight sums over the G query

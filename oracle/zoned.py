@@ -18,7 +18,7 @@ TriZone packed decoding]):
   into the products.
 
 Readings (the pages give neither formulas nor byte layouts); all of them are
-listed in DESIGN.md:
+listed here:
 
 * a token whose value width is 0 is dropped together with its key.
 * a key channel whose width is 0 is not stored: the kept old tokens' keys

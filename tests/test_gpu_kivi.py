@@ -104,13 +104,13 @@ def test_quantize_rounding_ties(dqa, bits, d):
     np.testing.assert_array_equal(host(gv[2]).view(np.uint16), vz.view(np.uint16))
 
 
-@pytest.mark.parametrize("name", ["c2", "c3"])
+@pytest.mark.parametrize("name", ["llama2-13b-decode-layer", "llama3.1-8b-gqa-32k"])
 def test_quantize_full_config_sampled_units(dqa, name):
     """Full-size quantization on the GPU; the oracle re-quantizes sampled
     (batch, KV head) units and compares them bit for bit."""
     cfg = CONFIGS[name]
     inp = kivi_inputs(cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["d"], cfg["T_q"], 0,
-                      seed=int(name[1:]), outliers=cfg["outliers"])
+                      seed=cfg["seed"], outliers=cfg["outliers"])
     for bits in cfg["bits"]:
         say("quantize full", name, bits)
         gk = dqa.quantize_pack_k(dev(inp["k"]), bits)
@@ -131,7 +131,7 @@ def test_quantize_full_config_sampled_units(dqa, name):
 
 DECODE_CASES = [
     # B, Hq, Hkv, d, T_q, R, bits, rope
-    (1, 1, 1, 64, 256, 0, 2, 0.0),          # c1 shape
+    (1, 1, 1, 64, 256, 0, 2, 0.0),          # tiny-kivi shape
     (2, 8, 2, 128, 320, 37, 2, 500000.0),   # GQA 4, ragged recent zone, RoPE
     (2, 8, 2, 128, 320, 37, 4, 500000.0),
     (1, 4, 4, 128, 128, 128, 8, 10000.0),   # MHA, full recent zone
@@ -190,13 +190,13 @@ def test_decode_two_phase_equals_one_call(dqa, T_q, R):
     assert np.array_equal(host(out), ref)
 
 
-@pytest.mark.parametrize("name,bits", [("c3", 2), ("c3", 4), ("c2", 2), ("c1", 2)])
+@pytest.mark.parametrize("name,bits", [("llama3.1-8b-gqa-32k", 2), ("llama3.1-8b-gqa-32k", 4), ("llama2-13b-decode-layer", 2), ("tiny-kivi", 2)])
 def test_decode_full_config_sampled_rows(dqa, name, bits):
     """Full-size decode in the launch configuration the bench times; the
     oracle computes sampled output rows one by one."""
     cfg = CONFIGS[name]
     inp = kivi_inputs(cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["d"], cfg["T_q"], cfg["R"],
-                      seed=int(name[1:]), outliers=cfg["outliers"])
+                      seed=cfg["seed"], outliers=cfg["outliers"])
     scale = 1.0 / math.sqrt(cfg["d"])
     say("decode full", name, bits)
     cache = gpu_cache(dqa, inp, bits, cfg["Hq"], cfg["rope_theta"])

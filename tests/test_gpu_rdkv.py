@@ -222,7 +222,7 @@ def test_maps_drive_the_zoned_cache(dqa):
 
 
 def test_full_size_invariants(dqa):
-    cfg = CONFIGS["c4"]
+    cfg = CONFIGS["mixed-width-zoned-16k"]
     B, Hq, Hkv, d, T = cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["d"], cfg["T_old"]
     G = Hq // Hkv
     inp = rdkv_inputs(B, Hq, Hkv, d, T, seed=4, outliers=cfg["outliers"])

@@ -90,10 +90,10 @@ def test_encode_random(dqa, n, N, Kc):
 
 
 def test_full_config_encode_and_decode(dqa):
-    cfg = CONFIGS["c5"]
+    cfg = CONFIGS["rvq-llama3.2-3b-8k"]
     inp = rvq_inputs(cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["d"], cfg["T"], cfg["N"], cfg["Kc"], seed=5)
     B, Hkv, T, d, N = cfg["B"], cfg["Hkv"], cfg["T"], cfg["d"], cfg["N"]
-    say("rvq full c5 encode")
+    say("rvq full rvq-llama3.2-3b-8k encode")
     ki = dqa.rvq_encode(dev(inp["k"].reshape(-1, d)), dev(inp["k_cb"])).reshape(B, Hkv, T, N)
     vi = dqa.rvq_encode(dev(inp["v"].reshape(-1, d)), dev(inp["v_cb"])).reshape(B, Hkv, T, N)
     kih, vih = host(ki), host(vi)
@@ -101,8 +101,8 @@ def test_full_config_encode_and_decode(dqa):
     rows = rng.choice(B * Hkv * T, size=48, replace=False)
     ties = check_indices(inp["k"].reshape(-1, d)[rows], inp["k_cb"], kih.reshape(-1, N)[rows])
     ties += check_indices(inp["v"].reshape(-1, d)[rows], inp["v_cb"], vih.reshape(-1, N)[rows])
-    print(f"c5 sampled vectors: documented ties {ties}", flush=True)
-    say("rvq full c5 decode")
+    print(f"rvq-llama3.2-3b-8k sampled vectors: documented ties {ties}", flush=True)
+    say("rvq full rvq-llama3.2-3b-8k decode")
     scale = 1.0 / math.sqrt(d)
     out = host(dqa.rvq_decode_attention(dev(inp["q"]), ki, vi, dev(inp["k_cb"]), dev(inp["v_cb"]), scale))
     G = cfg["Hq"] // Hkv
@@ -110,7 +110,7 @@ def test_full_config_encode_and_decode(dqa):
         ref = oracle.rvq_decode_attention(inp["q"][b:b + 1, h * G:(h + 1) * G], kih[b:b + 1, h:h + 1],
                                           vih[b:b + 1, h:h + 1], inp["k_cb"], inp["v_cb"], scale)
         err = rel_l2(out[b, h * G:(h + 1) * G][None], ref)
-        print(f"c5 decode unit ({b},{h}) rel_l2={err:.3e}", flush=True)
+        print(f"rvq-llama3.2-3b-8k decode unit ({b},{h}) rel_l2={err:.3e}", flush=True)
         assert err <= TOL
 
 

@@ -123,7 +123,7 @@ def test_append_full_config_flush(dqa):
     into a cache that already holds 32736 quantized tokens; the new group and
     the window equal the oracle's quantization of the same tokens."""
     B, Hq, Hkv, d, bits = 4, 32, 8, 128, 2
-    say("kivi_append c3 flush")
+    say("kivi_append llama3.1-8b-gqa-32k flush")
     T_q0 = 32768 - 32
     cache = _empty_gpu_cache(dqa, B, Hq, Hkv, d, bits, 32768, 128, 5e5)
     k, v = _tokens(B, Hkv, 129, d, seed=13)

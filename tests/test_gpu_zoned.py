@@ -75,11 +75,11 @@ def test_zoned_pack_and_decode(dqa, case):
 
 
 def test_zoned_full_config_sampled(dqa):
-    cfg = CONFIGS["c4"]
+    cfg = CONFIGS["mixed-width-zoned-16k"]
     inp = zoned_inputs(cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["d"], cfg["T_old"], cfg["C"], seed=4,
                        v_width_probs=cfg["v_width_probs"], k_width_probs=cfg["k_width_probs"],
                        outliers=cfg["outliers"])
-    say("zoned full c4")
+    say("zoned full mixed-width-zoned-16k")
     plan, blob = _run(dqa, inp, cfg["d"])
     scale = 1.0 / math.sqrt(cfg["d"])
     out = host(dqa.decode_attention_zoned(dev(inp["q"]), plan, blob, scale))
@@ -98,7 +98,7 @@ def test_zoned_full_config_sampled(dqa):
                                             sl(inp["v_bits"]), sl(inp["k_bits"]), sl(inp["k_new"]),
                                             sl(inp["v_new"]), scale)
         err = rel_l2(out[b, h * G:(h + 1) * G][None], ref)
-        print(f"c4 unit ({b},{h}) rel_l2={err:.3e}", flush=True)
+        print(f"mixed-width-zoned-16k unit ({b},{h}) rel_l2={err:.3e}", flush=True)
         assert err <= TOL
 
 

@@ -20,20 +20,20 @@ import numpy as np
 CONFIGS = {
     # tiny correctness case: one head, 256 quantized tokens, 2 fixed outlier
     # key channels scaled x50
-    "c1": dict(workload="tiny-kivi", kind="kivi", B=1, Hq=1, Hkv=1, d=64,
+    "tiny-kivi": dict(workload="tiny-kivi", seed=1, kind="kivi", B=1, Hq=1, Hkv=1, d=64,
                T_q=256, R=0, bits=(2,), rope_theta=0.0,
                outliers=("fixed", (5, 37), 50.0)),
     # Llama-2-13B-shaped layer: MHA, 4096 tokens, 4% outlier key channels
-    "c2": dict(workload="llama2-13b-decode-layer", kind="kivi", B=8, Hq=40,
+    "llama2-13b-decode-layer": dict(workload="llama2-13b-decode-layer", seed=2, kind="kivi", B=8, Hq=40,
                Hkv=40, d=128, T_q=4096, R=0, bits=(2,), rope_theta=0.0,
                outliers=("lognormal", 0.04, 3.0, 1.0)),
     # Llama-3.1-8B-shaped GQA decode: 32k quantized tokens + 128 fp16 recent
     # tokens, RoPE theta 5e5 applied to the dequantized pre-RoPE keys
-    "c3": dict(workload="llama3.1-8b-gqa-32k", kind="kivi", B=4, Hq=32,
+    "llama3.1-8b-gqa-32k": dict(workload="llama3.1-8b-gqa-32k", seed=3, kind="kivi", B=4, Hq=32,
                Hkv=8, d=128, T_q=32768, R=128, bits=(2, 4),
                rope_theta=500000.0, outliers=("lognormal", 0.04, 3.0, 1.0)),
     # mixed-width zoned cache: 16384 old tokens + 64 new fp16 tokens
-    "c4": dict(workload="mixed-width-zoned-16k", kind="zoned", B=2, Hq=32,
+    "mixed-width-zoned-16k": dict(workload="mixed-width-zoned-16k", seed=4, kind="zoned", B=2, Hq=32,
                Hkv=8, d=128, T_old=16384, C=64,
                v_width_probs={0: 0.5, 2: 0.2, 4: 0.15, 8: 0.1, 16: 0.05},
                k_width_probs={2: 0.4, 4: 0.3, 8: 0.2, 16: 0.1},
@@ -45,7 +45,7 @@ CONFIGS = {
                # plain layout: 4 sink tokens, one entry per key group
                zoned_variant=dict(sink=4, k_out=1)),
     # residual-VQ cache, Llama-3.2-3B shape: 4 codebooks x 1024 entries
-    "c5": dict(workload="rvq-llama3.2-3b-8k", kind="rvq", B=2, Hq=24, Hkv=8,
+    "rvq-llama3.2-3b-8k": dict(workload="rvq-llama3.2-3b-8k", seed=5, kind="rvq", B=2, Hq=24, Hkv=8,
                d=128, T=8192, N=4, Kc=1024),
 }
 
@@ -139,9 +139,9 @@ def rvq_inputs(B, Hq, Hkv, d, T, N, Kc, seed):
 
 
 def config_inputs(name, seed=None):
-    """Inputs of a named workload; the seed defaults to the config number."""
+    """Inputs of a named workload; the seed defaults to the workload's own."""
     cfg = CONFIGS[name]
-    seed = int(name[1:]) if seed is None else seed
+    seed = cfg["seed"] if seed is None else seed
     if cfg["kind"] == "kivi":
         return kivi_inputs(cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["d"], cfg["T_q"],
                            cfg["R"], seed, cfg["outliers"])
