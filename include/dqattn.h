@@ -56,7 +56,10 @@ enum {
 const char* dqa_status_string(int status);
 
 /* Version of this interface (increments on any signature or layout change). */
-int dqa_abi_version(void);  /* 6: zoned_plan takes a sink length and the
+int dqa_abi_version(void);  /* 7: quantize_pack_k/v and zoned_pack check
+                              16-byte alignment; kivi_append takes
+                              B <= 32767;
+                              6: zoned_plan takes a sink length and the
                               outlier entries per key group;
                               5: RDKV allocation entry points (rdkv_*);
                               4: dqa_kivi_cache carries buffer capacities
