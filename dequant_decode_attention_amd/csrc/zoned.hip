@@ -146,14 +146,32 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t* p, size_t n_wo
   for (; i < n_words; i += stride) p[i] = 0u;
 }
 
-// One workgroup (d threads) per (unit, group); the extra group index
-// `total_groups` copies zone C.
+// Codes of one value group (32 tokens' worth of one slot, W bits each) into
+// W words, fields from the low bits up.
+template <int W>
+__device__ __forceinline__ void pack_value_words(const float (&x)[kGroup], float mn, float sf, float rcp,
+                                                 uint32_t* dst) {
+  constexpr int per = 32 / W;
+  const float levels = static_cast<float>((1 << W) - 1);
+#pragma unroll
+  for (int i = 0; i < W; ++i) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int j = 0; j < per; ++j) word |= code_of(x[i * per + j], mn, sf, rcp, levels) << (j * W);
+    dst[i] = word;
+  }
+}
+
+// One workgroup (128 threads) per (unit, group); the extra group index
+// `total_groups` copies zone C.  Every global load of a group (its key rows
+// and this thread's value pieces) is issued at once, before any of the
+// group's arithmetic.
 __global__ __launch_bounds__(128) void zoned_pack_kernel(PackArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t lds_k[kGroup][128];   // the group's key rows (fp16, original order)
-  __shared__ uint8_t lds_c[kGroup][128];    // codes by permuted channel
+  __shared__ uint16_t lds_c[kGroup][128];   // by class position: codes, or raw fp16 bits of the 16-bit class
   __shared__ int lds_tok[kGroup];
-  __shared__ uint8_t lds_os[128][kMaxOutliers];   // removed slots per class position (0xFF: none)
-  __shared__ int lds_cnt[kGroup];
+  __shared__ unsigned long long lds_sm[2][kGroup];   // per wave: class positions whose outlier sits in slot s
+  __shared__ int lds_off[kGroup];
   const int d = a.d;
   const int unit = blockIdx.y;
   const int grp = blockIdx.x;
@@ -192,65 +210,125 @@ __global__ __launch_bounds__(128) void zoned_pack_kernel(PackArgs a) {
   const int n_valid = min(kGroup, n_seg - g * kGroup);
   uint8_t* gb = ub + U[U_SEG_OFF + seg] + static_cast<size_t>(g) * U[U_GRP_B + seg];
   if (tid < kGroup) lds_tok[tid] = tid < n_valid ? tokmap[U[U_TOK_PREFIX + seg] + g * kGroup + tid] : -1;
-  __syncthreads();
-  // 16-byte pieces of the key rows (d / 8 per row)
-  for (int e = tid; e < kGroup * (d / 8); e += blockDim.x) {
-    const int s = e / (d / 8), c8 = e % (d / 8);
-    uint4 u = uint4{0u, 0u, 0u, 0u};
-    if (lds_tok[s] >= 0) u = *reinterpret_cast<const uint4*>(a.k + src_unit + static_cast<size_t>(lds_tok[s]) * d + 8 * c8);
-    *reinterpret_cast<uint4*>(&lds_k[s][8 * c8]) = u;
-  }
+  const int pc = tid;                      // class position of this thread's key channel
+  const int ch = pc < d ? perm[pc] : 0;
   __syncthreads();
 
-  // ---- keys: thread = permuted channel position pc
-  const int m2 = U[U_M + 0], m4 = U[U_M + 1], m8 = U[U_M + 2];
-  const int n_kq = U[U_NKQ];
-  if (tid < d) {
-    const int pc = tid;
-    const int ch = perm[pc];
-    if (pc < n_kq) {
-      const int bits = pc < m2 ? 2 : (pc < m2 + m4 ? 4 : 8);
-      // outliers: slots taken out of this channel's group (bit s of `out`)
-      uint32_t out = 0u;
-      for (int i = 0; i < kMaxOutliers; ++i) lds_os[pc][i] = 0xFF;
-      for (int i = 0; i < a.k_out; ++i) {
-        int count = 0, hi = -1, lo = -1;
-        float total = 0.0f, vhi = -INFINITY, vlo = INFINITY;
-        for (int s = 0; s < n_valid; ++s) {
-          if (out >> s & 1u) continue;
-          const float x = h2f(lds_k[s][ch]);
-          total += x;                          // slot order, float32
-          ++count;
-          if (x > vhi) { vhi = x; hi = s; }    // first slot of the largest
-          if (x < vlo) { vlo = x; lo = s; }    // first slot of the smallest
-        }
-        if (count <= 2 || vhi == vlo) break;
-        const float mean = total / static_cast<float>(count);
-        const int pick = fabsf(vhi - mean) >= fabsf(vlo - mean) ? hi : lo;
-        out |= 1u << pick;
-        lds_os[pc][i] = static_cast<uint8_t>(pick);
+  // ---- loads: key rows in 16-byte pieces (piece e: slot e / pr, channels
+  // 8 (e % pr) ..), and either this thread's value group (code segments:
+  // slot tid / vpt, channels 32 (tid % vpt) ..) or zone-B pieces laid out
+  // like the key pieces.  Masked slots read row 0 and are zeroed below.
+  const int pr = d / 8;                    // pieces per row
+  const int kp = kGroup * pr;              // pieces per group: 128 i for i = 2 or 4
+  const int vpt = d / kGroup;              // value groups per slot
+  uint32_t kr[4][4] = {}, vr[4][4] = {};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (128 * i < kp) {
+      const int e = tid + 128 * i, s = e / pr;
+      const uint4 x = *reinterpret_cast<const uint4*>(a.k + src_unit + static_cast<size_t>(max(lds_tok[s], 0)) * d + 8 * (e % pr));
+      kr[i][0] = x.x; kr[i][1] = x.y; kr[i][2] = x.z; kr[i][3] = x.w;
+    }
+  }
+  if (w < 16) {
+    const int e = min(tid, d - 1), s = e / vpt;
+    const uint4* src = reinterpret_cast<const uint4*>(a.v + src_unit + static_cast<size_t>(max(lds_tok[s], 0)) * d +
+                                                      (e % vpt) * kGroup);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 x = src[i];
+      vr[i][0] = x.x; vr[i][1] = x.y; vr[i][2] = x.z; vr[i][3] = x.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (128 * i < kp) {
+        const int e = tid + 128 * i, s = e / pr;
+        const uint4 x = *reinterpret_cast<const uint4*>(a.v + src_unit + static_cast<size_t>(max(lds_tok[s], 0)) * d + 8 * (e % pr));
+        vr[i][0] = x.x; vr[i][1] = x.y; vr[i][2] = x.z; vr[i][3] = x.w;
       }
-      float mn = INFINITY, mx = -INFINITY;
-      for (int s = 0; s < n_valid; ++s) {
-        if (out >> s & 1u) continue;
-        const float x = h2f(lds_k[s][ch]);
-        mn = fminf(mn, x);
-        mx = fmaxf(mx, x);
-      }
-      const float levels = static_cast<float>((1 << bits) - 1);
-      const uint16_t s16 = f2h((mx - mn) / levels);
-      const float sf = h2f(s16), rcp = rcp_or_zero(sf);
-      uint16_t* ks = reinterpret_cast<uint16_t*>(gb + U[U_KCODES_B]);
-      uint16_t* kz = reinterpret_cast<uint16_t*>(gb + U[U_KCODES_B] + U[U_KSZ_B]);
-      ks[pc] = s16;
-      kz[pc] = f2h(mn);
-      for (int s = 0; s < kGroup; ++s)
-        lds_c[s][pc] = s < n_valid && !(out >> s & 1u)
-                           ? static_cast<uint8_t>(code_of(h2f(lds_k[s][ch]), mn, sf, rcp, levels)) : 0;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    asm volatile("" : "+v"(kr[i][0]), "+v"(kr[i][1]), "+v"(kr[i][2]), "+v"(kr[i][3]));
+    asm volatile("" : "+v"(vr[i][0]), "+v"(vr[i][1]), "+v"(vr[i][2]), "+v"(vr[i][3]));
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (128 * i < kp) {
+      const int e = tid + 128 * i, s = e / pr;
+      const bool keep = lds_tok[s] >= 0;
+      *reinterpret_cast<uint4*>(&lds_k[s][8 * (e % pr)]) =
+          keep ? uint4{kr[i][0], kr[i][1], kr[i][2], kr[i][3]} : uint4{0u, 0u, 0u, 0u};
     }
   }
   __syncthreads();
-  // side list: thread s gathers the entries of slot s in class-position order
+
+  // ---- keys: thread = class position pc (rows of masked slots are zero)
+  const int m2 = U[U_M + 0], m4 = U[U_M + 1], m8 = U[U_M + 2];
+  const int n_kq = U[U_NKQ];
+  const uint32_t valid = n_valid >= kGroup ? 0xFFFFFFFFu : ((1u << n_valid) - 1u);
+  uint32_t out = 0u;                       // slots moved to the side list (bit s)
+  if (pc < n_kq) {
+    const int bits = pc < m2 ? 2 : (pc < m2 + m4 ? 4 : 8);
+    float x[kGroup];
+#pragma unroll
+    for (int s = 0; s < kGroup; ++s) x[s] = h2f(lds_k[s][ch]);
+    // outliers: each round takes the live slot farthest from the live mean
+    // (the first slot of the largest or of the smallest value)
+    for (int i = 0; i < a.k_out; ++i) {
+      const uint32_t live = valid & ~out;
+      float sum = 0.0f, vhi = -INFINITY, vlo = INFINITY;
+      int hi = -1, lo = -1;
+#pragma unroll
+      for (int s = 0; s < kGroup; ++s) {
+        if (live >> s & 1u) {
+          sum += x[s];                         // slot order, float32
+          if (x[s] > vhi) { vhi = x[s]; hi = s; }
+          if (x[s] < vlo) { vlo = x[s]; lo = s; }
+        }
+      }
+      const int count = __builtin_popcount(live);
+      if (count <= 2 || vhi == vlo || hi < 0 || lo < 0) break;
+      const float mean = sum / static_cast<float>(count);
+      out |= 1u << (fabsf(vhi - mean) >= fabsf(vlo - mean) ? hi : lo);
+    }
+    const uint32_t live = valid & ~out;
+    float mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < kGroup; ++s) {
+      if (live >> s & 1u) {
+        mn = fminf(mn, x[s]);
+        mx = fmaxf(mx, x[s]);
+      }
+    }
+    const float levels = static_cast<float>((1 << bits) - 1);
+    const uint16_t s16 = f2h((mx - mn) / levels);
+    const float sf = h2f(s16), rcp = rcp_or_zero(sf);
+    uint16_t* ks = reinterpret_cast<uint16_t*>(gb + U[U_KCODES_B]);
+    uint16_t* kz = reinterpret_cast<uint16_t*>(gb + U[U_KCODES_B] + U[U_KSZ_B]);
+    ks[pc] = s16;
+    kz[pc] = f2h(mn);
+#pragma unroll
+    for (int s = 0; s < kGroup; ++s)
+      lds_c[s][pc] = live >> s & 1u ? static_cast<uint16_t>(code_of(x[s], mn, sf, rcp, levels)) : 0;
+  } else if (pc < d) {
+#pragma unroll
+    for (int s = 0; s < kGroup; ++s) lds_c[s][pc] = lds_k[s][ch];
+  }
+  if (a.k_out > 0) {
+    // slot s's entries, in class-position order: wave-wide masks of the
+    // positions that moved slot s
+    const int lane = tid & 63, wv = tid >> 6;
+#pragma unroll
+    for (int s = 0; s < kGroup; ++s) {
+      const unsigned long long m = __ballot(out >> s & 1u);
+      if (lane == s) lds_sm[wv][s] = m;
+    }
+  }
+  __syncthreads();
+  // side list: slot offsets, then each position writes its own entries
   if (a.k_out > 0) {
     const int cap = n_kq * a.k_out;
     uint8_t* ob = gb + U[U_KCODES_B] + 2 * U[U_KSZ_B];
@@ -258,120 +336,97 @@ __global__ __launch_bounds__(128) void zoned_pack_kernel(PackArgs a) {
     uint16_t* opc = reinterpret_cast<uint16_t*>(ob + kOffsBytes);
     uint16_t* oval = reinterpret_cast<uint16_t*>(ob + kOffsBytes + pad(static_cast<size_t>(cap) * 2, 16));
     if (tid < kGroup) {
-      int n = 0;
-      for (int pc = 0; pc < n_kq; ++pc)
-        for (int i = 0; i < a.k_out; ++i) n += lds_os[pc][i] == tid;
-      lds_cnt[tid] = n;
+      int o = 0;
+#pragma unroll
+      for (int s = 0; s < kGroup; ++s)
+        if (s < tid) o += __popcll(lds_sm[0][s]) + __popcll(lds_sm[1][s]);
+      lds_off[tid] = o;
+      offs[tid] = static_cast<uint16_t>(o);
+      if (tid == kGroup - 1) offs[kGroup] = static_cast<uint16_t>(o + __popcll(lds_sm[0][tid]) + __popcll(lds_sm[1][tid]));
     }
     __syncthreads();
-    if (tid < kGroup) {
-      int o = 0;
-      for (int s = 0; s < tid; ++s) o += lds_cnt[s];
-      offs[tid] = static_cast<uint16_t>(o);
-      if (tid == kGroup - 1) offs[kGroup] = static_cast<uint16_t>(o + lds_cnt[tid]);
-      for (int pc = 0; pc < n_kq; ++pc)
-        for (int i = 0; i < a.k_out; ++i)
-          if (lds_os[pc][i] == tid) {
-            opc[o] = static_cast<uint16_t>(pc);
-            oval[o] = lds_k[tid][perm[pc]];
-            ++o;
-          }
+    const int wv = tid >> 6;
+    for (uint32_t rest = out; rest != 0u; rest &= rest - 1u) {
+      const int s = __builtin_ctz(rest);
+      const unsigned long long m = lds_sm[wv][s];
+      const int rank = static_cast<int>(__builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                            __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u))) +
+                       (wv ? __popcll(lds_sm[0][s]) : 0);
+      const int o = lds_off[s] + rank;
+      opc[o] = static_cast<uint16_t>(pc);
+      oval[o] = lds_k[s][ch];
     }
   }
-  // key rows: word (slot, wi) of each class block
+  // key rows: word (slot, wi) of each class block, fields from lds_c
   const int kw2 = U[U_KWORDS + 0], kw4 = U[U_KWORDS + 1], kw8 = U[U_KWORDS + 2];
   const int W_K = U[U_WK];
   uint32_t* krow = reinterpret_cast<uint32_t*>(gb);
   for (int e = tid; e < kGroup * W_K; e += blockDim.x) {
     const int s = e / W_K, wi = e % W_K;
+    int cls_bits, first, count, wl;
+    if (wi < kw2) { cls_bits = 2; first = 0; count = m2; wl = wi; }
+    else if (wi < kw2 + kw4) { cls_bits = 4; first = m2; count = m4; wl = wi - kw2; }
+    else if (wi < kw2 + kw4 + kw8) { cls_bits = 8; first = m2 + m4; count = m8; wl = wi - kw2 - kw4; }
+    else { cls_bits = 16; first = n_kq; count = U[U_M + 3]; wl = wi - kw2 - kw4 - kw8; }
+    const int per = 32 / cls_bits;
     uint32_t word = 0;
-    if (s < n_valid) {
-      int cls_bits, first, count, wl;
-      if (wi < kw2) { cls_bits = 2; first = 0; count = m2; wl = wi; }
-      else if (wi < kw2 + kw4) { cls_bits = 4; first = m2; count = m4; wl = wi - kw2; }
-      else if (wi < kw2 + kw4 + kw8) { cls_bits = 8; first = m2 + m4; count = m8; wl = wi - kw2 - kw4; }
-      else { cls_bits = 16; first = n_kq; count = U[U_M + 3]; wl = wi - kw2 - kw4 - kw8; }
-      const int per = 32 / cls_bits;
-      for (int j = 0; j < per; ++j) {
-        const int idx = wl * per + j;
-        if (idx >= count) break;
-        const int pc = first + idx;
-        const uint32_t field = cls_bits == 16 ? static_cast<uint32_t>(lds_k[s][perm[pc]])
-                                              : static_cast<uint32_t>(lds_c[s][pc]);
-        word |= field << (j * cls_bits);
-      }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int idx = wl * per + j;
+      if (j < per && idx < count) word |= static_cast<uint32_t>(lds_c[s][first + idx]) << (j * cls_bits);
     }
     krow[e] = word;
   }
 
   // ---- values
   if (w < 16) {
-    const int vwpt = d * w / 32;                 // value words per slot
-    uint8_t* vbase = gb + U[U_KCODES_B] + 2 * U[U_KSZ_B] + U[U_OUT_B];
-    uint32_t* vcodes = reinterpret_cast<uint32_t*>(vbase);
-    const size_t vsz_b = pad(static_cast<size_t>(kGroup) * (d / kGroup) * 2, 16);
-    uint16_t* vs = reinterpret_cast<uint16_t*>(vbase + kGroup * vwpt * 4);
-    uint16_t* vz = reinterpret_cast<uint16_t*>(vbase + kGroup * vwpt * 4 + vsz_b);
-    for (int e = tid; e < kGroup * (d / kGroup); e += blockDim.x) {
-      const int s = e / (d / kGroup), vg = e % (d / kGroup);
+    if (tid < d) {                              // value group (slot s, vg)
+      const int vwpt = d * w / 32;              // value words per slot
+      uint8_t* vbase = gb + U[U_KCODES_B] + 2 * U[U_KSZ_B] + U[U_OUT_B];
+      uint32_t* vcodes = reinterpret_cast<uint32_t*>(vbase);
+      const size_t vsz_b = pad(static_cast<size_t>(kGroup) * vpt * 2, 16);
+      uint16_t* vs = reinterpret_cast<uint16_t*>(vbase + kGroup * vwpt * 4);
+      uint16_t* vz = reinterpret_cast<uint16_t*>(vbase + kGroup * vwpt * 4 + vsz_b);
+      const int e = tid, s = e / vpt, vg = e % vpt;
       uint32_t* dst = vcodes + s * vwpt + vg * w;
       if (s >= n_valid) {
         for (int i = 0; i < w; ++i) dst[i] = 0u;
         vs[e] = 0;
         vz[e] = 0;
-        continue;
-      }
-      const uint4* src = reinterpret_cast<const uint4*>(a.v + src_unit + static_cast<size_t>(lds_tok[s]) * d + vg * kGroup);
-      float x[kGroup];
-      float mn = INFINITY, mx = -INFINITY;
+      } else {
+        float x[kGroup];
+        float mn = INFINITY, mx = -INFINITY;
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const uint4 u = src[q4];
-        const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+        for (int q4 = 0; q4 < 4; ++q4)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          x[8 * q4 + 2 * j] = h2f(static_cast<uint16_t>(wd[j] & 0xFFFFu));
-          x[8 * q4 + 2 * j + 1] = h2f(static_cast<uint16_t>(wd[j] >> 16));
+          for (int j = 0; j < 4; ++j) {
+            x[8 * q4 + 2 * j] = h2f(static_cast<uint16_t>(vr[q4][j] & 0xFFFFu));
+            x[8 * q4 + 2 * j + 1] = h2f(static_cast<uint16_t>(vr[q4][j] >> 16));
+          }
+#pragma unroll
+        for (int i = 0; i < kGroup; ++i) {
+          mn = fminf(mn, x[i]);
+          mx = fmaxf(mx, x[i]);
         }
-      }
-#pragma unroll
-      for (int i = 0; i < kGroup; ++i) {
-        mn = fminf(mn, x[i]);
-        mx = fmaxf(mx, x[i]);
-      }
-      const float levels = static_cast<float>((1 << w) - 1);
-      const uint16_t s16 = f2h((mx - mn) / levels);
-      const float sf = h2f(s16), rcp = rcp_or_zero(sf);
-      vs[e] = s16;
-      vz[e] = f2h(mn);
-      const int per = 32 / w;
-      for (int i = 0; i < w; ++i) {
-        uint32_t word = 0;
-        for (int j = 0; j < per; ++j) word |= code_of(x[i * per + j], mn, sf, rcp, levels) << (j * w);
-        dst[i] = word;
+        const float levels = static_cast<float>((1 << w) - 1);
+        const uint16_t s16 = f2h((mx - mn) / levels);
+        const float sf = h2f(s16), rcp = rcp_or_zero(sf);
+        vs[e] = s16;
+        vz[e] = f2h(mn);
+        if (w == 2) pack_value_words<2>(x, mn, sf, rcp, dst);
+        else if (w == 4) pack_value_words<4>(x, mn, sf, rcp, dst);
+        else pack_value_words<8>(x, mn, sf, rcp, dst);
       }
     }
   } else {
-    // zone B rows of this group's slots, 16-byte pieces, four in flight
-    uint16_t* zb = reinterpret_cast<uint16_t*>(ub + U[U_ZB]) + static_cast<size_t>(g) * kGroup * d;
-    const int pr = d / 8;                        // pieces per row
-    for (int e0 = tid; e0 < kGroup * pr; e0 += 4 * 128) {
-      uint32_t u[4][4];
+    // zone B rows of this group's slots (masked slots store zeros)
+    uint4* zb = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(ub + U[U_ZB]) + static_cast<size_t>(g) * kGroup * d);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int e = min(e0 + 128 * i, kGroup * pr - 1), s = e / pr, c8 = e % pr;
-        const int tok = lds_tok[s] >= 0 ? lds_tok[s] : 0;    // masked slots read row 0 and store zeros
-        const uint4 x = *reinterpret_cast<const uint4*>(a.v + src_unit + static_cast<size_t>(tok) * d + 8 * c8);
-        const bool keep = lds_tok[s] >= 0;
-        u[i][0] = keep ? x.x : 0u;
-        u[i][1] = keep ? x.y : 0u;
-        u[i][2] = keep ? x.z : 0u;
-        u[i][3] = keep ? x.w : 0u;
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int e = e0 + 128 * i;
-        if (e < kGroup * pr) reinterpret_cast<uint4*>(zb)[e] = uint4{u[i][0], u[i][1], u[i][2], u[i][3]};
+    for (int i = 0; i < 4; ++i) {
+      if (128 * i < kp) {
+        const int e = tid + 128 * i;
+        const bool keep = lds_tok[e / pr] >= 0;
+        zb[e] = keep ? uint4{vr[i][0], vr[i][1], vr[i][2], vr[i][3]} : uint4{0u, 0u, 0u, 0u};
       }
     }
   }
