@@ -289,12 +289,20 @@ def zoned_plan(v_bits, k_bits, C_new, d, device, sink=0, k_out=0):
     return ZonedPlan(words, blob.value, device)
 
 
-def zoned_pack(plan, k, v, k_new=None, v_new=None):
-    """Pack fp16 caches into a uint8 blob of plan.blob_bytes bytes."""
+def zoned_pack(plan, k, v, k_new=None, v_new=None, out=None):
+    """Pack fp16 caches into a uint8 blob of plan.blob_bytes bytes (every
+    byte written; `out`, if given, is a uint8 device tensor of that size)."""
     k, v = _dev16(k, "k"), _dev16(v, "v")
     k_new = None if k_new is None else _dev16(k_new, "k_new")
     v_new = None if v_new is None else _dev16(v_new, "v_new")
-    blob = torch.empty(plan.blob_bytes, dtype=torch.uint8, device=k.device)
+    if out is None:
+        blob = torch.empty(plan.blob_bytes, dtype=torch.uint8, device=k.device)
+    else:
+        if out.dtype != torch.uint8 or out.numel() != plan.blob_bytes or not out.is_contiguous() \
+                or out.device != k.device:
+            raise ValueError(f"zoned_pack: out must be a contiguous uint8 tensor of {plan.blob_bytes} "
+                             f"bytes on {k.device}")
+        blob = out
     _check("zoned_pack", lib.zoned_pack(plan.host_ptr(), _ptr(plan.dev), _ptr(k), _ptr(v),
                                         _ptr(k_new), _ptr(v_new), _ptr(blob), _stream(k.device)))
     return blob

@@ -139,13 +139,6 @@ __device__ __forceinline__ void copy16(uint16_t* dst, const uint16_t* src, size_
   }
 }
 
-// Zero-fill (the blob's padding bytes are defined as zero).
-__global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t* p, size_t n_words) {
-  size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
-  for (; i < n_words; i += stride) p[i] = 0u;
-}
-
 // Codes of one value group (32 tokens' worth of one slot, W bits each) into
 // W words, fields from the low bits up.
 template <int W>
@@ -171,7 +164,7 @@ __global__ __launch_bounds__(128) void zoned_pack_kernel(PackArgs a) {
   __shared__ uint16_t lds_c[kGroup][128];   // by class position: codes, or raw fp16 bits of the 16-bit class
   __shared__ int lds_tok[kGroup];
   __shared__ unsigned long long lds_sm[2][kGroup];   // per wave: class positions whose outlier sits in slot s
-  __shared__ int lds_off[kGroup];
+  __shared__ int lds_off[kGroup + 1];      // slot offsets in the side list, then its entry count
   const int d = a.d;
   const int unit = blockIdx.y;
   const int grp = blockIdx.x;
@@ -197,6 +190,10 @@ __global__ __launch_bounds__(128) void zoned_pack_kernel(PackArgs a) {
     copy16(zc + n, a.v + src_unit, ns / 8, tid);
     copy16(zc + ns, a.k_new + src, (n - ns) / 8, tid);
     copy16(zc + n + ns, a.v_new + src, (n - ns) / 8, tid);
+    // the unit's tail padding (every block is a multiple of 16 bytes)
+    const size_t end = static_cast<size_t>(U[U_ZC]) + 4 * n;
+    const int tail16 = static_cast<int>((static_cast<size_t>(U[U_SIZE]) - end) / 16);
+    if (tid < tail16) reinterpret_cast<uint4*>(ub + end)[tid] = uint4{0u, 0u, 0u, 0u};
     return;
   }
   // locate the segment of this group
@@ -270,6 +267,12 @@ __global__ __launch_bounds__(128) void zoned_pack_kernel(PackArgs a) {
   const int n_kq = U[U_NKQ];
   const uint32_t valid = n_valid >= kGroup ? 0xFFFFFFFFu : ((1u << n_valid) - 1u);
   uint32_t out = 0u;                       // slots moved to the side list (bit s)
+  uint16_t* ks = reinterpret_cast<uint16_t*>(gb + U[U_KCODES_B]);
+  uint16_t* kz = reinterpret_cast<uint16_t*>(gb + U[U_KCODES_B] + U[U_KSZ_B]);
+  if (pc >= n_kq && pc < U[U_KSZ_B] / 2) {   // padding of the scale and zero blocks
+    ks[pc] = 0;
+    kz[pc] = 0;
+  }
   if (pc < n_kq) {
     const int bits = pc < m2 ? 2 : (pc < m2 + m4 ? 4 : 8);
     float x[kGroup];
@@ -306,8 +309,6 @@ __global__ __launch_bounds__(128) void zoned_pack_kernel(PackArgs a) {
     const float levels = static_cast<float>((1 << bits) - 1);
     const uint16_t s16 = f2h((mx - mn) / levels);
     const float sf = h2f(s16), rcp = rcp_or_zero(sf);
-    uint16_t* ks = reinterpret_cast<uint16_t*>(gb + U[U_KCODES_B]);
-    uint16_t* kz = reinterpret_cast<uint16_t*>(gb + U[U_KCODES_B] + U[U_KSZ_B]);
     ks[pc] = s16;
     kz[pc] = f2h(mn);
 #pragma unroll
@@ -342,9 +343,20 @@ __global__ __launch_bounds__(128) void zoned_pack_kernel(PackArgs a) {
         if (s < tid) o += __popcll(lds_sm[0][s]) + __popcll(lds_sm[1][s]);
       lds_off[tid] = o;
       offs[tid] = static_cast<uint16_t>(o);
-      if (tid == kGroup - 1) offs[kGroup] = static_cast<uint16_t>(o + __popcll(lds_sm[0][tid]) + __popcll(lds_sm[1][tid]));
+      if (tid == kGroup - 1) {
+        lds_off[kGroup] = o + __popcll(lds_sm[0][tid]) + __popcll(lds_sm[1][tid]);
+        offs[kGroup] = static_cast<uint16_t>(lds_off[kGroup]);
+      }
+    } else if (tid > kGroup && tid < kOffsBytes / 2) {
+      offs[tid] = 0;                             // padding after the 33 offsets
     }
     __syncthreads();
+    // unused entries up to the padded capacity are zero
+    const int cap16 = static_cast<int>(pad(static_cast<size_t>(cap) * 2, 16) / 2);
+    for (int i = lds_off[kGroup] + tid; i < cap16; i += blockDim.x) {
+      opc[i] = 0;
+      oval[i] = 0;
+    }
     const int wv = tid >> 6;
     for (uint32_t rest = out; rest != 0u; rest &= rest - 1u) {
       const int s = __builtin_ctz(rest);
@@ -1068,12 +1080,6 @@ extern "C" int zoned_pack(const int32_t* plan_host, const int32_t* plan_dev, con
   if (!aligned16(k) || !aligned16(v) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(blob))
     return DQA_ERR_ALIGN;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const size_t n_words = blob_bytes / 4;
-  size_t fb = (n_words + 255) / 256;
-  if (fb > 16384) fb = 16384;
-  hipLaunchKernelGGL(fill_zero_kernel, dim3(static_cast<unsigned>(fb)), dim3(256), 0, s,
-                     static_cast<uint32_t*>(blob), n_words);
-  DQA_CHECK_LAUNCH();
   PackArgs a{plan_dev, k, v, k_new, v_new, static_cast<uint8_t*>(blob), plan_host[H_TOLD],
              plan_host[H_C], plan_host[H_D], plan_host[H_SINK], plan_host[H_KOUT]};
   const dim3 grid(plan_host[H_MAX_GROUPS] + 1, units);

@@ -25,11 +25,17 @@ def dqa():
     return m
 
 
+def _marked_blob(plan):
+    """A blob buffer pre-filled with 0xA5, so that a byte the packer leaves
+    unwritten differs from the oracle's image (whose padding is zero)."""
+    return torch.full((plan.blob_bytes,), 0xA5, dtype=torch.uint8, device="cuda:0")
+
+
 def _run(dqa, inp, d):
     plan = dqa.zoned_plan(inp["v_bits"], inp["k_bits"], inp["k_new"].shape[2], d, "cuda:0")
     blob = dqa.zoned_pack(plan, dev(inp["k"]), dev(inp["v"]),
                           dev(inp["k_new"]) if inp["k_new"].shape[2] else None,
-                          dev(inp["v_new"]) if inp["v_new"].shape[2] else None)
+                          dev(inp["v_new"]) if inp["v_new"].shape[2] else None, out=_marked_blob(plan))
     return plan, blob
 
 
@@ -130,7 +136,8 @@ def test_zoned_sink_and_outliers(dqa, case):
     say("zoned sink/outliers", case[:8])
     plan = dqa.zoned_plan(inp["v_bits"], inp["k_bits"], C, d, "cuda:0", sink=S, k_out=ko)
     blob = dqa.zoned_pack(plan, dev(inp["k"]), dev(inp["v"]),
-                          dev(inp["k_new"]) if C else None, dev(inp["v_new"]) if C else None)
+                          dev(inp["k_new"]) if C else None, dev(inp["v_new"]) if C else None,
+                          out=_marked_blob(plan))
     ref_blob = oracle.zoned_pack(inp["k"], inp["v"], inp["v_bits"], inp["k_bits"], inp["k_new"],
                                  inp["v_new"], sink=S, k_out=ko)
     got_blob = host(blob)
