@@ -139,10 +139,45 @@ __device__ __forceinline__ void copy16(uint16_t* dst, const uint16_t* src, size_
   }
 }
 
-// Codes of one value group (32 tokens' worth of one slot, W bits each) into
-// W words, fields from the low bits up.
+// Packed fp16 min / max of two words (both halves at once), and min / max of
+// the two halves of one word (in both halves of the result).
+__device__ __forceinline__ uint32_t pk_min_h2(uint32_t a, uint32_t b) {
+  uint32_t r;
+  asm("v_pk_min_f16 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ uint32_t pk_max_h2(uint32_t a, uint32_t b) {
+  uint32_t r;
+  asm("v_pk_max_f16 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ uint32_t pk_min_halves(uint32_t w) {
+  uint32_t r;
+  asm("v_pk_min_f16 %0, %1, %1 op_sel:[1,0] op_sel_hi:[0,1]" : "=v"(r) : "v"(w));
+  return r;
+}
+__device__ __forceinline__ uint32_t pk_max_halves(uint32_t w) {
+  uint32_t r;
+  asm("v_pk_max_f16 %0, %1, %1 op_sel:[1,0] op_sel_hi:[0,1]" : "=v"(r) : "v"(w));
+  return r;
+}
+// x - z for the fp16 value in half H of word w, by one mixed-precision FMA
+// (x * 1 - z, one rounding): the fp32 subtraction of the widened value.
+template <int H>
+__device__ __forceinline__ float minus_zero(uint32_t w, float zf) {
+  float r;
+  if constexpr (H == 0)
+    asm("v_fma_mix_f32 %0, %1, 1.0, -%2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(w), "v"(zf));
+  else
+    asm("v_fma_mix_f32 %0, %1, 1.0, -%2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(w), "v"(zf));
+  return r;
+}
+
+// Value codes of one slot's value group (32 channels, fp16 pairs in v[16])
+// into W words, fields from the low bits up; code_of's arithmetic with the
+// subtraction done by minus_zero.
 template <int W>
-__device__ __forceinline__ void pack_value_words(const float (&x)[kGroup], float mn, float sf, float rcp,
+__device__ __forceinline__ void pack_value_words(const uint32_t (&v)[16], float zf, float sf, float rcp,
                                                  uint32_t* dst) {
   constexpr int per = 32 / W;
   const float levels = static_cast<float>((1 << W) - 1);
@@ -150,8 +185,38 @@ __device__ __forceinline__ void pack_value_words(const float (&x)[kGroup], float
   for (int i = 0; i < W; ++i) {
     uint32_t word = 0;
 #pragma unroll
-    for (int j = 0; j < per; ++j) word |= code_of(x[i * per + j], mn, sf, rcp, levels) << (j * W);
+    for (int j = 0; j < per; ++j) {
+      const int e = i * per + j;
+      const float t = (e & 1) ? minus_zero<1>(v[e >> 1], zf) : minus_zero<0>(v[e >> 1], zf);
+      const float y = t * rcp;
+      float q = rintf(y);
+      if (__builtin_expect(__builtin_fabsf(y - q) >= 0.499755859375f, 0) && sf != 0.0f) q = rintf(t / sf);
+      word |= static_cast<uint32_t>(__builtin_amdgcn_fmed3f(q, 0.0f, levels)) << (j * W);
+    }
     dst[i] = word;
+  }
+}
+
+constexpr int kCodeStride = 130;   // lds_c row stride (halves): a column read by slot hits distinct banks
+
+// Key words of one width class: word wl of slot s packs class positions
+// first + wl per .. (per = 32 / BITS), read from lds_c; written to the
+// slot-major word rows in LDS (row stride ws).  Thread = (slot, word) with
+// the slot fastest, so a column read touches 32 distinct banks.
+template <int BITS>
+__device__ __forceinline__ void pack_key_class(uint32_t* lds_w, int ws, int col, int first, int count, int nw,
+                                               const uint16_t (*lds_c)[kCodeStride], int tid) {
+  constexpr int per = 32 / BITS;
+  for (int e = tid; e < kGroup * nw; e += 128) {
+    const int s = e & (kGroup - 1), wl = e >> 5;
+    uint32_t word = 0;
+#pragma unroll
+    for (int j = 0; j < per; ++j) {
+      const int idx = wl * per + j;
+      const uint32_t f = lds_c[s][min(first + idx, 127)];
+      word |= (idx < count ? f : 0u) << (j * BITS);
+    }
+    lds_w[s * ws + col + wl] = word;
   }
 }
 
@@ -159,31 +224,37 @@ __device__ __forceinline__ void pack_value_words(const float (&x)[kGroup], float
 // `total_groups` copies zone C.  Every global load of a group (its key rows
 // and this thread's value pieces) is issued at once, before any of the
 // group's arithmetic.
+template <int D>
 __global__ __launch_bounds__(128) void zoned_pack_kernel(PackArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds_k[kGroup][128];   // the group's key rows (fp16, original order)
-  __shared__ uint16_t lds_c[kGroup][128];   // by class position: codes, or raw fp16 bits of the 16-bit class
+  constexpr int kPR = D / 8;                   // 16-byte pieces per row
+  constexpr int kKP = kGroup * kPR / 128;      // key (and zone-B) pieces per thread
+  constexpr int kVPT = D / kGroup;             // value groups per slot
+  // the group's key rows (fp16, row stride D); after the side list, the
+  // packed key words (row stride W_K | 1)
+  __shared__ __attribute__((aligned(16))) uint32_t lds_kw[kGroup * (D / 2 + 1)];
+  __shared__ uint16_t lds_c[kGroup][kCodeStride];   // by class position: codes, or raw fp16 bits of the 16-bit class
   __shared__ int lds_tok[kGroup];
-  __shared__ unsigned long long lds_sm[2][kGroup];   // per wave: class positions whose outlier sits in slot s
-  __shared__ int lds_off[kGroup + 1];      // slot offsets in the side list, then its entry count
-  const int d = a.d;
+  __shared__ unsigned long long lds_sm[2][kGroup];  // per wave: class positions whose outlier sits in slot s
+  __shared__ int lds_off[kGroup + 1];               // slot offsets in the side list, then its entry count
+  uint16_t (*lds_k)[D] = reinterpret_cast<uint16_t (*)[D]>(lds_kw);
   const int unit = blockIdx.y;
   const int grp = blockIdx.x;
   const int tid = threadIdx.x;
   const int32_t* P = a.plan;
   const int32_t* U = P + P[H_UNIT_OFF] + unit * kUnitWords;
-  const int32_t* perm = P + P[H_PERM_OFF] + unit * d;
+  const int32_t* perm = P + P[H_PERM_OFF] + unit * D;
   const int32_t* tokmap = P + P[H_TOK_OFF] + unit * a.T_old;
   const size_t base = static_cast<size_t>(static_cast<uint32_t>(U[U_BASE_LO])) |
                       (static_cast<size_t>(static_cast<uint32_t>(U[U_BASE_HI])) << 32);
   uint8_t* ub = a.blob + base;
-  const size_t src_unit = static_cast<size_t>(unit) * a.T_old * d;
+  const size_t src_unit = static_cast<size_t>(unit) * a.T_old * D;
   const int total = U[U_TOTAL_GROUPS];
   if (grp > total) return;
   if (grp == total) {                      // zone C: fp16 copies, sink tokens first
     uint16_t* zc = reinterpret_cast<uint16_t*>(ub + U[U_ZC]);
-    const size_t ns = static_cast<size_t>(a.sink) * d;
-    const size_t n = ns + static_cast<size_t>(a.C) * d;
-    const size_t src = static_cast<size_t>(unit) * a.C * d;
+    const size_t ns = static_cast<size_t>(a.sink) * D;
+    const size_t n = ns + static_cast<size_t>(a.C) * D;
+    const size_t src = static_cast<size_t>(unit) * a.C * D;
     // 16-byte pieces (rows are multiples of 16 bytes, every block 16-byte
     // aligned), four loads in flight per thread
     copy16(zc, a.k + src_unit, ns / 8, tid);
@@ -208,29 +279,25 @@ __global__ __launch_bounds__(128) void zoned_pack_kernel(PackArgs a) {
   uint8_t* gb = ub + U[U_SEG_OFF + seg] + static_cast<size_t>(g) * U[U_GRP_B + seg];
   if (tid < kGroup) lds_tok[tid] = tid < n_valid ? tokmap[U[U_TOK_PREFIX + seg] + g * kGroup + tid] : -1;
   const int pc = tid;                      // class position of this thread's key channel
-  const int ch = pc < d ? perm[pc] : 0;
+  const int ch = pc < D ? perm[pc] : 0;
   __syncthreads();
 
-  // ---- loads: key rows in 16-byte pieces (piece e: slot e / pr, channels
-  // 8 (e % pr) ..), and either this thread's value group (code segments:
-  // slot tid / vpt, channels 32 (tid % vpt) ..) or zone-B pieces laid out
+  // ---- loads: key rows in 16-byte pieces (piece e: slot e / kPR, channels
+  // 8 (e % kPR) ..), and either this thread's value group (code segments:
+  // slot tid / kVPT, channels 32 (tid % kVPT) ..) or zone-B pieces laid out
   // like the key pieces.  Masked slots read row 0 and are zeroed below.
-  const int pr = d / 8;                    // pieces per row
-  const int kp = kGroup * pr;              // pieces per group: 128 i for i = 2 or 4
-  const int vpt = d / kGroup;              // value groups per slot
-  uint32_t kr[4][4] = {}, vr[4][4] = {};
+  uint32_t kr[kKP][4], vr[4][4] = {};
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if (128 * i < kp) {
-      const int e = tid + 128 * i, s = e / pr;
-      const uint4 x = *reinterpret_cast<const uint4*>(a.k + src_unit + static_cast<size_t>(max(lds_tok[s], 0)) * d + 8 * (e % pr));
-      kr[i][0] = x.x; kr[i][1] = x.y; kr[i][2] = x.z; kr[i][3] = x.w;
-    }
+  for (int i = 0; i < kKP; ++i) {
+    const int e = tid + 128 * i, s = e / kPR;
+    const uint4 x = *reinterpret_cast<const uint4*>(a.k + src_unit + static_cast<size_t>(max(lds_tok[s], 0)) * D +
+                                                    8 * (e % kPR));
+    kr[i][0] = x.x; kr[i][1] = x.y; kr[i][2] = x.z; kr[i][3] = x.w;
   }
   if (w < 16) {
-    const int e = min(tid, d - 1), s = e / vpt;
-    const uint4* src = reinterpret_cast<const uint4*>(a.v + src_unit + static_cast<size_t>(max(lds_tok[s], 0)) * d +
-                                                      (e % vpt) * kGroup);
+    const int e = min(tid, D - 1), s = e / kVPT;
+    const uint4* src = reinterpret_cast<const uint4*>(a.v + src_unit + static_cast<size_t>(max(lds_tok[s], 0)) * D +
+                                                      (e % kVPT) * kGroup);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint4 x = src[i];
@@ -238,27 +305,23 @@ __global__ __launch_bounds__(128) void zoned_pack_kernel(PackArgs a) {
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (128 * i < kp) {
-        const int e = tid + 128 * i, s = e / pr;
-        const uint4 x = *reinterpret_cast<const uint4*>(a.v + src_unit + static_cast<size_t>(max(lds_tok[s], 0)) * d + 8 * (e % pr));
-        vr[i][0] = x.x; vr[i][1] = x.y; vr[i][2] = x.z; vr[i][3] = x.w;
-      }
+    for (int i = 0; i < kKP; ++i) {
+      const int e = tid + 128 * i, s = e / kPR;
+      const uint4 x = *reinterpret_cast<const uint4*>(a.v + src_unit + static_cast<size_t>(max(lds_tok[s], 0)) * D +
+                                                      8 * (e % kPR));
+      vr[i][0] = x.x; vr[i][1] = x.y; vr[i][2] = x.z; vr[i][3] = x.w;
     }
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    asm volatile("" : "+v"(kr[i][0]), "+v"(kr[i][1]), "+v"(kr[i][2]), "+v"(kr[i][3]));
-    asm volatile("" : "+v"(vr[i][0]), "+v"(vr[i][1]), "+v"(vr[i][2]), "+v"(vr[i][3]));
-  }
+  for (int i = 0; i < kKP; ++i) asm volatile("" : "+v"(kr[i][0]), "+v"(kr[i][1]), "+v"(kr[i][2]), "+v"(kr[i][3]));
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if (128 * i < kp) {
-      const int e = tid + 128 * i, s = e / pr;
-      const bool keep = lds_tok[s] >= 0;
-      *reinterpret_cast<uint4*>(&lds_k[s][8 * (e % pr)]) =
-          keep ? uint4{kr[i][0], kr[i][1], kr[i][2], kr[i][3]} : uint4{0u, 0u, 0u, 0u};
-    }
+  for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(vr[i][0]), "+v"(vr[i][1]), "+v"(vr[i][2]), "+v"(vr[i][3]));
+#pragma unroll
+  for (int i = 0; i < kKP; ++i) {
+    const int e = tid + 128 * i, s = e / kPR;
+    const bool keep = lds_tok[s] >= 0;
+    *reinterpret_cast<uint4*>(&lds_k[s][8 * (e % kPR)]) =
+        keep ? uint4{kr[i][0], kr[i][1], kr[i][2], kr[i][3]} : uint4{0u, 0u, 0u, 0u};
   }
   __syncthreads();
 
@@ -286,11 +349,13 @@ __global__ __launch_bounds__(128) void zoned_pack_kernel(PackArgs a) {
       int hi = -1, lo = -1;
 #pragma unroll
       for (int s = 0; s < kGroup; ++s) {
-        if (live >> s & 1u) {
-          sum += x[s];                         // slot order, float32
-          if (x[s] > vhi) { vhi = x[s]; hi = s; }
-          if (x[s] < vlo) { vlo = x[s]; lo = s; }
-        }
+        const bool l = live >> s & 1u;
+        sum = l ? sum + x[s] : sum;            // slot order, float32
+        const bool gh = l && x[s] > vhi, gl = l && x[s] < vlo;
+        vhi = gh ? x[s] : vhi;
+        hi = gh ? s : hi;
+        vlo = gl ? x[s] : vlo;
+        lo = gl ? s : lo;
       }
       const int count = __builtin_popcount(live);
       if (count <= 2 || vhi == vlo || hi < 0 || lo < 0) break;
@@ -301,10 +366,9 @@ __global__ __launch_bounds__(128) void zoned_pack_kernel(PackArgs a) {
     float mn = INFINITY, mx = -INFINITY;
 #pragma unroll
     for (int s = 0; s < kGroup; ++s) {
-      if (live >> s & 1u) {
-        mn = fminf(mn, x[s]);
-        mx = fmaxf(mx, x[s]);
-      }
+      const bool l = live >> s & 1u;
+      mn = fminf(mn, l ? x[s] : INFINITY);
+      mx = fmaxf(mx, l ? x[s] : -INFINITY);
     }
     const float levels = static_cast<float>((1 << bits) - 1);
     const uint16_t s16 = f2h((mx - mn) / levels);
@@ -314,7 +378,7 @@ __global__ __launch_bounds__(128) void zoned_pack_kernel(PackArgs a) {
 #pragma unroll
     for (int s = 0; s < kGroup; ++s)
       lds_c[s][pc] = live >> s & 1u ? static_cast<uint16_t>(code_of(x[s], mn, sf, rcp, levels)) : 0;
-  } else if (pc < d) {
+  } else if (pc < D) {
 #pragma unroll
     for (int s = 0; s < kGroup; ++s) lds_c[s][pc] = lds_k[s][ch];
   }
@@ -369,78 +433,79 @@ __global__ __launch_bounds__(128) void zoned_pack_kernel(PackArgs a) {
       oval[o] = lds_k[s][ch];
     }
   }
-  // key rows: word (slot, wi) of each class block, fields from lds_c
-  const int kw2 = U[U_KWORDS + 0], kw4 = U[U_KWORDS + 1], kw8 = U[U_KWORDS + 2];
+  __syncthreads();                               // lds_k is reused for the key words below
+  // key rows: class blocks of W_K words per slot, built in LDS (row stride
+  // W_K | 1), then copied out as 16-byte pieces
+  const int kw2 = U[U_KWORDS + 0], kw4 = U[U_KWORDS + 1], kw8 = U[U_KWORDS + 2], kw16 = U[U_KWORDS + 3];
   const int W_K = U[U_WK];
-  uint32_t* krow = reinterpret_cast<uint32_t*>(gb);
-  for (int e = tid; e < kGroup * W_K; e += blockDim.x) {
-    const int s = e / W_K, wi = e % W_K;
-    int cls_bits, first, count, wl;
-    if (wi < kw2) { cls_bits = 2; first = 0; count = m2; wl = wi; }
-    else if (wi < kw2 + kw4) { cls_bits = 4; first = m2; count = m4; wl = wi - kw2; }
-    else if (wi < kw2 + kw4 + kw8) { cls_bits = 8; first = m2 + m4; count = m8; wl = wi - kw2 - kw4; }
-    else { cls_bits = 16; first = n_kq; count = U[U_M + 3]; wl = wi - kw2 - kw4 - kw8; }
-    const int per = 32 / cls_bits;
-    uint32_t word = 0;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int idx = wl * per + j;
-      if (j < per && idx < count) word |= static_cast<uint32_t>(lds_c[s][first + idx]) << (j * cls_bits);
-    }
-    krow[e] = word;
-  }
+  const int ws = W_K | 1;
+  pack_key_class<2>(lds_kw, ws, 0, 0, m2, kw2, lds_c, tid);
+  pack_key_class<4>(lds_kw, ws, kw2, m2, m4, kw4, lds_c, tid);
+  pack_key_class<8>(lds_kw, ws, kw2 + kw4, m2 + m4, m8, kw8, lds_c, tid);
+  pack_key_class<16>(lds_kw, ws, kw2 + kw4 + kw8, n_kq, U[U_M + 3], kw16, lds_c, tid);
 
-  // ---- values
+  // ---- values (from registers; no LDS)
   if (w < 16) {
-    if (tid < d) {                              // value group (slot s, vg)
-      const int vwpt = d * w / 32;              // value words per slot
+    if (tid < D) {                              // value group (slot s, vg)
+      const int vwpt = D * w / 32;              // value words per slot
       uint8_t* vbase = gb + U[U_KCODES_B] + 2 * U[U_KSZ_B] + U[U_OUT_B];
       uint32_t* vcodes = reinterpret_cast<uint32_t*>(vbase);
-      const size_t vsz_b = pad(static_cast<size_t>(kGroup) * vpt * 2, 16);
+      constexpr size_t kVszB = static_cast<size_t>(kGroup) * kVPT * 2;   // a multiple of 16
       uint16_t* vs = reinterpret_cast<uint16_t*>(vbase + kGroup * vwpt * 4);
-      uint16_t* vz = reinterpret_cast<uint16_t*>(vbase + kGroup * vwpt * 4 + vsz_b);
-      const int e = tid, s = e / vpt, vg = e % vpt;
+      uint16_t* vz = reinterpret_cast<uint16_t*>(vbase + kGroup * vwpt * 4 + kVszB);
+      const int e = tid, s = e / kVPT, vg = e % kVPT;
       uint32_t* dst = vcodes + s * vwpt + vg * w;
       if (s >= n_valid) {
         for (int i = 0; i < w; ++i) dst[i] = 0u;
         vs[e] = 0;
         vz[e] = 0;
       } else {
-        float x[kGroup];
-        float mn = INFINITY, mx = -INFINITY;
+        uint32_t v[16];
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
+        for (int i = 0; i < 16; ++i) v[i] = vr[i >> 2][i & 3];
+        uint32_t pmn = pk_min_h2(v[0], v[1]), pmx = pk_max_h2(v[0], v[1]);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            x[8 * q4 + 2 * j] = h2f(static_cast<uint16_t>(vr[q4][j] & 0xFFFFu));
-            x[8 * q4 + 2 * j + 1] = h2f(static_cast<uint16_t>(vr[q4][j] >> 16));
-          }
-#pragma unroll
-        for (int i = 0; i < kGroup; ++i) {
-          mn = fminf(mn, x[i]);
-          mx = fmaxf(mx, x[i]);
+        for (int i = 2; i < 16; ++i) {
+          pmn = pk_min_h2(pmn, v[i]);
+          pmx = pk_max_h2(pmx, v[i]);
         }
+        const float mn = h2f(static_cast<uint16_t>(pk_min_halves(pmn) & 0xFFFFu));
+        const float mx = h2f(static_cast<uint16_t>(pk_max_halves(pmx) & 0xFFFFu));
         const float levels = static_cast<float>((1 << w) - 1);
         const uint16_t s16 = f2h((mx - mn) / levels);
         const float sf = h2f(s16), rcp = rcp_or_zero(sf);
         vs[e] = s16;
         vz[e] = f2h(mn);
-        if (w == 2) pack_value_words<2>(x, mn, sf, rcp, dst);
-        else if (w == 4) pack_value_words<4>(x, mn, sf, rcp, dst);
-        else pack_value_words<8>(x, mn, sf, rcp, dst);
+        if (w == 2) pack_value_words<2>(v, mn, sf, rcp, dst);
+        else if (w == 4) pack_value_words<4>(v, mn, sf, rcp, dst);
+        else pack_value_words<8>(v, mn, sf, rcp, dst);
       }
     }
   } else {
     // zone B rows of this group's slots (masked slots store zeros)
-    uint4* zb = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(ub + U[U_ZB]) + static_cast<size_t>(g) * kGroup * d);
+    uint4* zb = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(ub + U[U_ZB]) + static_cast<size_t>(g) * kGroup * D);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (128 * i < kp) {
-        const int e = tid + 128 * i;
-        const bool keep = lds_tok[e / pr] >= 0;
-        zb[e] = keep ? uint4{vr[i][0], vr[i][1], vr[i][2], vr[i][3]} : uint4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < kKP; ++i) {
+      const int e = tid + 128 * i;
+      const bool keep = lds_tok[e / kPR] >= 0;
+      zb[e] = keep ? uint4{vr[i][0], vr[i][1], vr[i][2], vr[i][3]} : uint4{0u, 0u, 0u, 0u};
+    }
+  }
+  __syncthreads();
+  // key words out: 32 W_K words, contiguous in the blob
+  uint4* krow = reinterpret_cast<uint4*>(gb);
+  for (int e = tid; e < kGroup * W_K / 4; e += 128) {
+    int s = (4 * e) / W_K, c = 4 * e - s * W_K;          // slot and word of the piece's first word
+    uint32_t q[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {                          // a piece may cross rows (W_K < 4 or not a multiple of 4)
+      q[j] = lds_kw[s * ws + c];
+      if (++c == W_K) {
+        c = 0;
+        ++s;
       }
     }
+    krow[e] = uint4{q[0], q[1], q[2], q[3]};
   }
 }
 
@@ -1083,7 +1148,10 @@ extern "C" int zoned_pack(const int32_t* plan_host, const int32_t* plan_dev, con
   PackArgs a{plan_dev, k, v, k_new, v_new, static_cast<uint8_t*>(blob), plan_host[H_TOLD],
              plan_host[H_C], plan_host[H_D], plan_host[H_SINK], plan_host[H_KOUT]};
   const dim3 grid(plan_host[H_MAX_GROUPS] + 1, units);
-  hipLaunchKernelGGL(zoned_pack_kernel, grid, dim3(128), 0, s, a);
+  if (plan_host[H_D] == 64)
+    hipLaunchKernelGGL(zoned_pack_kernel<64>, grid, dim3(128), 0, s, a);
+  else
+    hipLaunchKernelGGL(zoned_pack_kernel<128>, grid, dim3(128), 0, s, a);
   DQA_CHECK_LAUNCH();
   return DQA_OK;
 }
