@@ -190,7 +190,7 @@ def time_append(dqa, torch, dev, cfg, bits):
                       + 2 * d * 2 + 2 * 32 * (d // 32) * 2)   # key and value scales and zeros
     return {"kivi_append": _hbm_row("quantize_k_kernel + quantize_v_kernel + row copies", cfg["workload"], ms,
                                     nbytes, "one token into a full window: one 32-token group quantized per "
-                                    "(batch, KV head); five small launches, latency-bound")}
+                                    "(batch, KV head); three small launches, latency-bound")}
 
 
 def time_zoned(dqa, torch, dev):
