@@ -50,6 +50,7 @@ CASES = [
     (2, 4, 2, 128, 1000, 64, {0: .3, 8: .7}, {8: .5, 16: .5}),
     (1, 4, 2, 128, 300, 16, PV, {0: .25, 2: .25, 4: .2, 8: .15, 16: .15}),   # evicted key channels
     (1, 4, 1, 64, 100, 4, PV, {0: 1.0}),                                    # every key channel evicted
+    (2, 4, 2, 64, 150, 8, PV, {0: .85, 2: .1, 16: .05}),    # key rows of 1-3 words: 16-byte pieces span slots
 ]
 
 
