@@ -188,9 +188,10 @@ def time_append(dqa, torch, dev, cfg, bits):
                       + 2 * (R_cap + 1 - 32) * d * 2  # the kept rows written back
                       + 2 * 32 * w * 4                # the group's key and value codes
                       + 2 * d * 2 + 2 * 32 * (d // 32) * 2)   # key and value scales and zeros
-    return {"kivi_append": _hbm_row("quantize_k_kernel + quantize_v_kernel + row copies", cfg["workload"], ms,
-                                    nbytes, "one token into a full window: one 32-token group quantized per "
-                                    "(batch, KV head); three small launches, latency-bound")}
+    return {"kivi_append": _hbm_row("flush_window_kernel", cfg["workload"], ms,
+                                    nbytes, "one token into a full window: one 32-token group per (batch, KV head) "
+                                    "quantized straight from the window, then the window moved in place; "
+                                    "one launch of 64 workgroups, latency-bound")}
 
 
 def time_zoned(dqa, torch, dev):

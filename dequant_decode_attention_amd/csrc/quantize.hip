@@ -545,6 +545,93 @@ __global__ __launch_bounds__(256) void unstage_rows_kernel(const uint16_t* __res
   }
 }
 
+// Append without a flush: new rows [0, n) of each unit to window rows
+// [R, R + n) (R_cap rows per unit), keys and values in one launch.
+__global__ __launch_bounds__(256) void append_rows_kernel(const uint16_t* __restrict__ k_new,
+                                                          const uint16_t* __restrict__ v_new, int n, int R,
+                                                          uint16_t* __restrict__ k_rec, uint16_t* __restrict__ v_rec,
+                                                          int R_cap, size_t units, int d) {
+  const int cpr = d / 8;
+  const size_t total = units * static_cast<size_t>(n) * cpr;
+  for (size_t i2 = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i2 < 2 * total;
+       i2 += static_cast<size_t>(gridDim.x) * blockDim.x) {
+    const bool keys = i2 < total;
+    const size_t i = keys ? i2 : i2 - total;
+    const size_t u = i / (static_cast<size_t>(n) * cpr);
+    const size_t rem = i % (static_cast<size_t>(n) * cpr);
+    const int r = static_cast<int>(rem / cpr), ch = static_cast<int>(rem % cpr);
+    reinterpret_cast<uint4*>((keys ? k_rec : v_rec) + (u * R_cap + R + r) * d)[ch] =
+        reinterpret_cast<const uint4*>((keys ? k_new : v_new) + (u * n + r) * d)[ch];
+  }
+}
+
+// Flush whose f groups are the window's oldest rows (32 f <= R): one
+// workgroup per (KV head, batch) and tensor (grid y < B: keys of batch y,
+// else values of batch y - B) quantizes the groups straight from the window,
+// then moves the window's remaining R - 32 f rows and the n new rows to the
+// window start.  Every row of the new window is loaded before the first is
+// stored, so the move is safe in place.
+template <int D, int BITS>
+__global__ __launch_bounds__(D) void flush_window_kernel(const uint16_t* __restrict__ k_new,
+                                                         const uint16_t* __restrict__ v_new, uint16_t* k_rec,
+                                                         uint16_t* v_rec, int R_cap, int R, int n, int f, int Hkv,
+                                                         QuantizeOut ko, QuantizeOut vo, int dst_tiles, int tile0,
+                                                         int B) {
+  constexpr int kPR = D / 8;                   // 16-byte pieces per row
+  constexpr int kMaxPieces = kMaxRecent * kPR / D;   // per thread: the new window holds at most kMaxRecent rows
+  const int h = blockIdx.x;
+  const bool keys = static_cast<int>(blockIdx.y) < B;
+  const int b = keys ? blockIdx.y : blockIdx.y - B;
+  uint16_t* rec = keys ? k_rec : v_rec;
+  for (int t = 0; t < f; ++t) {
+    if (keys) quantize_k_tile<D, BITS>(rec, R_cap, Hkv, ko.codes, ko.scale, ko.zero, dst_tiles, tile0, t, h, b);
+    else quantize_v_tile<D, BITS>(rec, R_cap, Hkv, vo.codes, vo.scale, vo.zero, dst_tiles, tile0, t, h, b);
+    __syncthreads();                           // the tile's LDS and its reads of the window are done
+  }
+  const size_t unit = static_cast<size_t>(b) * Hkv + h;
+  const int keep = R - kGroup * f;
+  const int pieces = (keep + n) * kPR;
+  if (pieces == 0) return;
+  const uint16_t* nw = (keys ? k_new : v_new) + unit * n * D;
+  uint16_t* win = rec + unit * R_cap * D;
+  uint32_t buf[kMaxPieces][4];
+#pragma unroll
+  for (int i = 0; i < kMaxPieces; ++i) {
+    const int e = min(static_cast<int>(threadIdx.x) + D * i, pieces - 1), r = e / kPR, c8 = e % kPR;
+    const uint16_t* src = r < keep ? win + static_cast<size_t>(kGroup * f + r) * D : nw + static_cast<size_t>(r - keep) * D;
+    const uint4 x = reinterpret_cast<const uint4*>(src)[c8];
+    buf[i][0] = x.x;
+    buf[i][1] = x.y;
+    buf[i][2] = x.z;
+    buf[i][3] = x.w;
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's rows are in registers
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kMaxPieces; ++i) {
+    const int e = static_cast<int>(threadIdx.x) + D * i;
+    if (e < pieces) reinterpret_cast<uint4*>(win)[e] = uint4{buf[i][0], buf[i][1], buf[i][2], buf[i][3]};
+  }
+}
+
+void launch_flush_window(int d, int bits, dim3 grid, hipStream_t s, const uint16_t* k_new, const uint16_t* v_new,
+                         uint16_t* k_rec, uint16_t* v_rec, int R_cap, int R, int n, int f, int Hkv, QuantizeOut ko,
+                         QuantizeOut vo, int dst_tiles, int tile0, int B) {
+#define DQA_FW(D, BITS)                                                                                       \
+  hipLaunchKernelGGL((flush_window_kernel<D, BITS>), grid, dim3(D), 0, s, k_new, v_new, k_rec, v_rec, R_cap, R, \
+                     n, f, Hkv, ko, vo, dst_tiles, tile0, B)
+  if (d == 128) {
+    if (bits == 2) DQA_FW(128, 2);
+    else if (bits == 4) DQA_FW(128, 4);
+    else DQA_FW(128, 8);
+  } else {
+    if (bits == 2) DQA_FW(64, 2);
+    else if (bits == 4) DQA_FW(64, 4);
+    else DQA_FW(64, 8);
+  }
+#undef DQA_FW
+}
+
 // Flushes (groups of 32 quantized) when `rows` tokens sit in the recent zone
 // bounded by R_max: while more than R_max and at least 32 remain.
 int flush_count(int rows, int R_max) {
@@ -624,30 +711,48 @@ extern "C" int kivi_append(dqa_kivi_cache* c, const uint16_t* k_new, const uint1
 
   const int d = c->d;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  uint16_t* krec = const_cast<uint16_t*>(c->k_recent);
+  uint16_t* vrec = const_cast<uint16_t*>(c->v_recent);
+  if (f == 0) {                                // no flush: the new rows go after the window's rows
+    if (n_new > 0) {
+      const size_t chunks = units * static_cast<size_t>(n_new) * (d / 8);
+      hipLaunchKernelGGL(append_rows_kernel, dim3(copy_blocks(2 * chunks)), dim3(256), 0, s, k_new, v_new, n_new,
+                         c->R, krec, vrec, R_cap, units, d);
+      DQA_CHECK_LAUNCH();
+    }
+    c->R = R_new;
+    return DQA_OK;
+  }
+  uint32_t* kc = const_cast<uint32_t*>(c->k_codes);
+  uint16_t* ks = const_cast<uint16_t*>(c->k_scale);
+  uint16_t* kz = const_cast<uint16_t*>(c->k_zero);
+  uint32_t* vc = const_cast<uint32_t*>(c->v_codes);
+  uint16_t* vs = const_cast<uint16_t*>(c->v_scale);
+  uint16_t* vz = const_cast<uint16_t*>(c->v_zero);
+  const int dst_tiles = T_cap / kGroup, tile0 = c->T_q / kGroup;
+  if (kGroup * f <= c->R) {                    // the flushed groups are the window's oldest rows
+    launch_flush_window(d, c->bits, dim3(c->Hkv, 2 * c->B), s, k_new, v_new, krec, vrec, R_cap, c->R, n_new, f,
+                        c->Hkv, QuantizeOut{kc, ks, kz}, QuantizeOut{vc, vs, vz}, dst_tiles, tile0, c->B);
+    DQA_CHECK_LAUNCH();
+    c->T_q = T_new;
+    c->R = R_new;
+    return DQA_OK;
+  }
+  // general case (the groups reach into the new rows): window and new rows
+  // staged in the workspace, quantized from there, the rest moved back
   uint16_t* wk = static_cast<uint16_t*>(ws);
   uint16_t* wv = wk + units * static_cast<size_t>(rows) * d;
   const size_t chunks = units * static_cast<size_t>(rows) * (d / 8);
   hipLaunchKernelGGL(stage_rows_kernel, dim3(copy_blocks(2 * chunks)), dim3(256), 0, s,
                      RowPair{c->k_recent, k_new, wk}, RowPair{c->v_recent, v_new, wv}, c->R, R_cap, n_new, units, d);
   DQA_CHECK_LAUNCH();
-  if (f > 0) {
-    uint32_t* kc = const_cast<uint32_t*>(c->k_codes);
-    uint16_t* ks = const_cast<uint16_t*>(c->k_scale);
-    uint16_t* kz = const_cast<uint16_t*>(c->k_zero);
-    uint32_t* vc = const_cast<uint32_t*>(c->v_codes);
-    uint16_t* vs = const_cast<uint16_t*>(c->v_scale);
-    uint16_t* vz = const_cast<uint16_t*>(c->v_zero);
-    const dim3 grid(f, c->Hkv, 2 * c->B);
-    const int dst_tiles = T_cap / kGroup, tile0 = c->T_q / kGroup;
-    launch_quantize_kv(d, c->bits, grid, s, wk, wv, rows, c->Hkv, QuantizeOut{kc, ks, kz}, QuantizeOut{vc, vs, vz},
-                       dst_tiles, tile0, c->B);
-    DQA_CHECK_LAUNCH();
-  }
+  launch_quantize_kv(d, c->bits, dim3(f, c->Hkv, 2 * c->B), s, wk, wv, rows, c->Hkv, QuantizeOut{kc, ks, kz},
+                     QuantizeOut{vc, vs, vz}, dst_tiles, tile0, c->B);
+  DQA_CHECK_LAUNCH();
   if (R_new > 0) {
     const size_t kchunks = units * static_cast<size_t>(R_new) * (d / 8);
     hipLaunchKernelGGL(unstage_rows_kernel, dim3(copy_blocks(2 * kchunks)), dim3(256), 0, s, wk, wv, rows,
-                       f * kGroup, R_new, const_cast<uint16_t*>(c->k_recent), const_cast<uint16_t*>(c->v_recent),
-                       R_cap, units, d);
+                       f * kGroup, R_new, krec, vrec, R_cap, units, d);
     DQA_CHECK_LAUNCH();
   }
   c->T_q = T_new;

@@ -196,9 +196,13 @@ int decode_attention_qkv_merge(const dqa_kivi_cache* cache, const void* ws,
  *          may be null when n_new == 0
  *   R_max  0..128
  *   ws     (device) workspace of ws_bytes >= kivi_append_workspace_bytes
- * B <= 32767.  Enqueues up to three kernels on `stream` (stage, quantize,
- * move back; keys and values together in each); the recent buffers may be
- * rewritten in place (the kernels read a staged copy from ws).
+ * B <= 32767.  Enqueues on `stream` (keys and values together in each
+ * kernel): without a flush, one copy of the new rows behind the recent rows;
+ * with flushes whose groups are all recent rows (32 * flushes <= R), one
+ * kernel that quantizes them in place and then moves the rest of the window
+ * (every row it moves is loaded before any is stored); otherwise three
+ * kernels (stage the window and the new rows in ws, quantize from there,
+ * move back).  ws is required in every case.
  * Errors: DQA_ERR_NULL, DQA_ERR_SHAPE, DQA_ERR_BITS, DQA_ERR_WORKSPACE,
  * DQA_ERR_ALIGN, DQA_ERR_HIP. */
 size_t kivi_append_workspace_bytes(const dqa_kivi_cache* cache, int n_new);
