@@ -146,3 +146,26 @@ def test_append_full_config_flush(dqa):
     assert np.array_equal(t["v_recent"][:, :, :97], v[:, :, 32:129])
     # nothing before the new group was touched
     assert not t["k_codes"][:, :, :T_q0].any() and not t["k_scale"][:, :, :T_q0 // 32].any()
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_append_in_window_flush_every_width(dqa, bits, d):
+    """One token per step into a 32-row window: every flush quantizes the
+    window's oldest group in place and moves the rest of the window (the
+    in-window flush path), for each width and head dim; state bit-exact with
+    the oracle's stream after each flush and at the end."""
+    B, Hq, Hkv, T = 2, 4, 2, 120
+    say("kivi_append in-window flush", bits, d)
+    k, v = _tokens(B, Hkv, T, d, seed=100 + bits + d)
+    cache = _empty_gpu_cache(dqa, B, Hq, Hkv, d, bits, 128, 64, 0.0)
+    st = oracle.empty_stream(B, Hkv, d)
+    flushes = 0
+    for t in range(T):
+        f = dqa.kivi_append(cache, dev(k[:, :, t:t + 1]), dev(v[:, :, t:t + 1]), 32)
+        st = oracle.kivi_append(st, k[:, :, t:t + 1], v[:, :, t:t + 1], bits, 32)
+        flushes += f
+        if f or t == T - 1:
+            torch.cuda.synchronize()
+            _check_state(cache, st, bits)
+    assert flushes == 3 and (cache.T_q, cache.R) == (96, 24)
