@@ -583,30 +583,36 @@ __global__ __launch_bounds__(D) void flush_window_kernel(const uint16_t* __restr
   const bool keys = static_cast<int>(blockIdx.y) < B;
   const int b = keys ? blockIdx.y : blockIdx.y - B;
   uint16_t* rec = keys ? k_rec : v_rec;
+  const size_t unit = static_cast<size_t>(b) * Hkv + h;
+  const int keep = R - kGroup * f;
+  const int pieces = (keep + n) * kPR;
+  const uint16_t* nw = (keys ? k_new : v_new) + unit * n * D;
+  uint16_t* win = rec + unit * R_cap * D;
+  // the rows to move are loaded first: their sources (window rows 32 f ..
+  // and the new rows) are not among the rows being quantized, so both
+  // memory round trips overlap
+  uint32_t buf[kMaxPieces][4];
+  if (pieces > 0) {
+#pragma unroll
+    for (int i = 0; i < kMaxPieces; ++i) {
+      const int e = min(static_cast<int>(threadIdx.x) + D * i, pieces - 1), r = e / kPR, c8 = e % kPR;
+      const uint16_t* src =
+          r < keep ? win + static_cast<size_t>(kGroup * f + r) * D : nw + static_cast<size_t>(r - keep) * D;
+      const uint4 x = reinterpret_cast<const uint4*>(src)[c8];
+      buf[i][0] = x.x;
+      buf[i][1] = x.y;
+      buf[i][2] = x.z;
+      buf[i][3] = x.w;
+    }
+  }
   for (int t = 0; t < f; ++t) {
     if (keys) quantize_k_tile<D, BITS>(rec, R_cap, Hkv, ko.codes, ko.scale, ko.zero, dst_tiles, tile0, t, h, b);
     else quantize_v_tile<D, BITS>(rec, R_cap, Hkv, vo.codes, vo.scale, vo.zero, dst_tiles, tile0, t, h, b);
     __syncthreads();                           // the tile's LDS and its reads of the window are done
   }
-  const size_t unit = static_cast<size_t>(b) * Hkv + h;
-  const int keep = R - kGroup * f;
-  const int pieces = (keep + n) * kPR;
   if (pieces == 0) return;
-  const uint16_t* nw = (keys ? k_new : v_new) + unit * n * D;
-  uint16_t* win = rec + unit * R_cap * D;
-  uint32_t buf[kMaxPieces][4];
-#pragma unroll
-  for (int i = 0; i < kMaxPieces; ++i) {
-    const int e = min(static_cast<int>(threadIdx.x) + D * i, pieces - 1), r = e / kPR, c8 = e % kPR;
-    const uint16_t* src = r < keep ? win + static_cast<size_t>(kGroup * f + r) * D : nw + static_cast<size_t>(r - keep) * D;
-    const uint4 x = reinterpret_cast<const uint4*>(src)[c8];
-    buf[i][0] = x.x;
-    buf[i][1] = x.y;
-    buf[i][2] = x.z;
-    buf[i][3] = x.w;
-  }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's rows are in registers
-  __syncthreads();
+  __syncthreads();                                    // and every thread's: the window may be overwritten
 #pragma unroll
   for (int i = 0; i < kMaxPieces; ++i) {
     const int e = static_cast<int>(threadIdx.x) + D * i;
