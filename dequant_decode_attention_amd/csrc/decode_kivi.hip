@@ -125,6 +125,21 @@ __device__ __forceinline__ Words<NB> load_words(const void* p) {
 // A value the compiler must treat as unknown (keeps a VGPR constant out of
 // the scalar constant bus, and keeps shifted words from being folded back
 // into bit-field extracts).
+// A kernel-argument pointer as a wave-uniform value.  A lane-dependent
+// choice between two argument pointers would otherwise be folded into a
+// per-lane vector load of the pointer from the argument segment, issued
+// again on every use.
+template <typename T>
+__device__ __forceinline__ const T* uniform_ptr(const T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  // rebuilt as a global-memory pointer, so loads through it stay global loads
+  using GT = const __attribute__((address_space(1))) T;
+  GT* g = reinterpret_cast<GT*>((static_cast<uint64_t>(hi) << 32) | lo);
+  return (const T*)g;
+}
+
 __device__ __forceinline__ uint32_t opaque(uint32_t v) {
   asm volatile("" : "+v"(v));
   return v;
@@ -518,6 +533,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kDecodeWave
   for (int i = 0; i < CPS; ++i)
     sfac[i] = __builtin_ldexpf(1.0f, 24 - BITS * key_code_pos<BITS>(((lane & 31) * CPS + i) & 7));
   const size_t qstride = static_cast<size_t>(a.qtile_stride);      // tiles per (batch, KV head)
+  const uint16_t* const ksz_s = uniform_ptr(a.k_scale);
+  const uint16_t* const ksz_z = uniform_ptr(a.k_zero);
+  const uint16_t* const vsz_s = uniform_ptr(a.v_scale);
+  const uint16_t* const vsz_z = uniform_ptr(a.v_zero);
   const uint8_t* const kbase = reinterpret_cast<const uint8_t*>(a.k_codes) + unit * qstride * kGroup * KROW;
   const uint8_t* const vbase = reinterpret_cast<const uint8_t*>(a.v_codes) + unit * qstride * VBLK;
   constexpr int VW = BITS == 8 ? 2 : 1;   // 32-bit words per value chunk
@@ -550,8 +569,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kDecodeWave
     }
     // scale blocks: lanes 0..31 read scales, 32..63 zeros
     const int half = lane >> 5, r = lane & 31;
-    const uint16_t* ksrc = (half ? a.k_zero : a.k_scale) + (unit * qstride + ti) * D + r * (D / 32);
-    const uint16_t* vsrc = (half ? a.v_zero : a.v_scale) + ((unit * qstride + ti) * kGroup + r) * NVG;
+    const uint16_t* ksrc = (half ? ksz_z : ksz_s) + (unit * qstride + ti) * D + r * (D / 32);
+    const uint16_t* vsrc = (half ? vsz_z : vsz_s) + ((unit * qstride + ti) * kGroup + r) * NVG;
     const Words<4 * SZW> kw = load_words<4 * SZW>(ksrc);
     const Words<4 * SZW> vw = load_words<4 * SZW>(vsrc);
 #pragma unroll
