@@ -18,6 +18,10 @@ constexpr int kMaxRecent = 128;  // residual-buffer bound ([P1 para 8])
 // workspace sizes depend on the shape only.
 constexpr int kTargetWorkgroups = 1024;
 
+// Device pointers handed to the library must be 16-byte aligned (the
+// kernels move 16-byte pieces); DQA_ERR_ALIGN otherwise.
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
 #define DQA_CHECK_LAUNCH()                               \
   do {                                                   \
     if (hipPeekAtLastError() != hipSuccess) return DQA_ERR_HIP; \

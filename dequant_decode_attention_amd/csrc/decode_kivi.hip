@@ -820,7 +820,6 @@ void launch_decode(const KiviArgs& a, int G, int bits, bool rope, dim3 grid, hip
   else launch_bits<D, 8>(a, G, rope, grid, s);
 }
 
-bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 }  // namespace
 }  // namespace dqa

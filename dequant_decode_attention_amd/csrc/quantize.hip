@@ -433,7 +433,6 @@ void launch_quantize(int d, int bits, dim3 grid, hipStream_t s, const uint16_t* 
 
 
 
-bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int check_common(const void* in, int B, int Hkv, int T, int d, int bits,
                  const void* codes, const void* scale, const void* zero) {
@@ -695,11 +694,16 @@ extern "C" int kivi_append(dqa_kivi_cache* c, const uint16_t* k_new, const uint1
   const int R_cap = c->R_cap > 0 ? c->R_cap : c->R;
   if (T_new > T_cap || R_new > R_cap) return DQA_ERR_SHAPE;
   const size_t units = static_cast<size_t>(c->B) * c->Hkv;
-  if (units == 0 || rows == 0) {
+  // A capacity of 0 means "the current count"; the buffers' row strides are
+  // fixed by it, so it is written back below and stays put when R shrinks.
+  auto commit = [&]() {
+    c->T_cap = T_cap;
+    c->R_cap = R_cap;
     c->T_q = T_new;
     c->R = R_new;
     return DQA_OK;
-  }
+  };
+  if (units == 0 || rows == 0) return commit();
   if (n_new > 0 && (!k_new || !v_new)) return DQA_ERR_NULL;
   if (c->R > 0 || R_new > 0) {
     if (!c->k_recent || !c->v_recent) return DQA_ERR_NULL;
@@ -726,8 +730,7 @@ extern "C" int kivi_append(dqa_kivi_cache* c, const uint16_t* k_new, const uint1
                          c->R, krec, vrec, R_cap, units, d);
       DQA_CHECK_LAUNCH();
     }
-    c->R = R_new;
-    return DQA_OK;
+    return commit();
   }
   uint32_t* kc = const_cast<uint32_t*>(c->k_codes);
   uint16_t* ks = const_cast<uint16_t*>(c->k_scale);
@@ -740,9 +743,7 @@ extern "C" int kivi_append(dqa_kivi_cache* c, const uint16_t* k_new, const uint1
     launch_flush_window(d, c->bits, dim3(c->Hkv, 2 * c->B), s, k_new, v_new, krec, vrec, R_cap, c->R, n_new, f,
                         c->Hkv, QuantizeOut{kc, ks, kz}, QuantizeOut{vc, vs, vz}, dst_tiles, tile0, c->B);
     DQA_CHECK_LAUNCH();
-    c->T_q = T_new;
-    c->R = R_new;
-    return DQA_OK;
+    return commit();
   }
   // general case (the groups reach into the new rows): window and new rows
   // staged in the workspace, quantized from there, the rest moved back
@@ -761,7 +762,5 @@ extern "C" int kivi_append(dqa_kivi_cache* c, const uint16_t* k_new, const uint1
                        f * kGroup, R_new, krec, vrec, R_cap, units, d);
     DQA_CHECK_LAUNCH();
   }
-  c->T_q = T_new;
-  c->R = R_new;
-  return DQA_OK;
+  return commit();
 }

@@ -578,7 +578,6 @@ int alloc_run(const float* w, int rows, int n, long long budget, int8_t* widths,
   return DQA_OK;
 }
 
-bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int check_heads(int B, int Hq, int Hkv, int T, int d) {
   if (B < 0 || Hq <= 0 || Hkv <= 0 || T < 0 || Hq % Hkv != 0) return DQA_ERR_SHAPE;

@@ -613,6 +613,7 @@ extern "C" int rvq_encode(const uint16_t* x, int64_t n, int d, const uint16_t* c
   if (n == 0) return DQA_OK;
   if (!x || !codebooks || !idx) return DQA_ERR_NULL;
   if (!ws || ws_bytes < rvq_encode_workspace_bytes(N, Kc)) return DQA_ERR_WORKSPACE;
+  if (!aligned16(x) || !aligned16(codebooks) || !aligned16(ws)) return DQA_ERR_ALIGN;
   const int64_t blocks = (n + kEncRows - 1) / kEncRows;
   if (blocks > 0x7FFFFFFF) return DQA_ERR_SHAPE;
   hipStream_t s = static_cast<hipStream_t>(stream);

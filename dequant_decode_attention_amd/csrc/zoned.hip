@@ -75,13 +75,114 @@ size_t plan_words(int B, int Hkv, int T_old, int d) {
   return kHeaderWords + static_cast<size_t>(B) * Hkv * (kUnitWords + d + T_old);
 }
 
-int check_plan(const int32_t* p) {
+// Unit record of a unit whose kept old tokens number n[si] per value segment
+// (widths 2, 4, 8, 16) and whose quantized-or-raw key channels number m[ci]
+// per key class, placed at byte offset `base` of the blob.  Returns the
+// unit's region size in bytes (a multiple of 256), or -1 when it does not fit
+// the 31-bit size field.  zoned_plan builds every record with it, and
+// check_plan re-derives every record with it.
+long long fill_unit(int32_t* U, const int* n, const int* m, int d, int sink, int C_new, int k_out, size_t base) {
+  for (int w = 0; w < kUnitWords; ++w) U[w] = 0;
+  int nt = 0;
+  for (int i = 0; i < 4; ++i) {
+    U[U_N + i] = n[i];
+    U[U_M + i] = m[i];
+    U[U_GROUPS + i] = (n[i] + kGroup - 1) / kGroup;
+    U[U_KWORDS + i] = (m[i] * kSegW[i] + 31) / 32;
+    U[U_TOK_PREFIX + i] = nt;
+    nt += n[i];
+  }
+  const int W_K = U[U_KWORDS] + U[U_KWORDS + 1] + U[U_KWORDS + 2] + U[U_KWORDS + 3];
+  const int n_kq = m[0] + m[1] + m[2];
+  U[U_WK] = W_K;
+  U[U_NKQ] = n_kq;
+  U[U_KCODES_B] = kGroup * W_K * 4;
+  U[U_KSZ_B] = static_cast<int32_t>(pad(static_cast<size_t>(n_kq) * 2, 16));
+  U[U_OUT_B] = k_out > 0 ? kOffsBytes + 2 * static_cast<int32_t>(pad(static_cast<size_t>(n_kq) * k_out * 2, 16))
+                         : 0;
+  size_t off = 0;
+  int total = 0;
+  for (int si = 0; si < 4; ++si) {
+    size_t gbytes = static_cast<size_t>(U[U_KCODES_B]) + 2 * static_cast<size_t>(U[U_KSZ_B]) + U[U_OUT_B];
+    if (kSegW[si] < 16)
+      gbytes += static_cast<size_t>(kGroup) * (d * kSegW[si] / 32) * 4 +
+                2 * pad(static_cast<size_t>(kGroup) * (d / kGroup) * 2, 16);
+    U[U_SEG_OFF + si] = static_cast<int32_t>(off);
+    U[U_GRP_B + si] = static_cast<int32_t>(gbytes);
+    off += gbytes * U[U_GROUPS + si];
+    total += U[U_GROUPS + si];
+  }
+  U[U_ZB] = static_cast<int32_t>(off);
+  off += static_cast<size_t>(U[U_GROUPS + 3]) * kGroup * d * 2;
+  U[U_ZC] = static_cast<int32_t>(off);
+  off += 2 * static_cast<size_t>(sink + C_new) * d * 2;
+  const size_t size = pad(off, 256);
+  if (size > 0x7FFFFFFFu) return -1;
+  U[U_SIZE] = static_cast<int32_t>(size);
+  U[U_BASE_LO] = static_cast<int32_t>(base & 0xFFFFFFFFu);
+  U[U_BASE_HI] = static_cast<int32_t>(base >> 32);
+  U[U_TOTAL_GROUPS] = total;
+  return static_cast<long long>(size);
+}
+
+// A plan as zoned_plan writes it, checked in full before any launch: the
+// header, every unit record (re-derived from its token and channel counts),
+// the blob size, the per-unit channel permutation (each channel once) and,
+// with `tokens`, the token map (kept old tokens in [sink, T_old), increasing
+// within each segment).  Anything else is DQA_ERR_PLAN.
+int check_plan(const int32_t* p, bool tokens) {
   if (!p) return DQA_ERR_NULL;
   if (p[H_MAGIC] != kPlanMagic || p[H_VERSION] != kPlanVersion) return DQA_ERR_PLAN;
-  if (p[H_D] != 64 && p[H_D] != 128) return DQA_ERR_PLAN;
-  if (p[H_B] < 0 || p[H_HKV] < 0 || p[H_C] < 0 || p[H_SINK] < 0 || p[H_SINK] > p[H_TOLD]) return DQA_ERR_PLAN;
-  if (p[H_C] + p[H_SINK] > kMaxZoneC || p[H_KOUT] < 0 || p[H_KOUT] > kMaxOutliers) return DQA_ERR_PLAN;
+  const int d = p[H_D], T_old = p[H_TOLD], sink = p[H_SINK], C_new = p[H_C], k_out = p[H_KOUT];
+  if (d != 64 && d != 128) return DQA_ERR_PLAN;
+  if (p[H_B] < 0 || p[H_HKV] < 0 || C_new < 0 || sink < 0 || T_old < 0 || sink > T_old) return DQA_ERR_PLAN;
+  if (C_new + sink > kMaxZoneC || k_out < 0 || k_out > kMaxOutliers) return DQA_ERR_PLAN;
   if (static_cast<int64_t>(p[H_B]) * p[H_HKV] != p[H_UNITS]) return DQA_ERR_PLAN;
+  const int units = p[H_UNITS];
+  if (units > (1 << 20) || T_old > (1 << 24)) return DQA_ERR_PLAN;
+  if (p[H_UNIT_OFF] != kHeaderWords || p[H_PERM_OFF] != kHeaderWords + units * kUnitWords ||
+      static_cast<int64_t>(p[H_TOK_OFF]) != static_cast<int64_t>(p[H_PERM_OFF]) + static_cast<int64_t>(units) * d)
+    return DQA_ERR_PLAN;
+  size_t base = 0;
+  int max_groups = 0;
+  int32_t rec[kUnitWords];
+  for (int u = 0; u < units; ++u) {
+    const int32_t* U = p + kHeaderWords + static_cast<size_t>(u) * kUnitWords;
+    int n[4], m[4];
+    long long sn = 0, sm = 0;
+    for (int i = 0; i < 4; ++i) {
+      n[i] = U[U_N + i];
+      m[i] = U[U_M + i];
+      if (n[i] < 0 || m[i] < 0) return DQA_ERR_PLAN;
+      sn += n[i];
+      sm += m[i];
+    }
+    if (sn > T_old - sink || sm > d) return DQA_ERR_PLAN;
+    const long long size = fill_unit(rec, n, m, d, sink, C_new, k_out, base);
+    if (size < 0) return DQA_ERR_PLAN;
+    for (int w = 0; w < kUnitWords; ++w)
+      if (rec[w] != U[w]) return DQA_ERR_PLAN;
+    base += static_cast<size_t>(size);
+    if (rec[U_TOTAL_GROUPS] > max_groups) max_groups = rec[U_TOTAL_GROUPS];
+    const int32_t* perm = p + p[H_PERM_OFF] + static_cast<size_t>(u) * d;
+    uint64_t seen[2] = {0, 0};                    // d <= 128 channels
+    for (int c = 0; c < d; ++c) {
+      const int32_t ch = perm[c];
+      if (ch < 0 || ch >= d || ((seen[ch >> 6] >> (ch & 63)) & 1u)) return DQA_ERR_PLAN;
+      seen[ch >> 6] |= uint64_t{1} << (ch & 63);
+    }
+    if (tokens) {
+      const int32_t* tok = p + static_cast<size_t>(p[H_TOK_OFF]) + static_cast<size_t>(u) * T_old;
+      for (int si = 0; si < 4; ++si) {
+        const int32_t* t = tok + U[U_TOK_PREFIX + si];
+        for (int i = 0; i < n[si]; ++i)
+          if (t[i] < sink || t[i] >= T_old || (i > 0 && t[i] <= t[i - 1])) return DQA_ERR_PLAN;
+      }
+    }
+  }
+  const size_t blob = static_cast<size_t>(static_cast<uint32_t>(p[H_BLOB_LO])) |
+                      (static_cast<size_t>(static_cast<uint32_t>(p[H_BLOB_HI])) << 32);
+  if (blob != base || p[H_MAX_GROUPS] != max_groups) return DQA_ERR_PLAN;
   return DQA_OK;
 }
 
@@ -111,7 +212,6 @@ __device__ __forceinline__ uint32_t code_of(float x, float zf, float sf, float r
 }
 __device__ __forceinline__ float rcp_or_zero(float sf) { return sf == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(sf); }
 
-bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // n16 16-byte pieces from src to dst by a 128-thread workgroup, four loads
 // in flight per thread (dst and src 16-byte aligned).
@@ -975,7 +1075,7 @@ struct ZGeometry {
 };
 
 int zoned_geometry(const int32_t* p, int Hq, ZGeometry* g) {
-  int st = check_plan(p);
+  int st = check_plan(p, false);
   if (st != DQA_OK) return st;
   const int Hkv = p[H_HKV];
   if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return DQA_ERR_SHAPE;
@@ -1070,7 +1170,6 @@ extern "C" int zoned_plan(const int8_t* v_bits, const int8_t* k_bits, int B, int
           ++m;
         }
       U[U_M + ci] = m;
-      U[U_KWORDS + ci] = (m * kSegW[ci] + 31) / 32;
     }
     // evicted key channels (width 0) close the permutation; they are stored
     // nowhere and read by no product
@@ -1078,7 +1177,6 @@ extern "C" int zoned_plan(const int8_t* v_bits, const int8_t* k_bits, int B, int
       if (kb[c] == 0) perm[np++] = c;
     int nt = 0;
     for (int si = 0; si < 4; ++si) {
-      U[U_TOK_PREFIX + si] = nt;
       int n = 0;
       for (int t = sink; t < T_old; ++t)          // sink tokens live in zone C
         if (vb[t] == kSegW[si]) {
@@ -1086,40 +1184,17 @@ extern "C" int zoned_plan(const int8_t* v_bits, const int8_t* k_bits, int B, int
           ++n;
         }
       U[U_N + si] = n;
-      U[U_GROUPS + si] = (n + kGroup - 1) / kGroup;
     }
-    const int W_K = U[U_KWORDS] + U[U_KWORDS + 1] + U[U_KWORDS + 2] + U[U_KWORDS + 3];
-    const int n_kq = U[U_M] + U[U_M + 1] + U[U_M + 2];
-    U[U_WK] = W_K;
-    U[U_NKQ] = n_kq;
-    U[U_KCODES_B] = kGroup * W_K * 4;
-    U[U_KSZ_B] = static_cast<int32_t>(pad(static_cast<size_t>(n_kq) * 2, 16));
-    U[U_OUT_B] = k_out > 0 ? kOffsBytes + 2 * static_cast<int32_t>(pad(static_cast<size_t>(n_kq) * k_out * 2, 16))
-                           : 0;
-    size_t off = 0;
-    int total = 0;
-    for (int si = 0; si < 4; ++si) {
-      size_t gbytes = static_cast<size_t>(U[U_KCODES_B]) + 2 * static_cast<size_t>(U[U_KSZ_B]) + U[U_OUT_B];
-      if (kSegW[si] < 16)
-        gbytes += static_cast<size_t>(kGroup) * (d * kSegW[si] / 32) * 4 +
-                  2 * pad(static_cast<size_t>(kGroup) * (d / kGroup) * 2, 16);
-      U[U_SEG_OFF + si] = static_cast<int32_t>(off);
-      U[U_GRP_B + si] = static_cast<int32_t>(gbytes);
-      off += gbytes * U[U_GROUPS + si];
-      total += U[U_GROUPS + si];
+    int n[4], m[4];
+    for (int i = 0; i < 4; ++i) {
+      n[i] = U[U_N + i];
+      m[i] = U[U_M + i];
     }
-    U[U_ZB] = static_cast<int32_t>(off);
-    off += static_cast<size_t>(U[U_GROUPS + 3]) * kGroup * d * 2;
-    U[U_ZC] = static_cast<int32_t>(off);
-    off += 2 * static_cast<size_t>(sink + C_new) * d * 2;
-    const size_t size = pad(off, 256);
-    if (size > 0x7FFFFFFFu) return DQA_ERR_SHAPE;
-    U[U_SIZE] = static_cast<int32_t>(size);
-    U[U_BASE_LO] = static_cast<int32_t>(base & 0xFFFFFFFFu);
-    U[U_BASE_HI] = static_cast<int32_t>(base >> 32);
-    U[U_TOTAL_GROUPS] = total;
+    const long long size = fill_unit(U, n, m, d, sink, C_new, k_out, base);
+    if (size < 0) return DQA_ERR_SHAPE;
+    const int total = U[U_TOTAL_GROUPS];
     if (total > max_groups) max_groups = total;
-    base += size;
+    base += static_cast<size_t>(size);
   }
   plan[H_BLOB_LO] = static_cast<int32_t>(base & 0xFFFFFFFFu);
   plan[H_BLOB_HI] = static_cast<int32_t>(base >> 32);
@@ -1131,7 +1206,7 @@ extern "C" int zoned_plan(const int8_t* v_bits, const int8_t* k_bits, int B, int
 extern "C" int zoned_pack(const int32_t* plan_host, const int32_t* plan_dev, const uint16_t* k,
                           const uint16_t* v, const uint16_t* k_new, const uint16_t* v_new, void* blob,
                           void* stream) {
-  int st = check_plan(plan_host);
+  int st = check_plan(plan_host, true);
   if (st != DQA_OK) return st;
   if (!plan_dev) return DQA_ERR_NULL;
   const int units = plan_host[H_UNITS];
@@ -1172,6 +1247,7 @@ extern "C" int decode_attention_zoned(const uint16_t* q, int Hq, const int32_t* 
   if (!q || !out || !plan_dev || !blob) return DQA_ERR_NULL;
   if (!ws || ws_bytes < g.ws_bytes) return DQA_ERR_WORKSPACE;
   if (g.units > 65535) return DQA_ERR_SHAPE;
+  if (!aligned16(blob) || !aligned16(ws) || !aligned16(out)) return DQA_ERR_ALIGN;
   ZDecodeArgs a;
   a.plan = plan_dev;
   a.blob = static_cast<const uint8_t*>(blob);

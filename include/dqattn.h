@@ -56,7 +56,10 @@ enum {
 const char* dqa_status_string(int status);
 
 /* Version of this interface (increments on any signature or layout change). */
-int dqa_abi_version(void);  /* 7: quantize_pack_k/v and zoned_pack check
+int dqa_abi_version(void);  /* 8: decode_attention_zoned and rvq_encode check
+                              16-byte alignment; zoned plans are validated in
+                              full; kivi_append writes back zero capacities;
+                              7: quantize_pack_k/v and zoned_pack check
                               16-byte alignment; kivi_append takes
                               B <= 32767;
                               6: zoned_plan takes a sink length and the
@@ -188,7 +191,9 @@ int decode_attention_qkv_merge(const dqa_kivi_cache* cache, const void* ws,
  * quantize_pack_v would quantize them (one key group per channel, one value
  * group per token and 32 channels) into quantized positions T_q..T_q+31,
  * and T_q grows by 32.  The remaining recent tokens move to the front of
- * the recent buffers.  On success cache->T_q and cache->R are updated; the
+ * the recent buffers.  On success cache->T_q and cache->R are updated, and
+ * a T_cap or R_cap of 0 is replaced by the capacity the call used (the old
+ * T_q or R), so the buffers keep their row strides when R shrinks; the
  * buffers the cache points to must be writable device memory.
  *   cache  (host) descriptor with T_cap >= T_q + 32 * flushes and
  *          R_cap >= the new R (else DQA_ERR_SHAPE and nothing is written)
@@ -250,7 +255,11 @@ size_t zoned_plan_words(int B, int Hkv, int T_old, int d);
  *   plan   (host) int32 [plan_words], plan_words >= zoned_plan_words(...)
  *   blob_bytes (host) receives the size of the packed blob
  * The plan is self-describing; the caller copies the same words to device
- * memory for zoned_pack / decode_attention_zoned.
+ * memory for zoned_pack / decode_attention_zoned.  Those two calls validate
+ * the host words before any launch (header, every unit record re-derived
+ * from its token and channel counts, blob size, channel permutation, and
+ * for zoned_pack the token map) and read the device copy in the kernels, so
+ * the device words must be an unmodified copy of the host words.
  * Errors: DQA_ERR_NULL, DQA_ERR_SHAPE, DQA_ERR_BITS (a width outside its
  * set), DQA_ERR_WORKSPACE (plan_words too small). */
 int zoned_plan(const int8_t* v_bits, const int8_t* k_bits, int B, int Hkv,
@@ -259,6 +268,8 @@ int zoned_plan(const int8_t* v_bits, const int8_t* k_bits, int B, int Hkv,
 
 /* Pack the cache into the blob described by the plan.
  *   plan_host (host) and plan_dev (device): the same words from zoned_plan
+ *             (plan_dev a copy of plan_host; a plan that zoned_plan could
+ *             not have written is DQA_ERR_PLAN)
  *   k, v      (device) fp16 [B][Hkv][T_old][d] (the sink tokens are their
  *             first rows)
  *   k_new, v_new (device) fp16 [B][Hkv][C_new][d] (may be NULL if C_new == 0)
@@ -276,10 +287,13 @@ size_t decode_attention_zoned_workspace_bytes(const int32_t* plan_host, int Hq);
 /* Decode attention over zones A (kept tokens, masked slots skipped), B and
  * C, with dequantization fused into the products.
  *   q (device) fp16 [B][Hq][d], Hq a multiple of Hkv (ratio as above)
+ *   plan_host, plan_dev as for zoned_pack
+ *   blob (device) as written by zoned_pack
  *   out (device) fp32 [B][Hq][d]
+ * blob, ws and out must be 16-byte aligned (DQA_ERR_ALIGN).
  * Enqueues the split kernel and, with several splits, their merge.
  * Errors: DQA_ERR_NULL, DQA_ERR_PLAN, DQA_ERR_SHAPE, DQA_ERR_WORKSPACE,
- * DQA_ERR_UNSUPPORTED, DQA_ERR_HIP. */
+ * DQA_ERR_ALIGN, DQA_ERR_UNSUPPORTED, DQA_ERR_HIP. */
 int decode_attention_zoned(const uint16_t* q, int Hq, const int32_t* plan_host,
                            const int32_t* plan_dev, const void* blob,
                            float sm_scale, void* ws, size_t ws_bytes,
@@ -304,7 +318,9 @@ size_t rvq_encode_workspace_bytes(int N, int Kc);
  *   codebooks (device) fp16 [N][Kc][d], 1 <= N <= 8, 64 <= Kc <= 32768, Kc % 64 == 0
  *   idx       (device) int16 [n][N]
  *   ws        (device) >= rvq_encode_workspace_bytes(N, Kc)
- * Errors: DQA_ERR_NULL, DQA_ERR_SHAPE, DQA_ERR_WORKSPACE, DQA_ERR_HIP. */
+ * x, codebooks and ws must be 16-byte aligned (DQA_ERR_ALIGN).
+ * Errors: DQA_ERR_NULL, DQA_ERR_SHAPE, DQA_ERR_WORKSPACE, DQA_ERR_ALIGN,
+ * DQA_ERR_HIP. */
 int rvq_encode(const uint16_t* x, int64_t n, int d, const uint16_t* codebooks,
                int N, int Kc, int16_t* idx, void* ws, size_t ws_bytes,
                void* stream);

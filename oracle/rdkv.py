@@ -27,8 +27,9 @@ Readings fixed here:
   the unit prefers b' exactly while lam < w (2^-b - 2^-b') / (b' - b); the
   four factors 3/8, 3/32, 15/1024, 255/524288 decrease, so the minimizing
   width is 2[lam < 3w/8] + 2[lam < 3w/32] + 4[lam < 15w/1024]
-  + 8[lam < 255w/524288].  The rule is evaluated with exact products (a
-  float32 weight times one of these factors is exact in float64).
+  + 8[lam < 255w/524288].  The products w * factor are formed in float64:
+  exact for float32 weights (the tests' hand-made and GPU-produced weights),
+  one rounding for float64 weights.
 * a budget covers one row of units; the pipeline below uses one row per
   sequence, over all its KV heads (the objective sums over every unit of the
   cache under one B), with B = floor(average width x number of units).
@@ -159,13 +160,14 @@ def budget_bits(avg_width, n_units):
 def rdkv_widths(q16, k16, sm_scale, v_avg_width, k_avg_width):
     """Phases 1-3: (v_bits [B, Hkv, T], k_bits [B, Hkv, d]) int8.  One row per
     sequence over all its KV heads; the value budget counts tokens, the key
-    budget channels.  Token weights are rounded to float32 before the
-    allocation, as the GPU path stores them."""
+    budget channels.  The allocation runs on the weights exactly as their
+    definitions give them (float64), as [P3 sec 2.1] and [P3 sec 2.2,
+    bit-allocation pipeline] define the objective on w_u itself."""
     B, Hq, T, d = np.shape(q16)
     Hkv = np.shape(k16)[1]
-    wt = token_weights(q16, k16, sm_scale).astype(np.float32)
+    wt = token_weights(q16, k16, sm_scale)
     vb = allocate(wt.reshape(B, Hkv * T), budget_bits(v_avg_width, Hkv * T))
     vb = vb.reshape(B, Hkv, T)
-    wc = channel_weights(q16, k16, vb).astype(np.float32)
+    wc = channel_weights(q16, k16, vb)
     kb = allocate(wc.reshape(B, Hkv * d), budget_bits(k_avg_width, Hkv * d))
     return vb, kb.reshape(B, Hkv, d)

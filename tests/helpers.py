@@ -38,6 +38,16 @@ def worst_row_rel(got, ref):
     return float((num / den).max())
 
 
+def check_attention(got, ref, tol, label=""):
+    """Attention parity: relative L2 over the whole output and the worst
+    (batch, query head) row's relative L2, both within tol."""
+    err, worst = rel_l2(got, ref), worst_row_rel(got, ref)
+    print(f"{label} rel_l2={err:.3e} worst_row={worst:.3e}", flush=True)
+    assert err <= tol, (label, err)
+    assert worst <= tol, (label, worst)
+    return err
+
+
 def oracle_cache(inp, bits, Hq, rope_theta):
     """Oracle's own quantize + pack of the inputs, as the dict
     oracle.kivi_decode_attention reads."""

@@ -196,6 +196,75 @@ def test_zoned_plan_validation():
                                       0.1, FAKE, 1 << 20, FAKE, None) == 5   # ratio 3 not built
     assert lib.decode_attention_zoned(FAKE, 4, ctypes.c_void_p(words.ctypes.data), FAKE, FAKE,
                                       0.1, FAKE, 16, FAKE, None) == 4
+    odd = ctypes.c_void_p(0x1008)
+    for blob_p, ws_p, out_p in ((odd, FAKE, FAKE), (FAKE, odd, FAKE), (FAKE, FAKE, odd)):
+        assert lib.decode_attention_zoned(FAKE, 4, ctypes.c_void_p(words.ctypes.data), FAKE, blob_p,
+                                          0.1, ws_p, 1 << 20, out_p, None) == 8
+
+
+# plan word indices (header and unit record), as zoned.hip lays them out
+H_BLOB_LO, H_MAX_GROUPS, H_UNIT_OFF, H_PERM_OFF, H_TOK_OFF = 8, 10, 11, 12, 13
+U_N, U_M, U_SEG_OFF, U_SIZE, U_TOK_PREFIX = 0, 4, 20, 32, 34
+UNIT_WORDS = 40
+
+
+def _corruptions(words, units, d, T):
+    """(name, corrupted copy, token-map-only) for a valid plan."""
+    u1 = 16 + UNIT_WORDS          # record of unit 1
+    perm0, tok0 = words[H_PERM_OFF], words[H_TOK_OFF]
+    out = []
+
+    def mod(name, fn, tok_only=False):
+        w = words.copy()
+        fn(w)
+        out.append((name, w, tok_only))
+
+    mod("truncated (last unit's record and tables zeroed)",
+        lambda w: w.__setitem__(slice(16 + (units - 1) * UNIT_WORDS, None), 0))
+    mod("unit record offset", lambda w: w.__setitem__(H_UNIT_OFF, 17))
+    mod("permutation offset", lambda w: w.__setitem__(H_PERM_OFF, perm0 + 1))
+    mod("token map offset", lambda w: w.__setitem__(H_TOK_OFF, tok0 - 1))
+    mod("max groups", lambda w: w.__setitem__(H_MAX_GROUPS, w[H_MAX_GROUPS] + 1))
+    mod("blob size", lambda w: w.__setitem__(H_BLOB_LO, w[H_BLOB_LO] + 256))
+    mod("unit size", lambda w: w.__setitem__(u1 + U_SIZE, w[u1 + U_SIZE] + 256))
+    mod("segment offset", lambda w: w.__setitem__(u1 + U_SEG_OFF + 1, w[u1 + U_SEG_OFF + 1] + 16))
+    mod("kept tokens beyond T_old", lambda w: w.__setitem__(u1 + U_N, T + 1))
+    mod("negative channel count", lambda w: w.__setitem__(u1 + U_M, -1))
+    mod("channels beyond d", lambda w: w.__setitem__(u1 + U_M + 3, d + 1))
+    mod("token-map prefix", lambda w: w.__setitem__(u1 + U_TOK_PREFIX + 1, w[u1 + U_TOK_PREFIX + 1] + 1))
+    mod("unused record word", lambda w: w.__setitem__(u1 + 39, 5))
+    mod("channel listed twice", lambda w: w.__setitem__(perm0 + d + 1, w[perm0 + d]))
+    mod("channel out of range", lambda w: w.__setitem__(perm0 + 2, d))
+    mod("token out of range", lambda w: w.__setitem__(tok0 + T, T), tok_only=True)
+    mod("tokens out of order", lambda w: w.__setitem__(slice(tok0, tok0 + 2), w[tok0:tok0 + 2][::-1].copy()),
+        tok_only=True)
+    return out
+
+
+@pytest.mark.parametrize("sink,k_out", [(0, 0), (3, 2)])
+def test_zoned_plan_corruption_refused(sink, k_out):
+    """A plan zoned_plan could not have written is refused (DQA_ERR_PLAN)
+    by every entry point that reads it, before any launch: truncated plans,
+    shifted offsets, records that disagree with their own counts, a wrong
+    blob size, a broken channel permutation; the token map (read by the
+    packer only) is checked by zoned_pack."""
+    rng = np.random.default_rng(9)
+    B, H, T, d = 2, 3, 100, 128
+    vb = rng.choice([0, 2, 4, 8, 16], size=(B, H, T), p=[.3, .3, .2, .1, .1]).astype(np.int8)
+    kb = rng.choice([2, 4, 8, 16], size=(B, H, d), p=[.4, .3, .2, .1]).astype(np.int8)
+    st, words, blob = _plan(vb, kb, 8, d, sink, k_out)
+    assert st == 0
+    # each unit keeps several tokens, so a token-map entry can be moved
+    assert (vb[0, 0, sink:] != 0).sum() >= 2
+    ptr = lambda w: ctypes.c_void_p(w.ctypes.data)
+    assert lib.decode_attention_zoned_workspace_bytes(ptr(words), 4 * H) > 0
+    for name, w, tok_only in _corruptions(words, B * H, d, T):
+        assert lib.zoned_pack(ptr(w), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 7, name
+        if tok_only:
+            continue
+        assert lib.decode_attention_zoned_workspace_bytes(ptr(w), 4 * H) == 0, name
+        assert lib.decode_attention_zoned(FAKE, 4 * H, ptr(w), FAKE, FAKE, 0.1, FAKE, 1 << 30, FAKE,
+                                          None) == 7, name
 
 
 def test_rvq_validation_and_workspace():
@@ -209,6 +278,10 @@ def test_rvq_validation_and_workspace():
     assert lib.rvq_encode(None, 10, 128, FAKE, 4, 1024, FAKE, FAKE, ws, None) == 1
     assert lib.rvq_encode(FAKE, 10, 128, FAKE, 4, 1024, FAKE, FAKE, 100, None) == 4
     assert lib.rvq_encode(None, 0, 128, None, 4, 1024, None, None, 0, None) == 0    # empty
+    odd = ctypes.c_void_p(0x1004)
+    assert lib.rvq_encode(odd, 10, 128, FAKE, 4, 1024, FAKE, FAKE, ws, None) == 8     # alignment
+    assert lib.rvq_encode(FAKE, 10, 128, odd, 4, 1024, FAKE, FAKE, ws, None) == 8
+    assert lib.rvq_encode(FAKE, 10, 128, FAKE, 4, 1024, FAKE, odd, ws, None) == 8
     w = lib.rvq_decode_attention_workspace_bytes(2, 24, 8, 8192, 128)
     assert w > 16 * 65536                     # room for a 64 KB key-logit table per unit
     assert lib.rvq_decode_attention_workspace_bytes(2, 24, 8, 8192, 64) == 0
@@ -227,7 +300,7 @@ def test_rvq_validation_and_workspace():
 
 def test_kivi_append_validation():
     """Argument checks of the streaming append (all fail before any launch)."""
-    assert lib.dqa_abi_version() == 7
+    assert lib.dqa_abi_version() == 8
     c = _cache(T_cap=128, R_cap=128)
     # staging holds the recent and the new rows of K and V
     assert lib.kivi_append_workspace_bytes(ctypes.byref(c), 20) == 2 * 2 * 2 * (16 + 20) * 128 * 2
@@ -262,6 +335,18 @@ def test_kivi_append_validation():
     c1 = _cache(B=0, T_cap=128, R_cap=128)
     assert lib.kivi_append(ctypes.byref(c1), FAKE, FAKE, 40, 16, None, 0, None) == 0
     assert (c1.T_q, c1.R) == (64 + 32, 16 + 40 - 32)
+    # a capacity of 0 means the current count; the call writes back the
+    # capacity it used, so the recent rows keep their stride when R shrinks
+    c2 = _cache(B=0, T_q=64, R=40, T_cap=96, R_cap=0)
+    assert lib.kivi_append(ctypes.byref(c2), None, None, 0, 8, None, 0, None) == 0
+    assert (c2.T_q, c2.R, c2.T_cap, c2.R_cap) == (96, 8, 96, 40)
+    c3 = _cache(B=0, T_q=64, R=16, T_cap=0, R_cap=0)
+    assert lib.kivi_append(ctypes.byref(c3), None, None, 0, 16, None, 0, None) == 0
+    assert (c3.T_q, c3.R, c3.T_cap, c3.R_cap) == (64, 16, 64, 16)
+    # a failed call leaves the capacities as they were
+    c4 = _cache(B=0, T_q=64, R=40, T_cap=0, R_cap=0)
+    assert lib.kivi_append(ctypes.byref(c4), None, None, 0, 8, None, 0, None) == 2
+    assert (c4.T_q, c4.R, c4.T_cap, c4.R_cap) == (64, 40, 0, 0)
 
 
 def test_rdkv_validation():

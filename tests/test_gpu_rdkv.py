@@ -22,7 +22,7 @@ import pytest
 import torch
 
 import oracle
-from helpers import say, dev, host
+from helpers import say, dev, host, check_attention
 from workloads import rdkv_inputs, zoned_inputs, CONFIGS
 
 pytestmark = pytest.mark.gpu
@@ -192,12 +192,12 @@ def test_widths_pipeline(dqa, case):
     assert np.array_equal(kb, oracle.allocate(wc.reshape(B, -1).astype(np.float64), kbud).reshape(kb.shape))
     # against the oracle's own pipeline: equal except at near-ties
     rvb, rkb = oracle.rdkv_widths(inp["q"], inp["k"], scale, vm, km)
-    rwt = oracle.token_weights(inp["q"], inp["k"], scale).astype(np.float32)
+    rwt = oracle.token_weights(inp["q"], inp["k"], scale)
     for b in range(B):
         assert _near_tie_only(vb[b], rvb[b], rwt[b], vbud)
         assert vb[b].astype(int).sum() <= vbud and kb[b].astype(int).sum() <= kbud
     if np.array_equal(vb, rvb):
-        rwc = oracle.channel_weights(inp["q"], inp["k"], vb).astype(np.float32)
+        rwc = oracle.channel_weights(inp["q"], inp["k"], vb)
         for b in range(B):
             assert _near_tie_only(kb[b], rkb[b], rwc[b], kbud)
 
@@ -217,8 +217,7 @@ def test_maps_drive_the_zoned_cache(dqa):
     qd = z["q"]
     out = host(dqa.decode_attention_zoned(dev(qd), plan, blob, d ** -0.5))
     ref = oracle.zoned_decode_attention(qd, inp["k"], z["v"], vb, kb, z["k_new"], z["v_new"], d ** -0.5)
-    num = np.linalg.norm(out.astype(np.float64) - ref)
-    assert num / np.linalg.norm(ref) <= 1e-3
+    check_attention(out, ref, 1e-3, "rdkv maps -> zoned decode")
 
 
 def test_full_size_invariants(dqa):
@@ -237,6 +236,12 @@ def test_full_size_invariants(dqa):
     tail = np.arange(T - 16, T)
     ref_tail = oracle.token_weight_rows(inp["q"], inp["k"], scale, tail)[..., T - 16:]
     assert _rel(wt[..., T - 16:], ref_tail) <= WTOL
+    # a slice three quarters into the sequence, for one (batch, KV head):
+    # its weights need every query position from the slice on
+    m, b0, h0 = 3 * T // 4, 1, 5
+    ref_mid = oracle.token_weight_rows(inp["q"][b0:b0 + 1, h0 * G:(h0 + 1) * G], inp["k"][b0:b0 + 1, h0:h0 + 1],
+                                       scale, np.arange(m, T))[0, 0, m:m + 64]
+    assert _rel(wt[b0, h0, m:m + 64], ref_mid) <= WTOL
     vb, kb = (host(t) for t in dqa.rdkv_widths(q, k, scale, vbud, kbud))
     assert np.array_equal(vb, oracle.allocate(wt.reshape(B, -1).astype(np.float64), vbud).reshape(vb.shape))
     wc = host(dqa.rdkv_channel_weights(q, k, dev(vb)))

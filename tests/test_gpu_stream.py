@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import oracle
-from helpers import dev, host, rel_l2, say, worst_row_rel
+from helpers import dev, host, check_attention, say
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-3
@@ -95,9 +95,7 @@ def test_append_matches_oracle_stream_and_decodes(dqa, case):
     scale = 1.0 / math.sqrt(d)
     got = host(dqa.decode_attention_qkv(dev(q), cache, scale))
     ref = oracle.kivi_decode_attention(q, _oracle_cache(st, Hq, bits, rope), scale)
-    err = rel_l2(got, ref)
-    print(f"T_q={cache.T_q} R={cache.R} rel_l2={err:.3e} worst_row={worst_row_rel(got, ref):.3e}", flush=True)
-    assert err <= TOL
+    check_attention(got, ref, TOL, f"T_q={cache.T_q} R={cache.R}")
 
 
 def test_append_one_token_per_step_flush_points(dqa):
@@ -169,3 +167,46 @@ def test_append_in_window_flush_every_width(dqa, bits, d):
             torch.cuda.synchronize()
             _check_state(cache, st, bits)
     assert flushes == 3 and (cache.T_q, cache.R) == (96, 24)
+
+
+def test_append_capacity_zero_keeps_row_stride(dqa):
+    """A direct C caller passes R_cap = 0 (the recent buffers hold exactly R
+    rows) and T_cap = the quantized capacity: a flush that shrinks R must
+    leave the rows of every (batch, KV head) at the old stride, so that the
+    next decode (and append) reads them where they are.  Four units, so a
+    wrong stride would misplace the rows of all but the first."""
+    import ctypes
+    B, Hq, Hkv, d, bits = 2, 4, 2, 64, 2
+    say("kivi_append R_cap = 0 through the C ABI")
+    k, v = _tokens(B, Hkv, 161, d, seed=21)
+    cache = _empty_gpu_cache(dqa, B, Hq, Hkv, d, bits, 64, 128, 1e4)
+    st = oracle.empty_stream(B, Hkv, d)
+    # 160 tokens with R_max = 128: one group quantized, the window full
+    dqa.kivi_append(cache, dev(k[:, :, :160]), dev(v[:, :, :160]), 128)
+    st = oracle.kivi_append(st, k[:, :, :160], v[:, :, :160], bits, 128)
+    assert (cache.T_q, cache.R) == (32, 128)
+    c = cache.struct()
+    c.R_cap = 0                                  # "R rows", i.e. 128
+    kn, vn = dev(k[:, :, 160:]), dev(v[:, :, 160:])
+    n = dqa.lib.kivi_append_workspace_bytes(ctypes.byref(c), 1)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    assert dqa.lib.kivi_append(ctypes.byref(c), dqa._ptr(kn), dqa._ptr(vn), 1, 128, dqa._ptr(ws), n,
+                               dqa._stream(kn.device)) == 0
+    st = oracle.kivi_append(st, k[:, :, 160:], v[:, :, 160:], bits, 128)
+    assert (c.T_q, c.R, c.T_cap, c.R_cap) == (64, 97, 64, 128)
+    cache.T_q, cache.R = c.T_q, c.R
+    torch.cuda.synchronize()
+    _check_state(cache, st, bits)
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((B, Hq, d)).astype(np.float16)
+    scale = 1.0 / math.sqrt(d)
+    # decode through the same descriptor the append updated
+    qd = dev(q)
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda:0")
+    nws = dqa.lib.decode_attention_workspace_bytes(ctypes.byref(c))
+    dws = torch.empty(nws, dtype=torch.uint8, device="cuda:0")
+    assert dqa.lib.decode_attention_qkv(dqa._ptr(qd), ctypes.byref(c), ctypes.c_float(scale), dqa._ptr(dws),
+                                        nws, dqa._ptr(out), dqa._stream(qd.device)) == 0
+    torch.cuda.synchronize()
+    ref = oracle.kivi_decode_attention(q, _oracle_cache(st, Hq, bits, 1e4), scale)
+    check_attention(host(out), ref, TOL, "after the R_cap = 0 flush")

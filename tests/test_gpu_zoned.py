@@ -8,7 +8,7 @@ import pytest
 import torch
 
 import oracle
-from helpers import say, dev, host, rel_l2, worst_row_rel
+from helpers import say, dev, host, check_attention
 from workloads import zoned_inputs, CONFIGS
 
 pytestmark = pytest.mark.gpu
@@ -74,9 +74,7 @@ def test_zoned_pack_and_decode(dqa, case):
     if np.all(inp["v_bits"] == 0) and C == 0:
         assert np.all(out == 0)
         return
-    err = rel_l2(out, ref)
-    print(f"rel_l2={err:.3e} worst_row={worst_row_rel(out, ref):.3e}", flush=True)
-    assert err <= TOL
+    check_attention(out, ref, TOL)
     out2 = host(dqa.decode_attention_zoned(dev(inp["q"]), plan, blob, scale))
     assert np.array_equal(out2, out)
 
@@ -94,8 +92,8 @@ def test_zoned_full_config_sampled(dqa):
     units, total = oracle.zoned_layout(inp["v_bits"], inp["k_bits"], cfg["d"], cfg["C"])
     assert got_blob.size == total
     G = cfg["Hq"] // cfg["Hkv"]
-    for b, h in [(0, 0), (1, 5)]:
-        # the oracle packs and attends one unit at a time
+    for b, h in [(b, h) for b in range(cfg["B"]) for h in range(cfg["Hkv"])]:
+        # every unit; the oracle packs and attends one unit at a time
         sl = lambda x: x[b:b + 1, h:h + 1]
         ref_blob = oracle.zoned_pack(sl(inp["k"]), sl(inp["v"]), sl(inp["v_bits"]), sl(inp["k_bits"]),
                                      sl(inp["k_new"]), sl(inp["v_new"]))
@@ -104,9 +102,7 @@ def test_zoned_full_config_sampled(dqa):
         ref = oracle.zoned_decode_attention(inp["q"][b:b + 1, h * G:(h + 1) * G], sl(inp["k"]), sl(inp["v"]),
                                             sl(inp["v_bits"]), sl(inp["k_bits"]), sl(inp["k_new"]),
                                             sl(inp["v_new"]), scale)
-        err = rel_l2(out[b, h * G:(h + 1) * G][None], ref)
-        print(f"mixed-width-zoned-16k unit ({b},{h}) rel_l2={err:.3e}", flush=True)
-        assert err <= TOL
+        check_attention(out[b, h * G:(h + 1) * G][None], ref, TOL, f"mixed-width-zoned-16k unit ({b},{h})")
 
 
 SINK_OUT_CASES = [
@@ -150,6 +146,4 @@ def test_zoned_sink_and_outliers(dqa, case):
     out = host(dqa.decode_attention_zoned(dev(inp["q"]), plan, blob, scale))
     ref = oracle.zoned_decode_attention(inp["q"], inp["k"], inp["v"], inp["v_bits"], inp["k_bits"],
                                         inp["k_new"], inp["v_new"], scale, sink=S, k_out=ko)
-    err = rel_l2(out, ref)
-    print(f"rel_l2={err:.3e} worst_row={worst_row_rel(out, ref):.3e}", flush=True)
-    assert err <= TOL
+    check_attention(out, ref, TOL)

@@ -198,7 +198,7 @@ def test_pipeline_meets_both_budgets():
     assert set(np.unique(vb)) <= set(WIDTHS) and set(np.unique(kb)) <= set(WIDTHS)
     # the most attended token of a sequence never gets fewer bits than the
     # least attended one
-    wt = oracle.token_weights(q, k, d ** -0.5).astype(np.float32)
+    wt = oracle.token_weights(q, k, d ** -0.5)
     for b in range(B):
         i, j = np.argmax(wt[b]), np.argmin(wt[b])
         assert vb[b].ravel()[i] >= vb[b].ravel()[j]
