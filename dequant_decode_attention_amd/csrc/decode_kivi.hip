@@ -33,6 +33,7 @@
 // partial softmax state; split_merge_kernel (merge.h) merges the splits of
 // every (batch, KV head) in split order.
 #include <cmath>
+#include <mutex>
 
 #include "common.h"
 #include "merge.h"
@@ -214,29 +215,44 @@ __device__ __forceinline__ float mix_dequant(uint32_t m, float s, uint32_t z) {
   return r;
 }
 
-// Value chunk (8 tokens of one channel) -> fp16 operand holding code *
-// 2^-24 exactly: a code placed in the low bits of an fp16 bit pattern with a
-// zero exponent field is the subnormal code * 2^-24, which the matrix cores
-// multiply exactly (the accumulator is rescaled by 2^24 once, at the end).
-// Element 2i holds token i, element 2i+1 token i+4 (the same order is used
-// for the probabilities).
+// Value chunk (8 tokens of one channel) -> fp16 operand holding the codes as
+// fp16 subnormals, each code at the top of the 10-bit mantissa field: bits
+// 8-9 (2-bit: code * 2^-16), 6-9 (4-bit: code * 2^-18) or 2-9 (8-bit: code *
+// 2^-22).  The matrix cores multiply subnormal inputs exactly, but they sum
+// the products of subnormal operands as if each had the smallest normal
+// exponent, so a code in the low mantissa bits would lose up to 10 bits of
+// its product (measured on MI355X: sums of 32 such products off by up to
+// 1.5e-4 relative, biased toward zero; with the codes at the top, within a
+// few fp32 ulps).  The accumulator runs in the code * 2^-kCodeShift domain and
+// is rescaled once.  Element 2i holds token i, element 2i+1 token i+4 (the
+// same order is used for the probabilities).
+template <int BITS>
+constexpr int kCodeShift = BITS == 2 ? 16 : (BITS == 4 ? 18 : 22);
+template <int BITS>
+constexpr float kCodeScale = static_cast<float>(1u << kCodeShift<BITS>);
+
 template <int BITS>
 __device__ __forceinline__ half8 value_codes8(uint64_t chunk, uint32_t mask) {
   uint32_t r[4];
   if constexpr (BITS == 2) {
+    // tokens 0..3 at bits 0..7, tokens 4..7 at bits 16..23; token i (and
+    // i + 4) shifted to bits 8..9 (24..25)
     const uint32_t v = static_cast<uint32_t>(chunk);
     const uint32_t u = v | (v << 8);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) r[i] = (u >> (2 * i)) & mask;
+    for (int i = 0; i < 4; ++i) r[i] = (u << (8 - 2 * i)) & mask;
   } else if constexpr (BITS == 4) {
+    // token i at bits 4i..4i+3 and token i + 4 at 16 + 4i; moved to bits 6..9
     const uint32_t w = static_cast<uint32_t>(chunk);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) r[i] = (w >> (4 * i)) & mask;
+    r[0] = (w << 6) & mask;
+    r[1] = (w << 2) & mask;
+    r[2] = (w >> 2) & mask;
+    r[3] = (w >> 6) & mask;
   } else {
     const uint32_t lo = static_cast<uint32_t>(chunk), hi = static_cast<uint32_t>(chunk >> 32);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      r[i] = __builtin_amdgcn_perm(hi, lo, static_cast<uint32_t>(i | (0x0C << 8) | ((4 + i) << 16) | (0x0C << 24)));
+      r[i] = __builtin_amdgcn_perm(hi, lo, static_cast<uint32_t>(i | (0x0C << 8) | ((4 + i) << 16) | (0x0C << 24))) << 2;
   }
   half8 out;
 #pragma unroll
@@ -247,9 +263,6 @@ __device__ __forceinline__ half8 value_codes8(uint64_t chunk, uint32_t mask) {
   }
   return out;
 }
-// the value accumulator of quantized tiles is kept scaled by 2^-24
-constexpr float kCodeScale = 16777216.0f;   // 2^24
-
 // token offset (inside the lane's 8-token run) of operand element e
 __device__ __forceinline__ constexpr int vtok(int e) { return (e >> 1) + 4 * (e & 1); }
 
@@ -540,8 +553,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kDecodeWave
   const uint8_t* const kbase = reinterpret_cast<const uint8_t*>(a.k_codes) + unit * qstride * kGroup * KROW;
   const uint8_t* const vbase = reinterpret_cast<const uint8_t*>(a.v_codes) + unit * qstride * VBLK;
   constexpr int VW = BITS == 8 ? 2 : 1;   // 32-bit words per value chunk
-  // two codes per register: one in each fp16 half (subnormal code * 2^-24)
-  const uint32_t vmask = opaque(BITS == 2 ? 0x00030003u : 0x000F000Fu);
+  // two codes per register, one in each fp16 half, at the top of the
+  // subnormal mantissa (value_codes8)
+  const uint32_t vmask = opaque(BITS == 2 ? 0x03000300u : 0x03C003C0u);
   // a tile's raw inputs, loaded one tile ahead into registers that are not
   // touched until the tile is processed
   struct TileIn {
@@ -725,10 +739,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kDecodeWave
   if (qb < qe) load_tile(qb, buf0);
   for (int k = 0; k < r_mine; ++k) recent_tile(r_first + k);
   // fp16 value products are exact-scale; switch the accumulator to the
-  // 2^-24 domain of the code products (exact: a power of two)
+  // code-product domain (a power of two: exact)
   if (r_mine > 0) {
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) acc[mb] *= 1.0f / kCodeScale;
+    for (int mb = 0; mb < MB; ++mb) acc[mb] *= 1.0f / kCodeScale<BITS>;
   }
   if constexpr (!ROPE) {
     if (r_mine > 0) {
@@ -750,7 +764,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kDecodeWave
     for (int mb = 0; mb < MB; ++mb)
       if (mb / 2 == vg)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) lds_o[wave][qh][16 * mb + 4 * grp + r] = fmaf(acc[mb][r], kCodeScale, zacc);
+        for (int r = 0; r < 4; ++r) lds_o[wave][qh][16 * mb + 4 * grp + r] = fmaf(acc[mb][r], kCodeScale<BITS>, zacc);
   }
   if (lane < G) {
     lds_m[wave][lane] = m;
@@ -823,6 +837,34 @@ void launch_decode(const KiviArgs& a, int G, int bits, bool rope, dim3 grid, hip
 
 }  // namespace
 }  // namespace dqa
+
+// Partial-state memory of decode_attention_qkv_noalloc: one array per GPU
+// the library runs on, held until the process ends.  Host code never uses
+// the array's name as an address: the device address of each GPU's copy
+// comes from hipGetSymbolAddress, taken once per device.
+constexpr size_t kNoAllocScratchBytes = size_t{2} << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address (nullptr if it cannot be had).  The
+// first call on a device looks the symbol up with that device current.
+void* scratch_address(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
 
 using namespace dqa;
 
@@ -918,4 +960,20 @@ extern "C" int decode_attention_qkv(const uint16_t* q, const dqa_kivi_cache* c,
   const int st = decode_attention_qkv_partial(q, c, sm_scale, ws, ws_bytes, out, stream);
   if (st != DQA_OK) return st;
   return decode_attention_qkv_merge(c, ws, ws_bytes, out, stream);
+}
+
+extern "C" size_t decode_attention_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
+
+extern "C" int decode_attention_qkv_noalloc(const uint16_t* q, const dqa_kivi_cache* c, float sm_scale,
+                                            float* out, void* stream) {
+  Plan p;
+  const int st = make_plan(c, &p);
+  if (st != DQA_OK) return st;
+  if (p.ws_bytes > kNoAllocScratchBytes) return DQA_ERR_WORKSPACE;
+  if (p.units == 0) return DQA_OK;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return DQA_ERR_HIP;
+  void* ws = scratch_address(dev);
+  if (!ws) return DQA_ERR_HIP;
+  return decode_attention_qkv(q, c, sm_scale, ws, kNoAllocScratchBytes, out, stream);
 }
