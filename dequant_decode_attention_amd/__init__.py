@@ -55,6 +55,8 @@ _SIGS = {
     "quantize_pack_v": (_i, [_vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp]),
     "decode_attention_workspace_bytes": (_sz, [ctypes.POINTER(KiviCacheStruct)]),
     "decode_attention_qkv": (_i, [_vp, ctypes.POINTER(KiviCacheStruct), _f, _vp, _sz, _vp, _vp]),
+    "decode_attention_qkv_noalloc": (_i, [_vp, ctypes.POINTER(KiviCacheStruct), _f, _vp, _vp]),
+    "decode_attention_noalloc_scratch_bytes": (_sz, []),
     "decode_attention_qkv_partial": (_i, [_vp, ctypes.POINTER(KiviCacheStruct), _f, _vp, _sz, _vp, _vp]),
     "decode_attention_qkv_merge": (_i, [ctypes.POINTER(KiviCacheStruct), _vp, _sz, _vp, _vp]),
     "kivi_append_workspace_bytes": (_sz, [ctypes.POINTER(KiviCacheStruct), _i]),
@@ -210,6 +212,19 @@ def decode_attention_qkv(q, cache, sm_scale, out=None, workspace=None):
     _check("decode_attention_qkv",
            lib.decode_attention_qkv(_ptr(q), ctypes.byref(st), float(sm_scale), _ptr(ws),
                                     ws.numel(), _ptr(out), _stream(q.device)))
+    return out
+
+
+def decode_attention_qkv_noalloc(q, cache, sm_scale, out):
+    """decode_attention_qkv with the library's per-GPU partial-state array
+    instead of a workspace (the call allocates no device memory; calls that
+    overlap on one GPU race).  out: fp32 [B, Hq, d], provided by the caller."""
+    q = _dev16(q, "q")
+    st = cache.struct()
+    with torch.cuda.device(q.device):
+        _check("decode_attention_qkv_noalloc",
+               lib.decode_attention_qkv_noalloc(_ptr(q), ctypes.byref(st), float(sm_scale), _ptr(out),
+                                                _stream(q.device)))
     return out
 
 

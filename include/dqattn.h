@@ -56,7 +56,8 @@ enum {
 const char* dqa_status_string(int status);
 
 /* Version of this interface (increments on any signature or layout change). */
-int dqa_abi_version(void);  /* 8: decode_attention_zoned and rvq_encode check
+int dqa_abi_version(void);  /* 9: decode_attention_qkv_noalloc;
+                              8: decode_attention_zoned and rvq_encode check
                               16-byte alignment; zoned plans are validated in
                               full; kivi_append writes back zero capacities;
                               7: quantize_pack_k/v and zoned_pack check
@@ -181,6 +182,25 @@ int decode_attention_qkv_partial(const uint16_t* q, const dqa_kivi_cache* cache,
                                  float* out, void* stream);
 int decode_attention_qkv_merge(const dqa_kivi_cache* cache, const void* ws,
                                size_t ws_bytes, float* out, void* stream);
+
+/* decode_attention_qkv for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and results, with the partial softmax states
+ * kept in a library-owned device array of decode_attention_noalloc_scratch_bytes()
+ * bytes (2 MiB) per GPU, held until the process ends, instead of a caller
+ * workspace.  The array of the current device is used (the stream must
+ * belong to it); its address is looked up once per device, on the first
+ * call there.  The call itself allocates nothing.  Every call on a GPU shares
+ * that GPU's array: calls that may overlap on one GPU (different streams,
+ * or host threads) race and must be ordered by the caller.  The array needs
+ * no clearing: every split writes its whole state before the merge reads it.
+ * Arguments as decode_attention_qkv without ws / ws_bytes.
+ * Errors: as decode_attention_qkv; DQA_ERR_WORKSPACE when the cache shape
+ * needs more partial-state memory than the array holds (before any launch);
+ * DQA_ERR_HIP when the array's address cannot be obtained. */
+size_t decode_attention_noalloc_scratch_bytes(void);
+int decode_attention_qkv_noalloc(const uint16_t* q, const dqa_kivi_cache* cache,
+                                 float sm_scale, float* out, void* stream);
 
 /* Streaming append to the cache ([P1 para 8]: per-channel key statistics
  * need tokens not generated yet, so the newest tokens stay in fp16, up to

@@ -119,6 +119,24 @@ def test_decode_workspace_query_and_validation():
     assert lib.decode_attention_workspace_bytes(None) == 0
 
 
+def test_noalloc_decode_validation():
+    """The allocation-free decode rejects, before any HIP call, a shape whose
+    partial states exceed the library's array, and validates like the
+    workspace variant."""
+    scratch = lib.decode_attention_noalloc_scratch_bytes()
+    assert scratch == 2 << 20
+    f = lib.decode_attention_qkv_noalloc
+    assert f(FAKE, ctypes.byref(_cache(d=96)), 0.1, FAKE, None) == 2
+    assert f(FAKE, ctypes.byref(_cache(bits=3)), 0.1, FAKE, None) == 3
+    # grow the batch until the partial states no longer fit the array
+    B = 1
+    while lib.decode_attention_workspace_bytes(ctypes.byref(_cache(B=B, Hkv=8, Hq=32, T_q=256, R=0))) <= scratch:
+        B += 1
+        assert B < 4096
+    assert f(FAKE, ctypes.byref(_cache(B=B, Hkv=8, Hq=32, T_q=256, R=0)), 0.1, FAKE, None) == 4
+    assert f(None, ctypes.byref(_cache(B=0)), 0.1, None, None) == 0      # empty: nothing to do
+
+
 def test_stream_copy_validation():
     assert lib.dqa_stream_copy(FAKE, None, 64, None) == 1
     assert lib.dqa_stream_copy(FAKE, FAKE, 20, None) == 2
@@ -300,7 +318,7 @@ def test_rvq_validation_and_workspace():
 
 def test_kivi_append_validation():
     """Argument checks of the streaming append (all fail before any launch)."""
-    assert lib.dqa_abi_version() == 8
+    assert lib.dqa_abi_version() == 9
     c = _cache(T_cap=128, R_cap=128)
     # staging holds the recent and the new rows of K and V
     assert lib.kivi_append_workspace_bytes(ctypes.byref(c), 20) == 2 * 2 * 2 * (16 + 20) * 128 * 2
