@@ -7,9 +7,9 @@ One step = one decode step over the whole batch, i.e. what
 decode_attention_qkv enqueues: the split kernel (kivi_decode_kernel: every
 quantized token's packed codes and scales plus the fp16 recent zone are read
 from HBM, dequantized, rotated and attended) and the merge of the splits
-(kivi_merge_kernel).  The two phases are enqueued through their own entry
-points so that HIP events can bracket the split kernel inside the timed
-region; its average duration gives the roofline figure.  Inputs are resident
+(split_merge_kernel).  The split kernel's average duration, for the roofline
+figure, is timed separately over back-to-back launches of the split phase
+alone.  Inputs are resident
 in HBM before the timed region.  The compressed cache (~98 MiB) fits in the
 256 MB Infinity Cache, so the timed steps rotate over several independent
 replicas whose total exceeds it.
@@ -18,7 +18,9 @@ The line also carries "rows": the other steps of the path timed on their
 own workloads with HIP events, each against its own roofline (quantize +
 pack of the 32k cache; zoned pack and decode on the mixed-width 16k cache;
 residual-VQ encode, MFMA-bound, and decode on the 8k Llama-3.2-3B-shaped
-cache), and "cpu_baseline": the oracle timed on a sample of the same step.
+cache; the decode at the other bit width and on the Llama-2-13B-shaped layer),
+and "cpu_baseline": the oracle timed on a sample of the same step, with BLAS
+on every core of the affinity mask and on one thread.
 
 Prints one JSON line.  Usage:
     python bench.py [--steps K] [--warmup W] [--bits 2|4] [--replicas R]
@@ -82,12 +84,21 @@ def algorithmic_bytes(cfg, bits):
     return codes + k_sz + v_sz + recent + B * Hq * d * 2 + B * Hq * d * 4
 
 
-def cpu_baseline(inp, cfg, bits, scale, budget_s=12.0):
-    """Time the oracle's decode (dequantization from packed buffers + fp64
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_step_rate(inp, cfg, bits, scale, budget_s):
+    """The oracle's decode (dequantization from the packed buffers + fp64
     attention) on whole (batch, KV head) units until the budget is spent;
-    scale to KV-tokens/s of the full step."""
+    returns (KV-tokens/s of the full step, units done, seconds)."""
     import oracle
-    from threadpoolctl import threadpool_info
     B, Hkv, G = cfg["B"], cfg["Hkv"], cfg["Hq"] // cfg["Hkv"]
     units = [(b, h) for b in range(B) for h in range(Hkv)]
     done, elapsed = 0, 0.0
@@ -107,11 +118,25 @@ def cpu_baseline(inp, cfg, bits, scale, budget_s=12.0):
         if elapsed > budget_s:
             break
     step_s = elapsed / done * len(units)
-    blas = [i.get("num_threads", 1) for i in threadpool_info()]
-    return dict(value=B * (cfg["T_q"] + cfg["R"]) / step_s, unit="KV-tokens/s",
-                cores=int(max(blas) if blas else 1), kind="oracle",
-                sample=f"{done} of {len(units)} (batch, KV head) units, {elapsed:.1f} s; "
-                       f"numpy dequantization + fp64 attention, scaled to the full step")
+    return B * (cfg["T_q"] + cfg["R"]) / step_s, done, len(units), elapsed
+
+
+def cpu_baseline(inp, cfg, bits, scale, budget_s=10.0):
+    """The oracle timed on this machine's host cores in two settings: BLAS
+    threads = every core in the process's affinity mask, and one thread."""
+    from threadpoolctl import threadpool_limits
+    ncores = len(os.sched_getaffinity(0))
+    with threadpool_limits(limits=ncores):
+        v_all, done, n, el = _oracle_step_rate(inp, cfg, bits, scale, budget_s)
+    with threadpool_limits(limits=1):
+        v_one, done1, n1, el1 = _oracle_step_rate(inp, cfg, bits, scale, budget_s)
+    return dict(value=v_all, unit="KV-tokens/s", cores=ncores, kind="oracle",
+                sample=f"{done} of {n} (batch, KV head) units, {el:.1f} s, BLAS threads = {ncores} "
+                       f"(every core in the affinity mask); numpy dequantization + fp64 attention, "
+                       f"scaled to the full step",
+                single_thread={"value": v_one, "cores": 1,
+                               "sample": f"{done1} of {n1} units, {el1:.1f} s, BLAS threads = 1"},
+                cpu_model=_cpu_model())
 
 
 MFMA_FP16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 matrix peak, published
@@ -324,6 +349,75 @@ def time_rvq(dqa, torch, dev):
     return out
 
 
+def time_decode(dqa, torch, dev, cfg, bits, replicas, steps, warmup, inp=None):
+    """One decode step = decode_attention_qkv_partial (the split kernel) +
+    decode_attention_qkv_merge, over `replicas` independent copies of the
+    quantized cache (rotated so that the working set exceeds the 256 MB
+    Infinity Cache).  Returns the step time from HIP events around `steps`
+    steps, and the split kernel's average duration from HIP events around
+    `steps` back-to-back split-kernel launches (no merge in between)."""
+    from workloads import kivi_inputs
+    if inp is None:
+        inp = kivi_inputs(cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["d"], cfg["T_q"], cfg["R"], seed=cfg["seed"],
+                          outliers=cfg["outliers"])
+    scale = 1.0 / math.sqrt(cfg["d"])
+    k = torch.from_numpy(inp["k"]).to(dev)
+    v = torch.from_numpy(inp["v"]).to(dev)
+    kc, ks, kz = dqa.quantize_pack_k(k, bits)
+    vc, vs, vz = dqa.quantize_pack_v(v, bits)
+    del k, v
+    kr = torch.from_numpy(inp["k_recent"]).to(dev)
+    vr = torch.from_numpy(inp["v_recent"]).to(dev)
+    q = torch.from_numpy(inp["q"]).to(dev)
+    caches = []
+    for _ in range(replicas):
+        t = [x.clone() for x in (kc, ks, kz, vc, vs, vz)]
+        t += [x.clone() if x.shape[2] > 0 else None for x in (kr, vr)]
+        caches.append(dqa.KiviCache(cfg["Hq"], bits, *t, rope_theta=cfg["rope_theta"], T_q=cfg["T_q"],
+                                    B=cfg["B"], Hkv=cfg["Hkv"], d=cfg["d"]))
+    del kc, ks, kz, vc, vs, vz
+    out = torch.empty((cfg["B"], cfg["Hq"], cfg["d"]), dtype=torch.float32, device=dev)
+    ws = [c.workspace(dev) for c in caches]
+    stream = torch.cuda.current_stream(dev)
+    torch.cuda.synchronize()
+
+    def step(i):
+        c, w = caches[i % len(caches)], ws[i % len(ws)]
+        dqa.decode_attention_qkv_partial(q, c, scale, out, w)
+        dqa.decode_attention_qkv_merge(c, out, w)
+
+    def split_only(i):
+        dqa.decode_attention_qkv_partial(q, caches[i % len(caches)], scale, out, ws[i % len(ws)])
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    res = {}
+    for name, fn in (("step_ms", step), ("kernel_ms", split_only)):
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(steps):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) / steps
+    nbytes = algorithmic_bytes(cfg, bits)
+    res["algorithmic_bytes"] = nbytes
+    res["kv_tokens"] = cfg["B"] * (cfg["T_q"] + cfg["R"])
+    res["replica_bytes"] = nbytes
+    del caches, ws
+    return res
+
+
+def _decode_row(cfg, bits, r):
+    gbps = r["algorithmic_bytes"] / (r["kernel_ms"] * 1e-3) / 1e9
+    return {"kernel": "kivi_decode_kernel + split_merge_kernel", "workload": cfg["workload"], "bits": bits,
+            "us_per_step": r["step_ms"] * 1e3, "kv_tokens_per_s": r["kv_tokens"] / (r["step_ms"] * 1e-3),
+            "kernel_us": r["kernel_ms"] * 1e3, "bound": "hbm", "algorithmic_bytes": r["algorithmic_bytes"],
+            "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS,
+            "note": "kernel_us: back-to-back split-kernel launches; us_per_step: split kernel + merge"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -333,7 +427,7 @@ def main():
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rows", action="store_true",
-                    help="skip timing the other hot-path rows (quantize, zoned, RVQ)")
+                    help="skip timing the other hot-path rows (quantize, zoned, RVQ, other decode shapes)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus}); the decode path shards "
@@ -347,71 +441,23 @@ def main():
     cfg = CONFIGS["llama3.1-8b-gqa-32k"]
     bits = args.bits
     dev = torch.device("cuda:0")
-    inp = kivi_inputs(cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["d"], cfg["T_q"], cfg["R"], seed=3,
+    inp = kivi_inputs(cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["d"], cfg["T_q"], cfg["R"], seed=cfg["seed"],
                       outliers=cfg["outliers"])
     scale = 1.0 / math.sqrt(cfg["d"])
-    k = torch.from_numpy(inp["k"]).to(dev)
-    v = torch.from_numpy(inp["v"]).to(dev)
-    kc, ks, kz = dqa.quantize_pack_k(k, bits)
-    vc, vs, vz = dqa.quantize_pack_v(v, bits)
     rows = {}
     if not args.no_rows:
+        k = torch.from_numpy(inp["k"]).to(dev)
+        v = torch.from_numpy(inp["v"]).to(dev)
         rows.update(time_quantize(dqa, torch, k, v, bits, cfg))
-    kr = torch.from_numpy(inp["k_recent"]).to(dev)
-    vr = torch.from_numpy(inp["v_recent"]).to(dev)
-    q = torch.from_numpy(inp["q"]).to(dev)
-    del k, v
-    caches = []
-    for r in range(args.replicas):
-        t = [x.clone() for x in (kc, ks, kz, vc, vs, vz, kr, vr)]
-        caches.append(dqa.KiviCache(cfg["Hq"], bits, *t, rope_theta=cfg["rope_theta"]))
-    out = torch.empty((cfg["B"], cfg["Hq"], cfg["d"]), dtype=torch.float32, device=dev)
-    ws = [c.workspace(dev) for c in caches]
-    torch.cuda.synchronize()
-
-    def step(i, ev=None):
-        c, w = caches[i % len(caches)], ws[i % len(ws)]
-        if ev is not None:
-            ev[0].record(stream)
-        dqa.decode_attention_qkv_partial(q, c, scale, out, w)
-        if ev is not None:
-            ev[1].record(stream)
-        dqa.decode_attention_qkv_merge(c, out, w)
-
-    stream = torch.cuda.current_stream(dev)
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    # timed region: K steps (value, ms_per_step)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
-    # the same K steps again with events bracketing every split-kernel launch
-    # on its stream: the kernel's average duration for the roofline (the
-    # events add a few microseconds to each step, so the step rate above is
-    # taken without them)
-    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    e0.record(stream)
-    for i in range(args.steps):
-        step(i, kev[i])
-    e1.record(stream)
-    torch.cuda.synchronize()
-    kernel_ms = sum(a.elapsed_time(b) for a, b in kev) / args.steps
-    ms_events = e0.elapsed_time(e1) / args.steps
-
-    nbytes = algorithmic_bytes(cfg, bits)
+        del k, v
+    r = time_decode(dqa, torch, dev, cfg, bits, args.replicas, args.steps, args.warmup, inp)
+    ms, kernel_ms, nbytes = r["step_ms"], r["kernel_ms"], r["algorithmic_bytes"]
     achieved = nbytes / (kernel_ms * 1e-3) / 1e9
     traffic = measured_traffic(bits)
-    kv_tokens = cfg["B"] * (cfg["T_q"] + cfg["R"])
     line = {
         "metric": "decode attention KV-tokens/s over a 2-bit cache (+ achieved HBM GB/s, % of peak)"
                   if bits == 2 else "decode attention KV-tokens/s over a 4-bit cache",
-        "value": kv_tokens / (ms * 1e-3),
+        "value": r["kv_tokens"] / (ms * 1e-3),
         "unit": "KV-tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -420,7 +466,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "fp16 matrix-core operands (keys and query split hi+lo, fp16 p*scale for values), "
+                 "fp32 accumulation and softmax",
         "data": "synthetic",
         "config": {"workload": cfg["workload"], "batch": cfg["B"], "q_heads": cfg["Hq"],
                    "kv_heads": cfg["Hkv"], "head_dim": cfg["d"], "quantized_tokens": cfg["T_q"],
@@ -429,7 +476,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
                      "algorithmic_bytes": nbytes, "kernel": "kivi_decode_kernel",
-                     "kernel_ms": kernel_ms},
+                     "kernel_ms": kernel_ms,
+                     "kernel_ms_from": "HIP events around back-to-back split-kernel launches"},
     }
     # the vector-ALU issue rate the same kernel sustains (its instruction
     # count per launch from the committed counter summary)
@@ -440,6 +488,8 @@ def main():
                                     "unit": "G wave-instructions/s", "frac": rate / VALU_PEAK_GINST}
 
     # achievable streaming rate on a buffer of the same size, same run
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     src = torch.empty(nbytes // 16 * 16 * 4, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
     for _ in range(3):
@@ -450,11 +500,19 @@ def main():
         dqa.stream_copy(src, dst)
     e1.record(stream)
     torch.cuda.synchronize()
-    line["ms_per_step_with_kernel_events"] = ms_events
     line["stream_copy_gbps"] = 2 * src.numel() * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
     del src, dst
 
     if not args.no_rows:
+        # the other decode shapes: the same workload at the other width, and
+        # the Llama-2-13B-shaped MHA layer (no RoPE)
+        other = 4 if bits == 2 else 2
+        rows[f"decode_{other}bit"] = _decode_row(cfg, other, time_decode(dqa, torch, dev, cfg, other,
+                                                                        args.replicas, args.steps,
+                                                                        args.warmup, inp))
+        c2 = CONFIGS["llama2-13b-decode-layer"]
+        rows["decode_llama2_13b"] = _decode_row(c2, 2, time_decode(dqa, torch, dev, c2, 2, args.replicas,
+                                                                   args.steps, args.warmup))
         rows.update(time_append(dqa, torch, dev, cfg, bits))
         rows.update(time_zoned(dqa, torch, dev))
         rows.update(time_rvq(dqa, torch, dev))

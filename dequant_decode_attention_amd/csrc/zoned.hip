@@ -125,12 +125,12 @@ long long fill_unit(int32_t* U, const int* n, const int* m, int d, int sink, int
   return static_cast<long long>(size);
 }
 
-// A plan as zoned_plan writes it, checked in full before any launch: the
-// header, every unit record (re-derived from its token and channel counts),
-// the blob size, the per-unit channel permutation (each channel once) and,
-// with `tokens`, the token map (kept old tokens in [sink, T_old), increasing
-// within each segment).  Anything else is DQA_ERR_PLAN.
-int check_plan(const int32_t* p, bool tokens) {
+// A plan as zoned_plan writes it, checked before any launch: the header,
+// every unit record (re-derived from its token and channel counts), the blob
+// size and the per-unit channel permutation (each channel once); anything
+// else is DQA_ERR_PLAN.  The token map (T_old words per unit, the bulk of the
+// plan) is not read here: the packer clamps its entries into [0, T_old).
+int check_plan(const int32_t* p) {
   if (!p) return DQA_ERR_NULL;
   if (p[H_MAGIC] != kPlanMagic || p[H_VERSION] != kPlanVersion) return DQA_ERR_PLAN;
   const int d = p[H_D], T_old = p[H_TOLD], sink = p[H_SINK], C_new = p[H_C], k_out = p[H_KOUT];
@@ -170,14 +170,6 @@ int check_plan(const int32_t* p, bool tokens) {
       const int32_t ch = perm[c];
       if (ch < 0 || ch >= d || ((seen[ch >> 6] >> (ch & 63)) & 1u)) return DQA_ERR_PLAN;
       seen[ch >> 6] |= uint64_t{1} << (ch & 63);
-    }
-    if (tokens) {
-      const int32_t* tok = p + static_cast<size_t>(p[H_TOK_OFF]) + static_cast<size_t>(u) * T_old;
-      for (int si = 0; si < 4; ++si) {
-        const int32_t* t = tok + U[U_TOK_PREFIX + si];
-        for (int i = 0; i < n[si]; ++i)
-          if (t[i] < sink || t[i] >= T_old || (i > 0 && t[i] <= t[i - 1])) return DQA_ERR_PLAN;
-      }
     }
   }
   const size_t blob = static_cast<size_t>(static_cast<uint32_t>(p[H_BLOB_LO])) |
@@ -377,7 +369,10 @@ __global__ __launch_bounds__(128) void zoned_pack_kernel(PackArgs a) {
   const int n_seg = U[U_N + seg];
   const int n_valid = min(kGroup, n_seg - g * kGroup);
   uint8_t* gb = ub + U[U_SEG_OFF + seg] + static_cast<size_t>(g) * U[U_GRP_B + seg];
-  if (tid < kGroup) lds_tok[tid] = tid < n_valid ? tokmap[U[U_TOK_PREFIX + seg] + g * kGroup + tid] : -1;
+  // token-map entries are clamped into [0, T_old): a map zoned_plan did not
+  // write gives an unspecified blob, but every read stays in bounds
+  if (tid < kGroup)
+    lds_tok[tid] = tid < n_valid ? min(max(tokmap[U[U_TOK_PREFIX + seg] + g * kGroup + tid], 0), a.T_old - 1) : -1;
   const int pc = tid;                      // class position of this thread's key channel
   const int ch = pc < D ? perm[pc] : 0;
   __syncthreads();
@@ -1075,7 +1070,7 @@ struct ZGeometry {
 };
 
 int zoned_geometry(const int32_t* p, int Hq, ZGeometry* g) {
-  int st = check_plan(p, false);
+  int st = check_plan(p);
   if (st != DQA_OK) return st;
   const int Hkv = p[H_HKV];
   if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0) return DQA_ERR_SHAPE;
@@ -1206,7 +1201,7 @@ extern "C" int zoned_plan(const int8_t* v_bits, const int8_t* k_bits, int B, int
 extern "C" int zoned_pack(const int32_t* plan_host, const int32_t* plan_dev, const uint16_t* k,
                           const uint16_t* v, const uint16_t* k_new, const uint16_t* v_new, void* blob,
                           void* stream) {
-  int st = check_plan(plan_host, true);
+  int st = check_plan(plan_host);
   if (st != DQA_OK) return st;
   if (!plan_dev) return DQA_ERR_NULL;
   const int units = plan_host[H_UNITS];

@@ -277,9 +277,12 @@ size_t zoned_plan_words(int B, int Hkv, int T_old, int d);
  * The plan is self-describing; the caller copies the same words to device
  * memory for zoned_pack / decode_attention_zoned.  Those two calls validate
  * the host words before any launch (header, every unit record re-derived
- * from its token and channel counts, blob size, channel permutation, and
- * for zoned_pack the token map) and read the device copy in the kernels, so
- * the device words must be an unmodified copy of the host words.
+ * from its token and channel counts, blob size, channel permutation) and
+ * read the device copy in the kernels, so the device words must be an
+ * unmodified copy of the host words.  The token map (the bulk of the plan)
+ * is not validated on the host; the packer clamps its entries into
+ * [0, T_old), so a map zoned_plan did not write gives an unspecified blob
+ * but no out-of-bounds read.
  * Errors: DQA_ERR_NULL, DQA_ERR_SHAPE, DQA_ERR_BITS (a width outside its
  * set), DQA_ERR_WORKSPACE (plan_words too small). */
 int zoned_plan(const int8_t* v_bits, const int8_t* k_bits, int B, int Hkv,
@@ -288,8 +291,9 @@ int zoned_plan(const int8_t* v_bits, const int8_t* k_bits, int B, int Hkv,
 
 /* Pack the cache into the blob described by the plan.
  *   plan_host (host) and plan_dev (device): the same words from zoned_plan
- *             (plan_dev a copy of plan_host; a plan that zoned_plan could
- *             not have written is DQA_ERR_PLAN)
+ *             (plan_dev a copy of plan_host; a header, unit record or channel
+ *             permutation that zoned_plan could not have written is
+ *             DQA_ERR_PLAN)
  *   k, v      (device) fp16 [B][Hkv][T_old][d] (the sink tokens are their
  *             first rows)
  *   k_new, v_new (device) fp16 [B][Hkv][C_new][d] (may be NULL if C_new == 0)

@@ -253,9 +253,6 @@ def _corruptions(words, units, d, T):
     mod("unused record word", lambda w: w.__setitem__(u1 + 39, 5))
     mod("channel listed twice", lambda w: w.__setitem__(perm0 + d + 1, w[perm0 + d]))
     mod("channel out of range", lambda w: w.__setitem__(perm0 + 2, d))
-    mod("token out of range", lambda w: w.__setitem__(tok0 + T, T), tok_only=True)
-    mod("tokens out of order", lambda w: w.__setitem__(slice(tok0, tok0 + 2), w[tok0:tok0 + 2][::-1].copy()),
-        tok_only=True)
     return out
 
 
@@ -264,16 +261,14 @@ def test_zoned_plan_corruption_refused(sink, k_out):
     """A plan zoned_plan could not have written is refused (DQA_ERR_PLAN)
     by every entry point that reads it, before any launch: truncated plans,
     shifted offsets, records that disagree with their own counts, a wrong
-    blob size, a broken channel permutation; the token map (read by the
-    packer only) is checked by zoned_pack."""
+    blob size, a broken channel permutation.  (The token map is not read on
+    the host; the packer clamps its entries into range.)"""
     rng = np.random.default_rng(9)
     B, H, T, d = 2, 3, 100, 128
     vb = rng.choice([0, 2, 4, 8, 16], size=(B, H, T), p=[.3, .3, .2, .1, .1]).astype(np.int8)
     kb = rng.choice([2, 4, 8, 16], size=(B, H, d), p=[.4, .3, .2, .1]).astype(np.int8)
     st, words, blob = _plan(vb, kb, 8, d, sink, k_out)
     assert st == 0
-    # each unit keeps several tokens, so a token-map entry can be moved
-    assert (vb[0, 0, sink:] != 0).sum() >= 2
     ptr = lambda w: ctypes.c_void_p(w.ctypes.data)
     assert lib.decode_attention_zoned_workspace_bytes(ptr(words), 4 * H) > 0
     for name, w, tok_only in _corruptions(words, B * H, d, T):
