@@ -4,7 +4,7 @@ heads, head dim 128, 32768 quantized tokens + 128 fp16 recent tokens, RoPE
 theta 5e5).
 
 One step = one decode step over the whole batch, i.e. what
-decode_attention_qkv enqueues: the split kernel (kivi_decode_kernel: every
+decode_attention_qkv enqueues: the split kernel (kivi_feat_kernel: every
 quantized token's packed codes and scales plus the fp16 recent zone are read
 from HBM, dequantized, rotated and attended) and the merge of the splits
 (split_merge_kernel).  The split kernel's average duration, for the roofline
@@ -44,8 +44,8 @@ HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E, published
 # SIMD every 4 cycles (16 lanes per cycle) at the 2.4 GHz peak clock.
 VALU_PEAK_GINST = 256 * 4 * 2.4 / 4
 KERNEL_SOURCES = [os.path.join(ROOT, "dequant_decode_attention_amd", "csrc", f)
-                  for f in ("decode_kivi.hip", "merge.h", "common.h")]
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "kivi_decode_kernel_llama8b_gqa_32k_traffic.md")
+                  for f in ("decode_feat.hip", "decode_common.h", "decode_kivi.hip", "merge.h", "common.h")]
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "kivi_feat_kernel_llama8b_gqa_32k_traffic.md")
 
 
 def measured_traffic(bits, key_fmt="traffic_bytes_per_launch_{bits}bit"):
@@ -409,9 +409,15 @@ def time_decode(dqa, torch, dev, cfg, bits, replicas, steps, warmup, inp=None):
     return res
 
 
+def decode_kernel_name(cfg):
+    """The split kernel the library picks: the rotated-feature product for
+    2/4-bit caches with RoPE, the dequantize-then-rotate kernel otherwise."""
+    return "kivi_feat_kernel" if cfg["rope_theta"] > 0 else "kivi_decode_kernel"
+
+
 def _decode_row(cfg, bits, r):
     gbps = r["algorithmic_bytes"] / (r["kernel_ms"] * 1e-3) / 1e9
-    return {"kernel": "kivi_decode_kernel + split_merge_kernel", "workload": cfg["workload"], "bits": bits,
+    return {"kernel": f"{decode_kernel_name(cfg)} + split_merge_kernel", "workload": cfg["workload"], "bits": bits,
             "us_per_step": r["step_ms"] * 1e3, "kv_tokens_per_s": r["kv_tokens"] / (r["step_ms"] * 1e-3),
             "kernel_us": r["kernel_ms"] * 1e3, "bound": "hbm", "algorithmic_bytes": r["algorithmic_bytes"],
             "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS,
@@ -475,7 +481,7 @@ def main():
                    "rope_theta": cfg["rope_theta"], "replicas": args.replicas},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
-                     "algorithmic_bytes": nbytes, "kernel": "kivi_decode_kernel",
+                     "algorithmic_bytes": nbytes, "kernel": decode_kernel_name(cfg),
                      "kernel_ms": kernel_ms,
                      "kernel_ms_from": "HIP events around back-to-back split-kernel launches"},
     }

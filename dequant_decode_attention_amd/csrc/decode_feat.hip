@@ -1,0 +1,661 @@
+// Split-K decode attention over the uniform (KIVI) 2- and 4-bit cache with
+// RoPE: the key logits as one matrix product of per-token "features" and
+// per-tile factors, with no rotation or dequantization of keys on the VALU.
+//
+// [P1 para 7]: keys are quantized before RoPE and rotated after
+// dequantization.  [P1 para 4, 5]: one key scale/zero per (channel, 32-token
+// block), one value scale/zero per (token, 32-channel group).  [P1 para 2]:
+// the whole cache is read at every decode step, so the codes are read once
+// and expanded in registers.
+//
+// For channel pair i (channels a = 2i, b = 2i + 1) of the token at position
+// t0 + j of a 32-token tile that starts at t0, with codes c, the tile's
+// scales s and zeros z, and the query rotated back to t0 (q' = R(t0)^T q):
+//   q . R(t0 + j) khat = q' . R(j) khat
+//     = c_a cos(j w_i) (s_a q'_a) + c_a sin(j w_i) (s_a q'_b)
+//     + c_b cos(j w_i) (s_b q'_b) + c_b sin(j w_i) (-s_b q'_a)
+//     + cos(j w_i) (z_a q'_a + z_b q'_b) + sin(j w_i) (z_a q'_b - z_b q'_a).
+// Every term is a per-token factor (code times a trigonometric value of the
+// token's in-tile offset, or the trigonometric value alone) times a per-tile
+// factor of one query head.  So the logits of a tile are one matrix product:
+//   A (rows = tokens) = [code * trig | trig] features,
+//   B (columns = query heads) = the per-tile factors.
+// A trig value is held as a head with few significant bits (9 for 2-bit
+// codes, 7 for 4-bit) plus the exact tail, so code * head is exact in fp16
+// and code * tail errs by < 2^-20 of the feature; the per-tile factors are
+// formed in fp32 and split into fp16 hi + lo, which occupy separate B
+// columns (hi of head h in column h, lo in column G + h).  Two products per
+// K-step (A head, A tail) and one cross-lane add per logit give the logit to
+// about 2^-20 relative.  The trig values of a lane's two tokens and sixteen
+// pairs stay in registers for the whole kernel; per key element the VALU does
+// a share of the code extraction and two packed fp16 multiplies.
+//
+// Scale bookkeeping: a key code is extracted to bit 4 of its fp16 half (the
+// subnormal code * 2^-20) and the trig head/tail registers hold
+// trig * 2^15, so a feature is code * trig * 2^-5 (normal fp16 for all but
+// tiny trig values, whose errors are then tiny in absolute terms).  The code
+// factors of B carry 2^5; the zero-point features (trig * 2^15 alone) are
+// accumulated first, against B = z q' * 2^5, and that partial sum is scaled
+// by 2^-20 before the code features add to it.
+//
+// Values: as in the other decode kernel (A = value codes as fp16 subnormals,
+// B = p * scale), with the codes extracted near the top of the mantissa:
+// the matrix cores sum products of subnormal inputs as if their exponent were
+// the smallest normal one, so a code in the low mantissa bits would lose
+// precision.  Codes at two positions (2-bit: 6 and 8, 4-bit: 4 and 6); the
+// lower position's tokens carry a factor 4 in their value scales.
+//
+// Recent fp16 tokens (at most 4 tiles per (batch, KV head), spread over
+// different waves): keys rotated in fp32 from the trig table, split into
+// fp16 hi + lo, against the query rotated to the tile start.
+#include "decode_common.h"
+#include "merge.h"
+
+namespace dqa {
+namespace {
+
+constexpr int kFWaves = 4;          // waves per workgroup
+constexpr int kFWavesPerSimd = 2;   // resident waves per SIMD (register budget 256)
+
+// ---------------------------------------------------------------- helpers
+
+// Packed fp16 products with one code half broadcast: (c * t.x, c * t.y) for
+// c the low (HALF = 0) or high (HALF = 1) half of `code`.
+template <int HALF>
+__device__ __forceinline__ uint32_t pk_mul_bcast(uint32_t code, uint32_t t) {
+  uint32_t r;
+  if constexpr (HALF == 0)
+    asm("v_pk_mul_f16 %0, %1, %2 op_sel:[0,0] op_sel_hi:[0,1]" : "=v"(r) : "v"(code), "v"(t));
+  else
+    asm("v_pk_mul_f16 %0, %1, %2 op_sel:[1,0] op_sel_hi:[1,1]" : "=v"(r) : "v"(code), "v"(t));
+  return r;
+}
+
+// fp32 x with all but its top `bits` significant bits cleared (toward zero).
+__device__ __forceinline__ float trunc_sig(float x, int bits) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  return __builtin_bit_cast(float, u & ~((1u << (24 - bits)) - 1u));
+}
+
+__device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
+  half2v h;
+  h[0] = static_cast<_Float16>(lo);
+  h[1] = static_cast<_Float16>(hi);
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+// fp32 x -> fp16 hi (toward zero) + lo (the exact remainder, toward zero),
+// for two values: returns (hi pair, lo pair).  Subnormal remainders are kept.
+__device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(x0, x1));
+  lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(minus_half_lo(hi, x0), minus_half_hi(hi, x1)));
+}
+
+// Key code register e of a packed word (channels e and e + 16/BITS of the
+// word's 32/BITS channels, one per fp16 half), each code moved to bit 4 of
+// its half: the fp16 subnormal code * 2^-20.
+template <int BITS>
+__device__ __forceinline__ uint32_t key_code_at4(uint32_t w, int e) {
+  constexpr uint32_t kMask = BITS == 2 ? 0x00300030u : 0x00F000F0u;
+  const int sh = BITS * e - 4;
+  return (sh < 0 ? (w << (-sh)) : (w >> sh)) & kMask;
+}
+
+// Value chunk (8 tokens of one channel) -> fp16 operand, element 2i = token
+// i, 2i + 1 = token i + 4.  2-bit: tokens with i even at bits 6..7 of their
+// half, odd at 8..9; 4-bit: i = 0, 1 at bits 4..7, i = 2, 3 at bits 6..9.
+// The value codes' product domain is code * 2^-kVShift; tokens at the lower
+// position carry a factor 4 in their scale (feat_vscale_factor).
+template <int BITS>
+constexpr int kVShift = BITS == 2 ? 16 : 18;
+template <int BITS>
+__device__ __forceinline__ bool feat_vlow(int t) {
+  return BITS == 2 ? ((t & 1) == 0) : ((t & 3) < 2);
+}
+template <int BITS>
+__device__ __forceinline__ half8 feat_value_codes8(uint32_t chunk) {
+  uint32_t r[4];
+  if constexpr (BITS == 2) {
+    const uint32_t v = chunk & 0xFFFFu;
+    const uint32_t u = v | (v << 8);          // tokens 0..3 at bits 0..7, 4..7 at 16..23
+    const uint32_t u6 = u << 6, u2 = u << 2;
+    r[0] = u6 & 0x00C000C0u;                  // token 0 (bit 0 -> 6)
+    r[1] = u6 & 0x03000300u;                  // token 1 (bit 2 -> 8)
+    r[2] = u2 & 0x00C000C0u;                  // token 2 (bit 4 -> 6)
+    r[3] = u2 & 0x03000300u;                  // token 3 (bit 6 -> 8)
+  } else {
+    const uint32_t w = chunk;                 // token i at bits 4i, i + 4 at 16 + 4i
+    r[0] = (w << 4) & 0x00F000F0u;            // token 0 -> bits 4..7
+    r[1] = w & 0x00F000F0u;                   // token 1 at bits 4..7
+    r[2] = (w >> 2) & 0x03C003C0u;            // token 2 -> bits 6..9
+    r[3] = (w >> 6) & 0x03C003C0u;            // token 3 -> bits 6..9
+  }
+  half8 out;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const half2v h = __builtin_bit_cast(half2v, r[i]);
+    out[2 * i] = h[0];
+    out[2 * i + 1] = h[1];
+  }
+  return out;
+}
+
+// ----------------------------------------------------------------- kernel
+
+template <int D, int BITS, int G>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kFWavesPerSimd))) void kivi_feat_kernel(
+    KiviArgs a) {
+  static_assert(BITS == 2 || BITS == 4, "feature kernel: 2- and 4-bit codes");
+  constexpr int NP = D / 2;              // RoPE pairs
+  constexpr int PPG = NP / 4;            // pairs of one lane group (16 lanes)
+  constexpr int EPW = 16 / BITS;         // channels per fp16 half of a packed key word
+  constexpr int HPW = EPW / 2;           // pairs per fp16 half of a word
+  constexpr int NW = PPG * BITS / 16;    // key words per token of a lane group
+  constexpr int KSC = PPG / 2;           // code K-steps (2 pairs per lane group each)
+  constexpr int KSB = PPG / 4;           // zero-point K-steps (4 pairs per lane group each)
+  constexpr int KTOT = 32 * (KSC + KSB); // B rows
+  constexpr int BST = KTOT + 8;          // B column stride (halves): columns in different banks
+  constexpr int NBC = 2 * G;             // B columns in use (hi, lo per head)
+  constexpr int NITEM = G * 4 * KSB;     // per-tile factor items (head, lane group, K-step pair)
+  constexpr int HB = BITS == 2 ? 9 : 7;  // significant bits of a trig head
+  constexpr int MB = D / 16;             // channel blocks of the value product
+  constexpr int NVG = D / kGroup;        // value groups per token
+  constexpr int NCOL = G * NVG;          // value-operand columns in use
+  constexpr int KROW = D * BITS / 8;     // key bytes per token
+  constexpr int LROW = NW * 4;           // key bytes per token of one lane group
+  constexpr int VBLK = 4 * D * BITS;     // value bytes per 32-token block
+  constexpr int VST = 24;                // row stride of the fp16 value staging area (halves)
+  constexpr int KSR = D / 32;            // K-steps of a recent tile (channels)
+  constexpr float kTrigScale = 32768.0f; // 2^15
+  static_assert(NCOL <= 16, "value-operand columns");
+  static_assert(NITEM <= kWave, "one factor item per lane");
+  static_assert(G * 4 * KSR <= kWave, "one recent-query item per lane");
+  static_assert(HPW % 2 == 0 && KSC % 2 == 0, "K-step pairs share a word");
+
+  // fp32 (cos, sin) of j * w_i, j = 0..32, i < NP (the whole workgroup's
+  // table; row 32 steps the query from one tile start to the next)
+  __shared__ __attribute__((aligned(16))) float2 lds_trig[kGroup + 1][NP];
+  // per-tile factors (B operand), per wave: [column][K]
+  __shared__ __attribute__((aligned(16))) _Float16 lds_B[kFWaves][NBC][BST];
+  __shared__ __attribute__((aligned(16))) _Float16 lds_vsz[kFWaves][2][NVG][kGroup];
+  // a tile's key scales (row 0) and zeros (row 1)
+  __shared__ __attribute__((aligned(16))) _Float16 lds_ksz[kFWaves][2][D];
+  __shared__ __attribute__((aligned(16))) _Float16 lds_vst[kFWaves][kGroup * VST];
+  __shared__ float lds_m[kFWaves][G], lds_l[kFWaves][G];
+  __shared__ float lds_o[kFWaves][G][D];
+
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int col = lane & 15, grp = lane >> 4;
+  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const size_t unit = static_cast<size_t>(b) * a.Hkv + kvh;
+
+  // The wave's tiles: the (batch, KV head)'s n_q quantized and n_r recent
+  // tiles form n_q + n_r slots cut evenly over all its waves (contiguous
+  // runs [u0, u1)); recent tile r sits at slot floor((2r + 1)(n_q + n_r) /
+  // (2 n_r)), so recent tiles land in different waves.  A wave attends its
+  // recent tiles first, then its run [qb, qe) of quantized tiles.
+  const int n_tiles = a.n_qtiles + a.n_rtiles;
+  const long long nw = static_cast<long long>(a.total_splits) * kFWaves;
+  const long long gw = static_cast<long long>(split) * kFWaves + wave;
+  const int u0 = static_cast<int>(gw * n_tiles / nw);
+  const int u1 = static_cast<int>((gw + 1) * n_tiles / nw);
+  int r_before = 0, r_mine = 0, r_first = 0;
+  for (int r = 0; r < a.n_rtiles; ++r) {
+    const int slot = static_cast<int>((2LL * r + 1) * n_tiles / (2LL * a.n_rtiles));
+    if (slot < u0) ++r_before;
+    else if (slot < u1) {
+      if (r_mine == 0) r_first = r;
+      ++r_mine;
+    }
+  }
+  const int qb = u0 - r_before;
+  const int qe = u1 - r_before - r_mine;
+
+  // ---- trig table (accurate: angle reduced in fp64, sin/cos in fp32)
+  for (int e = tid; e < (kGroup + 1) * NP; e += 256) {
+    const int j = e / NP, i = e % NP;
+    float c, s;
+    rope_unit(static_cast<double>(j), a.omega[i], c, s);
+    lds_trig[j][i] = float2{c, s};
+  }
+  __syncthreads();
+
+  // ---- the lane's trig registers: tokens j(s) (rows of the A operand of
+  // half s), pairs grp * PPG + rho; head (HB significant bits) and tail,
+  // both times 2^15, as fp16 (cos, sin) pairs
+  uint32_t tsh[2][PPG], tsl[2][PPG];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int j = row_token(s, col);
+#pragma unroll
+    for (int rho = 0; rho < PPG; ++rho) {
+      const float2 cs = lds_trig[j][grp * PPG + rho];
+      const float ch = trunc_sig(cs.x, HB), sh = trunc_sig(cs.y, HB);
+      tsh[s][rho] = pack_f16(ch * kTrigScale, sh * kTrigScale);
+      tsl[s][rho] = pack_f16((cs.x - ch) * kTrigScale, (cs.y - sh) * kTrigScale);
+    }
+  }
+
+  // ---- per-tile factor item of this lane: head ih, lane group ig, K-step
+  // pair ikb (code K-steps 2 ikb, 2 ikb + 1; zero-point K-step ikb).  Its four
+  // pairs (relative to the lane group): p0 = piA(2 ikb), p1 = piB(2 ikb),
+  // p2 = p0 + 1, p3 = p1 + 1; channels cA..cA+3 (pairs p0, p2) and
+  // cA + EPW..cA + EPW + 3 (p1, p3), cA = 2 (ig PPG + p0).
+  const bool item = lane < NITEM;
+  const int it = item ? lane : 0;
+  const int ih = it / (4 * KSB), ig = (it / KSB) % 4, ikb = it % KSB;
+  const int iks = 2 * ikb;
+  const int ip0 = (iks / HPW) * EPW + iks % HPW;            // piA(2 ikb)
+  const int ich = 2 * (ig * PPG + ip0);                       // first channel of chunk A
+  // the item's query pairs in the order (p0, p2, p1, p3) = channels
+  // (cA, cA + 2, cA + EPW, cA + EPW + 2)
+  float iq[4][2];
+  {
+    const uint16_t* qh = a.q + (static_cast<size_t>(b) * a.Hq + kvh * G + ih) * D;
+    const float qs = a.q_scale * 32.0f;      // log2-domain logits, code factors carry 2^5
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int c = ich + 2 * (k & 1) + EPW * (k >> 1);
+      const int pi = c / 2;
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(qh + c);
+      const float x0 = h2f(static_cast<uint16_t>(w & 0xFFFFu)) * qs;
+      const float x1 = h2f(static_cast<uint16_t>(w >> 16)) * qs;
+      float cc, ss;
+      rope_unit(static_cast<double>(qb) * kGroup, a.omega[pi], cc, ss);
+      iq[k][0] = x0 * cc + x1 * ss;          // R(-t0) q
+      iq[k][1] = x1 * cc - x0 * ss;
+    }
+  }
+
+  _Float16* const Bw = &lds_B[wave][0][0];
+
+  float4v acc[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) acc[mb] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+  float m = -INFINITY, lsum = 0.0f, zacc = 0.0f;
+  const int qh = col % G;                         // logit column -> query head
+  const int vg = min(col / G, NVG - 1);           // value column -> value group
+  const int bcol = col % NBC;                     // B column this lane reads
+
+  // hi + lo logit columns: lanes col and col +- G (mod 2G) hold the same head
+  auto combine_cols = [&](float x) -> float {
+    if constexpr (G == 4) return x + dpp<0x124>(x);          // row_ror:4
+    else if constexpr (G == 2) return x + dpp<kDppQuadXor2>(x);
+    else return x + dpp<kDppQuadXor1>(x);
+  };
+
+  // online softmax over the lane's 8 logits (the column max over the 4 row
+  // groups); returns the probabilities in p
+  auto softmax_step = [&](float* lg, float* p) {
+    float tm = lg[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) tm = fmaxf(tm, lg[e]);
+    tm = max_rows(tm);
+    const float mn = fmaxf(m, tm);
+    if (__builtin_amdgcn_ballot_w64(mn > m) != 0) {
+      const float sc = merge_weight(m, mn);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) acc[mb] *= sc;
+      lsum *= sc;
+      zacc *= sc;
+    }
+    m = mn;
+    float ps = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      p[e] = (mn == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(lg[e] - mn);
+      ps += p[e];
+    }
+    lsum += ps;
+  };
+
+  // ------------------------------------------------------- quantized tile
+  const size_t qstride = static_cast<size_t>(a.qtile_stride);
+  const uint16_t* const ksz_s = uniform_ptr(a.k_scale);
+  const uint16_t* const ksz_z = uniform_ptr(a.k_zero);
+  const uint16_t* const vsz_s = uniform_ptr(a.v_scale);
+  const uint16_t* const vsz_z = uniform_ptr(a.v_zero);
+  const uint8_t* const kbase = reinterpret_cast<const uint8_t*>(a.k_codes) + unit * qstride * kGroup * KROW;
+  const uint8_t* const vbase = reinterpret_cast<const uint8_t*>(a.v_codes) + unit * qstride * VBLK;
+  // value-scale factor of this lane's staging token (lanes 0..31: scales)
+  const uint32_t vfac = (lane < 32 && feat_vlow<BITS>(lane & 31)) ? 0x44004400u : 0x3C003C00u;  // (4, 4) or (1, 1)
+  struct TileIn {
+    uint32_t k[2][NW];      // the lane's key words of its two tokens
+    uint32_t v[MB];         // value chunks (2-bit: 16 bits used)
+    uint32_t ksz[D / 64];   // lanes 0..31: key scales of D / 32 channels; 32..63: zeros
+    uint32_t vsz[NVG / 2];  // lanes 0..31: value scales of token lane; 32..63: zeros
+  };
+  auto load_tile = [&](int ti, TileIn& t) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const uint8_t* p = kbase + (static_cast<size_t>(ti) * kGroup + row_token(s, col)) * KROW + grp * LROW;
+      const Words<LROW> w = load_words<LROW>(p);
+#pragma unroll
+      for (int i = 0; i < NW; ++i) t.k[s][i] = w.w[i];
+    }
+    const uint8_t* blk = vbase + static_cast<size_t>(ti) * VBLK;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const uint8_t* p = blk + (16 * mb + col) * 4 * BITS + grp * BITS;
+      if constexpr (BITS == 2) t.v[mb] = *reinterpret_cast<const uint16_t*>(p);
+      else t.v[mb] = *reinterpret_cast<const uint32_t*>(p);
+    }
+    const int half = lane >> 5, r = lane & 31;
+    {
+      const Words<D / 16> kw = load_words<D / 16>((half ? ksz_z : ksz_s) + (unit * qstride + ti) * D + r * (D / 32));
+#pragma unroll
+      for (int i = 0; i < D / 64; ++i) t.ksz[i] = kw.w[i];
+    }
+    const uint16_t* vsrc = (half ? vsz_z : vsz_s) + ((unit * qstride + ti) * kGroup + r) * NVG;
+    const Words<2 * NVG> vw = load_words<2 * NVG>(vsrc);
+#pragma unroll
+    for (int i = 0; i < NVG / 2; ++i) t.vsz[i] = vw.w[i];
+  };
+
+  // per-tile factors of the item -> B (hi in column ih, lo in G + ih)
+  auto write_factors = [&]() {
+    if (!item) return;
+    // scales and zeros of channels (cA, cA+1, cA+2, cA+3) and (cA+EPW, ...)
+    float sv[2][4], zv[2][4];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const uint2 sw = *reinterpret_cast<const uint2*>(&lds_ksz[wave][0][ich + c * EPW]);
+      const uint2 zw = *reinterpret_cast<const uint2*>(&lds_ksz[wave][1][ich + c * EPW]);
+      const uint32_t sww[2] = {sw.x, sw.y}, zww[2] = {zw.x, zw.y};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        sv[c][k] = h2f(static_cast<uint16_t>(sww[k >> 1] >> (16 * (k & 1))));
+        zv[c][k] = h2f(static_cast<uint16_t>(zww[k >> 1] >> (16 * (k & 1))));
+      }
+    }
+    // code K-steps 2 ikb (pairs p0 = chunk A channels 0,1; p1 = chunk B
+    // channels 0,1) and 2 ikb + 1 (p2 = chunk A channels 2,3; p3 = B 2,3)
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      float f[8];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const float qa = iq[2 * c + kk][0], qb_ = iq[2 * c + kk][1];
+        const float sa = sv[c][2 * kk], sb = sv[c][2 * kk + 1];
+        f[4 * c + 0] = sa * qa;
+        f[4 * c + 1] = sa * qb_;
+        f[4 * c + 2] = sb * qb_;
+        f[4 * c + 3] = -(sb * qa);
+      }
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) split2(f[2 * i], f[2 * i + 1], hi[i], lo[i]);
+      const int K = 32 * (iks + kk) + 8 * ig;
+      *reinterpret_cast<uint4*>(Bw + ih * BST + K) = uint4{hi[0], hi[1], hi[2], hi[3]};
+      *reinterpret_cast<uint4*>(Bw + (G + ih) * BST + K) = uint4{lo[0], lo[1], lo[2], lo[3]};
+    }
+    // zero-point K-step ikb: pairs in the order p0, p1, p2, p3
+    {
+      float f[8];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int c = q4 & 1, kk = q4 >> 1;               // chunk, pair within chunk
+        const float qa = iq[2 * c + kk][0], qb_ = iq[2 * c + kk][1];
+        const float za = zv[c][2 * kk], zb = zv[c][2 * kk + 1];
+        f[2 * q4 + 0] = za * qa + zb * qb_;
+        f[2 * q4 + 1] = za * qb_ - zb * qa;
+      }
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) split2(f[2 * i], f[2 * i + 1], hi[i], lo[i]);
+      const int K = 32 * (KSC + ikb) + 8 * ig;
+      *reinterpret_cast<uint4*>(Bw + ih * BST + K) = uint4{hi[0], hi[1], hi[2], hi[3]};
+      *reinterpret_cast<uint4*>(Bw + (G + ih) * BST + K) = uint4{lo[0], lo[1], lo[2], lo[3]};
+    }
+    // the query to the next tile's start: q' <- R(-32 w) q'
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float2 st = lds_trig[kGroup][(ich + 2 * (k & 1) + EPW * (k >> 1)) / 2];
+      const float x0 = iq[k][0], x1 = iq[k][1];
+      iq[k][0] = x0 * st.x + x1 * st.y;
+      iq[k][1] = x1 * st.x - x0 * st.y;
+    }
+  };
+
+  auto quantized_tile = [&](int ti, const TileIn& cur, TileIn& nxt, bool prefetch) {
+    // value scales and zeros through LDS (scales times the position factor)
+    {
+      const int half = lane >> 5, r = lane & 31;
+#pragma unroll
+      for (int i = 0; i < NVG / 2; ++i) {
+        uint32_t w;
+        asm("v_pk_mul_f16 %0, %1, %2" : "=v"(w) : "v"(cur.vsz[i]), "v"(vfac));
+        lds_vsz[wave][half][2 * i][r] = __builtin_bit_cast(_Float16, static_cast<uint16_t>(w & 0xFFFFu));
+        lds_vsz[wave][half][2 * i + 1][r] = __builtin_bit_cast(_Float16, static_cast<uint16_t>(w >> 16));
+      }
+      if constexpr (D / 64 == 2)
+        *reinterpret_cast<uint2*>(&lds_ksz[wave][half][r * (D / 32)]) = uint2{cur.ksz[0], cur.ksz[1]};
+      else
+        *reinterpret_cast<uint32_t*>(&lds_ksz[wave][half][r * (D / 32)]) = cur.ksz[0];
+    }
+    wave_sync();
+    write_factors();
+    if (prefetch) load_tile(ti + 1, nxt);
+    wave_sync();
+
+    // logits: zero-point K-steps first (their partial sums carry 2^20), then
+    // the code K-steps
+    float4v sacc[2] = {float4v{0.0f, 0.0f, 0.0f, 0.0f}, float4v{0.0f, 0.0f, 0.0f, 0.0f}};
+#pragma unroll
+    for (int kb = 0; kb < KSB; ++kb) {
+      const half8 bv = *reinterpret_cast<const half8*>(Bw + bcol * BST + 32 * (KSC + kb) + 8 * grp);
+      const int k0 = 2 * kb, k1 = 2 * kb + 1;
+      const int pa0 = (k0 / HPW) * EPW + k0 % HPW, pa1 = (k1 / HPW) * EPW + k1 % HPW;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const uint32_t ah[4] = {tsh[s][pa0], tsh[s][pa0 + HPW], tsh[s][pa1], tsh[s][pa1 + HPW]};
+        const uint32_t al[4] = {tsl[s][pa0], tsl[s][pa0 + HPW], tsl[s][pa1], tsl[s][pa1 + HPW]};
+        sacc[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, ah), bv, sacc[s], 0, 0, 0);
+        sacc[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, al), bv, sacc[s], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s) sacc[s] *= 1.0f / 1048576.0f;   // 2^-20
+#pragma unroll
+    for (int ks = 0; ks < KSC; ++ks) {
+      const half8 bv = *reinterpret_cast<const half8*>(Bw + bcol * BST + 32 * ks + 8 * grp);
+      const int w = ks / HPW, ip = ks % HPW;
+      const int pa = w * EPW + ip, pb = pa + HPW;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const uint32_t ca = key_code_at4<BITS>(cur.k[s][w], 2 * ip);
+        const uint32_t cb = key_code_at4<BITS>(cur.k[s][w], 2 * ip + 1);
+        uint32_t ah[4], al[4];
+        ah[0] = pk_mul_bcast<0>(ca, tsh[s][pa]);
+        ah[1] = pk_mul_bcast<0>(cb, tsh[s][pa]);
+        ah[2] = pk_mul_bcast<1>(ca, tsh[s][pb]);
+        ah[3] = pk_mul_bcast<1>(cb, tsh[s][pb]);
+        al[0] = pk_mul_bcast<0>(ca, tsl[s][pa]);
+        al[1] = pk_mul_bcast<0>(cb, tsl[s][pa]);
+        al[2] = pk_mul_bcast<1>(ca, tsl[s][pb]);
+        al[3] = pk_mul_bcast<1>(cb, tsl[s][pb]);
+        sacc[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, ah), bv, sacc[s], 0, 0, 0);
+        sacc[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, al), bv, sacc[s], 0, 0, 0);
+      }
+    }
+    // element e of the lane's run is token 8 grp + vtok(e)
+    float lg[8], p[8];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      lg[2 * r] = combine_cols(sacc[0][r]);
+      lg[2 * r + 1] = combine_cols(sacc[1][r]);
+    }
+    softmax_step(lg, p);
+
+    // value product: column (head qh, group vg) holds p * scale
+    const half8 vs = *reinterpret_cast<const half8*>(&lds_vsz[wave][0][vg][8 * grp]);
+    const half8 vz = *reinterpret_cast<const half8*>(&lds_vsz[wave][1][vg][8 * grp]);
+    half8 bv;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int t = vtok(e);
+      bv[e] = static_cast<_Float16>(col < NCOL ? p[e] * static_cast<float>(vs[t]) : 0.0f);
+      zacc = fmaf(p[e], static_cast<float>(vz[t]), zacc);
+    }
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+      acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(feat_value_codes8<BITS>(cur.v[mb]), bv, acc[mb], 0, 0, 0);
+    wave_sync();
+  };
+
+  // ------------------------------------------------------ fp16 recent tile
+  const uint16_t* const krb = a.k_recent + unit * a.R_cap * D;
+  const uint16_t* const vrb = a.v_recent + unit * a.R_cap * D;
+  auto recent_tile = [&](int rt) {
+    const int r0 = rt * kGroup;
+    const double t0 = static_cast<double>(a.n_qtiles + rt) * kGroup;
+    // keys: the lane's 8 channels of K-step ks for its two tokens; value
+    // slabs: token lane / 2, 8 channels of block mb
+    uint4 kin[2][KSR], vin[MB];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int r = r0 + row_token(s, col);
+#pragma unroll
+      for (int ks = 0; ks < KSR; ++ks) {
+        kin[s][ks] = uint4{0u, 0u, 0u, 0u};
+        if (r < a.R)
+          kin[s][ks] = *reinterpret_cast<const uint4*>(krb + static_cast<size_t>(r) * D + 2 * PPG * grp + 8 * ks);
+      }
+    }
+    {
+      const int r = r0 + (lane >> 1);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        vin[mb] = uint4{0u, 0u, 0u, 0u};
+        if (r < a.R) vin[mb] = *reinterpret_cast<const uint4*>(vrb + static_cast<size_t>(r) * D + 16 * mb + 8 * (lane & 1));
+      }
+    }
+    // B: the query rotated to t0 (no 2^5), K = the lane group's channels in
+    // order: item (head, lane group, K-step) of this lane writes 8 channels
+    if (lane < G * 4 * KSR) {
+      const int h = lane / (4 * KSR), g = (lane / KSR) % 4, ks = lane % KSR;
+      const int c0 = 2 * PPG * g + 8 * ks;
+      const uint16_t* qh = a.q + (static_cast<size_t>(b) * a.Hq + kvh * G + h) * D + c0;
+      const uint4 qw = *reinterpret_cast<const uint4*>(qh);
+      const uint32_t qq[4] = {qw.x, qw.y, qw.z, qw.w};
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float x0 = h2f(static_cast<uint16_t>(qq[i] & 0xFFFFu)) * a.q_scale;
+        const float x1 = h2f(static_cast<uint16_t>(qq[i] >> 16)) * a.q_scale;
+        float cc, ss;
+        rope_unit(t0, a.omega[c0 / 2 + i], cc, ss);
+        split2(x0 * cc + x1 * ss, x1 * cc - x0 * ss, hi[i], lo[i]);
+      }
+      const int K = 32 * ks + 8 * g;
+      *reinterpret_cast<uint4*>(Bw + h * BST + K) = uint4{hi[0], hi[1], hi[2], hi[3]};
+      *reinterpret_cast<uint4*>(Bw + (G + h) * BST + K) = uint4{lo[0], lo[1], lo[2], lo[3]};
+    }
+    wave_sync();
+    float4v sacc[2] = {float4v{0.0f, 0.0f, 0.0f, 0.0f}, float4v{0.0f, 0.0f, 0.0f, 0.0f}};
+#pragma unroll
+    for (int ks = 0; ks < KSR; ++ks) {
+      const half8 bv = *reinterpret_cast<const half8*>(Bw + bcol * BST + 32 * ks + 8 * grp);
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int j = row_token(s, col);
+        const uint32_t w[4] = {kin[s][ks].x, kin[s][ks].y, kin[s][ks].z, kin[s][ks].w};
+        uint32_t ah[4], al[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float x0 = h2f(static_cast<uint16_t>(w[i] & 0xFFFFu));
+          const float x1 = h2f(static_cast<uint16_t>(w[i] >> 16));
+          const float2 cs = lds_trig[j][grp * PPG + 4 * ks + i];
+          split2(x0 * cs.x - x1 * cs.y, x0 * cs.y + x1 * cs.x, ah[i], al[i]);
+        }
+        sacc[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, ah), bv, sacc[s], 0, 0, 0);
+        sacc[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, al), bv, sacc[s], 0, 0, 0);
+      }
+    }
+    float lg[8], p[8];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      lg[2 * r] = combine_cols(sacc[0][r]);
+      lg[2 * r + 1] = combine_cols(sacc[1][r]);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (r0 + 8 * grp + vtok(e) >= a.R) lg[e] = -INFINITY;
+    softmax_step(lg, p);
+    half8 bv;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) bv[e] = static_cast<_Float16>(col < NCOL ? p[e] : 0.0f);
+    // values pass through LDS 16 channels at a time to form the
+    // channel-major operand
+    _Float16* const st = lds_vst[wave];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      *reinterpret_cast<uint4*>(&st[(lane >> 1) * VST + 8 * (lane & 1)]) = vin[mb];
+      wave_sync();
+      half8 av;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) av[e] = st[(8 * grp + vtok(e)) * VST + col];
+      wave_sync();
+      acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, acc[mb], 0, 0, 0);
+    }
+  };
+
+  // the wave's recent tiles, then its quantized run; two register buffers
+  // alternate so that the loads of tile i+1 stay in flight during tile i
+  TileIn buf0, buf1;
+  if (qb < qe) load_tile(qb, buf0);
+  for (int k = 0; k < r_mine; ++k) recent_tile(r_first + k);
+  // fp16 value products are exact-scale; switch the accumulator to the
+  // code-product domain (a power of two: exact)
+  if (r_mine > 0) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[mb] *= 1.0f / static_cast<float>(1u << kVShift<BITS>);
+  }
+  for (int ti = qb; ti < qe; ti += 2) {
+    quantized_tile(ti, buf0, buf1, ti + 1 < qe);
+    if (ti + 1 < qe) quantized_tile(ti + 1, buf1, buf0, ti + 2 < qe);
+  }
+
+  // ---- wave state -> LDS: row sums and zero-point sums over the 4 row
+  // groups of each column
+  lsum = sum_rows(lsum);
+  zacc = sum_rows(zacc);
+  if (col < NCOL) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+      if (mb / 2 == vg)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          lds_o[wave][qh][16 * mb + 4 * grp + r] =
+              fmaf(acc[mb][r], static_cast<float>(1u << kVShift<BITS>), zacc);
+  }
+  if (lane < G) {
+    lds_m[wave][lane] = m;
+    lds_l[wave][lane] = lsum;
+  }
+  __syncthreads();
+  write_split_state<D, G, kFWaves>(a.partials, a.out, a.Hq, unit, b, kvh, split, a.total_splits, lds_m, lds_l,
+                                   lds_o);
+}
+
+template <int D, int BITS>
+int launch_feat_g(const KiviArgs& a, int G, dim3 grid, hipStream_t s) {
+  switch (G) {
+    case 1: hipLaunchKernelGGL((kivi_feat_kernel<D, BITS, 1>), grid, dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((kivi_feat_kernel<D, BITS, 2>), grid, dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((kivi_feat_kernel<D, BITS, 4>), grid, dim3(256), 0, s, a); break;
+    default: return DQA_ERR_UNSUPPORTED;
+  }
+  return DQA_OK;
+}
+
+}  // namespace
+
+int feat_decode_workgroups() { return 256 * kFWavesPerSimd; }
+
+int launch_feat_decode(const KiviArgs& a, int d, int G, int bits, dim3 grid, hipStream_t s) {
+  if (d == 128) return bits == 2 ? launch_feat_g<128, 2>(a, G, grid, s) : launch_feat_g<128, 4>(a, G, grid, s);
+  return bits == 2 ? launch_feat_g<64, 2>(a, G, grid, s) : launch_feat_g<64, 4>(a, G, grid, s);
+}
+
+}  // namespace dqa

@@ -32,10 +32,9 @@
 // The online softmax runs once per tile per column.  Each split writes its
 // partial softmax state; split_merge_kernel (merge.h) merges the splits of
 // every (batch, KV head) in split order.
-#include <cmath>
 #include <mutex>
 
-#include "common.h"
+#include "decode_common.h"
 #include "merge.h"
 
 namespace dqa {
@@ -49,287 +48,8 @@ constexpr int kWavesPerWG = 4;
 template <int BITS>
 constexpr int kDecodeWavesPerSimd = BITS == 2 ? 3 : 2;
 inline int decode_workgroups(int bits) { return 256 * (bits == 2 ? kDecodeWavesPerSimd<2> : kDecodeWavesPerSimd<4>); }
-
-struct KiviArgs {
-  const uint16_t* q;
-  const uint32_t* k_codes;
-  const uint16_t* k_scale;
-  const uint16_t* k_zero;
-  const uint32_t* v_codes;
-  const uint16_t* v_scale;
-  const uint16_t* v_zero;
-  const uint16_t* k_recent;
-  const uint16_t* v_recent;
-  float* out;
-  float* partials;
-  int Hq, Hkv, T_q, R;
-  int qtile_stride;     // 32-token tiles of quantized-buffer capacity per (batch, KV head)
-  int R_cap;            // recent-buffer rows per (batch, KV head)
-  int n_qtiles;         // T_q / 32
-  int n_rtiles;         // ceil(R / 32)
-  int total_splits;     // splits (partial-state slots) per (batch, KV head)
-  float q_scale;        // sm_scale * log2(e): logits in the log2 domain
-  double omega[64];     // RoPE frequencies theta^(-2i/d), i < d/2 (host fp64)
-};
-
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef _Float16 half2v __attribute__((ext_vector_type(2)));
-typedef float float4v __attribute__((ext_vector_type(4)));
-
-// Accurate unit complex number e^{i * pos * omega}: the angle is formed and
-// reduced modulo 2*pi in fp64, then sin/cos are taken in fp32 on [-pi, pi].
-__device__ __forceinline__ void rope_unit(double pos, double omega, float& c, float& s) {
-  const double kTwoPiHi = 6.283185307179586;
-  const double kTwoPiLo = 2.4492935982947064e-16;
-  const double ang = pos * omega;
-  const double k = rint(ang * 0.15915494309189535);
-  double r = fma(-k, kTwoPiHi, ang);
-  r = fma(-k, kTwoPiLo, r);
-  sincosf(static_cast<float>(r), &s, &c);
-}
-
-// Orders LDS traffic of the lanes of one wave (no workgroup barrier).
-__device__ __forceinline__ void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-// NB consecutive bytes (4, 8, 16 or 32; NB-aligned, at most 16-aligned) as
-// 32-bit words.
-template <int NB>
-struct Words {
-  uint32_t w[NB / 4];
-};
-template <int NB>
-__device__ __forceinline__ Words<NB> load_words(const void* p) {
-  Words<NB> r;
-  if constexpr (NB == 4) {
-    r.w[0] = *reinterpret_cast<const uint32_t*>(p);
-  } else if constexpr (NB == 8) {
-    const uint2 u = *reinterpret_cast<const uint2*>(p);
-    r.w[0] = u.x;
-    r.w[1] = u.y;
-  } else {
-#pragma unroll
-    for (int i = 0; i < NB / 16; ++i) {
-      const uint4 u = reinterpret_cast<const uint4*>(p)[i];
-      r.w[4 * i] = u.x;
-      r.w[4 * i + 1] = u.y;
-      r.w[4 * i + 2] = u.z;
-      r.w[4 * i + 3] = u.w;
-    }
-  }
-  return r;
-}
-
-// A value the compiler must treat as unknown (keeps a VGPR constant out of
-// the scalar constant bus, and keeps shifted words from being folded back
-// into bit-field extracts).
-// A kernel-argument pointer as a wave-uniform value.  A lane-dependent
-// choice between two argument pointers would otherwise be folded into a
-// per-lane vector load of the pointer from the argument segment, issued
-// again on every use.
-template <typename T>
-__device__ __forceinline__ const T* uniform_ptr(const T* p) {
-  const uint64_t v = reinterpret_cast<uint64_t>(p);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
-  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
-  // rebuilt as a global-memory pointer, so loads through it stay global loads
-  using GT = const __attribute__((address_space(1))) T;
-  GT* g = reinterpret_cast<GT*>((static_cast<uint64_t>(hi) << 32) | lo);
-  return (const T*)g;
-}
-
-__device__ __forceinline__ uint32_t opaque(uint32_t v) {
-  asm volatile("" : "+v"(v));
-  return v;
-}
-
-// Key codes as fp16 subnormals.  A code c placed in the low bits of an fp16
-// bit pattern whose exponent field is zero is the value c * 2^-24; a code
-// left at bit offset 2p (2-bit) or 4p (4-bit) inside its 16-bit half is
-// c * 2^(bits * p) * 2^-24, still subnormal while it stays below bit 10.  One
-// mask of the packed word therefore yields two such values (one per half),
-// and the mixed-precision FMA widens them exactly and multiplies by the fp32
-// scale pre-multiplied by 2^(24 - bits * p): code * scale + zero with one
-// rounding, the same result as an fp32 FMA on the integer code.
-//
-// Position p of K-step element e (channel c0 + e) inside its half.
-template <int BITS>
-__device__ __forceinline__ constexpr int key_code_pos(int e) {
-  return BITS == 2 ? (e <= 4 ? e : e - 5) : (BITS == 4 ? (e & 1) : 0);
-}
-// The lane's masked key-code registers (key_code_reg / key_code_half give
-// the register and half of K-step element e).  2-bit: one word = 16
-// channels (two K-steps); register e holds channel e in the low half (even
-// K-step) and channel e + 8 in the high half (odd K-step).  4-bit: one word
-// = one K-step; register e & 3 holds channel e in half e >> 2.  8-bit: two
-// words = one K-step; word i gives registers 2i (channels 4i, 4i + 2) and
-// 2i + 1 (channels 4i + 1, 4i + 3).
-template <int BITS>
-__device__ __forceinline__ void key_code_regs(const uint32_t* w, int ks, uint32_t* m) {
-  if constexpr (BITS == 2) {
-    const uint32_t x = w[ks >> 1], x1 = opaque(x >> 10);
-#pragma unroll
-    for (int e = 0; e < 5; ++e) m[e] = x & (0x00030003u << (2 * e));
-#pragma unroll
-    for (int e = 5; e < 8; ++e) m[e] = x1 & (0x00030003u << (2 * (e - 5)));
-  } else if constexpr (BITS == 4) {
-    const uint32_t x = w[ks], x1 = opaque(x >> 8);
-    m[0] = x & 0x000F000Fu;    // channels 0, 4
-    m[1] = x & 0x00F000F0u;    // channels 1, 5
-    m[2] = x1 & 0x000F000Fu;   // channels 2, 6
-    m[3] = x1 & 0x00F000F0u;   // channels 3, 7
-  } else {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const uint32_t x = w[2 * ks + i];
-      m[2 * i] = x & 0x00FF00FFu;                 // channels 4i, 4i + 2
-      m[2 * i + 1] = opaque(x >> 8) & 0x00FF00FFu; // channels 4i + 1, 4i + 3
-    }
-  }
-}
-// register and half of K-step element e (ks: the K-step, for 2-bit)
-template <int BITS>
-__device__ __forceinline__ constexpr int key_code_reg(int e) {
-  return BITS == 2 ? e : (BITS == 4 ? (e & 3) : (2 * (e >> 2) + (e & 1)));
-}
-template <int BITS>
-__device__ __forceinline__ constexpr int key_code_half(int e, int ks) {
-  return BITS == 2 ? (ks & 1) : (BITS == 4 ? (e >> 2) : ((e >> 1) & 1));
-}
-
-// code (fp16 half A of m) * s + zero (fp16 half Z of z), one rounding
-template <int A, int Z>
-__device__ __forceinline__ float mix_dequant(uint32_t m, float s, uint32_t z) {
-  float r;
-  if constexpr (A == 0 && Z == 0)
-    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel_hi:[1,0,1]" : "=v"(r) : "v"(m), "v"(s), "v"(z));
-  else if constexpr (A == 1 && Z == 0)
-    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[1,0,0] op_sel_hi:[1,0,1]" : "=v"(r) : "v"(m), "v"(s), "v"(z));
-  else if constexpr (A == 0 && Z == 1)
-    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[0,0,1] op_sel_hi:[1,0,1]" : "=v"(r) : "v"(m), "v"(s), "v"(z));
-  else
-    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[1,0,1] op_sel_hi:[1,0,1]" : "=v"(r) : "v"(m), "v"(s), "v"(z));
-  return r;
-}
-
-// Value chunk (8 tokens of one channel) -> fp16 operand holding the codes as
-// fp16 subnormals, each code at the top of the 10-bit mantissa field: bits
-// 8-9 (2-bit: code * 2^-16), 6-9 (4-bit: code * 2^-18) or 2-9 (8-bit: code *
-// 2^-22).  The matrix cores multiply subnormal inputs exactly, but they sum
-// the products of subnormal operands as if each had the smallest normal
-// exponent, so a code in the low mantissa bits would lose up to 10 bits of
-// its product (measured on MI355X: sums of 32 such products off by up to
-// 1.5e-4 relative, biased toward zero; with the codes at the top, within a
-// few fp32 ulps).  The accumulator runs in the code * 2^-kCodeShift domain and
-// is rescaled once.  Element 2i holds token i, element 2i+1 token i+4 (the
-// same order is used for the probabilities).
-template <int BITS>
-constexpr int kCodeShift = BITS == 2 ? 16 : (BITS == 4 ? 18 : 22);
-template <int BITS>
-constexpr float kCodeScale = static_cast<float>(1u << kCodeShift<BITS>);
-
-template <int BITS>
-__device__ __forceinline__ half8 value_codes8(uint64_t chunk, uint32_t mask) {
-  uint32_t r[4];
-  if constexpr (BITS == 2) {
-    // tokens 0..3 at bits 0..7, tokens 4..7 at bits 16..23; token i (and
-    // i + 4) shifted to bits 8..9 (24..25)
-    const uint32_t v = static_cast<uint32_t>(chunk);
-    const uint32_t u = v | (v << 8);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) r[i] = (u << (8 - 2 * i)) & mask;
-  } else if constexpr (BITS == 4) {
-    // token i at bits 4i..4i+3 and token i + 4 at 16 + 4i; moved to bits 6..9
-    const uint32_t w = static_cast<uint32_t>(chunk);
-    r[0] = (w << 6) & mask;
-    r[1] = (w << 2) & mask;
-    r[2] = (w >> 2) & mask;
-    r[3] = (w >> 6) & mask;
-  } else {
-    const uint32_t lo = static_cast<uint32_t>(chunk), hi = static_cast<uint32_t>(chunk >> 32);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      r[i] = __builtin_amdgcn_perm(hi, lo, static_cast<uint32_t>(i | (0x0C << 8) | ((4 + i) << 16) | (0x0C << 24))) << 2;
-  }
-  half8 out;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const half2v h = __builtin_bit_cast(half2v, r[i]);
-    out[2 * i] = h[0];
-    out[2 * i + 1] = h[1];
-  }
-  return out;
-}
-// token offset (inside the lane's 8-token run) of operand element e
-__device__ __forceinline__ constexpr int vtok(int e) { return (e >> 1) + 4 * (e & 1); }
-
-// Token (0..31) of key-operand row m in half s of a tile: rows 4g..4g+3 of
-// the two halves cover tokens 8g..8g+7, so that output row 4g + r of half s
-// is token 8g + 4s + r.
-__device__ __forceinline__ constexpr int row_token(int s, int m) { return 8 * (m >> 2) + 4 * s + (m & 3); }
-
-// x - (fp32) of the low / high fp16 half of h, exact (the fp16 value is
-// widened exactly and one fp32 rounding applies, none here since hi is x
-// rounded toward zero).  One mixed-precision FMA each; the compiler forms
-// a widening conversion and a subtraction instead.
-__device__ __forceinline__ float minus_half_lo(uint32_t h, float x) {
-  float r;
-  asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "v"(x));
-  return r;
-}
-__device__ __forceinline__ float minus_half_hi(uint32_t h, float x) {
-  float r;
-  asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "v"(x));
-  return r;
-}
-
-// Split 8 fp32 values into fp16 hi + lo (hi rounded toward zero; lo the
-// exact fp32 remainder rounded toward zero).
-__device__ __forceinline__ void split8(const float* x, half8& hi, half8& lo) {
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(x[2 * p], x[2 * p + 1]));
-    const half2v hv = __builtin_bit_cast(half2v, h);
-    const half2v l = __builtin_bit_cast(
-        half2v, __builtin_amdgcn_cvt_pkrtz(minus_half_lo(h, x[2 * p]), minus_half_hi(h, x[2 * p + 1])));
-    hi[2 * p] = hv[0];
-    hi[2 * p + 1] = hv[1];
-    lo[2 * p] = l[0];
-    lo[2 * p + 1] = l[1];
-  }
-}
-
-// Reductions over the 4 lanes L, L^16, L^32, L^48 (the four 16-lane rows),
-// with the row-swap permutes of the VALU; every lane gets the result.  Each
-// permute swaps rows between two copies of v.  The two results are copied
-// into scalars before they are reinterpreted: a bit cast applied directly
-// to an element of the returned vector reads element 0.
-template <bool MAX>
-__device__ __forceinline__ float combine2(float v, bool rows32) {
-  const unsigned x = __builtin_bit_cast(unsigned, v);
-  unsigned r0, r1;
-  if (rows32) {
-    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-    r0 = r[0];
-    r1 = r[1];
-  } else {
-    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
-    r0 = r[0];
-    r1 = r[1];
-  }
-  const float f0 = __builtin_bit_cast(float, r0), f1 = __builtin_bit_cast(float, r1);
-  return MAX ? fmaxf(f0, f1) : f0 + f1;
-}
-__device__ __forceinline__ float max_rows(float v) { return combine2<true>(combine2<true>(v, true), false); }
-__device__ __forceinline__ float sum_rows(float v) { return combine2<false>(combine2<false>(v, true), false); }
-
-// First float of row j (token j of a tile) of the in-tile rotation table,
-// whose rows are ERF floats apart.
-template <int ERF>
-__device__ __forceinline__ constexpr int erow(int j) { return j * ERF + 16 * ((j >> 3) & 3); }
+// 2- and 4-bit caches with RoPE run the feature-product kernel (decode_feat.hip)
+inline bool use_feat(int bits, bool rope) { return rope && (bits == 2 || bits == 4); }
 
 // ------------------------------------------------------------- the kernel
 
@@ -801,7 +521,8 @@ int make_plan(const dqa_kivi_cache* c, Plan* p) {
   // kernel has waves per SIMD), at least one tile per wave when the cache is
   // long enough; an empty cache still gets one split (zero output).
   const long long n_tiles = p->n_qtiles + p->n_rtiles;
-  long long want = (decode_workgroups(c->bits) + static_cast<long long>(p->units) - 1) /
+  const int wg = use_feat(c->bits, c->rope_theta > 0.0f) ? feat_decode_workgroups() : decode_workgroups(c->bits);
+  long long want = (wg + static_cast<long long>(p->units) - 1) /
                    static_cast<long long>(p->units > 0 ? p->units : 1);
   long long cap = (n_tiles + kWavesPerWG - 1) / kWavesPerWG;
   if (want > cap) want = cap;
@@ -932,8 +653,14 @@ extern "C" int decode_attention_qkv_partial(const uint16_t* q, const dqa_kivi_ca
     a.omega[i] = (rope && i < c->d / 2) ? std::pow(static_cast<double>(c->rope_theta), -2.0 * i / c->d) : 0.0;
   const dim3 grid(p.total, c->Hkv, c->B);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (c->d == 128) launch_decode<128>(a, p.G, c->bits, rope, grid, s);
-  else launch_decode<64>(a, p.G, c->bits, rope, grid, s);
+  if (use_feat(c->bits, rope)) {
+    const int st2 = launch_feat_decode(a, c->d, p.G, c->bits, grid, s);
+    if (st2 != DQA_OK) return st2;
+  } else if (c->d == 128) {
+    launch_decode<128>(a, p.G, c->bits, rope, grid, s);
+  } else {
+    launch_decode<64>(a, p.G, c->bits, rope, grid, s);
+  }
   DQA_CHECK_LAUNCH();
   return DQA_OK;
 }
