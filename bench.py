@@ -3,13 +3,13 @@ one MI355X, Llama-3.1-8B-shaped GQA workload (batch 4, 32 query / 8 KV
 heads, head dim 128, 32768 quantized tokens + 128 fp16 recent tokens, RoPE
 theta 5e5).
 
-One step = one decode step over the whole batch, i.e. what
-decode_attention_qkv enqueues: the split kernel (kivi_feat_kernel: every
-quantized token's packed codes and scales plus the fp16 recent zone are read
-from HBM, dequantized, rotated and attended) and the merge of the splits
-(split_merge_kernel).  The split kernel's average duration, for the roofline
-figure, is timed separately over back-to-back launches of the split phase
-alone.  Inputs are resident
+One step = one decode step over the whole batch, i.e. one
+decode_attention_qkv call: one kernel (kivi_feat_kernel: every quantized
+token's packed codes and scales plus the fp16 recent zone are read from
+HBM and attended with the rotation folded into the key product; the last
+workgroup of each (batch, KV head) merges its splits).  The kernel's average
+duration, for the roofline figure, is timed separately over back-to-back
+launches through the split-phase entry point.  Inputs are resident
 in HBM before the timed region.  The compressed cache (~98 MiB) fits in the
 256 MB Infinity Cache, so the timed steps rotate over several independent
 replicas whose total exceeds it.
@@ -350,12 +350,13 @@ def time_rvq(dqa, torch, dev):
 
 
 def time_decode(dqa, torch, dev, cfg, bits, replicas, steps, warmup, inp=None):
-    """One decode step = decode_attention_qkv_partial (the split kernel) +
-    decode_attention_qkv_merge, over `replicas` independent copies of the
+    """One decode step = one decode_attention_qkv call (one kernel, which
+    also merges the splits), over `replicas` independent copies of the
     quantized cache (rotated so that the working set exceeds the 256 MB
     Infinity Cache).  Returns the step time from HIP events around `steps`
-    steps, and the split kernel's average duration from HIP events around
-    `steps` back-to-back split-kernel launches (no merge in between)."""
+    steps, and the kernel's average duration from HIP events around `steps`
+    back-to-back launches through decode_attention_qkv_partial (no host-side
+    merge call in between)."""
     from workloads import kivi_inputs
     if inp is None:
         inp = kivi_inputs(cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["d"], cfg["T_q"], cfg["R"], seed=cfg["seed"],
@@ -382,9 +383,7 @@ def time_decode(dqa, torch, dev, cfg, bits, replicas, steps, warmup, inp=None):
     torch.cuda.synchronize()
 
     def step(i):
-        c, w = caches[i % len(caches)], ws[i % len(ws)]
-        dqa.decode_attention_qkv_partial(q, c, scale, out, w)
-        dqa.decode_attention_qkv_merge(c, out, w)
+        dqa.decode_attention_qkv(q, caches[i % len(caches)], scale, out=out, workspace=ws[i % len(ws)])
 
     def split_only(i):
         dqa.decode_attention_qkv_partial(q, caches[i % len(caches)], scale, out, ws[i % len(ws)])
@@ -417,11 +416,12 @@ def decode_kernel_name(cfg):
 
 def _decode_row(cfg, bits, r):
     gbps = r["algorithmic_bytes"] / (r["kernel_ms"] * 1e-3) / 1e9
-    return {"kernel": f"{decode_kernel_name(cfg)} + split_merge_kernel", "workload": cfg["workload"], "bits": bits,
+    return {"kernel": decode_kernel_name(cfg), "workload": cfg["workload"], "bits": bits,
             "us_per_step": r["step_ms"] * 1e3, "kv_tokens_per_s": r["kv_tokens"] / (r["step_ms"] * 1e-3),
             "kernel_us": r["kernel_ms"] * 1e3, "bound": "hbm", "algorithmic_bytes": r["algorithmic_bytes"],
             "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS,
-            "note": "kernel_us: back-to-back split-kernel launches; us_per_step: split kernel + merge"}
+            "note": "kernel_us: back-to-back launches of the split-phase entry point; us_per_step: "
+                    "decode_attention_qkv calls"}
 
 
 def main():

@@ -190,11 +190,11 @@ class KiviCache:
         return lib.decode_attention_workspace_bytes(ctypes.byref(self.struct()))
 
     def workspace(self, device):
-        """A workspace of the required size, cached on the cache object
-        (it needs no initialization)."""
+        """A zeroed workspace of the required size, cached on the cache
+        object (every decode call leaves its merge counters zero)."""
         n = self.workspace_bytes()
         if self._ws is None or self._ws.numel() < n or self._ws.device != device:
-            self._ws = torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+            self._ws = torch.zeros(max(n, 256), dtype=torch.uint8, device=device)
         return self._ws
 
 

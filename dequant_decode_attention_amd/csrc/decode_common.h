@@ -20,6 +20,7 @@ struct KiviArgs {
   const uint16_t* v_recent;
   float* out;
   float* partials;
+  uint32_t* counters;   // merge counters, one per (batch, KV head)
   int Hq, Hkv, T_q, R;
   int qtile_stride;     // 32-token tiles of quantized-buffer capacity per (batch, KV head)
   int R_cap;            // recent-buffer rows per (batch, KV head)

@@ -48,6 +48,8 @@
 // Recent fp16 tokens (at most 4 tiles per (batch, KV head), spread over
 // different waves): keys rotated in fp32 from the trig table, split into
 // fp16 hi + lo, against the query rotated to the tile start.
+#include <type_traits>
+
 #include "decode_common.h"
 #include "merge.h"
 
@@ -140,6 +142,33 @@ __device__ __forceinline__ half8 feat_value_codes8(uint32_t chunk) {
   return out;
 }
 
+// Operand order of a lane group's trig registers.  Quad q (4 consecutive
+// registers, one MFMA A operand) holds the pairs zero-point K-step q reads:
+// those of code K-steps 2q and 2q + 1, each (pa, pb) with pa the pair of the
+// code word's low half and pb = pa + HPW the matching pair of its high half.
+// pair_at: position -> pair (relative to the lane group); pos_of: inverse.
+template <int EPW>
+__host__ __device__ constexpr int pair_at(int pos) {
+  constexpr int HPW = EPW / 2;
+  const int k = 2 * (pos / 4) + ((pos % 4) >> 1);
+  return (k / HPW) * EPW + k % HPW + (pos & 1) * HPW;
+}
+template <int EPW>
+__host__ __device__ constexpr int pos_of(int pair) {
+  constexpr int HPW = EPW / 2;
+  const int k = (pair / EPW) * HPW + pair % HPW;
+  return 4 * (k / 2) + 2 * (k % 2) + (pair % EPW) / HPW;
+}
+
+template <int EPW, int PPG>
+constexpr bool operand_order_is_permutation() {
+  for (int p = 0; p < PPG; ++p)
+    if (pair_at<EPW>(p) < 0 || pair_at<EPW>(p) >= PPG || pos_of<EPW>(pair_at<EPW>(p)) != p) return false;
+  return true;
+}
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 // ----------------------------------------------------------------- kernel
 
 template <int D, int BITS, int G>
@@ -171,6 +200,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kFWavesPerS
   static_assert(NITEM <= kWave, "one factor item per lane");
   static_assert(G * 4 * KSR <= kWave, "one recent-query item per lane");
   static_assert(HPW % 2 == 0 && KSC % 2 == 0, "K-step pairs share a word");
+  static_assert(operand_order_is_permutation<EPW, PPG>(), "trig operand order");
 
   // fp32 (cos, sin) of j * w_i, j = 0..32, i < NP (the whole workgroup's
   // table; row 32 steps the query from one tile start to the next)
@@ -182,7 +212,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kFWavesPerS
   __shared__ __attribute__((aligned(16))) _Float16 lds_ksz[kFWaves][2][D];
   __shared__ __attribute__((aligned(16))) _Float16 lds_vst[kFWaves][kGroup * VST];
   __shared__ float lds_m[kFWaves][G], lds_l[kFWaves][G];
-  __shared__ float lds_o[kFWaves][G][D];
+  // set-up area: the trig heads and tails as packed fp16 (cos, sin) pairs
+  // (times 2^15) of j = 0..31 and the unit numbers e^{i t0 w} of every
+  // wave's first quantized tile start t0; afterwards the waves' output rows
+  // (rows padded by 16 bytes: the 16 tokens one instruction reads start in
+  // different banks)
+  constexpr int TPR = NP + 4;
+  constexpr int kTrigPackBytes = 2 * kGroup * TPR * 4;
+  constexpr int kSetupBytes = kTrigPackBytes + kFWaves * NP * 8;
+  constexpr int kOutBytes = kFWaves * G * D * 4;
+  __shared__ __attribute__((aligned(16))) uint8_t lds_setup[kSetupBytes > kOutBytes ? kSetupBytes : kOutBytes];
+  uint32_t (*const lds_th)[TPR] = reinterpret_cast<uint32_t (*)[TPR]>(lds_setup);
+  uint32_t (*const lds_tl)[TPR] = reinterpret_cast<uint32_t (*)[TPR]>(lds_setup + kTrigPackBytes / 2);
+  float2 (*const lds_rot)[NP] = reinterpret_cast<float2 (*)[NP]>(lds_setup + kTrigPackBytes);
+  float (*const lds_o)[G][D] = reinterpret_cast<float (*)[G][D]>(lds_setup);
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int col = lane & 15, grp = lane >> 4;
@@ -211,31 +254,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kFWavesPerS
   const int qb = u0 - r_before;
   const int qe = u1 - r_before - r_mine;
 
-  // ---- trig table (accurate: angle reduced in fp64, sin/cos in fp32)
-  for (int e = tid; e < (kGroup + 1) * NP; e += 256) {
-    const int j = e / NP, i = e % NP;
-    float c, s;
-    rope_unit(static_cast<double>(j), a.omega[i], c, s);
-    lds_trig[j][i] = float2{c, s};
-  }
-  __syncthreads();
-
-  // ---- the lane's trig registers: tokens j(s) (rows of the A operand of
-  // half s), pairs grp * PPG + rho; head (HB significant bits) and tail,
-  // both times 2^15, as fp16 (cos, sin) pairs
-  uint32_t tsh[2][PPG], tsl[2][PPG];
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    const int j = row_token(s, col);
-#pragma unroll
-    for (int rho = 0; rho < PPG; ++rho) {
-      const float2 cs = lds_trig[j][grp * PPG + rho];
-      const float ch = trunc_sig(cs.x, HB), sh = trunc_sig(cs.y, HB);
-      tsh[s][rho] = pack_f16(ch * kTrigScale, sh * kTrigScale);
-      tsl[s][rho] = pack_f16((cs.x - ch) * kTrigScale, (cs.y - sh) * kTrigScale);
-    }
-  }
-
   // ---- per-tile factor item of this lane: head ih, lane group ig, K-step
   // pair ikb (code K-steps 2 ikb, 2 ikb + 1; zero-point K-step ikb).  Its four
   // pairs (relative to the lane group): p0 = piA(2 ikb), p1 = piB(2 ikb),
@@ -248,68 +266,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kFWavesPerS
   const int ip0 = (iks / HPW) * EPW + iks % HPW;            // piA(2 ikb)
   const int ich = 2 * (ig * PPG + ip0);                       // first channel of chunk A
   // the item's query pairs in the order (p0, p2, p1, p3) = channels
-  // (cA, cA + 2, cA + EPW, cA + EPW + 2)
-  float iq[4][2];
+  // (cA, cA + 2, cA + EPW, cA + EPW + 2), loaded now and rotated back to the
+  // first tile after the set-up
+  uint32_t qraw[4];
   {
     const uint16_t* qh = a.q + (static_cast<size_t>(b) * a.Hq + kvh * G + ih) * D;
-    const float qs = a.q_scale * 32.0f;      // log2-domain logits, code factors carry 2^5
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int c = ich + 2 * (k & 1) + EPW * (k >> 1);
-      const int pi = c / 2;
-      const uint32_t w = *reinterpret_cast<const uint32_t*>(qh + c);
-      const float x0 = h2f(static_cast<uint16_t>(w & 0xFFFFu)) * qs;
-      const float x1 = h2f(static_cast<uint16_t>(w >> 16)) * qs;
-      float cc, ss;
-      rope_unit(static_cast<double>(qb) * kGroup, a.omega[pi], cc, ss);
-      iq[k][0] = x0 * cc + x1 * ss;          // R(-t0) q
-      iq[k][1] = x1 * cc - x0 * ss;
-    }
+    for (int k = 0; k < 4; ++k)
+      qraw[k] = *reinterpret_cast<const uint32_t*>(qh + ich + 2 * (k & 1) + EPW * (k >> 1));
   }
 
-  _Float16* const Bw = &lds_B[wave][0][0];
-
-  float4v acc[MB];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) acc[mb] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
-  float m = -INFINITY, lsum = 0.0f, zacc = 0.0f;
-  const int qh = col % G;                         // logit column -> query head
-  const int vg = min(col / G, NVG - 1);           // value column -> value group
-  const int bcol = col % NBC;                     // B column this lane reads
-
-  // hi + lo logit columns: lanes col and col +- G (mod 2G) hold the same head
-  auto combine_cols = [&](float x) -> float {
-    if constexpr (G == 4) return x + dpp<0x124>(x);          // row_ror:4
-    else if constexpr (G == 2) return x + dpp<kDppQuadXor2>(x);
-    else return x + dpp<kDppQuadXor1>(x);
-  };
-
-  // online softmax over the lane's 8 logits (the column max over the 4 row
-  // groups); returns the probabilities in p
-  auto softmax_step = [&](float* lg, float* p) {
-    float tm = lg[0];
-#pragma unroll
-    for (int e = 1; e < 8; ++e) tm = fmaxf(tm, lg[e]);
-    tm = max_rows(tm);
-    const float mn = fmaxf(m, tm);
-    if (__builtin_amdgcn_ballot_w64(mn > m) != 0) {
-      const float sc = merge_weight(m, mn);
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) acc[mb] *= sc;
-      lsum *= sc;
-      zacc *= sc;
-    }
-    m = mn;
-    float ps = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      p[e] = (mn == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(lg[e] - mn);
-      ps += p[e];
-    }
-    lsum += ps;
-  };
-
-  // ------------------------------------------------------- quantized tile
+  // ---- tile inputs.  The first quantized tile's loads are issued before
+  // the set-up below, so their latency overlaps it.
   const size_t qstride = static_cast<size_t>(a.qtile_stride);
   const uint16_t* const ksz_s = uniform_ptr(a.k_scale);
   const uint16_t* const ksz_z = uniform_ptr(a.k_zero);
@@ -352,6 +320,124 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kFWavesPerS
     for (int i = 0; i < NVG / 2; ++i) t.vsz[i] = vw.w[i];
   };
 
+  TileIn buf0, buf1;
+  if (qb < qe) load_tile(qb, buf0);
+
+  // ---- trig tables.  e^{i j w} for j = 4a + b is the product of two of 11
+  // accurately rounded unit numbers (angle 4a w, a = 1..8, and b w, b =
+  // 1..3: angle reduced in fp64, sin/cos in fp32), staged in the B area; the
+  // same pass computes e^{i t0 w} of this wave's first quantized tile.
+  {
+    float2 (*const base)[NP] = reinterpret_cast<float2 (*)[NP]>(&lds_B[0][0][0]);
+    static_assert(sizeof(lds_B) >= 11 * NP * sizeof(float2), "trig bases fit the B area");
+    for (int e = tid; e < 11 * NP; e += 256) {
+      const int r = e / NP, i = e % NP;
+      float c, s;
+      rope_unit(static_cast<double>(r < 8 ? 4 * (r + 1) : r - 7), a.omega[i], c, s);
+      base[r][i] = float2{c, s};
+    }
+    if (lane < NP) {
+      float c, s;
+      rope_unit(static_cast<double>(qb) * kGroup, a.omega[lane], c, s);
+      lds_rot[wave][lane] = float2{c, s};
+    }
+    __syncthreads();
+    for (int e = tid; e < (kGroup + 1) * NP; e += 256) {
+      const int j = e / NP, i = e % NP;
+      const int ja = j >> 2, jb = j & 3;
+      const float2 u = ja ? base[ja - 1][i] : float2{1.0f, 0.0f};
+      const float2 v = jb ? base[7 + jb][i] : float2{1.0f, 0.0f};
+      const float c = fmaf(u.x, v.x, -(u.y * v.y)), s = fmaf(u.y, v.x, u.x * v.y);
+      lds_trig[j][i] = float2{c, s};
+      if (j < kGroup) {
+        const float ch = trunc_sig(c, HB), sh = trunc_sig(s, HB);
+        const int ps = (i / PPG) * PPG + pos_of<EPW>(i % PPG);
+        lds_th[j][ps] = pack_f16(ch * kTrigScale, sh * kTrigScale);
+        lds_tl[j][ps] = pack_f16((c - ch) * kTrigScale, (s - sh) * kTrigScale);
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- the lane's trig registers: tokens j(s) (rows of the A operand of
+  // half s), pairs grp * PPG + pair_at(pos); head (HB significant bits) and
+  // tail, both times 2^15, as fp16 (cos, sin) pairs, in operand order
+  u32x4 tqh[2][PPG / 4], tql[2][PPG / 4];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int j = row_token(s, col);
+#pragma unroll
+    for (int q = 0; q < PPG / 4; ++q) {
+      tqh[s][q] = *reinterpret_cast<const u32x4*>(&lds_th[j][grp * PPG + 4 * q]);
+      tql[s][q] = *reinterpret_cast<const u32x4*>(&lds_tl[j][grp * PPG + 4 * q]);
+    }
+  }
+  auto trig_h = [&](int s, int pair) -> uint32_t { return tqh[s][pos_of<EPW>(pair) / 4][pos_of<EPW>(pair) % 4]; };
+  auto trig_l = [&](int s, int pair) -> uint32_t { return tql[s][pos_of<EPW>(pair) / 4][pos_of<EPW>(pair) % 4]; };
+
+  float iq[4][2];
+  {
+    const float qs = a.q_scale * 32.0f;      // log2-domain logits, code factors carry 2^5
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int c = ich + 2 * (k & 1) + EPW * (k >> 1);
+      const float x0 = h2f(static_cast<uint16_t>(qraw[k] & 0xFFFFu)) * qs;
+      const float x1 = h2f(static_cast<uint16_t>(qraw[k] >> 16)) * qs;
+      const float2 r = lds_rot[wave][c / 2];
+      iq[k][0] = x0 * r.x + x1 * r.y;        // R(-t0) q
+      iq[k][1] = x1 * r.x - x0 * r.y;
+    }
+  }
+  // the set-up area is the output area from here on
+  __syncthreads();
+
+  _Float16* const Bw = &lds_B[wave][0][0];
+
+  float4v acc[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) acc[mb] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+  float m = -INFINITY, lsum = 0.0f, zacc = 0.0f;
+  const int qh = col % G;                         // logit column -> query head
+  const int vg = min(col / G, NVG - 1);           // value column -> value group
+  const int bcol = col % NBC;                     // B column this lane reads
+
+  // hi + lo logit columns: lanes col and col +- G (mod 2G) hold the same head
+  auto combine_cols = [&](float x) -> float {
+    if constexpr (G == 4) return x + dpp<0x124>(x);          // row_ror:4
+    else if constexpr (G == 2) return x + dpp<kDppQuadXor2>(x);
+    else return x + dpp<kDppQuadXor1>(x);
+  };
+
+  // online softmax over the lane's 8 logits (the column max over the 4 row
+  // groups); returns the probabilities in p.  MASKED: some logits may be
+  // -inf (a partial recent tile), so the running max may still be -inf.
+  auto softmax_step = [&](float* lg, float* p, auto masked) {
+    float tm = lg[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) tm = fmaxf(tm, lg[e]);
+    tm = max_rows(tm);
+    const float mn = fmaxf(m, tm);
+    if (__builtin_amdgcn_ballot_w64(mn > m) != 0) {
+      const float sc = merge_weight(m, mn);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) acc[mb] *= sc;
+      lsum *= sc;
+      zacc *= sc;
+    }
+    m = mn;
+    float ps = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if constexpr (decltype(masked)::value)
+        p[e] = (mn == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(lg[e] - mn);
+      else
+        p[e] = __builtin_amdgcn_exp2f(lg[e] - mn);
+      ps += p[e];
+    }
+    lsum += ps;
+  };
+
+  // ------------------------------------------------------- quantized tile
   // per-tile factors of the item -> B (hi in column ih, lo in G + ih)
   auto write_factors = [&]() {
     if (!item) return;
@@ -444,14 +530,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kFWavesPerS
 #pragma unroll
     for (int kb = 0; kb < KSB; ++kb) {
       const half8 bv = *reinterpret_cast<const half8*>(Bw + bcol * BST + 32 * (KSC + kb) + 8 * grp);
-      const int k0 = 2 * kb, k1 = 2 * kb + 1;
-      const int pa0 = (k0 / HPW) * EPW + k0 % HPW, pa1 = (k1 / HPW) * EPW + k1 % HPW;
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        const uint32_t ah[4] = {tsh[s][pa0], tsh[s][pa0 + HPW], tsh[s][pa1], tsh[s][pa1 + HPW]};
-        const uint32_t al[4] = {tsl[s][pa0], tsl[s][pa0 + HPW], tsl[s][pa1], tsl[s][pa1 + HPW]};
-        sacc[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, ah), bv, sacc[s], 0, 0, 0);
-        sacc[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, al), bv, sacc[s], 0, 0, 0);
+        sacc[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, tqh[s][kb]), bv, sacc[s], 0, 0, 0);
+        sacc[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, tql[s][kb]), bv, sacc[s], 0, 0, 0);
       }
     }
 #pragma unroll
@@ -466,14 +548,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kFWavesPerS
         const uint32_t ca = key_code_at4<BITS>(cur.k[s][w], 2 * ip);
         const uint32_t cb = key_code_at4<BITS>(cur.k[s][w], 2 * ip + 1);
         uint32_t ah[4], al[4];
-        ah[0] = pk_mul_bcast<0>(ca, tsh[s][pa]);
-        ah[1] = pk_mul_bcast<0>(cb, tsh[s][pa]);
-        ah[2] = pk_mul_bcast<1>(ca, tsh[s][pb]);
-        ah[3] = pk_mul_bcast<1>(cb, tsh[s][pb]);
-        al[0] = pk_mul_bcast<0>(ca, tsl[s][pa]);
-        al[1] = pk_mul_bcast<0>(cb, tsl[s][pa]);
-        al[2] = pk_mul_bcast<1>(ca, tsl[s][pb]);
-        al[3] = pk_mul_bcast<1>(cb, tsl[s][pb]);
+        ah[0] = pk_mul_bcast<0>(ca, trig_h(s, pa));
+        ah[1] = pk_mul_bcast<0>(cb, trig_h(s, pa));
+        ah[2] = pk_mul_bcast<1>(ca, trig_h(s, pb));
+        ah[3] = pk_mul_bcast<1>(cb, trig_h(s, pb));
+        al[0] = pk_mul_bcast<0>(ca, trig_l(s, pa));
+        al[1] = pk_mul_bcast<0>(cb, trig_l(s, pa));
+        al[2] = pk_mul_bcast<1>(ca, trig_l(s, pb));
+        al[3] = pk_mul_bcast<1>(cb, trig_l(s, pb));
         sacc[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, ah), bv, sacc[s], 0, 0, 0);
         sacc[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, al), bv, sacc[s], 0, 0, 0);
       }
@@ -485,7 +567,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kFWavesPerS
       lg[2 * r] = combine_cols(sacc[0][r]);
       lg[2 * r + 1] = combine_cols(sacc[1][r]);
     }
-    softmax_step(lg, p);
+    softmax_step(lg, p, std::false_type{});
 
     // value product: column (head qh, group vg) holds p * scale
     const half8 vs = *reinterpret_cast<const half8*>(&lds_vsz[wave][0][vg][8 * grp]);
@@ -581,7 +663,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kFWavesPerS
 #pragma unroll
     for (int e = 0; e < 8; ++e)
       if (r0 + 8 * grp + vtok(e) >= a.R) lg[e] = -INFINITY;
-    softmax_step(lg, p);
+    softmax_step(lg, p, std::true_type{});
     half8 bv;
 #pragma unroll
     for (int e = 0; e < 8; ++e) bv[e] = static_cast<_Float16>(col < NCOL ? p[e] : 0.0f);
@@ -602,8 +684,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kFWavesPerS
 
   // the wave's recent tiles, then its quantized run; two register buffers
   // alternate so that the loads of tile i+1 stay in flight during tile i
-  TileIn buf0, buf1;
-  if (qb < qe) load_tile(qb, buf0);
   for (int k = 0; k < r_mine; ++k) recent_tile(r_first + k);
   // fp16 value products are exact-scale; switch the accumulator to the
   // code-product domain (a power of two: exact)
@@ -634,8 +714,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kFWavesPerS
     lds_l[wave][lane] = lsum;
   }
   __syncthreads();
-  write_split_state<D, G, kFWaves>(a.partials, a.out, a.Hq, unit, b, kvh, split, a.total_splits, lds_m, lds_l,
-                                   lds_o);
+  write_split_state<D, G, kFWaves>(a.partials, a.counters, a.out, a.Hq, unit, b, kvh, split, a.total_splits,
+                                   lds_m, lds_l, lds_o);
 }
 
 template <int D, int BITS>

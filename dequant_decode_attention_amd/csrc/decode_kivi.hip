@@ -30,8 +30,8 @@
 //     exactly the tokens that column n of the value operand needs, so no
 //     data moves between the two products.
 // The online softmax runs once per tile per column.  Each split writes its
-// partial softmax state; split_merge_kernel (merge.h) merges the splits of
-// every (batch, KV head) in split order.
+// partial softmax state; the last split of every (batch, KV head) to finish
+// merges them in split order (merge.h).
 #include <mutex>
 
 #include "decode_common.h"
@@ -491,8 +491,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kDecodeWave
     lds_l[wave][lane] = lsum;
   }
   __syncthreads();
-  write_split_state<D, G, kWavesPerWG>(a.partials, a.out, a.Hq, unit, b, kvh, split, a.total_splits, lds_m,
-                                       lds_l, lds_o);
+  write_split_state<D, G, kWavesPerWG>(a.partials, a.counters, a.out, a.Hq, unit, b, kvh, split,
+                                       a.total_splits, lds_m, lds_l, lds_o);
 }
 
 // ---------------------------------------------------------------- host side
@@ -637,7 +637,8 @@ extern "C" int decode_attention_qkv_partial(const uint16_t* q, const dqa_kivi_ca
   a.k_recent = c->k_recent;
   a.v_recent = c->v_recent;
   a.out = out;
-  a.partials = static_cast<float*>(ws);
+  a.partials = merge_partials(ws, p.units);
+  a.counters = merge_counters(ws);
   a.Hq = c->Hq;
   a.Hkv = c->Hkv;
   a.T_q = c->T_q;
@@ -674,11 +675,8 @@ extern "C" int decode_attention_qkv_merge(const dqa_kivi_cache* c, const void* w
   if (!ws) return DQA_ERR_WORKSPACE;
   if (ws_bytes < p.ws_bytes) return DQA_ERR_WORKSPACE;
   if (!aligned16(ws) || !aligned16(out)) return DQA_ERR_ALIGN;
-  if (p.total == 1) return DQA_OK;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const float* parts = static_cast<const float*>(ws);
-  if (c->d == 128) return launch_split_merge<128>(parts, p.total, c->B, c->Hq, c->Hkv, out, s);
-  return launch_split_merge<64>(parts, p.total, c->B, c->Hq, c->Hkv, out, s);
+  (void)stream;   // the split kernel merges the splits itself
+  return DQA_OK;
 }
 
 extern "C" int decode_attention_qkv(const uint16_t* q, const dqa_kivi_cache* c,

@@ -4,14 +4,23 @@
 // (batch, KV head) over several workgroups.  A workgroup combines its waves'
 // states and writes one partial state per query head, [m, l, o[D]] in the
 // log2 domain: m the running maximum of the logits, l the sum of
-// 2^(logit - m), o the unnormalized output.  A second, small kernel merges
-// the splits of every (batch, KV head) in split order, so the result does
-// not depend on scheduling.  (A last-workgroup merge inside the decode
-// kernel would need a device-scope fence and a counter atomic per
-// workgroup; on this chip, whose L2 is private to each XCD, those cost more
-// than the decode work itself.)
+// 2^(logit - m), o the unnormalized output.  The workgroup that finishes
+// last among the splits of a (batch, KV head) -- found with one counter per
+// (batch, KV head), incremented once per workgroup -- merges all splits in
+// split order, so the result does not depend on scheduling, and sets the
+// counter back to zero for the next call.
 //
-// Partial-state layout (fp32): [B * Hkv][splits][G][D + 2].
+// The L2 caches are private to each XCD, and a device-scope release fence
+// (an L2 write-back) in every workgroup would cost more than the decode
+// work.  So the partial states are written with device-scope (write-through)
+// stores and read with device-scope loads, which bypass the non-coherent
+// caches; every wave waits for its stores to complete before the workgroup
+// barrier that precedes the counter increment.
+//
+// Workspace layout: uint32 counters [max(B * Hkv, 16384)] (rounded up to 256
+// bytes), then fp32 partial states [B * Hkv][splits][G][D + 2].  The
+// counters must be zero before the first call on a workspace; every call
+// leaves them zero.
 #pragma once
 
 #include "common.h"
@@ -19,18 +28,37 @@
 namespace dqa {
 namespace {
 
-// splits per (batch, KV head) at most (the merge keeps one weight per split)
-constexpr int kMaxSplitsMerge = 255;
+// splits per (batch, KV head) at most (their m and l must fit a workgroup's
+// output staging, NW * G * D floats, with NW >= 4 and D >= 64)
+constexpr int kMaxSplitsMerge = 128;
+
+// Counters at the start of a workspace: one per (batch, KV head), at least
+// 16384 of them, so that a workspace can serve cache shapes of up to 16384
+// (batch, KV head) units without being cleared again.
+constexpr size_t kMergeCountersMin = 16384;
+inline size_t merge_counter_bytes(size_t units) {
+  const size_t n = (units > kMergeCountersMin ? units : kMergeCountersMin) * sizeof(uint32_t);
+  return (n + 255) / 256 * 256;
+}
+inline uint32_t* merge_counters(void* ws) { return static_cast<uint32_t*>(ws); }
+inline float* merge_partials(void* ws, size_t units) {
+  return reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + merge_counter_bytes(units));
+}
 
 // Combine the NW wave states of a workgroup (LDS: lm, ll [NW][G], lo
-// [NW][G][D]) and write split `slot`'s partial state -- or, with a single
-// split, the normalized output out[b][kvh * G + h][c].  Called by every
-// thread of the workgroup.
+// [NW][G][D]).  With a single split: the normalized output
+// out[b][kvh * G + h][c].  Otherwise: split `slot`'s partial state, and if
+// this workgroup is the last of its (batch, KV head) to finish, the merge of
+// all splits into out (lo is reused as staging for the splits' m and l).
+// Called by every thread of the workgroup.
 template <int D, int G, int NW>
-__device__ __forceinline__ void write_split_state(float* partials, float* out, int Hq, size_t unit, int b,
-                                                  int kvh, int slot, int total_splits, const float (*lm)[G],
-                                                  const float (*ll)[G], const float (*lo)[G][D]) {
-  float* part = partials + (unit * total_splits + slot) * G * (D + 2);
+__device__ __forceinline__ void write_split_state(float* partials, uint32_t* counters, float* out, int Hq,
+                                                  size_t unit, int b, int kvh, int slot, int total_splits,
+                                                  const float (*lm)[G], const float (*ll)[G],
+                                                  float (*lo)[G][D]) {
+  static_assert(2 * kMaxSplitsMerge * G <= NW * G * D, "m and l of every split fit the output staging");
+  __shared__ int s_last;
+  float* const part = partials + (unit * total_splits + slot) * G * (D + 2);
   for (int e = threadIdx.x; e < G * D; e += blockDim.x) {
     const int h = e / D, c = e % D;
     float M = -INFINITY;
@@ -47,79 +75,83 @@ __device__ __forceinline__ void write_split_state(float* partials, float* out, i
       out[(static_cast<size_t>(b) * Hq + kvh * G + h) * D + c] = (L > 0.0f) ? O / L : 0.0f;
     } else {
       if (c == 0) {
-        part[h * (D + 2) + 0] = M;
-        part[h * (D + 2) + 1] = L;
+        __hip_atomic_store(part + h * (D + 2) + 0, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(part + h * (D + 2) + 1, L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
-      part[h * (D + 2) + 2 + c] = O;
+      __hip_atomic_store(part + h * (D + 2) + 2 + c, O, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-}
-
-// One wave per (64 output channels of one query head, KV head, batch): the
-// lanes compute the merge weight of every split (max over splits, then
-// exp2 weights and the weighted row sum, combined in a fixed butterfly
-// order), then each lane sums its channel over the splits in split order.
-// The first 32 splits' outputs are loaded together with the states.
-template <int D, int G>
-__global__ __launch_bounds__(64) void split_merge_kernel(const float* __restrict__ partials, int total_splits,
-                                                         int Hq, int Hkv, float* __restrict__ out) {
-  constexpr int kEarly = 32;
-  __shared__ float wts[kMaxSplitsMerge];
-  __shared__ float inv_l;
-  constexpr int CB = D / 64;                 // 64-channel blocks per head
-  const int h = blockIdx.x / CB, c = (blockIdx.x % CB) * 64 + threadIdx.x;
-  const int kvh = blockIdx.y, b = blockIdx.z;
-  const size_t unit = static_cast<size_t>(b) * Hkv + kvh;
-  const float* parts = partials + unit * total_splits * G * (D + 2) + h * (D + 2);
-  constexpr size_t kSplitStride = static_cast<size_t>(G) * (D + 2);
-  float early[kEarly];
-#pragma unroll
-  for (int i = 0; i < kEarly; ++i) early[i] = (i < total_splits) ? parts[i * kSplitStride + 2 + c] : 0.0f;
-  float M = -INFINITY;
-  for (int sl = threadIdx.x; sl < total_splits; sl += 64) M = fmaxf(M, parts[sl * kSplitStride]);
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
-  float L = 0.0f;
-  for (int sl = threadIdx.x; sl < total_splits; sl += 64) {
-    const float wt = merge_weight(parts[sl * kSplitStride], M);
-    wts[sl] = wt;
-    L = fmaf(parts[sl * kSplitStride + 1], wt, L);
-  }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o, 64);
-  if (threadIdx.x == 0) inv_l = (L > 0.0f) ? 1.0f / L : 0.0f;
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  if (total_splits == 1) return;
+  // every wave's partial-state stores have completed before the barrier
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  float O = 0.0f;
-#pragma unroll
-  for (int i = 0; i < kEarly; ++i)
-    if (i < total_splits) O = fmaf(early[i], wts[i], O);
-  for (int sl = kEarly; sl < total_splits; ++sl) O = fmaf(parts[sl * kSplitStride + 2 + c], wts[sl], O);
-  out[(static_cast<size_t>(b) * Hq + kvh * G + h) * D + c] = O * inv_l;
-}
-
-// Enqueue the merge of `total` splits (nothing for a single split).
-template <int D>
-int launch_split_merge(const float* partials, int total, int B, int Hq, int Hkv, float* out, hipStream_t s) {
-  if (total <= 1) return DQA_OK;
-  const int G = Hq / Hkv;
-  const dim3 grid(G * (D / 64), Hkv, B);
-  switch (G) {
-    case 1: hipLaunchKernelGGL((split_merge_kernel<D, 1>), grid, dim3(64), 0, s, partials, total, Hq, Hkv, out); break;
-    case 2: hipLaunchKernelGGL((split_merge_kernel<D, 2>), grid, dim3(64), 0, s, partials, total, Hq, Hkv, out); break;
-    case 3: hipLaunchKernelGGL((split_merge_kernel<D, 3>), grid, dim3(64), 0, s, partials, total, Hq, Hkv, out); break;
-    case 4: hipLaunchKernelGGL((split_merge_kernel<D, 4>), grid, dim3(64), 0, s, partials, total, Hq, Hkv, out); break;
-    default: return DQA_ERR_UNSUPPORTED;
+  if (threadIdx.x == 0) {
+    const uint32_t done = __hip_atomic_fetch_add(counters + unit, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = done == static_cast<uint32_t>(total_splits - 1);
   }
-  DQA_CHECK_LAUNCH();
-  return DQA_OK;
+  __syncthreads();
+  if (!s_last) return;
+
+  // ---- the last workgroup: merge every split in split order.  The output
+  // values of the first kChunk splits are loaded together with the splits'
+  // m and l (staged in LDS), so the merge costs one memory round trip for up
+  // to kChunk splits.
+  constexpr int kChunk = 16;
+  constexpr int kPer = (G * D + NW * 64 - 1) / (NW * 64);   // outputs per thread
+  const float* const parts = partials + unit * total_splits * G * (D + 2);
+  constexpr size_t kSplitStride = static_cast<size_t>(G) * (D + 2);
+  auto ld = [](const float* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+  float ov[kPer][kChunk];
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    const int e = threadIdx.x + r * NW * 64;
+    const int h = e / D, c = e % D;
+#pragma unroll
+    for (int k = 0; k < kChunk; ++k)
+      ov[r][k] = (e < G * D && k < total_splits) ? ld(parts + k * kSplitStride + h * (D + 2) + 2 + c) : 0.0f;
+  }
+  float* const sm = &lo[0][0][0];
+  float* const sl = sm + kMaxSplitsMerge * G;
+  // (m, l) of a split and head as one 8-byte load (8-byte aligned: the
+  // state of a head is D + 2 floats, D even)
+  for (int i = threadIdx.x; i < total_splits * G; i += NW * 64) {
+    const uint64_t* p = reinterpret_cast<const uint64_t*>(parts + (i / G) * kSplitStride + (i % G) * (D + 2));
+    const uint64_t ml = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sm[i] = __builtin_bit_cast(float, static_cast<uint32_t>(ml));
+    sl[i] = __builtin_bit_cast(float, static_cast<uint32_t>(ml >> 32));
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    const int e = threadIdx.x + r * NW * 64;
+    if (e >= G * D) break;
+    const int h = e / D, c = e % D;
+    float M = -INFINITY;
+    for (int k = 0; k < total_splits; ++k) M = fmaxf(M, sm[k * G + h]);
+    float L = 0.0f, O = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kChunk; ++k)
+      if (k < total_splits) {
+        const float wt = merge_weight(sm[k * G + h], M);
+        L = fmaf(sl[k * G + h], wt, L);
+        O = fmaf(ov[r][k], wt, O);
+      }
+    for (int k = kChunk; k < total_splits; ++k) {
+      const float wt = merge_weight(sm[k * G + h], M);
+      L = fmaf(sl[k * G + h], wt, L);
+      O = fmaf(ld(parts + k * kSplitStride + h * (D + 2) + 2 + c), wt, O);
+    }
+    out[(static_cast<size_t>(b) * Hq + kvh * G + h) * D + c] = (L > 0.0f) ? O / L : 0.0f;
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(counters + unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Bytes of partial states for `splits` splits (at least 256, so that a
-// workspace query of 0 always means an invalid shape).
+// Workspace bytes of the merge: the counters, then the partial states of
+// `splits` splits (never 0, so that a workspace query of 0 always means an
+// invalid shape).
 inline size_t partial_state_bytes(size_t units, int splits, int G, int D) {
   const size_t n = splits > 1 ? units * static_cast<size_t>(splits) * G * (D + 2) * sizeof(float) : 0;
-  return n < 256 ? 256 : n;
+  return merge_counter_bytes(units) + n;
 }
 
 }  // namespace

@@ -305,6 +305,7 @@ struct RvqDecArgs {
   const uint16_t* v_cb;
   float* out;
   float* partials;
+  uint32_t* counters;   // merge counters, one per (batch, KV head)
   const float* lut;     // [units][G][N][Kc] key-logit table (table path only)
   int Hq, Hkv, T, N, Kc, n_tiles, tiles_per_split, splits;
   float q_scale;
@@ -378,8 +379,8 @@ __device__ __forceinline__ void rebuild16(const uint16_t* cb, const int16_t* idx
 }
 
 // Lane = (token j of 8, 16-channel chunk ck of 8); 32-token tiles; online
-// softmax per tile; each split writes its partial state, merged by
-// split_merge_kernel (merge.h) in split order.
+// softmax per tile; each split writes its partial state, and the last split
+// of a (batch, KV head) to finish merges them in split order (merge.h).
 template <int G, bool LUT>
 __global__ __launch_bounds__(256) void rvq_decode_kernel(RvqDecArgs a) {
   constexpr int NCK = 8, TL = 8, IT = 4;
@@ -566,8 +567,8 @@ __global__ __launch_bounds__(256) void rvq_decode_kernel(RvqDecArgs a) {
     }
   }
   __syncthreads();
-  write_split_state<kD, G, kDecWaves>(a.partials, a.out, a.Hq, unit, b, kvh, split, a.splits, lds_m, lds_l,
-                                      lds_o);
+  write_split_state<kD, G, kDecWaves>(a.partials, a.counters, a.out, a.Hq, unit, b, kvh, split, a.splits,
+                                      lds_m, lds_l, lds_o);
 }
 
 struct RvqGeometry {
@@ -655,7 +656,8 @@ extern "C" int rvq_decode_attention(const uint16_t* q, int B, int Hq, int Hkv, i
   a.k_cb = k_cb;
   a.v_cb = v_cb;
   a.out = out;
-  a.partials = static_cast<float*>(ws);
+  a.partials = merge_partials(ws, g.units);
+  a.counters = merge_counters(ws);
   float* lut = reinterpret_cast<float*>(static_cast<char*>(ws) + g.lut_off);
   a.lut = lut;
   a.Hq = Hq;
@@ -703,5 +705,5 @@ extern "C" int rvq_decode_attention(const uint16_t* q, int B, int Hq, int Hkv, i
     default: return DQA_ERR_UNSUPPORTED;
   }
   DQA_CHECK_LAUNCH();
-  return launch_split_merge<kD>(a.partials, a.splits, B, Hq, Hkv, out, s);
+  return DQA_OK;
 }

@@ -622,6 +622,7 @@ struct ZDecodeArgs {
   const uint16_t* q;
   float* out;
   float* partials;
+  uint32_t* counters;                         // merge counters, one per (batch, KV head)
   int Hq, Hkv, C, items_per_split, splits;   // C: zone-C rows (sink + new tokens)
   int k_out;                                  // side-list entries per key group (0: none)
   float q_scale;
@@ -1060,8 +1061,8 @@ __global__ __launch_bounds__(256, 2) void zoned_decode_kernel(ZDecodeArgs a) {
     }
   }
   __syncthreads();
-  write_split_state<D, G, kZWaves>(a.partials, a.out, a.Hq, static_cast<size_t>(unit), b, kvh, split, a.splits,
-                                   lds_m, lds_l, lds_o);
+  write_split_state<D, G, kZWaves>(a.partials, a.counters, a.out, a.Hq, static_cast<size_t>(unit), b, kvh,
+                                   split, a.splits, lds_m, lds_l, lds_o);
 }
 
 struct ZGeometry {
@@ -1248,7 +1249,8 @@ extern "C" int decode_attention_zoned(const uint16_t* q, int Hq, const int32_t* 
   a.blob = static_cast<const uint8_t*>(blob);
   a.q = q;
   a.out = out;
-  a.partials = static_cast<float*>(ws);
+  a.partials = merge_partials(ws, static_cast<size_t>(g.units));
+  a.counters = merge_counters(ws);
   a.Hq = Hq;
   a.Hkv = plan_host[H_HKV];
   a.C = plan_host[H_C] + plan_host[H_SINK];
@@ -1258,11 +1260,6 @@ extern "C" int decode_attention_zoned(const uint16_t* q, int Hq, const int32_t* 
   a.q_scale = sm_scale * 1.4426950408889634f;
   const dim3 grid(g.splits, g.units);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int B = plan_host[H_B];
-  if (plan_host[H_D] == 128) {
-    st = zlaunch<128>(a, g.G, grid, s);
-    return st != DQA_OK ? st : launch_split_merge<128>(a.partials, g.splits, B, Hq, a.Hkv, out, s);
-  }
-  st = zlaunch<64>(a, g.G, grid, s);
-  return st != DQA_OK ? st : launch_split_merge<64>(a.partials, g.splits, B, Hq, a.Hkv, out, s);
+  if (plan_host[H_D] == 128) return zlaunch<128>(a, g.G, grid, s);
+  return zlaunch<64>(a, g.G, grid, s);
 }

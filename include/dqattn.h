@@ -28,6 +28,15 @@
  *   - Thread safety: entry points are stateless and may be called from
  *     several host threads; calls that share a workspace must be ordered by
  *     the caller (same stream or events).
+ *   - Decode workspaces (decode_attention_qkv, decode_attention_zoned,
+ *     rvq_decode_attention) start with one uint32 counter per (batch, KV
+ *     head), at least 16384 of them: the workgroup that finishes a (batch,
+ *     KV head) last merges the partial states of its splits and sets the
+ *     counter back to zero.  Zero a decode workspace once before its first
+ *     use (e.g. hipMemset after hipMalloc); every completed call leaves the
+ *     counters zero.  A workspace first used for more than 16384 (batch,
+ *     KV head) units must be zeroed again before a call with a different
+ *     B * Hkv.
  */
 #ifndef DQATTN_H
 #define DQATTN_H
@@ -56,7 +65,12 @@ enum {
 const char* dqa_status_string(int status);
 
 /* Version of this interface (increments on any signature or layout change). */
-int dqa_abi_version(void);  /* 9: decode_attention_qkv_noalloc;
+int dqa_abi_version(void);  /* 10: decode workspaces hold merge counters
+                              and must be zeroed before first use; the
+                              split kernel merges its splits itself
+                              (decode_attention_qkv_merge enqueues
+                              nothing);
+                              9: decode_attention_qkv_noalloc;
                               8: decode_attention_zoned and rvq_encode check
                               16-byte alignment; zoned plans are validated in
                               full; kivi_append writes back zero capacities;
@@ -140,9 +154,10 @@ typedef struct dqa_kivi_cache {
 } dqa_kivi_cache;
 
 /* Bytes of workspace decode_attention_qkv needs for this cache shape
- * (0 if the shape is invalid; at least 256 otherwise).  The workspace holds
- * the per-split partial softmax states; it needs no initialization and its
- * contents after a call are unspecified.  Calls that share a workspace must
+ * (0 if the shape is invalid; at least 64 KB otherwise).  The workspace
+ * holds the merge counters and the per-split partial softmax states; zero
+ * it before its first use (see the preamble); every call leaves the counters
+ * zero, the rest unspecified.  Calls that share a workspace must
  * not overlap (same stream, or ordered by events). */
 size_t decode_attention_workspace_bytes(const dqa_kivi_cache* cache);
 
@@ -155,9 +170,9 @@ size_t decode_attention_workspace_bytes(const dqa_kivi_cache* cache);
  *   cache (host) pointer to the descriptor above
  *   ws   (device) workspace of ws_bytes >= decode_attention_workspace_bytes
  *   out  (device) fp32 [B][Hq][d]; zeros when T_q + R == 0
- * Enqueues one kernel, or two when the tokens of a (batch, KV head) are
- * split over several workgroups (the second merges the splits in a fixed
- * order, so results are bit-reproducible run to run).
+ * Enqueues one kernel.  When the tokens of a (batch, KV head) are split
+ * over several workgroups, the workgroup that finishes last merges the
+ * splits in a fixed order, so results are bit-reproducible run to run.
  * Every device pointer (q, ws, out and the cache buffers in use) must be
  * 16-byte aligned (hipMalloc returns 256-byte aligned memory).
  * Supported head ratios Hq/Hkv: 1, 2, 4 (else DQA_ERR_UNSUPPORTED).
@@ -167,16 +182,14 @@ int decode_attention_qkv(const uint16_t* q, const dqa_kivi_cache* cache,
                          float sm_scale, void* ws, size_t ws_bytes, float* out,
                          void* stream);
 
-/* The two phases of decode_attention_qkv, for callers that schedule or time
- * them separately; decode_attention_qkv is exactly _partial then _merge on
- * the same stream, with the same cache, workspace and out.
- * decode_attention_qkv_partial enqueues the split kernel: every split of a
- * (batch, KV head) writes its partial softmax state into ws, or -- when the
- * cache shape gives a single split -- the final output into out.
- * decode_attention_qkv_merge enqueues the merge of the partial states in
- * split order into out (nothing when there is a single split); it reads ws
- * as left by the preceding _partial call.  Arguments, alignment and errors
- * as decode_attention_qkv (the merge checks cache, ws, ws_bytes and out). */
+/* The two phases of decode_attention_qkv; decode_attention_qkv is exactly
+ * _partial then _merge on the same stream, with the same cache, workspace
+ * and out.  decode_attention_qkv_partial enqueues the split kernel, which
+ * also merges the splits (see decode_attention_qkv) and writes out.
+ * decode_attention_qkv_merge enqueues nothing: it checks its arguments and
+ * returns (kept so that callers of the two-phase form keep working).
+ * Arguments, alignment and errors as decode_attention_qkv (the merge checks
+ * cache, ws, ws_bytes and out). */
 int decode_attention_qkv_partial(const uint16_t* q, const dqa_kivi_cache* cache,
                                  float sm_scale, void* ws, size_t ws_bytes,
                                  float* out, void* stream);
@@ -304,8 +317,9 @@ int zoned_pack(const int32_t* plan_host, const int32_t* plan_dev,
                const uint16_t* k, const uint16_t* v, const uint16_t* k_new,
                const uint16_t* v_new, void* blob, void* stream);
 
-/* Workspace bytes for decode_attention_zoned (0 if invalid; at least 256
- * otherwise): partial softmax states, no initialization needed. */
+/* Workspace bytes for decode_attention_zoned (0 if invalid; at least 64 KB
+ * otherwise): merge counters and partial softmax states; zero it before its
+ * first use (see the preamble). */
 size_t decode_attention_zoned_workspace_bytes(const int32_t* plan_host, int Hq);
 
 /* Decode attention over zones A (kept tokens, masked slots skipped), B and
@@ -315,7 +329,8 @@ size_t decode_attention_zoned_workspace_bytes(const int32_t* plan_host, int Hq);
  *   blob (device) as written by zoned_pack
  *   out (device) fp32 [B][Hq][d]
  * blob, ws and out must be 16-byte aligned (DQA_ERR_ALIGN).
- * Enqueues the split kernel and, with several splits, their merge.
+ * Enqueues the split kernel (the last split of each (batch, KV head) to
+ * finish merges the splits in split order).
  * Errors: DQA_ERR_NULL, DQA_ERR_PLAN, DQA_ERR_SHAPE, DQA_ERR_WORKSPACE,
  * DQA_ERR_ALIGN, DQA_ERR_UNSUPPORTED, DQA_ERR_HIP. */
 int decode_attention_zoned(const uint16_t* q, int Hq, const int32_t* plan_host,
@@ -349,9 +364,9 @@ int rvq_encode(const uint16_t* x, int64_t n, int d, const uint16_t* codebooks,
                int N, int Kc, int16_t* idx, void* ws, size_t ws_bytes,
                void* stream);
 
-/* Workspace bytes for rvq_decode_attention (0 if invalid): partial softmax
- * states, then room for the key-logit table, 64 KB per (batch, KV head); no
- * initialization needed. */
+/* Workspace bytes for rvq_decode_attention (0 if invalid): merge counters
+ * and partial softmax states, then room for the key-logit table, 64 KB per
+ * (batch, KV head); zero it before its first use (see the preamble). */
 size_t rvq_decode_attention_workspace_bytes(int B, int Hq, int Hkv, int T, int d);
 
 /* Decode attention with keys and values rebuilt on the fly from their
@@ -366,8 +381,9 @@ size_t rvq_decode_attention_workspace_bytes(int B, int Hq, int Hkv, int T, int d
  * staged in LDS, so each key costs N lookups instead of N gathered
  * codewords (one extra small kernel enqueued first); otherwise keys are
  * rebuilt like values.
- * Enqueues the table kernel (when used), the split kernel and, with several
- * splits, their merge.
+ * Enqueues the table kernel (when used) and the split kernel (the last
+ * split of each (batch, KV head) to finish merges the splits in split
+ * order).
  * Errors: DQA_ERR_NULL, DQA_ERR_SHAPE, DQA_ERR_ALIGN, DQA_ERR_WORKSPACE,
  * DQA_ERR_UNSUPPORTED, DQA_ERR_HIP. */
 int rvq_decode_attention(const uint16_t* q, int B, int Hq, int Hkv, int T,

@@ -76,11 +76,16 @@ def _cache(**kw):
 
 def test_decode_workspace_query_and_validation():
     ws = lib.decode_attention_workspace_bytes(ctypes.byref(_cache()))
+    # merge counters first: one uint32 per (batch, KV head), at least 16384
+    counters = 16384 * 4
     # 3 tiles per (batch, KV head): a single split, no partial states
-    assert ws == 256
+    assert ws == counters
     # 128 + 1 tiles over 4 units: 33 splits of partial states [m, l, o[d]] per head
     big = lib.decode_attention_workspace_bytes(ctypes.byref(_cache(T_q=4096)))
-    assert big == 4 * 33 * 4 * (128 + 2) * 4
+    assert big == counters + 4 * 33 * 4 * (128 + 2) * 4
+    # more than 16384 units: one counter each, rounded up to 256 bytes
+    many = lib.decode_attention_workspace_bytes(ctypes.byref(_cache(B=5000, Hkv=4, Hq=16)))
+    assert many == (5000 * 4 * 4 + 255) // 256 * 256
     for bad, code in [(dict(d=96), 2), (dict(bits=3), 3), (dict(T_q=40), 2), (dict(R=129), 2),
                       (dict(Hq=6, Hkv=4), 2), (dict(Hq=24, Hkv=2), 5), (dict(Hq=16, Hkv=2), 5),
                       (dict(k_codes=None), 1), (dict(k_recent=None), 1)]:
@@ -313,7 +318,7 @@ def test_rvq_validation_and_workspace():
 
 def test_kivi_append_validation():
     """Argument checks of the streaming append (all fail before any launch)."""
-    assert lib.dqa_abi_version() == 9
+    assert lib.dqa_abi_version() == 10
     c = _cache(T_cap=128, R_cap=128)
     # staging holds the recent and the new rows of K and V
     assert lib.kivi_append_workspace_bytes(ctypes.byref(c), 20) == 2 * 2 * 2 * (16 + 20) * 128 * 2

@@ -188,6 +188,31 @@ def test_decode_two_phase_equals_one_call(dqa, T_q, R):
     assert np.array_equal(host(out), ref)
 
 
+def test_merge_counters_reset_and_shared_workspace(dqa):
+    """The workgroup that finishes a (batch, KV head) last merges its splits
+    and sets the unit's counter back to zero: after every call the counter
+    area is zero again, and one workspace serves caches of different shapes
+    (different unit counts and split counts) in turn."""
+    cases = [(2, 8, 2, 128, 4096, 40, 2, 500000.0), (1, 4, 1, 128, 8192, 0, 4, 10000.0),
+             (3, 8, 4, 64, 2048, 100, 2, 0.0), (2, 8, 2, 128, 4096, 40, 2, 500000.0)]
+    caches = []
+    for case in cases:
+        B, Hq, Hkv, d, T_q, R, bits, rope = case
+        inp = kivi_inputs(B, Hq, Hkv, d, T_q, R, seed=T_q + R, outliers=("lognormal", 0.04, 3.0, 1.0))
+        caches.append((case, inp, gpu_cache(dqa, inp, bits, Hq, rope)))
+    n = max(c.workspace_bytes() for _, _, c in caches)
+    ws = torch.zeros(n, dtype=torch.uint8, device="cuda:0")
+    for case, inp, cache in caches:
+        B, Hq, Hkv, d, T_q, R, bits, rope = case
+        say("decode on a shared workspace", case)
+        scale = 1.0 / math.sqrt(d)
+        out = host(dqa.decode_attention_qkv(dev(inp["q"]), cache, scale, workspace=ws))
+        counters = host(ws[:16384 * 4]).view(np.uint32)
+        assert not counters.any(), np.nonzero(counters)
+        ref = oracle.kivi_decode_attention(inp["q"], oracle_cache(inp, bits, Hq, rope), scale)
+        check_attention(out, ref, TOL, f"shared workspace {case}")
+
+
 @pytest.mark.parametrize("name,bits", [("llama3.1-8b-gqa-32k", 2), ("llama3.1-8b-gqa-32k", 4), ("llama2-13b-decode-layer", 2), ("tiny-kivi", 2)])
 def test_decode_full_config_every_unit(dqa, name, bits):
     """Full-size decode in the launch configuration the bench times; the

@@ -204,7 +204,7 @@ def test_append_capacity_zero_keeps_row_stride(dqa):
     qd = dev(q)
     out = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda:0")
     nws = dqa.lib.decode_attention_workspace_bytes(ctypes.byref(c))
-    dws = torch.empty(nws, dtype=torch.uint8, device="cuda:0")
+    dws = torch.zeros(nws, dtype=torch.uint8, device="cuda:0")
     assert dqa.lib.decode_attention_qkv(dqa._ptr(qd), ctypes.byref(c), ctypes.c_float(scale), dqa._ptr(dws),
                                         nws, dqa._ptr(out), dqa._stream(qd.device)) == 0
     torch.cuda.synchronize()
