@@ -43,6 +43,37 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float float4v __attribute__((ext_vector_type(4)));
 
+// The tiles of one wave.  The n_q quantized tiles (one work unit each) and
+// n_r fp16 recent tiles (W units each: their set-up costs more) of a (batch,
+// KV head) lie on a line of n_q + W n_r units: recent tile r takes the W
+// units centred in the r-th of n_r equal segments, the quantized tiles fill
+// the other units in order.  The line is cut evenly over the nw waves of the
+// (batch, KV head); wave gw takes the quantized tiles whose units fall in
+// its cut [u0, u1) -- a contiguous run [qb, qb + nq) -- and the recent tiles
+// whose first unit does (r_mine of them from r_first).
+struct WaveTiles {
+  int qb, nq, r_first, r_mine;
+};
+__device__ __forceinline__ WaveTiles wave_tiles(int n_q, int n_r, int W, long long nw, long long gw) {
+  const long long total = n_q + static_cast<long long>(W) * n_r;
+  const long long u0 = gw * total / nw, u1 = (gw + 1) * total / nw;
+  long long before0 = 0, before1 = 0;   // recent units below u0 and below u1
+  WaveTiles t{0, 0, 0, 0};
+  for (int r = 0; r < n_r; ++r) {
+    const long long lo = r * total / n_r, hi = (r + 1) * total / n_r;
+    const long long start = lo + (hi - lo - W) / 2;
+    before0 += min(max(u0 - start, 0LL), static_cast<long long>(W));
+    before1 += min(max(u1 - start, 0LL), static_cast<long long>(W));
+    if (start >= u0 && start < u1) {
+      if (t.r_mine == 0) t.r_first = r;
+      ++t.r_mine;
+    }
+  }
+  t.qb = static_cast<int>(u0 - before0);
+  t.nq = static_cast<int>((u1 - before1) - (u0 - before0));
+  return t;
+}
+
 // Accurate unit complex number e^{i * pos * omega}: the angle is formed and
 // reduced modulo 2*pi in fp64, then sin/cos are taken in fp32 on [-pi, pi].
 __device__ __forceinline__ void rope_unit(double pos, double omega, float& c, float& s) {

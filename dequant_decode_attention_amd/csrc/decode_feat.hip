@@ -58,6 +58,9 @@ namespace {
 
 constexpr int kFWaves = 4;          // waves per workgroup
 constexpr int kFWavesPerSimd = 2;   // resident waves per SIMD (register budget 256)
+// work units of an fp16 recent tile in the split of tiles over waves (its
+// query rotation and fp32 key rotation cost about two more quantized tiles)
+constexpr int kRecentWeight = 3;
 
 // ---------------------------------------------------------------- helpers
 
@@ -195,6 +198,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kFWavesPerS
   constexpr int VBLK = 4 * D * BITS;     // value bytes per 32-token block
   constexpr int VST = 24;                // row stride of the fp16 value staging area (halves)
   constexpr int KSR = D / 32;            // K-steps of a recent tile (channels)
+  constexpr int TPR = NP + 4;            // packed trig row (padded: 16 rows start in different banks)
   constexpr float kTrigScale = 32768.0f; // 2^15
   static_assert(NCOL <= 16, "value-operand columns");
   static_assert(NITEM <= kWave, "one factor item per lane");
@@ -202,57 +206,45 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kFWavesPerS
   static_assert(HPW % 2 == 0 && KSC % 2 == 0, "K-step pairs share a word");
   static_assert(operand_order_is_permutation<EPW, PPG>(), "trig operand order");
 
-  // fp32 (cos, sin) of j * w_i, j = 0..32, i < NP (the whole workgroup's
-  // table; row 32 steps the query from one tile start to the next)
-  __shared__ __attribute__((aligned(16))) float2 lds_trig[kGroup + 1][NP];
-  // per-tile factors (B operand), per wave: [column][K]
-  __shared__ __attribute__((aligned(16))) _Float16 lds_B[kFWaves][NBC][BST];
-  __shared__ __attribute__((aligned(16))) _Float16 lds_vsz[kFWaves][2][NVG][kGroup];
-  // a tile's key scales (row 0) and zeros (row 1)
-  __shared__ __attribute__((aligned(16))) _Float16 lds_ksz[kFWaves][2][D];
-  __shared__ __attribute__((aligned(16))) _Float16 lds_vst[kFWaves][kGroup * VST];
-  __shared__ float lds_m[kFWaves][G], lds_l[kFWaves][G];
-  // set-up area: the trig heads and tails as packed fp16 (cos, sin) pairs
-  // (times 2^15) of j = 0..31 and the unit numbers e^{i t0 w} of every
-  // wave's first quantized tile start t0; afterwards the waves' output rows
-  // (rows padded by 16 bytes: the 16 tokens one instruction reads start in
-  // different banks)
-  constexpr int TPR = NP + 4;
+  // ---- LDS.  Per wave, two slots (tiles t and t + 1) of: the B operand
+  // [column][K], the key scales and zeros [scale/zero][channel], the value
+  // scales and zeros [scale/zero][group][token].  During the set-up the B
+  // area holds the trig bases and the packed trig table instead.
+  constexpr int kBBytes = kFWaves * 2 * NBC * BST * 2;
+  constexpr int kBaseBytes = 11 * NP * 8;
   constexpr int kTrigPackBytes = 2 * kGroup * TPR * 4;
-  constexpr int kSetupBytes = kTrigPackBytes + kFWaves * NP * 8;
+  constexpr int kBigBytes = kBBytes > kBaseBytes + kTrigPackBytes ? kBBytes : kBaseBytes + kTrigPackBytes;
+  __shared__ __attribute__((aligned(16))) uint8_t lds_big[kBigBytes];
+  __shared__ __attribute__((aligned(16))) _Float16 lds_ksz[kFWaves][2][2][D];
+  __shared__ __attribute__((aligned(16))) _Float16 lds_vsz[kFWaves][2][2][NVG][kGroup];
+  __shared__ float2 lds_step[NP];        // e^{i 32 w}: one tile start to the next
+  __shared__ float lds_m[kFWaves][G], lds_l[kFWaves][G];
+  // per wave: the output rows (after the tiles), the recent tiles' value
+  // staging, and a rotation per pair (the first quantized tile's start during
+  // the set-up, a recent tile's start later)
   constexpr int kOutBytes = kFWaves * G * D * 4;
-  __shared__ __attribute__((aligned(16))) uint8_t lds_setup[kSetupBytes > kOutBytes ? kSetupBytes : kOutBytes];
-  uint32_t (*const lds_th)[TPR] = reinterpret_cast<uint32_t (*)[TPR]>(lds_setup);
-  uint32_t (*const lds_tl)[TPR] = reinterpret_cast<uint32_t (*)[TPR]>(lds_setup + kTrigPackBytes / 2);
-  float2 (*const lds_rot)[NP] = reinterpret_cast<float2 (*)[NP]>(lds_setup + kTrigPackBytes);
-  float (*const lds_o)[G][D] = reinterpret_cast<float (*)[G][D]>(lds_setup);
+  constexpr int kVstBytes = kFWaves * kGroup * VST * 2;
+  constexpr int kRotBytes = kFWaves * NP * 8;
+  __shared__ __attribute__((aligned(16))) uint8_t lds_aux[kOutBytes + kVstBytes + kRotBytes];
+  float2 (*const base)[NP] = reinterpret_cast<float2 (*)[NP]>(lds_big);
+  uint32_t (*const lds_th)[TPR] = reinterpret_cast<uint32_t (*)[TPR]>(lds_big + kBaseBytes);
+  uint32_t (*const lds_tl)[TPR] = reinterpret_cast<uint32_t (*)[TPR]>(lds_big + kBaseBytes + kTrigPackBytes / 2);
+  float2 (*const lds_rot)[NP] = reinterpret_cast<float2 (*)[NP]>(lds_aux + kOutBytes + kVstBytes);
+  float (*const lds_o)[G][D] = reinterpret_cast<float (*)[G][D]>(lds_aux);
+  _Float16 (*const lds_vst)[kGroup * VST] = reinterpret_cast<_Float16 (*)[kGroup * VST]>(lds_aux + kOutBytes);
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int col = lane & 15, grp = lane >> 4;
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const size_t unit = static_cast<size_t>(b) * a.Hkv + kvh;
+  _Float16 (*const lds_B)[NBC][BST] = reinterpret_cast<_Float16 (*)[NBC][BST]>(lds_big) + 2 * wave;
 
-  // The wave's tiles: the (batch, KV head)'s n_q quantized and n_r recent
-  // tiles form n_q + n_r slots cut evenly over all its waves (contiguous
-  // runs [u0, u1)); recent tile r sits at slot floor((2r + 1)(n_q + n_r) /
-  // (2 n_r)), so recent tiles land in different waves.  A wave attends its
-  // recent tiles first, then its run [qb, qe) of quantized tiles.
-  const int n_tiles = a.n_qtiles + a.n_rtiles;
-  const long long nw = static_cast<long long>(a.total_splits) * kFWaves;
-  const long long gw = static_cast<long long>(split) * kFWaves + wave;
-  const int u0 = static_cast<int>(gw * n_tiles / nw);
-  const int u1 = static_cast<int>((gw + 1) * n_tiles / nw);
-  int r_before = 0, r_mine = 0, r_first = 0;
-  for (int r = 0; r < a.n_rtiles; ++r) {
-    const int slot = static_cast<int>((2LL * r + 1) * n_tiles / (2LL * a.n_rtiles));
-    if (slot < u0) ++r_before;
-    else if (slot < u1) {
-      if (r_mine == 0) r_first = r;
-      ++r_mine;
-    }
-  }
-  const int qb = u0 - r_before;
-  const int qe = u1 - r_before - r_mine;
+  // The wave's tiles (a recent tile weighs kRecentWeight quantized tiles):
+  // its recent tiles first, then its run [qb, qb + nq) of quantized tiles.
+  const WaveTiles wt = wave_tiles(a.n_qtiles, a.n_rtiles, kRecentWeight,
+                                  static_cast<long long>(a.total_splits) * kFWaves,
+                                  static_cast<long long>(split) * kFWaves + wave);
+  const int qb = wt.qb, nq = wt.nq, r_first = wt.r_first, r_mine = wt.r_mine;
 
   // ---- per-tile factor item of this lane: head ih, lane group ig, K-step
   // pair ikb (code K-steps 2 ikb, 2 ikb + 1; zero-point K-step ikb).  Its four
@@ -276,8 +268,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kFWavesPerS
       qraw[k] = *reinterpret_cast<const uint32_t*>(qh + ich + 2 * (k & 1) + EPW * (k >> 1));
   }
 
-  // ---- tile inputs.  The first quantized tile's loads are issued before
-  // the set-up below, so their latency overlaps it.
+  // ---- tile inputs: codes one tile ahead, scales two tiles ahead.  The
+  // first loads are issued before the set-up below, so their latency
+  // overlaps it.
   const size_t qstride = static_cast<size_t>(a.qtile_stride);
   const uint16_t* const ksz_s = uniform_ptr(a.k_scale);
   const uint16_t* const ksz_z = uniform_ptr(a.k_zero);
@@ -285,15 +278,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kFWavesPerS
   const uint16_t* const vsz_z = uniform_ptr(a.v_zero);
   const uint8_t* const kbase = reinterpret_cast<const uint8_t*>(a.k_codes) + unit * qstride * kGroup * KROW;
   const uint8_t* const vbase = reinterpret_cast<const uint8_t*>(a.v_codes) + unit * qstride * VBLK;
-  // value-scale factor of this lane's staging token (lanes 0..31: scales)
-  const uint32_t vfac = (lane < 32 && feat_vlow<BITS>(lane & 31)) ? 0x44004400u : 0x3C003C00u;  // (4, 4) or (1, 1)
-  struct TileIn {
+  struct Codes {
     uint32_t k[2][NW];      // the lane's key words of its two tokens
     uint32_t v[MB];         // value chunks (2-bit: 16 bits used)
+  };
+  struct Scales {
     uint32_t ksz[D / 64];   // lanes 0..31: key scales of D / 32 channels; 32..63: zeros
     uint32_t vsz[NVG / 2];  // lanes 0..31: value scales of token lane; 32..63: zeros
   };
-  auto load_tile = [&](int ti, TileIn& t) {
+  auto load_codes = [&](int ti, Codes& t) {
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const uint8_t* p = kbase + (static_cast<size_t>(ti) * kGroup + row_token(s, col)) * KROW + grp * LROW;
@@ -308,56 +301,54 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kFWavesPerS
       if constexpr (BITS == 2) t.v[mb] = *reinterpret_cast<const uint16_t*>(p);
       else t.v[mb] = *reinterpret_cast<const uint32_t*>(p);
     }
+  };
+  auto load_scales = [&](int ti, Scales& t) {
     const int half = lane >> 5, r = lane & 31;
-    {
-      const Words<D / 16> kw = load_words<D / 16>((half ? ksz_z : ksz_s) + (unit * qstride + ti) * D + r * (D / 32));
+    const Words<D / 16> kw = load_words<D / 16>((half ? ksz_z : ksz_s) + (unit * qstride + ti) * D + r * (D / 32));
 #pragma unroll
-      for (int i = 0; i < D / 64; ++i) t.ksz[i] = kw.w[i];
-    }
+    for (int i = 0; i < D / 64; ++i) t.ksz[i] = kw.w[i];
     const uint16_t* vsrc = (half ? vsz_z : vsz_s) + ((unit * qstride + ti) * kGroup + r) * NVG;
     const Words<2 * NVG> vw = load_words<2 * NVG>(vsrc);
 #pragma unroll
     for (int i = 0; i < NVG / 2; ++i) t.vsz[i] = vw.w[i];
   };
-
-  TileIn buf0, buf1;
-  if (qb < qe) load_tile(qb, buf0);
+  Codes c0, c1;
+  Scales s0, s1;
+  if (nq > 0) {
+    load_codes(qb, c0);
+    load_scales(qb, s0);
+  }
+  if (nq > 1) load_scales(qb + 1, s1);
 
   // ---- trig tables.  e^{i j w} for j = 4a + b is the product of two of 11
   // accurately rounded unit numbers (angle 4a w, a = 1..8, and b w, b =
-  // 1..3: angle reduced in fp64, sin/cos in fp32), staged in the B area; the
-  // same pass computes e^{i t0 w} of this wave's first quantized tile.
-  {
-    float2 (*const base)[NP] = reinterpret_cast<float2 (*)[NP]>(&lds_B[0][0][0]);
-    static_assert(sizeof(lds_B) >= 11 * NP * sizeof(float2), "trig bases fit the B area");
-    for (int e = tid; e < 11 * NP; e += 256) {
-      const int r = e / NP, i = e % NP;
-      float c, s;
-      rope_unit(static_cast<double>(r < 8 ? 4 * (r + 1) : r - 7), a.omega[i], c, s);
-      base[r][i] = float2{c, s};
-    }
-    if (lane < NP) {
-      float c, s;
-      rope_unit(static_cast<double>(qb) * kGroup, a.omega[lane], c, s);
-      lds_rot[wave][lane] = float2{c, s};
-    }
-    __syncthreads();
-    for (int e = tid; e < (kGroup + 1) * NP; e += 256) {
-      const int j = e / NP, i = e % NP;
-      const int ja = j >> 2, jb = j & 3;
-      const float2 u = ja ? base[ja - 1][i] : float2{1.0f, 0.0f};
-      const float2 v = jb ? base[7 + jb][i] : float2{1.0f, 0.0f};
-      const float c = fmaf(u.x, v.x, -(u.y * v.y)), s = fmaf(u.y, v.x, u.x * v.y);
-      lds_trig[j][i] = float2{c, s};
-      if (j < kGroup) {
-        const float ch = trunc_sig(c, HB), sh = trunc_sig(s, HB);
-        const int ps = (i / PPG) * PPG + pos_of<EPW>(i % PPG);
-        lds_th[j][ps] = pack_f16(ch * kTrigScale, sh * kTrigScale);
-        lds_tl[j][ps] = pack_f16((c - ch) * kTrigScale, (s - sh) * kTrigScale);
-      }
-    }
-    __syncthreads();
+  // 1..3: angle reduced in fp64, sin/cos in fp32); the same pass computes
+  // e^{i t0 w} of this wave's first quantized tile.
+  for (int e = tid; e < 11 * NP; e += 256) {
+    const int r = e / NP, i = e % NP;
+    float c, s;
+    rope_unit(static_cast<double>(r < 8 ? 4 * (r + 1) : r - 7), a.omega[i], c, s);
+    base[r][i] = float2{c, s};
   }
+  if (lane < NP) {
+    float c, s;
+    rope_unit(static_cast<double>(qb) * kGroup, a.omega[lane], c, s);
+    lds_rot[wave][lane] = float2{c, s};
+  }
+  __syncthreads();
+  for (int e = tid; e < kGroup * NP; e += 256) {
+    const int j = e / NP, i = e % NP;
+    const int ja = j >> 2, jb = j & 3;
+    const float2 u = ja ? base[ja - 1][i] : float2{1.0f, 0.0f};
+    const float2 v = jb ? base[7 + jb][i] : float2{1.0f, 0.0f};
+    const float c = fmaf(u.x, v.x, -(u.y * v.y)), s = fmaf(u.y, v.x, u.x * v.y);
+    const float ch = trunc_sig(c, HB), sh = trunc_sig(s, HB);
+    const int ps = (i / PPG) * PPG + pos_of<EPW>(i % PPG);
+    lds_th[j][ps] = pack_f16(ch * kTrigScale, sh * kTrigScale);
+    lds_tl[j][ps] = pack_f16((c - ch) * kTrigScale, (s - sh) * kTrigScale);
+  }
+  if (tid < NP) lds_step[tid] = base[7][tid];
+  __syncthreads();
 
   // ---- the lane's trig registers: tokens j(s) (rows of the A operand of
   // half s), pairs grp * PPG + pair_at(pos); head (HB significant bits) and
@@ -388,10 +379,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kFWavesPerS
       iq[k][1] = x1 * r.x - x0 * r.y;
     }
   }
-  // the set-up area is the output area from here on
+  // the set-up areas are free from here on
   __syncthreads();
-
-  _Float16* const Bw = &lds_B[wave][0][0];
 
   float4v acc[MB];
 #pragma unroll
@@ -437,16 +426,152 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kFWavesPerS
     lsum += ps;
   };
 
-  // ------------------------------------------------------- quantized tile
-  // per-tile factors of the item -> B (hi in column ih, lo in G + ih)
-  auto write_factors = [&]() {
+  // ------------------------------------------------------ fp16 recent tile
+  // Keys rotated in fp32 with the trig registers (head + tail), split into
+  // fp16 hi + lo, against the query rotated to the tile start.
+  const uint16_t* const krb = a.k_recent + unit * a.R_cap * D;
+  const uint16_t* const vrb = a.v_recent + unit * a.R_cap * D;
+  auto recent_tile = [&](int rt) {
+    const int r0 = rt * kGroup;
+    const double t0 = static_cast<double>(a.n_qtiles + rt) * kGroup;
+    _Float16* const Bw = &lds_B[0][0][0];
+    // keys: the lane's 8 channels of K-step ks for its two tokens (the
+    // value slabs are loaded after the key products, when these are dead)
+    uint4 kin[2][KSR];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int r = r0 + row_token(s, col);
+#pragma unroll
+      for (int ks = 0; ks < KSR; ++ks) {
+        kin[s][ks] = uint4{0u, 0u, 0u, 0u};
+        if (r < a.R)
+          kin[s][ks] = *reinterpret_cast<const uint4*>(krb + static_cast<size_t>(r) * D + 2 * PPG * grp + 8 * ks);
+      }
+    }
+    // e^{i t0 w} once per pair, shared through LDS
+    if (lane < NP) {
+      float c, s;
+      rope_unit(t0, a.omega[lane], c, s);
+      lds_rot[wave][lane] = float2{c, s};
+    }
+    wave_sync();
+    // B: the query rotated to t0 (no 2^5), K = the lane group's channels in
+    // order: item (head, lane group, K-step) of this lane writes 8 channels
+    if (lane < G * 4 * KSR) {
+      const int h = lane / (4 * KSR), g = (lane / KSR) % 4, ks = lane % KSR;
+      const int c0 = 2 * PPG * g + 8 * ks;
+      const uint16_t* qh = a.q + (static_cast<size_t>(b) * a.Hq + kvh * G + h) * D + c0;
+      const uint4 qw = *reinterpret_cast<const uint4*>(qh);
+      const uint32_t qq[4] = {qw.x, qw.y, qw.z, qw.w};
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float x0 = h2f(static_cast<uint16_t>(qq[i] & 0xFFFFu)) * a.q_scale;
+        const float x1 = h2f(static_cast<uint16_t>(qq[i] >> 16)) * a.q_scale;
+        const float2 r = lds_rot[wave][c0 / 2 + i];
+        split2(x0 * r.x + x1 * r.y, x1 * r.x - x0 * r.y, hi[i], lo[i]);
+      }
+      const int K = 32 * ks + 8 * g;
+      *reinterpret_cast<uint4*>(Bw + h * BST + K) = uint4{hi[0], hi[1], hi[2], hi[3]};
+      *reinterpret_cast<uint4*>(Bw + (G + h) * BST + K) = uint4{lo[0], lo[1], lo[2], lo[3]};
+    }
+    wave_sync();
+    float4v sacc[2] = {float4v{0.0f, 0.0f, 0.0f, 0.0f}, float4v{0.0f, 0.0f, 0.0f, 0.0f}};
+#pragma unroll
+    for (int ks = 0; ks < KSR; ++ks) {
+      const half8 bv = *reinterpret_cast<const half8*>(Bw + bcol * BST + 32 * ks + 8 * grp);
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const uint32_t w[4] = {kin[s][ks].x, kin[s][ks].y, kin[s][ks].z, kin[s][ks].w};
+        uint32_t ah[4], al[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const half2v th = __builtin_bit_cast(half2v, trig_h(s, 4 * ks + i));
+          const half2v tl = __builtin_bit_cast(half2v, trig_l(s, 4 * ks + i));
+          const float cs = (static_cast<float>(th[0]) + static_cast<float>(tl[0])) * (1.0f / kTrigScale);
+          const float sn = (static_cast<float>(th[1]) + static_cast<float>(tl[1])) * (1.0f / kTrigScale);
+          const float x0 = h2f(static_cast<uint16_t>(w[i] & 0xFFFFu));
+          const float x1 = h2f(static_cast<uint16_t>(w[i] >> 16));
+          split2(x0 * cs - x1 * sn, x0 * sn + x1 * cs, ah[i], al[i]);
+        }
+        sacc[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, ah), bv, sacc[s], 0, 0, 0);
+        sacc[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, al), bv, sacc[s], 0, 0, 0);
+      }
+    }
+    // value slabs: token lane / 2, 8 channels of block mb
+    uint4 vin[MB];
+    {
+      const int r = r0 + (lane >> 1);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        vin[mb] = uint4{0u, 0u, 0u, 0u};
+        if (r < a.R) vin[mb] = *reinterpret_cast<const uint4*>(vrb + static_cast<size_t>(r) * D + 16 * mb + 8 * (lane & 1));
+      }
+    }
+    float lg[8], p[8];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      lg[2 * r] = combine_cols(sacc[0][r]);
+      lg[2 * r + 1] = combine_cols(sacc[1][r]);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (r0 + 8 * grp + vtok(e) >= a.R) lg[e] = -INFINITY;
+    softmax_step(lg, p, std::true_type{});
+    half8 bv;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) bv[e] = static_cast<_Float16>(col < NCOL ? p[e] : 0.0f);
+    // values pass through LDS 16 channels at a time to form the
+    // channel-major operand
+    _Float16* const st = lds_vst[wave];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      *reinterpret_cast<uint4*>(&st[(lane >> 1) * VST + 8 * (lane & 1)]) = vin[mb];
+      wave_sync();
+      half8 av;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) av[e] = st[(8 * grp + vtok(e)) * VST + col];
+      wave_sync();
+      acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, acc[mb], 0, 0, 0);
+    }
+    wave_sync();
+  };
+
+  // ------------------------------------------------------- quantized tiles
+  // value-scale factor of this lane's staging token (lanes 0..31: scales)
+  const uint32_t vfac = (lane < 32 && feat_vlow<BITS>(lane & 31)) ? 0x44004400u : 0x3C003C00u;  // (4, 4) or (1, 1)
+  // a tile's key scales and zeros into slot sl (lanes 0..31 scales, 32..63 zeros)
+  auto stage_ksz = [&](const Scales& t, int sl) {
+    const int half = lane >> 5, r = lane & 31;
+    if constexpr (D / 64 == 2)
+      *reinterpret_cast<uint2*>(&lds_ksz[wave][sl][half][r * (D / 32)]) = uint2{t.ksz[0], t.ksz[1]};
+    else
+      *reinterpret_cast<uint32_t*>(&lds_ksz[wave][sl][half][r * (D / 32)]) = t.ksz[0];
+  };
+  // a tile's value scales (times the position factor) and zeros into slot sl
+  auto stage_vsz = [&](const Scales& t, int sl) {
+    const int half = lane >> 5, r = lane & 31;
+#pragma unroll
+    for (int i = 0; i < NVG / 2; ++i) {
+      uint32_t w;
+      asm("v_pk_mul_f16 %0, %1, %2" : "=v"(w) : "v"(t.vsz[i]), "v"(vfac));
+      lds_vsz[wave][sl][half][2 * i][r] = __builtin_bit_cast(_Float16, static_cast<uint16_t>(w & 0xFFFFu));
+      lds_vsz[wave][sl][half][2 * i + 1][r] = __builtin_bit_cast(_Float16, static_cast<uint16_t>(w >> 16));
+    }
+  };
+
+  // the per-tile factors of the item from the key scales and zeros in slot
+  // sl -> B of slot sl (hi in column ih, lo in G + ih); then the query steps
+  // to the next tile's start
+  auto write_factors = [&](int sl) {
     if (!item) return;
+    _Float16* const Bw = &lds_B[sl][0][0];
     // scales and zeros of channels (cA, cA+1, cA+2, cA+3) and (cA+EPW, ...)
     float sv[2][4], zv[2][4];
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      const uint2 sw = *reinterpret_cast<const uint2*>(&lds_ksz[wave][0][ich + c * EPW]);
-      const uint2 zw = *reinterpret_cast<const uint2*>(&lds_ksz[wave][1][ich + c * EPW]);
+      const uint2 sw = *reinterpret_cast<const uint2*>(&lds_ksz[wave][sl][0][ich + c * EPW]);
+      const uint2 zw = *reinterpret_cast<const uint2*>(&lds_ksz[wave][sl][1][ich + c * EPW]);
       const uint32_t sww[2] = {sw.x, sw.y}, zww[2] = {zw.x, zw.y};
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -496,48 +621,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kFWavesPerS
     // the query to the next tile's start: q' <- R(-32 w) q'
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const float2 st = lds_trig[kGroup][(ich + 2 * (k & 1) + EPW * (k >> 1)) / 2];
+      const float2 st = lds_step[(ich + 2 * (k & 1) + EPW * (k >> 1)) / 2];
       const float x0 = iq[k][0], x1 = iq[k][1];
       iq[k][0] = x0 * st.x + x1 * st.y;
       iq[k][1] = x1 * st.x - x0 * st.y;
     }
   };
 
-  auto quantized_tile = [&](int ti, const TileIn& cur, TileIn& nxt, bool prefetch) {
-    // value scales and zeros through LDS (scales times the position factor)
-    {
-      const int half = lane >> 5, r = lane & 31;
-#pragma unroll
-      for (int i = 0; i < NVG / 2; ++i) {
-        uint32_t w;
-        asm("v_pk_mul_f16 %0, %1, %2" : "=v"(w) : "v"(cur.vsz[i]), "v"(vfac));
-        lds_vsz[wave][half][2 * i][r] = __builtin_bit_cast(_Float16, static_cast<uint16_t>(w & 0xFFFFu));
-        lds_vsz[wave][half][2 * i + 1][r] = __builtin_bit_cast(_Float16, static_cast<uint16_t>(w >> 16));
-      }
-      if constexpr (D / 64 == 2)
-        *reinterpret_cast<uint2*>(&lds_ksz[wave][half][r * (D / 32)]) = uint2{cur.ksz[0], cur.ksz[1]};
-      else
-        *reinterpret_cast<uint32_t*>(&lds_ksz[wave][half][r * (D / 32)]) = cur.ksz[0];
-    }
+  // Tile i of the run (slot sl = i & 1): its B, value scales and the next
+  // tile's key scales are in LDS.  The logits of tile i run together with
+  // the factors of tile i + 1 (other slot); at the end the next tile's value
+  // scales and the key scales of tile i + 2 are staged.  `cur` holds tile
+  // i's codes, `nxt` receives tile i + 1's; `sn1` holds the scales of tile
+  // i + 1, `sn2` those of tile i + 2, and then receives tile i + 3's.
+  auto quantized_tile = [&](int i, int sl, const Codes& cur, Codes& nxt, Scales& sn1, Scales& sn2) {
     wave_sync();
-    write_factors();
-    if (prefetch) load_tile(ti + 1, nxt);
-    wave_sync();
+    // (past the run's end the last tile is loaded again, unused: no branch)
+    load_codes(qb + min(i + 1, nq - 1), nxt);
+    const _Float16* const Bw = &lds_B[sl][0][0];
 
-    // logits: zero-point K-steps first (their partial sums carry 2^20), then
-    // the code K-steps
-    float4v sacc[2] = {float4v{0.0f, 0.0f, 0.0f, 0.0f}, float4v{0.0f, 0.0f, 0.0f, 0.0f}};
+    // logits: zero-point K-steps (their sums carry 2^20) and code K-steps in
+    // separate accumulators
+    float4v zs[2] = {float4v{0.0f, 0.0f, 0.0f, 0.0f}, float4v{0.0f, 0.0f, 0.0f, 0.0f}};
+    float4v cs[2] = {float4v{0.0f, 0.0f, 0.0f, 0.0f}, float4v{0.0f, 0.0f, 0.0f, 0.0f}};
 #pragma unroll
     for (int kb = 0; kb < KSB; ++kb) {
       const half8 bv = *reinterpret_cast<const half8*>(Bw + bcol * BST + 32 * (KSC + kb) + 8 * grp);
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        sacc[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, tqh[s][kb]), bv, sacc[s], 0, 0, 0);
-        sacc[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, tql[s][kb]), bv, sacc[s], 0, 0, 0);
+        zs[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, tqh[s][kb]), bv, zs[s], 0, 0, 0);
+        zs[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, tql[s][kb]), bv, zs[s], 0, 0, 0);
       }
     }
-#pragma unroll
-    for (int s = 0; s < 2; ++s) sacc[s] *= 1.0f / 1048576.0f;   // 2^-20
 #pragma unroll
     for (int ks = 0; ks < KSC; ++ks) {
       const half8 bv = *reinterpret_cast<const half8*>(Bw + bcol * BST + 32 * ks + 8 * grp);
@@ -556,22 +671,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kFWavesPerS
         al[1] = pk_mul_bcast<0>(cb, trig_l(s, pa));
         al[2] = pk_mul_bcast<1>(ca, trig_l(s, pb));
         al[3] = pk_mul_bcast<1>(cb, trig_l(s, pb));
-        sacc[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, ah), bv, sacc[s], 0, 0, 0);
-        sacc[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, al), bv, sacc[s], 0, 0, 0);
+        cs[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, ah), bv, cs[s], 0, 0, 0);
+        cs[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, al), bv, cs[s], 0, 0, 0);
       }
     }
+    // the next tile's factors, independent of the products above (after the
+    // run's last tile they are computed from stale scales and never read)
+    write_factors(sl ^ 1);
+
     // element e of the lane's run is token 8 grp + vtok(e)
     float lg[8], p[8];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      lg[2 * r] = combine_cols(sacc[0][r]);
-      lg[2 * r + 1] = combine_cols(sacc[1][r]);
+      lg[2 * r] = combine_cols(fmaf(zs[0][r], 1.0f / 1048576.0f, cs[0][r]));
+      lg[2 * r + 1] = combine_cols(fmaf(zs[1][r], 1.0f / 1048576.0f, cs[1][r]));
     }
     softmax_step(lg, p, std::false_type{});
 
     // value product: column (head qh, group vg) holds p * scale
-    const half8 vs = *reinterpret_cast<const half8*>(&lds_vsz[wave][0][vg][8 * grp]);
-    const half8 vz = *reinterpret_cast<const half8*>(&lds_vsz[wave][1][vg][8 * grp]);
+    const half8 vs = *reinterpret_cast<const half8*>(&lds_vsz[wave][sl][0][vg][8 * grp]);
+    const half8 vz = *reinterpret_cast<const half8*>(&lds_vsz[wave][sl][1][vg][8 * grp]);
     half8 bv;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -582,108 +701,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kFWavesPerS
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
       acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(feat_value_codes8<BITS>(cur.v[mb]), bv, acc[mb], 0, 0, 0);
-    wave_sync();
+
+    // stage the next tile's value scales and the key scales two tiles on,
+    // then load the scales three tiles on into the buffer just staged from
+    if (i + 1 < nq) stage_vsz(sn1, sl ^ 1);
+    if (i + 2 < nq) stage_ksz(sn2, sl);
+    if (i + 3 < nq) load_scales(qb + i + 3, sn1);
   };
 
-  // ------------------------------------------------------ fp16 recent tile
-  const uint16_t* const krb = a.k_recent + unit * a.R_cap * D;
-  const uint16_t* const vrb = a.v_recent + unit * a.R_cap * D;
-  auto recent_tile = [&](int rt) {
-    const int r0 = rt * kGroup;
-    const double t0 = static_cast<double>(a.n_qtiles + rt) * kGroup;
-    // keys: the lane's 8 channels of K-step ks for its two tokens; value
-    // slabs: token lane / 2, 8 channels of block mb
-    uint4 kin[2][KSR], vin[MB];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int r = r0 + row_token(s, col);
-#pragma unroll
-      for (int ks = 0; ks < KSR; ++ks) {
-        kin[s][ks] = uint4{0u, 0u, 0u, 0u};
-        if (r < a.R)
-          kin[s][ks] = *reinterpret_cast<const uint4*>(krb + static_cast<size_t>(r) * D + 2 * PPG * grp + 8 * ks);
-      }
-    }
-    {
-      const int r = r0 + (lane >> 1);
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        vin[mb] = uint4{0u, 0u, 0u, 0u};
-        if (r < a.R) vin[mb] = *reinterpret_cast<const uint4*>(vrb + static_cast<size_t>(r) * D + 16 * mb + 8 * (lane & 1));
-      }
-    }
-    // B: the query rotated to t0 (no 2^5), K = the lane group's channels in
-    // order: item (head, lane group, K-step) of this lane writes 8 channels
-    if (lane < G * 4 * KSR) {
-      const int h = lane / (4 * KSR), g = (lane / KSR) % 4, ks = lane % KSR;
-      const int c0 = 2 * PPG * g + 8 * ks;
-      const uint16_t* qh = a.q + (static_cast<size_t>(b) * a.Hq + kvh * G + h) * D + c0;
-      const uint4 qw = *reinterpret_cast<const uint4*>(qh);
-      const uint32_t qq[4] = {qw.x, qw.y, qw.z, qw.w};
-      uint32_t hi[4], lo[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float x0 = h2f(static_cast<uint16_t>(qq[i] & 0xFFFFu)) * a.q_scale;
-        const float x1 = h2f(static_cast<uint16_t>(qq[i] >> 16)) * a.q_scale;
-        float cc, ss;
-        rope_unit(t0, a.omega[c0 / 2 + i], cc, ss);
-        split2(x0 * cc + x1 * ss, x1 * cc - x0 * ss, hi[i], lo[i]);
-      }
-      const int K = 32 * ks + 8 * g;
-      *reinterpret_cast<uint4*>(Bw + h * BST + K) = uint4{hi[0], hi[1], hi[2], hi[3]};
-      *reinterpret_cast<uint4*>(Bw + (G + h) * BST + K) = uint4{lo[0], lo[1], lo[2], lo[3]};
-    }
-    wave_sync();
-    float4v sacc[2] = {float4v{0.0f, 0.0f, 0.0f, 0.0f}, float4v{0.0f, 0.0f, 0.0f, 0.0f}};
-#pragma unroll
-    for (int ks = 0; ks < KSR; ++ks) {
-      const half8 bv = *reinterpret_cast<const half8*>(Bw + bcol * BST + 32 * ks + 8 * grp);
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const int j = row_token(s, col);
-        const uint32_t w[4] = {kin[s][ks].x, kin[s][ks].y, kin[s][ks].z, kin[s][ks].w};
-        uint32_t ah[4], al[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float x0 = h2f(static_cast<uint16_t>(w[i] & 0xFFFFu));
-          const float x1 = h2f(static_cast<uint16_t>(w[i] >> 16));
-          const float2 cs = lds_trig[j][grp * PPG + 4 * ks + i];
-          split2(x0 * cs.x - x1 * cs.y, x0 * cs.y + x1 * cs.x, ah[i], al[i]);
-        }
-        sacc[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, ah), bv, sacc[s], 0, 0, 0);
-        sacc[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, al), bv, sacc[s], 0, 0, 0);
-      }
-    }
-    float lg[8], p[8];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      lg[2 * r] = combine_cols(sacc[0][r]);
-      lg[2 * r + 1] = combine_cols(sacc[1][r]);
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      if (r0 + 8 * grp + vtok(e) >= a.R) lg[e] = -INFINITY;
-    softmax_step(lg, p, std::true_type{});
-    half8 bv;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) bv[e] = static_cast<_Float16>(col < NCOL ? p[e] : 0.0f);
-    // values pass through LDS 16 channels at a time to form the
-    // channel-major operand
-    _Float16* const st = lds_vst[wave];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      *reinterpret_cast<uint4*>(&st[(lane >> 1) * VST + 8 * (lane & 1)]) = vin[mb];
-      wave_sync();
-      half8 av;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) av[e] = st[(8 * grp + vtok(e)) * VST + col];
-      wave_sync();
-      acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, acc[mb], 0, 0, 0);
-    }
-  };
-
-  // the wave's recent tiles, then its quantized run; two register buffers
-  // alternate so that the loads of tile i+1 stay in flight during tile i
+  // the wave's recent tiles (B slot 0), then its quantized run
   for (int k = 0; k < r_mine; ++k) recent_tile(r_first + k);
   // fp16 value products are exact-scale; switch the accumulator to the
   // code-product domain (a power of two: exact)
@@ -691,9 +717,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kFWavesPerS
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) acc[mb] *= 1.0f / static_cast<float>(1u << kVShift<BITS>);
   }
-  for (int ti = qb; ti < qe; ti += 2) {
-    quantized_tile(ti, buf0, buf1, ti + 1 < qe);
-    if (ti + 1 < qe) quantized_tile(ti + 1, buf1, buf0, ti + 2 < qe);
+  if (nq > 0) {
+    // tile 0: key and value scales into slot 0, tile 1's key scales into
+    // slot 1; the factors of tile 0; tile 2's scales into the free buffer
+    stage_ksz(s0, 0);
+    stage_vsz(s0, 0);
+    if (nq > 1) stage_ksz(s1, 1);
+    wave_sync();
+    write_factors(0);
+    if (nq > 2) load_scales(qb + 2, s0);
+  }
+  for (int i = 0; i < nq; i += 2) {
+    // tile i: codes c0, slot 0, scales of i + 1 in s1 and of i + 2 in s0
+    quantized_tile(i, 0, c0, c1, s1, s0);
+    // tile i + 1: codes c1, slot 1, scales of i + 2 in s0 and of i + 3 in s1
+    if (i + 1 < nq) quantized_tile(i + 1, 1, c1, c0, s0, s1);
   }
 
   // ---- wave state -> LDS: row sums and zero-point sums over the 4 row

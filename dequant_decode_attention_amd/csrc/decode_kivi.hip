@@ -92,29 +92,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kDecodeWave
   const int col = lane & 15, grp = lane >> 4;
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const size_t unit = static_cast<size_t>(b) * a.Hkv + kvh;
-  // The wave's work: the (batch, KV head)'s n_q quantized and n_r recent
-  // tiles form a sequence of n_q + n_r slots cut evenly over all its waves
-  // (contiguous runs [u0, u1)).  Recent tile r sits at slot
-  // floor((2r + 1)(n_q + n_r) / (2 n_r)), so the recent tiles land in
-  // different waves far apart; the other slots hold the quantized tiles in
-  // order.  A wave attends its recent tiles first, then its contiguous run
-  // [qb, qe) of quantized tiles.
-  const int n_tiles = a.n_qtiles + a.n_rtiles;
-  const long long nw = static_cast<long long>(a.total_splits) * kWavesPerWG;
-  const long long gw = static_cast<long long>(split) * kWavesPerWG + wave;
-  const int u0 = static_cast<int>(gw * n_tiles / nw);
-  const int u1 = static_cast<int>((gw + 1) * n_tiles / nw);
-  int r_before = 0, r_mine = 0, r_first = 0;
-  for (int r = 0; r < a.n_rtiles; ++r) {
-    const int slot = static_cast<int>((2LL * r + 1) * n_tiles / (2LL * a.n_rtiles));
-    if (slot < u0) ++r_before;
-    else if (slot < u1) {
-      if (r_mine == 0) r_first = r;
-      ++r_mine;
-    }
-  }
-  const int qb = u0 - r_before;
-  const int qe = u1 - r_before - r_mine;
+  // The wave's work (wave_tiles, every tile one work unit): its recent tiles
+  // first, then its contiguous run [qb, qe) of quantized tiles.
+  const WaveTiles wt = wave_tiles(a.n_qtiles, a.n_rtiles, 1, static_cast<long long>(a.total_splits) * kWavesPerWG,
+                                  static_cast<long long>(split) * kWavesPerWG + wave);
+  const int qb = wt.qb, qe = wt.qb + wt.nq, r_first = wt.r_first, r_mine = wt.r_mine;
 
   // in-tile rotation table E[j][i] = e^{i j omega_i}, j = 0..31: thread
   // (pair i, block q) evaluates e^{i 8q omega_i} and e^{i omega_i} accurately
