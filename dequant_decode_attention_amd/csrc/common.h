@@ -35,6 +35,27 @@ __device__ __forceinline__ uint16_t f2h(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
 }
 
+// Arithmetic stays in C rather than inline asm: gfx950 needs independent
+// instructions between some dependent pairs (a transcendental result and
+// the next VALU instruction that reads it, a VALU result and a matrix
+// instruction or a lane permute that reads it), and the compiler inserts
+// them only around instructions it generates itself.
+//
+// Half H of a word of two fp16 values, widened to fp32 (exact).  An FMA
+// with one or two such operands compiles to one mixed-precision FMA.
+typedef _Float16 fp16x2 __attribute__((ext_vector_type(2)));
+template <int H>
+__device__ __forceinline__ float half_of(uint32_t w) {
+  return static_cast<float>(__builtin_bit_cast(fp16x2, w)[H]);
+}
+// A constant the optimizer does not see through (held in a scalar
+// register), so that fma(h, +-1, x) stays one mixed-precision FMA instead
+// of becoming a widening conversion and an addition.
+__device__ __forceinline__ float opaque_const(float c) {
+  asm("" : "+s"(c));
+  return c;
+}
+
 // Butterfly exchange inside a quad / half-row with DPP (no LDS traffic).
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {

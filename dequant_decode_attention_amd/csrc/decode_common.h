@@ -8,6 +8,20 @@
 
 namespace dqa {
 
+// The split of one (batch, KV head)'s tiles over its waves, computed on the
+// host.  The n_q quantized tiles (one work unit each) and n_r <= 4 fp16
+// recent tiles (W units each: their set-up costs more) lie on a line of
+// total = n_q + W n_r units: recent tile r takes the W units from rstart[r]
+// (centred in the r-th of n_r equal segments), the quantized tiles fill the
+// other units in order.  Wave gw of the (batch, KV head) takes the units
+// [gw per_wave + min(gw, extra), ...) -- per_wave of them, one more when
+// gw < extra: the quantized tiles among them (a contiguous run) and the
+// recent tiles that start among them.
+struct TileSplit {
+  int per_wave, extra, n_r, W;
+  int rstart[4];
+};
+
 struct KiviArgs {
   const uint16_t* q;
   const uint32_t* k_codes;
@@ -27,6 +41,7 @@ struct KiviArgs {
   int n_qtiles;         // T_q / 32
   int n_rtiles;         // ceil(R / 32)
   int total_splits;     // splits (partial-state slots) per (batch, KV head)
+  TileSplit split;      // tiles -> waves
   float q_scale;        // sm_scale * log2(e): logits in the log2 domain
   double omega[64];     // RoPE frequencies theta^(-2i/d), i < d/2 (host fp64)
 };
@@ -34,6 +49,7 @@ struct KiviArgs {
 // The feature-product decode kernel (2- and 4-bit codes with RoPE; see
 // decode_feat.hip): its resident workgroup target and its launch.
 int feat_decode_workgroups();
+int feat_recent_weight();
 int launch_feat_decode(const KiviArgs& a, int d, int G, int bits, dim3 grid, hipStream_t s);
 
 namespace {
@@ -43,35 +59,47 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float float4v __attribute__((ext_vector_type(4)));
 
-// The tiles of one wave.  The n_q quantized tiles (one work unit each) and
-// n_r fp16 recent tiles (W units each: their set-up costs more) of a (batch,
-// KV head) lie on a line of n_q + W n_r units: recent tile r takes the W
-// units centred in the r-th of n_r equal segments, the quantized tiles fill
-// the other units in order.  The line is cut evenly over the nw waves of the
-// (batch, KV head); wave gw takes the quantized tiles whose units fall in
-// its cut [u0, u1) -- a contiguous run [qb, qb + nq) -- and the recent tiles
-// whose first unit does (r_mine of them from r_first).
+// Host side of TileSplit for n_q quantized and n_r recent tiles, recent
+// weight W, over nw waves (total units below 2^31).
+inline TileSplit make_tile_split(int n_q, int n_r, int W, long long nw) {
+  TileSplit t{};
+  const long long total = n_q + static_cast<long long>(W) * n_r;
+  t.per_wave = static_cast<int>(total / nw);
+  t.extra = static_cast<int>(total % nw);
+  t.n_r = n_r;
+  t.W = W;
+  for (int r = 0; r < n_r && r < 4; ++r) {
+    const long long lo = r * total / n_r, hi = (r + 1) * total / n_r;
+    t.rstart[r] = static_cast<int>(lo + (hi - lo - W) / 2);
+  }
+  return t;
+}
+
+// The tiles of wave gw under a TileSplit: its quantized run [qb, qb + nq)
+// and its r_mine recent tiles from r_first.
 struct WaveTiles {
   int qb, nq, r_first, r_mine;
 };
-__device__ __forceinline__ WaveTiles wave_tiles(int n_q, int n_r, int W, long long nw, long long gw) {
-  const long long total = n_q + static_cast<long long>(W) * n_r;
-  const long long u0 = gw * total / nw, u1 = (gw + 1) * total / nw;
-  long long before0 = 0, before1 = 0;   // recent units below u0 and below u1
-  WaveTiles t{0, 0, 0, 0};
-  for (int r = 0; r < n_r; ++r) {
-    const long long lo = r * total / n_r, hi = (r + 1) * total / n_r;
-    const long long start = lo + (hi - lo - W) / 2;
-    before0 += min(max(u0 - start, 0LL), static_cast<long long>(W));
-    before1 += min(max(u1 - start, 0LL), static_cast<long long>(W));
-    if (start >= u0 && start < u1) {
-      if (t.r_mine == 0) t.r_first = r;
-      ++t.r_mine;
+__device__ __forceinline__ WaveTiles wave_tiles(const TileSplit& t, int gw) {
+  const int u0 = gw * t.per_wave + min(gw, t.extra);
+  const int u1 = u0 + t.per_wave + (gw < t.extra ? 1 : 0);
+  int before0 = 0, before1 = 0;   // recent units below u0 and below u1
+  WaveTiles w{0, 0, 0, 0};
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    if (r < t.n_r) {
+      const int start = t.rstart[r];
+      before0 += min(max(u0 - start, 0), t.W);
+      before1 += min(max(u1 - start, 0), t.W);
+      if (start >= u0 && start < u1) {
+        if (w.r_mine == 0) w.r_first = r;
+        ++w.r_mine;
+      }
     }
   }
-  t.qb = static_cast<int>(u0 - before0);
-  t.nq = static_cast<int>((u1 - before1) - (u0 - before0));
-  return t;
+  w.qb = u0 - before0;
+  w.nq = (u1 - before1) - w.qb;
+  return w;
 }
 
 // Accurate unit complex number e^{i * pos * omega}: the angle is formed and
@@ -201,16 +229,7 @@ __device__ __forceinline__ constexpr int key_code_half(int e, int ks) {
 // code (fp16 half A of m) * s + zero (fp16 half Z of z), one rounding
 template <int A, int Z>
 __device__ __forceinline__ float mix_dequant(uint32_t m, float s, uint32_t z) {
-  float r;
-  if constexpr (A == 0 && Z == 0)
-    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel_hi:[1,0,1]" : "=v"(r) : "v"(m), "v"(s), "v"(z));
-  else if constexpr (A == 1 && Z == 0)
-    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[1,0,0] op_sel_hi:[1,0,1]" : "=v"(r) : "v"(m), "v"(s), "v"(z));
-  else if constexpr (A == 0 && Z == 1)
-    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[0,0,1] op_sel_hi:[1,0,1]" : "=v"(r) : "v"(m), "v"(s), "v"(z));
-  else
-    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[1,0,1] op_sel_hi:[1,0,1]" : "=v"(r) : "v"(m), "v"(s), "v"(z));
-  return r;
+  return __builtin_fmaf(half_of<A>(m), s, half_of<Z>(z));
 }
 
 // Value chunk (8 tokens of one channel) -> fp16 operand holding the codes as
@@ -271,17 +290,12 @@ __device__ __forceinline__ constexpr int row_token(int s, int m) { return 8 * (m
 
 // x - (fp32) of the low / high fp16 half of h, exact (the fp16 value is
 // widened exactly and one fp32 rounding applies, none here since hi is x
-// rounded toward zero).  One mixed-precision FMA each; the compiler forms
-// a widening conversion and a subtraction instead.
+// rounded toward zero): one mixed-precision FMA each.
 __device__ __forceinline__ float minus_half_lo(uint32_t h, float x) {
-  float r;
-  asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "v"(x));
-  return r;
+  return __builtin_fmaf(half_of<0>(h), opaque_const(-1.0f), x);
 }
 __device__ __forceinline__ float minus_half_hi(uint32_t h, float x) {
-  float r;
-  asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "v"(x));
-  return r;
+  return __builtin_fmaf(half_of<1>(h), opaque_const(-1.0f), x);
 }
 
 // Split 8 fp32 values into fp16 hi + lo (hi rounded toward zero; lo the

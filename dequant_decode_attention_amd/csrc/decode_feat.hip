@@ -65,15 +65,26 @@ constexpr int kRecentWeight = 3;
 // ---------------------------------------------------------------- helpers
 
 // Packed fp16 products with one code half broadcast: (c * t.x, c * t.y) for
-// c the low (HALF = 0) or high (HALF = 1) half of `code`.
+// c the low (HALF = 0) or high (HALF = 1) half of `code` (one packed
+// multiply with the broadcast in its operand selection).
 template <int HALF>
 __device__ __forceinline__ uint32_t pk_mul_bcast(uint32_t code, uint32_t t) {
-  uint32_t r;
-  if constexpr (HALF == 0)
-    asm("v_pk_mul_f16 %0, %1, %2 op_sel:[0,0] op_sel_hi:[0,1]" : "=v"(r) : "v"(code), "v"(t));
-  else
-    asm("v_pk_mul_f16 %0, %1, %2 op_sel:[1,0] op_sel_hi:[1,1]" : "=v"(r) : "v"(code), "v"(t));
-  return r;
+  const half2v c = __builtin_bit_cast(half2v, code);
+  const half2v b = {c[HALF], c[HALF]};
+  return __builtin_bit_cast(uint32_t, b * __builtin_bit_cast(half2v, t));
+}
+
+// Mixed-precision products with an fp16 operand taken from half H of a
+// word (one mixed-precision FMA, no conversion): h * x (NEG: h * -x) and
+// h * x + c, in fp32.  The zero addend keeps the FMA form (h * x + 0 is
+// h * x except for the sign of a zero product).
+template <int H, bool NEG = false>
+__device__ __forceinline__ float mix_mul(uint32_t h2, float x) {
+  return __builtin_fmaf(half_of<H>(h2), NEG ? -x : x, 0.0f);
+}
+template <int H>
+__device__ __forceinline__ float mix_fma(uint32_t h2, float x, float c) {
+  return __builtin_fmaf(half_of<H>(h2), x, c);
 }
 
 // fp32 x with all but its top `bits` significant bits cleared (toward zero).
@@ -241,9 +252,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kFWavesPerS
 
   // The wave's tiles (a recent tile weighs kRecentWeight quantized tiles):
   // its recent tiles first, then its run [qb, qb + nq) of quantized tiles.
-  const WaveTiles wt = wave_tiles(a.n_qtiles, a.n_rtiles, kRecentWeight,
-                                  static_cast<long long>(a.total_splits) * kFWaves,
-                                  static_cast<long long>(split) * kFWaves + wave);
+  const WaveTiles wt = wave_tiles(a.split, split * kFWaves + wave);
   const int qb = wt.qb, nq = wt.nq, r_first = wt.r_first, r_mine = wt.r_mine;
 
   // ---- per-tile factor item of this lane: head ih, lane group ig, K-step
@@ -268,7 +277,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kFWavesPerS
       qraw[k] = *reinterpret_cast<const uint32_t*>(qh + ich + 2 * (k & 1) + EPW * (k >> 1));
   }
 
-  // ---- tile inputs: codes one tile ahead, scales two tiles ahead.  The
+  // ---- tile inputs: key codes two tiles ahead, value codes one, scales
+  // three (loads) and two (LDS staging).  The
   // first loads are issued before the set-up below, so their latency
   // overlaps it.
   const size_t qstride = static_cast<size_t>(a.qtile_stride);
@@ -286,7 +296,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kFWavesPerS
     uint32_t ksz[D / 64];   // lanes 0..31: key scales of D / 32 channels; 32..63: zeros
     uint32_t vsz[NVG / 2];  // lanes 0..31: value scales of token lane; 32..63: zeros
   };
-  auto load_codes = [&](int ti, Codes& t) {
+  auto load_keys = [&](int ti, Codes& t) {
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const uint8_t* p = kbase + (static_cast<size_t>(ti) * kGroup + row_token(s, col)) * KROW + grp * LROW;
@@ -294,6 +304,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kFWavesPerS
 #pragma unroll
       for (int i = 0; i < NW; ++i) t.k[s][i] = w.w[i];
     }
+  };
+  auto load_values = [&](int ti, Codes& t) {
     const uint8_t* blk = vbase + static_cast<size_t>(ti) * VBLK;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
@@ -315,10 +327,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kFWavesPerS
   Codes c0, c1;
   Scales s0, s1;
   if (nq > 0) {
-    load_codes(qb, c0);
+    load_keys(qb, c0);
+    load_values(qb, c0);
     load_scales(qb, s0);
   }
-  if (nq > 1) load_scales(qb + 1, s1);
+  if (nq > 1) {
+    load_keys(qb + 1, c1);
+    load_scales(qb + 1, s1);
+  }
 
   // ---- trig tables.  e^{i j w} for j = 4a + b is the product of two of 11
   // accurately rounded unit numbers (angle 4a w, a = 1..8, and b w, b =
@@ -553,8 +569,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kFWavesPerS
     const int half = lane >> 5, r = lane & 31;
 #pragma unroll
     for (int i = 0; i < NVG / 2; ++i) {
-      uint32_t w;
-      asm("v_pk_mul_f16 %0, %1, %2" : "=v"(w) : "v"(t.vsz[i]), "v"(vfac));
+      const uint32_t w = __builtin_bit_cast(
+          uint32_t, __builtin_bit_cast(half2v, t.vsz[i]) * __builtin_bit_cast(half2v, vfac));
       lds_vsz[wave][sl][half][2 * i][r] = __builtin_bit_cast(_Float16, static_cast<uint16_t>(w & 0xFFFFu));
       lds_vsz[wave][sl][half][2 * i + 1][r] = __builtin_bit_cast(_Float16, static_cast<uint16_t>(w >> 16));
     }
@@ -567,17 +583,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kFWavesPerS
     if (!item) return;
     _Float16* const Bw = &lds_B[sl][0][0];
     // scales and zeros of channels (cA, cA+1, cA+2, cA+3) and (cA+EPW, ...)
-    float sv[2][4], zv[2][4];
+    // as fp16 pairs: word kk of chunk c holds channels 2 kk, 2 kk + 1 (the
+    // a and b channel of the chunk's pair kk)
+    uint32_t sw[2][2], zw[2][2];
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      const uint2 sw = *reinterpret_cast<const uint2*>(&lds_ksz[wave][sl][0][ich + c * EPW]);
-      const uint2 zw = *reinterpret_cast<const uint2*>(&lds_ksz[wave][sl][1][ich + c * EPW]);
-      const uint32_t sww[2] = {sw.x, sw.y}, zww[2] = {zw.x, zw.y};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        sv[c][k] = h2f(static_cast<uint16_t>(sww[k >> 1] >> (16 * (k & 1))));
-        zv[c][k] = h2f(static_cast<uint16_t>(zww[k >> 1] >> (16 * (k & 1))));
-      }
+      const uint2 s2 = *reinterpret_cast<const uint2*>(&lds_ksz[wave][sl][0][ich + c * EPW]);
+      const uint2 z2 = *reinterpret_cast<const uint2*>(&lds_ksz[wave][sl][1][ich + c * EPW]);
+      sw[c][0] = s2.x;
+      sw[c][1] = s2.y;
+      zw[c][0] = z2.x;
+      zw[c][1] = z2.y;
     }
     // code K-steps 2 ikb (pairs p0 = chunk A channels 0,1; p1 = chunk B
     // channels 0,1) and 2 ikb + 1 (p2 = chunk A channels 2,3; p3 = B 2,3)
@@ -587,11 +603,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kFWavesPerS
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         const float qa = iq[2 * c + kk][0], qb_ = iq[2 * c + kk][1];
-        const float sa = sv[c][2 * kk], sb = sv[c][2 * kk + 1];
-        f[4 * c + 0] = sa * qa;
-        f[4 * c + 1] = sa * qb_;
-        f[4 * c + 2] = sb * qb_;
-        f[4 * c + 3] = -(sb * qa);
+        f[4 * c + 0] = mix_mul<0>(sw[c][kk], qa);       // s_a q'_a
+        f[4 * c + 1] = mix_mul<0>(sw[c][kk], qb_);      // s_a q'_b
+        f[4 * c + 2] = mix_mul<1>(sw[c][kk], qb_);      // s_b q'_b
+        f[4 * c + 3] = mix_mul<1, true>(sw[c][kk], qa);  // -s_b q'_a
       }
       uint32_t hi[4], lo[4];
 #pragma unroll
@@ -607,9 +622,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kFWavesPerS
       for (int q4 = 0; q4 < 4; ++q4) {
         const int c = q4 & 1, kk = q4 >> 1;               // chunk, pair within chunk
         const float qa = iq[2 * c + kk][0], qb_ = iq[2 * c + kk][1];
-        const float za = zv[c][2 * kk], zb = zv[c][2 * kk + 1];
-        f[2 * q4 + 0] = za * qa + zb * qb_;
-        f[2 * q4 + 1] = za * qb_ - zb * qa;
+        f[2 * q4 + 0] = mix_fma<0>(zw[c][kk], qa, mix_mul<1>(zw[c][kk], qb_));    // z_a q'_a + z_b q'_b
+        f[2 * q4 + 1] = mix_fma<0>(zw[c][kk], qb_, mix_mul<1, true>(zw[c][kk], qa));   // z_a q'_b - z_b q'_a
       }
       uint32_t hi[4], lo[4];
 #pragma unroll
@@ -633,11 +647,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kFWavesPerS
   // the factors of tile i + 1 (other slot); at the end the next tile's value
   // scales and the key scales of tile i + 2 are staged.  `cur` holds tile
   // i's codes, `nxt` receives tile i + 1's; `sn1` holds the scales of tile
-  // i + 1, `sn2` those of tile i + 2, and then receives tile i + 3's.
-  auto quantized_tile = [&](int i, int sl, const Codes& cur, Codes& nxt, Scales& sn1, Scales& sn2) {
+  // i + 1, `sn2` those of tile i + 2, and then receives tile i + 3's.  Key
+  // codes run two tiles ahead: `cur`'s keys, once used, receive tile i + 2's.
+  auto quantized_tile = [&](int i, int sl, Codes& cur, Codes& nxt, Scales& sn1, Scales& sn2) {
     wave_sync();
     // (past the run's end the last tile is loaded again, unused: no branch)
-    load_codes(qb + min(i + 1, nq - 1), nxt);
+    load_values(qb + min(i + 1, nq - 1), nxt);
     const _Float16* const Bw = &lds_B[sl][0][0];
 
     // logits: zero-point K-steps (their sums carry 2^20) and code K-steps in
@@ -675,6 +690,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kFWavesPerS
         cs[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, al), bv, cs[s], 0, 0, 0);
       }
     }
+    load_keys(qb + min(i + 2, nq - 1), cur);
     // the next tile's factors, independent of the products above (after the
     // run's last tile they are computed from stale scales and never read)
     write_factors(sl ^ 1);
@@ -689,14 +705,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kFWavesPerS
     softmax_step(lg, p, std::false_type{});
 
     // value product: column (head qh, group vg) holds p * scale
-    const half8 vs = *reinterpret_cast<const half8*>(&lds_vsz[wave][sl][0][vg][8 * grp]);
-    const half8 vz = *reinterpret_cast<const half8*>(&lds_vsz[wave][sl][1][vg][8 * grp]);
+    const uint4 vs4 = *reinterpret_cast<const uint4*>(&lds_vsz[wave][sl][0][vg][8 * grp]);
+    const uint4 vz4 = *reinterpret_cast<const uint4*>(&lds_vsz[wave][sl][1][vg][8 * grp]);
+    const uint32_t vsw[4] = {vs4.x, vs4.y, vs4.z, vs4.w}, vzw[4] = {vz4.x, vz4.y, vz4.z, vz4.w};
     half8 bv;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
+      // the staged scale of token t = vtok(e) is half t % 2 of word t / 2
       const int t = vtok(e);
-      bv[e] = static_cast<_Float16>(col < NCOL ? p[e] * static_cast<float>(vs[t]) : 0.0f);
-      zacc = fmaf(p[e], static_cast<float>(vz[t]), zacc);
+      const float pv = (t & 1) ? mix_mul<1>(vsw[t >> 1], p[e]) : mix_mul<0>(vsw[t >> 1], p[e]);
+      bv[e] = static_cast<_Float16>(col < NCOL ? pv : 0.0f);
+      zacc = (t & 1) ? mix_fma<1>(vzw[t >> 1], p[e], zacc) : mix_fma<0>(vzw[t >> 1], p[e], zacc);
     }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
@@ -770,6 +789,7 @@ int launch_feat_g(const KiviArgs& a, int G, dim3 grid, hipStream_t s) {
 }  // namespace
 
 int feat_decode_workgroups() { return 256 * kFWavesPerSimd; }
+int feat_recent_weight() { return kRecentWeight; }
 
 int launch_feat_decode(const KiviArgs& a, int d, int G, int bits, dim3 grid, hipStream_t s) {
   if (d == 128) return bits == 2 ? launch_feat_g<128, 2>(a, G, grid, s) : launch_feat_g<128, 4>(a, G, grid, s);

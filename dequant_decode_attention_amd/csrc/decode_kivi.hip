@@ -94,8 +94,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kDecodeWave
   const size_t unit = static_cast<size_t>(b) * a.Hkv + kvh;
   // The wave's work (wave_tiles, every tile one work unit): its recent tiles
   // first, then its contiguous run [qb, qe) of quantized tiles.
-  const WaveTiles wt = wave_tiles(a.n_qtiles, a.n_rtiles, 1, static_cast<long long>(a.total_splits) * kWavesPerWG,
-                                  static_cast<long long>(split) * kWavesPerWG + wave);
+  const WaveTiles wt = wave_tiles(a.split, split * kWavesPerWG + wave);
   const int qb = wt.qb, qe = wt.qb + wt.nq, r_first = wt.r_first, r_mine = wt.r_mine;
 
   // in-tile rotation table E[j][i] = e^{i j omega_i}, j = 0..31: thread
@@ -630,6 +629,8 @@ extern "C" int decode_attention_qkv_partial(const uint16_t* q, const dqa_kivi_ca
   a.n_qtiles = p.n_qtiles;
   a.n_rtiles = p.n_rtiles;
   a.total_splits = p.total;
+  a.split = make_tile_split(p.n_qtiles, p.n_rtiles, use_feat(c->bits, c->rope_theta > 0.0f) ? feat_recent_weight() : 1,
+                            static_cast<long long>(p.total) * kWavesPerWG);
   a.q_scale = sm_scale * 1.4426950408889634f;
   const bool rope = c->rope_theta > 0.0f;
   for (int i = 0; i < 64; ++i)

@@ -39,7 +39,10 @@ __device__ __forceinline__ GroupParams group_params(float mn, float mx, int bits
 // Packed fp16 minimum / maximum of two pairs (exact; the inputs are finite
 // fp16 values, so the plain instructions are used without the canonicalizing
 // moves the compiler would add for signalling NaNs), and a DPP lane exchange
-// of a 32-bit register.
+// of a 32-bit register.  A lane permute (DPP or row swap) may read a
+// register only two wait states after a vector instruction wrote it; the
+// compiler ensures that only for instructions it generates, so the
+// permutes below take their input through `settled`.
 __device__ __forceinline__ uint32_t pk_min_h2(uint32_t a, uint32_t b) {
   uint32_t r;
   asm("v_pk_min_f16 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
@@ -50,9 +53,13 @@ __device__ __forceinline__ uint32_t pk_max_h2(uint32_t a, uint32_t b) {
   asm("v_pk_max_f16 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
   return r;
 }
+__device__ __forceinline__ uint32_t settled(uint32_t v) {
+  asm("s_nop 1" : "+v"(v));
+  return v;
+}
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
-  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, false));
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(settled(v)), CTRL, 0xF, 0xF, false));
 }
 constexpr int kDppRowRor8 = 0x128;   // row_ror:8 (lane i <- lane (i + 8) mod 16 within its row)
 // Packed min (MAX = false) or max of lane L and lane L ^ 32 (rows32) or
@@ -60,6 +67,7 @@ constexpr int kDppRowRor8 = 0x128;   // row_ror:8 (lane i <- lane (i + 8) mod 16
 // permute's two results are copied into scalars before use.
 template <bool MAX>
 __device__ __forceinline__ uint32_t pk_swap_rows(uint32_t x, bool rows32) {
+  x = settled(x);
   uint32_t r0, r1;
   if (rows32) {
     const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
@@ -78,12 +86,7 @@ __device__ __forceinline__ uint32_t pk_swap_rows(uint32_t x, bool rows32) {
 // widened value.
 template <int H>
 __device__ __forceinline__ float minus_zero(uint32_t w, float zf) {
-  float r;
-  if constexpr (H == 0)
-    asm("v_fma_mix_f32 %0, %1, 1.0, -%2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(w), "v"(zf));
-  else
-    asm("v_fma_mix_f32 %0, %1, 1.0, -%2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(w), "v"(zf));
-  return r;
+  return __builtin_fmaf(half_of<H>(w), opaque_const(1.0f), -zf);
 }
 
 // code = clamp(rint((x - z) / s), 0, 2^b - 1) with the IEEE quotient, for

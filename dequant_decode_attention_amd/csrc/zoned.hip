@@ -257,12 +257,7 @@ __device__ __forceinline__ uint32_t pk_max_halves(uint32_t w) {
 // (x * 1 - z, one rounding): the fp32 subtraction of the widened value.
 template <int H>
 __device__ __forceinline__ float minus_zero(uint32_t w, float zf) {
-  float r;
-  if constexpr (H == 0)
-    asm("v_fma_mix_f32 %0, %1, 1.0, -%2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(w), "v"(zf));
-  else
-    asm("v_fma_mix_f32 %0, %1, 1.0, -%2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(w), "v"(zf));
-  return r;
+  return __builtin_fmaf(half_of<H>(w), opaque_const(1.0f), -zf);
 }
 
 // Value codes of one slot's value group (32 channels, fp16 pairs in v[16])
