@@ -16,7 +16,9 @@ import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libdqattn.so")
+# DQA_LIBRARY names another build of the same library (the host-sanitizer
+# build of build.py --host-sanitize, for CPU runs under AddressSanitizer)
+LIB_PATH = os.environ.get("DQA_LIBRARY") or os.path.join(_HERE, "libdqattn.so")
 
 DQA_OK = 0
 _STATUS = {0: "DQA_OK", 1: "DQA_ERR_NULL", 2: "DQA_ERR_SHAPE", 3: "DQA_ERR_BITS",

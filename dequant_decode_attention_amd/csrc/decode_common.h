@@ -149,9 +149,6 @@ __device__ __forceinline__ Words<NB> load_words(const void* p) {
   return r;
 }
 
-// A value the compiler must treat as unknown (keeps a VGPR constant out of
-// the scalar constant bus, and keeps shifted words from being folded back
-// into bit-field extracts).
 // A kernel-argument pointer as a wave-uniform value.  A lane-dependent
 // choice between two argument pointers would otherwise be folded into a
 // per-lane vector load of the pointer from the argument segment, issued
@@ -167,6 +164,9 @@ __device__ __forceinline__ const T* uniform_ptr(const T* p) {
   return (const T*)g;
 }
 
+// A value the compiler must treat as unknown (keeps a VGPR constant out of
+// the scalar constant bus, and keeps shifted words from being folded back
+// into bit-field extracts).  The asm statement is empty: no instruction.
 __device__ __forceinline__ uint32_t opaque(uint32_t v) {
   asm volatile("" : "+v"(v));
   return v;
