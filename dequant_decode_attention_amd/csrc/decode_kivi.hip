@@ -86,7 +86,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kDecodeWave
   __shared__ __attribute__((aligned(16))) _Float16 lds_kz[kWavesPerWG][D];
   __shared__ __attribute__((aligned(16))) _Float16 lds_vsz[kWavesPerWG][2][NVG][kGroup];
   __shared__ float lds_m[kWavesPerWG][G], lds_l[kWavesPerWG][G];
-  __shared__ float lds_o[kWavesPerWG][G][D];
+  __shared__ __attribute__((aligned(16))) float lds_o[kWavesPerWG][G][D];
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int col = lane & 15, grp = lane >> 4;

@@ -29,7 +29,8 @@ namespace dqa {
 namespace {
 
 // splits per (batch, KV head) at most (their m and l must fit a workgroup's
-// output staging, NW * G * D floats, with NW >= 4 and D >= 64)
+// output staging, NW * G * D floats, with NW >= 4 and D >= 64; one wave
+// reduces a head's maxima over two lanes' worth: 128)
 constexpr int kMaxSplitsMerge = 128;
 
 // Counters at the start of a workspace: one per (batch, KV head), at least
@@ -46,7 +47,7 @@ inline float* merge_partials(void* ws, size_t units) {
 }
 
 // Combine the NW wave states of a workgroup (LDS: lm, ll [NW][G], lo
-// [NW][G][D]).  With a single split: the normalized output
+// [NW][G][D], lo 16-byte aligned).  With a single split: the normalized output
 // out[b][kvh * G + h][c].  Otherwise: split `slot`'s partial state, and if
 // this workgroup is the last of its (batch, KV head) to finish, the merge of
 // all splits into out (lo is reused as staging for the splits' m and l).
@@ -92,56 +93,104 @@ __device__ __forceinline__ void write_split_state(float* partials, uint32_t* cou
   __syncthreads();
   if (!s_last) return;
 
-  // ---- the last workgroup: merge every split in split order.  The output
-  // values of the first kChunk splits are loaded together with the splits'
-  // m and l (staged in LDS), so the merge costs one memory round trip for up
-  // to kChunk splits.
-  constexpr int kChunk = 16;
+  // ---- the last workgroup: merge every split in split order.  Every
+  // phase has a fixed shape (no loop over the splits with a memory or LDS
+  // round trip per split): the output values of the splits are loaded
+  // kChunk splits at a time with all loads of a chunk in flight (the first
+  // chunk together with the splits' m and l); m and l are staged head-major
+  // in LDS (rows of kMaxSplitsMerge, -inf / 0 past the last split); one wave
+  // forms each head's maximum M; the weights 2^(m_k - M) replace m; each
+  // output then reads its head's weights and l values kChunk splits at a time.
+  constexpr int kChunk = 32;
+  constexpr int S = kMaxSplitsMerge;
   constexpr int kPer = (G * D + NW * 64 - 1) / (NW * 64);   // outputs per thread
+  constexpr int kStage = (G * S + NW * 64 - 1) / (NW * 64);  // staged (m, l) per thread
+  __shared__ float s_M[G];
   const float* const parts = partials + unit * total_splits * G * (D + 2);
   constexpr size_t kSplitStride = static_cast<size_t>(G) * (D + 2);
   auto ld = [](const float* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
   float ov[kPer][kChunk];
+  auto load_chunk = [&](int k0) {
 #pragma unroll
-  for (int r = 0; r < kPer; ++r) {
-    const int e = threadIdx.x + r * NW * 64;
-    const int h = e / D, c = e % D;
+    for (int r = 0; r < kPer; ++r) {
+      const int e = min(static_cast<int>(threadIdx.x) + r * NW * 64, G * D - 1);
+      const int h = e / D, c = e % D;
 #pragma unroll
-    for (int k = 0; k < kChunk; ++k)
-      ov[r][k] = (e < G * D && k < total_splits) ? ld(parts + k * kSplitStride + h * (D + 2) + 2 + c) : 0.0f;
-  }
-  float* const sm = &lo[0][0][0];
-  float* const sl = sm + kMaxSplitsMerge * G;
-  // (m, l) of a split and head as one 8-byte load (8-byte aligned: the
-  // state of a head is D + 2 floats, D even)
-  for (int i = threadIdx.x; i < total_splits * G; i += NW * 64) {
-    const uint64_t* p = reinterpret_cast<const uint64_t*>(parts + (i / G) * kSplitStride + (i % G) * (D + 2));
-    const uint64_t ml = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    sm[i] = __builtin_bit_cast(float, static_cast<uint32_t>(ml));
-    sl[i] = __builtin_bit_cast(float, static_cast<uint32_t>(ml >> 32));
+      for (int k = 0; k < kChunk; ++k)   // past the last split: the last split again, weight 0
+        ov[r][k] = ld(parts + min(k0 + k, total_splits - 1) * kSplitStride + h * (D + 2) + 2 + c);
+    }
+  };
+  load_chunk(0);
+  float* const sw = &lo[0][0][0];   // [G][S]: m, then the weights
+  float* const sl = sw + S * G;     // [G][S]: l
+  {
+    // (m, l) of a split and head as one 8-byte load (8-byte aligned: the
+    // state of a head is D + 2 floats, D even)
+    uint64_t ml[kStage];
+#pragma unroll
+    for (int j = 0; j < kStage; ++j) {
+      const int i = min(static_cast<int>(threadIdx.x) + j * NW * 64, G * S - 1);
+      const int h = i / S, k = min(i % S, total_splits - 1);
+      ml[j] = __hip_atomic_load(reinterpret_cast<const uint64_t*>(parts + k * kSplitStride + h * (D + 2)),
+                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+#pragma unroll
+    for (int j = 0; j < kStage; ++j) {
+      const int i = static_cast<int>(threadIdx.x) + j * NW * 64;
+      if (i < G * S) {
+        const bool in = i % S < total_splits;
+        sw[i] = in ? __builtin_bit_cast(float, static_cast<uint32_t>(ml[j])) : -INFINITY;
+        sl[i] = in ? __builtin_bit_cast(float, static_cast<uint32_t>(ml[j] >> 32)) : 0.0f;
+      }
+    }
   }
   __syncthreads();
+  if (threadIdx.x < 64) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float M = wave_max(fmaxf(sw[h * S + threadIdx.x], sw[h * S + 64 + threadIdx.x]));
+      if (threadIdx.x == 0) s_M[h] = M;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kStage; ++j) {
+    const int i = static_cast<int>(threadIdx.x) + j * NW * 64;
+    if (i < G * S) sw[i] = merge_weight(sw[i], s_M[i / S]);
+  }
+  __syncthreads();
+  float Lr[kPer], Or[kPer];
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    Lr[r] = 0.0f;
+    Or[r] = 0.0f;
+  }
+  for (int k0 = 0; k0 < total_splits; k0 += kChunk) {
+    if (k0 > 0) load_chunk(k0);
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+      const int h = min(static_cast<int>(threadIdx.x) + r * NW * 64, G * D - 1) / D;
+      float w[kChunk], l[kChunk];
+#pragma unroll
+      for (int q = 0; q < kChunk / 4; ++q) {
+        const float4 w4 = *reinterpret_cast<const float4*>(&sw[h * S + k0 + 4 * q]);
+        const float4 l4 = *reinterpret_cast<const float4*>(&sl[h * S + k0 + 4 * q]);
+        w[4 * q] = w4.x, w[4 * q + 1] = w4.y, w[4 * q + 2] = w4.z, w[4 * q + 3] = w4.w;
+        l[4 * q] = l4.x, l[4 * q + 1] = l4.y, l[4 * q + 2] = l4.z, l[4 * q + 3] = l4.w;
+      }
+#pragma unroll
+      for (int k = 0; k < kChunk; ++k) {
+        Lr[r] = fmaf(l[k], w[k], Lr[r]);
+        Or[r] = fmaf(ov[r][k], w[k], Or[r]);
+      }
+    }
+  }
 #pragma unroll
   for (int r = 0; r < kPer; ++r) {
     const int e = threadIdx.x + r * NW * 64;
     if (e >= G * D) break;
     const int h = e / D, c = e % D;
-    float M = -INFINITY;
-    for (int k = 0; k < total_splits; ++k) M = fmaxf(M, sm[k * G + h]);
-    float L = 0.0f, O = 0.0f;
-#pragma unroll
-    for (int k = 0; k < kChunk; ++k)
-      if (k < total_splits) {
-        const float wt = merge_weight(sm[k * G + h], M);
-        L = fmaf(sl[k * G + h], wt, L);
-        O = fmaf(ov[r][k], wt, O);
-      }
-    for (int k = kChunk; k < total_splits; ++k) {
-      const float wt = merge_weight(sm[k * G + h], M);
-      L = fmaf(sl[k * G + h], wt, L);
-      O = fmaf(ld(parts + k * kSplitStride + h * (D + 2) + 2 + c), wt, O);
-    }
-    out[(static_cast<size_t>(b) * Hq + kvh * G + h) * D + c] = (L > 0.0f) ? O / L : 0.0f;
+    out[(static_cast<size_t>(b) * Hq + kvh * G + h) * D + c] = (Lr[r] > 0.0f) ? Or[r] / Lr[r] : 0.0f;
   }
   if (threadIdx.x == 0) __hip_atomic_store(counters + unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

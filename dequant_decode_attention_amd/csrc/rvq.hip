@@ -384,7 +384,8 @@ __device__ __forceinline__ void rebuild16(const uint16_t* cb, const int16_t* idx
 template <int G, bool LUT>
 __global__ __launch_bounds__(256) void rvq_decode_kernel(RvqDecArgs a) {
   constexpr int NCK = 8, TL = 8, IT = 4;
-  __shared__ float lds_m[kDecWaves][G], lds_l[kDecWaves][G], lds_o[kDecWaves][G][kD];
+  __shared__ float lds_m[kDecWaves][G], lds_l[kDecWaves][G];
+  __shared__ __attribute__((aligned(16))) float lds_o[kDecWaves][G][kD];
   __shared__ __attribute__((aligned(16))) float lds_lut[LUT ? kLutFloats : 4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int j = lane / NCK, ck = lane % NCK, c0 = 16 * ck;
