@@ -350,6 +350,7 @@ __global__ __launch_bounds__(256) void rvq_lut_kernel(RvqDecArgs a, float* __res
 // summed, so a token costs one memory round trip per four stages.
 __device__ __forceinline__ void rebuild16(const uint16_t* cb, const int16_t* idx, int N, int Kc,
                                           int c0, float* out) {
+  const float one = opaque_const(1.0f);   // h * 1 + x: one mixed-precision FMA, the rounding of h + x
 #pragma unroll
   for (int c = 0; c < 16; ++c) out[c] = 0.0f;
   for (int s0 = 0; s0 < N; s0 += 4) {
@@ -371,8 +372,8 @@ __device__ __forceinline__ void rebuild16(const uint16_t* cb, const int16_t* idx
       const uint32_t w[8] = {ra[k].x, ra[k].y, ra[k].z, ra[k].w, rb[k].x, rb[k].y, rb[k].z, rb[k].w};
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        out[2 * i] += h2f(static_cast<uint16_t>(w[i] & 0xFFFFu));
-        out[2 * i + 1] += h2f(static_cast<uint16_t>(w[i] >> 16));
+        out[2 * i] = __builtin_fmaf(half_of<0>(w[i]), one, out[2 * i]);
+        out[2 * i + 1] = __builtin_fmaf(half_of<1>(w[i]), one, out[2 * i + 1]);
       }
     }
   }
@@ -391,6 +392,24 @@ __global__ __launch_bounds__(256) void rvq_decode_kernel(RvqDecArgs a) {
   const int j = lane / NCK, ck = lane % NCK, c0 = 16 * ck;
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const size_t unit = static_cast<size_t>(b) * a.Hkv + kvh;
+  // the indices of a tile: lane ck's key index (stage ck) and the value
+  // indices of token j (stages 0..3), per sub-tile; positions past T read
+  // the last token (in bounds).  The first tile's are requested before the
+  // table is staged, the next tile's while the current one is processed.
+  const int tb = split * a.tiles_per_split;
+  const int te = min(a.n_tiles, tb + a.tiles_per_split);
+  int kci[IT] = {}, vci[IT][4] = {}, kcn[IT] = {}, vcn[IT][4] = {};
+  auto load_idx = [&](int ti, int (&kc)[IT], int (&vc)[IT][4]) {
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int t = min(ti * kGroup + it * TL + j, a.T - 1);
+      const int16_t* vix = a.v_idx + (unit * a.T + t) * a.N;
+      kc[it] = LUT ? static_cast<uint16_t>(a.k_idx[(unit * a.T + t) * a.N + min(ck, a.N - 1)]) : 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) vc[it][k] = static_cast<uint16_t>(vix[min(k, a.N - 1)]);
+    }
+  };
+  if (tb + wave < te) load_idx(tb + wave, kci, vci);
   if constexpr (LUT) {
     // the unit's key-logit table into LDS (at most kLutFloats, checked on
     // the host), eight 16-byte loads per thread in flight before any store
@@ -427,26 +446,28 @@ __global__ __launch_bounds__(256) void rvq_decode_kernel(RvqDecArgs a) {
 #pragma unroll
     for (int c = 0; c < 16; ++c) acc[h][c] = 0.0f;
   }
-  const int tb = split * a.tiles_per_split;
-  const int te = min(a.n_tiles, tb + a.tiles_per_split);
   // value rows of up to 4 stages are prefetched one sub-tile ahead when
   // N <= 4 (wave-uniform); larger N rebuilds each sub-tile on its own
   const bool vpre = a.N <= 4;
+  // values: the 4 stages' codeword rows (the lane's 16 channels, two
+  // 16-byte loads each) of sub-tile it + 1 are in flight while sub-tile
+  // it is summed; sub-tile 0's are requested as soon as the indices are in
+  uint4 rows[2][4][2];
+  auto issue_rows = [&](int it, uint4 (&r)[4][2]) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int st = min(k, a.N - 1);
+      const uint32_t ci = min(static_cast<uint32_t>(vci[it][k]), static_cast<uint32_t>(a.Kc - 1));
+      const uint4* row = reinterpret_cast<const uint4*>(a.v_cb + (static_cast<size_t>(st) * a.Kc + ci) * kD + c0);
+      r[k][0] = row[0];
+      r[k][1] = row[1];
+    }
+  };
   for (int ti = tb + wave; ti < te; ti += kDecWaves) {
     float lg[IT][G];
     bool valid[IT];
-    // the tile's indices, every load issued before any is used: lane ck's
-    // key index (stage ck) and the value indices of token j (stages 0..3),
-    // per sub-tile; positions past T read the last token (in bounds)
-    int kci[IT], vci[IT][4];
-#pragma unroll
-    for (int it = 0; it < IT; ++it) {
-      const int t = min(ti * kGroup + it * TL + j, a.T - 1);
-      const int16_t* vix = a.v_idx + (unit * a.T + t) * a.N;
-      if constexpr (LUT) kci[it] = static_cast<uint16_t>(a.k_idx[(unit * a.T + t) * a.N + min(ck, a.N - 1)]);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) vci[it][k] = static_cast<uint16_t>(vix[min(k, a.N - 1)]);
-    }
+    if (vpre) issue_rows(0, rows[0]);
+    if (ti + kDecWaves < te) load_idx(ti + kDecWaves, kcn, vcn);
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
       const int t = ti * kGroup + it * TL + j;
@@ -501,21 +522,6 @@ __global__ __launch_bounds__(256) void rvq_decode_kernel(RvqDecArgs a) {
         m[h] = mnew[h];
       }
     }
-    // values: the 4 stages' codeword rows (the lane's 16 channels, two
-    // 16-byte loads each) of sub-tile it + 1 are in flight while sub-tile
-    // it is summed
-    uint4 rows[2][4][2];
-    auto issue_rows = [&](int it, uint4 (&r)[4][2]) {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int st = min(k, a.N - 1);
-        const uint32_t ci = min(static_cast<uint32_t>(vci[it][k]), static_cast<uint32_t>(a.Kc - 1));
-        const uint4* row = reinterpret_cast<const uint4*>(a.v_cb + (static_cast<size_t>(st) * a.Kc + ci) * kD + c0);
-        r[k][0] = row[0];
-        r[k][1] = row[1];
-      }
-    };
-    if (vpre) issue_rows(0, rows[0]);
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
       if (vpre && it + 1 < IT) issue_rows(it + 1, rows[(it + 1) & 1]);
@@ -529,10 +535,11 @@ __global__ __launch_bounds__(256) void rvq_decode_kernel(RvqDecArgs a) {
           if (k >= a.N) break;
           const uint4 ra = rows[it & 1][k][0], rb = rows[it & 1][k][1];
           const uint32_t w[8] = {ra.x, ra.y, ra.z, ra.w, rb.x, rb.y, rb.z, rb.w};
+          const float one = opaque_const(1.0f);
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
-            vh[2 * i] += h2f(static_cast<uint16_t>(w[i] & 0xFFFFu));
-            vh[2 * i + 1] += h2f(static_cast<uint16_t>(w[i] >> 16));
+            vh[2 * i] = __builtin_fmaf(half_of<0>(w[i]), one, vh[2 * i]);
+            vh[2 * i + 1] = __builtin_fmaf(half_of<1>(w[i]), one, vh[2 * i + 1]);
           }
         }
       } else {
@@ -546,6 +553,12 @@ __global__ __launch_bounds__(256) void rvq_decode_kernel(RvqDecArgs a) {
 #pragma unroll
         for (int c = 0; c < 16; ++c) acc[h][c] = fmaf(p, vh[c], acc[h][c]);
       }
+    }
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      kci[it] = kcn[it];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) vci[it][k] = vcn[it][k];
     }
   }
 #pragma unroll
