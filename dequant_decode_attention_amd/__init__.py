@@ -47,7 +47,8 @@ class KiviCacheStruct(ctypes.Structure):
                 ("T_q", _i), ("R", _i), ("rope_theta", _f),
                 ("k_codes", _vp), ("k_scale", _vp), ("k_zero", _vp),
                 ("v_codes", _vp), ("v_scale", _vp), ("v_zero", _vp),
-                ("k_recent", _vp), ("v_recent", _vp), ("T_cap", _i), ("R_cap", _i)]
+                ("k_recent", _vp), ("v_recent", _vp), ("T_cap", _i), ("R_cap", _i),
+                ("rope_table", _vp)]
 
 
 _SIGS = {
@@ -61,6 +62,8 @@ _SIGS = {
     "decode_attention_noalloc_scratch_bytes": (_sz, []),
     "decode_attention_qkv_partial": (_i, [_vp, ctypes.POINTER(KiviCacheStruct), _f, _vp, _sz, _vp, _vp]),
     "decode_attention_qkv_merge": (_i, [ctypes.POINTER(KiviCacheStruct), _vp, _sz, _vp, _vp]),
+    "kivi_rope_table_words": (_sz, [_i]),
+    "kivi_rope_table": (_i, [_f, _i, _i, _vp, _vp]),
     "kivi_append_workspace_bytes": (_sz, [ctypes.POINTER(KiviCacheStruct), _i]),
     "kivi_append": (_i, [ctypes.POINTER(KiviCacheStruct), _vp, _vp, _i, _i, _vp, _sz, _vp]),
     "zoned_plan_words": (_sz, [_i, _i, _i, _i]),
@@ -153,6 +156,16 @@ def quantize_pack_v(v, bits, out=None):
 
 # ---------------------------------------------------------------- KIVI decode
 
+def kivi_rope_table(rope_theta, d, bits, device):
+    """The in-tile rotation table of a RoPE cache: int32 [kivi_rope_table_words(d)] on device."""
+    n = lib.kivi_rope_table_words(d)
+    if n == 0:
+        raise DqaError("kivi_rope_table", 2)
+    table = torch.empty(n, dtype=torch.int32, device=device)
+    _check("kivi_rope_table", lib.kivi_rope_table(float(rope_theta), d, bits, _ptr(table), _stream(device)))
+    return table
+
+
 class KiviCache:
     """Device tensors of a uniform-layout cache plus its descriptor.
 
@@ -160,12 +173,14 @@ class KiviCache:
     [B, Hkv, T_cap/32, d]; v_scale/v_zero fp16 [B, Hkv, T_cap, d/32];
     k_recent/v_recent fp16 [B, Hkv, R_cap, d] (keys before RoPE) or None.
     The capacities are the tensors' token dimensions; T_q (default T_cap)
-    and R (default R_cap) are the tokens in use.
+    and R (default R_cap) are the tokens in use.  A 2- or 4-bit cache with
+    RoPE builds its in-tile rotation table once (kivi_rope_table) unless
+    rope_table=False.
     """
 
     def __init__(self, Hq, bits, k_codes, k_scale, k_zero, v_codes, v_scale, v_zero,
                  k_recent=None, v_recent=None, rope_theta=0.0, T_q=None, B=None, Hkv=None, d=None,
-                 R=None):
+                 R=None, rope_table=True):
         ref = k_codes if k_codes is not None else k_recent
         self.B = ref.shape[0] if B is None else B
         self.Hkv = ref.shape[1] if Hkv is None else Hkv
@@ -179,6 +194,9 @@ class KiviCache:
                             v_scale=v_scale, v_zero=v_zero, k_recent=k_recent, v_recent=v_recent)
         self.tensors = {k: (None if v is None else v.contiguous()) for k, v in self.tensors.items()}
         self._ws = None
+        self.rope_table = None
+        if rope_table and self.rope_theta > 0 and bits in (2, 4):
+            self.rope_table = kivi_rope_table(self.rope_theta, self.d, bits, ref.device)
 
     def struct(self):
         t = self.tensors
@@ -186,7 +204,8 @@ class KiviCache:
                                self.rope_theta, *[(None if t[n] is None else t[n].data_ptr()) for n in
                                                   ("k_codes", "k_scale", "k_zero", "v_codes",
                                                    "v_scale", "v_zero", "k_recent", "v_recent")],
-                               self.T_cap, self.R_cap)
+                               self.T_cap, self.R_cap,
+                               None if self.rope_table is None else self.rope_table.data_ptr())
 
     def workspace_bytes(self):
         return lib.decode_attention_workspace_bytes(ctypes.byref(self.struct()))

@@ -43,7 +43,20 @@ struct KiviArgs {
   int total_splits;     // splits (partial-state slots) per (batch, KV head)
   TileSplit split;      // tiles -> waves
   float q_scale;        // sm_scale * log2(e): logits in the log2 domain
+  float rope_theta;
+  const uint32_t* rope_table;   // the cache's built in-tile trig table, or null
   double omega[64];     // RoPE frequencies theta^(-2i/d), i < d/2 (host fp64)
+};
+
+// RoPE frequencies omega_i = theta^(-2i/d), i < d/2, in fp64 on the host
+// (zero past d/2); the same values reach every kernel that rotates.
+inline void rope_omega(float theta, int d, double* omega) {
+  for (int i = 0; i < 64; ++i)
+    omega[i] = (theta > 0.0f && i < d / 2) ? std::pow(static_cast<double>(theta), -2.0 * i / d) : 0.0;
+}
+struct RopeOmega {
+  double omega[64];
+  float theta;
 };
 
 // The feature-product decode kernel (2- and 4-bit codes with RoPE; see
@@ -51,6 +64,10 @@ struct KiviArgs {
 int feat_decode_workgroups();
 int feat_recent_weight();
 int launch_feat_decode(const KiviArgs& a, int d, int G, int bits, dim3 grid, hipStream_t s);
+// The in-tile trig table of a cache (kivi_rope_table): its size in uint32
+// words for head dim d, and its build kernel (bits 2 or 4, d 64 or 128).
+size_t feat_rope_table_words(int d);
+int launch_rope_table(float theta, int d, int bits, uint32_t* table, hipStream_t s);
 
 namespace {
 

@@ -183,6 +183,76 @@ constexpr bool operand_order_is_permutation() {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// ----------------------------------------------------- in-tile trig table
+// For the token at offset j = 0..31 of a tile and RoPE pair i: e^{i j w_i}
+// as a head with kTrigHeadBits significant bits plus the tail, both times
+// kTrigScale, packed as fp16 (cos, sin) words at the pair's position in the
+// operand order of its lane group; and e^{i 32 w_i}, the step from one tile
+// start to the next.  e^{i j w} for j = 4a + b is the product of two of 11
+// accurately rounded unit numbers (angle 4a w, a = 1..8, and b w, b = 1..3).
+// The decode kernel builds the table in LDS at its start, or copies it from a
+// table built once per cache by kivi_rope_table (same arithmetic, same bits).
+template <int BITS>
+constexpr int kTrigHeadBits = BITS == 2 ? 9 : 7;
+constexpr float kTrigScale = 32768.0f;   // 2^15
+constexpr uint32_t kRopeTableMagic = 0x52545442u;   // header word 0 of a built table
+// Layout of a built table (uint32 words): header [magic, bits, d, theta bits],
+// then head words [32][NP], tail words [32][NP] (NP = d / 2 pairs, at their
+// operand-order positions), then the steps as float (cos, sin) [NP].
+constexpr int kRopeTableHeader = 4;
+inline size_t rope_table_words(int d) { return kRopeTableHeader + 2 * 32 * (d / 2) + 2 * (d / 2); }
+
+// Builds the table with the NT threads of a workgroup (tid = thread index).
+// base: LDS scratch of 11 * NP float2.  put(j, ps, head, tail) stores token
+// j's words at operand position ps, put_step(i, e^{i 32 w_i}).  Ends with
+// every base read done (a barrier inside, none at the end).
+template <int D, int BITS, int NT, typename Put, typename PutStep>
+__device__ __forceinline__ void build_trig_table(const double* omega, float2 (*base)[D / 2], int tid, Put put,
+                                                 PutStep put_step) {
+  constexpr int NP = D / 2, PPG = NP / 4, EPW = 16 / BITS, HB = kTrigHeadBits<BITS>;
+  for (int e = tid; e < 11 * NP; e += NT) {
+    const int r = e / NP, i = e % NP;
+    float c, s;
+    rope_unit(static_cast<double>(r < 8 ? 4 * (r + 1) : r - 7), omega[i], c, s);
+    base[r][i] = float2{c, s};
+  }
+  __syncthreads();
+  for (int e = tid; e < kGroup * NP; e += NT) {
+    const int j = e / NP, i = e % NP;
+    const int ja = j >> 2, jb = j & 3;
+    const float2 u = ja ? base[ja - 1][i] : float2{1.0f, 0.0f};
+    const float2 v = jb ? base[7 + jb][i] : float2{1.0f, 0.0f};
+    const float c = fmaf(u.x, v.x, -(u.y * v.y)), s = fmaf(u.y, v.x, u.x * v.y);
+    const float ch = trunc_sig(c, HB), sh = trunc_sig(s, HB);
+    const int ps = (i / PPG) * PPG + pos_of<EPW>(i % PPG);
+    put(j, ps, pack_f16(ch * kTrigScale, sh * kTrigScale), pack_f16((c - ch) * kTrigScale, (s - sh) * kTrigScale));
+  }
+  if (tid < NP) put_step(tid, base[7][tid]);
+}
+
+// kivi_rope_table's kernel: one workgroup of 256 threads.
+template <int D, int BITS>
+__global__ __launch_bounds__(256) void rope_table_kernel(RopeOmega w, uint32_t* __restrict__ table) {
+  constexpr int NP = D / 2;
+  __shared__ float2 base[11][NP];
+  uint32_t* const th = table + kRopeTableHeader;
+  uint32_t* const tl = th + kGroup * NP;
+  float2* const st = reinterpret_cast<float2*>(tl + kGroup * NP);
+  build_trig_table<D, BITS, 256>(
+      w.omega, base, static_cast<int>(threadIdx.x),
+      [&](int j, int ps, uint32_t h, uint32_t l) {
+        th[j * NP + ps] = h;
+        tl[j * NP + ps] = l;
+      },
+      [&](int i, float2 v) { st[i] = v; });
+  if (threadIdx.x == 0) {
+    table[0] = kRopeTableMagic;
+    table[1] = BITS;
+    table[2] = D;
+    table[3] = __builtin_bit_cast(uint32_t, w.theta);
+  }
+}
+
 // ----------------------------------------------------------------- kernel
 
 template <int D, int BITS, int G>
@@ -200,7 +270,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kFWavesPerS
   constexpr int BST = KTOT + 8;          // B column stride (halves): columns in different banks
   constexpr int NBC = 2 * G;             // B columns in use (hi, lo per head)
   constexpr int NITEM = G * 4 * KSB;     // per-tile factor items (head, lane group, K-step pair)
-  constexpr int HB = BITS == 2 ? 9 : 7;  // significant bits of a trig head
   constexpr int MB = D / 16;             // channel blocks of the value product
   constexpr int NVG = D / kGroup;        // value groups per token
   constexpr int NCOL = G * NVG;          // value-operand columns in use
@@ -210,7 +279,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kFWavesPerS
   constexpr int VST = 24;                // row stride of the fp16 value staging area (halves)
   constexpr int KSR = D / 32;            // K-steps of a recent tile (channels)
   constexpr int TPR = NP + 4;            // packed trig row (padded: 16 rows start in different banks)
-  constexpr float kTrigScale = 32768.0f; // 2^15
   static_assert(NCOL <= 16, "value-operand columns");
   static_assert(NITEM <= kWave, "one factor item per lane");
   static_assert(G * 4 * KSR <= kWave, "one recent-query item per lane");
@@ -254,6 +322,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kFWavesPerS
   // its recent tiles first, then its run [qb, qb + nq) of quantized tiles.
   const WaveTiles wt = wave_tiles(a.split, split * kFWaves + wave);
   const int qb = wt.qb, nq = wt.nq, r_first = wt.r_first, r_mine = wt.r_mine;
+
 
   // ---- per-tile factor item of this lane: head ih, lane group ig, K-step
   // pair ikb (code K-steps 2 ikb, 2 ikb + 1; zero-point K-step ikb).  Its four
@@ -336,34 +405,53 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kFWavesPerS
     load_scales(qb + 1, s1);
   }
 
-  // ---- trig tables.  e^{i j w} for j = 4a + b is the product of two of 11
-  // accurately rounded unit numbers (angle 4a w, a = 1..8, and b w, b =
-  // 1..3: angle reduced in fp64, sin/cos in fp32); the same pass computes
-  // e^{i t0 w} of this wave's first quantized tile.
-  for (int e = tid; e < 11 * NP; e += 256) {
-    const int r = e / NP, i = e % NP;
-    float c, s;
-    rope_unit(static_cast<double>(r < 8 ? 4 * (r + 1) : r - 7), a.omega[i], c, s);
-    base[r][i] = float2{c, s};
-  }
+  // ---- trig tables (build_trig_table): copied from the cache's built table
+  // when its header matches (bits, d, theta), else built here; and e^{i t0 w}
+  // of this wave's first quantized tile.
   if (lane < NP) {
     float c, s;
     rope_unit(static_cast<double>(qb) * kGroup, a.omega[lane], c, s);
     lds_rot[wave][lane] = float2{c, s};
   }
-  __syncthreads();
-  for (int e = tid; e < kGroup * NP; e += 256) {
-    const int j = e / NP, i = e % NP;
-    const int ja = j >> 2, jb = j & 3;
-    const float2 u = ja ? base[ja - 1][i] : float2{1.0f, 0.0f};
-    const float2 v = jb ? base[7 + jb][i] : float2{1.0f, 0.0f};
-    const float c = fmaf(u.x, v.x, -(u.y * v.y)), s = fmaf(u.y, v.x, u.x * v.y);
-    const float ch = trunc_sig(c, HB), sh = trunc_sig(s, HB);
-    const int ps = (i / PPG) * PPG + pos_of<EPW>(i % PPG);
-    lds_th[j][ps] = pack_f16(ch * kTrigScale, sh * kTrigScale);
-    lds_tl[j][ps] = pack_f16((c - ch) * kTrigScale, (s - sh) * kTrigScale);
+  {
+    // the cache's built trig table (if any): header and contents requested
+    // together, the header checked when they arrive (requesting them at the
+    // kernel's start was measured slower: more registers live across the
+    // tile loads)
+    constexpr int kPieces = (2 * kGroup * NP / 4 + 255) / 256;   // 16-byte pieces per thread
+    bool copy = false;
+    uint4 tv[kPieces];
+    float2 step{1.0f, 0.0f};
+    if (a.rope_table != nullptr) {
+      const uint4 hdr = *reinterpret_cast<const uint4*>(a.rope_table);
+      const uint32_t* const gt = a.rope_table + kRopeTableHeader;
+#pragma unroll
+      for (int k = 0; k < kPieces; ++k)
+        tv[k] = reinterpret_cast<const uint4*>(gt)[min(tid + 256 * k, 2 * kGroup * NP / 4 - 1)];
+      if (tid < NP) step = reinterpret_cast<const float2*>(gt + 2 * kGroup * NP)[tid];
+      copy = hdr.x == kRopeTableMagic && hdr.y == static_cast<uint32_t>(BITS) && hdr.z == static_cast<uint32_t>(D) &&
+             hdr.w == __builtin_bit_cast(uint32_t, a.rope_theta);
+    }
+    if (copy) {
+#pragma unroll
+      for (int k = 0; k < kPieces; ++k) {
+        const int w0 = 4 * (tid + 256 * k);
+        if (w0 < 2 * kGroup * NP) {
+          const int half = w0 / (kGroup * NP), j = (w0 % (kGroup * NP)) / NP, ps = w0 % NP;
+          *reinterpret_cast<uint4*>(half ? &lds_tl[j][ps] : &lds_th[j][ps]) = tv[k];
+        }
+      }
+      if (tid < NP) lds_step[tid] = step;
+    } else {
+      build_trig_table<D, BITS, 256>(
+          a.omega, base, tid,
+          [&](int j, int ps, uint32_t h, uint32_t l) {
+            lds_th[j][ps] = h;
+            lds_tl[j][ps] = l;
+          },
+          [&](int i, float2 v) { lds_step[i] = v; });
+    }
   }
-  if (tid < NP) lds_step[tid] = base[7][tid];
   __syncthreads();
 
   // ---- the lane's trig registers: tokens j(s) (rows of the A operand of
@@ -790,6 +878,22 @@ int launch_feat_g(const KiviArgs& a, int G, dim3 grid, hipStream_t s) {
 
 int feat_decode_workgroups() { return 256 * kFWavesPerSimd; }
 int feat_recent_weight() { return kRecentWeight; }
+
+size_t feat_rope_table_words(int d) { return rope_table_words(d); }
+
+int launch_rope_table(float theta, int d, int bits, uint32_t* table, hipStream_t s) {
+  RopeOmega w;
+  rope_omega(theta, d, w.omega);
+  w.theta = theta;
+  if (d == 128) {
+    if (bits == 2) hipLaunchKernelGGL((rope_table_kernel<128, 2>), dim3(1), dim3(256), 0, s, w, table);
+    else hipLaunchKernelGGL((rope_table_kernel<128, 4>), dim3(1), dim3(256), 0, s, w, table);
+  } else {
+    if (bits == 2) hipLaunchKernelGGL((rope_table_kernel<64, 2>), dim3(1), dim3(256), 0, s, w, table);
+    else hipLaunchKernelGGL((rope_table_kernel<64, 4>), dim3(1), dim3(256), 0, s, w, table);
+  }
+  return hipPeekAtLastError() == hipSuccess ? DQA_OK : DQA_ERR_HIP;
+}
 
 int launch_feat_decode(const KiviArgs& a, int d, int G, int bits, dim3 grid, hipStream_t s) {
   if (d == 128) return bits == 2 ? launch_feat_g<128, 2>(a, G, grid, s) : launch_feat_g<128, 4>(a, G, grid, s);

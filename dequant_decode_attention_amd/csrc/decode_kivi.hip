@@ -570,6 +570,18 @@ void* scratch_address(int dev) {
 
 using namespace dqa;
 
+extern "C" size_t kivi_rope_table_words(int d) {
+  return (d == 64 || d == 128) ? feat_rope_table_words(d) : 0;
+}
+
+extern "C" int kivi_rope_table(float rope_theta, int d, int bits, uint32_t* table, void* stream) {
+  if (!table) return DQA_ERR_NULL;
+  if (!(rope_theta > 0.0f) || (d != 64 && d != 128)) return DQA_ERR_SHAPE;
+  if (bits != 2 && bits != 4) return DQA_ERR_BITS;
+  if (!aligned16(table)) return DQA_ERR_ALIGN;
+  return launch_rope_table(rope_theta, d, bits, table, static_cast<hipStream_t>(stream));
+}
+
 extern "C" size_t decode_attention_workspace_bytes(const dqa_kivi_cache* cache) {
   Plan p;
   if (make_plan(cache, &p) != DQA_OK) return 0;
@@ -596,6 +608,7 @@ int check_decode(const uint16_t* q, const dqa_kivi_cache* c, const void* ws, siz
                      !aligned16(c->v_codes) || !aligned16(c->v_scale) || !aligned16(c->v_zero)))
     return DQA_ERR_ALIGN;
   if (c->R > 0 && (!aligned16(c->k_recent) || !aligned16(c->v_recent))) return DQA_ERR_ALIGN;
+  if (c->rope_table && !aligned16(c->rope_table)) return DQA_ERR_ALIGN;
   return DQA_OK;
 }
 
@@ -633,8 +646,9 @@ extern "C" int decode_attention_qkv_partial(const uint16_t* q, const dqa_kivi_ca
                             static_cast<long long>(p.total) * kWavesPerWG);
   a.q_scale = sm_scale * 1.4426950408889634f;
   const bool rope = c->rope_theta > 0.0f;
-  for (int i = 0; i < 64; ++i)
-    a.omega[i] = (rope && i < c->d / 2) ? std::pow(static_cast<double>(c->rope_theta), -2.0 * i / c->d) : 0.0;
+  rope_omega(c->rope_theta, c->d, a.omega);
+  a.rope_theta = c->rope_theta;
+  a.rope_table = rope ? c->rope_table : nullptr;
   const dim3 grid(p.total, c->Hkv, c->B);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (use_feat(c->bits, rope)) {

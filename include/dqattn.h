@@ -65,7 +65,9 @@ enum {
 const char* dqa_status_string(int status);
 
 /* Version of this interface (increments on any signature or layout change). */
-int dqa_abi_version(void);  /* 10: decode workspaces hold merge counters
+int dqa_abi_version(void);  /* 11: dqa_kivi_cache ends with an optional
+                              rope_table; kivi_rope_table(_words);
+                              10: decode workspaces hold merge counters
                               and must be zeroed before first use; the
                               split kernel merges its splits itself
                               (decode_attention_qkv_merge enqueues
@@ -151,7 +153,32 @@ typedef struct dqa_kivi_cache {
                           /* with T_cap >= T_q, a multiple of 32; 0 means T_q   */
   int R_cap;              /* rows of the recent buffers per (batch, KV head),   */
                           /* >= R; 0 means R                                    */
+  const uint32_t* rope_table; /* optional, may be NULL: the in-tile rotation    */
+                          /* table kivi_rope_table built for this rope_theta, */
+                          /* d and bits (2-/4-bit caches with RoPE); the      */
+                          /* decode kernel copies it instead of evaluating   */
+                          /* the rotations itself (same values).  A table    */
+                          /* whose header names another theta, d or bits is  */
+                          /* ignored.  kivi_rope_table_words(d) words,       */
+                          /* 16-byte aligned.                                */
 } dqa_kivi_cache;
+
+/* In-tile rotation table of a RoPE cache ([P1 para 7]: keys are rotated
+ * after dequantization).  For the token at offset j = 0..31 of a 32-token
+ * tile and channel pair i it holds e^{i j w_i} (w_i = theta^(-2i/d)) in the
+ * split fp16 form the 2- and 4-bit decode kernel multiplies codes with, and
+ * e^{i 32 w_i}; the values depend on theta, d and bits only, so a cache
+ * builds its table once.
+ * kivi_rope_table_words: uint32 words of the table for head dim d (0 unless
+ * d is 64 or 128).
+ * kivi_rope_table: writes the table (device, kivi_rope_table_words(d) words,
+ * 16-byte aligned); enqueues one kernel.  rope_theta > 0, d in {64, 128}
+ * (else DQA_ERR_SHAPE), bits in {2, 4} (else DQA_ERR_BITS).
+ * Errors: DQA_ERR_NULL, DQA_ERR_SHAPE, DQA_ERR_BITS, DQA_ERR_ALIGN,
+ * DQA_ERR_HIP. */
+size_t kivi_rope_table_words(int d);
+int kivi_rope_table(float rope_theta, int d, int bits, uint32_t* table,
+                    void* stream);
 
 /* Bytes of workspace decode_attention_qkv needs for this cache shape
  * (0 if the shape is invalid; at least 64 KB otherwise).  The workspace

@@ -61,7 +61,7 @@ def oracle_cache(inp, bits, Hq, rope_theta):
                 k_recent=inp["k_recent"], v_recent=inp["v_recent"])
 
 
-def gpu_cache(dqa, inp, bits, Hq, rope_theta, device="cuda:0"):
+def gpu_cache(dqa, inp, bits, Hq, rope_theta, device="cuda:0", rope_table=True):
     """The library's quantize + pack of the same inputs, as a KiviCache."""
     B, Hkv, T_q, d = inp["k"].shape
     R = inp["k_recent"].shape[2]
@@ -73,4 +73,4 @@ def gpu_cache(dqa, inp, bits, Hq, rope_theta, device="cuda:0"):
     kr = dev(inp["k_recent"], device) if R > 0 else None
     vr = dev(inp["v_recent"], device) if R > 0 else None
     return dqa.KiviCache(Hq, bits, kc, ks, kz, vc, vs, vz, kr, vr, rope_theta=rope_theta,
-                         T_q=T_q, B=B, Hkv=Hkv, d=d)
+                         T_q=T_q, B=B, Hkv=Hkv, d=d, rope_table=rope_table)

@@ -69,7 +69,8 @@ def test_quantize_validation(fn):
 def _cache(**kw):
     base = dict(B=2, Hq=8, Hkv=2, d=128, bits=2, T_q=64, R=16, rope_theta=0.0,
                 k_codes=0x1000, k_scale=0x1000, k_zero=0x1000, v_codes=0x1000,
-                v_scale=0x1000, v_zero=0x1000, k_recent=0x1000, v_recent=0x1000, T_cap=0, R_cap=0)
+                v_scale=0x1000, v_zero=0x1000, k_recent=0x1000, v_recent=0x1000, T_cap=0, R_cap=0,
+                rope_table=None)
     base.update(kw)
     return KiviCacheStruct(*[base[n] for n, _ in KiviCacheStruct._fields_])
 
@@ -100,8 +101,8 @@ def test_decode_workspace_query_and_validation():
     odd = ctypes.c_void_p(0x1008)
     assert lib.decode_attention_qkv(odd, ctypes.byref(c), 0.1, FAKE, 1 << 30, FAKE, None) == 8
     assert lib.decode_attention_qkv(FAKE, ctypes.byref(c), 0.1, FAKE, 1 << 30, odd, None) == 8
-    for name in ["k_codes", "v_scale", "v_recent"]:
-        c2 = _cache(**{name: 0x1004})
+    for name in ["k_codes", "v_scale", "v_recent", "rope_table"]:
+        c2 = _cache(**{name: 0x1004}, rope_theta=1e4)
         assert lib.decode_attention_qkv(FAKE, ctypes.byref(c2), 0.1, FAKE, 1 << 30, FAKE, None) == 8
     # the recent-zone pointers are not used (nor checked) without recent tokens
     c3 = _cache(R=0, k_recent=0x1002, v_recent=None)
@@ -122,6 +123,20 @@ def test_decode_workspace_query_and_validation():
     assert lib.decode_attention_qkv_partial(None, ctypes.byref(c), 0.1, FAKE, 1 << 30, FAKE, None) == 1
     assert lib.decode_attention_workspace_bytes(ctypes.byref(_cache(d=80))) == 0
     assert lib.decode_attention_workspace_bytes(None) == 0
+
+
+def test_rope_table_validation():
+    assert lib.kivi_rope_table_words(128) == 4 + 2 * 32 * 64 + 2 * 64
+    assert lib.kivi_rope_table_words(64) == 4 + 2 * 32 * 32 + 2 * 32
+    assert lib.kivi_rope_table_words(96) == 0
+    f = lib.kivi_rope_table
+    assert f(1e4, 128, 2, None, None) == 1
+    assert f(0.0, 128, 2, FAKE, None) == 2          # no RoPE
+    assert f(-1.0, 128, 2, FAKE, None) == 2
+    assert f(1e4, 80, 2, FAKE, None) == 2
+    assert f(1e4, 128, 8, FAKE, None) == 3          # the table serves the 2- and 4-bit kernel
+    assert f(1e4, 128, 3, FAKE, None) == 3
+    assert f(1e4, 128, 4, ctypes.c_void_p(0x1004), None) == 8
 
 
 def test_noalloc_decode_validation():
@@ -318,7 +333,7 @@ def test_rvq_validation_and_workspace():
 
 def test_kivi_append_validation():
     """Argument checks of the streaming append (all fail before any launch)."""
-    assert lib.dqa_abi_version() == 10
+    assert lib.dqa_abi_version() == 11
     c = _cache(T_cap=128, R_cap=128)
     # staging holds the recent and the new rows of K and V
     assert lib.kivi_append_workspace_bytes(ctypes.byref(c), 20) == 2 * 2 * 2 * (16 + 20) * 128 * 2

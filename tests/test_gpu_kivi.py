@@ -170,6 +170,38 @@ def test_decode_attention_parity(dqa, case):
     assert np.array_equal(host(out2), got)
 
 
+@pytest.mark.parametrize("bits,d", [(2, 128), (4, 128), (2, 64), (4, 64)])
+def test_rope_table_copy_equals_in_kernel_build(dqa, bits, d):
+    """A cache's built in-tile rotation table (kivi_rope_table) gives outputs
+    bit-identical to the kernel's own evaluation of the rotations (same
+    arithmetic), and a table built for another theta, or another code width,
+    is ignored (its header does not match)."""
+    B, Hq, Hkv, T_q, R, rope = 2, 8, 2, 320, 37, 500000.0
+    inp = kivi_inputs(B, Hq, Hkv, d, T_q, R, seed=T_q + R + d, outliers=("lognormal", 0.04, 3.0, 1.0))
+    scale = 1.0 / math.sqrt(d)
+    say("rope table", bits, d)
+    with_table = gpu_cache(dqa, inp, bits, Hq, rope)
+    assert with_table.rope_table is not None
+    built = gpu_cache(dqa, inp, bits, Hq, rope, rope_table=False)
+    assert built.rope_table is None
+    q = dev(inp["q"])
+    a = host(dqa.decode_attention_qkv(q, with_table, scale))
+    b = host(dqa.decode_attention_qkv(q, built, scale))
+    assert np.array_equal(a, b)
+    ref = oracle.kivi_decode_attention(inp["q"], oracle_cache(inp, bits, Hq, rope), scale)
+    check_attention(a, ref, TOL, f"rope table {bits} {d}")
+    # the kernel reads the table it is given: contents altered behind a
+    # valid header change the output
+    altered = with_table.rope_table.clone()
+    altered[4:] = 0
+    with_table.rope_table = altered
+    assert not np.array_equal(host(dqa.decode_attention_qkv(q, with_table, scale)), b)
+    for other in (dqa.kivi_rope_table(1e4, d, bits, q.device), dqa.kivi_rope_table(rope, d, 6 - bits, q.device)):
+        with_table.rope_table = other
+        c = host(dqa.decode_attention_qkv(q, with_table, scale))
+        assert np.array_equal(c, b)
+
+
 @pytest.mark.parametrize("T_q,R", [(4096, 77), (64, 5)])
 def test_decode_two_phase_equals_one_call(dqa, T_q, R):
     """decode_attention_qkv is exactly _partial then _merge (bit-identical),
