@@ -145,12 +145,28 @@ def cpu_baseline(inp, cfg, bits, scale, budget_s=10.0):
 MFMA_FP16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 matrix peak, published
 
 
+WARM_S = 0.3   # seconds of untimed work before each timed region
+
+
+def _warm(torch, fn, n, seconds=WARM_S):
+    """n untimed calls of fn(i), then more until `seconds` of wall time have
+    passed: the GPU's clocks ramp up over the first tens of milliseconds of
+    sustained work (a decode step measured 64.8 us at first, 56.5 us in
+    steady state), and a few calls are over before that."""
+    t0 = time.perf_counter()
+    i = 0
+    while i < n or time.perf_counter() - t0 < seconds:
+        fn(i)
+        i += 1
+        if i % 64 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+
 def _event_ms(torch, fn, iters, warmup=3):
     """Average duration of fn() over iters calls, HIP events on the current
-    stream (fn enqueues work only)."""
-    for _ in range(warmup):
-        fn(0)
-    torch.cuda.synchronize()
+    stream (fn enqueues work only), after the warm-up of _warm."""
+    _warm(torch, fn, warmup)
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
@@ -394,9 +410,7 @@ def time_decode(dqa, torch, dev, cfg, bits, replicas, steps, warmup, inp=None):
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     res = {}
     for name, fn in (("step_ms", step), ("kernel_ms_back_to_back", split_only)):
-        for i in range(warmup):
-            fn(i)
-        torch.cuda.synchronize()
+        _warm(torch, fn, warmup)
         e0.record(stream)
         for i in range(steps):
             fn(i)
@@ -408,9 +422,7 @@ def time_decode(dqa, torch, dev, cfg, bits, replicas, steps, warmup, inp=None):
     # kernel trace does (back to back, a launch's last workgroups overlap the
     # next launch's first ones)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for i in range(warmup):
-        split_only(i)
-    torch.cuda.synchronize()
+    _warm(torch, split_only, warmup)
     for i, (a, b) in enumerate(evs):
         a.record(stream)
         split_only(i)
