@@ -32,8 +32,9 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float float4v __attribute__((ext_vector_type(4)));
 
 constexpr int kD = 128;
-constexpr int kEncRows = 256;        // vectors per workgroup
-constexpr int kEncWaves = 8;         // 32 rows (2 MFMA row blocks) per wave
+constexpr int kEncMB = 2;            // MFMA row blocks (16 vectors each) per wave
+constexpr int kEncWaves = 8;         // waves per workgroup
+constexpr int kEncRows = 16 * kEncMB * kEncWaves;   // vectors per workgroup
 constexpr int kTileCW = 64;          // codewords per LDS tile
 constexpr int kRowPad = kD + 8;      // LDS row stride in halves (bank spread)
 constexpr int kMaxStages = 8;        // codebooks per vector at most
@@ -61,15 +62,20 @@ __device__ __forceinline__ void split_neg2(const float* r, half8& hi, half8& lo)
   }
 }
 
-__global__ __launch_bounds__(512) void rvq_encode_kernel(const uint16_t* __restrict__ x, int64_t n,
+template <int MB, int NW>
+__global__ __launch_bounds__(NW * 64) void rvq_encode_kernel(const uint16_t* __restrict__ x, int64_t n,
                                                          const uint16_t* __restrict__ cbs,
                                                          const float* __restrict__ norms, int N,
                                                          int Kc, int16_t* __restrict__ idx_out) {
   __shared__ __attribute__((aligned(16))) _Float16 lds_cb[2][kTileCW][kRowPad];
-  __shared__ int16_t lds_idx[kEncWaves][kMaxStages][32];   // chosen indices, per stage
+  constexpr int RW = 16 * MB;          // vectors per wave
+  constexpr int NT = NW * 64;          // threads
+  constexpr int CPT = kTileCW * kD / 8 / NT;   // 16-byte chunks of a codeword tile per thread
+  static_assert(CPT * NT == kTileCW * kD / 8, "a tile's chunks split evenly over the threads");
+  __shared__ int16_t lds_idx[NW][kMaxStages][RW];   // chosen indices, per stage
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
-  const int64_t row_base = static_cast<int64_t>(blockIdx.x) * kEncRows + wave * 32;
+  const int64_t row_base = static_cast<int64_t>(blockIdx.x) * (NW * RW) + wave * RW;
 
   // The residual of stage s is rebuilt at the start of the stage from x and
   // the codewords chosen at stages 0..s-1, subtracted in stage order -- the
@@ -81,20 +87,19 @@ __global__ __launch_bounds__(512) void rvq_encode_kernel(const uint16_t* __restr
   for (int s = 0; s < N; ++s) {
     const uint16_t* cb = cbs + static_cast<size_t>(s) * Kc * kD;
     const float* nrm = norms + static_cast<size_t>(s) * Kc;
-    half8 ahi[2][4], alo[2][4];
+    half8 ahi[MB][4], alo[MB][4];
     {
       // all of a stage's loads of x (or of one earlier stage's codewords)
       // are issued together: one memory round trip per earlier stage
-      float r[2][4][8];
-      auto add_chunks = [&](const uint16_t* row0, const uint16_t* row1, bool subtract) {
-        uint4 u[2][4];
+      float r[MB][4][8];
+      auto add_chunks = [&](const uint16_t* const (&rows)[MB], bool subtract) {
+        uint4 u[MB][4];
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          u[0][ks] = *reinterpret_cast<const uint4*>(row0 + 32 * ks + 8 * grp);
-          u[1][ks] = *reinterpret_cast<const uint4*>(row1 + 32 * ks + 8 * grp);
-        }
+        for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+          for (int ks = 0; ks < 4; ++ks) u[mb][ks] = *reinterpret_cast<const uint4*>(rows[mb] + 32 * ks + 8 * grp);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
           for (int ks = 0; ks < 4; ++ks) {
             const uint32_t w[4] = {u[mb][ks].x, u[mb][ks].y, u[mb][ks].z, u[mb][ks].w};
@@ -107,10 +112,16 @@ __global__ __launch_bounds__(512) void rvq_encode_kernel(const uint16_t* __restr
       };
       // rows past the end of x read row 0 and are zeroed (their indices are
       // never stored)
-      const bool valid[2] = {row_base + col < n, row_base + 16 + col < n};
-      add_chunks(x + (valid[0] ? row_base + col : 0) * kD, x + (valid[1] ? row_base + 16 + col : 0) * kD, false);
+      bool valid[MB];
+      const uint16_t* xr[MB];
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < MB; ++mb) {
+        valid[mb] = row_base + 16 * mb + col < n;
+        xr[mb] = x + (valid[mb] ? row_base + 16 * mb + col : 0) * kD;
+      }
+      add_chunks(xr, false);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
         if (!valid[mb])
 #pragma unroll
           for (int ks = 0; ks < 4; ++ks)
@@ -118,42 +129,54 @@ __global__ __launch_bounds__(512) void rvq_encode_kernel(const uint16_t* __restr
             for (int j = 0; j < 8; ++j) r[mb][ks][j] = 0.0f;
       for (int sp = 0; sp < s; ++sp) {
         const uint16_t* cbp = cbs + static_cast<size_t>(sp) * Kc * kD;
-        add_chunks(cbp + static_cast<size_t>(lds_idx[wave][sp][col]) * kD,
-                   cbp + static_cast<size_t>(lds_idx[wave][sp][16 + col]) * kD, true);
+        const uint16_t* cr[MB];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) cr[mb] = cbp + static_cast<size_t>(lds_idx[wave][sp][16 * mb + col]) * kD;
+        add_chunks(cr, true);
       }
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) split_neg2(r[mb][ks], ahi[mb][ks], alo[mb][ks]);
     }
-    float bestk[2][4];
-    int besti[2][4];
+    float bestk[MB][4];
+    int besti[MB][4];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         bestk[mb][r] = INFINITY;
         besti[mb][r] = 0;
       }
 
-    // codeword tiles: thread tid moves 16-byte chunks 2*tid and 2*tid+1 of
-    // a 64-codeword tile (global -> registers -> LDS buffer); the tile after
-    // next is in flight while the current tile is consumed.  The norms |c|^2
-    // of the lane's 4 codeword columns come straight from global memory,
-    // one tile ahead.
-    const int ch0 = 2 * tid, ch1 = 2 * tid + 1;
-    auto gchunk = [&](int t, int c) {
-      return *reinterpret_cast<const uint4*>(cb + (static_cast<size_t>(t) * kTileCW + c / 16) * kD + (c % 16) * 8);
+    // codeword tiles: thread tid moves 16-byte chunks CPT*tid .. CPT*tid +
+    // CPT-1 of a 64-codeword tile (global -> registers -> LDS buffer); the
+    // tile after next is in flight while the current tile is consumed.  The
+    // norms |c|^2 of the lane's 4 codeword columns come straight from global
+    // memory, one tile ahead.
+    auto gchunks = [&](int t, uint4 (&u)[CPT]) {
+#pragma unroll
+      for (int k = 0; k < CPT; ++k) {
+        const int c = CPT * tid + k;
+        u[k] = *reinterpret_cast<const uint4*>(cb + (static_cast<size_t>(t) * kTileCW + c / 16) * kD + (c % 16) * 8);
+      }
     };
-    auto lstore = [&](int buf, uint4 u0, uint4 u1) {
-      *reinterpret_cast<uint4*>(&lds_cb[buf][ch0 / 16][(ch0 % 16) * 8]) = u0;
-      *reinterpret_cast<uint4*>(&lds_cb[buf][ch1 / 16][(ch1 % 16) * 8]) = u1;
+    auto lstore = [&](int buf, const uint4 (&u)[CPT]) {
+#pragma unroll
+      for (int k = 0; k < CPT; ++k) {
+        const int c = CPT * tid + k;
+        *reinterpret_cast<uint4*>(&lds_cb[buf][c / 16][(c % 16) * 8]) = u[k];
+      }
     };
     auto gnorms = [&](int t, float (&nv)[4]) {
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) nv[nb] = nrm[t * kTileCW + 16 * nb + col];
     };
-    lstore(0, gchunk(0, ch0), gchunk(0, ch1));
+    {
+      uint4 u[CPT];
+      gchunks(0, u);
+      lstore(0, u);
+    }
     __syncthreads();
     // A codeword tile is consumed in two halves of 32 codewords (4 output
     // blocks: 2 row blocks x 2 codeword blocks).  Keys are |c|^2 - 2 r.c,
@@ -170,40 +193,40 @@ __global__ __launch_bounds__(512) void rvq_encode_kernel(const uint16_t* __restr
         for (int ks = 0; ks < 4; ++ks)
           bf[nh][ks] = *reinterpret_cast<const half8*>(&lds_cb[buf][16 * (2 * h + nh) + col][32 * ks + 8 * grp]);
     };
-    auto init_acc = [&](float4v (&acc)[2][2], const float (&nv)[4], int h) {
+    auto init_acc = [&](float4v (&acc)[MB][2], const float (&nv)[4], int h) {
 #pragma unroll
       for (int nh = 0; nh < 2; ++nh)
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
+        for (int mb = 0; mb < MB; ++mb) {
           const float v = nv[2 * h + nh];
           acc[mb][nh] = float4v{v, v, v, v};
         }
     };
-    auto products = [&](float4v (&acc)[2][2], const half8 (&bf)[2][4], auto lo_tag) {
+    auto products = [&](float4v (&acc)[MB][2], const half8 (&bf)[2][4], auto lo_tag) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
         for (int nh = 0; nh < 2; ++nh)
 #pragma unroll
-          for (int mb = 0; mb < 2; ++mb)
+          for (int mb = 0; mb < MB; ++mb)
             acc[mb][nh] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[mb][ks], bf[nh][ks], acc[mb][nh], 0, 0, 0);
         if constexpr (decltype(lo_tag)::value) {
 #pragma unroll
           for (int nh = 0; nh < 2; ++nh)
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
+            for (int mb = 0; mb < MB; ++mb)
               acc[mb][nh] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[mb][ks], bf[nh][ks], acc[mb][nh], 0, 0, 0);
         }
       }
     };
     // codewords visited in increasing index order per (row, lane): strict <
     // keeps the lowest index of equal keys
-    auto running_min = [&](const float4v (&acc)[2][2], int cw0) {
+    auto running_min = [&](const float4v (&acc)[MB][2], int cw0) {
 #pragma unroll
       for (int nh = 0; nh < 2; ++nh) {
         const int cw = cw0 + 16 * nh + col;
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+        for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const float key = acc[mb][nh][r];
@@ -215,14 +238,15 @@ __global__ __launch_bounds__(512) void rvq_encode_kernel(const uint16_t* __restr
     };
     auto tiles = [&](auto lo_tag) {
       half8 bf0[2][4], bf1[2][4];
-      float4v acc0[2][2], acc1[2][2];
+      float4v acc0[MB][2], acc1[MB][2];
       float nv[4];
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int nh = 0; nh < 2; ++nh) acc1[mb][nh] = float4v{INFINITY, INFINITY, INFINITY, INFINITY};
       gnorms(0, nv);
-      uint4 u0 = gchunk(min(1, n_tiles - 1), ch0), u1 = gchunk(min(1, n_tiles - 1), ch1);
+      uint4 u[CPT];
+      gchunks(min(1, n_tiles - 1), u);
       read_half(bf0, 0, 0);
       for (int t = 0; t < n_tiles; ++t) {
         const int buf = t & 1;
@@ -232,9 +256,8 @@ __global__ __launch_bounds__(512) void rvq_encode_kernel(const uint16_t* __restr
         products(acc0, bf0, lo_tag);
         // before tile 0, acc1 holds +inf: no update
         running_min(acc1, (t - 1) * kTileCW + 32);
-        lstore(buf ^ 1, u0, u1);                   // tile t+1 (the final tile rewrites a dead buffer)
-        u0 = gchunk(t2, ch0);
-        u1 = gchunk(t2, ch1);
+        lstore(buf ^ 1, u);                        // tile t+1 (the final tile rewrites a dead buffer)
+        gchunks(t2, u);
         init_acc(acc1, nv, 1);
         gnorms(tn, nv);
         products(acc1, bf1, lo_tag);
@@ -249,7 +272,7 @@ __global__ __launch_bounds__(512) void rvq_encode_kernel(const uint16_t* __restr
 
     // lexicographic (key, index) minimum across the 16 lanes of a row group
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float k = bestk[mb][r];
@@ -267,7 +290,7 @@ __global__ __launch_bounds__(512) void rvq_encode_kernel(const uint16_t* __restr
       }
     if (col == 0) {
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) lds_idx[wave][s][16 * mb + 4 * grp + r] = static_cast<int16_t>(besti[mb][r]);
     }
@@ -277,8 +300,8 @@ __global__ __launch_bounds__(512) void rvq_encode_kernel(const uint16_t* __restr
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
-  // lane l < 32 stores the N indices of row row_base + l
-  if (lane < 32 && row_base + lane < n) {
+  // lane l < RW stores the N indices of row row_base + l
+  if (lane < RW && row_base + lane < n) {
     int16_t* dst = idx_out + (row_base + lane) * N;
     for (int s = 0; s < N; ++s) dst[s] = lds_idx[wave][s][lane];
   }
@@ -637,7 +660,7 @@ extern "C" int rvq_encode(const uint16_t* x, int64_t n, int d, const uint16_t* c
   hipLaunchKernelGGL(rvq_norms_kernel, dim3(static_cast<unsigned>((n_cw + 255) / 256)), dim3(256), 0, s,
                      codebooks, n_cw, norms);
   DQA_CHECK_LAUNCH();
-  hipLaunchKernelGGL(rvq_encode_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kEncWaves * 64), 0, s,
+  hipLaunchKernelGGL((rvq_encode_kernel<kEncMB, kEncWaves>), dim3(static_cast<unsigned>(blocks)), dim3(kEncWaves * 64), 0, s,
                      x, n, codebooks, norms, N, Kc, idx);
   DQA_CHECK_LAUNCH();
   return DQA_OK;
