@@ -383,6 +383,12 @@ def rvq_decode_attention(q, k_idx, v_idx, k_codebooks, v_codebooks, sm_scale, ou
     B, Hq, d = q.shape
     _, Hkv, T, N = k_idx.shape
     Kc = k_codebooks.shape[1]
+    if tuple(k_codebooks.shape) != (N, Kc, d) or tuple(v_codebooks.shape) != (N, Kc, d):
+        raise ValueError(f"codebooks must both be [N={N}, Kc, d={d}], got {tuple(k_codebooks.shape)} "
+                         f"and {tuple(v_codebooks.shape)}")
+    if tuple(k_idx.shape) != (B, k_idx.shape[1], k_idx.shape[2], N) or tuple(v_idx.shape) != tuple(k_idx.shape):
+        raise ValueError(f"k_idx and v_idx must both be [B, Hkv, T, N], got {tuple(k_idx.shape)} "
+                         f"and {tuple(v_idx.shape)}")
     k_idx, v_idx = k_idx.contiguous(), v_idx.contiguous()
     if out is None:
         out = torch.empty(q.shape, dtype=torch.float32, device=q.device)

@@ -8,7 +8,8 @@
 // last among the splits of a (batch, KV head) -- found with one counter per
 // (batch, KV head), incremented once per workgroup -- merges all splits in
 // split order, so the result does not depend on scheduling, and sets the
-// counter back to zero for the next call.
+// counter back to zero for the next call.  (write_split_state_flagged finds
+// a merging workgroup with per-split flags instead.)
 //
 // The L2 caches are private to each XCD, and a device-scope release fence
 // (an L2 write-back) in every workgroup would cost more than the decode
@@ -47,18 +48,14 @@ inline float* merge_partials(void* ws, size_t units) {
 }
 
 // Combine the NW wave states of a workgroup (LDS: lm, ll [NW][G], lo
-// [NW][G][D], lo 16-byte aligned).  With a single split: the normalized output
-// out[b][kvh * G + h][c].  Otherwise: split `slot`'s partial state, and if
-// this workgroup is the last of its (batch, KV head) to finish, the merge of
-// all splits into out (lo is reused as staging for the splits' m and l).
-// Called by every thread of the workgroup.
+// [NW][G][D], lo 16-byte aligned).  With a single split: the normalized
+// output out[b][kvh * G + h][c], and false.  Otherwise: split `slot`'s
+// partial state (device-scope write-through stores, each wave waits for
+// its own), and true.  Called by every thread of the workgroup.
 template <int D, int G, int NW>
-__device__ __forceinline__ void write_split_state(float* partials, uint32_t* counters, float* out, int Hq,
-                                                  size_t unit, int b, int kvh, int slot, int total_splits,
-                                                  const float (*lm)[G], const float (*ll)[G],
-                                                  float (*lo)[G][D]) {
-  static_assert(2 * kMaxSplitsMerge * G <= NW * G * D, "m and l of every split fit the output staging");
-  __shared__ int s_last;
+__device__ __forceinline__ bool store_split_state(float* partials, float* out, int Hq, size_t unit, int b, int kvh,
+                                                  int slot, int total_splits, const float (*lm)[G],
+                                                  const float (*ll)[G], const float (*lo)[G][D]) {
   float* const part = partials + (unit * total_splits + slot) * G * (D + 2);
   for (int e = threadIdx.x; e < G * D; e += blockDim.x) {
     const int h = e / D, c = e % D;
@@ -82,25 +79,27 @@ __device__ __forceinline__ void write_split_state(float* partials, uint32_t* cou
       __hip_atomic_store(part + h * (D + 2) + 2 + c, O, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-  if (total_splits == 1) return;
-  // every wave's partial-state stores have completed before the barrier
+  if (total_splits == 1) return false;
+  // every wave's partial-state stores have completed before the caller's
+  // workgroup barrier
   __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t done = __hip_atomic_fetch_add(counters + unit, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = done == static_cast<uint32_t>(total_splits - 1);
-  }
-  __syncthreads();
-  if (!s_last) return;
+  return true;
+}
 
-  // ---- the last workgroup: merge every split in split order.  Every
-  // phase has a fixed shape (no loop over the splits with a memory or LDS
-  // round trip per split): the output values of the splits are loaded
-  // kChunk splits at a time with all loads of a chunk in flight (the first
-  // chunk together with the splits' m and l); m and l are staged head-major
-  // in LDS (rows of kMaxSplitsMerge, -inf / 0 past the last split); one wave
-  // forms each head's maximum M; the weights 2^(m_k - M) replace m; each
-  // output then reads its head's weights and l values kChunk splits at a time.
+// Merge every split of a (batch, KV head) in split order into out (lo is
+// reused as staging for the splits' m and l).  Every phase has a fixed
+// shape (no loop over the splits with a memory or LDS round trip per
+// split): the output values of the splits are loaded kChunk splits at a time
+// with all loads of a chunk in flight (the first chunk together with the
+// splits' m and l); m and l are staged head-major in LDS (rows of
+// kMaxSplitsMerge, -inf / 0 past the last split); one wave forms each head's
+// maximum M; the weights 2^(m_k - M) replace m; each output then reads its
+// head's weights and l values kChunk splits at a time.  Called by every
+// thread of the workgroup.
+template <int D, int G, int NW>
+__device__ __forceinline__ void merge_splits(const float* partials, float* out, int Hq, size_t unit, int b, int kvh,
+                                             int total_splits, float (*lo)[G][D]) {
+  static_assert(2 * kMaxSplitsMerge * G <= NW * G * D, "m and l of every split fit the output staging");
   constexpr int kChunk = 32;
   constexpr int S = kMaxSplitsMerge;
   constexpr int kPer = (G * D + NW * 64 - 1) / (NW * 64);   // outputs per thread
@@ -192,7 +191,75 @@ __device__ __forceinline__ void write_split_state(float* partials, uint32_t* cou
     const int h = e / D, c = e % D;
     out[(static_cast<size_t>(b) * Hq + kvh * G + h) * D + c] = (Lr[r] > 0.0f) ? Or[r] / Lr[r] : 0.0f;
   }
+}
+
+
+// The partial state of split `slot` (store_split_state), and the merge of
+// all splits (merge_splits) by the workgroup that finishes last among the
+// splits of its (batch, KV head), found with one counter per (batch, KV
+// head) that every workgroup increments once; that workgroup sets the
+// counter back to zero.  Called by every thread of the workgroup.
+template <int D, int G, int NW>
+__device__ __forceinline__ void write_split_state(float* partials, uint32_t* counters, float* out, int Hq,
+                                                  size_t unit, int b, int kvh, int slot, int total_splits,
+                                                  const float (*lm)[G], const float (*ll)[G],
+                                                  float (*lo)[G][D]) {
+  __shared__ int s_last;
+  if (!store_split_state<D, G, NW>(partials, out, Hq, unit, b, kvh, slot, total_splits, lm, ll, lo)) return;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t done = __hip_atomic_fetch_add(counters + unit, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = done == static_cast<uint32_t>(total_splits - 1);
+  }
+  __syncthreads();
+  if (!s_last) return;
+  merge_splits<D, G, NW>(partials, out, Hq, unit, b, kvh, total_splits, lo);
   if (threadIdx.x == 0) __hip_atomic_store(counters + unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// As write_split_state, with per-split flags in place of the counter: the
+// device-scope read-modify-writes of many workgroups on one counter are
+// carried out one after another, so that the last of 32 splits learns that
+// it is last several microseconds after its partial state is stored.  Each
+// split stores `epoch` (this call's value, one more than the previous
+// call's) into flags[slot] once its partial state has completed, then reads
+// every split's flag; a workgroup that finds them all equal to epoch merges.
+// At least one does (of the last two to store their flags, the second
+// reads the first one's flag after that store has completed), and several
+// may: the merge reads the same states in the same order, so they write the
+// same values.  A merging workgroup (or the only split) then stores epoch
+// into *epoch_word, which the next call reads at its start; every split of
+// this call has read it before storing its flag.  flags and *epoch_word
+// start at zero.  Called by every thread of the workgroup.
+template <int D, int G, int NW>
+__device__ __forceinline__ void write_split_state_flagged(float* partials, uint32_t* flags, uint32_t* epoch_word,
+                                                          uint32_t epoch, float* out, int Hq, size_t unit, int b,
+                                                          int kvh, int slot, int total_splits,
+                                                          const float (*lm)[G], const float (*ll)[G],
+                                                          float (*lo)[G][D]) {
+  __shared__ int s_merge;
+  if (!store_split_state<D, G, NW>(partials, out, Hq, unit, b, kvh, slot, total_splits, lm, ll, lo)) {
+    if (threadIdx.x == 0) __hip_atomic_store(epoch_word, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    if (lane == 0) __hip_atomic_store(flags + slot, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0);
+    bool missing = false;
+#pragma unroll
+    for (int k = 0; k < kMaxSplitsMerge / 64; ++k) {
+      const int i = lane + 64 * k;
+      if (i < total_splits && i != slot)
+        missing |= __hip_atomic_load(flags + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != epoch;
+    }
+    if (lane == 0) s_merge = __builtin_amdgcn_ballot_w64(missing) == 0;
+  }
+  __syncthreads();
+  if (!s_merge) return;
+  merge_splits<D, G, NW>(partials, out, Hq, unit, b, kvh, total_splits, lo);
+  if (threadIdx.x == 0) __hip_atomic_store(epoch_word, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Workspace bytes of the merge: the counters, then the partial states of

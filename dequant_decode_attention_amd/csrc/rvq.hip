@@ -316,6 +316,13 @@ constexpr int kDecWaves = 4;
 // table of one (batch, KV head) fits this many floats of LDS.
 constexpr int kLutFloats = 16384;   // 64 KB
 constexpr int kLutWorkgroups = 512; // table-path workgroups resident at once (2 per compute unit)
+// polls of a unit's table flags before a workgroup builds the whole table
+// itself (the pieces come from workgroups that do not wait for anything, so
+// this bound is only reached when they cannot all be resident)
+constexpr int kTablePolls = 1 << 18;
+// per-(batch, KV head) synchronization words: the call epoch, a table-piece
+// flag per split, a merge flag per split
+constexpr int kSyncWords = 1 + 2 * kMaxSplitsMerge;
 
 // floats between the tables of consecutive units (16-byte aligned rows)
 __host__ __device__ inline int lut_stride(int G, int N, int Kc) { return (G * N * Kc + 63) / 64 * 64; }
@@ -327,44 +334,47 @@ struct RvqDecArgs {
   const uint16_t* k_cb;
   const uint16_t* v_cb;
   float* out;
-  float* partials;
-  uint32_t* counters;   // merge counters, one per (batch, KV head)
-  const float* lut;     // [units][G][N][Kc] key-logit table (table path only)
+  float* partials;      // [units][splits][G][D + 2] partial softmax states
+  float* lut;           // [units][G][N][Kc] key-logit tables (table path only)
+  uint32_t* sync;       // [units][kSyncWords]
   int Hq, Hkv, T, N, Kc, n_tiles, tiles_per_split, splits;
+  int vidx_words;       // N == 4 and v_idx 8-byte aligned: a token's value indices are two words
   float q_scale;
 };
 
-// The key-logit table of every (batch, KV head), on the matrix cores: per
-// wave 16 codewords (A operand rows, exact fp16) against the fp16 query of
-// the G heads (B operand columns, exact; columns >= G are zero), fp32
-// accumulation over the 128 channels, then the log2-domain softmax scale.
-template <int G>
-__global__ __launch_bounds__(256) void rvq_lut_kernel(RvqDecArgs a, float* __restrict__ lut) {
-  const int unit = blockIdx.y;
-  const int b = unit / a.Hkv, kvh = unit % a.Hkv;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// One 16-codeword tile of a unit's key-logit table on the matrix cores:
+// codewords [base, base + 16) of the unit's N * Kc (A operand rows, exact
+// fp16) against the fp16 query of its G heads (qb: B operand columns, exact;
+// columns >= G are zero), fp32 accumulation over the 128 channels.  Lane l
+// gets codewords base + 4 (l >> 4) + r, r < 4, for head l & 15.
+__device__ __forceinline__ float4v table_tile(const uint16_t* k_cb, const half8 (&qb)[4], int base, int n_cw,
+                                              int lane) {
   const int col = lane & 15, grp = lane >> 4;
-  const int n_cw = a.N * a.Kc;
-  const int base = (blockIdx.x * 4 + wave) * 16;
-  if (base >= n_cw) return;
-  const int cw = min(base + col, n_cw - 1);
-  const uint16_t* qh = a.q + (static_cast<size_t>(b) * a.Hq + kvh * G + min(col, G - 1)) * kD;
+  const uint16_t* row = k_cb + static_cast<size_t>(min(base + col, n_cw - 1)) * kD + 8 * grp;
+  half8 av[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) av[ks] = *reinterpret_cast<const half8*>(row + 32 * ks);
   float4v acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-  for (int ks = 0; ks < kD / 32; ++ks) {
-    const half8 av = *reinterpret_cast<const half8*>(a.k_cb + static_cast<size_t>(cw) * kD + 32 * ks + 8 * grp);
-    half8 bv = *reinterpret_cast<const half8*>(qh + 32 * ks + 8 * grp);
-    if (col >= G) bv = half8{0, 0, 0, 0, 0, 0, 0, 0};
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, acc, 0, 0, 0);
-  }
-  // D[row = codeword base + 4 grp + r][column = head col]
-  if (col < G) {
-    float* dst = lut + static_cast<size_t>(unit) * lut_stride(G, a.N, a.Kc) + static_cast<size_t>(col) * n_cw;
+  for (int ks = 0; ks < 4; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[ks], qb[ks], acc, 0, 0, 0);
+  return acc;
+}
+
+// The lane's 16 channels: [8 ck, 8 ck + 8) and [64 + 8 ck, 64 + 8 ck + 8),
+// so that the 8 lanes of a token read whole 128-byte halves of a codeword
+// row with one instruction.
+__device__ __forceinline__ int lane_channel(int ck, int c) { return c < 8 ? 8 * ck + c : 64 + 8 * ck + (c - 8); }
+
+// Add one codeword row's 16 channels (as loaded: two 16-byte pieces) to the
+// lane's fp32 sums: h * 1 + x is one mixed-precision FMA with the rounding of
+// h + x.
+__device__ __forceinline__ void add_row16(const uint4& ra, const uint4& rb, float* out) {
+  const float one = opaque_const(1.0f);
+  const uint32_t w[8] = {ra.x, ra.y, ra.z, ra.w, rb.x, rb.y, rb.z, rb.w};
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int e = base + 4 * grp + r;
-      if (e < n_cw) dst[e] = acc[r] * a.q_scale;
-    }
+  for (int i = 0; i < 8; ++i) {
+    out[2 * i] = __builtin_fmaf(half_of<0>(w[i]), one, out[2 * i]);
+    out[2 * i + 1] = __builtin_fmaf(half_of<1>(w[i]), one, out[2 * i + 1]);
   }
 }
 
@@ -372,8 +382,7 @@ __global__ __launch_bounds__(256) void rvq_lut_kernel(RvqDecArgs a, float* __res
 // stage order).  The rows of up to four stages are requested before any is
 // summed, so a token costs one memory round trip per four stages.
 __device__ __forceinline__ void rebuild16(const uint16_t* cb, const int16_t* idx, int N, int Kc,
-                                          int c0, float* out) {
-  const float one = opaque_const(1.0f);   // h * 1 + x: one mixed-precision FMA, the rounding of h + x
+                                          int ck, float* out) {
 #pragma unroll
   for (int c = 0; c < 16; ++c) out[c] = 0.0f;
   for (int s0 = 0; s0 < N; s0 += 4) {
@@ -385,81 +394,214 @@ __device__ __forceinline__ void rebuild16(const uint16_t* cb, const int16_t* idx
       // row 0 of the last stage and are not summed)
       const int s = min(s0 + k, N - 1);
       const uint32_t ci = min(static_cast<uint32_t>(static_cast<uint16_t>(idx[s])), static_cast<uint32_t>(Kc - 1));
-      const uint4* row = reinterpret_cast<const uint4*>(cb + (static_cast<size_t>(s) * Kc + ci) * kD + c0);
-      ra[k] = row[0];
-      rb[k] = row[1];
+      const uint4* row = reinterpret_cast<const uint4*>(cb + (static_cast<size_t>(s) * Kc + ci) * kD);
+      ra[k] = row[ck];
+      rb[k] = row[8 + ck];
     }
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       if (s0 + k >= N) break;
-      const uint32_t w[8] = {ra[k].x, ra[k].y, ra[k].z, ra[k].w, rb[k].x, rb[k].y, rb[k].z, rb[k].w};
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        out[2 * i] = __builtin_fmaf(half_of<0>(w[i]), one, out[2 * i]);
-        out[2 * i + 1] = __builtin_fmaf(half_of<1>(w[i]), one, out[2 * i + 1]);
-      }
+      add_row16(ra[k], rb[k], out);
     }
   }
 }
 
-// Lane = (token j of 8, 16-channel chunk ck of 8); 32-token tiles; online
-// softmax per tile; each split writes its partial state, and the last split
-// of a (batch, KV head) to finish merges them in split order (merge.h).
-template <int G, bool LUT>
+// Lane = (token j of 8, channel chunk ck of 8); 32-token tiles of four
+// 8-token sub-tiles; online softmax per tile; each split writes its partial
+// state, and the last split of a (batch, KV head) to finish merges them in
+// split order (merge.h).
+//
+// With at most four stages the value codeword rows of RB sub-tiles are in
+// flight at any time (all four of a tile when the registers allow it): a
+// ring that runs on across tiles, each slot refilled as soon as it has been
+// summed.  The value indices that address the ring are loaded two tiles
+// ahead (four 16-bit indices in two words per sub-tile), the key indices
+// one tile ahead; the first tile's rows are requested while the table is
+// staged.
+template <int G, bool LUT, bool VPRE>
 __global__ __launch_bounds__(256) void rvq_decode_kernel(RvqDecArgs a) {
   constexpr int NCK = 8, TL = 8, IT = 4;
+  constexpr int RB = (LUT && G <= 3) ? 4 : 2;
+  static_assert(IT % RB == 0, "ring slots map onto fixed sub-tiles");
   __shared__ float lds_m[kDecWaves][G], lds_l[kDecWaves][G];
   __shared__ __attribute__((aligned(16))) float lds_o[kDecWaves][G][kD];
   __shared__ __attribute__((aligned(16))) float lds_lut[LUT ? kLutFloats : 4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int j = lane / NCK, ck = lane % NCK, c0 = 16 * ck;
+  const int j = lane / NCK, ck = lane % NCK;
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const size_t unit = static_cast<size_t>(b) * a.Hkv + kvh;
-  // the indices of a tile: lane ck's key index (stage ck) and the value
-  // indices of token j (stages 0..3), per sub-tile; positions past T read
-  // the last token (in bounds).  The first tile's are requested before the
-  // table is staged, the next tile's while the current one is processed.
   const int tb = split * a.tiles_per_split;
   const int te = min(a.n_tiles, tb + a.tiles_per_split);
-  int kci[IT] = {}, vci[IT][4] = {}, kcn[IT] = {}, vcn[IT][4] = {};
-  auto load_idx = [&](int ti, int (&kc)[IT], int (&vc)[IT][4]) {
+  constexpr bool vpre = VPRE;   // N <= 4: the value rows through the ring
+  // index words of tile ti for this lane, per sub-tile; positions past T
+  // read the last token (in bounds)
+  auto load_kidx = [&](int ti, uint32_t (&kc)[IT]) {
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int t = min(ti * kGroup + it * TL + j, a.T - 1);
+      kc[it] = static_cast<uint16_t>(a.k_idx[(unit * a.T + t) * a.N + min(ck, a.N - 1)]);
+    }
+  };
+  auto load_vidx = [&](int ti, uint32_t (&vp)[IT][2]) {
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
       const int t = min(ti * kGroup + it * TL + j, a.T - 1);
       const int16_t* vix = a.v_idx + (unit * a.T + t) * a.N;
-      kc[it] = LUT ? static_cast<uint16_t>(a.k_idx[(unit * a.T + t) * a.N + min(ck, a.N - 1)]) : 0;
+      if (a.vidx_words) {   // four stages, 8-byte aligned rows
+        const uint2 w = *reinterpret_cast<const uint2*>(vix);
+        vp[it][0] = w.x;
+        vp[it][1] = w.y;
+      } else {
+        uint32_t e[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) vc[it][k] = static_cast<uint16_t>(vix[min(k, a.N - 1)]);
+        for (int k = 0; k < 4; ++k) e[k] = static_cast<uint16_t>(vix[min(k, a.N - 1)]);
+        vp[it][0] = e[0] | (e[1] << 16);
+        vp[it][1] = e[2] | (e[3] << 16);
+      }
     }
   };
-  if (tb + wave < te) load_idx(tb + wave, kci, vci);
-  if constexpr (LUT) {
-    // the unit's key-logit table into LDS (at most kLutFloats, checked on
-    // the host), eight 16-byte loads per thread in flight before any store
-    const int n4 = lut_stride(G, a.N, a.Kc) / 4;
-    const float4* src = reinterpret_cast<const float4*>(a.lut + unit * static_cast<size_t>(4 * n4));
-    float4* dst = reinterpret_cast<float4*>(lds_lut);
-    for (int base = 0; base < n4; base += 8 * 256) {
-      float4 r[8];
+  // the 4 stages' codeword rows (the lane's 16 channels) of one sub-tile;
+  // stages past N re-read the last stage and are not summed
+  // (32-bit byte offsets from the codebook base: at most 8 x 32768 rows of
+  // 256 bytes)
+  const char* const vcb = reinterpret_cast<const char*>(a.v_cb);
+  auto issue = [&](const uint32_t (&vp)[2], uint4 (&r)[4][2]) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int i = base + 256 * k + static_cast<int>(threadIdx.x);
-        r[k] = i < n4 ? src[i] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t st = static_cast<uint32_t>(min(k, a.N - 1));
+      const uint32_t ci = min((vp[k >> 1] >> (16 * (k & 1))) & 0xFFFFu, static_cast<uint32_t>(a.Kc - 1));
+      const uint32_t off = (st * static_cast<uint32_t>(a.Kc) + ci) * (kD * 2) + 16 * ck;
+      r[k][0] = *reinterpret_cast<const uint4*>(vcb + off);
+      r[k][1] = *reinterpret_cast<const uint4*>(vcb + off + 128);
+    }
+  };
+  // this call's epoch: one more than the previous call's (flags of this
+  // call that equal it are set)
+  uint32_t* const sync = a.sync + unit * kSyncWords;
+  const uint32_t epoch = __hip_atomic_load(sync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+  uint32_t kc[IT] = {}, vcur[IT][2] = {}, vnx[IT][2] = {}, vnn[IT][2] = {};
+  uint4 rows[RB][4][2];
+  const int t0 = tb + wave;
+  if (t0 < te) {
+    if (LUT) load_kidx(t0, kc);
+    if (vpre) load_vidx(t0, vcur);
+  }
+  if (vpre && t0 + kDecWaves < te) load_vidx(t0 + kDecWaves, vnx);
+  auto issue_first = [&]() {
+    if (vpre && t0 < te) {
+#pragma unroll
+      for (int s = 0; s < RB; ++s) issue(vcur[s], rows[s]);
+    }
+  };
+  if constexpr (LUT) {
+    // ---- the unit's key-logit table, built by the unit's workgroups
+    // together: split p writes tiles [p per, (p + 1) per) of the N * Kc
+    // codewords (device-scope write-through stores), then sets its table
+    // flag to the epoch; each workgroup then waits for every split's flag
+    // and stages the table into LDS with device-scope loads.  A workgroup
+    // never waits before its own flag is set, so the wait ends once the
+    // unit's workgroups have started; should it not end within kTablePolls
+    // polls (workgroups of the unit not resident together), the workgroup
+    // builds the whole table itself.
+    const int n_cw = a.N * a.Kc;
+    const int n16 = (n_cw + 15) / 16;
+    float* const tab = a.lut + unit * static_cast<size_t>(lut_stride(G, a.N, a.Kc));
+    const int col = lane & 15, grp = lane >> 4;
+    half8 qb[4];
+    {
+      const uint16_t* qh = a.q + (static_cast<size_t>(b) * a.Hq + kvh * G + min(col, G - 1)) * kD + 8 * grp;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        qb[ks] = col < G ? *reinterpret_cast<const half8*>(qh + 32 * ks) : half8{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+    {
+      const int per = (n16 + a.splits - 1) / a.splits;
+      const int p0 = split * per, p1 = min(n16, p0 + per);
+      // two tiles per wave at a time, both tiles' operands in flight
+      for (int t = p0 + wave; t < p1; t += 2 * kDecWaves) {
+        float4v r4[2];
+        r4[0] = table_tile(a.k_cb, qb, 16 * t, n_cw, lane);
+        r4[1] = table_tile(a.k_cb, qb, 16 * min(t + kDecWaves, p1 - 1), n_cw, lane);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int tu = t + u * kDecWaves;
+          if (col < G && tu < p1) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int e = 16 * tu + 4 * grp + r;
+              if (e < n_cw)
+                __hip_atomic_store(tab + col * n_cw + e, r4[u][r] * a.q_scale, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            }
+          }
+        }
+      }
+      // the piece's stores have completed before its flag is set
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (threadIdx.x == 0) __hip_atomic_store(sync + 1 + split, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __shared__ int s_table;
+    if (wave == 0) {
+      bool done = false;
+      for (int n = 0; n < kTablePolls; ++n) {
+        bool missing = false;
+#pragma unroll
+        for (int k = 0; k < kMaxSplitsMerge / 64; ++k) {
+          const int i = lane + 64 * k;
+          if (i < a.splits)
+            missing |= __hip_atomic_load(sync + 1 + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != epoch;
+        }
+        done = __builtin_amdgcn_ballot_w64(missing) == 0;
+        if (done) break;
+        __builtin_amdgcn_s_sleep(1);
+      }
+      if (lane == 0) s_table = done;
+    }
+    __syncthreads();
+    if (s_table) {
+      // at most kLutFloats / 2 8-byte words: 32 per thread, all in flight
+      constexpr int kWords = kLutFloats / 2 / 256;
+      const int n8 = lut_stride(G, a.N, a.Kc) / 2;
+      const uint64_t* src = reinterpret_cast<const uint64_t*>(tab);
+      uint64_t* dst = reinterpret_cast<uint64_t*>(lds_lut);
+      uint64_t w[kWords];
+#pragma unroll
+      for (int k = 0; k < kWords; ++k) {
+        const int i = 256 * k + static_cast<int>(threadIdx.x);
+        w[k] = i < n8 ? __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
       }
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int i = base + 256 * k + static_cast<int>(threadIdx.x);
-        if (i < n4) dst[i] = r[k];
+      for (int k = 0; k < kWords; ++k) {
+        const int i = 256 * k + static_cast<int>(threadIdx.x);
+        if (i < n8) dst[i] = w[k];
+      }
+    } else {
+      for (int t = wave; t < n16; t += kDecWaves) {
+        const float4v r4 = table_tile(a.k_cb, qb, 16 * t, n_cw, lane);
+        if (col < G) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int e = 16 * t + 4 * grp + r;
+            if (e < n_cw) lds_lut[col * n_cw + e] = r4[r] * a.q_scale;
+          }
+        }
       }
     }
     __syncthreads();
   }
+  // the first tile's value rows (requested after the table's flags and
+  // staging: requested earlier, they delay those loads and stores of the
+  // other workgroup on the compute unit)
+  issue_first();
   float qr[G][16];
+  if constexpr (!LUT) {
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const uint16_t* qp = a.q + (static_cast<size_t>(b) * a.Hq + kvh * G + h) * kD + c0;
+    for (int h = 0; h < G; ++h) {
+      const uint16_t* qp = a.q + (static_cast<size_t>(b) * a.Hq + kvh * G + h) * kD;
 #pragma unroll
-    for (int c = 0; c < 16; ++c) qr[h][c] = h2f(qp[c]) * a.q_scale;
+      for (int c = 0; c < 16; ++c) qr[h][c] = h2f(qp[lane_channel(ck, c)]) * a.q_scale;
+    }
   }
   float m[G], l[G], acc[G][16];
 #pragma unroll
@@ -469,28 +611,10 @@ __global__ __launch_bounds__(256) void rvq_decode_kernel(RvqDecArgs a) {
 #pragma unroll
     for (int c = 0; c < 16; ++c) acc[h][c] = 0.0f;
   }
-  // value rows of up to 4 stages are prefetched one sub-tile ahead when
-  // N <= 4 (wave-uniform); larger N rebuilds each sub-tile on its own
-  const bool vpre = a.N <= 4;
-  // values: the 4 stages' codeword rows (the lane's 16 channels, two
-  // 16-byte loads each) of sub-tile it + 1 are in flight while sub-tile
-  // it is summed; sub-tile 0's are requested as soon as the indices are in
-  uint4 rows[2][4][2];
-  auto issue_rows = [&](int it, uint4 (&r)[4][2]) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int st = min(k, a.N - 1);
-      const uint32_t ci = min(static_cast<uint32_t>(vci[it][k]), static_cast<uint32_t>(a.Kc - 1));
-      const uint4* row = reinterpret_cast<const uint4*>(a.v_cb + (static_cast<size_t>(st) * a.Kc + ci) * kD + c0);
-      r[k][0] = row[0];
-      r[k][1] = row[1];
-    }
-  };
-  for (int ti = tb + wave; ti < te; ti += kDecWaves) {
+  for (int ti = t0; ti < te; ti += kDecWaves) {
+    const bool has_next = ti + kDecWaves < te;
     float lg[IT][G];
     bool valid[IT];
-    if (vpre) issue_rows(0, rows[0]);
-    if (ti + kDecWaves < te) load_idx(ti + kDecWaves, kcn, vcn);
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
       const int t = ti * kGroup + it * TL + j;
@@ -501,7 +625,7 @@ __global__ __launch_bounds__(256) void rvq_decode_kernel(RvqDecArgs a) {
 #pragma unroll
         for (int h = 0; h < G; ++h) part[h] = 0.0f;
         if (valid[it] && ck < a.N) {
-          const int ci = min(kci[it], a.Kc - 1);
+          const int ci = min(static_cast<int>(kc[it]), a.Kc - 1);
 #pragma unroll
           for (int h = 0; h < G; ++h) part[h] = lds_lut[(h * a.N + ck) * a.Kc + ci];
         }
@@ -510,7 +634,7 @@ __global__ __launch_bounds__(256) void rvq_decode_kernel(RvqDecArgs a) {
       } else {
         float kh[16];
         if (valid[it]) {
-          rebuild16(a.k_cb, a.k_idx + (unit * a.T + t) * a.N, a.N, a.Kc, c0, kh);
+          rebuild16(a.k_cb, a.k_idx + (unit * a.T + t) * a.N, a.N, a.Kc, ck, kh);
         } else {
 #pragma unroll
           for (int c = 0; c < 16; ++c) kh[c] = 0.0f;
@@ -524,6 +648,8 @@ __global__ __launch_bounds__(256) void rvq_decode_kernel(RvqDecArgs a) {
         }
       }
     }
+    if (LUT && has_next) load_kidx(ti + kDecWaves, kc);
+    if (vpre && ti + 2 * kDecWaves < te) load_vidx(ti + 2 * kDecWaves, vnn);
     bool grow = false;
     float mnew[G];
 #pragma unroll
@@ -547,28 +673,27 @@ __global__ __launch_bounds__(256) void rvq_decode_kernel(RvqDecArgs a) {
     }
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
-      if (vpre && it + 1 < IT) issue_rows(it + 1, rows[(it + 1) & 1]);
-      if (!valid[it]) continue;
       float vh[16];
       if (vpre) {
+        const int slot = it % RB;
 #pragma unroll
         for (int c = 0; c < 16; ++c) vh[c] = 0.0f;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           if (k >= a.N) break;
-          const uint4 ra = rows[it & 1][k][0], rb = rows[it & 1][k][1];
-          const uint32_t w[8] = {ra.x, ra.y, ra.z, ra.w, rb.x, rb.y, rb.z, rb.w};
-          const float one = opaque_const(1.0f);
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            vh[2 * i] = __builtin_fmaf(half_of<0>(w[i]), one, vh[2 * i]);
-            vh[2 * i + 1] = __builtin_fmaf(half_of<1>(w[i]), one, vh[2 * i + 1]);
-          }
+          add_row16(rows[slot][k][0], rows[slot][k][1], vh);
         }
-      } else {
+        // refill the slot: sub-tile it + RB of this tile, else of the next
+        if (it + RB < IT) {
+          issue(vcur[it + RB], rows[slot]);
+        } else if (has_next) {
+          issue(vnx[it + RB - IT], rows[slot]);
+        }
+      } else if (valid[it]) {
         const int t = ti * kGroup + it * TL + j;
-        rebuild16(a.v_cb, a.v_idx + (unit * a.T + t) * a.N, a.N, a.Kc, c0, vh);
+        rebuild16(a.v_cb, a.v_idx + (unit * a.T + t) * a.N, a.N, a.Kc, ck, vh);
       }
+      if (!valid[it]) continue;
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         const float p = exp2f(lg[it][h] - m[h]);
@@ -579,9 +704,11 @@ __global__ __launch_bounds__(256) void rvq_decode_kernel(RvqDecArgs a) {
     }
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
-      kci[it] = kcn[it];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) vci[it][k] = vcn[it][k];
+      for (int w = 0; w < 2; ++w) {
+        vcur[it][w] = vnx[it][w];
+        vnx[it][w] = vnn[it][w];
+      }
     }
   }
 #pragma unroll
@@ -594,7 +721,7 @@ __global__ __launch_bounds__(256) void rvq_decode_kernel(RvqDecArgs a) {
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int c = 0; c < 16; ++c) lds_o[wave][h][c0 + c] = acc[h][c];
+      for (int c = 0; c < 16; ++c) lds_o[wave][h][lane_channel(ck, c)] = acc[h][c];
   }
   if (lane == 0) {
 #pragma unroll
@@ -604,13 +731,13 @@ __global__ __launch_bounds__(256) void rvq_decode_kernel(RvqDecArgs a) {
     }
   }
   __syncthreads();
-  write_split_state<kD, G, kDecWaves>(a.partials, a.counters, a.out, a.Hq, unit, b, kvh, split, a.splits,
-                                      lds_m, lds_l, lds_o);
+  write_split_state_flagged<kD, G, kDecWaves>(a.partials, sync + 1 + kMaxSplitsMerge, sync, epoch, a.out, a.Hq,
+                                              unit, b, kvh, split, a.splits, lds_m, lds_l, lds_o);
 }
 
 struct RvqGeometry {
   int G, n_tiles, tps, splits;
-  size_t units, ws_bytes, lut_off;
+  size_t units, ws_bytes, lut_off, sync_off;
 };
 
 int rvq_geometry(int B, int Hq, int Hkv, int T, int d, RvqGeometry* g) {
@@ -628,9 +755,12 @@ int rvq_geometry(int B, int Hq, int Hkv, int T, int d, RvqGeometry* g) {
   if (s < 1) s = 1;
   g->tps = g->n_tiles > 0 ? static_cast<int>((g->n_tiles + s - 1) / s) : 1;
   g->splits = g->n_tiles > 0 ? (g->n_tiles + g->tps - 1) / g->tps : 1;
-  // partial states, then room for the key-logit table of every unit
-  g->lut_off = (partial_state_bytes(g->units, g->splits, g->G, kD) + 255) / 256 * 256;
-  g->ws_bytes = g->lut_off + g->units * kLutFloats * sizeof(float);
+  // partial states (none with one split), room for the key-logit table of
+  // every unit, then the synchronization words
+  const size_t part = g->splits > 1 ? g->units * g->splits * g->G * (kD + 2) * sizeof(float) : 0;
+  g->lut_off = (part + 255) / 256 * 256;
+  g->sync_off = g->lut_off + g->units * kLutFloats * sizeof(float);
+  g->ws_bytes = g->sync_off + (g->units * kSyncWords * sizeof(uint32_t) + 255) / 256 * 256;
   return DQA_OK;
 }
 
@@ -693,10 +823,9 @@ extern "C" int rvq_decode_attention(const uint16_t* q, int B, int Hq, int Hkv, i
   a.k_cb = k_cb;
   a.v_cb = v_cb;
   a.out = out;
-  a.partials = merge_partials(ws, g.units);
-  a.counters = merge_counters(ws);
-  float* lut = reinterpret_cast<float*>(static_cast<char*>(ws) + g.lut_off);
-  a.lut = lut;
+  a.partials = static_cast<float*>(ws);
+  a.lut = reinterpret_cast<float*>(static_cast<char*>(ws) + g.lut_off);
+  a.sync = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + g.sync_off);
   a.Hq = Hq;
   a.Hkv = Hkv;
   a.T = T;
@@ -705,6 +834,7 @@ extern "C" int rvq_decode_attention(const uint16_t* q, int B, int Hq, int Hkv, i
   a.n_tiles = g.n_tiles;
   a.tiles_per_split = g.tps;
   a.splits = g.splits;
+  a.vidx_words = N == 4 && (reinterpret_cast<uintptr_t>(v_idx) & 7u) == 0;
   const bool use_lut = T > 0 && static_cast<long long>(g.G) * N * Kc <= kLutFloats && N <= 8;
   if (use_lut) {
     // two table-holding workgroups fit a compute unit: one resident round
@@ -718,27 +848,21 @@ extern "C" int rvq_decode_attention(const uint16_t* q, int B, int Hq, int Hkv, i
   a.q_scale = sm_scale * 1.4426950408889634f;
   const dim3 grid(a.splits, Hkv, B);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  // the table path needs the unit's table in LDS and one stage per lookup lane
-  if (use_lut) {
-    const dim3 lgrid((N * Kc + 63) / 64, static_cast<unsigned>(g.units));
-    switch (g.G) {
-      case 1: hipLaunchKernelGGL(rvq_lut_kernel<1>, lgrid, dim3(256), 0, s, a, lut); break;
-      case 2: hipLaunchKernelGGL(rvq_lut_kernel<2>, lgrid, dim3(256), 0, s, a, lut); break;
-      case 3: hipLaunchKernelGGL(rvq_lut_kernel<3>, lgrid, dim3(256), 0, s, a, lut); break;
-      case 4: hipLaunchKernelGGL(rvq_lut_kernel<4>, lgrid, dim3(256), 0, s, a, lut); break;
-      default: return DQA_ERR_UNSUPPORTED;
-    }
-    DQA_CHECK_LAUNCH();
-  }
-  switch (g.G * 2 + (use_lut ? 1 : 0)) {
-    case 2: hipLaunchKernelGGL((rvq_decode_kernel<1, false>), grid, dim3(256), 0, s, a); break;
-    case 3: hipLaunchKernelGGL((rvq_decode_kernel<1, true>), grid, dim3(256), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((rvq_decode_kernel<2, false>), grid, dim3(256), 0, s, a); break;
-    case 5: hipLaunchKernelGGL((rvq_decode_kernel<2, true>), grid, dim3(256), 0, s, a); break;
-    case 6: hipLaunchKernelGGL((rvq_decode_kernel<3, false>), grid, dim3(256), 0, s, a); break;
-    case 7: hipLaunchKernelGGL((rvq_decode_kernel<3, true>), grid, dim3(256), 0, s, a); break;
-    case 8: hipLaunchKernelGGL((rvq_decode_kernel<4, false>), grid, dim3(256), 0, s, a); break;
-    case 9: hipLaunchKernelGGL((rvq_decode_kernel<4, true>), grid, dim3(256), 0, s, a); break;
+  // the table path: the unit's table in LDS, one stage per lookup lane
+  const bool vpre = N <= 4;
+  switch (g.G * 4 + (use_lut ? 2 : 0) + (vpre ? 1 : 0)) {
+#define DQA_RVQ_CASE(G_, L_, V_) \
+  case G_ * 4 + (L_ ? 2 : 0) + (V_ ? 1 : 0): \
+    hipLaunchKernelGGL((rvq_decode_kernel<G_, L_, V_>), grid, dim3(256), 0, s, a); \
+    break;
+#define DQA_RVQ_CASES(G_) DQA_RVQ_CASE(G_, false, false) DQA_RVQ_CASE(G_, false, true) \
+  DQA_RVQ_CASE(G_, true, false) DQA_RVQ_CASE(G_, true, true)
+    DQA_RVQ_CASES(1)
+    DQA_RVQ_CASES(2)
+    DQA_RVQ_CASES(3)
+    DQA_RVQ_CASES(4)
+#undef DQA_RVQ_CASES
+#undef DQA_RVQ_CASE
     default: return DQA_ERR_UNSUPPORTED;
   }
   DQA_CHECK_LAUNCH();

@@ -65,7 +65,11 @@ enum {
 const char* dqa_status_string(int status);
 
 /* Version of this interface (increments on any signature or layout change). */
-int dqa_abi_version(void);  /* 11: dqa_kivi_cache ends with an optional
+int dqa_abi_version(void);  /* 12: rvq_decode_attention is one launch
+                              (the key-logit tables are built in it) and
+                              its workspace ends with synchronization
+                              words (a larger workspace);
+                              11: dqa_kivi_cache ends with an optional
                               rope_table; kivi_rope_table(_words);
                               10: decode workspaces hold merge counters
                               and must be zeroed before first use; the
@@ -391,9 +395,12 @@ int rvq_encode(const uint16_t* x, int64_t n, int d, const uint16_t* codebooks,
                int N, int Kc, int16_t* idx, void* ws, size_t ws_bytes,
                void* stream);
 
-/* Workspace bytes for rvq_decode_attention (0 if invalid): merge counters
- * and partial softmax states, then room for the key-logit table, 64 KB per
- * (batch, KV head); zero it before its first use (see the preamble). */
+/* Workspace bytes for rvq_decode_attention (0 if invalid): partial softmax
+ * states, room for the key-logit table (64 KB per (batch, KV head)), then
+ * 257 synchronization words per (batch, KV head) (a call counter, and a
+ * table-piece flag and a merge flag per split).  Zero it before its first
+ * use; every call leaves the words as the next call on it expects (for any
+ * shape), so it is not cleared again. */
 size_t rvq_decode_attention_workspace_bytes(int B, int Hq, int Hkv, int T, int d);
 
 /* Decode attention with keys and values rebuilt on the fly from their
@@ -404,13 +411,13 @@ size_t rvq_decode_attention_workspace_bytes(int B, int Hq, int Hkv, int T, int d
  *   out (device) fp32 [B][Hq][d]
  *   q and the codebooks 16-byte aligned (else DQA_ERR_ALIGN)
  * When G * N * Kc <= 16384 (G = Hq / Hkv) the key logits go through a
- * per-(batch, KV head) table of q_h . Ck_s[c] kept in the workspace and
- * staged in LDS, so each key costs N lookups instead of N gathered
- * codewords (one extra small kernel enqueued first); otherwise keys are
- * rebuilt like values.
- * Enqueues the table kernel (when used) and the split kernel (the last
- * split of each (batch, KV head) to finish merges the splits in split
- * order).
+ * per-(batch, KV head) table of q_h . Ck_s[c], built by the workgroups of
+ * that (batch, KV head) in the same launch (a piece each, through the
+ * workspace) and staged in LDS, so each key costs N lookups instead of N
+ * gathered codewords; otherwise keys are rebuilt like values.
+ * Enqueues one kernel; a split that finds every split's partial state
+ * stored merges them in split order.  Calls that overlap on one workspace
+ * race.
  * Errors: DQA_ERR_NULL, DQA_ERR_SHAPE, DQA_ERR_ALIGN, DQA_ERR_WORKSPACE,
  * DQA_ERR_UNSUPPORTED, DQA_ERR_HIP. */
 int rvq_decode_attention(const uint16_t* q, int B, int Hq, int Hkv, int T,

@@ -130,3 +130,58 @@ def test_decode_attention_small(dqa, B, Hq, Hkv, T, N, Kc):
                                         dev(inp["v_cb"]), scale))
     ref = oracle.rvq_decode_attention(inp["q"], ki, vi, inp["k_cb"], inp["v_cb"], scale)
     check_attention(out, ref, TOL)
+
+
+# long splits: up to three tiles per wave, so the value-row ring runs across
+# tiles and the value indices are read two tiles ahead (table path at G = 3,
+# gather path at G = 2); and four stages whose value indices are not 8-byte
+# aligned (read one at a time)
+@pytest.mark.parametrize("B,Hq,Hkv,T,N,Kc,v_offset", [(1, 3, 1, 40000, 4, 1024, 0),
+                                                      (1, 2, 1, 40000, 4, 4096, 0),
+                                                      (1, 4, 2, 3000, 4, 256, 1),
+                                                      (2, 3, 1, 500, 3, 512, 0)])
+def test_decode_attention_long_splits_and_index_alignment(dqa, B, Hq, Hkv, T, N, Kc, v_offset):
+    inp = rvq_inputs(B, Hq, Hkv, 128, T, N, Kc, seed=T + N)
+    rng = np.random.default_rng(T + Kc)
+    ki = rng.integers(0, Kc, size=(B, Hkv, T, N)).astype(np.int16)
+    vi = rng.integers(0, Kc, size=(B, Hkv, T, N)).astype(np.int16)
+    # v_idx at v_offset int16 elements past an aligned allocation
+    buf = torch.zeros(vi.size + v_offset, dtype=torch.int16, device="cuda")
+    buf[v_offset:] = dev(vi.reshape(-1))
+    v_dev = buf[v_offset:].view(vi.shape)
+    assert (v_dev.data_ptr() % 8 == 0) == (v_offset == 0)
+    scale = 1.0 / math.sqrt(128)
+    say("rvq_decode_attention long/aligned", B, Hq, Hkv, T, N, Kc, v_offset)
+    out = host(dqa.rvq_decode_attention(dev(inp["q"]), dev(ki), v_dev, dev(inp["k_cb"]),
+                                        dev(inp["v_cb"]), scale))
+    ref = oracle.rvq_decode_attention(inp["q"], ki, vi, inp["k_cb"], inp["v_cb"], scale)
+    check_attention(out, ref, TOL)
+
+
+def test_decode_attention_workspace_reuse(dqa):
+    """One workspace for several calls: new queries over the same cache (the
+    key-logit tables are rebuilt every call), another shape, and back; the
+    table path and the gather path; each call against the oracle."""
+    Kc, N = 512, 4
+    shapes = [(2, 6, 2, 3000), (2, 6, 2, 3000), (1, 3, 1, 700), (2, 6, 2, 3000)]
+    cases = []
+    for i, (B, Hq, Hkv, T) in enumerate(shapes):
+        inp = rvq_inputs(B, Hq, Hkv, 128, T, N, Kc, seed=100 + (i if i != 3 else 0))
+        rng = np.random.default_rng(T)
+        ki = rng.integers(0, Kc, size=(B, Hkv, T, N)).astype(np.int16)
+        vi = rng.integers(0, Kc, size=(B, Hkv, T, N)).astype(np.int16)
+        cases.append((inp, ki, vi))
+    big = max(dqa.lib.rvq_decode_attention_workspace_bytes(B, Hq, Hkv, T, 128) for B, Hq, Hkv, T in shapes)
+    for kc_gather in (False, True):
+        ws = torch.zeros(big, dtype=torch.uint8, device="cuda")
+        for i, (inp, ki, vi) in enumerate(cases):
+            kcb, vcb = inp["k_cb"], inp["v_cb"]
+            if kc_gather:   # G * N * Kc above the table's limit: keys by gathered codewords
+                kcb = np.ascontiguousarray(np.concatenate([kcb] * 9, axis=1))
+                vcb = np.ascontiguousarray(np.concatenate([vcb] * 9, axis=1))
+            scale = 1.0 / math.sqrt(128)
+            say("rvq_decode_attention workspace reuse", i, shapes[i], "gather" if kc_gather else "table")
+            out = host(dqa.rvq_decode_attention(dev(inp["q"]), dev(ki), dev(vi), dev(kcb), dev(vcb),
+                                                scale, workspace=ws))
+            ref = oracle.rvq_decode_attention(inp["q"], ki, vi, kcb, vcb, scale)
+            check_attention(out, ref, TOL, f"reuse call {i}")
