@@ -14,11 +14,14 @@
 // exact, fp32 accumulation):
 //   1. per query row, the log-sum-exp of its causal logits (base 2);
 //   2. per key tile, sum over rows and over the G heads of a KV head of
-//      exp2(logit - lse).  A workgroup owns its 128 keys (4 waves x 32,
+//      exp2(logit - lse).  A workgroup owns its 256 keys (4 waves x 64,
 //      sharing each query tile), so the sums are written without atomics
-//      and repeat bit for bit.  Wider workgroups (8 or 16 waves) stream the
-//      query rows fewer times but measured slower: the caches already serve
-//      most re-reads, and the wider barrier costs more.
+//      and repeat bit for bit.  Each query fragment read from LDS feeds the
+//      products of a wave's four key blocks (with two, the LDS reads took
+//      as long as the products and the pass 15% longer).  Wider workgroups
+//      (8 or 16 waves) stream the query rows fewer times but measured
+//      slower: the caches already serve most re-reads, and the wider
+//      barrier costs more.
 // Both passes see identical logits (same operands, same order).  Pass 1
 // walks key tiles from 0 upward and pass 2 query tiles from the last one
 // downward, so the workgroups of one KV head that run together read the
@@ -51,7 +54,7 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));  // promotable (HIP'
 constexpr int kLseRows = 128;   // query rows per workgroup in pass 1 (4 waves x 32)
 constexpr int kLseKeys = 64;    // keys per LDS tile in pass 1
 constexpr int kSumWaves = 4;    // waves per workgroup in pass 2, sharing one query tile
-constexpr int kSumNB = 2;       // 16-key blocks per wave in pass 2 (keys in registers)
+constexpr int kSumNB = 4;       // 16-key blocks per wave in pass 2 (keys in registers)
 constexpr int kSumRB = 4;       // 16-row blocks per query tile in pass 2
 constexpr int kSumKeys = 16 * kSumNB * kSumWaves;  // keys per workgroup in pass 2
 constexpr int kSumRows = 16 * kSumRB;               // query rows per LDS tile in pass 2
