@@ -60,7 +60,7 @@ constexpr int kSumKeys = 16 * kSumNB * kSumWaves;  // keys per workgroup in pass
 constexpr int kSumRows = 16 * kSumRB;               // query rows per LDS tile in pass 2
 constexpr int kChanRows = 256;  // positions per workgroup of the channel sums
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLazy = 8.0f;        // log2 headroom before the reference max moves
+constexpr float kRescale = 0x1p100f;  // a row sum at or above this moves its reference
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -99,7 +99,7 @@ __global__ __launch_bounds__(256) void rdkv_lse_kernel(const uint16_t* __restric
       a[rb][s] = *reinterpret_cast<const half8*>(qh + static_cast<size_t>(row) * D + 32 * s + 8 * grp);
   }
 
-  float mc[2][4], l[2][4], tm[2][4];
+  float mc[2][4], l[2][4];
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
@@ -147,36 +147,41 @@ __global__ __launch_bounds__(256) void rdkv_lse_kernel(const uint16_t* __restric
       }
     }
     // Per lane and row: l = sum of exp2(c x - mc) against a reference mc
-    // (log2 units).  The reference moves only when a logit passes it by more
-    // than 2^8 (a uniform branch, rare after the first tiles); moving it by
-    // any delta (mc += delta, l *= 2^-delta) leaves the sum exact.  Key tile
-    // 0 always takes that branch: a lane with nothing accumulated yet takes
-    // its own maximum as the reference.  Every wave that reaches a later
-    // tile holds rows >= 64, all of which saw a valid key in tile 0, so no
-    // lane starts its sum after tile 0.
+    // (log2 units).  A tile's terms are first added against the current
+    // reference; only if that sum is not below kRescale (a large logit, an
+    // overflow to infinity: a uniform branch, rare after the first tile) is
+    // the tile redone with the reference moved up to the tile's maximum
+    // (moving it by any delta, mc += delta, l *= 2^-delta, leaves the sum
+    // exact).  Key tile 0 always takes that branch: a lane with nothing
+    // accumulated yet takes its own maximum as the reference.  Every wave
+    // that reaches a later tile holds rows >= 64, all of which saw a valid
+    // key in tile 0, so no lane starts its sum after tile 0.
     auto update = [&](auto masked) {
-      float t[2][4][4];
+      float t[2][4][4], ls[2][4];
       bool need = false;
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
+          float sum = l[rb][r];
 #pragma unroll
           for (int nb = 0; nb < 4; ++nb) {
             t[rb][r][nb] = fmaf(acc[rb][nb][r], c, -mc[rb][r]);
             if constexpr (decltype(masked)::value)
               if (kbase + 16 * nb + col > q0 + 16 * rb + 4 * grp + r) t[rb][r][nb] = -INFINITY;
+            sum += fast_exp2(t[rb][r][nb]);
           }
-          tm[rb][r] = fmaxf(fmaxf(t[rb][r][0], t[rb][r][1]), fmaxf(t[rb][r][2], t[rb][r][3]));
-          need |= tm[rb][r] > kLazy;
+          ls[rb][r] = sum;
+          need |= !(sum < kRescale);
         }
       if (kt == 0 || __builtin_amdgcn_ballot_w64(need)) {
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
+            const float tm = fmaxf(fmaxf(t[rb][r][0], t[rb][r][1]), fmaxf(t[rb][r][2], t[rb][r][3]));
             const bool fresh = l[rb][r] == 0.0f;
-            float delta = fresh ? tm[rb][r] : fmaxf(tm[rb][r], 0.0f);
+            float delta = fresh ? tm : fmaxf(tm, 0.0f);
             delta = delta > -INFINITY ? delta : 0.0f;  // no valid key in this lane yet
             mc[rb][r] += delta;
             float sum = fresh ? 0.0f : l[rb][r] * fast_exp2(-delta);
@@ -188,12 +193,7 @@ __global__ __launch_bounds__(256) void rdkv_lse_kernel(const uint16_t* __restric
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float sum = l[rb][r];
-#pragma unroll
-            for (int nb = 0; nb < 4; ++nb) sum += fast_exp2(t[rb][r][nb]);
-            l[rb][r] = sum;
-          }
+          for (int r = 0; r < 4; ++r) l[rb][r] = ls[rb][r];
       }
     };
     if (kbase + kLseKeys - 1 > q0)
