@@ -149,22 +149,23 @@ __global__ __launch_bounds__(NW * 64) void rvq_encode_kernel(const uint16_t* __r
         besti[mb][r] = 0;
       }
 
-    // codeword tiles: thread tid moves 16-byte chunks CPT*tid .. CPT*tid +
-    // CPT-1 of a 64-codeword tile (global -> registers -> LDS buffer); the
+    // codeword tiles: thread tid moves 16-byte chunks tid, tid + NT, ... of
+    // a 64-codeword tile (global -> registers -> LDS buffer; consecutive
+    // threads store consecutive chunks, free of bank conflicts); the
     // tile after next is in flight while the current tile is consumed.  The
     // norms |c|^2 of the lane's 4 codeword columns come straight from global
     // memory, one tile ahead.
     auto gchunks = [&](int t, uint4 (&u)[CPT]) {
 #pragma unroll
       for (int k = 0; k < CPT; ++k) {
-        const int c = CPT * tid + k;
+        const int c = tid + NT * k;
         u[k] = *reinterpret_cast<const uint4*>(cb + (static_cast<size_t>(t) * kTileCW + c / 16) * kD + (c % 16) * 8);
       }
     };
     auto lstore = [&](int buf, const uint4 (&u)[CPT]) {
 #pragma unroll
       for (int k = 0; k < CPT; ++k) {
-        const int c = CPT * tid + k;
+        const int c = tid + NT * k;
         *reinterpret_cast<uint4*>(&lds_cb[buf][c / 16][(c % 16) * 8]) = u[k];
       }
     };
