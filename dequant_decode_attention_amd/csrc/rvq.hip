@@ -542,6 +542,10 @@ __global__ __launch_bounds__(256) void rvq_decode_kernel(RvqDecArgs a) {
       __syncthreads();
       if (threadIdx.x == 0) __hip_atomic_store(sync + 1 + split, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+    // the first tile's value rows are requested while the flags are polled
+    // and the table is staged (with a shared counter in place of the flags,
+    // these gathers held back the neighbouring workgroup's counter update)
+    issue_first();
     __shared__ int s_table;
     if (wave == 0) {
       bool done = false;
@@ -591,10 +595,7 @@ __global__ __launch_bounds__(256) void rvq_decode_kernel(RvqDecArgs a) {
     }
     __syncthreads();
   }
-  // the first tile's value rows (requested after the table's flags and
-  // staging: requested earlier, they delay those loads and stores of the
-  // other workgroup on the compute unit)
-  issue_first();
+  if constexpr (!LUT) issue_first();
   float qr[G][16];
   if constexpr (!LUT) {
 #pragma unroll
