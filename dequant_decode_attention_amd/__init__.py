@@ -76,6 +76,7 @@ _SIGS = {
     "rvq_decode_attention_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "rvq_decode_attention": (_i, [_vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _i, _i, _f,
                                   _vp, _sz, _vp, _vp]),
+    "rvq_decode_set_table_polls": (_i, [_i]),
     "rdkv_token_weights_workspace_bytes": (_sz, [_i, _i, _i]),
     "rdkv_token_weights": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _f, _vp, _vp, _sz, _vp]),
     "rdkv_channel_weights_workspace_bytes": (_sz, [_i, _i, _i, _i]),
@@ -402,6 +403,15 @@ def rvq_decode_attention(q, k_idx, v_idx, k_codebooks, v_codebooks, sm_scale, ou
                                     float(sm_scale), _ptr(workspace), workspace.numel(),
                                     _ptr(out), _stream(q.device)))
     return out
+
+
+def rvq_decode_set_table_polls(polls):
+    """Polls of a unit's table flags before a workgroup builds the table
+    alone (test hook; 0 forces that path).  Returns the previous value."""
+    prev = lib.rvq_decode_set_table_polls(int(polls))
+    if prev < 0:
+        raise ValueError(f"polls must be >= 0, got {polls}")
+    return prev
 
 
 # ---------------------------------------------------------------- RDKV

@@ -340,8 +340,12 @@ struct RvqDecArgs {
   uint32_t* sync;       // [units][kSyncWords]
   int Hq, Hkv, T, N, Kc, n_tiles, tiles_per_split, splits;
   int vidx_words;       // N == 4 and v_idx 8-byte aligned: a token's value indices are two words
+  int table_polls;      // polls of the table flags before building the table alone
   float q_scale;
 };
+
+// polls of the table flags per workgroup (rvq_decode_set_table_polls)
+int g_table_polls = kTablePolls;
 
 // One 16-codeword tile of a unit's key-logit table on the matrix cores:
 // codewords [base, base + 16) of the unit's N * Kc (A operand rows, exact
@@ -501,7 +505,7 @@ __global__ __launch_bounds__(256) void rvq_decode_kernel(RvqDecArgs a) {
     // flag to the epoch; each workgroup then waits for every split's flag
     // and stages the table into LDS with device-scope loads.  A workgroup
     // never waits before its own flag is set, so the wait ends once the
-    // unit's workgroups have started; should it not end within kTablePolls
+    // unit's workgroups have started; should it not end within table_polls
     // polls (workgroups of the unit not resident together), the workgroup
     // builds the whole table itself.
     const int n_cw = a.N * a.Kc;
@@ -549,7 +553,7 @@ __global__ __launch_bounds__(256) void rvq_decode_kernel(RvqDecArgs a) {
     __shared__ int s_table;
     if (wave == 0) {
       bool done = false;
-      for (int n = 0; n < kTablePolls; ++n) {
+      for (int n = 0; n < a.table_polls; ++n) {
         bool missing = false;
 #pragma unroll
         for (int k = 0; k < kMaxSplitsMerge / 64; ++k) {
@@ -837,6 +841,7 @@ extern "C" int rvq_decode_attention(const uint16_t* q, int B, int Hq, int Hkv, i
   a.tiles_per_split = g.tps;
   a.splits = g.splits;
   a.vidx_words = N == 4 && (reinterpret_cast<uintptr_t>(v_idx) & 7u) == 0;
+  a.table_polls = g_table_polls;
   const bool use_lut = T > 0 && static_cast<long long>(g.G) * N * Kc <= kLutFloats && N <= 8;
   if (use_lut) {
     // two table-holding workgroups fit a compute unit: one resident round
@@ -869,4 +874,11 @@ extern "C" int rvq_decode_attention(const uint16_t* q, int B, int Hq, int Hkv, i
   }
   DQA_CHECK_LAUNCH();
   return DQA_OK;
+}
+
+extern "C" int rvq_decode_set_table_polls(int polls) {
+  if (polls < 0) return -1;
+  const int prev = g_table_polls;
+  g_table_polls = polls;
+  return prev;
 }

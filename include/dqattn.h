@@ -65,7 +65,8 @@ enum {
 const char* dqa_status_string(int status);
 
 /* Version of this interface (increments on any signature or layout change). */
-int dqa_abi_version(void);  /* 12: rvq_decode_attention is one launch
+int dqa_abi_version(void);  /* 13: rvq_decode_set_table_polls;
+                              12: rvq_decode_attention is one launch
                               (the key-logit tables are built in it) and
                               its workspace ends with synchronization
                               words (a larger workspace);
@@ -426,6 +427,16 @@ int rvq_decode_attention(const uint16_t* q, int B, int Hq, int Hkv, int T,
                          const uint16_t* v_codebooks, int N, int Kc,
                          float sm_scale, void* ws, size_t ws_bytes, float* out,
                          void* stream);
+
+/* Test hook for rvq_decode_attention's table path: the number of polls of a
+ * (batch, KV head)'s table flags after which a workgroup stops waiting for
+ * the other workgroups' pieces and builds the whole table itself (the path
+ * taken when the workgroups of one (batch, KV head) cannot all be resident
+ * at once).  Default 262144; 0 sends every workgroup down that path.
+ * Applies to later calls in this process (not synchronized with calls on
+ * other host threads).  Returns the previous value, or -1 for polls < 0
+ * (nothing changed). */
+int rvq_decode_set_table_polls(int polls);
 
 /* ------------------------------------------------------------------------
  * RDKV bit allocation ([P3 sec 2.1, theoretical formulation]; [P3 sec 2.2,

@@ -333,7 +333,7 @@ def test_rvq_validation_and_workspace():
 
 def test_kivi_append_validation():
     """Argument checks of the streaming append (all fail before any launch)."""
-    assert lib.dqa_abi_version() == 12
+    assert lib.dqa_abi_version() == 13
     c = _cache(T_cap=128, R_cap=128)
     # staging holds the recent and the new rows of K and V
     assert lib.kivi_append_workspace_bytes(ctypes.byref(c), 20) == 2 * 2 * 2 * (16 + 20) * 128 * 2
@@ -438,3 +438,12 @@ def test_rdkv_validation():
     assert wd(wsb=need - 1) == 4
     assert wd(d=80) == 5
     assert wd(B=0, q=None, k=None, v=None, kbits=None, ws=None) == 0
+
+
+def test_rvq_table_polls_hook():
+    """The table-poll bound is a process setting: a negative value is
+    refused and changes nothing; each call returns the previous value."""
+    prev = lib.rvq_decode_set_table_polls(5)
+    assert prev >= 0
+    assert lib.rvq_decode_set_table_polls(-1) == -1
+    assert lib.rvq_decode_set_table_polls(prev) == 5

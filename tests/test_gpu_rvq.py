@@ -185,3 +185,31 @@ def test_decode_attention_workspace_reuse(dqa):
                                                 scale, workspace=ws))
             ref = oracle.rvq_decode_attention(inp["q"], ki, vi, kcb, vcb, scale)
             check_attention(out, ref, TOL, f"reuse call {i}")
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,T,N,Kc", [(2, 6, 2, 3000, 4, 512), (1, 3, 1, 40000, 4, 1024),
+                                             (1, 4, 4, 1, 1, 64), (2, 2, 1, 700, 8, 64)])
+def test_decode_attention_table_built_alone(dqa, B, Hq, Hkv, T, N, Kc):
+    """The path a workgroup takes when its (batch, KV head)'s other
+    workgroups do not set their table flags within the poll bound: with the
+    bound at 0 every workgroup builds the whole key-logit table itself (the
+    flags are still set, so the calls after it find a consistent state)."""
+    inp = rvq_inputs(B, Hq, Hkv, 128, T, N, Kc, seed=T + 1)
+    rng = np.random.default_rng(T + 1)
+    ki = rng.integers(0, Kc, size=(B, Hkv, T, N)).astype(np.int16)
+    vi = rng.integers(0, Kc, size=(B, Hkv, T, N)).astype(np.int16)
+    scale = 1.0 / math.sqrt(128)
+    ref = oracle.rvq_decode_attention(inp["q"], ki, vi, inp["k_cb"], inp["v_cb"], scale)
+    n = dqa.lib.rvq_decode_attention_workspace_bytes(B, Hq, Hkv, T, 128)
+    ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    args = (dev(inp["q"]), dev(ki), dev(vi), dev(inp["k_cb"]), dev(inp["v_cb"]), scale)
+    prev = dqa.rvq_decode_set_table_polls(0)
+    try:
+        say("rvq_decode_attention table built alone", B, Hq, Hkv, T, N, Kc)
+        alone = host(dqa.rvq_decode_attention(*args, workspace=ws))
+    finally:
+        dqa.rvq_decode_set_table_polls(prev)
+    check_attention(alone, ref, TOL, "table built alone")
+    say("rvq_decode_attention after it, shared table", B, Hq, Hkv, T, N, Kc)
+    shared = host(dqa.rvq_decode_attention(*args, workspace=ws))
+    check_attention(shared, ref, TOL, "shared table after")
