@@ -743,6 +743,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kFWavesPerS
     load_values(qb + min(i + 1, nq - 1), nxt);
     const _Float16* const Bw = &lds_B[sl][0][0];
 
+    // The wave runs at raised priority from its logit products through its
+    // softmax: of the two waves on a SIMD, the one feeding the matrix cores
+    // (and then needing their results) issues first, and the other fills the
+    // gaps with its value product, staging and loads (measured: kernel 55
+    // against 59 us at 2 bits, 62.7 against 64.4 us at 4 bits).
+    __builtin_amdgcn_s_setprio(1);
     // logits: zero-point K-steps (their sums carry 2^20) and code K-steps in
     // separate accumulators
     float4v zs[2] = {float4v{0.0f, 0.0f, 0.0f, 0.0f}, float4v{0.0f, 0.0f, 0.0f, 0.0f}};
@@ -791,6 +797,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kFWavesPerS
       lg[2 * r + 1] = combine_cols(fmaf(zs[1][r], 1.0f / 1048576.0f, cs[1][r]));
     }
     softmax_step(lg, p, std::false_type{});
+    __builtin_amdgcn_s_setprio(0);
 
     // value product: column (head qh, group vg) holds p * scale
     const uint4 vs4 = *reinterpret_cast<const uint4*>(&lds_vsz[wave][sl][0][vg][8 * grp]);
