@@ -866,7 +866,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kFWavesPerS
     lds_l[wave][lane] = lsum;
   }
   __syncthreads();
-  write_split_state<D, G, kFWaves>(a.partials, a.counters, a.out, a.Hq, unit, b, kvh, split, a.total_splits,
+  write_split_state<D, G, kFWaves>(a.partials, a.counters + unit, a.out, a.Hq, unit, b, kvh, split, a.total_splits,
                                    lds_m, lds_l, lds_o);
 }
 

@@ -472,7 +472,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kDecodeWave
     lds_l[wave][lane] = lsum;
   }
   __syncthreads();
-  write_split_state<D, G, kWavesPerWG>(a.partials, a.counters, a.out, a.Hq, unit, b, kvh, split,
+  write_split_state<D, G, kWavesPerWG>(a.partials, a.counters + unit, a.out, a.Hq, unit, b, kvh, split,
                                        a.total_splits, lds_m, lds_l, lds_o);
 }
 

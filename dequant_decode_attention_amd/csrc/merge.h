@@ -8,8 +8,7 @@
 // last among the splits of a (batch, KV head) -- found with one counter per
 // (batch, KV head), incremented once per workgroup -- merges all splits in
 // split order, so the result does not depend on scheduling, and sets the
-// counter back to zero for the next call.  (write_split_state_flagged finds
-// a merging workgroup with per-split flags instead.)
+// counter back to zero for the next call.
 //
 // The L2 caches are private to each XCD, and a device-scope release fence
 // (an L2 write-back) in every workgroup would cost more than the decode
@@ -196,70 +195,30 @@ __device__ __forceinline__ void merge_splits(const float* partials, float* out, 
 
 // The partial state of split `slot` (store_split_state), and the merge of
 // all splits (merge_splits) by the workgroup that finishes last among the
-// splits of its (batch, KV head), found with one counter per (batch, KV
-// head) that every workgroup increments once; that workgroup sets the
-// counter back to zero.  Called by every thread of the workgroup.
+// splits of its (batch, KV head), found with the unit's counter, which
+// every workgroup increments once; that workgroup sets the counter back to
+// zero (and, if epoch_word is given, stores epoch there).  Called by every
+// thread of the workgroup.
 template <int D, int G, int NW>
-__device__ __forceinline__ void write_split_state(float* partials, uint32_t* counters, float* out, int Hq,
+__device__ __forceinline__ void write_split_state(float* partials, uint32_t* counter, float* out, int Hq,
                                                   size_t unit, int b, int kvh, int slot, int total_splits,
                                                   const float (*lm)[G], const float (*ll)[G],
-                                                  float (*lo)[G][D]) {
+                                                  float (*lo)[G][D], uint32_t* epoch_word = nullptr,
+                                                  uint32_t epoch = 0u) {
   __shared__ int s_last;
   if (!store_split_state<D, G, NW>(partials, out, Hq, unit, b, kvh, slot, total_splits, lm, ll, lo)) return;
   __syncthreads();
   if (threadIdx.x == 0) {
-    const uint32_t done = __hip_atomic_fetch_add(counters + unit, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t done = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_last = done == static_cast<uint32_t>(total_splits - 1);
   }
   __syncthreads();
   if (!s_last) return;
   merge_splits<D, G, NW>(partials, out, Hq, unit, b, kvh, total_splits, lo);
-  if (threadIdx.x == 0) __hip_atomic_store(counters + unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// As write_split_state, with per-split flags in place of the counter: the
-// device-scope read-modify-writes of many workgroups on one counter are
-// carried out one after another, so that the last of 32 splits learns that
-// it is last several microseconds after its partial state is stored.  Each
-// split stores `epoch` (this call's value, one more than the previous
-// call's) into flags[slot] once its partial state has completed, then reads
-// every split's flag; a workgroup that finds them all equal to epoch merges.
-// At least one does (of the last two to store their flags, the second
-// reads the first one's flag after that store has completed), and several
-// may: the merge reads the same states in the same order, so they write the
-// same values.  A merging workgroup (or the only split) then stores epoch
-// into *epoch_word, which the next call reads at its start; every split of
-// this call has read it before storing its flag.  flags and *epoch_word
-// start at zero.  Called by every thread of the workgroup.
-template <int D, int G, int NW>
-__device__ __forceinline__ void write_split_state_flagged(float* partials, uint32_t* flags, uint32_t* epoch_word,
-                                                          uint32_t epoch, float* out, int Hq, size_t unit, int b,
-                                                          int kvh, int slot, int total_splits,
-                                                          const float (*lm)[G], const float (*ll)[G],
-                                                          float (*lo)[G][D]) {
-  __shared__ int s_merge;
-  if (!store_split_state<D, G, NW>(partials, out, Hq, unit, b, kvh, slot, total_splits, lm, ll, lo)) {
-    if (threadIdx.x == 0) __hip_atomic_store(epoch_word, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return;
+  if (threadIdx.x == 0) {
+    __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (epoch_word) __hip_atomic_store(epoch_word, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  __syncthreads();
-  if (threadIdx.x < 64) {
-    const int lane = threadIdx.x;
-    if (lane == 0) __hip_atomic_store(flags + slot, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __builtin_amdgcn_s_waitcnt(0);
-    bool missing = false;
-#pragma unroll
-    for (int k = 0; k < kMaxSplitsMerge / 64; ++k) {
-      const int i = lane + 64 * k;
-      if (i < total_splits && i != slot)
-        missing |= __hip_atomic_load(flags + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != epoch;
-    }
-    if (lane == 0) s_merge = __builtin_amdgcn_ballot_w64(missing) == 0;
-  }
-  __syncthreads();
-  if (!s_merge) return;
-  merge_splits<D, G, NW>(partials, out, Hq, unit, b, kvh, total_splits, lo);
-  if (threadIdx.x == 0) __hip_atomic_store(epoch_word, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Workspace bytes of the merge: the counters, then the partial states of

@@ -34,7 +34,7 @@ extern "C" const char* dqa_status_string(int status) {
   }
 }
 
-extern "C" int dqa_abi_version(void) { return 13; }
+extern "C" int dqa_abi_version(void) { return 14; }
 
 extern "C" int dqa_stream_copy(const void* src, void* dst, size_t bytes, void* stream) {
   if (bytes == 0) return DQA_OK;

@@ -322,8 +322,8 @@ constexpr int kLutWorkgroups = 512; // table-path workgroups resident at once (2
 // this bound is only reached when they cannot all be resident)
 constexpr int kTablePolls = 1 << 18;
 // per-(batch, KV head) synchronization words: the call epoch, a table-piece
-// flag per split, a merge flag per split
-constexpr int kSyncWords = 1 + 2 * kMaxSplitsMerge;
+// flag per split, the merge counter
+constexpr int kSyncWords = 2 + kMaxSplitsMerge;
 
 // floats between the tables of consecutive units (16-byte aligned rows)
 __host__ __device__ inline int lut_stride(int G, int N, int Kc) { return (G * N * Kc + 63) / 64 * 64; }
@@ -541,7 +541,10 @@ __global__ __launch_bounds__(256) void rvq_decode_kernel(RvqDecArgs a) {
           }
         }
       }
-      // the piece's stores have completed before its flag is set
+      // the piece's stores (device-scope, write-through) have completed
+      // before its flag is set, as the partial states before the merge
+      // counter: a device-scope release fence (an L2 write-back) here cost
+      // 4.7 us per step
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       if (threadIdx.x == 0) __hip_atomic_store(sync + 1 + split, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -737,13 +740,20 @@ __global__ __launch_bounds__(256) void rvq_decode_kernel(RvqDecArgs a) {
     }
   }
   __syncthreads();
-  write_split_state_flagged<kD, G, kDecWaves>(a.partials, sync + 1 + kMaxSplitsMerge, sync, epoch, a.out, a.Hq,
-                                              unit, b, kvh, split, a.splits, lds_m, lds_l, lds_o);
+  // the merge: the last split to finish, found with the unit's counter
+  // (the per-split flags that find the table's pieces complete are not
+  // used to elect a merging split: with the workgroups of a unit in two
+  // resident rounds, a split so elected read another split's state before
+  // it had arrived, one head in some runs)
+  write_split_state<kD, G, kDecWaves>(a.partials, sync + kSyncWords - 1, a.out, a.Hq, unit, b, kvh, split, a.splits,
+                                      lds_m, lds_l, lds_o, sync, epoch);
+  if (a.splits == 1 && threadIdx.x == 0)
+    __hip_atomic_store(sync, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 struct RvqGeometry {
   int G, n_tiles, tps, splits;
-  size_t units, ws_bytes, lut_off, sync_off;
+  size_t units, ws_bytes, lut_off, sync_bytes;
 };
 
 int rvq_geometry(int B, int Hq, int Hkv, int T, int d, RvqGeometry* g) {
@@ -761,12 +771,16 @@ int rvq_geometry(int B, int Hq, int Hkv, int T, int d, RvqGeometry* g) {
   if (s < 1) s = 1;
   g->tps = g->n_tiles > 0 ? static_cast<int>((g->n_tiles + s - 1) / s) : 1;
   g->splits = g->n_tiles > 0 ? (g->n_tiles + g->tps - 1) / g->tps : 1;
-  // partial states (none with one split), room for the key-logit table of
-  // every unit, then the synchronization words
+  // the synchronization words first, at offsets that do not depend on the
+  // shape (one block per (batch, KV head), for at least 16384 of them, as the
+  // merge counters of the other decode paths), so that one workspace serves
+  // calls of any shape without being cleared again; then the partial states
+  // (none with one split) and the key-logit table of every unit
+  const size_t sync_units = g->units > kMergeCountersMin ? g->units : kMergeCountersMin;
+  g->sync_bytes = (sync_units * kSyncWords * sizeof(uint32_t) + 255) / 256 * 256;
   const size_t part = g->splits > 1 ? g->units * g->splits * g->G * (kD + 2) * sizeof(float) : 0;
-  g->lut_off = (part + 255) / 256 * 256;
-  g->sync_off = g->lut_off + g->units * kLutFloats * sizeof(float);
-  g->ws_bytes = g->sync_off + (g->units * kSyncWords * sizeof(uint32_t) + 255) / 256 * 256;
+  g->lut_off = g->sync_bytes + (part + 255) / 256 * 256;
+  g->ws_bytes = g->lut_off + g->units * kLutFloats * sizeof(float);
   return DQA_OK;
 }
 
@@ -829,9 +843,9 @@ extern "C" int rvq_decode_attention(const uint16_t* q, int B, int Hq, int Hkv, i
   a.k_cb = k_cb;
   a.v_cb = v_cb;
   a.out = out;
-  a.partials = static_cast<float*>(ws);
+  a.sync = static_cast<uint32_t*>(ws);
+  a.partials = reinterpret_cast<float*>(static_cast<char*>(ws) + g.sync_bytes);
   a.lut = reinterpret_cast<float*>(static_cast<char*>(ws) + g.lut_off);
-  a.sync = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + g.sync_off);
   a.Hq = Hq;
   a.Hkv = Hkv;
   a.T = T;

@@ -1056,7 +1056,7 @@ __global__ __launch_bounds__(256, 2) void zoned_decode_kernel(ZDecodeArgs a) {
     }
   }
   __syncthreads();
-  write_split_state<D, G, kZWaves>(a.partials, a.counters, a.out, a.Hq, static_cast<size_t>(unit), b, kvh,
+  write_split_state<D, G, kZWaves>(a.partials, a.counters + unit, a.out, a.Hq, static_cast<size_t>(unit), b, kvh,
                                    split, a.splits, lds_m, lds_l, lds_o);
 }
 

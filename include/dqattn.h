@@ -65,7 +65,9 @@ enum {
 const char* dqa_status_string(int status);
 
 /* Version of this interface (increments on any signature or layout change). */
-int dqa_abi_version(void);  /* 13: rvq_decode_set_table_polls;
+int dqa_abi_version(void);  /* 14: rvq_decode_attention's workspace starts
+                              with its synchronization words;
+                              13: rvq_decode_set_table_polls;
                               12: rvq_decode_attention is one launch
                               (the key-logit tables are built in it) and
                               its workspace ends with synchronization
@@ -396,12 +398,13 @@ int rvq_encode(const uint16_t* x, int64_t n, int d, const uint16_t* codebooks,
                int N, int Kc, int16_t* idx, void* ws, size_t ws_bytes,
                void* stream);
 
-/* Workspace bytes for rvq_decode_attention (0 if invalid): partial softmax
- * states, room for the key-logit table (64 KB per (batch, KV head)), then
- * 257 synchronization words per (batch, KV head) (a call counter, and a
- * table-piece flag and a merge flag per split).  Zero it before its first
- * use; every call leaves the words as the next call on it expects (for any
- * shape), so it is not cleared again. */
+/* Workspace bytes for rvq_decode_attention (0 if invalid): 130
+ * synchronization words per (batch, KV head), for at least 16384 of them,
+ * at the start (a call counter, a table-piece flag per split, the merge
+ * counter), then partial softmax states and room for the key-logit table
+ * (64 KB per (batch, KV head)).  Zero it before its first use; every call
+ * leaves the words as the next call on it expects, for any shape of up to
+ * 16384 (batch, KV head) units, so it is not cleared again. */
 size_t rvq_decode_attention_workspace_bytes(int B, int Hq, int Hkv, int T, int d);
 
 /* Decode attention with keys and values rebuilt on the fly from their
@@ -416,8 +419,8 @@ size_t rvq_decode_attention_workspace_bytes(int B, int Hq, int Hkv, int T, int d
  * that (batch, KV head) in the same launch (a piece each, through the
  * workspace) and staged in LDS, so each key costs N lookups instead of N
  * gathered codewords; otherwise keys are rebuilt like values.
- * Enqueues one kernel; a split that finds every split's partial state
- * stored merges them in split order.  Calls that overlap on one workspace
+ * Enqueues one kernel; the last split of each (batch, KV head) to finish
+ * merges the splits in split order.  Calls that overlap on one workspace
  * race.
  * Errors: DQA_ERR_NULL, DQA_ERR_SHAPE, DQA_ERR_ALIGN, DQA_ERR_WORKSPACE,
  * DQA_ERR_UNSUPPORTED, DQA_ERR_HIP. */

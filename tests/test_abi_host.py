@@ -333,7 +333,7 @@ def test_rvq_validation_and_workspace():
 
 def test_kivi_append_validation():
     """Argument checks of the streaming append (all fail before any launch)."""
-    assert lib.dqa_abi_version() == 13
+    assert lib.dqa_abi_version() == 14
     c = _cache(T_cap=128, R_cap=128)
     # staging holds the recent and the new rows of K and V
     assert lib.kivi_append_workspace_bytes(ctypes.byref(c), 20) == 2 * 2 * 2 * (16 + 20) * 128 * 2

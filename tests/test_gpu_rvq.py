@@ -213,3 +213,22 @@ def test_decode_attention_table_built_alone(dqa, B, Hq, Hkv, T, N, Kc):
     say("rvq_decode_attention after it, shared table", B, Hq, Hkv, T, N, Kc)
     shared = host(dqa.rvq_decode_attention(*args, workspace=ws))
     check_attention(shared, ref, TOL, "shared table after")
+
+
+def test_decode_attention_two_rounds_of_workgroups(dqa):
+    """Keys by gathered codewords at 8 (batch, KV head) units x 86 splits:
+    more workgroups than are resident at once, so the splits of one unit
+    run in two rounds and its merge waits on the last; three calls, each
+    against the oracle (a merge that reads a split's state before it has
+    arrived shows as one wrong head)."""
+    B, Hq, Hkv, T, N, Kc = 2, 12, 4, 8192, 4, 4608
+    inp = rvq_inputs(B, Hq, Hkv, 128, T, N, Kc, seed=100)
+    rng = np.random.default_rng(T)
+    ki = rng.integers(0, Kc, size=(B, Hkv, T, N)).astype(np.int16)
+    vi = rng.integers(0, Kc, size=(B, Hkv, T, N)).astype(np.int16)
+    scale = 1.0 / math.sqrt(128)
+    ref = oracle.rvq_decode_attention(inp["q"], ki, vi, inp["k_cb"], inp["v_cb"], scale)
+    args = (dev(inp["q"]), dev(ki), dev(vi), dev(inp["k_cb"]), dev(inp["v_cb"]), scale)
+    for call in range(3):
+        say("rvq_decode_attention two rounds", call)
+        check_attention(host(dqa.rvq_decode_attention(*args)), ref, TOL, f"two rounds call {call}")
