@@ -310,13 +310,13 @@ __global__ __launch_bounds__(NW * 64) void rvq_encode_kernel(const uint16_t* __r
 
 // ------------------------------------------------------------------ decode
 
-constexpr int kDecWaves = 4;
+constexpr int kDecWaves = 8;     // one workgroup per compute unit, two waves per SIMD
 // Key logits through a table: q . k_hat = sum_s q . Ck_s[k_idx[s]], so a
 // table T[h][s][c] = q_h . Ck_s[c] (scaled into the log2 domain) turns each
 // key logit into N lookups instead of N gathered codewords.  Used when the
 // table of one (batch, KV head) fits this many floats of LDS.
 constexpr int kLutFloats = 16384;   // 64 KB
-constexpr int kLutWorkgroups = 512; // table-path workgroups resident at once (2 per compute unit)
+constexpr int kLutWorkgroups = 256; // table-path workgroups resident at once (one per compute unit)
 // polls of a unit's table flags before a workgroup builds the whole table
 // itself (the pieces come from workgroups that do not wait for anything, so
 // this bound is only reached when they cannot all be resident)
@@ -424,7 +424,7 @@ __device__ __forceinline__ void rebuild16(const uint16_t* cb, const int16_t* idx
 // one tile ahead; the first tile's rows are requested while the table is
 // staged.
 template <int G, bool LUT, bool VPRE>
-__global__ __launch_bounds__(256) void rvq_decode_kernel(RvqDecArgs a) {
+__global__ __launch_bounds__(64 * kDecWaves) void rvq_decode_kernel(RvqDecArgs a) {
   constexpr int NCK = 8, TL = 8, IT = 4;
   constexpr int RB = (LUT && G <= 3) ? 4 : 2;
   static_assert(IT % RB == 0, "ring slots map onto fixed sub-tiles");
@@ -572,20 +572,20 @@ __global__ __launch_bounds__(256) void rvq_decode_kernel(RvqDecArgs a) {
     }
     __syncthreads();
     if (s_table) {
-      // at most kLutFloats / 2 8-byte words: 32 per thread, all in flight
-      constexpr int kWords = kLutFloats / 2 / 256;
+      // at most kLutFloats / 2 8-byte words: 16 per thread, all in flight
+      constexpr int kWords = kLutFloats / 2 / (64 * kDecWaves);
       const int n8 = lut_stride(G, a.N, a.Kc) / 2;
       const uint64_t* src = reinterpret_cast<const uint64_t*>(tab);
       uint64_t* dst = reinterpret_cast<uint64_t*>(lds_lut);
       uint64_t w[kWords];
 #pragma unroll
       for (int k = 0; k < kWords; ++k) {
-        const int i = 256 * k + static_cast<int>(threadIdx.x);
+        const int i = 64 * kDecWaves * k + static_cast<int>(threadIdx.x);
         w[k] = i < n8 ? __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
       }
 #pragma unroll
       for (int k = 0; k < kWords; ++k) {
-        const int i = 256 * k + static_cast<int>(threadIdx.x);
+        const int i = 64 * kDecWaves * k + static_cast<int>(threadIdx.x);
         if (i < n8) dst[i] = w[k];
       }
     } else {
@@ -858,8 +858,9 @@ extern "C" int rvq_decode_attention(const uint16_t* q, int B, int Hq, int Hkv, i
   a.table_polls = g_table_polls;
   const bool use_lut = T > 0 && static_cast<long long>(g.G) * N * Kc <= kLutFloats && N <= 8;
   if (use_lut) {
-    // two table-holding workgroups fit a compute unit: one resident round
-    // of them, so that each stages its table once for more tiles
+    // one table-holding workgroup of eight waves per compute unit (the
+    // table once in its LDS): one resident round of them, so that each
+    // stages its table once for more tiles
     long long sp = kLutWorkgroups / static_cast<long long>(g.units);
     if (sp > g.splits) sp = g.splits;
     if (sp < 1) sp = 1;
@@ -874,7 +875,7 @@ extern "C" int rvq_decode_attention(const uint16_t* q, int B, int Hq, int Hkv, i
   switch (g.G * 4 + (use_lut ? 2 : 0) + (vpre ? 1 : 0)) {
 #define DQA_RVQ_CASE(G_, L_, V_) \
   case G_ * 4 + (L_ ? 2 : 0) + (V_ ? 1 : 0): \
-    hipLaunchKernelGGL((rvq_decode_kernel<G_, L_, V_>), grid, dim3(256), 0, s, a); \
+    hipLaunchKernelGGL((rvq_decode_kernel<G_, L_, V_>), grid, dim3(64 * kDecWaves), 0, s, a); \
     break;
 #define DQA_RVQ_CASES(G_) DQA_RVQ_CASE(G_, false, false) DQA_RVQ_CASE(G_, false, true) \
   DQA_RVQ_CASE(G_, true, false) DQA_RVQ_CASE(G_, true, true)
