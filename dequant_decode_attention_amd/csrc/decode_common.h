@@ -63,6 +63,7 @@ struct RopeOmega {
 // decode_feat.hip): its resident workgroup target and its launch.
 int feat_decode_workgroups();
 int feat_recent_weight();
+int feat_waves_per_wg();
 int launch_feat_decode(const KiviArgs& a, int d, int G, int bits, dim3 grid, hipStream_t s);
 // The in-tile trig table of a cache (kivi_rope_table): its size in uint32
 // words for head dim d, and its build kernel (bits 2 or 4, d 64 or 128).

@@ -56,7 +56,7 @@
 namespace dqa {
 namespace {
 
-constexpr int kFWaves = 4;          // waves per workgroup
+constexpr int kFWaves = 8;          // waves per workgroup (one workgroup per compute unit)
 constexpr int kFWavesPerSimd = 2;   // resident waves per SIMD (register budget 256)
 // work units of an fp16 recent tile in the split of tiles over waves (its
 // query rotation and fp32 key rotation cost about two more quantized tiles)
@@ -256,7 +256,7 @@ __global__ __launch_bounds__(256) void rope_table_kernel(RopeOmega w, uint32_t* 
 // ----------------------------------------------------------------- kernel
 
 template <int D, int BITS, int G>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kFWavesPerSimd))) void kivi_feat_kernel(
+__global__ __launch_bounds__(64 * kFWaves) __attribute__((amdgpu_waves_per_eu(kFWavesPerSimd))) void kivi_feat_kernel(
     KiviArgs a) {
   static_assert(BITS == 2 || BITS == 4, "feature kernel: 2- and 4-bit codes");
   constexpr int NP = D / 2;              // RoPE pairs
@@ -418,7 +418,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kFWavesPerS
     // together, the header checked when they arrive (requesting them at the
     // kernel's start was measured slower: more registers live across the
     // tile loads)
-    constexpr int kPieces = (2 * kGroup * NP / 4 + 255) / 256;   // 16-byte pieces per thread
+    constexpr int kPieces = (2 * kGroup * NP / 4 + 64 * kFWaves - 1) / (64 * kFWaves);   // 16-byte pieces per thread
     bool copy = false;
     uint4 tv[kPieces];
     float2 step{1.0f, 0.0f};
@@ -427,7 +427,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kFWavesPerS
       const uint32_t* const gt = a.rope_table + kRopeTableHeader;
 #pragma unroll
       for (int k = 0; k < kPieces; ++k)
-        tv[k] = reinterpret_cast<const uint4*>(gt)[min(tid + 256 * k, 2 * kGroup * NP / 4 - 1)];
+        tv[k] = reinterpret_cast<const uint4*>(gt)[min(tid + 64 * kFWaves * k, 2 * kGroup * NP / 4 - 1)];
       if (tid < NP) step = reinterpret_cast<const float2*>(gt + 2 * kGroup * NP)[tid];
       copy = hdr.x == kRopeTableMagic && hdr.y == static_cast<uint32_t>(BITS) && hdr.z == static_cast<uint32_t>(D) &&
              hdr.w == __builtin_bit_cast(uint32_t, a.rope_theta);
@@ -435,7 +435,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kFWavesPerS
     if (copy) {
 #pragma unroll
       for (int k = 0; k < kPieces; ++k) {
-        const int w0 = 4 * (tid + 256 * k);
+        const int w0 = 4 * (tid + 64 * kFWaves * k);
         if (w0 < 2 * kGroup * NP) {
           const int half = w0 / (kGroup * NP), j = (w0 % (kGroup * NP)) / NP, ps = w0 % NP;
           *reinterpret_cast<uint4*>(half ? &lds_tl[j][ps] : &lds_th[j][ps]) = tv[k];
@@ -443,7 +443,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kFWavesPerS
       }
       if (tid < NP) lds_step[tid] = step;
     } else {
-      build_trig_table<D, BITS, 256>(
+      build_trig_table<D, BITS, 64 * kFWaves>(
           a.omega, base, tid,
           [&](int j, int ps, uint32_t h, uint32_t l) {
             lds_th[j][ps] = h;
@@ -873,9 +873,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kFWavesPerS
 template <int D, int BITS>
 int launch_feat_g(const KiviArgs& a, int G, dim3 grid, hipStream_t s) {
   switch (G) {
-    case 1: hipLaunchKernelGGL((kivi_feat_kernel<D, BITS, 1>), grid, dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((kivi_feat_kernel<D, BITS, 2>), grid, dim3(256), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((kivi_feat_kernel<D, BITS, 4>), grid, dim3(256), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((kivi_feat_kernel<D, BITS, 1>), grid, dim3(64 * kFWaves), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((kivi_feat_kernel<D, BITS, 2>), grid, dim3(64 * kFWaves), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((kivi_feat_kernel<D, BITS, 4>), grid, dim3(64 * kFWaves), 0, s, a); break;
     default: return DQA_ERR_UNSUPPORTED;
   }
   return DQA_OK;
@@ -883,7 +883,8 @@ int launch_feat_g(const KiviArgs& a, int G, dim3 grid, hipStream_t s) {
 
 }  // namespace
 
-int feat_decode_workgroups() { return 256 * kFWavesPerSimd; }
+int feat_decode_workgroups() { return 256 * kFWavesPerSimd * 4 / kFWaves; }
+int feat_waves_per_wg() { return kFWaves; }
 int feat_recent_weight() { return kRecentWeight; }
 
 size_t feat_rope_table_words(int d) { return rope_table_words(d); }

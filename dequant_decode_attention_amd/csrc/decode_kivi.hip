@@ -643,7 +643,7 @@ extern "C" int decode_attention_qkv_partial(const uint16_t* q, const dqa_kivi_ca
   a.n_rtiles = p.n_rtiles;
   a.total_splits = p.total;
   a.split = make_tile_split(p.n_qtiles, p.n_rtiles, use_feat(c->bits, c->rope_theta > 0.0f) ? feat_recent_weight() : 1,
-                            static_cast<long long>(p.total) * kWavesPerWG);
+                            static_cast<long long>(p.total) * (use_feat(c->bits, c->rope_theta > 0.0f) ? feat_waves_per_wg() : kWavesPerWG));
   a.q_scale = sm_scale * 1.4426950408889634f;
   const bool rope = c->rope_theta > 0.0f;
   rope_omega(c->rope_theta, c->d, a.omega);
