@@ -602,10 +602,12 @@ __global__ __launch_bounds__(128) void zoned_pack_kernel(PackArgs a) {
 
 // ------------------------------------------------------------------ reader
 
-constexpr int kZWaves = 4;
-// Workgroups per launch: one resident round (two workgroups of four waves
-// per compute unit on 256 CUs), so every wave pays its start-up once.
-constexpr int kZoneWorkgroups = 512;
+constexpr int kZWaves = 8;
+// Workgroups per launch: one resident round (one workgroup of eight waves,
+// two per SIMD, per compute unit on 256 CUs), so every wave pays its
+// start-up once and a (batch, KV head) has half as many splits to merge as
+// with two workgroups of four waves per CU.
+constexpr int kZoneWorkgroups = 256;
 // Staging bytes per wave: a zone-A group's key block (at most 8,480 B for
 // d = 128: 32 key rows of at most 66 words, then scales and zeros), or a
 // zone-C chunk's fp16 keys (8 KiB).  The host checks every unit against it.
@@ -715,7 +717,7 @@ __device__ __forceinline__ void stage_block(const uint4* src, uint4* dst, int n1
 // group) and summed over lanes once at the end.  fp16 value rows (zone B,
 // zone C) are loaded into registers while the keys are staged.
 template <int D, int G>
-__global__ __launch_bounds__(256, 2) void zoned_decode_kernel(ZDecodeArgs a) {
+__global__ __launch_bounds__(64 * kZWaves, 1) void zoned_decode_kernel(ZDecodeArgs a) {
   constexpr int CV = D / 64;                        // value channels per lane
   constexpr int NG = D / kGroup;                    // value groups per token
   constexpr int NGH = NG / 2;                       // value groups per lane half
@@ -1092,9 +1094,9 @@ int zoned_geometry(const int32_t* p, int Hq, ZGeometry* g) {
 template <int D>
 int zlaunch(const ZDecodeArgs& a, int G, dim3 grid, hipStream_t s) {
   switch (G) {
-    case 1: hipLaunchKernelGGL((zoned_decode_kernel<D, 1>), grid, dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((zoned_decode_kernel<D, 2>), grid, dim3(256), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((zoned_decode_kernel<D, 4>), grid, dim3(256), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((zoned_decode_kernel<D, 1>), grid, dim3(64 * kZWaves), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((zoned_decode_kernel<D, 2>), grid, dim3(64 * kZWaves), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((zoned_decode_kernel<D, 4>), grid, dim3(64 * kZWaves), 0, s, a); break;
     default: return DQA_ERR_UNSUPPORTED;
   }
   DQA_CHECK_LAUNCH();
